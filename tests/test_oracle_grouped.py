@@ -1,0 +1,109 @@
+"""Pins for the grouped GEMM oracle (Modular page
+"grouped_matmul_sm100_persistent": a_offsets prefix sum, expert_ids with
+negative entries skipping, expert_usage_stats[1] = active count, transpose_b)."""
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import numerics as nm
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "grouped_worked_example.json")
+SENT = 0xFFC1  # a bf16 NaN pattern used as "never written" sentinel
+
+
+def test_worked_example_from_fixture():
+    g = json.load(open(GOLD))
+    a = nm.bf16_bits_of(np.array(g["A"], dtype=np.float64))
+    b = nm.bf16_bits_of(np.array(g["B"], dtype=np.float64))
+    c0 = nm.bf16_bits_of(np.array(g["C_prior"], dtype=np.float64))
+    c = oracle.grouped_gemm(c0, a, np.array(g["a_offsets"], np.uint32), b,
+                            np.array(g["expert_ids"], np.int32), np.array(g["usage"], np.uint32))
+    assert np.array_equal(nm.decode_bf16(c), np.array(g["C_expected"], dtype=np.float64))
+
+
+def test_single_group_reduces_to_plain_gemm():
+    T, K, N = 37, 64, 24
+    d = synth.grouped_inputs(seed=1, E=1, T=T, K=K, N=N, skip_frac=0.0)
+    c0 = np.full((T, N), SENT, np.uint16)
+    c = oracle.grouped_gemm(c0, d.a, np.array([0, T], np.uint32), d.b, np.array([0], np.int32),
+                            np.array([T, 1], np.uint32))
+    ta = torch.from_numpy(nm.decode_bf16(d.a))
+    tb = torch.from_numpy(nm.decode_bf16(d.b[0]))
+    ref = (ta @ tb.T).numpy()
+    assert np.array_equal(nm.decode_bf16(c), nm.round_to_bf16(ref))
+
+
+def test_skip_everything_leaves_c_untouched():
+    d = synth.grouped_inputs(seed=2, E=4, T=20, K=32, N=16)
+    c0 = np.full((20, 16), SENT, np.uint16)
+    ids = np.full(4, -1, np.int32)
+    assert np.array_equal(oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, ids, d.usage), c0)
+    assert np.array_equal(oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids,
+                                              np.array([5, 0], np.uint32)), c0)
+
+
+def test_routing_with_scaled_identities_is_exact():
+    """B[e] = 2^((e mod 16) - 8) * I, so each written row is its A row times its expert's factor."""
+    E, T, K = 12, 90, 32
+    rng = np.random.default_rng(3)
+    d = synth.grouped_inputs(seed=3, E=E, T=T, K=K, N=K, skip_frac=0.2)
+    ids = rng.permutation(d.expert_ids)
+    fac = np.ldexp(1.0, (np.arange(E) % 16) - 8)
+    b = nm.bf16_bits_of(fac[:, None, None] * np.eye(K)[None])
+    c0 = np.full((T, K), SENT, np.uint16)
+    c = oracle.grouped_gemm(c0, d.a, d.a_offsets, b, ids, d.usage)
+    a = nm.decode_bf16(d.a)
+    for g in range(E):
+        r0, r1 = d.a_offsets[g], d.a_offsets[g + 1]
+        if ids[g] < 0:
+            assert np.all(c[r0:r1] == SENT)
+        else:
+            assert np.array_equal(nm.decode_bf16(c[r0:r1]), a[r0:r1] * fac[ids[g]])
+
+
+def test_edges_empty_duplicate_partial_offset():
+    """Empty groups, repeated experts, fewer active groups than listed, a_offsets[0] > 0."""
+    T, K, N = 30, 16, 8
+    d = synth.grouped_inputs(seed=4, E=3, T=T, K=K, N=N, skip_frac=0.0)
+    a_off = np.array([2, 2, 9, 20, 28], np.uint32)       # group 0 empty; rows 0..1, 28.. unlisted
+    ids = np.array([1, 1, 0, 2], np.int32)                # expert 1 twice
+    usage = np.array([11, 3], np.uint32)                  # group 3 not active
+    c0 = np.full((T, N), SENT, np.uint16)
+    c = oracle.grouped_gemm(c0, d.a, a_off, d.b, ids, usage)
+    a = nm.decode_bf16(d.a)
+    b = nm.decode_bf16(d.b)
+    assert np.all(c[:2] == SENT) and np.all(c[20:] == SENT)
+    assert np.array_equal(nm.decode_bf16(c[2:9]), nm.round_to_bf16(a[2:9] @ b[1].T))
+    assert np.array_equal(nm.decode_bf16(c[9:20]), nm.round_to_bf16(a[9:20] @ b[0].T))
+
+
+def test_brute_force_loops_and_both_b_layouts():
+    E, G, T, K, N = 4, 5, 40, 32, 32
+    rng = np.random.default_rng(5)
+    d = synth.grouped_inputs(seed=5, E=E, T=T, K=K, N=N, skip_frac=0.0)
+    cuts = np.sort(rng.integers(0, T + 1, G - 1))
+    a_off = np.concatenate([[0], cuts, [T]]).astype(np.uint32)
+    ids = np.array([3, -1, 0, 3, 1], np.int32)
+    usage = np.array([T, G], np.uint32)
+    c0 = np.full((T, N), SENT, np.uint16)
+    c = oracle.grouped_gemm(c0, d.a, a_off, d.b, ids, usage)
+    a = nm.decode_bf16(d.a)
+    b = nm.decode_bf16(d.b)
+    ref = np.full((T, N), np.nan)
+    for g in range(G):
+        if ids[g] < 0:
+            continue
+        for r in range(a_off[g], a_off[g + 1]):
+            for n in range(N):
+                ref[r, n] = sum(a[r, k] * b[ids[g], n, k] for k in range(K))
+    written = ~np.isnan(ref[:, 0])
+    assert np.array_equal(nm.decode_bf16(c[written]), nm.round_to_bf16(ref[written]))
+    assert np.all(c[~written] == SENT)
+    # transpose_b = False: the same weights stored [E, K, N]
+    bt = np.ascontiguousarray(d.b.transpose(0, 2, 1))
+    c2 = oracle.grouped_gemm(c0, d.a, a_off, bt, ids, usage, transpose_b=False)
+    assert np.array_equal(c2, c)

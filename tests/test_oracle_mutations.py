@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least one
+pin fails for each: evidence that the pins constrain the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import numerics as nm
+from oracle import w4 as ow4
+from oracle import kproj as okp
+import test_oracle_w4 as tw4
+import test_oracle_kproj as tkp
+import test_oracle_numerics as tnm
+
+_orig_dequant = ow4.dequant_w4
+
+
+def _dequant_variant(kind):
+    def f(b_packed, scales_bits, group_size, pack_factor=8):
+        b = np.asarray(b_packed, dtype=np.uint32)
+        K = b.shape[0] * 8
+        s = nm.decode_f16(scales_bits)
+        order = np.arange(8)[::-1] if kind == "nibble_order" else np.arange(8)
+        shifts = (4 * order.astype(np.uint32))[None, :, None]
+        q = ((b[:, None, :] >> shifts) & np.uint32(0xF)).astype(np.int64).reshape(K, -1)
+        zp = 7 if kind == "zero_point" else 8
+        gsz = group_size // 2 if kind == "group_index" else group_size
+        gidx = np.minimum(np.arange(K) // gsz, s.shape[0] - 1)
+        w = (q - zp).astype(np.float64) * s[gidx, :]
+        if kind == "signed_code":
+            w = np.where(q >= 8, q - 16, q).astype(np.float64) * s[gidx, :]
+        return w
+    return f
+
+
+W4_PINS = [tw4.test_worked_examples_from_fixture, tw4.test_nibble_position,
+           tw4.test_identity_gives_unpacked_weights_exactly, tw4.test_closed_form_ones_and_power_of_two_scales]
+
+
+@pytest.mark.parametrize("kind", ["nibble_order", "zero_point", "group_index", "signed_code"])
+def test_w4_mutation_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(ow4, "dequant_w4", _dequant_variant(kind))
+    failures = 0
+    for pin in W4_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, kind
+
+
+def test_round_mutation_is_caught(monkeypatch):
+    """Round half away from zero instead of half to even."""
+    def bad(x, fmt):
+        x = np.asarray(x, dtype=np.float64)
+        _, e = np.frexp(x)
+        q = np.ldexp(1.0, np.maximum(e - 1, fmt.emin) - (fmt.p - 1))
+        return np.sign(x) * np.floor(np.abs(x) / q + 0.5) * q
+    monkeypatch.setattr(nm, "round_to", bad)
+    with pytest.raises(AssertionError):
+        tnm.test_round_f16_brute_force_and_numpy()
+
+
+def test_kproj_mutations_are_caught(monkeypatch):
+    # page index taken from the token index instead of the cache position
+    orig = okp.token_slots
+
+    def bad_slots(row_offsets, cache_lengths, page_table, page_size):
+        return orig(row_offsets, np.zeros_like(np.asarray(cache_lengths)), page_table, page_size)
+    monkeypatch.setattr(okp, "token_slots", bad_slots)
+    with pytest.raises(AssertionError):
+        tkp.test_placement_fingerprint_and_untouched_bytes()
+    monkeypatch.setattr(okp, "token_slots", orig)
+
+    # weight scale indexed with a transposed block index
+    orig_rows = okp.kproj_rows
+
+    def bad_rows(hidden_bits, weight_codes, input_scale, weight_scale, granularity=(1, 128, 128)):
+        return orig_rows(hidden_bits, weight_codes, input_scale, np.ascontiguousarray(weight_scale.T), granularity)
+    monkeypatch.setattr(okp, "kproj_rows", bad_rows)
+    with pytest.raises(AssertionError):
+        tkp.test_brute_force_loops()

@@ -1,0 +1,160 @@
+"""Pins for the W4A16 oracle (Modular page "multistage_gemm_q": group_size and
+pack_factor parameters; rank-2 requirement in its Raises section).
+
+Each pin is chosen so that a plausible slip in the oracle (nibble order, the
+zero point, the group index, a transposed operand, a dropped group) fails."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import numerics as nm
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "w4_worked_examples.json")
+ONE = 0x3C00  # fp16 1.0
+
+
+def _const(shape, v, dtype):
+    return np.full(shape, v, dtype=dtype)
+
+
+def _brute(a_bits, b, s_bits, gs):
+    """Scalar loops; codes read as hexadecimal digits counted from the right."""
+    M, K = a_bits.shape
+    N = b.shape[1]
+    a = a_bits.view(np.float16).astype(np.float64)
+    s = s_bits.view(np.float16).astype(np.float64)
+    out = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                digits = "%08x" % int(b[k // 8, n])
+                q = int(digits[7 - (k % 8)], 16)
+                acc += float(a[m, k]) * (q - 8) * float(s[k // gs, n])
+            out[m, n] = acc
+    return out
+
+
+def test_worked_examples_from_fixture():
+    ex = json.load(open(GOLD))["examples"]
+    assert len(ex) >= 4
+    for e in ex:
+        K, N, M, gs = e["K"], e["N"], e["M"], e["group_size"]
+        b = _const((K // 8, N), int(e["word"], 16), np.uint32)
+        if "scale_bits_per_group" in e:
+            s = np.array([[int(v, 16)] * N for v in e["scale_bits_per_group"]], dtype=np.uint16)
+        else:
+            s = _const((K // gs, N), int(e["scale_bits"], 16), np.uint16)
+        a = _const((M, K), int(e["a_bits"], 16), np.uint16)
+        c = oracle.qgemm_w4(a, b, s, gs)
+        assert [hex(v) for v in c.ravel()] == [hex(int(v, 16)) for v in e["expected_bits"]], e["name"]
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(1, 3, 128, 128), (3, 5, 256, 128), (2, 4, 256, 64), (4, 2, 64, 32)])
+def test_brute_force_small(M, N, K, gs):
+    w = synth.w4_inputs(M, N, K, seed=11 + M, group_size=gs)
+    got = oracle.w4.qgemm_w4_f64(w.a, w.b, w.scales, gs)
+    ref = _brute(w.a, w.b, w.scales, gs)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(oracle.qgemm_w4(w.a, w.b, w.scales, gs), nm.f16_bits_of(nm.round_to_f16(ref)))
+
+
+def test_nibble_position():
+    """Only code j of each word is 9 (weight +1 * scale); a unit A row picks out one K row."""
+    K, gs = 128, 128
+    for j in range(8):
+        b = _const((K // 8, 1), 0x88888888 + (1 << (4 * j)), np.uint32)
+        s = _const((1, 1), ONE, np.uint16)
+        a = np.zeros((8, K), dtype=np.uint16)
+        for jj in range(8):
+            a[jj, 8 * 5 + jj] = ONE          # rows of word kp = 5
+        c = oracle.qgemm_w4(a, b, s, gs).view(np.float16).astype(np.float64).ravel()
+        expect = np.zeros(8)
+        expect[j] = 1.0
+        assert np.array_equal(c, expect), j
+
+
+def test_identity_gives_unpacked_weights_exactly():
+    """A = I_K: C[k, n] = round_fp16((q - 8) * scale) for every k, n."""
+    K, N, gs = 256, 8, 128
+    w = synth.w4_inputs(1, N, K, seed=3, group_size=gs)
+    a = np.zeros((K, K), dtype=np.uint16)
+    np.fill_diagonal(a, ONE)
+    c = oracle.qgemm_w4(a, w.b, w.scales, gs).view(np.float16).astype(np.float64)
+    s = w.scales.view(np.float16).astype(np.float64)
+    for k in range(K):
+        for n in range(N):
+            q = (int(w.b[k // 8, n]) >> (4 * (k % 8))) & 15
+            assert c[k, n] == np.float64(np.float16((q - 8) * s[k // gs, n]))
+
+
+def test_zero_scale_equals_zero_activation_block():
+    M, N, K, gs = 4, 16, 512, 128
+    w = synth.w4_inputs(M, N, K, seed=5, group_size=gs)
+    for g in range(K // gs):
+        s0 = w.scales.copy()
+        s0[g] = 0
+        a0 = w.a.copy()
+        a0[:, g * gs:(g + 1) * gs] = 0
+        c1 = oracle.w4.qgemm_w4_f64(w.a, w.b, s0, gs)
+        c2 = oracle.w4.qgemm_w4_f64(a0, w.b, w.scales, gs)
+        assert np.allclose(c1, c2, rtol=1e-13, atol=1e-13)
+        # and the removed part is that group's own product
+        full = oracle.w4.qgemm_w4_f64(w.a, w.b, w.scales, gs)
+        a_only = np.zeros_like(w.a)
+        a_only[:, g * gs:(g + 1) * gs] = w.a[:, g * gs:(g + 1) * gs]
+        part = oracle.w4.qgemm_w4_f64(a_only, w.b, w.scales, gs)
+        assert np.allclose(full - part, c1, rtol=1e-12, atol=1e-12)
+
+
+def test_scale_linearity_is_exact():
+    M, N, K, gs = 3, 8, 256, 128
+    w = synth.w4_inputs(M, N, K, seed=6, group_size=gs)
+    s2 = nm.f16_bits_of(2 * w.scales.view(np.float16).astype(np.float64))
+    c1 = oracle.qgemm_w4(w.a, w.b, w.scales, gs).view(np.float16).astype(np.float64)
+    c2 = oracle.qgemm_w4(w.a, w.b, s2, gs).view(np.float16).astype(np.float64)
+    assert np.array_equal(c2, 2 * c1)
+
+
+def test_closed_form_ones_and_power_of_two_scales():
+    """A = ones and scales = distinct powers of two: C[n] = sum_g s[g][n] * sum_{k in g} (q - 8)."""
+    N, K, gs = 6, 512, 128
+    rng = np.random.default_rng(7)
+    b = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    G = K // gs
+    exps = rng.integers(-8, -2, size=(G, N))
+    s = nm.f16_bits_of(np.ldexp(1.0, exps))
+    a = _const((1, K), ONE, np.uint16)
+    c64 = oracle.w4.qgemm_w4_f64(a, b, s, gs)[0]
+    c = oracle.qgemm_w4(a, b, s, gs).view(np.float16).astype(np.float64)[0]
+    for n in range(N):
+        total = 0.0
+        for g in range(G):
+            qsum = 0
+            for kp in range(g * gs // 8, (g + 1) * gs // 8):
+                word = int(b[kp, n])
+                qsum += sum(((word >> (4 * i)) & 15) - 8 for i in range(8))
+            total += qsum * 2.0 ** int(exps[g, n])
+        assert c64[n] == total                       # exact: dyadic terms
+        assert c[n] == np.float64(np.float16(total))  # one nearest-even rounding
+
+
+def test_column_permutation():
+    M, N, K, gs = 2, 12, 256, 128
+    w = synth.w4_inputs(M, N, K, seed=8, group_size=gs)
+    perm = np.random.default_rng(0).permutation(N)
+    c = oracle.qgemm_w4(w.a, w.b, w.scales, gs)
+    cp = oracle.qgemm_w4(w.a, w.b[:, perm], w.scales[:, perm], gs)
+    assert np.array_equal(cp, c[:, perm])
+
+
+def test_rank2_is_required():
+    w = synth.w4_inputs(2, 8, 128, seed=1)
+    with pytest.raises(ValueError):
+        oracle.qgemm_w4(w.a[None], w.b, w.scales, 128)
+    with pytest.raises(ValueError):
+        oracle.qgemm_w4(w.a, w.b.ravel(), w.scales, 128)
