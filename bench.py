@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark of the dequant-in-kernel GEMM hot path on one MI355X.
+
+Default workload (the headline): decode-shaped W4A16 GEMM, N = K = 4096,
+group_size 128, M in {1, 4, 16}. One step = one qgemm_w4 call per M (three
+launches). Weights, scales, activations and outputs are rotated over enough
+device copies (>= 1 GiB) that every launch reads its operands from HBM, not
+from the 256 MB Infinity Cache or the L2s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|square|grouped|kproj]
+
+Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
+steps (the decode shapes are bound by HBM); TFLOP/s is reported beside it. The
+`roofline` object uses the kernel's average launch duration measured with HIP
+events on the launch stream; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2516.6
+FP8_MFMA_PEAK_TFLOPS = 5033.2
+ROTATE_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "kproj"])
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def event_time_ms(torch, fn_launches, stream):
+    """Total ms of a sequence of launches, bracketed by events on `stream`."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    fn_launches()
+    e.record(stream)
+    e.synchronize()
+    return s.elapsed_time(e)
+
+
+def cpu_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+def w4_bytes(M, N, K, gs):
+    return M * K * 2 + K * N // 2 + (K // gs) * N * 2 + M * N * 2
+
+
+class DecodeW4:
+    name = "w4a16_decode_N4096_K4096_gs128_M1_4_16"
+    kernel = "w4_decode_kernel"
+    bound = "hbm"
+
+    def __init__(self, torch, q, synth):
+        self.torch, self.q = torch, q
+        cfgs = synth.W4_DECODE
+        N, K = cfgs[0]["N"], cfgs[0]["K"]
+        self.N, self.K, self.gs = N, K, 128
+        self.Ms = [c["M"] for c in cfgs]
+        self.inputs = [synth.w4_inputs(**c) for c in cfgs]
+        foot = sum(w4_bytes(M, N, K, 128) for M in self.Ms)
+        self.R = max(1, math.ceil(ROTATE_BYTES / foot))
+        dev = torch.device("cuda")
+        b = torch.from_numpy(self.inputs[0].b.view(np.int32)).to(dev)
+        s = torch.from_numpy(self.inputs[0].scales.view(np.int16)).to(dev).view(torch.float16)
+        self.slots = []
+        for r in range(self.R):
+            slot = []
+            for i, M in enumerate(self.Ms):
+                a = torch.from_numpy(self.inputs[i].a.view(np.int16)).to(dev).view(torch.float16)
+                slot.append((torch.empty(M, N, dtype=torch.float16, device=dev), a, b.clone(), s.clone()))
+            self.slots.append(slot)
+        self.bytes_per_step = sum(w4_bytes(M, N, K, 128) for M in self.Ms)
+        self.flops_per_step = sum(2 * M * N * K for M in self.Ms)
+
+    def launches(self, step):
+        slot = self.slots[step % self.R]
+        return [lambda c=c, a=a, b=b, s=s: self.q.qgemm_w4(c, a, b, s, 128) for (c, a, b, s) in slot]
+
+    dtype = "f16"
+
+    def unit_bytes(self):
+        return self.bytes_per_step / len(self.Ms)
+
+    def unit_flops(self):
+        return self.flops_per_step / len(self.Ms)
+
+    def cpu_sample(self):
+        import oracle
+        for w in self.inputs:
+            oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size)
+        return self.flops_per_step, self.bytes_per_step, "full steps (M = 1, 4, 16)"
+
+    def describe(self):
+        return {"workload": self.name, "M": self.Ms, "N": self.N, "K": self.K, "group_size": self.gs,
+                "pack_factor": 8, "rotating_copies": self.R}
+
+
+class PrefillW4:
+    """Prefill-shaped W4A16: M=2048, K=4096, N=11008 (or N=4096 for the square shape)."""
+    kernel = "w4_prefill_kernel"
+    bound = "mfma"
+    dtype = "f16"
+
+    def __init__(self, torch, q, synth, square=False):
+        self.torch, self.q = torch, q
+        cfg = synth.W4_SQUARE_PREFILL if square else synth.W4_PREFILL
+        self.w = synth.w4_inputs(**cfg)
+        M, N, K = self.w.shape
+        self.M, self.N, self.K = M, N, K
+        self.name = f"w4a16_prefill_M{M}_N{N}_K{K}_gs128"
+        foot = w4_bytes(M, N, K, 128)
+        self.R = max(1, math.ceil(ROTATE_BYTES / foot))
+        dev = torch.device("cuda")
+        a = torch.from_numpy(self.w.a.view(np.int16)).to(dev).view(torch.float16)
+        b = torch.from_numpy(self.w.b.view(np.int32)).to(dev)
+        sc = torch.from_numpy(self.w.scales.view(np.int16)).to(dev).view(torch.float16)
+        self.slots = [(torch.empty(M, N, dtype=torch.float16, device=dev), a.clone(), b.clone(), sc.clone())
+                      for _ in range(self.R)]
+        self.bytes_per_step = foot
+        self.flops_per_step = 2 * M * N * K
+
+    def launches(self, step):
+        c, a, b, s = self.slots[step % self.R]
+        return [lambda: self.q.qgemm_w4(c, a, b, s, 128)]
+
+    def unit_bytes(self):
+        return self.bytes_per_step
+
+    def unit_flops(self):
+        return self.flops_per_step
+
+    def cpu_sample(self):
+        import oracle
+        rows = 256
+        oracle.qgemm_w4(self.w.a[:rows], self.w.b, self.w.scales, 128)
+        return 2 * rows * self.N * self.K, w4_bytes(rows, self.N, self.K, 128), f"{rows} of {self.M} rows"
+
+    def describe(self):
+        return {"workload": self.name, "M": self.M, "N": self.N, "K": self.K, "group_size": 128,
+                "pack_factor": 8, "rotating_copies": self.R}
+
+
+class GroupedBF16:
+    """64 experts, 4096 routed rows, K=2048, N=1408, 10% of groups skipped (seed 4)."""
+    kernel = "grouped_bf16_kernel"
+    bound = "hbm"
+    dtype = "bf16"
+
+    def __init__(self, torch, q, synth):
+        self.torch, self.q = torch, q
+        d = synth.grouped_inputs()
+        self.d = d
+        T, K = d.a.shape
+        E, N, _ = d.b.shape
+        self.T, self.K, self.N, self.E = T, K, N, E
+        off = d.a_offsets.astype(np.int64)
+        rows = off[1:] - off[:-1]
+        act = (d.expert_ids >= 0) & (rows > 0)
+        self.active_rows = int(rows[act].sum())
+        self.active_experts = len(set(d.expert_ids[act].tolist()))
+        self.bytes_per_step = (self.active_rows * K * 2 + self.active_experts * N * K * 2
+                               + self.active_rows * N * 2 + (E + 1) * 4 + E * 4)
+        self.flops_per_step = 2 * self.active_rows * N * K
+        self.R = max(1, math.ceil(ROTATE_BYTES / (d.b.nbytes + d.a.nbytes + T * N * 2)))
+        dev = torch.device("cuda")
+        a = torch.from_numpy(d.a.view(np.int16)).to(dev).view(torch.bfloat16)
+        b = torch.from_numpy(d.b.view(np.int16)).to(dev).view(torch.bfloat16)
+        off_t = torch.from_numpy(d.a_offsets.view(np.int32)).to(dev)
+        ids = torch.from_numpy(d.expert_ids).to(dev)
+        self.slots = [(torch.empty(T, N, dtype=torch.bfloat16, device=dev), a.clone(), off_t, b.clone() if r else b, ids)
+                      for r in range(self.R)]
+        self.usage = [int(v) for v in d.usage]
+        self.name = f"grouped_bf16_E{E}_T{T}_K{K}_N{N}_skip10pct"
+
+    def launches(self, step):
+        c, a, off, b, ids = self.slots[step % self.R]
+        return [lambda: self.q.grouped_gemm(c, a, off, b, ids, self.usage)]
+
+    def unit_bytes(self):
+        return self.bytes_per_step
+
+    def unit_flops(self):
+        return self.flops_per_step
+
+    def cpu_sample(self):
+        import oracle
+        d = self.d
+        G = 8
+        usage = np.array([d.usage[0], G], np.uint32)
+        c0 = np.zeros((self.T, self.N), np.uint16)
+        oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, usage)
+        off = d.a_offsets.astype(np.int64)
+        rows = sum(int(off[g + 1] - off[g]) for g in range(G) if d.expert_ids[g] >= 0)
+        ne = sum(1 for g in range(G) if d.expert_ids[g] >= 0)
+        byt = rows * self.K * 2 + ne * self.N * self.K * 2 + rows * self.N * 2
+        return 2 * rows * self.N * self.K, byt, f"first {G} of {self.E} groups"
+
+    def describe(self):
+        return {"workload": self.name, "experts": self.E, "routed_rows": self.T, "K": self.K, "N": self.N,
+                "active_rows": self.active_rows, "active_experts": self.active_experts, "transpose_b": True,
+                "rotating_copies": self.R}
+
+
+class KProjFP8:
+    """8 sequences (lengths U[1,1024], seed 5: T=4312), hidden 4096 bf16, W [4096,1024] e4m3 with 1x128x128
+    block scales, bf16 keys written into a paged cache (page 128, 2 layers, layer 1)."""
+    kernel = "kproj_fp8_paged_kernel"
+    bound = "mfma"
+    dtype = "bf16"
+
+    def __init__(self, torch, q, synth):
+        self.torch, self.q = torch, q
+        k = synth.kproj_inputs()
+        self.k = k
+        T, Kh = k.hidden.shape
+        N = k.weight.shape[1]
+        self.T, self.Kh, self.N = T, Kh, N
+        self.flops_per_step = 2 * T * Kh * N
+        self.bytes_per_step = (T * Kh * 2 + Kh * N + k.input_scale.nbytes + k.weight_scale.nbytes + T * N * 2
+                               + k.row_offsets.nbytes + k.cache_lengths.nbytes + k.page_table.nbytes)
+        foot = k.hidden.nbytes + k.weight.nbytes + k.blocks.nbytes + k.input_scale.nbytes
+        self.R = max(1, math.ceil(ROTATE_BYTES / foot))
+        dev = torch.device("cuda")
+        h = torch.from_numpy(k.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(k.weight).to(dev).view(torch.float8_e4m3fn)
+        isc = torch.from_numpy(k.input_scale).to(dev)
+        wsc = torch.from_numpy(k.weight_scale).to(dev)
+        blocks = torch.from_numpy(k.blocks.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.offs = torch.from_numpy(k.row_offsets.view(np.int32)).to(dev)
+        self.cl = torch.from_numpy(k.cache_lengths.view(np.int32)).to(dev)
+        self.pt = torch.from_numpy(k.page_table.view(np.int32)).to(dev)
+        self.slots = [(h.clone(), w.clone(), isc.clone(), wsc.clone(), blocks.clone()) for _ in range(self.R)]
+        self.name = f"kproj_fp8_paged_T{T}_K{Kh}_N{N}_page128"
+
+    def launches(self, step):
+        h, w, isc, wsc, blocks = self.slots[step % self.R]
+        k = self.k
+        return [lambda: self.q.k_matmul_ragged_paged_scale(h, self.offs, w, isc, wsc, blocks, self.cl, self.pt,
+                                                           k.layer_idx)]
+
+    def unit_bytes(self):
+        return self.bytes_per_step
+
+    def unit_flops(self):
+        return self.flops_per_step
+
+    def cpu_sample(self):
+        import oracle
+        k = self.k
+        rows = 512
+        oracle.kproj_rows(k.hidden[:rows], k.weight, k.input_scale[:rows], k.weight_scale)
+        return 2 * rows * self.Kh * self.N, rows * self.Kh * 2 + self.Kh * self.N + rows * self.N * 2, \
+            f"{rows} of {self.T} token rows (matmul + rounding; placement excluded)"
+
+    def describe(self):
+        k = self.k
+        return {"workload": self.name, "tokens": self.T, "batch": len(k.row_offsets) - 1, "hidden": self.Kh,
+                "N": self.N, "page_size": int(k.blocks.shape[3]), "layers": int(k.blocks.shape[0]),
+                "layer_idx": k.layer_idx, "granularity_mnk": [1, 128, 128], "rotating_copies": self.R}
+
+
+WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
+             "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
+             "grouped": GroupedBF16, "kproj": KProjFP8}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import grouped_gemm_qgemm_amd as q
+    import synth
+    q.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.config](torch, q, synth)
+
+    for i in range(args.warmup):
+        for f in wl.launches(i):
+            f()
+    torch.cuda.synchronize()
+
+    # The K steps are captured once into a HIP graph so the GPU runs the kernels
+    # back to back; from Python each launch costs more than the kernel itself.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            for f in wl.launches(i):
+                f()
+    torch.cuda.synchronize()
+    graph.replay()                      # warm replay
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, events on the stream the graph runs on
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = event_time_ms(torch, graph.replay, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ms / args.steps
+    n_launch = len(wl.launches(0))
+    avg_launch_ms = ms / (args.steps * n_launch)
+
+    gbs = wl.bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    tflops = wl.flops_per_step / (ms_per_step * 1e-3) / 1e12
+    if wl.bound == "hbm":
+        value, unit = gbs, "GB/s"
+        achieved, peak, runit = wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        value, unit = tflops, "TFLOP/s"
+        achieved, peak, runit = wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12, F16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    out = {
+        "metric": "W4A16 GEMM TFLOP/s + HBM GB/s (% roofline) at M=1..16 and M=2048, N=K=4096",
+        "value": round(value, 3), "unit": unit,
+        "gbs": round(gbs, 2), "tflops": round(tflops, 3),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": wl.describe(),
+        "roofline": {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": runit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": wl.kernel, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": wl.unit_bytes(),
+                     "algorithmic_flops_per_launch": wl.unit_flops()},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        n = 0
+        fl = by = 0
+        while True:
+            f, b, what = wl.cpu_sample()
+            fl += f
+            by += b
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        cv = by / dt / 1e9 if wl.bound == "hbm" else fl / dt / 1e12
+        out["cpu_baseline"] = {"value": round(cv, 6), "unit": unit, "cores": cpu_cores(), "kind": "oracle",
+                               "sample": f"{n} x ({what}) of the same workload, fp64 numpy oracle, {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+"""Python binding of libqgemm.so (the gfx950 dequant-in-kernel GEMM library).
+
+Argument marshalling only: tensors are described to the C ABI in
+include/qgemm.h (qg_tensor: pointer, dtype, rank, shape) and every step of the
+computation runs in the library's HIP kernels. Torch tensors supply device
+memory and the stream; nothing here computes a result. If the library is not
+built, load() raises: there is no fallback path.
+
+Entry points (same names as the C ABI):
+    qgemm_w4(c, a, b_packed, scales, group_size=128, pack_factor=8)
+    grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
+    k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
+                                weight_scale, kv_blocks, cache_lengths, page_table,
+                                layer_idx, scales_granularity_mnk=(1, 128, 128))
+Each returns None on success and raises QgError carrying the status otherwise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["load", "QgError", "qgemm_w4", "grouped_gemm", "k_matmul_ragged_paged_scale",
+           "status_string", "LIB_PATH", "QG"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
+
+
+class QG:
+    OK, ERR_NULL, ERR_RANK, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_INVALID_ARG, ERR_LAUNCH = range(9)
+    F16, BF16, F32, FP8_E4M3, U32, I32 = range(6)
+
+
+MAX_RANK = 6
+
+
+class QgTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("rank", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * MAX_RANK)]
+
+
+class QgPagedKV(ctypes.Structure):
+    _fields_ = [("blocks", QgTensor), ("cache_lengths", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int64)]
+
+
+class QgError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"qgemm status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_TORCH_TO_QG = {
+    torch.float16: QG.F16, torch.bfloat16: QG.BF16, torch.float32: QG.F32,
+    torch.float8_e4m3fn: QG.FP8_E4M3, torch.uint32: QG.U32, torch.int32: QG.I32,
+}
+
+
+def load(path: str | None = None):
+    """Load the built library (raises if it is missing; build with __graft_entry__.build())."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run python -m grouped_gemm_qgemm_amd.build")
+    lib = ctypes.CDLL(p)
+    T = ctypes.POINTER(QgTensor)
+    lib.qgemm_w4.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.qgemm_w4.restype = ctypes.c_int
+    lib.grouped_gemm.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                 ctypes.c_void_p]
+    lib.grouped_gemm.restype = ctypes.c_int
+    lib.k_matmul_ragged_paged_scale.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(QgPagedKV), ctypes.c_uint32, ctypes.c_void_p]
+    lib.k_matmul_ragged_paged_scale.restype = ctypes.c_int
+    lib.qg_status_string.argtypes = [ctypes.c_int]
+    lib.qg_status_string.restype = ctypes.c_char_p
+    lib.qg_version.argtypes = []
+    lib.qg_version.restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(s: int) -> str:
+    return load().qg_status_string(s).decode()
+
+
+def describe(t, dtype: int | None = None) -> QgTensor:
+    """qg_tensor for a contiguous torch tensor (or None -> a NULL-data rank-0 record)."""
+    d = QgTensor()
+    if t is None:
+        d.data = None
+        d.dtype = dtype if dtype is not None else 0
+        d.rank = 0
+        return d
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    if t.dim() > MAX_RANK:
+        raise ValueError("rank above 6")
+    d.data = t.data_ptr() if t.numel() > 0 else (t.data_ptr() or None)
+    d.dtype = dtype if dtype is not None else _TORCH_TO_QG.get(t.dtype, -1)
+    d.rank = t.dim()
+    for i, s in enumerate(t.shape):
+        d.shape[i] = s
+    return d
+
+
+def _u32(t):
+    """Tables of uint32 may be held in int32 or uint32 tensors."""
+    return QG.U32 if t is not None and t.dtype in (torch.int32, torch.uint32) else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(st: int):
+    if st != QG.OK:
+        raise QgError(st, status_string(st))
+
+
+def qgemm_w4(c, a, b_packed, scales, group_size: int = 128, pack_factor: int = 8, stream=None,
+             raise_on_error: bool = True) -> int:
+    """C[M,N] (f16) = A[M,K] (f16) . dequant(B[K/8,N] u32, scales[K/gs,N] f16)."""
+    lib = load()
+    st = lib.qgemm_w4(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                      ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
+                      group_size, pack_factor, _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b: bool = True,
+                 stream=None, raise_on_error: bool = True) -> int:
+    """Rows of each active, non-skipped group g: C = A . B[expert_ids[g]]^T (bf16)."""
+    lib = load()
+    usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
+    st = lib.grouped_gemm(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                          ctypes.byref(describe(a_offsets, _u32(a_offsets))), ctypes.byref(describe(b)),
+                          ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)),
+                          _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale, weight_scale,
+                                kv_blocks, cache_lengths, page_table, layer_idx: int,
+                                scales_granularity_mnk=(1, 128, 128), stream=None,
+                                raise_on_error: bool = True) -> int:
+    """K rows = (hidden * input_scale) . (weight * weight_scale), written into the key
+    plane of layer `layer_idx` of the paged cache `kv_blocks` [L, 2, P, S, Hkv, D]."""
+    lib = load()
+    gran = (ctypes.c_int32 * 3)(*[int(v) for v in scales_granularity_mnk])
+    kv = QgPagedKV()
+    kv.blocks = describe(kv_blocks)
+    kv.cache_lengths = cache_lengths.data_ptr() if cache_lengths is not None else None
+    kv.page_table = page_table.data_ptr() if page_table is not None else None
+    kv.max_pages_per_seq = page_table.shape[1] if page_table is not None and page_table.dim() == 2 else 0
+    st = lib.k_matmul_ragged_paged_scale(
+        ctypes.byref(describe(hidden)), ctypes.byref(describe(input_row_offsets, _u32(input_row_offsets))),
+        ctypes.byref(describe(weight)), ctypes.byref(describe(input_scale)),
+        ctypes.byref(describe(weight_scale)), gran, ctypes.byref(kv), int(layer_idx), _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st

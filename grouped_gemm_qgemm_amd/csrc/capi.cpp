@@ -1,0 +1,199 @@
+// C ABI entry points: host-side argument checks, kernel-variant choice and
+// launch. Every check runs before the first HIP call, so a rejected call
+// enqueues nothing and touches no output.
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qgemm.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qg_status check_tensor(const qg_tensor* t, int rank, qg_dtype dt) {
+  if (!t) return QG_ERR_NULL;
+  if (t->rank != rank) return QG_ERR_RANK;
+  if (t->dtype != dt) return QG_ERR_DTYPE;
+  int64_t n = 1;
+  for (int i = 0; i < rank; ++i) {
+    if (t->shape[i] < 0) return QG_ERR_SHAPE;
+    n *= t->shape[i];
+  }
+  if (n > 0) {
+    if (!t->data) return QG_ERR_NULL;
+    if (!aligned16(t->data)) return QG_ERR_ALIGN;
+  }
+  return QG_OK;
+}
+
+// Optional variant override for tuning sweeps: QG_<NAME>_VARIANT=<int>.
+int env_variant(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+int device_cus() {
+  static int cache[kMaxDevices] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+qg_status launch_status(hipError_t e) {
+  if (e == hipErrorNotSupported) return QG_ERR_UNSUPPORTED;
+  return e == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qg_status_string(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL";
+    case QG_ERR_RANK: return "a tensor has the wrong rank";
+    case QG_ERR_DTYPE: return "a tensor has the wrong dtype";
+    case QG_ERR_SHAPE: return "tensor shapes are inconsistent";
+    case QG_ERR_ALIGN: return "a base pointer or row length is not 16-byte aligned";
+    case QG_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case QG_ERR_INVALID_ARG: return "a scalar argument is out of range";
+    case QG_ERR_LAUNCH: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t qg_version(void) { return 100; }
+
+qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                   const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                   hipStream_t stream) {
+  if (!c || !a || !b_packed || !scales) return QG_ERR_NULL;
+  // rank-2 requirement first: the page's only stated error condition
+  if (c->rank != 2 || a->rank != 2 || b_packed->rank != 2 || scales->rank != 2) return QG_ERR_RANK;
+  qg_status st;
+  if ((st = check_tensor(c, 2, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(a, 2, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(b_packed, 2, QG_U32)) != QG_OK) return st;
+  if ((st = check_tensor(scales, 2, QG_F16)) != QG_OK) return st;
+  if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
+  if (group_size <= 0) return QG_ERR_INVALID_ARG;
+  const int64_t M = a->shape[0], K = a->shape[1], N = c->shape[1];
+  if (c->shape[0] != M) return QG_ERR_SHAPE;
+  if (K % group_size != 0) return QG_ERR_SHAPE;
+  if (b_packed->shape[0] * pack_factor != K || b_packed->shape[1] != N) return QG_ERR_SHAPE;
+  if (scales->shape[0] != K / group_size || scales->shape[1] != N) return QG_ERR_SHAPE;
+  if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
+    return QG_ERR_UNSUPPORTED;
+  if (N % 8 != 0) return QG_ERR_ALIGN;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return QG_OK;
+  if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of C
+  qg::W4Args p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
+               static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
+               M, N, K, group_size};
+  if (M <= 16) {
+    return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 0), stream));
+  }
+  return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", 0), stream));
+}
+
+qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                       const qg_tensor* b, const qg_tensor* expert_ids,
+                       const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                       hipStream_t stream) {
+  if (!c || !a || !a_offsets || !b || !expert_ids || !expert_usage_stats_host) return QG_ERR_NULL;
+  if (c->rank != 2 || a->rank != 2 || a_offsets->rank != 1 || b->rank != 3 || expert_ids->rank != 1)
+    return QG_ERR_RANK;
+  qg_status st;
+  if ((st = check_tensor(c, 2, QG_BF16)) != QG_OK) return st;
+  if ((st = check_tensor(a, 2, QG_BF16)) != QG_OK) return st;
+  if ((st = check_tensor(a_offsets, 1, QG_U32)) != QG_OK) return st;
+  if ((st = check_tensor(b, 3, QG_BF16)) != QG_OK) return st;
+  if ((st = check_tensor(expert_ids, 1, QG_I32)) != QG_OK) return st;
+  const int64_t T = a->shape[0], K = a->shape[1];
+  const int64_t E = b->shape[0];
+  const int64_t N = transpose_b ? b->shape[1] : b->shape[2];
+  const int64_t Kb = transpose_b ? b->shape[2] : b->shape[1];
+  const int64_t G = expert_ids->shape[0];
+  if (c->shape[0] != T || c->shape[1] != N || Kb != K) return QG_ERR_SHAPE;
+  if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
+  const uint32_t num_active = expert_usage_stats_host[1];
+  if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
+  if (!transpose_b) return QG_ERR_UNSUPPORTED;
+  if (K % 8 != 0 || N % 8 != 0) return QG_ERR_ALIGN;
+  if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (num_active == 0 || T == 0 || N == 0 || E == 0) return QG_OK;
+  if (K == 0) return QG_ERR_UNSUPPORTED;
+  qg::GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
+                    static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
+                    static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
+                    (int)expert_usage_stats_host[0], device_cus()};
+  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", 0), stream));
+}
+
+qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                                      const qg_tensor* weight, const qg_tensor* input_scale,
+                                      const qg_tensor* weight_scale,
+                                      const int32_t* scales_granularity_mnk,
+                                      const qg_paged_kv* kv, uint32_t layer_idx,
+                                      hipStream_t stream) {
+  if (!hidden || !input_row_offsets || !weight || !input_scale || !weight_scale ||
+      !scales_granularity_mnk || !kv)
+    return QG_ERR_NULL;
+  if (hidden->rank != 2 || input_row_offsets->rank != 1 || weight->rank != 2 || input_scale->rank != 2 ||
+      weight_scale->rank != 2 || kv->blocks.rank != 6)
+    return QG_ERR_RANK;
+  qg_status st;
+  if ((st = check_tensor(hidden, 2, QG_BF16)) != QG_OK) return st;
+  if ((st = check_tensor(input_row_offsets, 1, QG_U32)) != QG_OK) return st;
+  if ((st = check_tensor(weight, 2, QG_FP8_E4M3)) != QG_OK) return st;
+  if ((st = check_tensor(input_scale, 2, QG_F32)) != QG_OK) return st;
+  if ((st = check_tensor(weight_scale, 2, QG_F32)) != QG_OK) return st;
+  if ((st = check_tensor(&kv->blocks, 6, QG_BF16)) != QG_OK) return st;
+  if (scales_granularity_mnk[0] != 1 || scales_granularity_mnk[1] != 128 || scales_granularity_mnk[2] != 128)
+    return QG_ERR_UNSUPPORTED;
+  const int64_t T = hidden->shape[0], Kh = hidden->shape[1];
+  const int64_t N = weight->shape[1];
+  const int64_t B = input_row_offsets->shape[0] - 1;
+  const int64_t* bs = kv->blocks.shape;
+  const int64_t L = bs[0], P = bs[2], S = bs[3], Hkv = bs[4], D = bs[5];
+  if (B < 0) return QG_ERR_SHAPE;
+  if (weight->shape[0] != Kh) return QG_ERR_SHAPE;
+  if (Kh % 128 != 0 || N % 128 != 0) return QG_ERR_SHAPE;
+  if (input_scale->shape[0] != T || input_scale->shape[1] != Kh / 128) return QG_ERR_SHAPE;
+  if (weight_scale->shape[0] != Kh / 128 || weight_scale->shape[1] != N / 128) return QG_ERR_SHAPE;
+  if (bs[1] != 2 || Hkv * D != N) return QG_ERR_SHAPE;
+  if ((int64_t)layer_idx >= L) return QG_ERR_INVALID_ARG;
+  if (kv->max_pages_per_seq <= 0 && T > 0) return QG_ERR_INVALID_ARG;
+  if (B > 0 && T > 0 && (!kv->cache_lengths || !kv->page_table)) return QG_ERR_NULL;
+  if (T > INT32_MAX / 2 || Kh > INT32_MAX / 2 || N > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (T == 0 || B == 0 || N == 0) return QG_OK;
+  if (Kh == 0) return QG_ERR_UNSUPPORTED;
+  qg::KProjArgs p{static_cast<const uint16_t*>(hidden->data),
+                  static_cast<const uint32_t*>(input_row_offsets->data),
+                  static_cast<const uint8_t*>(weight->data),
+                  static_cast<const float*>(input_scale->data),
+                  static_cast<const float*>(weight_scale->data),
+                  static_cast<uint16_t*>(kv->blocks.data),
+                  kv->cache_lengths, kv->page_table,
+                  T, Kh, N, B, kv->max_pages_per_seq, L, P, S, layer_idx, device_cus()};
+  return launch_status(qg::launch_kproj_fp8(p, env_variant("QG_KPROJ_VARIANT", 0), stream));
+}
+
+}  // extern "C"

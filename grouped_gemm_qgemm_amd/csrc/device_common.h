@@ -1,0 +1,88 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// MFMA wrappers, 4-bit dequantization and fp8 decoding in registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// v_mfma_f32_16x16x32_f16: D[16x16] += A[16x32] . B[32x16].
+// Lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16]; it holds
+// D[4*(l/16) + i][l%16] for i = 0..3. Any permutation of the 8 K slots is fine as
+// long as A and B use the same one.
+__device__ __forceinline__ float4_t mfma16x16x32_f16(u32x4_t a, u32x4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma16x16x32_bf16(u32x4_t a, u32x4_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
+// weights (q - 8), exact, as four packed half pairs in the K-slot order
+// (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of
+// 1024.0 (0x6400) gives 1024 + q exactly; subtracting 1032 leaves q - 8.
+__device__ __forceinline__ u32x4_t dequant_w4_word(uint32_t w) {
+  const uint32_t m = 0x000F000Fu, bias = 0x64006400u;
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  uint32_t p0 = (w & m) | bias;
+  uint32_t p1 = ((w >> 4) & m) | bias;
+  uint32_t p2 = ((w >> 8) & m) | bias;
+  uint32_t p3 = ((w >> 12) & m) | bias;
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p0) - off);
+  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p1) - off);
+  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p2) - off);
+  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p3) - off);
+  return r;
+}
+
+// Eight consecutive fp16 values (a0..a7 in four registers) reordered to the
+// K-slot order used by dequant_w4_word: (a0,a4), (a1,a5), (a2,a6), (a3,a7).
+__device__ __forceinline__ u32x4_t permute_k_0415(u32x4_t v) {
+  u32x4_t r;
+  r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return r;
+}
+
+// Packed fp16 multiply of a register pair by s. Vector lanes are always read
+// into scalars first: bit-casting an element of a vector that is being
+// reassigned in place (v.y = bit_cast(..., v.y) ...) is miscompiled by this
+// toolchain (later lanes pick up the already updated first lane).
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, half2_t s) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) * s);
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f2h_rn(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f2bf_rn(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace qg

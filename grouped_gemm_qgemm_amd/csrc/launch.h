@@ -1,0 +1,56 @@
+// Internal launcher interface between the C ABI layer (capi.cpp) and the
+// kernels. Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+struct W4Args {
+  uint16_t* C;          // f16 [M, N]
+  const uint16_t* A;    // f16 [M, K]
+  const uint32_t* B;    // u32 [K/8, N]
+  const uint16_t* S;    // f16 [K/group_size, N]
+  int64_t M, N, K;
+  int group_size;
+};
+
+struct GroupedArgs {
+  uint16_t* C;              // bf16 [T, N]
+  const uint16_t* A;        // bf16 [T, K]
+  const uint32_t* a_offsets;  // [G+1]
+  const uint16_t* B;        // bf16 [E, N, K]
+  const int32_t* expert_ids;  // [G]
+  int64_t T, N, K, E;
+  int num_active;
+  int max_rows_hint;
+  int num_cus;
+};
+
+struct KProjArgs {
+  const uint16_t* hidden;        // bf16 [T, Kh]
+  const uint32_t* row_offsets;   // [B+1]
+  const uint8_t* weight;         // e4m3 [Kh, N]
+  const float* input_scale;      // [T, Kh/128]
+  const float* weight_scale;     // [Kh/128, N/128]
+  uint16_t* blocks;              // bf16 [L, 2, P, S, Hkv, D]
+  const uint32_t* cache_lengths; // [B]
+  const uint32_t* page_table;    // [B, max_pages]
+  int64_t T, Kh, N, batch, max_pages;
+  int64_t num_layers, num_pages, page_size;
+  uint32_t layer_idx;
+  int num_cus;
+};
+
+// Decode-shaped W4A16 (M <= 16). `variant` picks columns-per-lane and waves.
+hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream);
+
+// Prefill-shaped W4A16 (M > 16).
+hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream);
+
+hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream);
+
+hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream);
+
+}  // namespace qg

@@ -1,0 +1,230 @@
+// MFMA-tiled W4A16 GEMM for M > 16 (the prefill-shaped case of the group-
+// quantized GEMM on the Modular page "multistage_gemm_q"; Parameters:
+// group_size, pack_factor; its Description's multi-stage shared-memory
+// pipeline becomes an LDS double buffer here).
+//
+// Workgroup tile BM x BN, K advanced BK = 64 at a time:
+//   * A (fp16) and the packed B words of the next K tile are fetched from HBM
+//     into registers while the current tile is multiplied out of LDS, then
+//     written to the other LDS buffer (one barrier per K tile).
+//   * A rows sit in LDS with an XOR swizzle on their 16-byte chunks so the
+//     MFMA operand reads of 16 consecutive rows hit distinct banks; the eight
+//     fp16 values of each chunk are stored in the K-slot order (0,4,1,5,2,6,3,7)
+//     that the in-register 4-bit unpack produces for B.
+//   * Each wave reads 16 bytes of packed B per lane per 32-deep K step: four
+//     words = four MFMA column tiles (lane j of tile t is column 4j + t), so its
+//     fp16 results for one row come out as four adjacent columns.
+//   * Dequantization happens once per wave per word, in VGPRs: nibble -> fp16
+//     (q - 8) exactly, then one packed multiply by the column's group scale.
+//   * 16x16x32 fp16 MFMA, fp32 accumulation, fp16 round-to-nearest-even store.
+//   * Workgroup ids are remapped so each XCD works on a contiguous run of tiles,
+//     M-fastest, sharing B panels (and A panels) in its own L2.
+#include "device_common.h"
+#include "launch.h"
+
+namespace qg {
+
+namespace {
+
+constexpr int BK = 64;            // K per LDS stage (two 32-deep MFMA steps)
+constexpr int CHUNKS = BK / 8;    // 16-byte chunks per A row in LDS
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+
+}  // namespace
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
+  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
+  constexpr int TM = BM / WAVES_M;       // rows per wave
+  constexpr int TN = BN / WAVES_N;       // columns per wave
+  constexpr int MT = TM / 16;            // MFMA row tiles per wave
+  constexpr int NB = TN / 64;            // 64-column blocks per wave (4 MFMA column tiles each)
+  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
+  constexpr int A_CHUNKS = BM * CHUNKS;              // 16-byte chunks of A per stage
+  constexpr int A_PER_T = A_CHUNKS / NTHR;
+  static_assert(A_CHUNKS % NTHR == 0, "A chunks per thread");
+  constexpr int B_CHUNKS = (BK / 8) * (BN / 4);      // 16-byte chunks of packed B per stage
+  constexpr int B_PER_T = B_CHUNKS >= NTHR ? B_CHUNKS / NTHR : 1;
+  static_assert(B_CHUNKS % NTHR == 0 || NTHR % B_CHUNKS == 0, "B chunks per thread");
+
+  __shared__ __attribute__((aligned(16))) uint32_t lds_a[2][BM * BK / 2];     // fp16 pairs
+  __shared__ __attribute__((aligned(16))) uint32_t lds_b[2][(BK / 8) * BN];   // packed words
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous
+  // range of the M-fastest linear tile order.
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin % tiles_m) * BM;
+  const int n0 = (lin / tiles_m) * BN;
+
+  // ---- global -> register staging (addresses clamped into range) ----
+  int a_row[A_PER_T], a_chunk[A_PER_T];
+  const uint16_t* a_src[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    a_row[i] = id / CHUNKS;
+    a_chunk[i] = id % CHUNKS;
+    const int gr = min(m0 + a_row[i], M - 1);
+    a_src[i] = A + (size_t)gr * K + a_chunk[i] * 8;
+  }
+  const bool b_loader = tid < B_CHUNKS;
+  int b_kp[B_PER_T], b_c4[B_PER_T], b_col[B_PER_T];
+#pragma unroll
+  for (int i = 0; i < B_PER_T; ++i) {
+    const int id = (tid + i * NTHR) % B_CHUNKS;
+    b_kp[i] = id / (BN / 4);
+    b_c4[i] = id % (BN / 4);
+    b_col[i] = min(n0 + 4 * b_c4[i], N - 4);
+  }
+  const int kp_total = K / 8;
+
+  // this lane's scale columns: 4 adjacent columns per 64-column block
+  int s_col[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) s_col[nb] = min(n0 + wn * TN + nb * 64 + 4 * (lane & 15), N - 4);
+
+  u32x4_t ra[A_PER_T];
+  u32x4_t rb[B_PER_T];
+
+  auto load_stage = [&](int kt, u32x2_t (&sc)[2][NB]) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int kk = min(k0 + a_chunk[i] * 8, K - 8) - a_chunk[i] * 8;
+      ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kk);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) {
+      const int kp = min(k0 / 8 + b_kp[i], kp_total - 1);
+      rb[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)kp * N + b_col[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int g = min(k0 + 32 * s, K - 1) / group_size;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[s][nb] = *reinterpret_cast<const u32x2_t*>(S + (size_t)g * N + s_col[nb]);
+    }
+  };
+
+  auto store_stage = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      u32x4_t v = permute_k_0415(ra[i]);
+      if (k0 + a_chunk[i] * 8 >= K) v = u32x4_t{0u, 0u, 0u, 0u};  // K tail
+      *reinterpret_cast<u32x4_t*>(&lds_a[buf][(a_row[i] * CHUNKS + swz(a_row[i], a_chunk[i])) * 4]) = v;
+    }
+    if (b_loader) {
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<u32x4_t*>(&lds_b[buf][b_kp[i] * BN + 4 * b_c4[i]]) = rb[i];
+    }
+  };
+
+  float4_t acc[MT][NB * 4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NB * 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + BK - 1) / BK;
+  u32x2_t sc_cur[2][NB], sc_nxt[2][NB];
+  load_stage(0, sc_cur);
+  store_stage(0, 0);
+  __syncthreads();
+
+  const int q = lane >> 4;      // K slot group within a 32-deep step
+  const int r16 = lane & 15;    // row / column index within an MFMA tile
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load_stage(kt + 1, sc_nxt);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // B: 16 bytes per lane per 64-column block -> 4 column tiles
+      u32x4_t bq[NB * 4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(
+            &lds_b[cur][(s * 4 + q) * BN + wn * TN + nb * 64 + 4 * r16]);
+        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
+        const uint32_t sp[2] = {sc_cur[s][nb].x, sc_cur[s][nb].y};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t sh = (sp[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+          const half2_t s2 = __builtin_bit_cast(half2_t, sh | (sh << 16));
+          const u32x4_t d = dequant_w4_word(words[t]);
+          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+          bq[nb * 4 + t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * TM + mt * 16 + r16;
+        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
+            &lds_a[cur][(row * CHUNKS + swz(row, s * 4 + q)) * 4]);
+#pragma unroll
+        for (int j = 0; j < NB * 4; ++j) acc[mt][j] = mfma16x16x32_f16(av, bq[j], acc[mt][j]);
+      }
+    }
+    if (more) store_stage(kt + 1, cur ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
+  }
+
+  // ---- epilogue: fp32 -> fp16 (RNE), four adjacent columns per 8-byte store ----
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
+        if (col >= N) continue;
+        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
+        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
+        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
+  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
+  const int tiles = tm * tn;
+  const int grid = ((tiles + 7) / 8) * 8;
+  hipLaunchKernelGGL((w4_prefill_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
+                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
+  return hipGetLastError();
+}
+
+// Variants: tile shapes (BM x BN, wave grid).
+hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
+  switch (variant) {
+    case 0: return launch_tile<256, 128, 2, 2>(p, stream);
+    case 1: return launch_tile<128, 128, 2, 2>(p, stream);
+    case 2: return launch_tile<128, 256, 2, 2>(p, stream);
+    case 3: return launch_tile<64, 128, 1, 2>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace qg

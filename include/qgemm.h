@@ -1,0 +1,180 @@
+/*
+ * qgemm.h - C ABI of the MI355X (gfx950) dequant-in-kernel GEMM library.
+ *
+ * Three operations, each a GEMM whose B operand holds low-precision weights
+ * that the kernel dequantizes on the fly:
+ *
+ *   qgemm_w4                     4-bit group-quantized weights, fp16 activations
+ *                                (Modular MAX page "multistage_gemm_q")
+ *   grouped_gemm                 per-expert bf16 GEMM routed by row offsets
+ *                                (Modular MAX page "grouped_matmul_sm100_persistent")
+ *   k_matmul_ragged_paged_scale  block-scaled fp8 weights, ragged rows, output
+ *                                written into a paged KV cache
+ *                                (Modular MAX page "k_matmul_ragged_paged_scale")
+ *
+ * Conventions shared by every entry point
+ *   - Tensor data pointers are DEVICE pointers unless a comment says "host".
+ *     Every tensor is dense, row-major (last dimension contiguous), and its base
+ *     address must be 16-byte aligned.
+ *   - The caller allocates and owns every buffer. The library never allocates or
+ *     frees device memory and keeps no pointer after the call returns.
+ *   - All argument checks run on the host before anything is enqueued. On any
+ *     error nothing is launched and every output is left untouched; the return
+ *     value says what was wrong (qg_status_string gives a message).
+ *   - Work is enqueued on `stream` and the call returns without synchronizing.
+ *     Empty problems (a zero-sized M, T, N or no active group) are a successful
+ *     no-op that enqueues nothing.
+ *   - Outputs must not alias inputs. Calls on different streams may run
+ *     concurrently; the library holds no mutable global state besides a cache of
+ *     device properties.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QG_OK = 0,
+  QG_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  QG_ERR_RANK = 2,         /* a tensor has the wrong number of dimensions         */
+  QG_ERR_DTYPE = 3,        /* a tensor has the wrong element type                 */
+  QG_ERR_SHAPE = 4,        /* dimensions disagree with each other                 */
+  QG_ERR_ALIGN = 5,        /* base pointer or a row length breaks 16-byte alignment */
+  QG_ERR_UNSUPPORTED = 6,  /* a valid configuration this build does not implement */
+  QG_ERR_INVALID_ARG = 7,  /* a scalar argument is out of range                   */
+  QG_ERR_LAUNCH = 8        /* the HIP runtime reported an error at launch         */
+} qg_status;
+
+typedef enum {
+  QG_F16 = 0,       /* IEEE binary16                               */
+  QG_BF16 = 1,      /* bfloat16                                    */
+  QG_F32 = 2,       /* IEEE binary32                               */
+  QG_FP8_E4M3 = 3,  /* OCP FP8 E4M3 ("fn": max 448, no infinities) */
+  QG_U32 = 4,
+  QG_I32 = 5
+} qg_dtype;
+
+#define QG_MAX_RANK 6
+
+/* A dense row-major tensor: `rank` dimensions in shape[0..rank-1]. */
+typedef struct {
+  void* data;
+  qg_dtype dtype;
+  int32_t rank;
+  int64_t shape[QG_MAX_RANK];
+} qg_tensor;
+
+/*
+ * qgemm_w4 - C = A . dequant(B)   (W4A16 group-quantized GEMM)
+ *
+ * Follows "multistage_gemm_q": group_size K elements share one scale
+ * (Parameters: group_size); pack_factor 4-bit codes sit in one uint32
+ * (Parameters: pack_factor); tensors that are not rank-2 are an error (Raises).
+ * Code layout and zero point, which the page leaves open, are fixed here:
+ * word B[kp][n] holds the codes of K rows 8*kp + i (i = 0..7) in bits
+ * 4i..4i+3, and code q stands for the weight (q - 8) * scales[k / group_size][n].
+ *
+ *   c        f16 [M, N]                      output, written entirely
+ *   a        f16 [M, K]                      activations
+ *   b_packed u32 [K / pack_factor, N]        packed 4-bit weight codes
+ *   scales   f16 [K / group_size, N]         one scale per group per column
+ *   group_size   multiple of 32, divides K   (QG_ERR_SHAPE / QG_ERR_UNSUPPORTED)
+ *   pack_factor  must be 8                   (QG_ERR_UNSUPPORTED otherwise)
+ *
+ * Accumulation is fp32; the result is rounded to fp16 (nearest-even).
+ * N must be a multiple of 8 and K a multiple of group_size (QG_ERR_ALIGN /
+ * QG_ERR_SHAPE). M <= 16 runs the skinny-M (decode) kernel, larger M the
+ * MFMA-tiled (prefill) kernel.
+ */
+qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                   const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                   hipStream_t stream);
+
+/*
+ * grouped_gemm - per-group GEMM over routed rows (MoE expert GEMM)
+ *
+ * Follows "grouped_matmul_sm100_persistent" (Args): a_offsets is the per-expert
+ * prefix sum of A row offsets; expert_ids gives each group's expert, negative
+ * entries skip the group; expert_usage_stats[1] is the active count; transpose_b
+ * (Parameters) says each expert matrix is stored [N, K].
+ *
+ *   c          bf16 [T, N]   output; for g < num_active with expert_ids[g] >= 0,
+ *                            rows a_offsets[g] .. a_offsets[g+1]-1 are set to
+ *                            A[rows] . B[expert_ids[g]]^T; all other rows keep
+ *                            their prior content
+ *   a          bf16 [T, K]
+ *   a_offsets  u32  [G + 1]  non-decreasing, a_offsets[num_active] <= T
+ *   b          bf16 [E, N, K] when transpose_b != 0, else [E, K, N]
+ *   expert_ids i32  [G]      each < E, or negative to skip
+ *   expert_usage_stats_host  HOST u32[2]: [1] = num_active (<= G) groups to
+ *                            process; [0] = largest rows-per-group (a hint only)
+ *
+ * K and N must be multiples of 8 (QG_ERR_ALIGN). Accumulation is fp32; results are
+ * rounded to bf16 (nearest-even). The device-side tables are not re-validated:
+ * offsets past T, or expert ids >= E, are undefined behaviour.
+ * transpose_b == 0 returns QG_ERR_UNSUPPORTED.
+ */
+qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                       const qg_tensor* b, const qg_tensor* expert_ids,
+                       const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                       hipStream_t stream);
+
+/* A paged KV cache collection (keys and values of every layer). */
+typedef struct {
+  qg_tensor blocks;                /* bf16 [L, 2, P, S, Hkv, D]: layer, K/V plane (0 = keys),
+                                      physical page, slot in page, kv head, head dim     */
+  const uint32_t* cache_lengths;   /* device u32 [B]: tokens already cached per sequence  */
+  const uint32_t* page_table;      /* device u32 [B, max_pages_per_seq]: physical page ids */
+  int64_t max_pages_per_seq;
+} qg_paged_kv;
+
+/*
+ * k_matmul_ragged_paged_scale - K = (hidden * input_scale) . (weight * weight_scale),
+ * written into the key plane of layer `layer_idx` of a paged KV cache.
+ *
+ * Follows "k_matmul_ragged_paged_scale" (Args): hidden_state is
+ * (sum(seq_lens), num_heads*head_size); input_row_offsets (batch+1) marks where
+ * each sequence starts; weight is (num_heads*head_size, num_kv_heads*head_size);
+ * input_scale / weight_scale multiply the input / the weight; the layer's cache is
+ * chosen by layer_idx (Parameters: scales_granularity_mnk gives the scale blocks).
+ *
+ *   hidden            bf16 [T, Kh]
+ *   input_row_offsets u32  [B + 1]   offs[0] = 0, non-decreasing, offs[B] = T
+ *   weight            fp8 e4m3 [Kh, N], N = Hkv * D
+ *   input_scale       f32  [T, Kh / 128]
+ *   weight_scale      f32  [Kh / 128, N / 128]
+ *   scales_granularity_mnk  HOST int32[3], must be {1, 128, 128}
+ *   kv                paged cache; token j of sequence b goes to position
+ *                     p = cache_lengths[b] + j: page page_table[b][p / S], slot p % S
+ *   layer_idx         < L (QG_ERR_INVALID_ARG otherwise)
+ *
+ * Only the addressed (page, slot) rows of plane 0 of layer layer_idx are written;
+ * every other byte of the cache is left as it was, and cache_lengths is not
+ * updated. Kh and N must be multiples of 128 (QG_ERR_SHAPE). Accumulation is fp32;
+ * results are rounded to bf16 (nearest-even). Offsets, cache lengths and page ids
+ * are not re-validated on the device: a position past max_pages_per_seq * S or a
+ * page id >= P is undefined behaviour, as is two tokens addressing one slot.
+ */
+qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                                      const qg_tensor* weight, const qg_tensor* input_scale,
+                                      const qg_tensor* weight_scale,
+                                      const int32_t* scales_granularity_mnk,
+                                      const qg_paged_kv* kv, uint32_t layer_idx,
+                                      hipStream_t stream);
+
+/* Static, never-NULL text for a status code. */
+const char* qg_status_string(qg_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

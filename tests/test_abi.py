@@ -1,0 +1,160 @@
+"""CPU checks of the C ABI boundary: the library loads, exports every function
+include/qgemm.h declares, and rejects bad arguments before touching the GPU.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import grouped_gemm_qgemm_amd as q
+from grouped_gemm_qgemm_amd import QG, QgTensor, QgPagedKV
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\*?([A-Za-z_]\w*)\s*\(", txt, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("QG")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"qgemm_w4", "grouped_gemm", "k_matmul_ragged_paged_scale", "qg_status_string"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert len(q.status_string(s)) > 0
+    assert q.status_string(0) == "ok"
+    assert lib.qg_version() >= 100
+
+
+class Buf:
+    """Host memory standing in for device pointers: validation never dereferences them."""
+    def __init__(self):
+        self.keep = []
+
+    def t(self, shape, dtype, misalign=False):
+        n = int(np.prod(shape)) if len(shape) else 1
+        arr = np.zeros(max(n, 1) * 4 + 64, np.uint8)
+        self.keep.append(arr)
+        base = arr.ctypes.data
+        base = (base + 15) & ~15
+        d = QgTensor()
+        d.data = base + (2 if misalign else 0)
+        d.dtype = dtype
+        d.rank = len(shape)
+        for i, s in enumerate(shape):
+            d.shape[i] = s
+        return d
+
+
+def w4_call(lib, c, a, b, s, gs=128, pf=8):
+    return lib.qgemm_w4(ctypes.byref(c), ctypes.byref(a), ctypes.byref(b), ctypes.byref(s), gs, pf, None)
+
+
+def w4_args(bb, M=4, N=64, K=256, gs=128):
+    return (bb.t((M, N), QG.F16), bb.t((M, K), QG.F16), bb.t((K // 8, N), QG.U32), bb.t((K // gs, N), QG.F16))
+
+
+def test_w4_rejections(lib):
+    bb = Buf()
+    c, a, b, s = w4_args(bb)
+    # rank-2 requirement (the page's stated error)
+    assert w4_call(lib, bb.t((1, 4, 64), QG.F16), a, b, s) == QG.ERR_RANK
+    assert w4_call(lib, c, a, bb.t((32 * 64,), QG.U32), s) == QG.ERR_RANK
+    assert w4_call(lib, c, bb.t((4, 256), QG.BF16), b, s) == QG.ERR_DTYPE
+    assert w4_call(lib, c, a, bb.t((32, 64), QG.I32), s) == QG.ERR_DTYPE
+    assert w4_call(lib, c, a, b, s, pf=4) == QG.ERR_UNSUPPORTED
+    assert w4_call(lib, c, a, b, s, gs=100) == QG.ERR_SHAPE
+    assert w4_call(lib, c, a, b, bb.t((16, 64), QG.F16), gs=16) == QG.ERR_UNSUPPORTED
+    assert w4_call(lib, c, a, bb.t((31, 64), QG.U32), s) == QG.ERR_SHAPE
+    assert w4_call(lib, c, a, b, bb.t((3, 64), QG.F16)) == QG.ERR_SHAPE
+    assert w4_call(lib, bb.t((5, 64), QG.F16), a, b, s) == QG.ERR_SHAPE
+    c2, a2, b2, s2 = w4_args(bb, N=60)
+    assert w4_call(lib, c2, a2, b2, s2) == QG.ERR_ALIGN
+    assert w4_call(lib, bb.t((4, 64), QG.F16, misalign=True), a, b, s) == QG.ERR_ALIGN
+    nul = bb.t((4, 64), QG.F16)
+    nul.data = None
+    assert w4_call(lib, nul, a, b, s) == QG.ERR_NULL
+    assert lib.qgemm_w4(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(s), 128, 8, None) == QG.ERR_NULL
+
+
+def test_w4_empty_problem_is_a_noop(lib):
+    bb = Buf()
+    c, a, b, s = w4_args(bb, M=0)
+    assert w4_call(lib, c, a, b, s) == QG.OK
+
+
+def gg_call(lib, c, a, off, b, ids, usage, tb=1):
+    u = (ctypes.c_uint32 * 2)(*usage)
+    return lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
+                            ctypes.byref(ids), u, tb, None)
+
+
+def test_grouped_rejections(lib):
+    bb = Buf()
+    T, K, N, E, G = 32, 64, 48, 4, 4
+    c, a = bb.t((T, N), QG.BF16), bb.t((T, K), QG.BF16)
+    off, b, ids = bb.t((G + 1,), QG.U32), bb.t((E, N, K), QG.BF16), bb.t((G,), QG.I32)
+    assert gg_call(lib, c, a, off, bb.t((E * N, K), QG.BF16), ids, [8, 4]) == QG.ERR_RANK
+    assert gg_call(lib, c, bb.t((T, K), QG.F16), off, b, ids, [8, 4]) == QG.ERR_DTYPE
+    assert gg_call(lib, c, a, bb.t((G,), QG.U32), b, ids, [8, 4]) == QG.ERR_SHAPE
+    assert gg_call(lib, c, a, off, bb.t((E, N, K + 8), QG.BF16), ids, [8, 4]) == QG.ERR_SHAPE
+    assert gg_call(lib, c, a, off, b, ids, [8, 5]) == QG.ERR_INVALID_ARG
+    assert gg_call(lib, c, a, off, bb.t((E, K, N), QG.BF16), ids, [8, 4], tb=0) == QG.ERR_UNSUPPORTED
+    assert gg_call(lib, c, a, off, b, ids, [8, 0]) == QG.OK       # nothing active: no-op
+    u = (ctypes.c_uint32 * 2)(8, 4)
+    assert lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
+                            ctypes.byref(ids), None, 1, None) == QG.ERR_NULL
+
+
+def kp_call(lib, h, offs, w, isc, wsc, blocks, layer, gran=(1, 128, 128), cl=1, pt=1, maxp=2):
+    g = (ctypes.c_int32 * 3)(*gran)
+    kv = QgPagedKV()
+    kv.blocks = blocks
+    kv.cache_lengths = cl
+    kv.page_table = pt
+    kv.max_pages_per_seq = maxp
+    return lib.k_matmul_ragged_paged_scale(ctypes.byref(h), ctypes.byref(offs), ctypes.byref(w),
+                                           ctypes.byref(isc), ctypes.byref(wsc), g, ctypes.byref(kv),
+                                           layer, None)
+
+
+def test_kproj_rejections(lib):
+    bb = Buf()
+    T, Kh, N, B = 10, 256, 256, 2
+    h, offs = bb.t((T, Kh), QG.BF16), bb.t((B + 1,), QG.U32)
+    w, isc, wsc = bb.t((Kh, N), QG.FP8_E4M3), bb.t((T, 2), QG.F32), bb.t((2, 2), QG.F32)
+    blocks = bb.t((2, 2, 4, 16, 2, 128), QG.BF16)
+    assert kp_call(lib, h, offs, w, isc, wsc, blocks, 2) == QG.ERR_INVALID_ARG   # layer_idx >= L
+    assert kp_call(lib, h, offs, w, isc, wsc, blocks, 0, gran=(1, 64, 128)) == QG.ERR_UNSUPPORTED
+    assert kp_call(lib, h, offs, w, isc, wsc, bb.t((2, 4, 16, 2, 128), QG.BF16), 0) == QG.ERR_RANK
+    assert kp_call(lib, h, offs, bb.t((Kh, N), QG.BF16), isc, wsc, blocks, 0) == QG.ERR_DTYPE
+    assert kp_call(lib, h, offs, w, bb.t((T, 3), QG.F32), wsc, blocks, 0) == QG.ERR_SHAPE
+    assert kp_call(lib, h, offs, w, isc, wsc, bb.t((2, 2, 4, 16, 1, 128), QG.BF16), 0) == QG.ERR_SHAPE
+    assert kp_call(lib, bb.t((T, 200), QG.BF16), offs, bb.t((200, N), QG.FP8_E4M3), isc, wsc, blocks, 0) == QG.ERR_SHAPE
+    assert kp_call(lib, h, offs, w, isc, wsc, blocks, 0, cl=None) == QG.ERR_NULL
+    h0, isc0 = bb.t((0, Kh), QG.BF16), bb.t((0, 2), QG.F32)
+    assert kp_call(lib, h0, offs, w, isc0, wsc, blocks, 0) == QG.OK             # no tokens: no-op
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        q.load(str(tmp_path / "missing.so"))

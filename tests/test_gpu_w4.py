@@ -1,0 +1,137 @@
+"""GPU parity of qgemm_w4 (through the C ABI) against the CPU oracle.
+
+Modular page "multistage_gemm_q": group_size K elements per scale,
+pack_factor 4-bit codes per uint32. Float outputs: |gpu - oracle| <=
+1e-2 (|oracle| + 1) per element; unpacked weights: bit-exact."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, assert_close, dev16, dev32, f16v, host16, say
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x7E00  # fp16 NaN pattern: never produced by the kernels
+
+
+def run_w4(lib, w: synth.W4Inputs, variant_env=None, variant=None):
+    M, N, K = w.shape
+    a = dev16(w.a, torch.float16)
+    b = dev32(w.b)
+    s = dev16(w.scales, torch.float16)
+    out = Guarded((M, N), torch.float16, SENT)
+    if variant is not None:
+        os.environ[variant_env] = str(variant)
+    try:
+        lib.qgemm_w4(out.view, a, b, s, w.group_size)
+    finally:
+        if variant is not None:
+            del os.environ[variant_env]
+    got = host16(out.view)
+    assert out.bands_intact(), "write outside C"
+    return got
+
+
+def check(lib, w, what, **kw):
+    M, N, K = w.shape
+    say(f"[w4] {what}: M={M} N={N} K={K} gs={w.group_size} {kw}")
+    got = run_w4(lib, w, **kw)
+    ref = oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size)
+    return assert_close(f16v(got), f16v(ref), what=what)
+
+
+DECODE_VARIANTS = range(9)
+
+
+def test_tiny_config(gpu, lib):
+    w = synth.w4_inputs(**synth.W4_TINY)
+    check(lib, w, "tiny")
+
+
+@pytest.mark.parametrize("variant", DECODE_VARIANTS)
+def test_decode_variants_tiny_and_ragged(gpu, lib, variant):
+    for (M, N, K, gs) in [(16, 256, 512, 128), (3, 264, 384, 128), (13, 72, 256, 32), (7, 520, 512, 64),
+                          (16, 8, 256, 256), (1, 4104, 1024, 128)]:
+        w = synth.w4_inputs(M, N, K, seed=M * 7 + N, group_size=gs)
+        check(lib, w, f"decode v{variant}", variant_env="QG_W4_DECODE_VARIANT", variant=variant)
+
+
+@pytest.mark.parametrize("cfg", synth.W4_DECODE, ids=lambda c: f"M{c['M']}")
+def test_decode_full_size(gpu, lib, cfg):
+    w = synth.w4_inputs(**cfg)
+    d = check(lib, w, "decode-full")
+    say("  diagnostics", d)
+
+
+def test_decode_unpacked_weights_bit_exact(gpu, lib):
+    """Unit rows of A pick single K rows: C = round_fp16((q - 8) * s), compared bitwise."""
+    N, K, gs = 4096, 4096, 128
+    w = synth.w4_inputs(16, N, K, seed=2, a_seed=1)
+    ks = np.array([0, 1, 7, 8, 127, 128, 129, 1000, 2047, 2048, 3071, 3072, 4000, 4093, 4094, 4095])
+    a = np.zeros((16, K), np.uint16)
+    a[np.arange(16), ks] = 0x3C00
+    w.a = a
+    got = run_w4(lib, w)
+    ref = oracle.qgemm_w4(w.a, w.b, w.scales, gs)
+    assert np.array_equal(got, ref)
+
+
+def test_decode_zero_point_and_determinism(gpu, lib):
+    w = synth.w4_inputs(16, 512, 1024, seed=9)
+    w.b[:] = 0x88888888
+    got = run_w4(lib, w)
+    assert np.all(f16v(got) == 0.0)
+    w2 = synth.w4_inputs(16, 4096, 4096, seed=2, a_seed=216)
+    g1 = run_w4(lib, w2)
+    g2 = run_w4(lib, w2)
+    assert np.array_equal(g1, g2)
+
+
+# ---------------------------------------------------------------- prefill (M > 16)
+
+PREFILL_VARIANTS = range(4)
+
+
+@pytest.mark.parametrize("variant", PREFILL_VARIANTS)
+def test_prefill_variants_ragged(gpu, lib, variant):
+    for (M, N, K, gs) in [(48, 256, 512, 128), (17, 64, 256, 128), (100, 136, 96, 32), (257, 1000, 448, 64),
+                          (300, 264, 1024, 256), (129, 8, 128, 128)]:
+        w = synth.w4_inputs(M, N, K, seed=M + N + K, group_size=gs)
+        check(lib, w, f"prefill v{variant}", variant_env="QG_W4_PREFILL_VARIANT", variant=variant)
+
+
+@pytest.mark.parametrize("cfg", [synth.W4_PREFILL, synth.W4_SQUARE_PREFILL], ids=["N11008", "N4096"])
+def test_prefill_full_size_sampled_rows(gpu, lib, cfg):
+    """Full-size launch; the oracle recomputes 48 sampled rows (each row of C depends
+    only on its row of A) plus first and last rows."""
+    w = synth.w4_inputs(**cfg)
+    M, N, K = w.shape
+    say(f"[w4] prefill full M={M} N={N} K={K}")
+    got = run_w4(lib, w)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(0).choice(M, 48, replace=False)]))
+    ref = oracle.qgemm_w4(w.a[rows], w.b, w.scales, w.group_size)
+    d = assert_close(f16v(got[rows]), f16v(ref), what="prefill-full")
+    say("  diagnostics", d)
+
+
+def test_prefill_unpacked_weights_bit_exact(gpu, lib):
+    """A = I_K: every output is exactly round_fp16((q - 8) * s)."""
+    K, N, gs = 512, 320, 128
+    w = synth.w4_inputs(K, N, K, seed=4, group_size=gs)
+    w.a = np.zeros((K, K), np.uint16)
+    np.fill_diagonal(w.a, 0x3C00)
+    got = run_w4(lib, w)
+    ref = oracle.qgemm_w4(w.a, w.b, w.scales, gs)
+    assert np.array_equal(got, ref)
+
+
+def test_prefill_zero_point_and_determinism(gpu, lib):
+    w = synth.w4_inputs(64, 256, 512, seed=10)
+    w.b[:] = 0x88888888
+    assert np.all(f16v(run_w4(lib, w)) == 0.0)
+    w2 = synth.w4_inputs(300, 1024, 1024, seed=11)
+    assert np.array_equal(run_w4(lib, w2), run_w4(lib, w2))
