@@ -51,6 +51,31 @@ __device__ __forceinline__ u32x4_t dequant_w4_word(uint32_t w) {
   return r;
 }
 
+// (a & m) | b in one VALU op. v_and_or_b32 takes no literal operands, so the
+// mask is kept in a VGPR and the bias in an SGPR (the compiler would otherwise
+// split the expression into v_and_b32 + v_or_b32 with two literals).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "s"(b));
+  return d;
+}
+
+// Same unpack as dequant_w4_word with fused mask-and-bias operations; `m` must
+// hold 0x000F000F (in a VGPR) and `bias` 0x64006400.
+__device__ __forceinline__ u32x4_t dequant_w4_word_fused(uint32_t w, uint32_t m, uint32_t bias) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const uint32_t p0 = and_or(w, m, bias);
+  const uint32_t p1 = and_or(w >> 4, m, bias);
+  const uint32_t p2 = and_or(w >> 8, m, bias);
+  const uint32_t p3 = and_or(w >> 12, m, bias);
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p0) - off);
+  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p1) - off);
+  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p2) - off);
+  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p3) - off);
+  return r;
+}
+
 // Eight consecutive fp16 values (a0..a7 in four registers) reordered to the
 // K-slot order used by dequant_w4_word: (a0,a4), (a1,a5), (a2,a6), (a3,a7).
 __device__ __forceinline__ u32x4_t permute_k_0415(u32x4_t v) {

@@ -5,21 +5,22 @@
 //
 // The problem is bound by reading each active expert's weights once, so the
 // schedule is weight-stationary: a work tile is (group, block of up to 128 of
-// its rows, 64 output columns); the workgroup streams that 64 x K slice of the
-// expert's weights from HBM exactly once and multiplies every row of the block
-// against it.
-//   * Each of the four waves owns 16 columns. Its B operand for a 32-deep K step
-//     is one 16-byte load per lane of B[e][n][k..k+7] (transpose_b layout puts K
-//     contiguous), kept in registers and prefetched several K steps ahead, so
-//     weights never pass through LDS.
-//   * The rows' activations are shared by the four waves through a double-
-//     buffered LDS stage, stored in MFMA fragment order (each 1 KiB fragment is
-//     read back as lane * 16 bytes: no bank conflicts, no swizzle).
-//   * 16x16x32 bf16 MFMA with fp32 accumulation; bf16 round-to-nearest-even.
-//   * A persistent grid walks the tile list computed on the device from
-//     a_offsets / expert_ids; each XCD takes a contiguous range of tiles so
-//     the n-tiles of one group, which share its activation rows, meet in the
-//     same L2. Rows of skipped or unlisted groups are never written.
+// its rows, 64 output columns). A workgroup of four waves owns a tile; each
+// wave streams a 16-column slice of the expert's weights from HBM exactly once
+// while it multiplies every row of the block against it.
+//   * Weight fragments go straight from HBM into registers, 16 bytes per lane
+//     per 32-deep K step (transpose_b puts K contiguous in both operands),
+//     several steps ahead. The rows' activation fragments are loaded once per
+//     workgroup (split over the waves, same distance ahead) and shared through
+//     an LDS ring in MFMA fragment order (read back as lane * 16 bytes: no bank
+//     conflicts, no swizzle).
+//   * The activation rows of a group are re-read by each of its column tiles;
+//     the tiles of one group are adjacent in the tile order and every XCD takes
+//     a contiguous range of it, so those re-reads hit that XCD's L2.
+//   * 16x16x32 bf16 MFMA, fp32 accumulation, bf16 round-to-nearest-even.
+//   * The tile list is derived on the device from a_offsets / expert_ids by
+//     each workgroup walking the group table once (groups are visited in
+//     order). Rows of skipped or unlisted groups are never written.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,27 +28,115 @@ namespace qg {
 
 namespace {
 
-constexpr int GBM = 128;         // rows per work tile (8 MFMA row tiles)
-constexpr int GMT = GBM / 16;
-constexpr int GBN = 64;          // columns per work tile: 4 waves x 16
-constexpr int GWAVES = 4;
-constexpr int GTHR = GWAVES * kWave;
-constexpr int GSTEPS = 2;        // 32-deep K steps per LDS stage (BK = 64)
-constexpr int GP = 4;            // B prefetch distance, in stages
+constexpr int GWAVES = 4;           // waves per workgroup
+constexpr int GBN = 16 * GWAVES;    // columns per work tile: 16 per wave
+constexpr int GMAXMT = 8;           // row tiles per work tile (128 rows)
+constexpr int GBM = 16 * GMAXMT;
 
 }  // namespace
 
-__global__ __launch_bounds__(GTHR) void grouped_bf16_kernel(
+// One work tile with MT row tiles. D = steps of prefetch (ring depth).
+//
+// Every wave issues, per 32-deep K step, one 16-byte load of its own weight
+// fragment and (MT / 4, rounded up) of the tile's activation fragments. Loads
+// run D steps ahead. At step s each wave copies its activation fragments of
+// step s into the LDS ring, one barrier makes all of them visible, and each
+// wave multiplies every row tile against its own weight fragment. Because a
+// wave's loads are issued in step order and each step waits only for its own
+// (oldest) loads, the hardware's in-order load counter never forces a wave to
+// wait for a prefetch that lies further ahead.
+template <int MT, int D>
+__device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
+                                             const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
+                                             int N, int K, int e, int r_begin, int rows, int n0) {
+  constexpr int FPW = (MT + GWAVES - 1) / GWAVES;   // activation fragments per wave per step
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int nfull = K >> 5;
+
+  const uint16_t* a_base = A + (size_t)r_begin * K;
+  const uint16_t* b_base = B + (size_t)e * N * K;
+  uint32_t a_off[FPW];
+  int a_frag[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    a_frag[i] = min(wave + i * GWAVES, MT - 1);   // fragments past MT repeat the last one
+    a_off[i] = (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8);
+  }
+  const uint32_t b_off = (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8);
+
+  u32x4_t ra[D][FPW], rb[D];
+  auto k_of = [&](int s) { return max(0, min(s * 32, K - 8 - q * 8)); };
+  auto load_step = [&](int s, u32x4_t (&a)[FPW], u32x4_t& b) {
+    const int k = k_of(s);
+    b = *reinterpret_cast<const u32x4_t*>(b_base + (b_off + k));
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + k));
+  };
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one step out of ring slot u (data already in registers)
+  auto step = [&](int u, const u32x4_t (&a)[FPW], const u32x4_t& b) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) ring[(u * GMAXMT + a_frag[i]) * kWave + lane] = a[i];
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = mfma16x16x32_bf16(ring[(u * GMAXMT + mt) * kWave + lane], b, acc[mt]);
+  };
+
+  __syncthreads();   // the previous tile's readers are done with the ring
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_step(max(0, min(u, nfull - 1)), ra[u], rb[u]);
+
+  int s0 = 0;
+  for (; s0 + D <= nfull; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      step(u, ra[u], rb[u]);
+      load_step(min(s0 + u + D, nfull - 1), ra[u], rb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // fewer than D whole steps left: slots 0 .. nfull - s0 - 1 hold them
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (u < nfull - s0) step(u, ra[u], rb[u]);
+  // partial last step (K % 32 != 0): chunks past K enter the MFMA as zeros
+  if (K & 31) {
+    load_step(nfull, ra[0], rb[0]);
+    const bool past = nfull * 32 + q * 8 >= K;
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) ra[0][i] = past ? u32x4_t{0u, 0u, 0u, 0u} : ra[0][i];
+    // the ring slot used last may still be read by slower waves
+    __syncthreads();
+    step(0, ra[0], rb[0]);
+  }
+
+  // ---- epilogue: bf16 RNE ----
+  const int col = n0 + wave * 16 + r16;
+  if (col < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + q * 4 + i;
+        if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(GWAVES * kWave, 2) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
     int tiles_n) {
-  // A stage: [GMT row tiles][GSTEPS steps][64 lanes][16 bytes]
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][GMT * GSTEPS * kWave];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r16 = lane & 15, q = lane >> 4;
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[D * GMAXMT * kWave];
 
   // ---- tile count (every workgroup walks the same small table) ----
   int total = 0;
@@ -60,10 +149,7 @@ __global__ __launch_bounds__(GTHR) void grouped_bf16_kernel(
   const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
 
   int g = 0, g_first = 0;  // group cursor and the first tile index of group g
-  const int nst = (K + 32 * GSTEPS - 1) / (32 * GSTEPS);
-
   for (int t = lo + (int)(blockIdx.x >> 3); t < hi; t += per_xcd) {
-    // advance the cursor to the group holding tile t
     int cnt;
     for (;;) {
       const int rows = (int)(a_off[g + 1] - a_off[g]);
@@ -77,109 +163,37 @@ __global__ __launch_bounds__(GTHR) void grouped_bf16_kernel(
     const int e = ids[g];
     const int r_begin = (int)a_off[g] + chunk * GBM;
     const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
-    const int mt_n = (rows + 15) >> 4;
-    const int r_last = r_begin + rows - 1;
-
-    // B: this wave's 16 columns, this lane's column and K slot
-    const int ncol = min(nt * GBN + wave * 16 + r16, N - 1);
-    const uint16_t* bsrc = B + ((size_t)e * N + ncol) * K + q * 8;
-
-    // A loaders: fragment f = (mt, s) is 64 lanes x 16 bytes
-    auto load_a = [&](int st, u32x4_t (&ra)[GMT * GSTEPS / GWAVES]) {
-#pragma unroll
-      for (int i = 0; i < GMT * GSTEPS / GWAVES; ++i) {
-        const int f = wave + i * GWAVES;          // wave-uniform fragment id
-        const int mt = f / GSTEPS, s = f % GSTEPS;
-        if (mt < mt_n) {
-          const int row = min(r_begin + mt * 16 + r16, r_last);
-          const int k = st * 32 * GSTEPS + s * 32 + q * 8;
-          ra[i] = *reinterpret_cast<const u32x4_t*>(A + (size_t)row * K + min(k, K - 8));
-          if (k >= K) ra[i] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    };
-    auto store_a = [&](int buf, const u32x4_t (&ra)[GMT * GSTEPS / GWAVES]) {
-#pragma unroll
-      for (int i = 0; i < GMT * GSTEPS / GWAVES; ++i) {
-        const int f = wave + i * GWAVES;
-        if (f / GSTEPS < mt_n) lds_a[buf][f * kWave + lane] = ra[i];
-      }
-    };
-    auto load_b = [&](int st, u32x4_t (&rb)[GSTEPS]) {
-#pragma unroll
-      for (int s = 0; s < GSTEPS; ++s) {
-        const int k = min(st * 32 * GSTEPS + s * 32, K - 8 - q * 8);
-        rb[s] = *reinterpret_cast<const u32x4_t*>(bsrc + k);
-      }
-    };
-
-    float4_t acc[GMT];
-#pragma unroll
-    for (int i = 0; i < GMT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    u32x4_t ring[GP][GSTEPS];
-    u32x4_t ra[GMT * GSTEPS / GWAVES];
-#pragma unroll
-    for (int u = 0; u < GP; ++u) load_b(min(u, nst - 1), ring[u]);
-    load_a(0, ra);
-    __syncthreads();  // the previous tile's readers are done with both buffers
-    store_a(0, ra);
-    __syncthreads();
-
-    for (int st0 = 0; st0 < nst; st0 += GP) {
-#pragma unroll
-      for (int u = 0; u < GP; ++u) {
-        const int st = st0 + u;
-        if (st < nst) {
-          const bool more = st + 1 < nst;
-          if (more) load_a(st + 1, ra);
-          u32x4_t bq[GSTEPS];
-#pragma unroll
-          for (int s = 0; s < GSTEPS; ++s) bq[s] = ring[u][s];
-          load_b(min(st + GP, nst - 1), ring[u]);   // refill this slot GP stages ahead
-          __builtin_amdgcn_sched_barrier(0);
-          const int buf = st & 1;
-#pragma unroll
-          for (int s = 0; s < GSTEPS; ++s) {
-#pragma unroll
-            for (int mt = 0; mt < GMT; ++mt) {
-              if (mt < mt_n) {
-                const u32x4_t av = lds_a[buf][(mt * GSTEPS + s) * kWave + lane];
-                acc[mt] = mfma16x16x32_bf16(av, bq[s], acc[mt]);
-              }
-            }
-          }
-          if (more) store_a(buf ^ 1, ra);
-          __syncthreads();
-        }
-      }
-    }
-
-    // ---- epilogue: bf16 RNE; rows past the block and columns past N are not written ----
-    const int col = nt * GBN + wave * 16 + r16;
-    if (col < N) {
-#pragma unroll
-      for (int mt = 0; mt < GMT; ++mt) {
-        if (mt < mt_n) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = mt * 16 + q * 4 + i;
-            if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
-          }
-        }
-      }
+    const int n0 = nt * GBN;
+    switch ((rows + 15) >> 4) {
+      case 1: grouped_tile<1, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 2: grouped_tile<2, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 3: grouped_tile<3, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 4: grouped_tile<4, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 5: grouped_tile<5, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 6: grouped_tile<6, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 7: grouped_tile<7, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      default: grouped_tile<8, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
     }
   }
 }
 
-hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream) {
-  (void)variant;
+template <int D>
+static hipError_t launch_g(const GroupedArgs& p, int wg_per_cu, hipStream_t stream) {
   const int tiles_n = (int)((p.N + GBN - 1) / GBN);
-  int grid = 2 * p.num_cus;
-  grid = ((grid + 7) / 8) * 8;
-  hipLaunchKernelGGL(grouped_bf16_kernel, dim3(grid), dim3(GTHR), 0, stream, p.C, p.A, p.a_offsets, p.B,
-                     p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+  const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
+  hipLaunchKernelGGL((grouped_bf16_kernel<D>), dim3(grid), dim3(GWAVES * kWave), 0, stream, p.C, p.A, p.a_offsets,
+                     p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
   return hipGetLastError();
+}
+
+hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream) {
+  switch (variant) {
+    case 0: return launch_g<8>(p, 2, stream);
+    case 1: return launch_g<4>(p, 2, stream);
+    case 2: return launch_g<8>(p, 1, stream);
+    case 3: return launch_g<6>(p, 2, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace qg

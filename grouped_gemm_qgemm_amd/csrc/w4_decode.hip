@@ -130,6 +130,165 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
   }
 }
 
+// Variant with the activations staged through LDS. Each wave copies the A
+// columns of its own K batch (MROWS >= M rows, 512 columns) into a private LDS
+// slice with one coalesced 16-byte load per lane per row, reordering the K slots
+// once on the way in; the MFMA A fragments are then read from LDS. For small M
+// this removes the per-step A loads and K-slot permutes of the variant above
+// (rows >= M are never loaded), and the fused mask/bias unpack trims the B path.
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS>
+__global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
+  constexpr int SN = 16 * CPL;
+  constexpr int STEPS = SPG > BSTEPS ? SPG : BSTEPS;   // K steps per batch
+  constexpr int GB = STEPS / SPG;              // groups per batch
+  constexpr int CH = STEPS * 4;                // 16-byte A chunks per row per batch
+  constexpr int AIT = (MROWS * CH + kWave - 1) / kWave;   // A chunk loads per lane
+  __shared__ u32x4_t a_lds[NW][MROWS * CH];
+  __shared__ float red[NW][16][SN];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quarter = lane >> 4;
+  const int col16 = lane & 15;
+  const uint32_t vmask = 0x000F000Fu;   // lives in a VGPR for the fused unpack
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+
+  int strip = blockIdx.x;
+  if (xcd_remap) {
+    const int per = gridDim.x >> 3;
+    strip = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  const int n0 = strip * SN;
+  const int ncol_raw = n0 + CPL * col16;
+  const bool col_ok = ncol_raw < N;
+  const int ncol = col_ok ? ncol_raw : N - CPL;
+  const int frag_row = col16 < MROWS ? col16 : MROWS - 1;   // rows >= M hold copies; never stored
+
+  const int groups = K / (SPG * 32);
+  const int g_begin = (wave * groups) / NW;
+  const int g_end = ((wave + 1) * groups) / NW;
+
+  float4_t acc[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int g0 = g_begin; g0 < g_end; g0 += GB) {
+    const int kb0 = g0 * SPG * 32;
+    // 1. this batch's activation columns (all rows < MROWS), coalesced; chunk ids
+    //    past the slice repeat the last chunk (same data to the same place)
+    u32x4_t av[AIT];
+#pragma unroll
+    for (int it = 0; it < AIT; ++it) {
+      const int id = min(lane + it * kWave, MROWS * CH - 1);
+      const int i = id / CH, c = id % CH;
+      const int row = i < M ? i : M - 1;
+      const int k = min(kb0 + c * 8, K - 8);
+      av[it] = *reinterpret_cast<const u32x4_t*>(A + (size_t)row * K + k);
+    }
+    // 2. scales and packed weights of the batch
+    uint32_t w[GB][SPG][CPL];
+    uint16_t sc[GB][CPL];
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      const int g = g0 + j < g_end ? g0 + j : g_end - 1;
+      if constexpr (CPL == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(S + (size_t)g * N + ncol);
+        sc[j][0] = v.x & 0xFFFF; sc[j][1] = v.x >> 16; sc[j][2] = v.y & 0xFFFF; sc[j][3] = v.y >> 16;
+      } else if constexpr (CPL == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(S + (size_t)g * N + ncol);
+        sc[j][0] = v & 0xFFFF; sc[j][1] = v >> 16;
+      } else {
+        sc[j][0] = S[(size_t)g * N + ncol];
+      }
+#pragma unroll
+      for (int s = 0; s < SPG; ++s) {
+        const uint32_t* bp = B + (size_t)((g * SPG + s) * 4 + quarter) * N + ncol;
+        if constexpr (CPL == 4) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp);
+          w[j][s][0] = v.x; w[j][s][1] = v.y; w[j][s][2] = v.z; w[j][s][3] = v.w;
+        } else if constexpr (CPL == 2) {
+          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(bp);
+          w[j][s][0] = v.x; w[j][s][1] = v.y;
+        } else {
+          w[j][s][0] = *bp;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. activations -> this wave's LDS slice, K slots reordered, chunks swizzled by row
+#pragma unroll
+    for (int it = 0; it < AIT; ++it) {
+      const int id = min(lane + it * kWave, MROWS * CH - 1);
+      const int i = id / CH, c = id % CH;
+      a_lds[wave][i * CH + (c ^ (i & 15 & (CH - 1)))] = permute_k_0415(av[it]);
+    }
+    // 4. per group: MFMA chain on (q - 8), then one scaled FMA
+#pragma unroll
+    for (int j = 0; j < GB; ++j) {
+      float4_t part[CPL];
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < SPG; ++s) {
+        const int chunk = (j * SPG + s) * 4 + quarter;
+        const u32x4_t a = a_lds[wave][frag_row * CH + (chunk ^ (frag_row & 15 & (CH - 1)))];
+#pragma unroll
+        for (int t = 0; t < CPL; ++t)
+          part[t] = mfma16x16x32_f16(a, dequant_w4_word_fused(w[j][s][t], vmask, bias), part[t]);
+      }
+      const bool keep = col_ok && (g0 + j < g_end);
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) acc[t] += (keep ? h2f(sc[j][t]) : 0.f) * part[t];
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < CPL; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][quarter * 4 + i][CPL * col16 + t] = acc[t][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * SN; e += NW * kWave) {
+    const int row = e / SN, col = e % SN;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) sum += red[v][row][col];
+    if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = f2h_rn(sum);
+  }
+}
+
+template <int CPL, int NW, int SPG, int MROWS>
+static hipError_t launch_lds_cfg(const W4Args& p, hipStream_t stream) {
+  constexpr int SN = 16 * CPL;
+  constexpr int BSTEPS = NW >= 16 ? 8 : 16;   // LDS: NW * MROWS * BSTEPS * 64 bytes
+  const int strips = (int)((p.N + SN - 1) / SN);
+  const int remap = (strips % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS>), dim3(strips), dim3(NW * kWave), 0, stream,
+                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
+  return hipGetLastError();
+}
+
+template <int CPL, int NW, int MROWS>
+static hipError_t launch_lds_spg(const W4Args& p, hipStream_t stream) {
+  switch (p.group_size) {
+    case 32: return launch_lds_cfg<CPL, NW, 1, MROWS>(p, stream);
+    case 64: return launch_lds_cfg<CPL, NW, 2, MROWS>(p, stream);
+    case 128: return launch_lds_cfg<CPL, NW, 4, MROWS>(p, stream);
+    case 256: return launch_lds_cfg<CPL, NW, 8, MROWS>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int CPL, int NW>
+static hipError_t launch_lds(const W4Args& p, hipStream_t stream) {
+  if (p.M <= 1) return launch_lds_spg<CPL, NW, 1>(p, stream);
+  if (p.M <= 2) return launch_lds_spg<CPL, NW, 2>(p, stream);
+  if (p.M <= 4) return launch_lds_spg<CPL, NW, 4>(p, stream);
+  if (p.M <= 8) return launch_lds_spg<CPL, NW, 8>(p, stream);
+  return launch_lds_spg<CPL, NW, 16>(p, stream);
+}
+
 template <int CPL, int NW, int SPG>
 static hipError_t launch_cfg(const W4Args& p, hipStream_t stream) {
   constexpr int SN = 16 * CPL;
@@ -164,6 +323,13 @@ hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream) {
     case 6: return launch_spg<2, 4>(p, stream);
     case 7: return launch_spg<4, 4>(p, stream);
     case 8: return launch_spg<4, 16>(p, stream);
+    case 9: return launch_lds<1, 8>(p, stream);
+    case 10: return launch_lds<2, 8>(p, stream);
+    case 11: return launch_lds<1, 4>(p, stream);
+    case 12: return launch_lds<2, 4>(p, stream);
+    case 13: return launch_lds<4, 4>(p, stream);
+    case 14: return launch_lds<1, 16>(p, stream);
+    case 15: return launch_lds<2, 16>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

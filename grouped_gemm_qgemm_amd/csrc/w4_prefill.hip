@@ -30,6 +30,9 @@ constexpr int BK = 64;            // K per LDS stage (two 32-deep MFMA steps)
 constexpr int CHUNKS = BK / 8;    // 16-byte chunks per A row in LDS
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// transposed fp16 B rows: the 16 rows {4j + t} one fragment read touches get
+// distinct chunk positions
+__device__ __forceinline__ int swzb(int n, int chunk) { return chunk ^ ((n >> 2) & 7); }
 
 }  // namespace
 
@@ -206,6 +209,196 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_kernel(
   }
 }
 
+// Second design: the workgroup dequantizes each packed word once (not once per
+// wave) into an fp16 copy of the B tile in LDS, stored transposed ([n][k], k
+// contiguous) so both MFMA operands are plain 16-byte LDS reads; 8 waves
+// (2 per SIMD) overlap one wave's VALU work with the other's MFMAs; global
+// loads run two K tiles ahead through a pair of register sets.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_lds_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
+  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
+  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  constexpr int MT = TM / 16, NT = TN / 16;
+  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
+  constexpr int A_PER_T = BM * CHUNKS / NTHR;               // 16-byte A chunks per thread per stage
+  static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
+  constexpr int WORDS = (BK / 8) * BN;                      // packed words per stage
+  constexpr int W_PER_T = WORDS / NTHR;                     // 1, 2 or 4 adjacent columns per thread
+  static_assert(WORDS % NTHR == 0 && (W_PER_T == 1 || W_PER_T == 2 || W_PER_T == 4), "B staging");
+
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BN * CHUNKS];   // [n][k chunk]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin % tiles_m) * BM;
+  const int n0 = (lin / tiles_m) * BN;
+
+  // A staging map
+  int a_row[A_PER_T], a_ch[A_PER_T];
+  uint32_t a_off[A_PER_T];
+  const uint16_t* a_base = A;
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    a_row[i] = id / CHUNKS;
+    a_ch[i] = id % CHUNKS;
+    a_off[i] = (uint32_t)(min(m0 + a_row[i], M - 1) * K + a_ch[i] * 8);
+  }
+  // B staging map: packed row kp of the stage, W_PER_T adjacent columns
+  constexpr int CPT = BN / W_PER_T;   // threads per packed row
+  const int b_kp = tid / CPT;
+  const int b_c = (tid % CPT) * W_PER_T;
+  const int b_col = min(n0 + b_c, N - W_PER_T);
+  const int kp_total = K / 8;
+
+  struct Regs {
+    u32x4_t a[A_PER_T];
+    uint32_t w[W_PER_T];
+    uint32_t s[(W_PER_T + 1) / 2];
+  };
+  auto load_stage = [&](int kt, Regs& r) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int kk = min(k0 + a_ch[i] * 8, K - 8) - a_ch[i] * 8;
+      r.a[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + kk));
+    }
+    const int kp = min(k0 / 8 + b_kp, kp_total - 1);
+    const uint32_t* bp = B + (size_t)kp * N + b_col;
+    if constexpr (W_PER_T == 4) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp);
+      r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    } else if constexpr (W_PER_T == 2) {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(bp);
+      r.w[0] = v.x; r.w[1] = v.y;
+    } else {
+      r.w[0] = *bp;
+    }
+    const int g = (kp * 8) / group_size;
+    const uint16_t* sp = S + (size_t)g * N + b_col;
+    if constexpr (W_PER_T == 4) {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sp);
+      r.s[0] = v.x; r.s[1] = v.y;
+    } else if constexpr (W_PER_T == 2) {
+      r.s[0] = *reinterpret_cast<const uint32_t*>(sp);
+    } else {
+      r.s[0] = *sp;
+    }
+  };
+  auto store_stage = [&](int kt, int buf, const Regs& r) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      u32x4_t v = permute_k_0415(r.a[i]);
+      if (k0 + a_ch[i] * 8 >= K) v = u32x4_t{0u, 0u, 0u, 0u};   // K tail
+      lds_a[buf][a_row[i] * CHUNKS + swz(a_row[i], a_ch[i])] = v;
+    }
+    const uint32_t vmask = 0x000F000Fu;
+    const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+#pragma unroll
+    for (int j = 0; j < W_PER_T; ++j) {
+      const uint32_t sh = (r.s[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const half2_t s2 = __builtin_bit_cast(half2_t, sh | (sh << 16));
+      const u32x4_t d = dequant_w4_word_fused(r.w[j], vmask, bias);
+      const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+      const int n = b_c + j;
+      lds_b[buf][n * CHUNKS + swzb(n, b_kp)] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+    }
+  };
+
+  float4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t bf[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        // column tile t of the wave: lane j holds column 4j + (t & 3) of 64-column block t / 4
+        const int n = wn * TN + (t >> 2) * 64 + 4 * r16 + (t & 3);
+        bf[t] = lds_b[buf][n * CHUNKS + swzb(n, s * 4 + q)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * TM + mt * 16 + r16;
+        const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, s * 4 + q)];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16x16x32_f16(av, bf[t], acc[mt][t]);
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  Regs r0, r1;
+  load_stage(0, r0);
+  if (nk > 1) load_stage(1, r1);
+  store_stage(0, 0, r0);
+  __syncthreads();
+  if (nk > 2) load_stage(2, r0);
+  // iteration kt: compute stage kt; stage kt+1 (in the other register set) goes
+  // to LDS; the freed set fetches stage kt+3. Unrolled by two so set indices are static.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    compute(0);
+    store_stage(kt + 1, 1, r1);
+    __syncthreads();
+    if (kt + 3 < nk) load_stage(kt + 3, r1);
+    if (kt + 2 < nk) {
+      compute(1);
+      store_stage(kt + 2, 0, r0);
+      __syncthreads();
+      if (kt + 4 < nk) load_stage(kt + 4, r0);
+    } else {
+      compute(1);
+      kt += 2;
+      break;
+    }
+  }
+  if (kt < nk) compute(kt & 1);
+
+  // epilogue: four adjacent columns per 8-byte store
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int nb = 0; nb < NT / 4; ++nb) {
+        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
+        if (col >= N) continue;
+        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
+        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
+        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_lds_tile(const W4Args& p, hipStream_t stream) {
+  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
+  const int grid = ((tm * tn + 7) / 8) * 8;
+  hipLaunchKernelGGL((w4_prefill_lds_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
+                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
@@ -223,6 +416,10 @@ hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
     case 1: return launch_tile<128, 128, 2, 2>(p, stream);
     case 2: return launch_tile<128, 256, 2, 2>(p, stream);
     case 3: return launch_tile<64, 128, 1, 2>(p, stream);
+    case 4: return launch_lds_tile<256, 128, 4, 2>(p, stream);
+    case 5: return launch_lds_tile<128, 128, 2, 2>(p, stream);
+    case 6: return launch_lds_tile<256, 128, 2, 2>(p, stream);
+    case 7: return launch_lds_tile<128, 256, 2, 4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

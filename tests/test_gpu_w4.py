@@ -44,7 +44,7 @@ def check(lib, w, what, **kw):
     return assert_close(f16v(got), f16v(ref), what=what)
 
 
-DECODE_VARIANTS = range(9)
+DECODE_VARIANTS = range(16)
 
 
 def test_tiny_config(gpu, lib):
@@ -93,7 +93,7 @@ def test_decode_zero_point_and_determinism(gpu, lib):
 
 # ---------------------------------------------------------------- prefill (M > 16)
 
-PREFILL_VARIANTS = range(4)
+PREFILL_VARIANTS = range(8)
 
 
 @pytest.mark.parametrize("variant", PREFILL_VARIANTS)
