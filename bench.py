@@ -34,6 +34,41 @@ F16_MFMA_PEAK_TFLOPS = 2516.6
 FP8_MFMA_PEAK_TFLOPS = 5033.2
 ROTATE_BYTES = 1 << 30
 
+# HBM traffic per launch of each workload's kernel, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, each scaled by what the same counter reads for a
+# 256 MiB device copy); the summaries and commands are in profiles/. A figure is
+# reported only while the kernel sources still hash to the value it was taken at.
+KERNEL_SOURCES = {
+    "decode": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
+    "prefill": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "square": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
+    "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
+}
+MEASURED_TRAFFIC = {
+    # workload: (bytes per launch, source hash the counters were taken at)
+    "decode": (9019628, "e8671d8789f65808"),
+    "prefill": (672146327, "2ba896a6ff7acf90"),
+    "grouped": (368533321, "a99f5acb7460d421"),
+    "kproj": (128856285, "148ba49d98e5d910"),
+}
+
+
+def kernel_source_hash(cfg):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[cfg]:
+        with open(os.path.join(ROOT, "grouped_gemm_qgemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg):
+    t = MEASURED_TRAFFIC.get(cfg)
+    if t is None or t[1] != kernel_source_hash(cfg):
+        return None
+    return t[0]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -43,6 +78,10 @@ def parse():
     p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--source-hash", action="store_true", help="print the kernel source hash of --config and exit")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="before warmup, run 5 device-to-device copies of this many MiB (a plain copy kernel "
+                        "of known size whose HBM counters calibrate FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -297,6 +336,9 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
 
 def main():
     args = parse()
+    if args.source_hash:
+        print(kernel_source_hash(args.config))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
@@ -309,6 +351,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     wl = WORKLOADS[args.config](torch, q, synth)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 18          # int32 elements
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         for f in wl.launches(i):
@@ -355,7 +405,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic",
         "config": wl.describe(),
         "roofline": {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": runit, "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": runit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config),
                      "kernel": wl.kernel, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": wl.unit_bytes(),
                      "algorithmic_flops_per_launch": wl.unit_flops()},

@@ -108,9 +108,11 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
                static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
                M, N, K, group_size};
   if (M <= 16) {
-    return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 0), stream));
+    return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
   }
-  return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", 0), stream));
+  // 128x128 register-dequant tiles for wide N; cooperative-dequant 128x256 tiles otherwise
+  const int dflt = N > 8192 ? 1 : 7;
+  return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
 
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
