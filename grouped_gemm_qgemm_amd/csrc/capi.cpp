@@ -7,7 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/qgemm.h"
+#include "qgemm.h"
 #include "launch.h"
 
 namespace {
@@ -110,8 +110,7 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   if (M <= 16) {
     return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
   }
-  // 128x128 register-dequant tiles for wide N; cooperative-dequant 128x256 tiles otherwise
-  const int dflt = N > 8192 ? 1 : 7;
+  const int dflt = 9;   // 128 x 256 tiles, wave tile 128 x 64, two workgroups per CU
   return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
 

@@ -218,8 +218,237 @@ __global__ __launch_bounds__(KTHR) void kproj_fp8_paged_kernel(
   }
 }
 
+// Second design: workgroup tile BM tokens x 128 columns with BM chosen on the
+// host so the tile count fits the CU count (4312 tokens -> 144-row tiles ->
+// 240 tiles on 256 CUs). Four waves each own 32 columns and all BM rows (wave
+// tile BM x 32, BM/16 MFMA row tiles), so every fp8 weight element is
+// converted once per workgroup and every hidden fragment is read by all four
+// waves from LDS. One 128-deep stage = one scale block: the stage's MFMA
+// partial is scaled once per element by is[t][kb] * ws[kb][nb] (is for the
+// tile's rows sits in LDS, transposed, so a lane's four rows are one 16-byte
+// read). Hidden rows and the transposed bf16 weights are double-buffered in LDS
+// and prefetched one stage ahead through registers.
+__device__ __forceinline__ int swz_bt(int n, int c) { return c ^ (((n >> 1) ^ (n >> 5)) & 15); }
+
+template <int BM>
+__global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
+    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n) {
+  constexpr int MT = BM / 16;
+  constexpr int A_PER_T = BM * KCH / 256;
+  static_assert((BM * KCH) % 256 == 0, "A staging");
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * KCH];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][KBN * KCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32 per pass
+  __shared__ long long row_dst[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  // staging maps
+  uint32_t a_off[A_PER_T];
+  int a_lds[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * 256;
+    const int row = id / KCH, ch = id % KCH;
+    a_off[i] = (uint32_t)(min(m0 + row, T - 1) * Kh + ch * 8);
+    a_lds[i] = row * KCH + swz_a(row, ch);
+  }
+  const int ng = tid & 7, kq = tid >> 3;                 // weight block: 4 K rows x 16 columns
+  const uint32_t w_off = (uint32_t)(4 * kq * N + n0 + 16 * ng);
+
+  struct ARegs {
+    u32x4_t a[A_PER_T];
+  };
+  u32x4_t rw[4];
+  auto load_a = [&](int kb, ARegs& r) {
+    const int k0 = kb * KBK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
+  };
+  auto load_w = [&](int kb) {
+    const uint8_t* wb = W + (size_t)(kb * KBK) * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const u32x4_t*>(wb + w_off + j * N);
+  };
+  auto store_stage = [&](int buf, const ARegs& rr) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = rr.a[i];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      float2_t f[4][2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t word = rw[r][c4];
+        f[r][0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+        f[r][1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = 16 * ng + 4 * c4 + b;
+        const float x0 = f[0][b >> 1][b & 1], x1 = f[1][b >> 1][b & 1];
+        const float x2 = f[2][b >> 1][b & 1], x3 = f[3][b >> 1][b & 1];
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 1)]) + (kq & 1) * 2;
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{bf16pair_hi(x0, x1), bf16pair_hi(x2, x3)};
+      }
+    }
+  };
+
+  // input scales of the tile's rows, transposed to [kb][row]
+  for (int e = tid; e < KB * BM; e += 256) {
+    const int row = e % BM, kb = e / BM;
+    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
+  }
+
+  float4_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one 128-deep stage out of LDS buffer `buf`: MFMA partial, then scaled add
+  auto compute = [&](int kb, int buf) {
+    float4_t part[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int n = wave * 32 + 2 * r16 + t;   // column tile t of the wave: lane j holds column 2j + t
+        bf[t] = lds_b[buf][n * KCH + swz_bt(n, s * 4 + q)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + r16;
+        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
+        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
+        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
+      }
+      // keep each K step's fragment reads next to its MFMAs (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + mt * 16 + q * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = is4[i] * wsv;
+        acc[mt][0][i] += f * part[mt][0][i];
+        acc[mt][1][i] += f * part[mt][1][i];
+      }
+    }
+  };
+
+  // Stage kb is multiplied out of LDS buffer kb & 1 while stage kb+1 loads into
+  // registers; it is converted into the other buffer after the multiply. One
+  // barrier per stage: the buffer written at stage kb was last read at kb-1.
+  ARegs ra;
+  load_w(0);
+  load_a(0, ra);
+  store_stage(0, ra);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    if (more) {
+      load_w(kb + 1);
+      load_a(kb + 1, ra);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb, kb & 1);
+    if (more) store_stage((kb + 1) & 1, ra);
+    __syncthreads();
+  }
+
+  if (tid < BM) {
+    const int t = m0 + tid;
+    long long dst = -1;
+    if (t < T) {
+      int lo = 0, hi = batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
+      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
+      const int slot = pos % page_size;
+      dst = ((((long long)layer * 2 + 0) * num_pages + page) * page_size + slot) * (long long)N;
+    }
+    row_dst[tid] = dst;
+  }
+  __syncthreads();
+  const int col = n0 + wave * 32 + 2 * r16;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long long d = row_dst[mt * 16 + q * 4 + i];
+      if (d >= 0) {
+        const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
+        *reinterpret_cast<uint32_t*>(blocks + d + col) = v;
+      }
+    }
+  }
+}
+
+template <int BM>
+static hipError_t launch_kproj_v2(const KProjArgs& p, hipStream_t stream) {
+  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  hipLaunchKernelGGL((kproj_fp8_v2_kernel<BM>), dim3(grid), dim3(256), 0, stream, p.hidden, p.row_offsets,
+                     p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                     (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                     (int)p.layer_idx, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// Row-tile height for the v2 kernel, from the fill of the last pass over the CUs.
+static int pick_kproj_bm(const KProjArgs& p) {
+  static const int cand[] = {48, 64, 96, 128, 144};
+  const long long tn = p.N / KBN;
+  double eff[5];
+  double best_eff = 0.0;
+  for (int i = 0; i < 5; ++i) {
+    const int bm = cand[i];
+    const long long tiles = ((p.T + bm - 1) / bm) * tn;
+    const long long rounds = (tiles + p.num_cus - 1) / p.num_cus;
+    eff[i] = (double)p.T * tn / ((double)rounds * p.num_cus * bm);
+    if (eff[i] > best_eff) best_eff = eff[i];
+  }
+  // taller tiles reuse each weight fragment across more rows: take the tallest
+  // one within 3% of the best fill
+  for (int i = 4; i >= 0; --i)
+    if (eff[i] >= best_eff - 0.03) return cand[i];
+  return cand[4];
+}
+
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
-  (void)variant;
+  if (p.Kh / KBK > 32) variant = 1;   // the v2 kernel keeps at most 32 input-scale blocks in LDS
+  if (variant == 0) variant = 2;
+  if (variant >= 2) {
+    int bm = variant == 2 ? pick_kproj_bm(p) : (variant == 3 ? 128 : (variant == 4 ? 64 : 144));
+    switch (bm) {
+      case 48: return launch_kproj_v2<48>(p, stream);
+      case 64: return launch_kproj_v2<64>(p, stream);
+      case 96: return launch_kproj_v2<96>(p, stream);
+      case 128: return launch_kproj_v2<128>(p, stream);
+      default: return launch_kproj_v2<144>(p, stream);
+    }
+  }
   const int tiles_m = (int)((p.T + KBM - 1) / KBM), tiles_n = (int)(p.N / KBN);
   const int tiles = tiles_m * tiles_n;
   const int grid = ((tiles + 7) / 8) * 8;

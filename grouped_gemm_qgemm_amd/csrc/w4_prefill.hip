@@ -399,6 +399,201 @@ static hipError_t launch_lds_tile(const W4Args& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Third design (the default for large N): per-wave dequantization as in the
+// first kernel, but sized so the unpack work is amortised over eight MFMA row
+// tiles (wave tile 128 x 64, 2 x 2 waves, 256 x 128 workgroup tile), and lean
+// enough (<= 256 registers, 72 KiB LDS) for two workgroups per CU, so one
+// workgroup's VALU unpack overlaps the other's MFMAs. Unpack uses the fused
+// mask/bias form; scale pairs are built with one byte permute; the K tail is
+// handled only in the last stage; addresses are 32-bit offsets from
+// wave-uniform bases.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
+  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
+  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  constexpr int MT = TM / 16, NB = TN / 64;
+  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
+  constexpr int A_PER_T = BM * CHUNKS / NTHR;
+  static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
+  constexpr int B_CHUNKS = (BK / 8) * (BN / 4);
+  constexpr int B_PER_T = B_CHUNKS / NTHR;   // 16-byte packed chunks per thread
+  static_assert(B_CHUNKS % NTHR == 0, "B staging");
+
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][(BK / 8) * BN / 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin % tiles_m) * BM;
+  const int n0 = (lin / tiles_m) * BN;
+
+  // A staging: chunk id -> (row, chunk); 32-bit element offsets
+  uint32_t a_off[A_PER_T];
+  int a_lds[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    const int row = id / CHUNKS, ch = id % CHUNKS;
+    a_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + ch * 8);
+    a_lds[i] = row * CHUNKS + swz(row, ch);
+  }
+  const int a_ch0 = tid % CHUNKS;   // the chunk index is the same for all of a thread's A chunks
+  // B staging: 16-byte chunks (4 words, 4 adjacent columns of one packed row)
+  uint32_t b_off[B_PER_T];
+#pragma unroll
+  for (int i = 0; i < B_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
+    b_off[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4));
+  }
+  const int kp_total = K / 8;
+  // this lane's 4 output columns per 64-column block (scale columns)
+  uint32_t s_off[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) s_off[nb] = (uint32_t)min(n0 + wn * TN + nb * 64 + 4 * r16, N - 4);
+
+  u32x4_t ra[A_PER_T];
+  u32x4_t rb[B_PER_T];
+  u32x2_t sc_nxt[2][NB], sc_cur[2][NB];
+  auto load_stage = [&](int kt) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(A + k0 + a_off[i]);
+      const uint32_t* bbase = B + (size_t)(k0 / 8) * N;
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase + b_off[i]);
+    } else {
+      // partial last stage (K % 64 == 32): per-chunk clamped addresses; A chunks
+      // past K are zeroed when stored, so the clamped B rows never contribute
+      const int k = min(k0 + a_ch0 * 8, K - 8) - a_ch0 * 8;
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(A + k + a_off[i]);
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) {
+        const int b_kp = (tid + i * NTHR) / (BN / 4);
+        const int kp = min(k0 / 8 + b_kp, kp_total - 1);
+        rb[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)(kp - b_kp) * N + b_off[i]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint16_t* sbase = S + (size_t)(min(k0 + 32 * s, K - 1) / group_size) * N;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc_nxt[s][nb] = *reinterpret_cast<const u32x2_t*>(sbase + s_off[nb]);
+    }
+  };
+  auto store_stage = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(ra[i]);
+    } else {
+      // partial last stage: chunks past K enter as zeros
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const bool past = k0 + a_ch0 * 8 >= K;
+        lds_a[buf][a_lds[i]] = past ? u32x4_t{0u, 0u, 0u, 0u} : permute_k_0415(ra[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) lds_b[buf][tid + i * NTHR] = rb[i];
+  };
+
+  float4_t acc[MT][NB * 4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NB * 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t vmask = 0x000F000Fu;
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+  const int nk = (K + BK - 1) / BK;
+  load_stage(0);
+  store_stage(0, 0);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load_stage(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4_t bq[NB * 4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        // packed row s*4+q of the stage, this lane's 4 adjacent columns
+        const u32x4_t wv = lds_b[cur][(s * 4 + q) * (BN / 4) + (wn * TN + nb * 64) / 4 + r16];
+        const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
+        const uint32_t sp[2] = {sc_cur[s][nb].x, sc_cur[s][nb].y};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // (s_t, s_t) from the packed scales with one byte permute
+          const uint32_t pair = __builtin_amdgcn_perm(sp[t >> 1], sp[t >> 1], (t & 1) ? 0x03020302u : 0x01000100u);
+          const half2_t s2 = __builtin_bit_cast(half2_t, pair);
+          const u32x4_t d = dequant_w4_word_fused(w4[t], vmask, bias);
+          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+          bq[nb * 4 + t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * TM + mt * 16 + r16;
+        const u32x4_t av = lds_a[cur][row * CHUNKS + swz(row, s * 4 + q)];
+#pragma unroll
+        for (int j = 0; j < NB * 4; ++j) acc[mt][j] = mfma16x16x32_f16(av, bq[j], acc[mt][j]);
+      }
+    }
+    if (more) store_stage(kt + 1, cur ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
+      if (row >= M) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
+        if (col >= N) continue;
+        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
+        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
+        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_v3_tile(const W4Args& p, hipStream_t stream) {
+  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
+  const int grid = ((tm * tn + 7) / 8) * 8;
+  hipLaunchKernelGGL((w4_prefill_v3_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
+                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
@@ -420,6 +615,9 @@ hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
     case 5: return launch_lds_tile<128, 128, 2, 2>(p, stream);
     case 6: return launch_lds_tile<256, 128, 2, 2>(p, stream);
     case 7: return launch_lds_tile<128, 256, 2, 4>(p, stream);
+    case 8: return launch_v3_tile<256, 128, 2, 2>(p, stream);
+    case 9: return launch_v3_tile<128, 256, 1, 4>(p, stream);
+    case 10: return launch_v3_tile<128, 128, 1, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
