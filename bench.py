@@ -117,7 +117,7 @@ def w4_bytes(M, N, K, gs):
 
 class DecodeW4:
     name = "w4a16_decode_N4096_K4096_gs128_M1_4_16"
-    kernel = "w4_decode_kernel"
+    kernel = "w4_decode_lds_kernel"
     bound = "hbm"
 
     def __init__(self, torch, q, synth):
@@ -167,7 +167,7 @@ class DecodeW4:
 
 class PrefillW4:
     """Prefill-shaped W4A16: M=2048, K=4096, N=11008 (or N=4096 for the square shape)."""
-    kernel = "w4_prefill_kernel"
+    kernel = "w4_prefill_v3_kernel"
     bound = "mfma"
     dtype = "f16"
 
@@ -274,7 +274,7 @@ class GroupedBF16:
 class KProjFP8:
     """8 sequences (lengths U[1,1024], seed 5: T=4312), hidden 4096 bf16, W [4096,1024] e4m3 with 1x128x128
     block scales, bf16 keys written into a paged cache (page 128, 2 layers, layer 1)."""
-    kernel = "kproj_fp8_paged_kernel"
+    kernel = "kproj_fp8_v2_kernel"
     bound = "mfma"
     dtype = "bf16"
 

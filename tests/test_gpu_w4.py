@@ -55,7 +55,8 @@ def test_tiny_config(gpu, lib):
 @pytest.mark.parametrize("variant", DECODE_VARIANTS)
 def test_decode_variants_tiny_and_ragged(gpu, lib, variant):
     for (M, N, K, gs) in [(16, 256, 512, 128), (3, 264, 384, 128), (13, 72, 256, 32), (7, 520, 512, 64),
-                          (16, 8, 256, 256), (1, 4104, 1024, 128)]:
+                          (16, 8, 256, 256), (1, 4104, 1024, 128), (5, 1024, 2048, 64), (2, 192, 8192, 256),
+                          (9, 128, 1024, 32)]:
         w = synth.w4_inputs(M, N, K, seed=M * 7 + N, group_size=gs)
         check(lib, w, f"decode v{variant}", variant_env="QG_W4_DECODE_VARIANT", variant=variant)
 
@@ -78,6 +79,13 @@ def test_decode_unpacked_weights_bit_exact(gpu, lib):
     got = run_w4(lib, w)
     ref = oracle.qgemm_w4(w.a, w.b, w.scales, gs)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 9, 15, 16])
+def test_decode_every_row_count_class(gpu, lib, M):
+    """Default decode path at each padded row count (1, 2, 4, 8, 16) and between."""
+    w = synth.w4_inputs(M, 2048, 2048, seed=100 + M, group_size=128)
+    check(lib, w, "decode rows")
 
 
 def test_decode_zero_point_and_determinism(gpu, lib):
