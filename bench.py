@@ -47,10 +47,11 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9019628, "e8671d8789f65808"),
-    "prefill": (672146327, "2ba896a6ff7acf90"),
-    "grouped": (368533321, "a99f5acb7460d421"),
-    "kproj": (128856285, "148ba49d98e5d910"),
+    "decode": (9019628, "f9a6bf8fcb4f39f6"),
+    "prefill": (248964768, "f3a0699db4f89d07"),
+    "square": (101390528, "f3a0699db4f89d07"),
+    "grouped": (368552739, "2784f1cfb0e85fb9"),
+    "kproj": (85664619, "f59c03064c0ffb65"),
 }
 
 

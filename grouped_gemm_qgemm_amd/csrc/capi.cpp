@@ -110,7 +110,9 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   if (M <= 16) {
     return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
   }
-  const int dflt = 9;   // 128 x 256 tiles, wave tile 128 x 64, two workgroups per CU
+  // 128 x 256 tiles of 32x32x16 MFMAs, two workgroups per CU, each XCD sweeping
+  // groups of eight row panels across N
+  const int dflt = 15;
   return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
 

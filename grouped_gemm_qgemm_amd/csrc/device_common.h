@@ -32,6 +32,20 @@ __device__ __forceinline__ float4_t mfma16x16x32_bf16(u32x4_t a, u32x4_t b, floa
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_{f16,bf16}: D[32x32] += A[32x16] . B[16x32]. Lane l
+// supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; it holds
+// D[8*(i/4) + 4*(l/32) + i%4][l%32] for i = 0..15. On gfx950 this shape runs
+// at twice the sustained rate of the 16x16x32 one.
+__device__ __forceinline__ float16_t mfma32x32x16_f16(u32x4_t a, u32x4_t b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float16_t mfma32x32x16_bf16(u32x4_t a, u32x4_t b, float16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
 // weights (q - 8), exact, as four packed half pairs in the K-slot order
 // (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of

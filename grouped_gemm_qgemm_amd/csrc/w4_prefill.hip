@@ -585,12 +585,258 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_ke
   }
 }
 
+// Fourth design: the third design's staging with 32x32x16 MFMA tiles, which
+// gfx950 runs at twice the rate of 16x16x32. A wave tile is TM x 64: TM / 32
+// row tiles by two column tiles of 32, where column tile t holds the columns
+// 2j + t (lane j of the tile), so one 8-byte read of packed B per lane per
+// 16-deep K step yields both tiles' words and the results of a row come out as
+// two adjacent columns. Per 16-deep step a wave unpacks two words per lane and
+// issues 2 * TM / 32 MFMAs. Global loads run PD stages ahead of the multiply
+// (PD register sets); a stage's loads are written to LDS at the end of the
+// stage before it is multiplied, so with PD = 2 they have two stages to land.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, MINB) void w4_prefill_v4_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
+  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
+  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  constexpr int MT = TM / 32;
+  static_assert(TN == 64 && TM % 32 == 0, "wave tile");
+  static_assert(PD == 1 || PD == 2, "prefetch distance");
+  constexpr int A_PER_T = BM * CHUNKS / NTHR;
+  static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
+  constexpr int B_CHUNKS = (BK / 8) * (BN / 4);
+  constexpr int B_PER_T = B_CHUNKS / NTHR;   // 16-byte packed chunks per thread
+  static_assert(B_CHUNKS % NTHR == 0, "B staging");
+
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][(BK / 8) * BN / 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int h = lane >> 5, c32 = lane & 31;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  // tile order within an XCD's run: 0 = M fastest, 1 = N fastest, else groups
+  // of `order` row panels swept across N
+  int tm, tn;
+  if (order == 0) {
+    tm = lin % tiles_m;
+    tn = lin / tiles_m;
+  } else if (order == 1) {
+    tm = lin / tiles_n;
+    tn = lin % tiles_n;
+  } else {
+    const int span = order * tiles_n;
+    const int first = (lin / span) * order;
+    const int gm = min(tiles_m - first, order);
+    const int r = lin % span;
+    tm = first + r % gm;
+    tn = r / gm;
+  }
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
+
+  // A staging: chunk id -> (row, chunk); 32-bit element offsets
+  uint32_t a_off[A_PER_T];
+  int a_lds[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    const int row = id / CHUNKS, ch = id % CHUNKS;
+    a_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + ch * 8);
+    a_lds[i] = row * CHUNKS + swz(row, ch);
+  }
+  const int a_ch0 = tid % CHUNKS;   // the chunk index is the same for all of a thread's A chunks
+  // B staging: 16-byte chunks (4 words, 4 adjacent columns of one packed row)
+  uint32_t b_off[B_PER_T];
+#pragma unroll
+  for (int i = 0; i < B_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
+    b_off[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4));
+  }
+  const int kp_total = K / 8;
+  // this lane's two output columns (scale columns)
+  const uint32_t s_off = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2);
+
+  // one stage of prefetched operands: A chunks, packed B chunks, the lane's scale pairs
+  struct Regs {
+    u32x4_t a[A_PER_T];
+    u32x4_t b[B_PER_T];
+    uint32_t sc[2];
+  };
+  auto load_stage = [&](int kt, Regs& r) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(A + k0 + a_off[i]);
+      const uint32_t* bbase = B + (size_t)(k0 / 8) * N;
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) r.b[i] = *reinterpret_cast<const u32x4_t*>(bbase + b_off[i]);
+    } else {
+      // partial last stage (K % 64 == 32): per-chunk clamped addresses; A chunks
+      // past K are zeroed when stored, so the clamped B rows never contribute
+      const int k = min(k0 + a_ch0 * 8, K - 8) - a_ch0 * 8;
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(A + k + a_off[i]);
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i) {
+        const int b_kp = (tid + i * NTHR) / (BN / 4);
+        const int kp = min(k0 / 8 + b_kp, kp_total - 1);
+        r.b[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)(kp - b_kp) * N + b_off[i]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      r.sc[s] = *reinterpret_cast<const uint32_t*>(S + (size_t)(min(k0 + 32 * s, K - 1) / group_size) * N + s_off);
+  };
+  auto store_stage = [&](int kt, int buf, const Regs& r) {
+    const int k0 = kt * BK;
+    if (k0 + BK <= K) {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
+    } else {
+      // partial last stage: chunks past K enter as zeros
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) {
+        const bool past = k0 + a_ch0 * 8 >= K;
+        lds_a[buf][a_lds[i]] = past ? u32x4_t{0u, 0u, 0u, 0u} : permute_k_0415(r.a[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER_T; ++i) lds_b[buf][tid + i * NTHR] = r.b[i];
+  };
+
+  float16_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
+
+  const uint32_t vmask = 0x000F000Fu;
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+  // one stage out of LDS buffer `buf` with the scale pairs `sc`
+  auto compute = [&](int buf, const uint32_t (&sc)[2]) {
+    const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds_b[buf]);
+#pragma unroll
+    for (int j = 0; j < BK / 16; ++j) {
+      // packed row 2j + h of the stage, columns 2*c32 and 2*c32 + 1 of the wave's 64
+      const uint64_t w2 = bw[(2 * j + h) * (BN / 2) + wn * (TN / 2) + c32];
+      const uint32_t sp = sc[j >> 1];
+      u32x4_t bq[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
+        const half2_t s2 = __builtin_bit_cast(half2_t, pair);
+        const u32x4_t d = dequant_w4_word_fused((uint32_t)(w2 >> (32 * t)), vmask, bias);
+        const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+        bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * TM + mt * 32 + c32;
+        const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
+        acc[mt][0] = mfma32x32x16_f16(av, bq[0], acc[mt][0]);
+        acc[mt][1] = mfma32x32x16_f16(av, bq[1], acc[mt][1]);
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  if constexpr (PD == 1) {
+    Regs r;
+    uint32_t sc_cur[2];
+    load_stage(0, r);
+    store_stage(0, 0, r);
+    sc_cur[0] = r.sc[0];
+    sc_cur[1] = r.sc[1];
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) load_stage(kt + 1, r);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt & 1, sc_cur);
+      if (more) store_stage(kt + 1, (kt + 1) & 1, r);
+      __syncthreads();
+      sc_cur[0] = r.sc[0];
+      sc_cur[1] = r.sc[1];
+    }
+  } else {
+    // Stage kt + 1 waits in one register set while stage kt + 2 loads into the
+    // other; unrolled by two so the sets are static. Set u holds stages of
+    // parity u. Loads retire in issue order, so waiting for the older set never
+    // waits for the newer one.
+    Regs r0, r1;
+    uint32_t sc_cur[2];
+    load_stage(0, r0);
+    if (nk > 1) load_stage(1, r1);
+    store_stage(0, 0, r0);
+    sc_cur[0] = r0.sc[0];
+    sc_cur[1] = r0.sc[1];
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      // even stage kt: buffer 0; stage kt + 1 is in r1
+      if (kt + 2 < nk) load_stage(kt + 2, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, sc_cur);
+      store_stage(kt + 1, 1, r1);
+      __syncthreads();
+      sc_cur[0] = r1.sc[0];
+      sc_cur[1] = r1.sc[1];
+      // odd stage kt + 1: buffer 1; stage kt + 2 (if any) is in r0
+      if (kt + 3 < nk) load_stage(kt + 3, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(1, sc_cur);
+      if (kt + 2 < nk) {
+        store_stage(kt + 2, 0, r0);
+        sc_cur[0] = r0.sc[0];
+        sc_cur[1] = r0.sc[1];
+      }
+      __syncthreads();
+    }
+    if (kt < nk) compute(0, sc_cur);   // nk odd: the last stage sits in buffer 0
+  }
+
+  // epilogue: two adjacent columns per 4-byte store
+  const int col = n0 + wn * TN + 2 * c32;
+  if (col < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (row < M)
+          *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
+              (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN>
 static hipError_t launch_v3_tile(const W4Args& p, hipStream_t stream) {
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
   const int grid = ((tm * tn + 7) / 8) * 8;
   hipLaunchKernelGGL((w4_prefill_v3_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
                      p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int MINB, int PD>
+static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order = 0) {
+  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
+  const int grid = ((tm * tn + 7) / 8) * 8;
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
+                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
   return hipGetLastError();
 }
 
@@ -618,6 +864,12 @@ hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
     case 8: return launch_v3_tile<256, 128, 2, 2>(p, stream);
     case 9: return launch_v3_tile<128, 256, 1, 4>(p, stream);
     case 10: return launch_v3_tile<128, 128, 1, 2>(p, stream);
+    // fourth design, 128 x 256 tiles; the last argument is the tile order
+    case 11: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 0);
+    case 12: return launch_v4_tile<128, 256, 1, 4, 2, 2>(p, stream, 8);
+    case 13: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 1);
+    case 14: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 4);
+    case 15: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 8);
     default: return hipErrorInvalidValue;
   }
 }
