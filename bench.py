@@ -275,7 +275,7 @@ class GroupedBF16:
 class KProjFP8:
     """8 sequences (lengths U[1,1024], seed 5: T=4312), hidden 4096 bf16, W [4096,1024] e4m3 with 1x128x128
     block scales, bf16 keys written into a paged cache (page 128, 2 layers, layer 1)."""
-    kernel = "kproj_fp8_v2_kernel"
+    kernel = "kproj_fp8_v3_kernel"
     bound = "mfma"
     dtype = "bf16"
 

@@ -8,8 +8,10 @@
 // with 128 x 128 weight-scale blocks and 1 x 128 input-scale blocks. Tokens of
 // all sequences are one flat row dimension (raggedness costs nothing in the
 // GEMM); the sequence only matters for where a finished row is stored.
-//   * Workgroup tile 64 tokens x 128 columns; each 128-deep K stage is exactly
-//     one scale block, so the stage's MFMA partial is scaled once, in fp32, by
+//   * Three designs: 64 x 128 tiles (first), BM x 128 tiles with four waves
+//     (second), and the same tiles with 4 * BM / 48 waves (third, the default;
+//     described above its kernel). Each 128-deep K stage is exactly one scale
+//     block, so the stage's MFMA partial is scaled once, in fp32, by
 //     is[t][kb] * ws[kb][nb] (ws is uniform over the tile) and added to the
 //     accumulator. Activations are never re-rounded.
 //   * The fp8 weight tile [128 k][128 n] is fetched with coalesced 16-byte row
@@ -19,8 +21,9 @@
 //   * Hidden rows are staged through LDS with an XOR swizzle; double-buffered
 //     stages, one barrier per stage.
 //   * 16x16x32 bf16 MFMA, fp32 accumulation. Column tile t of a wave holds
-//     columns 4j + t (j = lane % 16), so each lane finishes four adjacent
-//     columns of a row and stores them with one 8-byte write.
+//     columns 4j + t (j = lane % 16) in the first design, so each lane finishes
+//     four adjacent columns of a row (one 8-byte write); the second and third
+//     designs use columns 2j + t and 4-byte writes.
 //   * Epilogue: token t -> sequence b (binary search of the row offsets) ->
 //     position cache_lengths[b] + (t - offs[b]) -> (page_table entry, slot);
 //     the bf16 row lands in plane 0 (keys) of layer layer_idx. Nothing else in
@@ -405,6 +408,201 @@ __global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
   }
 }
 
+// Third design: the second design's tiles (BM = 48 * WM rows x 128 columns,
+// one 128-deep stage per scale block) with WM x 4 waves, each owning a 48 x 32
+// wave tile (three 16-row by two 16-column MFMA tiles). With WM = 3 (the
+// 144-row tiles that fill 256 CUs at 4312 tokens) a SIMD runs three waves, so
+// one wave's LDS and load waits are covered by the others' MFMAs; with one wave
+// per SIMD those waits were exposed on every stage. The first min(512, threads)
+// threads stage the weight tile (RPT K rows of 16 columns each).
+template <int WM>
+__global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
+    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n) {
+  constexpr int BM = 48 * WM;
+  constexpr int NTHR = WM * 256;
+  constexpr int MT = 3;                          // 16-row MFMA tiles per wave
+  constexpr int A_PER_T = BM * KCH / NTHR;       // 16-byte hidden chunks per thread per stage
+  static_assert(A_PER_T * NTHR == BM * KCH, "A staging");
+  constexpr int WT = NTHR < 512 ? NTHR : 512;    // threads that stage the weight tile
+  constexpr int RPT = 1024 / WT;                 // K rows per staging thread (128 rows x 8 column groups)
+  static_assert(RPT == 2 || RPT == 4, "weight staging");
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * KCH];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][KBN * KCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
+  __shared__ long long row_dst[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  uint32_t a_off[A_PER_T];
+  int a_lds[A_PER_T];
+#pragma unroll
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int id = tid + i * NTHR;
+    const int row = id / KCH, ch = id % KCH;
+    a_off[i] = (uint32_t)(min(m0 + row, T - 1) * Kh + ch * 8);
+    a_lds[i] = row * KCH + swz_a(row, ch);
+  }
+  const bool wstage = tid < WT;                          // wave-uniform
+  const int ng = tid & 7, kq = (tid >> 3) & (WT / 8 - 1);  // 16-column group, K-row group
+  const uint32_t w_off = (uint32_t)(RPT * kq * N + n0 + 16 * ng);
+
+  u32x4_t ra[A_PER_T];
+  u32x4_t rw[RPT];
+  auto load_stage = [&](int kb) {
+    const int k0 = kb * KBK;
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
+    if (wstage) {
+      const uint8_t* wb = W + (size_t)k0 * N;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) rw[r] = *reinterpret_cast<const u32x4_t*>(wb + w_off + r * N);
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = ra[i];
+    if (wstage) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        float2_t f[RPT][2];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+          const uint32_t word = rw[r][c4];
+          f[r][0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+          f[r][1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int n = 16 * ng + 4 * c4 + b;
+          if constexpr (RPT == 4) {
+            // K rows 4kq .. 4kq+3: half of a 16-byte chunk
+            uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 1)]) + (kq & 1) * 2;
+            *reinterpret_cast<u32x2_t*>(dst) =
+                u32x2_t{bf16pair_hi(f[0][b >> 1][b & 1], f[1][b >> 1][b & 1]),
+                        bf16pair_hi(f[2][b >> 1][b & 1], f[3][b >> 1][b & 1])};
+          } else {
+            // K rows 2kq, 2kq+1: one word of a 16-byte chunk
+            uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 2)]) + (kq & 3);
+            *dst = bf16pair_hi(f[0][b >> 1][b & 1], f[1][b >> 1][b & 1]);
+          }
+        }
+      }
+    }
+  };
+
+  for (int e = tid; e < KB * BM; e += NTHR) {
+    const int row = e % BM, kb = e / BM;
+    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
+  }
+
+  float4_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int kb, int buf) {
+    float4_t part[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int n = wn * 32 + 2 * r16 + t;   // column tile t of the wave: lane j holds column 2j + t
+        bf[t] = lds_b[buf][n * KCH + swz_bt(n, s * 4 + q)];
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 48 + mt * 16 + r16;
+        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
+        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
+        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
+      }
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = is4[i] * wsv;
+        acc[mt][0][i] += f * part[mt][0][i];
+        acc[mt][1][i] += f * part[mt][1][i];
+      }
+    }
+  };
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    if (more) load_stage(kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb, kb & 1);
+    if (more) store_stage((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  if (tid < BM) {
+    const int t = m0 + tid;
+    long long dst = -1;
+    if (t < T) {
+      int lo = 0, hi = batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
+      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
+      const int slot = pos % page_size;
+      dst = ((((long long)layer * 2 + 0) * num_pages + page) * page_size + slot) * (long long)N;
+    }
+    row_dst[tid] = dst;
+  }
+  __syncthreads();
+  const int col = n0 + wn * 32 + 2 * r16;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
+      if (d >= 0) {
+        const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
+        *reinterpret_cast<uint32_t*>(blocks + d + col) = v;
+      }
+    }
+  }
+}
+
+template <int WM>
+static hipError_t launch_kproj_v3(const KProjArgs& p, hipStream_t stream) {
+  constexpr int BM = 48 * WM;
+  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden, p.row_offsets,
+                     p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                     (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                     (int)p.layer_idx, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <int BM>
 static hipError_t launch_kproj_v2(const KProjArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
@@ -416,31 +614,44 @@ static hipError_t launch_kproj_v2(const KProjArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Row-tile height for the v2 kernel, from the fill of the last pass over the CUs.
-static int pick_kproj_bm(const KProjArgs& p) {
-  static const int cand[] = {48, 64, 96, 128, 144};
+// Row-tile height from the fill of the last pass over the CUs: the tallest
+// candidate within 3% of the best fill (taller tiles reuse each weight
+// fragment across more rows).
+static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
   const long long tn = p.N / KBN;
-  double eff[5];
+  double eff[8];
   double best_eff = 0.0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < n; ++i) {
     const int bm = cand[i];
     const long long tiles = ((p.T + bm - 1) / bm) * tn;
     const long long rounds = (tiles + p.num_cus - 1) / p.num_cus;
     eff[i] = (double)p.T * tn / ((double)rounds * p.num_cus * bm);
     if (eff[i] > best_eff) best_eff = eff[i];
   }
-  // taller tiles reuse each weight fragment across more rows: take the tallest
-  // one within 3% of the best fill
-  for (int i = 4; i >= 0; --i)
+  for (int i = n - 1; i >= 0; --i)
     if (eff[i] >= best_eff - 0.03) return cand[i];
-  return cand[4];
+  return cand[n - 1];
 }
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
-  if (p.Kh / KBK > 32) variant = 1;   // the v2 kernel keeps at most 32 input-scale blocks in LDS
-  if (variant == 0) variant = 2;
+  if (p.Kh / KBK > 32) variant = 1;   // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
+  if (variant == 0) variant = 6;
+  if (variant >= 6) {
+    // third design: 48, 96 or 144-row tiles (auto), or forced
+    int wm = variant == 7 ? 1 : (variant == 8 ? 2 : (variant == 9 ? 3 : 0));
+    if (wm == 0) {
+      static const int cand[] = {48, 96, 144};
+      wm = pick_kproj_rows(p, cand, 3) / 48;
+    }
+    switch (wm) {
+      case 1: return launch_kproj_v3<1>(p, stream);
+      case 2: return launch_kproj_v3<2>(p, stream);
+      default: return launch_kproj_v3<3>(p, stream);
+    }
+  }
   if (variant >= 2) {
-    int bm = variant == 2 ? pick_kproj_bm(p) : (variant == 3 ? 128 : (variant == 4 ? 64 : 144));
+    static const int cand[] = {48, 64, 96, 128, 144};
+    int bm = variant == 2 ? pick_kproj_rows(p, cand, 5) : (variant == 3 ? 128 : (variant == 4 ? 64 : 144));
     switch (bm) {
       case 48: return launch_kproj_v2<48>(p, stream);
       case 64: return launch_kproj_v2<64>(p, stream);
