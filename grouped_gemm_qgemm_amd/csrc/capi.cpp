@@ -110,9 +110,11 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   if (M <= 16) {
     return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
   }
-  // 128 x 256 tiles of 32x32x16 MFMAs, two workgroups per CU, each XCD sweeping
-  // groups of eight row panels across N
-  const int dflt = 15;
+  // 128 x 256 tiles of 32x32x16 MFMAs, each XCD sweeping groups of eight row
+  // panels across N: with fewer than four tiles per CU one workgroup of two
+  // K groups per CU (16), otherwise two workgroups of one K group (15)
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  const int dflt = tiles < 4 * (int64_t)device_cus() ? 16 : 15;
   return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
 

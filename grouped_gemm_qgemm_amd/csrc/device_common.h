@@ -46,6 +46,18 @@ __device__ __forceinline__ float16_t mfma32x32x16_bf16(u32x4_t a, u32x4_t b, flo
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Raw buffer access: a 128-bit descriptor (base, size in bytes) in SGPRs, a
+// per-lane byte offset in one VGPR and a uniform byte offset in an SGPR, so a
+// loop of loads that advance together costs no per-load 64-bit address math.
+// Reads at or past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
 // weights (q - 8), exact, as four packed half pairs in the K-slot order
 // (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of

@@ -55,38 +55,49 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   const int r16 = lane & 15, q = lane >> 4;
   const int nfull = K >> 5;
 
-  const uint16_t* a_base = A + (size_t)r_begin * K;
-  const uint16_t* b_base = B + (size_t)e * N * K;
-  uint32_t a_off[FPW];
+  // buffer descriptors over this tile's activation rows and the expert's weights;
+  // per-lane byte offsets, the step's K offset is uniform (an SGPR)
+  const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)r_begin * K, (uint32_t)rows * K * 2);
+  const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + (size_t)e * N * K, (uint32_t)N * K * 2);
+  uint32_t a_voff[FPW];
   int a_frag[FPW];
 #pragma unroll
   for (int i = 0; i < FPW; ++i) {
     a_frag[i] = min(wave + i * GWAVES, MT - 1);   // fragments past MT repeat the last one
-    a_off[i] = (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8);
+    a_voff[i] = (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2;
   }
-  const uint32_t b_off = (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8);
+  const uint32_t b_voff = (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8) * 2;
 
   u32x4_t ra[D][FPW], rb[D];
-  auto k_of = [&](int s) { return max(0, min(s * 32, K - 8 - q * 8)); };
+  // whole step s: K elements 32s .. 32s + 31
   auto load_step = [&](int s, u32x4_t (&a)[FPW], u32x4_t& b) {
-    const int k = k_of(s);
-    b = *reinterpret_cast<const u32x4_t*>(b_base + (b_off + k));
+    const uint32_t soff = (uint32_t)s * 64;
+    b = buffer_load16(b_src, b_voff, soff);
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + k));
+    for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i], soff);
+  };
+  // partial last step (K % 32 != 0): each lane's chunk start is clamped into its row
+  auto load_tail = [&](u32x4_t (&a)[FPW], u32x4_t& b) {
+    const uint32_t k2 = (uint32_t)max(0, min(nfull * 32, K - 8 - q * 8)) * 2;
+    b = buffer_load16(b_src, b_voff + k2, 0);
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i] + k2, 0);
   };
 
   float4_t acc[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // one step out of ring slot u (data already in registers)
-  auto step = [&](int u, const u32x4_t (&a)[FPW], const u32x4_t& b) {
+  // one step through LDS slot `slot` (data already in registers). Two slots
+  // suffice: the slot written at step s was last read at step s - 2, and every
+  // wave has passed step s - 1's barrier, so it is done with those reads.
+  auto step = [&](int slot, const u32x4_t (&a)[FPW], const u32x4_t& b) {
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) ring[(u * GMAXMT + a_frag[i]) * kWave + lane] = a[i];
+    for (int i = 0; i < FPW; ++i) ring[(slot * GMAXMT + a_frag[i]) * kWave + lane] = a[i];
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = mfma16x16x32_bf16(ring[(u * GMAXMT + mt) * kWave + lane], b, acc[mt]);
+      acc[mt] = mfma16x16x32_bf16(ring[(slot * GMAXMT + mt) * kWave + lane], b, acc[mt]);
   };
 
   __syncthreads();   // the previous tile's readers are done with the ring
@@ -97,24 +108,24 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   for (; s0 + D <= nfull; s0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
-      step(u, ra[u], rb[u]);
+      step((s0 + u) & 1, ra[u], rb[u]);
       load_step(min(s0 + u + D, nfull - 1), ra[u], rb[u]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // fewer than D whole steps left: slots 0 .. nfull - s0 - 1 hold them
+  // fewer than D whole steps left: register slots 0 .. nfull - s0 - 1 hold them
 #pragma unroll
   for (int u = 0; u < D - 1; ++u)
-    if (u < nfull - s0) step(u, ra[u], rb[u]);
-  // partial last step (K % 32 != 0): chunks past K enter the MFMA as zeros
+    if (u < nfull - s0) step((s0 + u) & 1, ra[u], rb[u]);
+  // partial last step (K % 32 != 0): chunks past K enter the MFMA as zeros on
+  // both sides
   if (K & 31) {
-    load_step(nfull, ra[0], rb[0]);
+    load_tail(ra[0], rb[0]);
     const bool past = nfull * 32 + q * 8 >= K;
+    rb[0] = past ? u32x4_t{0u, 0u, 0u, 0u} : rb[0];
 #pragma unroll
     for (int i = 0; i < FPW; ++i) ra[0][i] = past ? u32x4_t{0u, 0u, 0u, 0u} : ra[0][i];
-    // the ring slot used last may still be read by slower waves
-    __syncthreads();
-    step(0, ra[0], rb[0]);
+    step(nfull & 1, ra[0], rb[0]);
   }
 
   // ---- epilogue: bf16 RNE ----
@@ -131,12 +142,12 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(GWAVES * kWave, 2) void grouped_bf16_kernel(
+template <int D, int OCC>
+__global__ __launch_bounds__(GWAVES * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
     int tiles_n) {
-  __shared__ __attribute__((aligned(16))) u32x4_t ring[D * GMAXMT * kWave];
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
 
   // ---- tile count (every workgroup walks the same small table) ----
   int total = 0;
@@ -164,34 +175,42 @@ __global__ __launch_bounds__(GWAVES * kWave, 2) void grouped_bf16_kernel(
     const int r_begin = (int)a_off[g] + chunk * GBM;
     const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
     const int n0 = nt * GBN;
+    // Tiles of more than four row tiles load two activation fragments per wave
+    // per step, so they run half as many steps ahead: the same registers and
+    // about the same bytes in flight.
     switch ((rows + 15) >> 4) {
       case 1: grouped_tile<1, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
       case 2: grouped_tile<2, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
       case 3: grouped_tile<3, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
       case 4: grouped_tile<4, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 5: grouped_tile<5, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 6: grouped_tile<6, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 7: grouped_tile<7, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      default: grouped_tile<8, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 5: grouped_tile<5, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 6: grouped_tile<6, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 7: grouped_tile<7, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      default: grouped_tile<8, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
     }
   }
 }
 
-template <int D>
-static hipError_t launch_g(const GroupedArgs& p, int wg_per_cu, hipStream_t stream) {
+template <int D, int OCC>
+static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
+  const int wg_per_cu = OCC;
   const int tiles_n = (int)((p.N + GBN - 1) / GBN);
   const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
-  hipLaunchKernelGGL((grouped_bf16_kernel<D>), dim3(grid), dim3(GWAVES * kWave), 0, stream, p.C, p.A, p.a_offsets,
+  hipLaunchKernelGGL((grouped_bf16_kernel<D, OCC>), dim3(grid), dim3(GWAVES * kWave), 0, stream, p.C, p.A, p.a_offsets,
                      p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream) {
   switch (variant) {
-    case 0: return launch_g<8>(p, 2, stream);
-    case 1: return launch_g<4>(p, 2, stream);
-    case 2: return launch_g<8>(p, 1, stream);
-    case 3: return launch_g<6>(p, 2, stream);
+    case 0: return launch_g<8, 2>(p, stream);
+    case 1: return launch_g<4, 2>(p, stream);
+    case 2: return launch_g<8, 1>(p, stream);
+    case 3: return launch_g<12, 2>(p, stream);
+    case 4: return launch_g<16, 2>(p, stream);
+    case 5: return launch_g<8, 3>(p, stream);
+    case 6: return launch_g<12, 3>(p, stream);
+    case 7: return launch_g<24, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -594,27 +594,37 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_ke
 // issues 2 * TM / 32 MFMAs. Global loads run PD stages ahead of the multiply
 // (PD register sets); a stage's loads are written to LDS at the end of the
 // stage before it is multiplied, so with PD = 2 they have two stages to land.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, MINB) void w4_prefill_v4_kernel(
+// With KG = 2 the workgroup holds two groups of WAVES_M x WAVES_N waves that
+// take the even and the odd K stages (each with its own LDS buffers) and sum
+// their accumulators through LDS at the end: the same tile and the same unpack
+// work per wave, twice the waves per SIMD to cover each other's waits (for
+// shapes with about one tile per CU).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
-  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
+  constexpr int NTHR = WAVES_M * WAVES_N * kWave;   // threads of one K group
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
   static_assert(TN == 64 && TM % 32 == 0, "wave tile");
   static_assert(PD == 1 || PD == 2, "prefetch distance");
+  static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
   static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
   constexpr int B_CHUNKS = (BK / 8) * (BN / 4);
   constexpr int B_PER_T = B_CHUNKS / NTHR;   // 16-byte packed chunks per thread
   static_assert(B_CHUNKS % NTHR == 0, "B staging");
 
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][(BK / 8) * BN / 4];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a_all[KG][2][BM * CHUNKS];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b_all[KG][2][(BK / 8) * BN / 4];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave_all / (WAVES_M * WAVES_N);        // K group
+  const int wave = wave_all % (WAVES_M * WAVES_N);      // wave within the group
+  const int tid = threadIdx.x % NTHR;                  // thread within the group
+  auto& lds_a = lds_a_all[kg];
+  auto& lds_b = lds_b_all[kg];
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int h = lane >> 5, c32 = lane & 31;
 
@@ -751,7 +761,60 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, MINB) void w4_prefill_v4
   };
 
   const int nk = (K + BK - 1) / BK;
-  if constexpr (PD == 1) {
+  if constexpr (KG == 2) {
+    // group kg takes stages kg, kg + 2, ...; both groups run the same number of
+    // iterations so every wave reaches every barrier
+    Regs r;
+    uint32_t sc_cur[2] = {0u, 0u};
+    if (kg < nk) {
+      load_stage(kg, r);
+      store_stage(kg, 0, r);
+      sc_cur[0] = r.sc[0];
+      sc_cur[1] = r.sc[1];
+    }
+    __syncthreads();
+    const int iters = (nk + 1) / 2;
+    for (int j = 0; j < iters; ++j) {
+      const int kt = kg + 2 * j;
+      const bool more = kt + 2 < nk;
+      if (more) load_stage(kt + 2, r);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt < nk) compute(j & 1, sc_cur);
+      if (more) store_stage(kt + 2, (j + 1) & 1, r);
+      __syncthreads();
+      if (more) {
+        sc_cur[0] = r.sc[0];
+        sc_cur[1] = r.sc[1];
+      }
+    }
+    // group 1 hands its partial sums to group 0 through the (now free) A
+    // buffers, two row tiles at a time; lane-major so the accesses are
+    // conflict-free
+    float* red = reinterpret_cast<float*>(&lds_a_all[0][0][0]);
+    static_assert(sizeof(lds_a_all) >= 64 * NTHR * sizeof(float), "reduction space");
+#pragma unroll
+    for (int p = 0; p < MT / 2; ++p) {
+      if (kg == 1) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[((m * 2 + t) * 16 + i) * NTHR + tid] = acc[2 * p + m][t][i];
+      }
+      __syncthreads();
+      if (kg == 0) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[2 * p + m][t][i] += red[((m * 2 + t) * 16 + i) * NTHR + tid];
+      }
+      __syncthreads();
+    }
+    if (kg == 1) return;
+  } else if constexpr (PD == 1) {
     Regs r;
     uint32_t sc_cur[2];
     load_stage(0, r);
@@ -831,11 +894,11 @@ static hipError_t launch_v3_tile(const W4Args& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int MINB, int PD>
+template <int BM, int BN, int WM, int WN, int MINB, int PD, int KG = 1>
 static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order = 0) {
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
   const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG>), dim3(grid), dim3(WM * WN * kWave * KG), 0, stream,
                      p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
   return hipGetLastError();
 }
@@ -870,6 +933,9 @@ hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
     case 13: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 1);
     case 14: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 4);
     case 15: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 8);
+    // two K groups of four waves (128 x 64 wave tiles), one workgroup per CU
+    case 16: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 8);
+    case 17: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 0);
     default: return hipErrorInvalidValue;
   }
 }

@@ -101,7 +101,7 @@ def test_decode_zero_point_and_determinism(gpu, lib):
 
 # ---------------------------------------------------------------- prefill (M > 16)
 
-PREFILL_VARIANTS = range(16)
+PREFILL_VARIANTS = range(18)
 
 
 @pytest.mark.parametrize("variant", PREFILL_VARIANTS)
