@@ -114,7 +114,8 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   // panels across N: with fewer than four tiles per CU one workgroup of two
   // K groups per CU (16), otherwise two workgroups of one K group (15)
   const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  const int dflt = tiles < 4 * (int64_t)device_cus() ? 16 : 15;
+  int dflt = tiles < 4 * (int64_t)device_cus() ? 16 : 15;
+  if (K / 8 * N * 4 > 0xFFFFFFFFLL) dflt = 9;   // beyond 32-bit buffer offsets: the third design
   return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
 

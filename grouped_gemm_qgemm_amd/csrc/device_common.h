@@ -58,6 +58,10 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
 // weights (q - 8), exact, as four packed half pairs in the K-slot order
 // (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of

@@ -652,28 +652,35 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  // A staging: chunk id -> (row, chunk); 32-bit element offsets
-  uint32_t a_off[A_PER_T];
+  // Staging through raw buffer loads: descriptors over the tile's A rows, over
+  // B from column n0 on and over the scales; per-lane byte offsets, the stage's
+  // K offset is uniform (an SGPR). Reads past a descriptor's end return zeros,
+  // which is what the packed rows past K of a partial last stage need.
+  const int rows = min(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)m0 * K, (uint32_t)rows * K * 2);
+  const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + n0, (uint32_t)((size_t)(K / 8) * N - n0) * 4);
+  const __amdgpu_buffer_rsrc_t s_src = buffer_rsrc(S, (uint32_t)((size_t)(K / group_size) * N * 2));
+  const int gshift = __builtin_ctz(group_size);
+  uint32_t a_voff[A_PER_T];
   int a_lds[A_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
     const int id = tid + i * NTHR;
     const int row = id / CHUNKS, ch = id % CHUNKS;
-    a_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + ch * 8);
+    a_voff[i] = (uint32_t)(min(row, rows - 1) * K + ch * 8) * 2;
     a_lds[i] = row * CHUNKS + swz(row, ch);
   }
   const int a_ch0 = tid % CHUNKS;   // the chunk index is the same for all of a thread's A chunks
   // B staging: 16-byte chunks (4 words, 4 adjacent columns of one packed row)
-  uint32_t b_off[B_PER_T];
+  uint32_t b_voff[B_PER_T];
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
     const int id = tid + i * NTHR;
     const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
-    b_off[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4));
+    b_voff[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4) - n0) * 4;
   }
-  const int kp_total = K / 8;
   // this lane's two output columns (scale columns)
-  const uint32_t s_off = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2);
+  const uint32_t s_voff = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2) * 2;
 
   // one stage of prefetched operands: A chunks, packed B chunks, the lane's scale pairs
   struct Regs {
@@ -683,42 +690,23 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
   };
   auto load_stage = [&](int kt, Regs& r) {
     const int k0 = kt * BK;
-    if (k0 + BK <= K) {
 #pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(A + k0 + a_off[i]);
-      const uint32_t* bbase = B + (size_t)(k0 / 8) * N;
+    for (int i = 0; i < A_PER_T; ++i) r.a[i] = buffer_load16(a_src, a_voff[i], (uint32_t)k0 * 2);
 #pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) r.b[i] = *reinterpret_cast<const u32x4_t*>(bbase + b_off[i]);
-    } else {
-      // partial last stage (K % 64 == 32): per-chunk clamped addresses; A chunks
-      // past K are zeroed when stored, so the clamped B rows never contribute
-      const int k = min(k0 + a_ch0 * 8, K - 8) - a_ch0 * 8;
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(A + k + a_off[i]);
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) {
-        const int b_kp = (tid + i * NTHR) / (BN / 4);
-        const int kp = min(k0 / 8 + b_kp, kp_total - 1);
-        r.b[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)(kp - b_kp) * N + b_off[i]);
-      }
-    }
+    for (int i = 0; i < B_PER_T; ++i) r.b[i] = buffer_load16(b_src, b_voff[i], (uint32_t)(k0 / 8) * N * 4);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      r.sc[s] = *reinterpret_cast<const uint32_t*>(S + (size_t)(min(k0 + 32 * s, K - 1) / group_size) * N + s_off);
+      r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)(min(k0 + 32 * s, K - 1) >> gshift) * N * 2);
+    // partial last stage (K % 64 == 32): A chunks past K must enter as zeros
+    if (k0 + BK > K && k0 + a_ch0 * 8 >= K) {
+#pragma unroll
+      for (int i = 0; i < A_PER_T; ++i) r.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
   };
   auto store_stage = [&](int kt, int buf, const Regs& r) {
-    const int k0 = kt * BK;
-    if (k0 + BK <= K) {
+    (void)kt;
 #pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
-    } else {
-      // partial last stage: chunks past K enter as zeros
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) {
-        const bool past = k0 + a_ch0 * 8 >= K;
-        lds_a[buf][a_lds[i]] = past ? u32x4_t{0u, 0u, 0u, 0u} : permute_k_0415(r.a[i]);
-      }
-    }
+    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) lds_b[buf][tid + i * NTHR] = r.b[i];
   };
@@ -896,6 +884,8 @@ static hipError_t launch_v3_tile(const W4Args& p, hipStream_t stream) {
 
 template <int BM, int BN, int WM, int WN, int MINB, int PD, int KG = 1>
 static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order = 0) {
+  // byte offsets into B and the scales are 32-bit buffer offsets
+  if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL || p.K / p.group_size * p.N * 2 > 0xFFFFFFFFLL) return hipErrorNotSupported;
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
   const int grid = ((tm * tn + 7) / 8) * 8;
   hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG>), dim3(grid), dim3(WM * WN * kWave * KG), 0, stream,
