@@ -150,7 +150,7 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
                     static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
                     static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
                     (int)expert_usage_stats_host[0], device_cus()};
-  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", 0), stream));
+  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", 3), stream));
 }
 
 qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,

@@ -5,9 +5,10 @@
 //
 // The problem is bound by reading each active expert's weights once, so the
 // schedule is weight-stationary: a work tile is (group, block of up to 128 of
-// its rows, 64 output columns). A workgroup of four waves owns a tile; each
+// its rows, 16 * W output columns). A workgroup of W waves owns a tile; each
 // wave streams a 16-column slice of the expert's weights from HBM exactly once
-// while it multiplies every row of the block against it.
+// while it multiplies every row of the block against it. All loads are raw
+// buffer loads (descriptor in SGPRs, uniform per-step offset).
 //   * Weight fragments go straight from HBM into registers, 16 bytes per lane
 //     per 32-deep K step (transpose_b puts K contiguous in both operands),
 //     several steps ahead. The rows' activation fragments are loaded once per
@@ -28,8 +29,6 @@ namespace qg {
 
 namespace {
 
-constexpr int GWAVES = 4;           // waves per workgroup
-constexpr int GBN = 16 * GWAVES;    // columns per work tile: 16 per wave
 constexpr int GMAXMT = 8;           // row tiles per work tile (128 rows)
 constexpr int GBM = 16 * GMAXMT;
 
@@ -45,11 +44,12 @@ constexpr int GBM = 16 * GMAXMT;
 // wave's loads are issued in step order and each step waits only for its own
 // (oldest) loads, the hardware's in-order load counter never forces a wave to
 // wait for a prefetch that lies further ahead.
-template <int MT, int D>
+template <int W, int MT, int D>
 __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                              int N, int K, int e, int r_begin, int rows, int n0) {
-  constexpr int FPW = (MT + GWAVES - 1) / GWAVES;   // activation fragments per wave per step
+  constexpr int FPW = (MT + W - 1) / W;   // activation fragments per wave per step
+  static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
@@ -59,12 +59,15 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   // per-lane byte offsets, the step's K offset is uniform (an SGPR)
   const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)r_begin * K, (uint32_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + (size_t)e * N * K, (uint32_t)N * K * 2);
+  // Wave w loads fragments w, w + W, ... Those past MT are not needed: their
+  // offset lies past the descriptor, so the load returns zeros without a memory
+  // request, and they land in LDS slots MT .. GMAXMT-1 that no MFMA reads.
   uint32_t a_voff[FPW];
   int a_frag[FPW];
 #pragma unroll
   for (int i = 0; i < FPW; ++i) {
-    a_frag[i] = min(wave + i * GWAVES, MT - 1);   // fragments past MT repeat the last one
-    a_voff[i] = (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2;
+    a_frag[i] = wave + i * W;
+    a_voff[i] = a_frag[i] < MT ? (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2 : 0x80000000u;
   }
   const uint32_t b_voff = (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8) * 2;
 
@@ -142,8 +145,8 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   }
 }
 
-template <int D, int OCC>
-__global__ __launch_bounds__(GWAVES * kWave, OCC) void grouped_bf16_kernel(
+template <int W, int D, int OCC>
+__global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
     int tiles_n) {
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(GWAVES * kWave, OCC) void grouped_bf16_kernel(
     const int rows = (int)(a_off[g + 1] - a_off[g]);
     if (ids[g] >= 0 && rows > 0) total += ((rows + GBM - 1) / GBM) * tiles_n;
   }
+  constexpr int GBN = 16 * W;   // columns per work tile: 16 per wave
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;
   const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
@@ -175,42 +179,44 @@ __global__ __launch_bounds__(GWAVES * kWave, OCC) void grouped_bf16_kernel(
     const int r_begin = (int)a_off[g] + chunk * GBM;
     const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
     const int n0 = nt * GBN;
-    // Tiles of more than four row tiles load two activation fragments per wave
-    // per step, so they run half as many steps ahead: the same registers and
-    // about the same bytes in flight.
+    // With four waves, tiles of more than four row tiles load two activation
+    // fragments per wave per step, so they run half as many steps ahead: the
+    // same registers and about the same bytes in flight.
+    constexpr int D5 = W >= 8 ? D : D / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile<1, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 2: grouped_tile<2, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 3: grouped_tile<3, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 4: grouped_tile<4, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 5: grouped_tile<5, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 6: grouped_tile<6, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 7: grouped_tile<7, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      default: grouped_tile<8, D / 2>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 1: grouped_tile<W, 1, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 2: grouped_tile<W, 2, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 3: grouped_tile<W, 3, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 4: grouped_tile<W, 4, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 5: grouped_tile<W, 5, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 6: grouped_tile<W, 6, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 7: grouped_tile<W, 7, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      default: grouped_tile<W, 8, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
     }
   }
 }
 
-template <int D, int OCC>
+template <int W, int D, int OCC>
 static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
   const int wg_per_cu = OCC;
-  const int tiles_n = (int)((p.N + GBN - 1) / GBN);
+  const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
   const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
-  hipLaunchKernelGGL((grouped_bf16_kernel<D, OCC>), dim3(grid), dim3(GWAVES * kWave), 0, stream, p.C, p.A, p.a_offsets,
+  hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A, p.a_offsets,
                      p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream) {
   switch (variant) {
-    case 0: return launch_g<8, 2>(p, stream);
-    case 1: return launch_g<4, 2>(p, stream);
-    case 2: return launch_g<8, 1>(p, stream);
-    case 3: return launch_g<12, 2>(p, stream);
-    case 4: return launch_g<16, 2>(p, stream);
-    case 5: return launch_g<8, 3>(p, stream);
-    case 6: return launch_g<12, 3>(p, stream);
-    case 7: return launch_g<24, 2>(p, stream);
+    // <waves (16 columns each), steps ahead, workgroups per CU>
+    case 0: return launch_g<4, 8, 2>(p, stream);
+    case 1: return launch_g<4, 4, 2>(p, stream);
+    case 2: return launch_g<4, 8, 1>(p, stream);
+    case 3: return launch_g<4, 12, 2>(p, stream);
+    case 4: return launch_g<4, 8, 3>(p, stream);
+    case 5: return launch_g<8, 8, 1>(p, stream);
+    case 6: return launch_g<8, 12, 1>(p, stream);
+    case 7: return launch_g<8, 16, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
