@@ -10,6 +10,8 @@ Sources (Modular MAX API reference pages):
     group_size K-elements per scale and pack_factor 4-bit codes per uint32.
   * "grouped_matmul_sm100_persistent" (linalg / grouped_matmul_sm100):
     grouped GEMM routed by a_offsets / expert_ids / expert_usage_stats.
+  * Both together: the grouped W4A16 GEMM (experts in the first page's
+    packed format, routed as on the second).
   * "k_matmul_ragged_paged_scale" (nn / kv_cache_ragged): scaled matmul over
     ragged rows whose result is written into a paged KV cache.
 
@@ -19,11 +21,12 @@ from .numerics import (round_to_f16, round_to_bf16, round_to, decode_f16, decode
                        decode_e4m3, f16_bits_of, bf16_bits_of, F16, BF16)
 from .w4 import dequant_w4, qgemm_w4
 from .grouped import grouped_gemm
+from .grouped_w4 import grouped_gemm_w4
 from .kproj import k_matmul_ragged_paged_scale, kproj_rows, token_slots
 
 __all__ = [
     "round_to_f16", "round_to_bf16", "round_to", "decode_f16", "decode_bf16", "decode_e4m3",
     "f16_bits_of", "bf16_bits_of", "F16", "BF16",
-    "dequant_w4", "qgemm_w4", "grouped_gemm", "k_matmul_ragged_paged_scale", "kproj_rows",
+    "dequant_w4", "qgemm_w4", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale", "kproj_rows",
     "token_slots",
 ]

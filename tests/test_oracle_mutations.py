@@ -79,3 +79,30 @@ def test_kproj_mutations_are_caught(monkeypatch):
     monkeypatch.setattr(okp, "kproj_rows", bad_rows)
     with pytest.raises(AssertionError):
         tkp.test_brute_force_loops()
+
+
+def _grouped_w4_variant(kind):
+    from oracle import grouped_w4 as og
+    orig = og.grouped_gemm_w4
+
+    def f(c_bits, a_bits, a_offsets, b_packed, scales_bits, expert_ids, usage_stats, group_size):
+        ids = np.array(expert_ids, dtype=np.int32, copy=True)
+        if kind == "expert_is_group":
+            ids = np.where(ids >= 0, np.arange(len(ids)) % np.asarray(b_packed).shape[0], ids).astype(np.int32)
+        elif kind == "no_skip":
+            ids = np.where(ids < 0, 0, ids).astype(np.int32)
+        return orig(c_bits, a_bits, a_offsets, b_packed, scales_bits, ids, usage_stats, group_size)
+    return f
+
+
+@pytest.mark.parametrize("kind", ["expert_is_group", "no_skip"])
+def test_grouped_w4_mutation_is_caught(kind, monkeypatch):
+    import test_oracle_grouped_w4 as tgw
+    monkeypatch.setattr(oracle, "grouped_gemm_w4", _grouped_w4_variant(kind))
+    failures = 0
+    for pin in (tgw.test_skip_semantics, tgw.test_each_group_uses_its_expert):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, kind
