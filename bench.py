@@ -7,7 +7,8 @@ launches). Weights, scales, activations and outputs are rotated over enough
 device copies (>= 1 GiB) that every launch reads its operands from HBM, not
 from the 256 MB Infinity Cache or the L2s.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|square|grouped|kproj]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config decode|prefill|square|grouped|grouped_w4|kproj]
 
 Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
 steps (the decode shapes are bound by HBM); TFLOP/s is reported beside it. The
@@ -48,6 +49,7 @@ KERNEL_SOURCES = {
     "prefill": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "square": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
+    "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
 }
 MEASURED_TRAFFIC = {
@@ -81,7 +83,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "kproj"])
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "grouped_w4",
+                                                           "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -287,6 +290,72 @@ class GroupedBF16:
         return None   # HBM-bound: the copy of the same byte count is the context number
 
 
+class GroupedW4:
+    """64 int4 experts (group 128), 4096 routed rows, K=2048, N=1408, 10% of groups skipped (seed 6)."""
+    kernel = "w4_grouped_kernel"
+    bound = "hbm"
+    dtype = "f16"
+
+    def __init__(self, torch, q, synth):
+        self.torch, self.q = torch, q
+        d = synth.grouped_w4_inputs()
+        self.d = d
+        T, K = d.a.shape
+        E, _, N = d.b.shape
+        self.T, self.K, self.N, self.E = T, K, N, E
+        off = d.a_offsets.astype(np.int64)
+        rows = off[1:] - off[:-1]
+        act = (d.expert_ids >= 0) & (rows > 0)
+        self.active_rows = int(rows[act].sum())
+        self.active_experts = len(set(d.expert_ids[act].tolist()))
+        gs = d.group_size
+        self.bytes_per_step = (self.active_rows * K * 2 + self.active_experts * (K * N // 2 + (K // gs) * N * 2)
+                               + self.active_rows * N * 2 + (E + 1) * 4 + E * 4)
+        self.flops_per_step = 2 * self.active_rows * N * K
+        self.R = max(1, math.ceil(ROTATE_BYTES / (d.b.nbytes + d.scales.nbytes + d.a.nbytes + T * N * 2)))
+        dev = torch.device("cuda")
+        a = torch.from_numpy(d.a.view(np.int16)).to(dev).view(torch.float16)
+        b = torch.from_numpy(d.b.view(np.int32)).to(dev)
+        s = torch.from_numpy(d.scales.view(np.int16)).to(dev).view(torch.float16)
+        off_t = torch.from_numpy(d.a_offsets.view(np.int32)).to(dev)
+        ids = torch.from_numpy(d.expert_ids).to(dev)
+        self.slots = [(torch.empty(T, N, dtype=torch.float16, device=dev), a.clone(), off_t, b.clone(), s.clone(),
+                       ids) for _ in range(self.R)]
+        self.usage = [int(v) for v in d.usage]
+        self.name = f"grouped_w4a16_E{E}_T{T}_K{K}_N{N}_gs{gs}_skip10pct"
+
+    def launches(self, step):
+        c, a, off, b, s, ids = self.slots[step % self.R]
+        return [lambda: self.q.grouped_gemm_w4(c, a, off, b, s, ids, self.usage, self.d.group_size)]
+
+    def unit_bytes(self):
+        return self.bytes_per_step
+
+    def unit_flops(self):
+        return self.flops_per_step
+
+    def cpu_sample(self):
+        import oracle
+        d = self.d
+        G = 8
+        usage = np.array([d.usage[0], G], np.uint32)
+        c0 = np.zeros((self.T, self.N), np.uint16)
+        oracle.grouped_gemm_w4(c0, d.a, d.a_offsets, d.b, d.scales, d.expert_ids, usage, d.group_size)
+        off = d.a_offsets.astype(np.int64)
+        rows = sum(int(off[g + 1] - off[g]) for g in range(G) if d.expert_ids[g] >= 0)
+        ne = sum(1 for g in range(G) if d.expert_ids[g] >= 0)
+        byt = rows * self.K * 2 + ne * (self.N * self.K // 2 + (self.K // d.group_size) * self.N * 2) + rows * self.N * 2
+        return 2 * rows * self.N * self.K, byt, f"first {G} of {self.E} groups"
+
+    def describe(self):
+        return {"workload": self.name, "experts": self.E, "routed_rows": self.T, "K": self.K, "N": self.N,
+                "group_size": self.d.group_size, "pack_factor": 8, "active_rows": self.active_rows,
+                "active_experts": self.active_experts, "rotating_copies": self.R}
+
+    def dense_equivalent(self):
+        return None
+
+
 class KProjFP8:
     """8 sequences (lengths U[1,1024], seed 5: T=4312), hidden 4096 bf16, W [4096,1024] e4m3 with 1x128x128
     block scales, bf16 keys written into a paged cache (page 128, 2 layers, layer 1)."""
@@ -404,7 +473,7 @@ def context_numbers(torch, wl, steps):
 
 WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
-             "grouped": GroupedBF16, "kproj": KProjFP8}
+             "grouped": GroupedBF16, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 
 def main():

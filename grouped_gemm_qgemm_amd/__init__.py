@@ -9,6 +9,8 @@ built, load() raises: there is no fallback path.
 Entry points (same names as the C ABI):
     qgemm_w4(c, a, b_packed, scales, group_size=128, pack_factor=8)
     grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
+    grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats,
+                    group_size=128, pack_factor=8)
     k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
                                 weight_scale, kv_blocks, cache_lengths, page_table,
                                 layer_idx, scales_granularity_mnk=(1, 128, 128))
@@ -21,7 +23,7 @@ import os
 
 import torch
 
-__all__ = ["load", "QgError", "qgemm_w4", "grouped_gemm", "k_matmul_ragged_paged_scale",
+__all__ = ["load", "QgError", "qgemm_w4", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
            "status_string", "LIB_PATH", "QG"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
@@ -74,6 +76,9 @@ def load(path: str | None = None):
     lib.grouped_gemm.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                  ctypes.c_void_p]
     lib.grouped_gemm.restype = ctypes.c_int
+    lib.grouped_gemm_w4.argtypes = [T, T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    lib.grouped_gemm_w4.restype = ctypes.c_int
     lib.k_matmul_ragged_paged_scale.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(QgPagedKV), ctypes.c_uint32, ctypes.c_void_p]
     lib.k_matmul_ragged_paged_scale.restype = ctypes.c_int
@@ -147,6 +152,20 @@ def grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b
                           ctypes.byref(describe(a_offsets, _u32(a_offsets))), ctypes.byref(describe(b)),
                           ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)),
                           _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats, group_size: int = 128,
+                    pack_factor: int = 8, stream=None, raise_on_error: bool = True) -> int:
+    """Rows of each active, non-skipped group g: C = A . dequant(B[expert_ids[g]], scales[expert_ids[g]]) (f16)."""
+    lib = load()
+    usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
+    st = lib.grouped_gemm_w4(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                             ctypes.byref(describe(a_offsets, _u32(a_offsets))),
+                             ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
+                             ctypes.byref(describe(expert_ids)), usage, group_size, pack_factor, _stream(stream))
     if raise_on_error:
         _check(st)
     return st

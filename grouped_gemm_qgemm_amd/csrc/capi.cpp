@@ -153,6 +153,46 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
   return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", 3), stream));
 }
 
+qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                          const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
+                          const uint32_t* expert_usage_stats_host, int32_t group_size, int32_t pack_factor,
+                          hipStream_t stream) {
+  if (!c || !a || !a_offsets || !b_packed || !scales || !expert_ids || !expert_usage_stats_host)
+    return QG_ERR_NULL;
+  if (c->rank != 2 || a->rank != 2 || a_offsets->rank != 1 || b_packed->rank != 3 || scales->rank != 3 ||
+      expert_ids->rank != 1)
+    return QG_ERR_RANK;
+  qg_status st;
+  if ((st = check_tensor(c, 2, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(a, 2, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(a_offsets, 1, QG_U32)) != QG_OK) return st;
+  if ((st = check_tensor(b_packed, 3, QG_U32)) != QG_OK) return st;
+  if ((st = check_tensor(scales, 3, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(expert_ids, 1, QG_I32)) != QG_OK) return st;
+  if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
+  if (group_size <= 0) return QG_ERR_INVALID_ARG;
+  const int64_t T = a->shape[0], K = a->shape[1], N = c->shape[1];
+  const int64_t E = b_packed->shape[0], G = expert_ids->shape[0];
+  if (c->shape[0] != T) return QG_ERR_SHAPE;
+  if (K % group_size != 0) return QG_ERR_SHAPE;
+  if (b_packed->shape[1] * pack_factor != K || b_packed->shape[2] != N) return QG_ERR_SHAPE;
+  if (scales->shape[0] != E || scales->shape[1] != K / group_size || scales->shape[2] != N) return QG_ERR_SHAPE;
+  if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
+  if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
+    return QG_ERR_UNSUPPORTED;
+  if (N % 8 != 0) return QG_ERR_ALIGN;
+  const uint32_t num_active = expert_usage_stats_host[1];
+  if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
+  if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || E > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (T == 0 || N == 0 || num_active == 0) return QG_OK;
+  if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of the routed rows
+  qg::W4GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
+                      static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
+                      static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
+                      T, N, K, E, group_size, (int)num_active};
+  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 2), stream));
+}
+
 qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
                                       const qg_tensor* weight, const qg_tensor* input_scale,
                                       const qg_tensor* weight_scale,

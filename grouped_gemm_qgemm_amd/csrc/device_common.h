@@ -62,6 +62,45 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Locates work tile t of a routed (grouped) GEMM. Group g < num_active with
+// ids[g] >= 0 and rows = a_off[g+1] - a_off[g] > 0 owns ceil(rows / bm) * tiles_n
+// consecutive tiles, in group order. The calling wave scans 64 groups at a
+// time (one group per lane, prefix sum by shuffles, ballot for the owner);
+// every lane gets the same result: the group (-1 past the last tile) and the
+// tile's index within it.
+struct TileLoc {
+  int g, local;
+};
+
+__device__ __forceinline__ TileLoc locate_tile(int t, const uint32_t* __restrict__ a_off,
+                                               const int32_t* __restrict__ ids, int num_active, int bm,
+                                               int tiles_n) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int g0 = 0; g0 < num_active; g0 += 64) {
+    const int g = g0 + lane;
+    int cnt = 0;
+    if (g < num_active) {
+      const int rows = (int)(a_off[g + 1] - a_off[g]);
+      cnt = (ids[g] >= 0 && rows > 0) ? ((rows + bm - 1) / bm) * tiles_n : 0;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const unsigned long long hit = __ballot(t < base + incl);
+    if (hit) {
+      const int first = __ffsll((long long)hit) - 1;
+      const int excl = __shfl(incl - cnt, first);
+      return TileLoc{g0 + first, t - base - excl};
+    }
+    base += __shfl(incl, 63);
+  }
+  return TileLoc{-1, 0};
+}
+
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
 // weights (q - 8), exact, as four packed half pairs in the K-slot order
 // (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of

@@ -16,6 +16,18 @@ struct W4Args {
   int group_size;
 };
 
+struct W4GroupedArgs {
+  uint16_t* C;                // f16 [T, N]
+  const uint16_t* A;          // f16 [T, K]
+  const uint32_t* a_offsets;  // [G+1]
+  const uint32_t* B;          // u32 [E, K/8, N]
+  const uint16_t* S;          // f16 [E, K/group_size, N]
+  const int32_t* expert_ids;  // [G]
+  int64_t T, N, K, E;
+  int group_size;
+  int num_active;
+};
+
 struct GroupedArgs {
   uint16_t* C;              // bf16 [T, N]
   const uint16_t* A;        // bf16 [T, K]
@@ -50,6 +62,9 @@ hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream);
 hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream);
 
 hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream);
+
+// Grouped W4A16 (int4 experts, fp16 activations).
+hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t stream);
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream);
 

@@ -599,10 +599,20 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_ke
 // their accumulators through LDS at the end: the same tile and the same unpack
 // work per wave, twice the waves per SIMD to cover each other's waits (for
 // shapes with about one tile per CU).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
-    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
+// LDS of one fourth-design tile: per K group, two stages of A chunks and of packed B.
+template <int BM, int BN, int KG>
+struct W4TileLds {
+  u32x4_t a[KG][2][BM * CHUNKS];
+  u32x4_t b[KG][2][(BK / 8) * BN / 4];
+};
+
+// One BM x BN output tile of the fourth design: rows m0 .. m0+BM-1 (those < M)
+// and columns n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG>
+__device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
+                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
+                                             int M, int N, int K, int group_size, int m0, int n0,
+                                             W4TileLds<BM, BN, KG>& lds) {
   constexpr int NTHR = WAVES_M * WAVES_N * kWave;   // threads of one K group
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
@@ -615,42 +625,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
   constexpr int B_PER_T = B_CHUNKS / NTHR;   // 16-byte packed chunks per thread
   static_assert(B_CHUNKS % NTHR == 0, "B staging");
 
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a_all[KG][2][BM * CHUNKS];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b_all[KG][2][(BK / 8) * BN / 4];
-
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = wave_all / (WAVES_M * WAVES_N);        // K group
   const int wave = wave_all % (WAVES_M * WAVES_N);      // wave within the group
   const int tid = threadIdx.x % NTHR;                  // thread within the group
-  auto& lds_a = lds_a_all[kg];
-  auto& lds_b = lds_b_all[kg];
+  auto& lds_a = lds.a[kg];
+  auto& lds_b = lds.b[kg];
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int h = lane >> 5, c32 = lane & 31;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  // tile order within an XCD's run: 0 = M fastest, 1 = N fastest, else groups
-  // of `order` row panels swept across N
-  int tm, tn;
-  if (order == 0) {
-    tm = lin % tiles_m;
-    tn = lin / tiles_m;
-  } else if (order == 1) {
-    tm = lin / tiles_n;
-    tn = lin % tiles_n;
-  } else {
-    const int span = order * tiles_n;
-    const int first = (lin / span) * order;
-    const int gm = min(tiles_m - first, order);
-    const int r = lin % span;
-    tm = first + r % gm;
-    tn = r / gm;
-  }
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
 
   // Staging through raw buffer loads: descriptors over the tile's A rows, over
   // B from column n0 on and over the scales; per-lane byte offsets, the stage's
@@ -775,11 +758,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
         sc_cur[1] = r.sc[1];
       }
     }
-    // group 1 hands its partial sums to group 0 through the (now free) A
+    // group 1 hands its partial sums to group 0 through the (now free) stage
     // buffers, two row tiles at a time; lane-major so the accesses are
     // conflict-free
-    float* red = reinterpret_cast<float*>(&lds_a_all[0][0][0]);
-    static_assert(sizeof(lds_a_all) >= 64 * NTHR * sizeof(float), "reduction space");
+    float* red = reinterpret_cast<float*>(&lds);
+    static_assert(sizeof(W4TileLds<BM, BN, KG>) >= 64 * NTHR * sizeof(float), "reduction space");
 #pragma unroll
     for (int p = 0; p < MT / 2; ++p) {
       if (kg == 1) {
@@ -870,6 +853,89 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
               (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
       }
     }
+  }
+}
+
+// Dense fourth-design kernel: one tile per workgroup, tile order within each
+// XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
+// swept across N.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
+  __shared__ W4TileLds<BM, BN, KG> lds;
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  int tm, tn;
+  if (order == 0) {
+    tm = lin % tiles_m;
+    tn = lin / tiles_m;
+  } else if (order == 1) {
+    tm = lin / tiles_n;
+    tn = lin % tiles_n;
+  } else {
+    const int span = order * tiles_n;
+    const int first = (lin / span) * order;
+    const int gm = min(tiles_m - first, order);
+    const int r = lin % span;
+    tm = first + r % gm;
+    tn = r / gm;
+  }
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds);
+}
+
+// Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
+// rows a_off[g] .. a_off[g+1]-1) is cut into ceil(rows / BM) row chunks times
+// ceil(N / BN) column tiles; tiles are numbered group by group and each XCD
+// takes a contiguous run, so a group's column tiles share that XCD's L2 for its
+// activation rows. Expert e's packed words and scales are b[e] ([K/8, N]) and
+// s[e] ([K/group_size, N]). Rows of skipped groups are never written. The grid
+// is an upper bound on the tile count; workgroups past the last tile exit.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
+    const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
+    int group_size, int num_active, int tiles_n) {
+  __shared__ W4TileLds<BM, BN, KG> lds;
+  const int per = gridDim.x >> 3;
+  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const TileLoc loc = locate_tile(t, a_off, ids, num_active, BM, tiles_n);
+  if (loc.g < 0) return;
+  const int chunk = loc.local / tiles_n, nt = loc.local - chunk * tiles_n;
+  const int e = ids[loc.g];
+  const int r_begin = (int)a_off[loc.g] + chunk * BM;
+  const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
+  const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, 1, KG>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
+                                               S + e * spe, rows, N, K, group_size, 0, nt * BN, lds);
+}
+
+template <int BM, int BN, int WM, int WN, int MINB, int KG>
+static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream) {
+  if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL) return hipErrorNotSupported;
+  const int tiles_n = (int)((p.N + BN - 1) / BN);
+  // every group has at most ceil(rows / BM) <= rows / BM + 1 row chunks
+  const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
+  if (bound > INT32_MAX / 2) return hipErrorNotSupported;
+  const int grid = (int)((bound + 7) / 8 * 8);
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
+                     stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
+                     p.num_active, tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t stream) {
+  switch (variant) {
+    case 0: return launch_grouped_tile<128, 256, 1, 4, 1, 2>(p, stream);
+    case 1: return launch_grouped_tile<128, 256, 1, 4, 2, 1>(p, stream);
+    case 2: return launch_grouped_tile<64, 256, 1, 4, 2, 1>(p, stream);
+    case 3: return launch_grouped_tile<64, 256, 1, 4, 1, 2>(p, stream);
+    case 4: return launch_grouped_tile<64, 256, 1, 4, 3, 1>(p, stream);
+    case 5: return launch_grouped_tile<32, 256, 1, 4, 4, 1>(p, stream);
+    case 6: return launch_grouped_tile<64, 128, 1, 2, 4, 1>(p, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -1,7 +1,7 @@
 /*
  * qgemm.h - C ABI of the MI355X (gfx950) dequant-in-kernel GEMM library.
  *
- * Three operations, each a GEMM whose B operand holds low-precision weights
+ * Four operations, each a GEMM whose B operand holds low-precision weights
  * that the kernel dequantizes on the fly:
  *
  *   qgemm_w4                     4-bit group-quantized weights, fp16 activations
@@ -11,6 +11,8 @@
  *   k_matmul_ragged_paged_scale  block-scaled fp8 weights, ragged rows, output
  *                                written into a paged KV cache
  *                                (Modular MAX page "k_matmul_ragged_paged_scale")
+ *   grouped_gemm_w4              the routing of grouped_gemm over experts stored in
+ *                                qgemm_w4's packed 4-bit format
  *
  * Conventions shared by every entry point
  *   - Tensor data pointers are DEVICE pointers unless a comment says "host".
@@ -123,6 +125,38 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
                        const qg_tensor* b, const qg_tensor* expert_ids,
                        const uint32_t* expert_usage_stats_host, int32_t transpose_b,
                        hipStream_t stream);
+
+/*
+ * grouped_gemm_w4 - per-group W4A16 GEMM over routed rows (MoE with 4-bit experts)
+ *
+ * The routing of "grouped_matmul_sm100_persistent" (Args: a_offsets, expert_ids
+ * with negative entries skipping the group, expert_usage_stats[1] = active count)
+ * over experts stored in the format of "multistage_gemm_q" (Parameters:
+ * pack_factor = 8 codes per uint32, group_size K elements per scale). Neither page
+ * defines the combination; this is the plain joint reading: for g < num_active
+ * with e = expert_ids[g] >= 0, rows a_offsets[g] .. a_offsets[g+1]-1 of c are set to
+ * round_fp16(A[rows] . W_e) with W_e[k][n] = (q - 8) * scales[e][k / group_size][n],
+ * q = code k % 8 of b_packed[e][k / 8][n] (bits 4(k%8) .. 4(k%8)+3). All other
+ * rows of c keep their prior content.
+ *
+ *   c          f16 [T, N]
+ *   a          f16 [T, K]
+ *   a_offsets  u32 [G + 1]   non-decreasing, a_offsets[num_active] <= T
+ *   b_packed   u32 [E, K / 8, N]
+ *   scales     f16 [E, K / group_size, N]
+ *   expert_ids i32 [G]       each < E, or negative to skip
+ *   expert_usage_stats_host  HOST u32[2]: [1] = num_active (<= G); [0] a hint only
+ *   group_size multiple of 32 and a power of two, at most 256, dividing K
+ *   pack_factor must be 8
+ *
+ * N must be a multiple of 8 (QG_ERR_ALIGN). Accumulation is fp32; results are
+ * rounded to fp16 (nearest-even). The device-side tables are not re-validated:
+ * offsets past T, or expert ids >= E, are undefined behaviour.
+ */
+qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                          const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
+                          const uint32_t* expert_usage_stats_host, int32_t group_size,
+                          int32_t pack_factor, hipStream_t stream);
 
 /* A paged KV cache collection (keys and values of every layer). */
 typedef struct {

@@ -30,7 +30,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"qgemm_w4", "grouped_gemm", "k_matmul_ragged_paged_scale", "qg_status_string"} <= set(names)
+    assert {"qgemm_w4", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
+            "qg_status_string"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     for n in names:
@@ -123,6 +124,33 @@ def test_grouped_rejections(lib):
     u = (ctypes.c_uint32 * 2)(8, 4)
     assert lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
                             ctypes.byref(ids), None, 1, None) == QG.ERR_NULL
+
+
+def gw_call(lib, c, a, off, b, s, ids, usage, gs=128, pf=8):
+    u = (ctypes.c_uint32 * 2)(*usage)
+    return lib.grouped_gemm_w4(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
+                               ctypes.byref(s), ctypes.byref(ids), u, gs, pf, None)
+
+
+def test_grouped_w4_rejections(lib):
+    bb = Buf()
+    T, K, N, E, G = 32, 256, 48, 4, 4
+    c, a = bb.t((T, N), QG.F16), bb.t((T, K), QG.F16)
+    off, ids = bb.t((G + 1,), QG.U32), bb.t((G,), QG.I32)
+    b, s = bb.t((E, K // 8, N), QG.U32), bb.t((E, K // 128, N), QG.F16)
+    assert gw_call(lib, c, a, off, bb.t((E * K // 8, N), QG.U32), s, ids, [8, 4]) == QG.ERR_RANK
+    assert gw_call(lib, c, bb.t((T, K), QG.BF16), off, b, s, ids, [8, 4]) == QG.ERR_DTYPE
+    assert gw_call(lib, c, a, off, b, bb.t((E, K // 64, N), QG.F16), ids, [8, 4]) == QG.ERR_SHAPE
+    assert gw_call(lib, c, a, off, b, bb.t((E + 1, K // 128, N), QG.F16), ids, [8, 4]) == QG.ERR_SHAPE
+    assert gw_call(lib, c, a, bb.t((G,), QG.U32), b, s, ids, [8, 4]) == QG.ERR_SHAPE
+    assert gw_call(lib, c, a, off, b, s, ids, [8, 4], pf=4) == QG.ERR_UNSUPPORTED
+    assert gw_call(lib, c, a, off, b, bb.t((E, K // 96, N), QG.F16), ids, [8, 4], gs=96) == QG.ERR_SHAPE
+    assert gw_call(lib, c, a, off, b, s, ids, [8, 5]) == QG.ERR_INVALID_ARG
+    assert gw_call(lib, c, a, off, b, s, ids, [8, 0]) == QG.OK       # nothing active: no-op
+    assert gw_call(lib, c, a, off, b, s, ids, [8, 4], gs=0) == QG.ERR_INVALID_ARG
+    u = (ctypes.c_uint32 * 2)(8, 4)
+    assert lib.grouped_gemm_w4(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
+                               ctypes.byref(s), ctypes.byref(ids), None, 128, 8, None) == QG.ERR_NULL
 
 
 def kp_call(lib, h, offs, w, isc, wsc, blocks, layer, gran=(1, 128, 128), cl=1, pt=1, maxp=2):
