@@ -101,6 +101,25 @@ __device__ __forceinline__ TileLoc locate_tile(int t, const uint32_t* __restrict
   return TileLoc{-1, 0};
 }
 
+// Total work tiles of a routed GEMM (see locate_tile), by the same wave scan.
+__device__ __forceinline__ int count_tiles(const uint32_t* __restrict__ a_off, const int32_t* __restrict__ ids,
+                                           int num_active, int bm, int tiles_n) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int g0 = 0; g0 < num_active; g0 += 64) {
+    const int g = g0 + lane;
+    int cnt = 0;
+    if (g < num_active) {
+      const int rows = (int)(a_off[g + 1] - a_off[g]);
+      cnt = (ids[g] >= 0 && rows > 0) ? ((rows + bm - 1) / bm) * tiles_n : 0;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
+    total += cnt;
+  }
+  return total;
+}
+
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
 // weights (q - 8), exact, as four packed half pairs in the K-slot order
 // (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of

@@ -19,9 +19,10 @@
 //     the tiles of one group are adjacent in the tile order and every XCD takes
 //     a contiguous range of it, so those re-reads hit that XCD's L2.
 //   * 16x16x32 bf16 MFMA, fp32 accumulation, bf16 round-to-nearest-even.
-//   * The tile list is derived on the device from a_offsets / expert_ids by
-//     each workgroup walking the group table once (groups are visited in
-//     order). Rows of skipped or unlisted groups are never written.
+//   * The tile list is derived on the device from a_offsets / expert_ids: each
+//     wave scans the group table 64 groups at a time (one per lane) to count
+//     the tiles and to find each tile's group. Rows of skipped or unlisted
+//     groups are never written.
 #include "device_common.h"
 #include "launch.h"
 
@@ -152,29 +153,18 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
 
-  // ---- tile count (every workgroup walks the same small table) ----
-  int total = 0;
-  for (int g = 0; g < num_active; ++g) {
-    const int rows = (int)(a_off[g + 1] - a_off[g]);
-    if (ids[g] >= 0 && rows > 0) total += ((rows + GBM - 1) / GBM) * tiles_n;
-  }
   constexpr int GBN = 16 * W;   // columns per work tile: 16 per wave
+  // every wave scans the group table itself (one group per lane), so no
+  // workgroup waits on a serial walk of it
+  const int total = count_tiles(a_off, ids, num_active, GBM, tiles_n);
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;
   const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
 
-  int g = 0, g_first = 0;  // group cursor and the first tile index of group g
   for (int t = lo + (int)(blockIdx.x >> 3); t < hi; t += per_xcd) {
-    int cnt;
-    for (;;) {
-      const int rows = (int)(a_off[g + 1] - a_off[g]);
-      cnt = (ids[g] >= 0 && rows > 0) ? ((rows + GBM - 1) / GBM) * tiles_n : 0;
-      if (t < g_first + cnt) break;
-      g_first += cnt;
-      ++g;
-    }
-    const int local = t - g_first;
-    const int chunk = local / tiles_n, nt = local % tiles_n;
+    const TileLoc loc = locate_tile(t, a_off, ids, num_active, GBM, tiles_n);
+    const int g = loc.g;
+    const int chunk = loc.local / tiles_n, nt = loc.local % tiles_n;
     const int e = ids[g];
     const int r_begin = (int)a_off[g] + chunk * GBM;
     const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
