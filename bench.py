@@ -54,11 +54,12 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9019628, "f9a6bf8fcb4f39f6"),
-    "prefill": (248964768, "f3a0699db4f89d07"),
-    "square": (101390528, "f3a0699db4f89d07"),
-    "grouped": (368552739, "2784f1cfb0e85fb9"),
-    "kproj": (85664619, "f59c03064c0ffb65"),
+    "decode": (9019628, "7eea08f6a447e2d2"),
+    "prefill": (302821291, "87eb1f9f22793be5"),
+    "square": (101378817, "87eb1f9f22793be5"),
+    "grouped": (367954489, "0ae87ba6f551c5aa"),
+    "grouped_w4": (117908837, "87eb1f9f22793be5"),
+    "kproj": (85578290, "ff0a5e271101b025"),
 }
 
 
