@@ -111,10 +111,10 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
     return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
   }
   // 128 x 256 tiles of 32x32x16 MFMAs, each XCD sweeping groups of eight row
-  // panels across N: with fewer than four tiles per CU one workgroup of two
-  // K groups per CU (16), otherwise two workgroups of one K group (15)
+  // panels across N: with at most one tile per CU one workgroup of two K
+  // groups per CU (16), otherwise two workgroups of one K group (15)
   const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  int dflt = tiles < 4 * (int64_t)device_cus() ? 16 : 15;
+  int dflt = tiles <= (int64_t)device_cus() ? 16 : 15;
   if (K / 8 * N * 4 > 0xFFFFFFFFLL) dflt = 9;   // beyond 32-bit buffer offsets: the third design
   return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
 }
@@ -190,7 +190,7 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
                       static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
                       static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
                       T, N, K, E, group_size, (int)num_active};
-  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 2), stream));
+  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 8), stream));
 }
 
 qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,

@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
 // one wave's LDS and load waits are covered by the others' MFMAs; with one wave
 // per SIMD those waits were exposed on every stage. The first min(512, threads)
 // threads stage the weight tile (RPT K rows of 16 columns each).
-template <int WM>
+template <int WM, int PD>
 __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
     const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
@@ -462,19 +462,23 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
   const int ng = tid & 7, kq = (tid >> 3) & (WT / 8 - 1);  // 16-column group, K-row group
   const uint32_t w_off = (uint32_t)(RPT * kq * N + n0 + 16 * ng);
 
-  u32x4_t ra[A_PER_T];
-  u32x4_t rw[RPT];
-  auto load_stage = [&](int kb) {
+  // staging registers: PD stages of loads in flight
+  u32x4_t ra[PD][A_PER_T];
+  u32x4_t rw[PD][RPT];
+  // With two stages in flight every thread issues every load (threads past the
+  // weight stagers read weight rows they never store): the compiler's in-order
+  // load counting then sees one fixed sequence and waits only for the older set.
+  auto load_stage = [&](int kb, u32x4_t (&ra)[A_PER_T], u32x4_t (&rw)[RPT]) {
     const int k0 = kb * KBK;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
-    if (wstage) {
+    if (PD == 2 || wstage) {
       const uint8_t* wb = W + (size_t)k0 * N;
 #pragma unroll
       for (int r = 0; r < RPT; ++r) rw[r] = *reinterpret_cast<const u32x4_t*>(wb + w_off + r * N);
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const u32x4_t (&ra)[A_PER_T], const u32x4_t (&rw)[RPT]) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = ra[i];
     if (wstage) {
@@ -548,16 +552,38 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     }
   };
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
-    if (more) load_stage(kb + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kb, kb & 1);
-    if (more) store_stage((kb + 1) & 1);
+  if constexpr (PD == 1) {
+    load_stage(0, ra[0], rw[0]);
+    store_stage(0, ra[0], rw[0]);
     __syncthreads();
+    for (int kb = 0; kb < KB; ++kb) {
+      const bool more = kb + 1 < KB;
+      if (more) load_stage(kb + 1, ra[0], rw[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kb, kb & 1);
+      if (more) store_stage((kb + 1) & 1, ra[0], rw[0]);
+      __syncthreads();
+    }
+  } else {
+    // two stages in flight: stage kb + 2 is requested while stage kb is
+    // multiplied, stage kb + 1 (already in registers) is stored after it
+    // (loads past the last stage re-read it; the copies stored from them are never read)
+    load_stage(0, ra[0], rw[0]);
+    load_stage(min(1, KB - 1), ra[1], rw[1]);
+    store_stage(0, ra[0], rw[0]);
+    __syncthreads();
+    for (int kb = 0; kb < KB; kb += 2) {
+      load_stage(min(kb + 2, KB - 1), ra[0], rw[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kb, 0);
+      store_stage(1, ra[1], rw[1]);
+      __syncthreads();
+      load_stage(min(kb + 3, KB - 1), ra[1], rw[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb + 1 < KB) compute(kb + 1, 1);
+      store_stage(0, ra[0], rw[0]);
+      __syncthreads();
+    }
   }
 
   if (tid < BM) {
@@ -591,12 +617,12 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
   }
 }
 
-template <int WM>
+template <int WM, int PD = 1>
 static hipError_t launch_kproj_v3(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
-  hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden, p.row_offsets,
+  hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden, p.row_offsets,
                      p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
                      (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                      (int)p.layer_idx, tiles_m, tiles_n);
@@ -636,6 +662,8 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
   if (p.Kh / KBK > 32) variant = 1;   // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
   if (variant == 0) variant = 6;
+  if (variant == 10) return launch_kproj_v3<3, 2>(p, stream);
+  if (variant == 11) return launch_kproj_v3<2, 2>(p, stream);
   if (variant >= 6) {
     // third design: 48, 96 or 144-row tiles (auto), or forced
     int wm = variant == 7 ? 1 : (variant == 8 ? 2 : (variant == 9 ? 3 : 0));

@@ -817,9 +817,12 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     sc_cur[1] = r0.sc[1];
     __syncthreads();
     int kt = 0;
+    // Loads past the last stage re-read it (their copies are never stored), so
+    // every iteration issues the same loads and the compiler's in-order load
+    // counting waits only for the older register set.
     for (; kt + 1 < nk; kt += 2) {
       // even stage kt: buffer 0; stage kt + 1 is in r1
-      if (kt + 2 < nk) load_stage(kt + 2, r0);
+      load_stage(min(kt + 2, nk - 1), r0);
       __builtin_amdgcn_sched_barrier(0);
       compute(0, sc_cur);
       store_stage(kt + 1, 1, r1);
@@ -827,7 +830,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       sc_cur[0] = r1.sc[0];
       sc_cur[1] = r1.sc[1];
       // odd stage kt + 1: buffer 1; stage kt + 2 (if any) is in r0
-      if (kt + 3 < nk) load_stage(kt + 3, r1);
+      load_stage(min(kt + 3, nk - 1), r1);
       __builtin_amdgcn_sched_barrier(0);
       compute(1, sc_cur);
       if (kt + 2 < nk) {
@@ -893,7 +896,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
 // activation rows. Expert e's packed words and scales are b[e] ([K/8, N]) and
 // s[e] ([K/group_size, N]). Rows of skipped groups are never written. The grid
 // is an upper bound on the tile count; workgroups past the last tile exit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
@@ -908,11 +911,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   const int r_begin = (int)a_off[loc.g] + chunk * BM;
   const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
   const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, 1, KG>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
                                                S + e * spe, rows, N, K, group_size, 0, nt * BN, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int MINB, int KG>
+template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1>
 static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream) {
   if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL) return hipErrorNotSupported;
   const int tiles_n = (int)((p.N + BN - 1) / BN);
@@ -920,7 +923,7 @@ static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
   if (bound > INT32_MAX / 2) return hipErrorNotSupported;
   const int grid = (int)((bound + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
                      stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
                      p.num_active, tiles_n);
   return hipGetLastError();
@@ -935,6 +938,12 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t st
     case 4: return launch_grouped_tile<64, 256, 1, 4, 3, 1>(p, stream);
     case 5: return launch_grouped_tile<32, 256, 1, 4, 4, 1>(p, stream);
     case 6: return launch_grouped_tile<64, 128, 1, 2, 4, 1>(p, stream);
+    // two stages of prefetch in registers
+    case 7: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 2>(p, stream);
+    case 8: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 2>(p, stream);
+    case 9: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2>(p, stream);
+    case 10: return launch_grouped_tile<64, 128, 1, 2, 4, 1, 2>(p, stream);
+    case 11: return launch_grouped_tile<128, 256, 1, 4, 2, 1, 2>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -118,3 +118,20 @@ def test_full_size_with_history(gpu, lib):
 def test_determinism(gpu, lib):
     k = small(8, (200, 31))
     assert np.array_equal(run_kproj(lib, k), run_kproj(lib, k))
+
+
+# every selectable design: 1 first, 2-5 second (auto / 128 / 64 / 144 rows),
+# 6-9 third (auto / 48 / 96 / 144 rows), 10-11 third with two stages in flight
+KPROJ_VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]
+
+
+@pytest.mark.parametrize("variant", KPROJ_VARIANTS)
+def test_every_design(gpu, lib, variant):
+    import os
+    os.environ["QG_KPROJ_VARIANT"] = str(variant)
+    try:
+        check(lib, small(40 + variant, (100, 1, 64, 65, 0, 130), Kh=512, cache_lengths=(0, 3, 17, 128, 5, 250)),
+              f"v{variant} ragged")
+        check(lib, small(60 + variant, (300, 7), Kh=384, hkv=2, D=128, page_size=16), f"v{variant} odd stages")
+    finally:
+        del os.environ["QG_KPROJ_VARIANT"]
