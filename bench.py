@@ -8,7 +8,7 @@ device copies (>= 1 GiB) that every launch reads its operands from HBM, not
 from the 256 MB Infinity Cache or the L2s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config decode|prefill|square|grouped|grouped_w4|kproj]
+                    [--config decode|prefill|square|grouped|grouped_kn|grouped_w4|kproj]
 
 Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
 steps (the decode shapes are bound by HBM); TFLOP/s is reported beside it. The
@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "prefill": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "square": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
+    "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
 }
@@ -84,7 +85,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "grouped_w4",
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "grouped_kn", "grouped_w4",
                                                            "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
@@ -228,10 +229,11 @@ class PrefillW4:
 
 
 class GroupedBF16:
-    """64 experts, 4096 routed rows, K=2048, N=1408, 10% of groups skipped (seed 4)."""
-    kernel = "grouped_bf16_kernel"
+    """64 experts, 4096 routed rows, K=2048, N=1408, 10% of groups skipped (seed 4), experts stored [E, N, K]."""
+    kernel = "grouped_bf16_wl_kernel"
     bound = "hbm"
     dtype = "bf16"
+    transpose_b = True
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
@@ -251,17 +253,18 @@ class GroupedBF16:
         self.R = max(1, math.ceil(ROTATE_BYTES / (d.b.nbytes + d.a.nbytes + T * N * 2)))
         dev = torch.device("cuda")
         a = torch.from_numpy(d.a.view(np.int16)).to(dev).view(torch.bfloat16)
-        b = torch.from_numpy(d.b.view(np.int16)).to(dev).view(torch.bfloat16)
+        bh = d.b if self.transpose_b else np.ascontiguousarray(d.b.transpose(0, 2, 1))
+        b = torch.from_numpy(bh.view(np.int16)).to(dev).view(torch.bfloat16)
         off_t = torch.from_numpy(d.a_offsets.view(np.int32)).to(dev)
         ids = torch.from_numpy(d.expert_ids).to(dev)
         self.slots = [(torch.empty(T, N, dtype=torch.bfloat16, device=dev), a.clone(), off_t, b.clone() if r else b, ids)
                       for r in range(self.R)]
         self.usage = [int(v) for v in d.usage]
-        self.name = f"grouped_bf16_E{E}_T{T}_K{K}_N{N}_skip10pct"
+        self.name = f"grouped_bf16_E{E}_T{T}_K{K}_N{N}_skip10pct" + ("" if self.transpose_b else "_b_KxN")
 
     def launches(self, step):
         c, a, off, b, ids = self.slots[step % self.R]
-        return [lambda: self.q.grouped_gemm(c, a, off, b, ids, self.usage)]
+        return [lambda: self.q.grouped_gemm(c, a, off, b, ids, self.usage, self.transpose_b)]
 
     def unit_bytes(self):
         return self.bytes_per_step
@@ -275,7 +278,11 @@ class GroupedBF16:
         G = 8
         usage = np.array([d.usage[0], G], np.uint32)
         c0 = np.zeros((self.T, self.N), np.uint16)
-        oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, usage)
+        if self.transpose_b:
+            oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, usage)
+        else:
+            oracle.grouped_gemm(c0, d.a, d.a_offsets, np.ascontiguousarray(d.b.transpose(0, 2, 1)), d.expert_ids,
+                                usage, transpose_b=False)
         off = d.a_offsets.astype(np.int64)
         rows = sum(int(off[g + 1] - off[g]) for g in range(G) if d.expert_ids[g] >= 0)
         ne = sum(1 for g in range(G) if d.expert_ids[g] >= 0)
@@ -284,11 +291,18 @@ class GroupedBF16:
 
     def describe(self):
         return {"workload": self.name, "experts": self.E, "routed_rows": self.T, "K": self.K, "N": self.N,
-                "active_rows": self.active_rows, "active_experts": self.active_experts, "transpose_b": True,
+                "active_rows": self.active_rows, "active_experts": self.active_experts,
+                "transpose_b": self.transpose_b,
                 "rotating_copies": self.R}
 
     def dense_equivalent(self):
         return None   # HBM-bound: the copy of the same byte count is the context number
+
+
+class GroupedBF16KN(GroupedBF16):
+    """The same grouped workload with the experts stored [E, K, N] (transpose_b = False)."""
+    kernel = "grouped_bf16_kernel"
+    transpose_b = False
 
 
 class GroupedW4:
@@ -474,7 +488,7 @@ def context_numbers(torch, wl, steps):
 
 WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
-             "grouped": GroupedBF16, "grouped_w4": GroupedW4, "kproj": KProjFP8}
+             "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 
 def main():

@@ -141,16 +141,18 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
   if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
   const uint32_t num_active = expert_usage_stats_host[1];
   if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
-  if (!transpose_b) return QG_ERR_UNSUPPORTED;
   if (K % 8 != 0 || N % 8 != 0) return QG_ERR_ALIGN;
   if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (N * K * 2 > 0xFFFFFFFFLL) return QG_ERR_UNSUPPORTED;   // 32-bit buffer offsets within an expert
   if (num_active == 0 || T == 0 || N == 0 || E == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;
   qg::GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                     static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
                     static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
-                    (int)expert_usage_stats_host[0], device_cus()};
-  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", 3), stream));
+                    (int)expert_usage_stats_host[0], device_cus(), transpose_b ? 1 : 0};
+  // both layouts stage the weights through LDS as whole 128-byte row segments:
+  // [E, N, K] in 64-deep steps (19), [E, K, N] with transpose reads (12)
+  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", transpose_b ? 19 : 12), stream));
 }
 
 qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,

@@ -5,16 +5,20 @@
 //
 // The problem is bound by reading each active expert's weights once, so the
 // schedule is weight-stationary: a work tile is (group, block of up to 128 of
-// its rows, 16 * W output columns). A workgroup of W waves owns a tile; each
-// wave streams a 16-column slice of the expert's weights from HBM exactly once
-// while it multiplies every row of the block against it. All loads are raw
+// its rows, 16 * W output columns). A workgroup of W waves owns a tile and
+// streams the tile's columns of the expert's weights from HBM exactly once
+// while it multiplies every row of the block against them. All loads are raw
 // buffer loads (descriptor in SGPRs, uniform per-step offset).
-//   * Weight fragments go straight from HBM into registers, 16 bytes per lane
-//     per 32-deep K step (transpose_b puts K contiguous in both operands),
-//     several steps ahead. The rows' activation fragments are loaded once per
-//     workgroup (split over the waves, same distance ahead) and shared through
-//     an LDS ring in MFMA fragment order (read back as lane * 16 bytes: no bank
-//     conflicts, no swizzle).
+//   * Three weight paths. The default for each layout stages the weights
+//     through LDS, loaded as whole 128-byte row segments: the vector memory
+//     path spends one request per cache line an instruction touches, and a
+//     per-wave MFMA fragment can only cover half a line of each of 16 weight
+//     rows ([E, N, K]: 64-deep steps, ds_read_b128 fragments; [E, K, N]: LDS
+//     transpose reads). The first design loads [E, N, K] fragments straight
+//     into registers (16 bytes per lane per 32-deep step), 18 % slower.
+//   * The rows' activation fragments are loaded once per workgroup (split over
+//     the waves, several steps ahead) and shared through an LDS ring in MFMA
+//     fragment order (read back as lane * 16 bytes: no bank conflicts).
 //   * The activation rows of a group are re-read by each of its column tiles;
 //     the tiles of one group are adjacent in the tile order and every XCD takes
 //     a contiguous range of it, so those re-reads hit that XCD's L2.
@@ -45,10 +49,27 @@ constexpr int GBM = 16 * GMAXMT;
 // wave's loads are issued in step order and each step waits only for its own
 // (oldest) loads, the hardware's in-order load counter never forces a wave to
 // wait for a prefetch that lies further ahead.
-template <int W, int MT, int D>
+//
+// With the weights stored [E, K, N] (TB false) the workgroup loads the step's
+// 32 x 16W weight tile cooperatively (one 16-byte chunk per thread, whole
+// 32W-byte row segments), stores it into a second LDS ring and every wave reads
+// its B fragment with two 16-bit LDS transpose reads: within each 16-lane
+// group, element j of lane i comes from the 8 bytes named by lane 4j + i / 4, at
+// element i % 4, so lane m naming K row 8q + 4h + m / 4, columns 4(m % 4) .. + 3
+// of the wave's sixteen hands lane i column i at K rows 8q + 4h .. + 3.
+template <int W>
+struct WRing {
+  static constexpr int ROW = 2 * W + 2;   // 16-byte chunks per K row (two spare: rows land on distinct banks)
+  static constexpr int SLOT = 32 * ROW;
+};
+
+// P > 1: the loads of P consecutive steps are issued together (a weight row's
+// P * 64 contiguous bytes requested back to back).
+template <int W, int MT, int D, bool TB, int P>
 __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
-                                             int N, int K, int e, int r_begin, int rows, int n0) {
+                                             u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
+                                             int rows, int n0) {
   constexpr int FPW = (MT + W - 1) / W;   // activation fragments per wave per step
   static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   const int lane = threadIdx.x & 63;
@@ -60,6 +81,14 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   // per-lane byte offsets, the step's K offset is uniform (an SGPR)
   const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)r_begin * K, (uint32_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + (size_t)e * N * K, (uint32_t)N * K * 2);
+  // TB false: this thread's chunk of the step's weight tile (K rows past the
+  // expert's end read as zeros)
+  constexpr int WROW = WRing<W>::ROW;
+  const int w_kr = threadIdx.x / (2 * W), w_c = threadIdx.x % (2 * W);
+  const uint32_t wt_voff = (uint32_t)(w_kr * N + n0 + 8 * w_c) * 2;
+  const int wt_lds = w_kr * WROW + w_c;
+  // byte offsets of this lane's two transpose reads within a weight slot
+  const int tr_off = (8 * q + (r16 >> 2)) * WROW * 16 + wave * 32 + 8 * (r16 & 3);
   // Wave w loads fragments w, w + W, ... Those past MT are not needed: their
   // offset lies past the descriptor, so the load returns zeros without a memory
   // request, and they land in LDS slots MT .. GMAXMT-1 that no MFMA reads.
@@ -70,20 +99,20 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
     a_frag[i] = wave + i * W;
     a_voff[i] = a_frag[i] < MT ? (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2 : 0x80000000u;
   }
-  const uint32_t b_voff = (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8) * 2;
+  const uint32_t b_voff = TB ? (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8) * 2 : wt_voff;
 
   u32x4_t ra[D][FPW], rb[D];
   // whole step s: K elements 32s .. 32s + 31
   auto load_step = [&](int s, u32x4_t (&a)[FPW], u32x4_t& b) {
     const uint32_t soff = (uint32_t)s * 64;
-    b = buffer_load16(b_src, b_voff, soff);
+    b = buffer_load16(b_src, b_voff, TB ? soff : (uint32_t)s * 32 * N * 2);
 #pragma unroll
     for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i], soff);
   };
   // partial last step (K % 32 != 0): each lane's chunk start is clamped into its row
   auto load_tail = [&](u32x4_t (&a)[FPW], u32x4_t& b) {
     const uint32_t k2 = (uint32_t)max(0, min(nfull * 32, K - 8 - q * 8)) * 2;
-    b = buffer_load16(b_src, b_voff + k2, 0);
+    b = TB ? buffer_load16(b_src, b_voff + k2, 0) : buffer_load16(b_src, b_voff, (uint32_t)nfull * 32 * N * 2);
 #pragma unroll
     for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i] + k2, 0);
   };
@@ -98,10 +127,22 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   auto step = [&](int slot, const u32x4_t (&a)[FPW], const u32x4_t& b) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) ring[(slot * GMAXMT + a_frag[i]) * kWave + lane] = a[i];
+    if constexpr (!TB) wring[slot * WRing<W>::SLOT + wt_lds] = b;
     __syncthreads();
+    u32x4_t bf = b;
+    if constexpr (!TB) {
+      const unsigned char* base = reinterpret_cast<const unsigned char*>(wring + slot * WRing<W>::SLOT) + tr_off;
+      typedef short s16x4_t __attribute__((ext_vector_type(4)));
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(__attribute__((address_space(3))) const unsigned char*)base);
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(__attribute__((address_space(3))) const unsigned char*)(base + 4 * WROW * 16));
+      const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+      bf = u32x4_t{l2.x, l2.y, h2.x, h2.y};
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = mfma16x16x32_bf16(ring[(slot * GMAXMT + mt) * kWave + lane], b, acc[mt]);
+      acc[mt] = mfma16x16x32_bf16(ring[(slot * GMAXMT + mt) * kWave + lane], bf, acc[mt]);
   };
 
   __syncthreads();   // the previous tile's readers are done with the ring
@@ -113,7 +154,10 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       step((s0 + u) & 1, ra[u], rb[u]);
-      load_step(min(s0 + u + D, nfull - 1), ra[u], rb[u]);
+      if ((u + 1) % P == 0) {
+#pragma unroll
+        for (int v = u + 1 - P; v <= u; ++v) load_step(min(s0 + v + D, nfull - 1), ra[v], rb[v]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -126,7 +170,7 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   if (K & 31) {
     load_tail(ra[0], rb[0]);
     const bool past = nfull * 32 + q * 8 >= K;
-    rb[0] = past ? u32x4_t{0u, 0u, 0u, 0u} : rb[0];
+    if constexpr (TB) rb[0] = past ? u32x4_t{0u, 0u, 0u, 0u} : rb[0];
 #pragma unroll
     for (int i = 0; i < FPW; ++i) ra[0][i] = past ? u32x4_t{0u, 0u, 0u, 0u} : ra[0][i];
     step(nfull & 1, ra[0], rb[0]);
@@ -146,12 +190,185 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   }
 }
 
+// Transposed weights ([E, N, K]) staged through LDS in 64-deep steps. A 16-byte
+// load can only feed the MFMA lane that owns its column, so per-wave weight
+// fragments touch each 128-byte line of a weight row half at a time; here the
+// workgroup loads the step's 16W x 64 weight tile as whole 128-byte row
+// segments (eight lanes per row, two chunks per thread), stores it into an LDS
+// slot (16-byte chunks XOR-swizzled by row) and every wave reads its fragments
+// back with 16-byte LDS reads. A step is two 32-deep MFMA sub-steps; the
+// activation ring holds both. D steps are in flight.
+template <int W, int MT, int D>
+__device__ __forceinline__ void grouped_tile_wl(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
+                                                const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
+                                                u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
+                                                int rows, int n0) {
+  constexpr int FPW = (MT + W - 1) / W;
+  static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
+  constexpr int WSLOT = 16 * W * 8;   // 16-byte chunks of one weight step
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int ns = K >> 6;          // whole 64-deep steps
+  const int ktail = K & 63;       // elements of the partial last step (a multiple of 8)
+
+  const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)r_begin * K, (uint32_t)rows * K * 2);
+  const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + (size_t)e * N * K, (uint32_t)N * K * 2);
+  uint32_t a_voff[FPW];
+  int a_frag[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    a_frag[i] = wave + i * W;
+    a_voff[i] = a_frag[i] < MT ? (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2 : 0x80000000u;
+  }
+  // weight chunks h = 0, 1 of this thread: row h * 8W + tid / 8, chunk tid % 8
+  const int tid = threadIdx.x;
+  const int w_c = tid & 7;
+  uint32_t w_voff[2];
+  int w_lds[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = h * 8 * W + (tid >> 3);
+    w_voff[h] = (uint32_t)(min(n0 + r, N - 1) * K + 8 * w_c) * 2;
+    w_lds[h] = r * 8 + (w_c ^ ((r >> 1) & 7));
+  }
+  // this lane's fragment rows in a weight slot
+  const int f_row = wave * 16 + r16;
+
+  u32x4_t ra[D][FPW][2], rb[D][2];
+  auto load_step = [&](int s, u32x4_t (&a)[FPW][2], u32x4_t (&b)[2]) {
+    const uint32_t soff = (uint32_t)s * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) b[h] = buffer_load16(b_src, w_voff[h], soff);
+#pragma unroll
+    for (int i = 0; i < FPW; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) a[i][j] = buffer_load16(a_src, a_voff[i] + 64 * j, soff);
+  };
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // slot `slot` of both rings; the slot written at step s was last read at
+  // step s - 2, before every wave passed step s - 1's barrier
+  auto step = [&](int slot, const u32x4_t (&a)[FPW][2], const u32x4_t (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ring[((slot * 2 + j) * GMAXMT + a_frag[i]) * kWave + lane] = a[i][j];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) wring[slot * WSLOT + w_lds[h]] = b[h];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4_t bf = wring[slot * WSLOT + f_row * 8 + ((4 * j + q) ^ ((f_row >> 1) & 7))];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma16x16x32_bf16(ring[((slot * 2 + j) * GMAXMT + mt) * kWave + lane], bf, acc[mt]);
+    }
+  };
+
+  __syncthreads();   // the previous tile's readers are done with both rings
+#pragma unroll
+  for (int u = 0; u < D; ++u) load_step(max(0, min(u, ns - 1)), ra[u], rb[u]);
+  int s0 = 0;
+  for (; s0 + D <= ns; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      step((s0 + u) & 1, ra[u], rb[u]);
+      load_step(min(s0 + u + D, ns - 1), ra[u], rb[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u)
+    if (u < ns - s0) step((s0 + u) & 1, ra[u], rb[u]);
+  // partial last step: chunks at or past K enter the MFMA as zeros on both sides
+  if (ktail) {
+    load_step(ns, ra[0], rb[0]);
+    const bool w_past = 8 * w_c >= ktail;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) rb[0][h] = w_past ? u32x4_t{0u, 0u, 0u, 0u} : rb[0][h];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool past = 32 * j + 8 * q >= ktail;
+#pragma unroll
+      for (int i = 0; i < FPW; ++i) ra[0][i][j] = past ? u32x4_t{0u, 0u, 0u, 0u} : ra[0][i][j];
+    }
+    step(ns & 1, ra[0], rb[0]);
+  }
+
+  const int col = n0 + wave * 16 + r16;
+  if (col < N) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + q * 4 + i;
+        if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
+      }
+    }
+  }
+}
+
+// Persistent workgroups over the same tile list, weights through LDS (above).
 template <int W, int D, int OCC>
+__global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
+    const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
+    int tiles_n) {
+  __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * 2 * GMAXMT * kWave];
+  __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * 16 * W * 8];
+  constexpr int GBN = 16 * W;
+  const int total = count_tiles(a_off, ids, num_active, GBM, tiles_n);
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = gridDim.x >> 3;
+  const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
+  for (int t = lo + (int)(blockIdx.x >> 3); t < hi; t += per_xcd) {
+    const TileLoc loc = locate_tile(t, a_off, ids, num_active, GBM, tiles_n);
+    const int g = loc.g;
+    const int chunk = loc.local / tiles_n, nt = loc.local % tiles_n;
+    const int e = ids[g];
+    const int r_begin = (int)a_off[g] + chunk * GBM;
+    const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
+    const int n0 = nt * GBN;
+    // two activation fragments per wave per sub-step beyond four row tiles
+    // (four waves): half as many steps in flight
+    constexpr int D5 = W >= 8 ? D : (D + 1) / 2;
+    switch ((rows + 15) >> 4) {
+      case 1: grouped_tile_wl<W, 1, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 2: grouped_tile_wl<W, 2, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 3: grouped_tile_wl<W, 3, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 4: grouped_tile_wl<W, 4, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 5: grouped_tile_wl<W, 5, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 6: grouped_tile_wl<W, 6, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 7: grouped_tile_wl<W, 7, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      default: grouped_tile_wl<W, 8, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+    }
+  }
+}
+
+template <int W, int D, int OCC>
+static hipError_t launch_wl(const GroupedArgs& p, hipStream_t stream) {
+  if (!p.transpose_b) return hipErrorInvalidValue;
+  const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
+  const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
+  hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
+                     p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+  return hipGetLastError();
+}
+
+template <int D, int P>
+constexpr int fit_group() { return D % P == 0 ? P : (D % 2 == 0 ? 2 : 1); }
+
+template <int W, int D, int OCC, bool TB, int P>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
     int tiles_n) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
+  __shared__ __attribute__((aligned(16))) u32x4_t wring[TB ? 1 : 2 * WRing<W>::SLOT];
 
   constexpr int GBN = 16 * W;   // columns per work tile: 16 per wave
   // every wave scans the group table itself (one group per lane), so no
@@ -174,25 +391,29 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     // same registers and about the same bytes in flight.
     constexpr int D5 = W >= 8 ? D : D / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile<W, 1, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 2: grouped_tile<W, 2, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 3: grouped_tile<W, 3, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 4: grouped_tile<W, 4, D>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 5: grouped_tile<W, 5, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 6: grouped_tile<W, 6, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      case 7: grouped_tile<W, 7, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
-      default: grouped_tile<W, 8, D5>(C, A, B, ring, N, K, e, r_begin, rows, n0); break;
+      case 1: grouped_tile<W, 1, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 2: grouped_tile<W, 2, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 3: grouped_tile<W, 3, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 4: grouped_tile<W, 4, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 5: grouped_tile<W, 5, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 6: grouped_tile<W, 6, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 7: grouped_tile<W, 7, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      default: grouped_tile<W, 8, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
     }
   }
 }
 
-template <int W, int D, int OCC>
+template <int W, int D, int OCC, int P = 1>
 static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
   const int wg_per_cu = OCC;
   const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
   const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
-  hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A, p.a_offsets,
-                     p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+  if (p.transpose_b)
+    hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, true, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
+                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+  else
+    hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, false, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
+                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
   return hipGetLastError();
 }
 
@@ -207,6 +428,22 @@ hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t st
     case 5: return launch_g<8, 8, 1>(p, stream);
     case 6: return launch_g<8, 12, 1>(p, stream);
     case 7: return launch_g<8, 16, 1>(p, stream);
+    // loads of 2 or 4 consecutive steps issued together
+    case 8: return launch_g<4, 8, 2, 2>(p, stream);
+    case 9: return launch_g<4, 8, 2, 4>(p, stream);
+    case 10: return launch_g<4, 12, 2, 2>(p, stream);
+    case 11: return launch_g<4, 12, 2, 4>(p, stream);
+    case 12: return launch_g<8, 8, 1, 2>(p, stream);
+    case 13: return launch_g<8, 8, 1, 4>(p, stream);
+    // transposed weights staged through LDS as whole 128-byte row segments
+    case 14: return launch_wl<4, 4, 2>(p, stream);
+    case 15: return launch_wl<4, 6, 2>(p, stream);
+    case 16: return launch_wl<4, 4, 3>(p, stream);
+    case 17: return launch_wl<8, 4, 1>(p, stream);
+    case 18: return launch_wl<8, 6, 1>(p, stream);
+    case 19: return launch_wl<8, 4, 2>(p, stream);
+    case 20: return launch_wl<8, 2, 2>(p, stream);
+    case 21: return launch_wl<4, 3, 3>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -32,12 +32,13 @@ struct GroupedArgs {
   uint16_t* C;              // bf16 [T, N]
   const uint16_t* A;        // bf16 [T, K]
   const uint32_t* a_offsets;  // [G+1]
-  const uint16_t* B;        // bf16 [E, N, K]
+  const uint16_t* B;        // bf16 [E, N, K] (transpose_b) or [E, K, N]
   const int32_t* expert_ids;  // [G]
   int64_t T, N, K, E;
   int num_active;
   int max_rows_hint;
   int num_cus;
+  int transpose_b;
 };
 
 struct KProjArgs {

@@ -107,8 +107,9 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
  *
  *   c          bf16 [T, N]   output; for g < num_active with expert_ids[g] >= 0,
  *                            rows a_offsets[g] .. a_offsets[g+1]-1 are set to
- *                            A[rows] . B[expert_ids[g]]^T; all other rows keep
- *                            their prior content
+ *                            A[rows] . B[expert_ids[g]]^T (transpose_b != 0) or
+ *                            A[rows] . B[expert_ids[g]] (transpose_b == 0); all
+ *                            other rows keep their prior content
  *   a          bf16 [T, K]
  *   a_offsets  u32  [G + 1]  non-decreasing, a_offsets[num_active] <= T
  *   b          bf16 [E, N, K] when transpose_b != 0, else [E, K, N]
@@ -118,8 +119,8 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
  *
  * K and N must be multiples of 8 (QG_ERR_ALIGN). Accumulation is fp32; results are
  * rounded to bf16 (nearest-even). The device-side tables are not re-validated:
- * offsets past T, or expert ids >= E, are undefined behaviour.
- * transpose_b == 0 returns QG_ERR_UNSUPPORTED.
+ * offsets past T, or expert ids >= E, are undefined behaviour. An expert
+ * matrix of more than 2^32 - 1 bytes returns QG_ERR_UNSUPPORTED.
  */
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                        const qg_tensor* b, const qg_tensor* expert_ids,

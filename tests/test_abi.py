@@ -119,7 +119,19 @@ def test_grouped_rejections(lib):
     assert gg_call(lib, c, a, bb.t((G,), QG.U32), b, ids, [8, 4]) == QG.ERR_SHAPE
     assert gg_call(lib, c, a, off, bb.t((E, N, K + 8), QG.BF16), ids, [8, 4]) == QG.ERR_SHAPE
     assert gg_call(lib, c, a, off, b, ids, [8, 5]) == QG.ERR_INVALID_ARG
-    assert gg_call(lib, c, a, off, bb.t((E, K, N), QG.BF16), ids, [8, 4], tb=0) == QG.ERR_UNSUPPORTED
+    # transpose_b == 0 takes B as [E, K, N]: the [E, N, K] buffer no longer matches K
+    assert gg_call(lib, c, a, off, b, ids, [8, 4], tb=0) == QG.ERR_SHAPE
+    # an expert matrix beyond 32-bit byte offsets (shape only: validation never reads the buffers)
+    big = QgTensor()
+    big.data, big.dtype, big.rank = b.data, QG.BF16, 3
+    big.shape[0], big.shape[1], big.shape[2] = E, 65536, 32768
+    big_c = QgTensor()
+    big_c.data, big_c.dtype, big_c.rank = c.data, QG.BF16, 2
+    big_c.shape[0], big_c.shape[1] = T, 65536
+    big_a = QgTensor()
+    big_a.data, big_a.dtype, big_a.rank = a.data, QG.BF16, 2
+    big_a.shape[0], big_a.shape[1] = T, 32768
+    assert gg_call(lib, big_c, big_a, off, big, ids, [8, 4]) == QG.ERR_UNSUPPORTED
     assert gg_call(lib, c, a, off, b, ids, [8, 0]) == QG.OK       # nothing active: no-op
     u = (ctypes.c_uint32 * 2)(8, 4)
     assert lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),

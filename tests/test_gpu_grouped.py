@@ -18,15 +18,17 @@ pytestmark = pytest.mark.gpu
 SENT = 0xFFC1  # bf16 NaN pattern: never produced by the kernel
 
 
-def run_grouped(lib, d: synth.GroupedInputs, a_off=None, ids=None, usage=None):
+def run_grouped(lib, d: synth.GroupedInputs, a_off=None, ids=None, usage=None, transpose_b=True):
     a_off = d.a_offsets if a_off is None else a_off
     ids = d.expert_ids if ids is None else ids
     usage = d.usage if usage is None else usage
     T, K = d.a.shape
     N = d.b.shape[1]
+    # transpose_b == False: the same expert matrices stored [E, K, N]
+    b = d.b if transpose_b else np.ascontiguousarray(d.b.transpose(0, 2, 1))
     out = Guarded((T, N), torch.bfloat16, SENT)
-    lib.grouped_gemm(out.view, dev16(d.a, torch.bfloat16), dev32(a_off), dev16(d.b, torch.bfloat16),
-                     dev32(np.asarray(ids, np.int32)), [int(v) for v in usage], True)
+    lib.grouped_gemm(out.view, dev16(d.a, torch.bfloat16), dev32(a_off), dev16(b, torch.bfloat16),
+                     dev32(np.asarray(ids, np.int32)), [int(v) for v in usage], transpose_b)
     got = host16(out.view)
     assert out.bands_intact(), "write outside C"
     return got
@@ -40,7 +42,11 @@ def check(lib, d, what, **kw):
     ids = kw.get("ids", d.expert_ids)
     usage = kw.get("usage", d.usage)
     c0 = np.full(got.shape, SENT, np.uint16)
-    ref = oracle.grouped_gemm(c0, d.a, a_off, d.b, ids, usage)
+    if kw.get("transpose_b", True):
+        ref = oracle.grouped_gemm(c0, d.a, a_off, d.b, ids, usage)
+    else:
+        ref = oracle.grouped_gemm(c0, d.a, a_off, np.ascontiguousarray(d.b.transpose(0, 2, 1)), ids, usage,
+                                  transpose_b=False)
     written = ref[:, 0] != SENT
     # routing: exactly the rows the oracle writes are written
     assert np.array_equal(got[:, 0] != SENT, written), "row routing differs"
@@ -104,3 +110,44 @@ def test_full_size_config(gpu, lib):
 def test_determinism(gpu, lib):
     d = synth.grouped_inputs(seed=11, E=16, T=1000, K=256, N=192)
     assert np.array_equal(run_grouped(lib, d), run_grouped(lib, d))
+
+
+# every launch shape: waves per workgroup, steps in flight, workgroups per CU,
+# steps whose loads are issued together (variant 7 is left out: it spills)
+GROUPED_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 8, 9, 10, 11, 12, 13]
+# transposed weights staged through LDS as whole 128-byte row segments (transposed weights only)
+GROUPED_VARIANTS_TB = GROUPED_VARIANTS + [14, 15, 16, 17, 18, 19, 20, 21]
+
+
+@pytest.mark.parametrize("variant", GROUPED_VARIANTS_TB)
+def test_every_launch_shape(gpu, lib, variant):
+    import os
+    os.environ["QG_GROUPED_VARIANT"] = str(variant)
+    try:
+        for (E, T, K, N, seed) in [(8, 200, 64, 64, 21), (5, 77, 40, 24, 22), (16, 600, 456, 200, 23),
+                                   (3, 300, 96, 136, 24), (4, 520, 384, 72, 25), (6, 900, 136, 48, 26)]:
+            d = synth.grouped_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
+            check(lib, d, f"v{variant} seed{seed}")
+    finally:
+        del os.environ["QG_GROUPED_VARIANT"]
+
+
+# transpose_b == False ([E, K, N] experts): LDS-transposed weight fragments
+@pytest.mark.parametrize("variant", GROUPED_VARIANTS)
+def test_b_not_transposed(gpu, lib, variant):
+    import os
+    os.environ["QG_GROUPED_VARIANT"] = str(variant)
+    try:
+        for (E, T, K, N, seed) in [(8, 200, 64, 64, 11), (5, 77, 40, 24, 12), (16, 600, 256, 200, 13),
+                                   (3, 300, 96, 136, 14), (4, 520, 72, 1032, 15)]:
+            d = synth.grouped_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
+            check(lib, d, f"[E,K,N] v{variant} seed{seed}", transpose_b=False)
+    finally:
+        del os.environ["QG_GROUPED_VARIANT"]
+
+
+def test_b_not_transposed_full_size(gpu, lib):
+    """64 experts, 4096 routed rows, K = 2048, N = 1408, experts stored [E, K, N]."""
+    d = synth.grouped_inputs()
+    diag = check(lib, d, "full [E,K,N]", transpose_b=False)
+    say("  diagnostics", diag)
