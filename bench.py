@@ -55,12 +55,13 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9019628, "7eea08f6a447e2d2"),
-    "prefill": (302821291, "87eb1f9f22793be5"),
-    "square": (101378817, "87eb1f9f22793be5"),
-    "grouped": (367954489, "0ae87ba6f551c5aa"),
-    "grouped_w4": (117908837, "87eb1f9f22793be5"),
-    "kproj": (85578290, "ff0a5e271101b025"),
+    "decode": (9019628, "f5be18eb391916bd"),
+    "prefill": (271155781, "7e88e26862b0c500"),
+    "square": (101378817, "7e88e26862b0c500"),
+    "grouped": (367992844, "846169e22572cd19"),
+    "grouped_kn": (365854045, "846169e22572cd19"),
+    "grouped_w4": (117818797, "7e88e26862b0c500"),
+    "kproj": (85578290, "7e7880aa3aaf52ae"),
 }
 
 
