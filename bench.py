@@ -8,7 +8,7 @@ device copies (>= 1 GiB) that every launch reads its operands from HBM, not
 from the 256 MB Infinity Cache or the L2s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config decode|prefill|square|grouped|grouped_kn|grouped_w4|kproj]
+                    [--config decode|prefill|square|decode_bf16|prefill_bf16|grouped|grouped_kn|grouped_w4|kproj]
 
 Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
 steps (the decode shapes are bound by HBM); TFLOP/s is reported beside it. The
@@ -48,6 +48,8 @@ KERNEL_SOURCES = {
     "decode": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
     "prefill": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "square": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "decode_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
+    "prefill_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
@@ -86,8 +88,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "grouped", "grouped_kn", "grouped_w4",
-                                                           "kproj"])
+    p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "decode_bf16", "prefill_bf16",
+                                                           "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -132,6 +134,7 @@ class DecodeW4:
     name = "w4a16_decode_N4096_K4096_gs128_M1_4_16"
     kernel = "w4_decode_lds_kernel"
     bound = "hbm"
+    dtype = "f16"
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
@@ -139,18 +142,19 @@ class DecodeW4:
         N, K = cfgs[0]["N"], cfgs[0]["K"]
         self.N, self.K, self.gs = N, K, 128
         self.Ms = [c["M"] for c in cfgs]
-        self.inputs = [synth.w4_inputs(**c) for c in cfgs]
+        self.inputs = [synth.w4_inputs(**c, dtype=self.dtype) for c in cfgs]
         foot = sum(w4_bytes(M, N, K, 128) for M in self.Ms)
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
         dev = torch.device("cuda")
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
         b = torch.from_numpy(self.inputs[0].b.view(np.int32)).to(dev)
-        s = torch.from_numpy(self.inputs[0].scales.view(np.int16)).to(dev).view(torch.float16)
+        s = torch.from_numpy(self.inputs[0].scales.view(np.int16)).to(dev).view(tdt)
         self.slots = []
         for r in range(self.R):
             slot = []
             for i, M in enumerate(self.Ms):
-                a = torch.from_numpy(self.inputs[i].a.view(np.int16)).to(dev).view(torch.float16)
-                slot.append((torch.empty(M, N, dtype=torch.float16, device=dev), a, b.clone(), s.clone()))
+                a = torch.from_numpy(self.inputs[i].a.view(np.int16)).to(dev).view(tdt)
+                slot.append((torch.empty(M, N, dtype=tdt, device=dev), a, b.clone(), s.clone()))
             self.slots.append(slot)
         self.bytes_per_step = sum(w4_bytes(M, N, K, 128) for M in self.Ms)
         self.flops_per_step = sum(2 * M * N * K for M in self.Ms)
@@ -158,8 +162,6 @@ class DecodeW4:
     def launches(self, step):
         slot = self.slots[step % self.R]
         return [lambda c=c, a=a, b=b, s=s: self.q.qgemm_w4(c, a, b, s, 128) for (c, a, b, s) in slot]
-
-    dtype = "f16"
 
     def unit_bytes(self):
         return self.bytes_per_step / len(self.Ms)
@@ -170,7 +172,7 @@ class DecodeW4:
     def cpu_sample(self):
         import oracle
         for w in self.inputs:
-            oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size)
+            oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size, dtype=self.dtype)
         return self.flops_per_step, self.bytes_per_step, "full steps (M = 1, 4, 16)"
 
     def describe(self):
@@ -190,17 +192,18 @@ class PrefillW4:
     def __init__(self, torch, q, synth, square=False):
         self.torch, self.q = torch, q
         cfg = synth.W4_SQUARE_PREFILL if square else synth.W4_PREFILL
-        self.w = synth.w4_inputs(**cfg)
+        self.w = synth.w4_inputs(**cfg, dtype=self.dtype)
         M, N, K = self.w.shape
         self.M, self.N, self.K = M, N, K
-        self.name = f"w4a16_prefill_M{M}_N{N}_K{K}_gs128"
+        self.name = f"w4a16_prefill_M{M}_N{N}_K{K}_gs128" + ("_bf16" if self.dtype == "bf16" else "")
         foot = w4_bytes(M, N, K, 128)
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
         dev = torch.device("cuda")
-        a = torch.from_numpy(self.w.a.view(np.int16)).to(dev).view(torch.float16)
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
+        a = torch.from_numpy(self.w.a.view(np.int16)).to(dev).view(tdt)
         b = torch.from_numpy(self.w.b.view(np.int32)).to(dev)
-        sc = torch.from_numpy(self.w.scales.view(np.int16)).to(dev).view(torch.float16)
-        self.slots = [(torch.empty(M, N, dtype=torch.float16, device=dev), a.clone(), b.clone(), sc.clone())
+        sc = torch.from_numpy(self.w.scales.view(np.int16)).to(dev).view(tdt)
+        self.slots = [(torch.empty(M, N, dtype=tdt, device=dev), a.clone(), b.clone(), sc.clone())
                       for _ in range(self.R)]
         self.bytes_per_step = foot
         self.flops_per_step = 2 * M * N * K
@@ -218,7 +221,7 @@ class PrefillW4:
     def cpu_sample(self):
         import oracle
         rows = 256
-        oracle.qgemm_w4(self.w.a[:rows], self.w.b, self.w.scales, 128)
+        oracle.qgemm_w4(self.w.a[:rows], self.w.b, self.w.scales, 128, dtype=self.dtype)
         return 2 * rows * self.N * self.K, w4_bytes(rows, self.N, self.K, 128), f"{rows} of {self.M} rows"
 
     def describe(self):
@@ -226,7 +229,18 @@ class PrefillW4:
                 "pack_factor": 8, "rotating_copies": self.R}
 
     def dense_equivalent(self):
-        return (self.M, self.K, self.N, self.torch.float16)
+        return (self.M, self.K, self.N, self.torch.bfloat16 if self.dtype == "bf16" else self.torch.float16)
+
+
+class DecodeW4BF16(DecodeW4):
+    """The decode workload with bf16 activations, scales and output."""
+    name = "w4a16_decode_N4096_K4096_gs128_M1_4_16_bf16"
+    dtype = "bf16"
+
+
+class PrefillW4BF16(PrefillW4):
+    """The 2048 x 11008 x 4096 prefill with bf16 activations, scales and output."""
+    dtype = "bf16"
 
 
 class GroupedBF16:
@@ -489,6 +503,7 @@ def context_numbers(torch, wl, steps):
 
 WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
+             "decode_bf16": DecodeW4BF16, "prefill_bf16": PrefillW4BF16,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 

@@ -87,10 +87,13 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   // rank-2 requirement first: the page's only stated error condition
   if (c->rank != 2 || a->rank != 2 || b_packed->rank != 2 || scales->rank != 2) return QG_ERR_RANK;
   qg_status st;
-  if ((st = check_tensor(c, 2, QG_F16)) != QG_OK) return st;
-  if ((st = check_tensor(a, 2, QG_F16)) != QG_OK) return st;
+  // activations, scales and output are all fp16 or all bf16 (the page's a_type
+  // and c_type parameters)
+  const qg_dtype act = a->dtype == QG_BF16 ? QG_BF16 : QG_F16;
+  if ((st = check_tensor(c, 2, act)) != QG_OK) return st;
+  if ((st = check_tensor(a, 2, act)) != QG_OK) return st;
   if ((st = check_tensor(b_packed, 2, QG_U32)) != QG_OK) return st;
-  if ((st = check_tensor(scales, 2, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(scales, 2, act)) != QG_OK) return st;
   if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
   if (group_size <= 0) return QG_ERR_INVALID_ARG;
   const int64_t M = a->shape[0], K = a->shape[1], N = c->shape[1];
@@ -106,17 +109,24 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of C
   qg::W4Args p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
-               M, N, K, group_size};
+               M, N, K, group_size, act == QG_BF16 ? 1 : 0};
   if (M <= 16) {
-    return launch_status(qg::launch_w4_decode(p, env_variant("QG_W4_DECODE_VARIANT", 9), stream));
+    const int v = env_variant("QG_W4_DECODE_VARIANT", 9);
+    if (p.bf16 && v < 9) return QG_ERR_UNSUPPORTED;   // bf16 runs in the LDS-staged decode kernel
+    return launch_status(qg::launch_w4_decode(p, v, stream));
   }
   // 128 x 256 tiles of 32x32x16 MFMAs, each XCD sweeping groups of eight row
   // panels across N: with at most one tile per CU one workgroup of two K
   // groups per CU (16), otherwise two workgroups of one K group (15)
   const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
   int dflt = tiles <= (int64_t)device_cus() ? 16 : 15;
-  if (K / 8 * N * 4 > 0xFFFFFFFFLL) dflt = 9;   // beyond 32-bit buffer offsets: the third design
-  return launch_status(qg::launch_w4_prefill(p, env_variant("QG_W4_PREFILL_VARIANT", dflt), stream));
+  if (K / 8 * N * 4 > 0xFFFFFFFFLL) {           // beyond 32-bit buffer offsets: the third design
+    if (p.bf16) return QG_ERR_UNSUPPORTED;       // (fp16 only)
+    dflt = 9;
+  }
+  const int v = env_variant("QG_W4_PREFILL_VARIANT", dflt);
+  if (p.bf16 && v < 11) return QG_ERR_UNSUPPORTED;   // bf16 runs in the fourth design
+  return launch_status(qg::launch_w4_prefill(p, v, stream));
 }
 
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,

@@ -139,13 +139,12 @@ __device__ __forceinline__ u32x4_t dequant_w4_word(uint32_t w) {
   return r;
 }
 
-// (a & m) | b in one VALU op. v_and_or_b32 takes no literal operands, so the
-// mask is kept in a VGPR and the bias in an SGPR (the compiler would otherwise
-// split the expression into v_and_b32 + v_or_b32 with two literals).
+// (a & m) | b. Written in C (no inline assembly): the compiler's hazard checks
+// do not cover instructions hidden in inline assembly, and a VGPR write issued
+// right after an MFMA that reads the same register as an operand must be
+// spaced by the compiler.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(m), "s"(b));
-  return d;
+  return (a & m) | b;
 }
 
 // Same unpack as dequant_w4_word with fused mask-and-bias operations; `m` must
@@ -189,6 +188,37 @@ __device__ __forceinline__ float h2f(uint16_t h) {
 
 __device__ __forceinline__ uint16_t f2h_rn(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> a bf16 pair (lo, hi), round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f2bf2_rn(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
+
+// One packed word -> its eight weights (q - 8) * s rounded to bf16, as four bf16
+// pairs in the K-slot order of dequant_w4_word_fused: (0,4), (1,5), (2,6),
+// (3,7). The nibbles are spread into bytes (even codes of w & 0x0F0F0F0F, odd
+// codes of (w >> 4) & 0x0F0F0F0F), each byte converts to float in one
+// instruction, and q * s - 8s is exact in fp32 (at most 12 significant bits),
+// so the only rounding is the final one to bf16.
+__device__ __forceinline__ u32x4_t dequant_w4_word_bf16(uint32_t w, float s) {
+  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+  const float m8s = -8.0f * s;
+  // (v_cvt_f32_ubyte0..3: one instruction per byte)
+  const float q0 = (float)(ev & 0xFFu), q2 = (float)((ev >> 8) & 0xFFu);
+  const float q4 = (float)((ev >> 16) & 0xFFu), q6 = (float)(ev >> 24);
+  const float q1 = (float)(od & 0xFFu), q3 = (float)((od >> 8) & 0xFFu);
+  const float q5 = (float)((od >> 16) & 0xFFu), q7 = (float)(od >> 24);
+  return u32x4_t{f2bf2_rn(__builtin_fmaf(q0, s, m8s), __builtin_fmaf(q4, s, m8s)),
+                 f2bf2_rn(__builtin_fmaf(q1, s, m8s), __builtin_fmaf(q5, s, m8s)),
+                 f2bf2_rn(__builtin_fmaf(q2, s, m8s), __builtin_fmaf(q6, s, m8s)),
+                 f2bf2_rn(__builtin_fmaf(q3, s, m8s), __builtin_fmaf(q7, s, m8s))};
 }
 
 // fp32 -> bf16, round to nearest even (inputs are finite).

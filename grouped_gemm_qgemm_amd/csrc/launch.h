@@ -8,12 +8,13 @@
 namespace qg {
 
 struct W4Args {
-  uint16_t* C;          // f16 [M, N]
-  const uint16_t* A;    // f16 [M, K]
+  uint16_t* C;          // f16 or bf16 [M, N]
+  const uint16_t* A;    // f16 or bf16 [M, K]
   const uint32_t* B;    // u32 [K/8, N]
-  const uint16_t* S;    // f16 [K/group_size, N]
+  const uint16_t* S;    // f16 or bf16 [K/group_size, N]
   int64_t M, N, K;
   int group_size;
+  int bf16;             // A, S and C are bf16
 };
 
 struct W4GroupedArgs {

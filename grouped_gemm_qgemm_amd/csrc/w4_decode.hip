@@ -136,7 +136,13 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
 // once on the way in; the MFMA A fragments are then read from LDS. For small M
 // this removes the per-step A loads and K-slot permutes of the variant above
 // (rows >= M are never loaded), and the fused mask/bias unpack trims the B path.
-template <int CPL, int NW, int SPG, int MROWS, int BSTEPS>
+//
+// BF: bf16 activations, scales and output. A packed code q then enters the bf16
+// MFMA as 128 + q (exact: the pair is 0x4300 | q in each half), and one more
+// MFMA per step against a constant -136 matrix adds -136 * (sum of the row's
+// activations), so each group's partial is exactly the sum of a * (q - 8) up
+// to fp32 accumulation order.
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
 __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
@@ -153,7 +159,8 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
   const int quarter = lane >> 4;
   const int col16 = lane & 15;
   const uint32_t vmask = 0x000F000Fu;   // lives in a VGPR for the fused unpack
-  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
+  const uint32_t m136 = 0xC308C308u;    // bf16 pair (-136, -136)
 
   int strip = blockIdx.x;
   if (xcd_remap) {
@@ -228,19 +235,34 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
       float4_t part[CPL];
+      float4_t corr = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < CPL; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < SPG; ++s) {
         const int chunk = (j * SPG + s) * 4 + quarter;
         const u32x4_t a = a_lds[wave][frag_row * CH + (chunk ^ (frag_row & 15 & (CH - 1)))];
+        if constexpr (BF) {
+          corr = mfma16x16x32_bf16(a, u32x4_t{m136, m136, m136, m136}, corr);
 #pragma unroll
-        for (int t = 0; t < CPL; ++t)
-          part[t] = mfma16x16x32_f16(a, dequant_w4_word_fused(w[j][s][t], vmask, bias), part[t]);
+          for (int t = 0; t < CPL; ++t) {
+            const uint32_t wd = w[j][s][t];
+            part[t] = mfma16x16x32_bf16(a, u32x4_t{and_or(wd, vmask, bias), and_or(wd >> 4, vmask, bias),
+                                                  and_or(wd >> 8, vmask, bias), and_or(wd >> 12, vmask, bias)},
+                                        part[t]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < CPL; ++t)
+            part[t] = mfma16x16x32_f16(a, dequant_w4_word_fused(w[j][s][t], vmask, bias), part[t]);
+        }
       }
       const bool keep = col_ok && (g0 + j < g_end);
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) acc[t] += (keep ? h2f(sc[j][t]) : 0.f) * part[t];
+      for (int t = 0; t < CPL; ++t) {
+        const float sv = keep ? (BF ? bf2f(sc[j][t]) : h2f(sc[j][t])) : 0.f;
+        acc[t] += sv * (BF ? part[t] + corr : part[t]);
+      }
     }
   }
 
@@ -254,7 +276,7 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) sum += red[v][row][col];
-    if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = f2h_rn(sum);
+    if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(sum) : f2h_rn(sum);
   }
 }
 
@@ -264,8 +286,12 @@ static hipError_t launch_lds_cfg(const W4Args& p, hipStream_t stream) {
   constexpr int BSTEPS = NW >= 16 ? 8 : 16;   // LDS: NW * MROWS * BSTEPS * 64 bytes
   const int strips = (int)((p.N + SN - 1) / SN);
   const int remap = (strips % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS>), dim3(strips), dim3(NW * kWave), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
+  if (p.bf16)
+    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), dim3(strips), dim3(NW * kWave), 0,
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
+  else
+    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), dim3(strips), dim3(NW * kWave), 0,
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
   return hipGetLastError();
 }
 
@@ -313,6 +339,7 @@ static hipError_t launch_spg(const W4Args& p, hipStream_t stream) {
 
 // Variants: (columns per lane, waves per workgroup).
 hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream) {
+  if (p.bf16 && variant < 9) return hipErrorInvalidValue;   // bf16 only in the LDS-staged kernel
   switch (variant) {
     case 0: return launch_spg<1, 8>(p, stream);
     case 1: return launch_spg<2, 8>(p, stream);

@@ -608,7 +608,9 @@ struct W4TileLds {
 
 // One BM x BN output tile of the fourth design: rows m0 .. m0+BM-1 (those < M)
 // and columns n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG>
+// BF: activations, scales and output are bf16 (weights (q - 8) * s rounded to
+// bf16 through fp32, bf16 MFMAs); otherwise fp16.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
@@ -715,18 +717,27 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       u32x4_t bq[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
-        const half2_t s2 = __builtin_bit_cast(half2_t, pair);
-        const u32x4_t d = dequant_w4_word_fused((uint32_t)(w2 >> (32 * t)), vmask, bias);
-        const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
-        bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        if constexpr (BF) {
+          bq[t] = dequant_w4_word_bf16((uint32_t)(w2 >> (32 * t)), bf2f((uint16_t)(t ? sp >> 16 : sp & 0xFFFFu)));
+        } else {
+          const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
+          const half2_t s2 = __builtin_bit_cast(half2_t, pair);
+          const u32x4_t d = dequant_w4_word_fused((uint32_t)(w2 >> (32 * t)), vmask, bias);
+          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+          bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = wm * TM + mt * 32 + c32;
         const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
-        acc[mt][0] = mfma32x32x16_f16(av, bq[0], acc[mt][0]);
-        acc[mt][1] = mfma32x32x16_f16(av, bq[1], acc[mt][1]);
+        if constexpr (BF) {
+          acc[mt][0] = mfma32x32x16_bf16(av, bq[0], acc[mt][0]);
+          acc[mt][1] = mfma32x32x16_bf16(av, bq[1], acc[mt][1]);
+        } else {
+          acc[mt][0] = mfma32x32x16_f16(av, bq[0], acc[mt][0]);
+          acc[mt][1] = mfma32x32x16_f16(av, bq[1], acc[mt][1]);
+        }
       }
     }
   };
@@ -853,7 +864,8 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
         if (row < M)
           *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
-              (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+              BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
+                 : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
       }
     }
   }
@@ -862,7 +874,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 // Dense fourth-design kernel: one tile per workgroup, tile order within each
 // XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
 // swept across N.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
@@ -886,7 +898,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
     tm = first + r % gm;
     tn = r / gm;
   }
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -911,7 +923,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   const int r_begin = (int)a_off[loc.g] + chunk * BM;
   const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
   const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
                                                S + e * spe, rows, N, K, group_size, 0, nt * BN, lds);
 }
 
@@ -963,8 +975,12 @@ static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order 
   if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL || p.K / p.group_size * p.N * 2 > 0xFFFFFFFFLL) return hipErrorNotSupported;
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
   const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG>), dim3(grid), dim3(WM * WN * kWave * KG), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
+  if (p.bf16)
+    hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, true>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
+  else
+    hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, false>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
   return hipGetLastError();
 }
 
@@ -980,6 +996,7 @@ static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
 
 // Variants: tile shapes (BM x BN, wave grid).
 hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
+  if (p.bf16 && variant < 11) return hipErrorInvalidValue;   // bf16 only in the fourth design
   switch (variant) {
     case 0: return launch_tile<256, 128, 2, 2>(p, stream);
     case 1: return launch_tile<128, 128, 2, 2>(p, stream);

@@ -81,17 +81,21 @@ typedef struct {
  * word B[kp][n] holds the codes of K rows 8*kp + i (i = 0..7) in bits
  * 4i..4i+3, and code q stands for the weight (q - 8) * scales[k / group_size][n].
  *
- *   c        f16 [M, N]                      output, written entirely
- *   a        f16 [M, K]                      activations
+ *   c        f16 or bf16 [M, N]              output, written entirely
+ *   a        f16 or bf16 [M, K]              activations
  *   b_packed u32 [K / pack_factor, N]        packed 4-bit weight codes
- *   scales   f16 [K / group_size, N]         one scale per group per column
+ *   scales   f16 or bf16 [K / group_size, N] one scale per group per column
  *   group_size   multiple of 32, divides K   (QG_ERR_SHAPE / QG_ERR_UNSUPPORTED)
  *   pack_factor  must be 8                   (QG_ERR_UNSUPPORTED otherwise)
  *
- * Accumulation is fp32; the result is rounded to fp16 (nearest-even).
- * N must be a multiple of 8 and K a multiple of group_size (QG_ERR_ALIGN /
- * QG_ERR_SHAPE). M <= 16 runs the skinny-M (decode) kernel, larger M the
- * MFMA-tiled (prefill) kernel.
+ * a, scales and c share one type, fp16 or bf16 (the page's a_type and c_type
+ * parameters; QG_ERR_DTYPE when they differ). Accumulation is fp32; the result
+ * is rounded to the output type (nearest-even). N must be a multiple of 8 and K a
+ * multiple of group_size (QG_ERR_ALIGN / QG_ERR_SHAPE). M <= 16 runs the
+ * skinny-M (decode) kernel, which keeps (q - 8) exact and scales each group's
+ * fp32 partial; larger M the MFMA-tiled (prefill) kernel, which rounds each
+ * weight (q - 8) * scale to the activation type before its MFMAs. bf16 with a
+ * packed matrix beyond 2^32 - 1 bytes returns QG_ERR_UNSUPPORTED.
  */
 qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
                    const qg_tensor* scales, int32_t group_size, int32_t pack_factor,

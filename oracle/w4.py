@@ -13,12 +13,19 @@ Readings where the page is silent (each also a parity assumption):
     runs of K starting at k = 0, so row k uses scale row k // group_size.
   * A code q in 0..15 stands for the weight (q - 8) * scale (no zero-point array).
   * The result is rounded to fp16 with round-to-nearest-even.
+  * a_type / c_type (Parameters): activations, scales and result share one type,
+    fp16 (the default) or bf16; the arithmetic is the same, only the decoding of
+    the inputs and the rounding of the result change.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .numerics import decode_f16, round_to_f16, f16_bits_of
+from .numerics import (bf16_bits_of, decode_bf16, decode_f16, f16_bits_of, round_to_bf16,
+                       round_to_f16)
+
+_DECODE = {"f16": decode_f16, "bf16": decode_bf16}
+_ROUND = {"f16": (round_to_f16, f16_bits_of), "bf16": (round_to_bf16, bf16_bits_of)}
 
 
 def _check_rank2(*arrs):
@@ -27,8 +34,8 @@ def _check_rank2(*arrs):
             raise ValueError("multistage_gemm_q: input tensors must be rank-2")
 
 
-def dequant_w4(b_packed, scales_bits, group_size: int, pack_factor: int = 8) -> np.ndarray:
-    """Packed codes + fp16 scales -> float64 weights W [K, N] (exact)."""
+def dequant_w4(b_packed, scales_bits, group_size: int, pack_factor: int = 8, dtype: str = "f16") -> np.ndarray:
+    """Packed codes + fp16 (or bf16) scales -> float64 weights W [K, N] (exact)."""
     _check_rank2(b_packed, scales_bits)
     if pack_factor != 8:
         raise ValueError("only 8 four-bit codes per uint32 exist")
@@ -37,7 +44,7 @@ def dequant_w4(b_packed, scales_bits, group_size: int, pack_factor: int = 8) -> 
     K = kp * pack_factor
     if K % group_size:
         raise ValueError("K must be a multiple of group_size")
-    s = decode_f16(scales_bits)
+    s = _DECODE[dtype](scales_bits)
     if s.shape != (K // group_size, n):
         raise ValueError("scales must be [K/group_size, N]")
     shifts = (4 * np.arange(pack_factor, dtype=np.uint32))[None, :, None]
@@ -47,18 +54,21 @@ def dequant_w4(b_packed, scales_bits, group_size: int, pack_factor: int = 8) -> 
     return (q - 8).astype(np.float64) * s[group_of_k, :]
 
 
-def qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size: int, pack_factor: int = 8) -> np.ndarray:
+def qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size: int, pack_factor: int = 8,
+                 dtype: str = "f16") -> np.ndarray:
     """Unrounded fp64 product A . W."""
     _check_rank2(a_bits, b_packed, scales_bits)
-    a = decode_f16(a_bits)
-    w = dequant_w4(b_packed, scales_bits, group_size, pack_factor)
+    a = _DECODE[dtype](a_bits)
+    w = dequant_w4(b_packed, scales_bits, group_size, pack_factor, dtype)
     if a.shape[1] != w.shape[0]:
         raise ValueError("A is [M, K] and B unpacks to [K, N]")
     return a @ w
 
 
-def qgemm_w4(a_bits, b_packed, scales_bits, group_size: int, pack_factor: int = 8) -> np.ndarray:
-    """C = round_fp16(A . dequant(B)) as fp16 bit patterns [M, N]."""
-    c = round_to_f16(qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor))
-    assert np.all(np.isfinite(c)), "fp16 overflow in the reference result"
-    return f16_bits_of(c)
+def qgemm_w4(a_bits, b_packed, scales_bits, group_size: int, pack_factor: int = 8,
+             dtype: str = "f16") -> np.ndarray:
+    """C = round(A . dequant(B)) as fp16 (or bf16) bit patterns [M, N]."""
+    rnd, bits_of = _ROUND[dtype]
+    c = rnd(qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor, dtype))
+    assert np.all(np.isfinite(c)), "overflow in the reference result"
+    return bits_of(c)

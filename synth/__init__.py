@@ -65,35 +65,41 @@ def e4m3_codes(x: np.ndarray) -> np.ndarray:
 
 @dataclasses.dataclass
 class W4Inputs:
-    a: np.ndarray          # uint16 [M, K]   fp16 bits
+    a: np.ndarray          # uint16 [M, K]   fp16 (or bf16) bits
     b: np.ndarray          # uint32 [K/8, N] packed 4-bit codes
-    scales: np.ndarray     # uint16 [K/group_size, N] fp16 bits
+    scales: np.ndarray     # uint16 [K/group_size, N] fp16 (or bf16) bits
     group_size: int
+    dtype: str = "f16"     # storage type of a and scales (and of the result)
 
     @property
     def shape(self):
         return self.a.shape[0], self.b.shape[1], self.a.shape[1]
 
 
-def w4_weights(seed: int, N: int, K: int, group_size: int = 128):
+def _bits(x, dtype: str):
+    return bf16_bits(x) if dtype == "bf16" else f16_bits(x)
+
+
+def w4_weights(seed: int, N: int, K: int, group_size: int = 128, dtype: str = "f16"):
     """Packed weights and scales for an N x K problem (draw order: words, scales)."""
     rng = np.random.default_rng(seed)
     b = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
-    s = f16_bits(rng.uniform(0.005, 0.02, size=(K // group_size, N)))
+    s = _bits(rng.uniform(0.005, 0.02, size=(K // group_size, N)), dtype)
     return b, s
 
 
-def w4_activations(seed: int, M: int, K: int):
+def w4_activations(seed: int, M: int, K: int, dtype: str = "f16"):
     rng = np.random.default_rng(seed)
-    return f16_bits(rng.standard_normal((M, K)))
+    return _bits(rng.standard_normal((M, K)), dtype)
 
 
 def w4_inputs(M: int, N: int, K: int, seed: int = 1, a_seed: int | None = None,
-              group_size: int = 128) -> W4Inputs:
-    """W4A16 problem: weights from `seed`, activations from `a_seed` (default: seed+100)."""
-    b, s = w4_weights(seed, N, K, group_size)
-    a = w4_activations(seed + 100 if a_seed is None else a_seed, M, K)
-    return W4Inputs(a=a, b=b, scales=s, group_size=group_size)
+              group_size: int = 128, dtype: str = "f16") -> W4Inputs:
+    """W4A16 problem: weights from `seed`, activations from `a_seed` (default: seed+100);
+    dtype "f16" or "bf16" stores the activations and scales (the same draws)."""
+    b, s = w4_weights(seed, N, K, group_size, dtype)
+    a = w4_activations(seed + 100 if a_seed is None else a_seed, M, K, dtype)
+    return W4Inputs(a=a, b=b, scales=s, group_size=group_size, dtype=dtype)
 
 
 # Named W4 workloads: (M, N, K, weight seed, activation seed)

@@ -81,6 +81,11 @@ def test_w4_rejections(lib):
     assert w4_call(lib, bb.t((1, 4, 64), QG.F16), a, b, s) == QG.ERR_RANK
     assert w4_call(lib, c, a, bb.t((32 * 64,), QG.U32), s) == QG.ERR_RANK
     assert w4_call(lib, c, bb.t((4, 256), QG.BF16), b, s) == QG.ERR_DTYPE
+    # bf16 activations need bf16 scales and output (one type for all three)
+    cb, ab, sb = bb.t((4, 64), QG.BF16), bb.t((4, 256), QG.BF16), bb.t((2, 64), QG.BF16)
+    assert w4_call(lib, cb, ab, b, s) == QG.ERR_DTYPE
+    assert w4_call(lib, c, ab, b, sb) == QG.ERR_DTYPE
+    assert w4_call(lib, cb, ab, b, sb, pf=4) == QG.ERR_UNSUPPORTED
     assert w4_call(lib, c, a, bb.t((32, 64), QG.I32), s) == QG.ERR_DTYPE
     assert w4_call(lib, c, a, b, s, pf=4) == QG.ERR_UNSUPPORTED
     assert w4_call(lib, c, a, b, s, gs=100) == QG.ERR_SHAPE

@@ -15,10 +15,10 @@ _orig_dequant = ow4.dequant_w4
 
 
 def _dequant_variant(kind):
-    def f(b_packed, scales_bits, group_size, pack_factor=8):
+    def f(b_packed, scales_bits, group_size, pack_factor=8, dtype="f16"):
         b = np.asarray(b_packed, dtype=np.uint32)
         K = b.shape[0] * 8
-        s = nm.decode_f16(scales_bits)
+        s = nm.decode_bf16(scales_bits) if dtype == "bf16" and kind != "bf16_as_f16" else nm.decode_f16(scales_bits)
         order = np.arange(8)[::-1] if kind == "nibble_order" else np.arange(8)
         shifts = (4 * order.astype(np.uint32))[None, :, None]
         q = ((b[:, None, :] >> shifts) & np.uint32(0xF)).astype(np.int64).reshape(K, -1)
@@ -36,11 +36,14 @@ W4_PINS = [tw4.test_worked_examples_from_fixture, tw4.test_nibble_position,
            tw4.test_identity_gives_unpacked_weights_exactly, tw4.test_closed_form_ones_and_power_of_two_scales]
 
 
-@pytest.mark.parametrize("kind", ["nibble_order", "zero_point", "group_index", "signed_code"])
+W4_BF16_PINS = [lambda: tw4.test_bf16_brute_force_small(3, 5, 256, 64), tw4.test_bf16_unit_rows_read_codes_back]
+
+
+@pytest.mark.parametrize("kind", ["nibble_order", "zero_point", "group_index", "signed_code", "bf16_as_f16"])
 def test_w4_mutation_is_caught(kind, monkeypatch):
     monkeypatch.setattr(ow4, "dequant_w4", _dequant_variant(kind))
     failures = 0
-    for pin in W4_PINS:
+    for pin in (W4_BF16_PINS if kind == "bf16_as_f16" else W4_PINS):
         try:
             pin()
         except AssertionError:

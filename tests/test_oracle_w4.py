@@ -158,3 +158,61 @@ def test_rank2_is_required():
         oracle.qgemm_w4(w.a[None], w.b, w.scales, 128)
     with pytest.raises(ValueError):
         oracle.qgemm_w4(w.a, w.b.ravel(), w.scales, 128)
+
+
+# ---- bf16 activations / scales / result (the page's a_type and c_type) ----
+
+def _bf16_to_f64(bits):
+    """bfloat16 bit patterns -> float64 by placing them in the top half of a float32."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,N,K,gs", [(1, 3, 128, 128), (3, 5, 256, 64), (2, 4, 64, 32)])
+def test_bf16_brute_force_small(M, N, K, gs):
+    """Scalar loops over the bf16 inputs (decoded here by bit placement, not by
+    the oracle's decoder) against the oracle's unrounded product."""
+    w = synth.w4_inputs(M, N, K, seed=31 + M, group_size=gs, dtype="bf16")
+    a = _bf16_to_f64(w.a)
+    s = _bf16_to_f64(w.scales)
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                q = (int(w.b[k // 8, n]) >> (4 * (k % 8))) & 0xF
+                acc += a[m, k] * (q - 8) * s[k // gs, n]
+            ref[m, n] = acc
+    got = oracle.w4.qgemm_w4_f64(w.a, w.b, w.scales, gs, dtype="bf16")
+    assert np.allclose(got, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+
+
+def test_bf16_unit_rows_read_codes_back():
+    """A = identity rows: row k of C is W[k, :] = (q - 8) * s, which is exact in
+    bf16 whenever s is a power of two."""
+    K, N, gs = 64, 16, 32
+    rng = np.random.default_rng(5)
+    b = rng.integers(0, 2**32, size=(K // 8, N), dtype=np.uint32)
+    s_vals = 2.0 ** rng.integers(-6, 0, size=(K // gs, N))
+    s = synth.bf16_bits(s_vals)
+    a = synth.bf16_bits(np.eye(K))
+    c = _bf16_to_f64(oracle.qgemm_w4(a, b, s, gs, dtype="bf16"))
+    codes = np.array([[(int(b[k // 8, n]) >> (4 * (k % 8))) & 0xF for n in range(N)] for k in range(K)])
+    assert np.array_equal(c, (codes - 8) * s_vals[np.arange(K) // gs])
+
+
+def test_bf16_result_rounding_differs_from_f16():
+    """The same exactly representable inputs give the bf16-rounded product: a sum
+    whose exact value needs more than 8 significant bits rounds to nearest even."""
+    K, N, gs = 32, 1, 32
+    # one active code per row: a = [1 + 2^-7] at k = 0, code 9 (weight +1 * s), s = 1
+    a = np.zeros((1, K))
+    a[0, 0] = 1.0 + 2.0 ** -7
+    a[0, 1] = 2.0 ** -9          # tips the sum to 1 + 2^-7 + 2^-9: between bf16 neighbours
+    b = np.full((K // 8, N), 0x88888888, np.uint32)   # code 8 (weight 0) everywhere...
+    b[0, 0] = 0x88888899                               # ...but codes 9 at k = 0 and k = 1
+    s = synth.bf16_bits(np.ones((1, N)))
+    got = _bf16_to_f64(oracle.qgemm_w4(synth.bf16_bits(a), b, s, gs, dtype="bf16"))[0, 0]
+    exact = 1.0 + 2.0 ** -7 + 2.0 ** -9
+    assert got == 1.0 + 2.0 ** -7             # bf16 nearest of the exact sum (8 significant bits)
+    f16 = oracle.qgemm_w4(synth.f16_bits(a), b, synth.f16_bits(np.ones((1, N))), gs).view(np.float16)[0, 0]
+    assert float(f16) == exact                # fp16 keeps it
