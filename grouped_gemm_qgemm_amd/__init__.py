@@ -8,6 +8,8 @@ built, load() raises: there is no fallback path.
 
 Entry points (same names as the C ABI):
     qgemm_w4(c, a, b_packed, scales, group_size=128, pack_factor=8)
+    qgemm_w4_epilogue(c, a, b_packed, scales, epilogue, bias=None, residual=None,
+                      group_size=128, pack_factor=8)
     grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
     grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats,
                     group_size=128, pack_factor=8)
@@ -23,8 +25,12 @@ import os
 
 import torch
 
-__all__ = ["load", "QgError", "qgemm_w4", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
-           "status_string", "LIB_PATH", "QG"]
+__all__ = ["load", "QgError", "qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4",
+           "k_matmul_ragged_paged_scale", "status_string", "LIB_PATH", "QG", "EPI_BIAS", "EPI_RESIDUAL",
+           "EPI_SILU_GATE"]
+
+# qgemm_w4_epilogue flags
+EPI_BIAS, EPI_RESIDUAL, EPI_SILU_GATE = 1, 2, 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqgemm.so")
 
@@ -73,6 +79,9 @@ def load(path: str | None = None):
     T = ctypes.POINTER(QgTensor)
     lib.qgemm_w4.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.qgemm_w4.restype = ctypes.c_int
+    lib.qgemm_w4_epilogue.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, T, T,
+                                      ctypes.c_void_p]
+    lib.qgemm_w4_epilogue.restype = ctypes.c_int
     lib.grouped_gemm.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                  ctypes.c_void_p]
     lib.grouped_gemm.restype = ctypes.c_int
@@ -138,6 +147,21 @@ def qgemm_w4(c, a, b_packed, scales, group_size: int = 128, pack_factor: int = 8
     st = lib.qgemm_w4(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
                       ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
                       group_size, pack_factor, _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def qgemm_w4_epilogue(c, a, b_packed, scales, epilogue: int, bias=None, residual=None, group_size: int = 128,
+                      pack_factor: int = 8, stream=None, raise_on_error: bool = True) -> int:
+    """qgemm_w4 followed by a fixed epilogue (EPI_BIAS | EPI_SILU_GATE | EPI_RESIDUAL)."""
+    lib = load()
+    st = lib.qgemm_w4_epilogue(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                               ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
+                               group_size, pack_factor, int(epilogue),
+                               ctypes.byref(describe(bias)) if bias is not None else None,
+                               ctypes.byref(describe(residual)) if residual is not None else None,
+                               _stream(stream))
     if raise_on_error:
         _check(st)
     return st

@@ -80,9 +80,10 @@ const char* qg_status_string(qg_status s) {
 
 int32_t qg_version(void) { return 100; }
 
-qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
-                   const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
-                   hipStream_t stream) {
+static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                               const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                               int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
+                               hipStream_t stream) {
   if (!c || !a || !b_packed || !scales) return QG_ERR_NULL;
   // rank-2 requirement first: the page's only stated error condition
   if (c->rank != 2 || a->rank != 2 || b_packed->rank != 2 || scales->rank != 2) return QG_ERR_RANK;
@@ -96,23 +97,44 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   if ((st = check_tensor(scales, 2, act)) != QG_OK) return st;
   if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
   if (group_size <= 0) return QG_ERR_INVALID_ARG;
-  const int64_t M = a->shape[0], K = a->shape[1], N = c->shape[1];
-  if (c->shape[0] != M) return QG_ERR_SHAPE;
+  if (epilogue & ~(QG_EPI_BIAS | QG_EPI_RESIDUAL | QG_EPI_SILU_GATE)) return QG_ERR_INVALID_ARG;
+  const int64_t M = a->shape[0], K = a->shape[1], N = b_packed->shape[1];
+  const bool gate = (epilogue & QG_EPI_SILU_GATE) != 0;
+  if (gate && N % 16 != 0) return QG_ERR_ALIGN;   // (gate, up) pairs, and an 8-aligned output
+  const int64_t N_out = gate ? N / 2 : N;
+  if (c->shape[0] != M || c->shape[1] != N_out) return QG_ERR_SHAPE;
   if (K % group_size != 0) return QG_ERR_SHAPE;
-  if (b_packed->shape[0] * pack_factor != K || b_packed->shape[1] != N) return QG_ERR_SHAPE;
+  if (b_packed->shape[0] * pack_factor != K) return QG_ERR_SHAPE;
   if (scales->shape[0] != K / group_size || scales->shape[1] != N) return QG_ERR_SHAPE;
   if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
     return QG_ERR_UNSUPPORTED;
   if (N % 8 != 0) return QG_ERR_ALIGN;
+  qg::W4Epilogue epi;
+  epi.flags = epilogue;
+  if (epilogue & QG_EPI_BIAS) {
+    if (!bias) return QG_ERR_NULL;
+    if (bias->rank != 1) return QG_ERR_RANK;
+    if ((st = check_tensor(bias, 1, act)) != QG_OK) return st;
+    if (bias->shape[0] != N) return QG_ERR_SHAPE;
+    epi.bias = static_cast<const uint16_t*>(bias->data);
+  }
+  if (epilogue & QG_EPI_RESIDUAL) {
+    if (!residual) return QG_ERR_NULL;
+    if (residual->rank != 2) return QG_ERR_RANK;
+    if ((st = check_tensor(residual, 2, act)) != QG_OK) return st;
+    if (residual->shape[0] != M || residual->shape[1] != N_out) return QG_ERR_SHAPE;
+    epi.residual = static_cast<const uint16_t*>(residual->data);
+  }
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of C
   qg::W4Args p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
-               M, N, K, group_size, act == QG_BF16 ? 1 : 0};
+               M, N, K, group_size, act == QG_BF16 ? 1 : 0, epi};
+  const bool wide = p.bf16 || epilogue;   // bf16 and epilogues run in the newer kernels
   if (M <= 16) {
     const int v = env_variant("QG_W4_DECODE_VARIANT", 9);
-    if (p.bf16 && v < 9) return QG_ERR_UNSUPPORTED;   // bf16 runs in the LDS-staged decode kernel
+    if (wide && v < 9) return QG_ERR_UNSUPPORTED;   // the LDS-staged decode kernel
     return launch_status(qg::launch_w4_decode(p, v, stream));
   }
   // 128 x 256 tiles of 32x32x16 MFMAs, each XCD sweeping groups of eight row
@@ -121,12 +143,25 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
   const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
   int dflt = tiles <= (int64_t)device_cus() ? 16 : 15;
   if (K / 8 * N * 4 > 0xFFFFFFFFLL) {           // beyond 32-bit buffer offsets: the third design
-    if (p.bf16) return QG_ERR_UNSUPPORTED;       // (fp16 only)
+    if (wide) return QG_ERR_UNSUPPORTED;         // (fp16 only, no epilogue)
     dflt = 9;
   }
   const int v = env_variant("QG_W4_PREFILL_VARIANT", dflt);
-  if (p.bf16 && v < 11) return QG_ERR_UNSUPPORTED;   // bf16 runs in the fourth design
+  if (wide && v < 11) return QG_ERR_UNSUPPORTED;   // the fourth design
   return launch_status(qg::launch_w4_prefill(p, v, stream));
+}
+
+qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                   const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                   hipStream_t stream) {
+  return qgemm_w4_impl(c, a, b_packed, scales, group_size, pack_factor, 0, nullptr, nullptr, stream);
+}
+
+qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                            const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                            int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
+                            hipStream_t stream) {
+  return qgemm_w4_impl(c, a, b_packed, scales, group_size, pack_factor, epilogue, bias, residual, stream);
 }
 
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,

@@ -7,6 +7,18 @@
 
 namespace qg {
 
+// Fixed epilogue of the W4 GEMM, applied in fp32 before the output rounding.
+// EPI_BIAS: y += bias[n]; EPI_SILU_GATE: columns come in (gate, up) pairs and
+// z[m][j] = silu(y[m][2j]) * y[m][2j+1] (output N / 2 wide); EPI_RESIDUAL:
+// z += residual[m][j] (residual shaped like the output). Bias and residual have
+// the output type.
+enum { EPI_BIAS = 1, EPI_RESIDUAL = 2, EPI_SILU_GATE = 4 };
+struct W4Epilogue {
+  const uint16_t* bias = nullptr;      // [N]
+  const uint16_t* residual = nullptr;  // [M, N_out]
+  int flags = 0;
+};
+
 struct W4Args {
   uint16_t* C;          // f16 or bf16 [M, N]
   const uint16_t* A;    // f16 or bf16 [M, K]
@@ -15,6 +27,7 @@ struct W4Args {
   int64_t M, N, K;
   int group_size;
   int bf16;             // A, S and C are bf16
+  W4Epilogue epi;       // C is [M, N / 2] with EPI_SILU_GATE
 };
 
 struct W4GroupedArgs {

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
 template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
 __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, W4Epilogue ep) {
   constexpr int SN = 16 * CPL;
   constexpr int STEPS = SPG > BSTEPS ? SPG : BSTEPS;   // K steps per batch
   constexpr int GB = STEPS / SPG;              // groups per batch
@@ -276,7 +276,26 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) sum += red[v][row][col];
-    if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(sum) : f2h_rn(sum);
+    if (ep.flags == 0) {
+      if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(sum) : f2h_rn(sum);
+    } else if (!(ep.flags & 4) || !(col & 1)) {
+      // epilogue on column pairs (col, col + 1): the thread of the even column
+      // also sums the odd one (the strip width and n0 are even)
+      float sum1 = 0.f;
+      if (col + 1 < SN) {
+#pragma unroll
+        for (int v = 0; v < NW; ++v) sum1 += red[v][row][col + 1];
+      }
+      if (ep.flags & 4) {
+        if (row < M && n0 + col < N) store_pair_epi<BF>(C, N, row, n0 + col, sum, sum1, ep);
+      } else if (row < M && n0 + col < N) {
+        // one column per thread without the gate
+        float y = sum;
+        if (ep.flags & 1) y += ld16<BF>(ep.bias, n0 + col);
+        if (ep.flags & 2) y += ld16<BF>(ep.residual, (size_t)row * N + n0 + col);
+        C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(y) : f2h_rn(y);
+      }
+    }
   }
 }
 
@@ -288,10 +307,10 @@ static hipError_t launch_lds_cfg(const W4Args& p, hipStream_t stream) {
   const int remap = (strips % 8 == 0) ? 1 : 0;
   if (p.bf16)
     hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), dim3(strips), dim3(NW * kWave), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap, p.epi);
   else
     hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), dim3(strips), dim3(NW * kWave), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap, p.epi);
   return hipGetLastError();
 }
 
@@ -339,7 +358,7 @@ static hipError_t launch_spg(const W4Args& p, hipStream_t stream) {
 
 // Variants: (columns per lane, waves per workgroup).
 hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream) {
-  if (p.bf16 && variant < 9) return hipErrorInvalidValue;   // bf16 only in the LDS-staged kernel
+  if ((p.bf16 || p.epi.flags) && variant < 9) return hipErrorInvalidValue;   // bf16, epilogues: LDS-staged kernel
   switch (variant) {
     case 0: return launch_spg<1, 8>(p, stream);
     case 1: return launch_spg<2, 8>(p, stream);

@@ -614,7 +614,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = fa
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
-                                             W4TileLds<BM, BN, KG>& lds) {
+                                             W4TileLds<BM, BN, KG>& lds, const W4Epilogue& ep) {
   constexpr int NTHR = WAVES_M * WAVES_N * kWave;   // threads of one K group
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
@@ -854,7 +854,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     if (kt < nk) compute(0, sc_cur);   // nk odd: the last stage sits in buffer 0
   }
 
-  // epilogue: two adjacent columns per 4-byte store
+  // epilogue: two adjacent columns per 4-byte store (or one gated output)
   const int col = n0 + wn * TN + 2 * c32;
   if (col < N) {
 #pragma unroll
@@ -862,10 +862,14 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (row < M)
-          *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
-              BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
-                 : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+        if (row < M) {
+          if (ep.flags == 0)
+            *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
+                BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
+                   : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+          else
+            store_pair_epi<BF>(C, N, row, col, acc[mt][0][i], acc[mt][1][i], ep);
+        }
       }
     }
   }
@@ -877,7 +881,8 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order) {
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
+    W4Epilogue ep) {
   __shared__ W4TileLds<BM, BN, KG> lds;
   const int tiles = tiles_m * tiles_n;
   const int per = (tiles + 7) >> 3;
@@ -898,7 +903,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
     tm = first + r % gm;
     tn = r / gm;
   }
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
   const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
   w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
-                                               S + e * spe, rows, N, K, group_size, 0, nt * BN, lds);
+                                               S + e * spe, rows, N, K, group_size, 0, nt * BN, lds, W4Epilogue{});
 }
 
 template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1>
@@ -977,10 +982,10 @@ static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order 
   const int grid = ((tm * tn + 7) / 8) * 8;
   if (p.bf16)
     hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, true>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order, p.epi);
   else
     hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, false>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order);
+                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order, p.epi);
   return hipGetLastError();
 }
 
@@ -996,7 +1001,7 @@ static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
 
 // Variants: tile shapes (BM x BN, wave grid).
 hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
-  if (p.bf16 && variant < 11) return hipErrorInvalidValue;   // bf16 only in the fourth design
+  if ((p.bf16 || p.epi.flags) && variant < 11) return hipErrorInvalidValue;   // bf16 and epilogues: fourth design
   switch (variant) {
     case 0: return launch_tile<256, 128, 2, 2>(p, stream);
     case 1: return launch_tile<128, 128, 2, 2>(p, stream);

@@ -102,6 +102,33 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
                    hipStream_t stream);
 
 /*
+ * qgemm_w4_epilogue - qgemm_w4 with a fixed epilogue
+ *
+ * Stands in for the page's elementwise_lambda_fn parameter (Parameters: a
+ * device function run on each output element), which a C ABI cannot carry:
+ * a bitwise OR of the operations below, applied to the fp32 product Y =
+ * A . dequant(B) ([M, N]) before the single rounding to the output type.
+ *
+ *   QG_EPI_BIAS       Y[m][n] += bias[n]                    bias [N]
+ *   QG_EPI_SILU_GATE  columns come in (gate, up) pairs:     c [M, N / 2]
+ *                     Z[m][j] = silu(Y[m][2j]) * Y[m][2j+1], silu(x) = x / (1 + e^-x)
+ *                     (without it Z = Y, c [M, N])
+ *   QG_EPI_RESIDUAL   Z[m][j] += residual[m][j]             residual shaped like c
+ *
+ * bias and residual have the activations' type (fp16 or bf16) and may be NULL
+ * when their operation is not requested (QG_ERR_NULL otherwise). Other flag bits
+ * are QG_ERR_INVALID_ARG; with QG_EPI_SILU_GATE, N must be a multiple of 16
+ * (QG_ERR_ALIGN). Everything else as qgemm_w4; epilogue 0 is qgemm_w4.
+ */
+#define QG_EPI_BIAS 1
+#define QG_EPI_RESIDUAL 2
+#define QG_EPI_SILU_GATE 4
+qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                            const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                            int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
+                            hipStream_t stream);
+
+/*
  * grouped_gemm - per-group GEMM over routed rows (MoE expert GEMM)
  *
  * Follows "grouped_matmul_sm100_persistent" (Args): a_offsets is the per-expert

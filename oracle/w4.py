@@ -16,6 +16,11 @@ Readings where the page is silent (each also a parity assumption):
   * a_type / c_type (Parameters): activations, scales and result share one type,
     fp16 (the default) or bf16; the arithmetic is the same, only the decoding of
     the inputs and the rounding of the result change.
+  * Epilogue (Parameters, the optional per-output-element function): a C ABI
+    cannot carry a device function, so three fixed element-wise steps stand in
+    for it, applied to the exact fp64 product before the single rounding:
+    bias add over columns, then a SiLU-gated product of column pairs
+    (2j, 2j+1) that halves N, then a residual add. SiLU is x / (1 + e^-x).
 """
 from __future__ import annotations
 
@@ -70,5 +75,33 @@ def qgemm_w4(a_bits, b_packed, scales_bits, group_size: int, pack_factor: int = 
     """C = round(A . dequant(B)) as fp16 (or bf16) bit patterns [M, N]."""
     rnd, bits_of = _ROUND[dtype]
     c = rnd(qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor, dtype))
+    assert np.all(np.isfinite(c)), "overflow in the reference result"
+    return bits_of(c)
+
+
+# Fixed epilogue flags (the C ABI's qgemm_w4_epilogue); they stand in for the
+# page's optional per-element epilogue function.
+EPI_BIAS, EPI_RESIDUAL, EPI_SILU_GATE = 1, 2, 4
+
+
+def silu(x):
+    """x * sigmoid(x) with sigmoid(x) = 1 / (1 + e^-x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def qgemm_w4_epilogue(a_bits, b_packed, scales_bits, group_size: int, epilogue: int, bias_bits=None,
+                      residual_bits=None, pack_factor: int = 8, dtype: str = "f16") -> np.ndarray:
+    """Y = A . dequant(B) in fp64; Y += bias (EPI_BIAS); Z = silu(Y[:, 0::2]) * Y[:, 1::2]
+    (EPI_SILU_GATE, else Z = Y); Z += residual (EPI_RESIDUAL); one rounding to `dtype`."""
+    dec = _DECODE[dtype]
+    rnd, bits_of = _ROUND[dtype]
+    y = qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor, dtype)
+    if epilogue & EPI_BIAS:
+        y = y + dec(bias_bits)[None, :]
+    z = silu(y[:, 0::2]) * y[:, 1::2] if epilogue & EPI_SILU_GATE else y
+    if epilogue & EPI_RESIDUAL:
+        z = z + dec(residual_bits)
+    c = rnd(z)
     assert np.all(np.isfinite(c)), "overflow in the reference result"
     return bits_of(c)

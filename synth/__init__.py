@@ -102,6 +102,15 @@ def w4_inputs(M: int, N: int, K: int, seed: int = 1, a_seed: int | None = None,
     return W4Inputs(a=a, b=b, scales=s, group_size=group_size, dtype=dtype)
 
 
+def w4_epilogue_operands(seed: int, M: int, N_out: int, N: int, dtype: str = "f16"):
+    """Bias [N] and residual [M, N_out] for the fixed W4 epilogues (draw order:
+    bias, residual), standard normal in `dtype`."""
+    rng = np.random.default_rng(seed)
+    bias = _bits(rng.standard_normal(N), dtype)
+    residual = _bits(rng.standard_normal((M, N_out)), dtype)
+    return bias, residual
+
+
 # Named W4 workloads: (M, N, K, weight seed, activation seed)
 W4_TINY = dict(M=16, N=256, K=512, seed=1, a_seed=101)
 W4_DECODE = [dict(M=m, N=4096, K=4096, seed=2, a_seed=200 + m) for m in (1, 4, 16)]

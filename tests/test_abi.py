@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"qgemm_w4", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
+    assert {"qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
             "qg_status_string"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -106,6 +106,44 @@ def test_w4_empty_problem_is_a_noop(lib):
     bb = Buf()
     c, a, b, s = w4_args(bb, M=0)
     assert w4_call(lib, c, a, b, s) == QG.OK
+
+
+def epi_call(lib, c, a, b, s, flags, bias=None, res=None, gs=128):
+    r = lambda t: ctypes.byref(t) if t is not None else None
+    return lib.qgemm_w4_epilogue(ctypes.byref(c), ctypes.byref(a), ctypes.byref(b), ctypes.byref(s), gs, 8,
+                                 flags, r(bias), r(res), None)
+
+
+def test_w4_epilogue_rejections(lib):
+    bb = Buf()
+    M, N, K = 4, 64, 256
+    c, a, b, s = w4_args(bb, M=M, N=N, K=K)
+    bias, res = bb.t((N,), QG.F16), bb.t((M, N), QG.F16)
+    half = bb.t((M, N // 2), QG.F16)
+    # unknown flag bits
+    assert epi_call(lib, c, a, b, s, 8) == QG.ERR_INVALID_ARG
+    assert epi_call(lib, c, a, b, s, -1) == QG.ERR_INVALID_ARG
+    # a requested operand must be given
+    assert epi_call(lib, c, a, b, s, q.EPI_BIAS) == QG.ERR_NULL
+    assert epi_call(lib, c, a, b, s, q.EPI_RESIDUAL, bias=bias) == QG.ERR_NULL
+    # bias: rank 1, the activations' type, N entries
+    assert epi_call(lib, c, a, b, s, q.EPI_BIAS, bias=bb.t((1, N), QG.F16)) == QG.ERR_RANK
+    assert epi_call(lib, c, a, b, s, q.EPI_BIAS, bias=bb.t((N,), QG.BF16)) == QG.ERR_DTYPE
+    assert epi_call(lib, c, a, b, s, q.EPI_BIAS, bias=bb.t((N - 8,), QG.F16)) == QG.ERR_SHAPE
+    # residual: shaped like the output
+    assert epi_call(lib, c, a, b, s, q.EPI_RESIDUAL, res=bb.t((M * N,), QG.F16)) == QG.ERR_RANK
+    assert epi_call(lib, c, a, b, s, q.EPI_RESIDUAL, res=bb.t((M, N), QG.BF16)) == QG.ERR_DTYPE
+    assert epi_call(lib, c, a, b, s, q.EPI_RESIDUAL, res=bb.t((M, N - 8), QG.F16)) == QG.ERR_SHAPE
+    # SiLU gate halves N: the output (and residual) are [M, N / 2]
+    assert epi_call(lib, c, a, b, s, q.EPI_SILU_GATE) == QG.ERR_SHAPE
+    assert epi_call(lib, half, a, b, s, q.EPI_SILU_GATE | q.EPI_RESIDUAL, res=res) == QG.ERR_SHAPE
+    c2, a2, b2, s2 = w4_args(bb, M=M, N=72, K=K)   # N % 8 == 0 but N % 16 != 0
+    assert epi_call(lib, bb.t((M, 36), QG.F16), a2, b2, s2, q.EPI_SILU_GATE) == QG.ERR_ALIGN
+    # empty problems with valid epilogue operands are no-ops
+    c0, a0, b0, s0 = w4_args(bb, M=0, N=N, K=K)
+    assert epi_call(lib, bb.t((0, N // 2), QG.F16), a0, b0, s0, 7, bias=bias,
+                    res=bb.t((0, N // 2), QG.F16)) == QG.OK
+    assert epi_call(lib, c0, a0, b0, s0, 0) == QG.OK
 
 
 def gg_call(lib, c, a, off, b, ids, usage, tb=1):

@@ -51,6 +51,46 @@ def test_w4_mutation_is_caught(kind, monkeypatch):
     assert failures >= 1, kind
 
 
+def _epilogue_variant(kind):
+    def f(a_bits, b_packed, scales_bits, group_size, epilogue, bias_bits=None, residual_bits=None,
+          pack_factor=8, dtype="f16"):
+        dec = ow4._DECODE[dtype]
+        rnd, bits_of = ow4._ROUND[dtype]
+        y = ow4.qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor, dtype)
+        if kind == "early_rounding":
+            y = rnd(y)
+        silu = (lambda x: x / (1.0 + np.exp(x))) if kind == "silu_sign" else ow4.silu
+        if epilogue & ow4.EPI_BIAS and kind != "bias_after_gate":
+            y = y + dec(bias_bits)[None, :]
+        if epilogue & ow4.EPI_SILU_GATE:
+            z = silu(y[:, 1::2]) * y[:, 0::2] if kind == "gate_swapped" else silu(y[:, 0::2]) * y[:, 1::2]
+        else:
+            z = y
+        if epilogue & ow4.EPI_BIAS and kind == "bias_after_gate":
+            z = z + dec(bias_bits)[None, :z.shape[1]]
+        if epilogue & ow4.EPI_RESIDUAL:
+            z = z + dec(residual_bits)
+        return bits_of(rnd(z))
+    return f
+
+
+EPI_PINS = [lambda: [tw4.test_epilogue_brute_force_every_flag_set(f) for f in range(8)],
+            tw4.test_epilogue_zero_activations_give_bias_and_residual, tw4.test_epilogue_gate_pairs_gate_then_up,
+            tw4.test_epilogue_bias_is_added_before_the_gate]
+
+
+@pytest.mark.parametrize("kind", ["gate_swapped", "bias_after_gate", "silu_sign", "early_rounding"])
+def test_epilogue_mutation_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(oracle, "qgemm_w4_epilogue", _epilogue_variant(kind))
+    failures = 0
+    for pin in EPI_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, kind
+
+
 def test_round_mutation_is_caught(monkeypatch):
     """Round half away from zero instead of half to even."""
     def bad(x, fmt):

@@ -216,3 +216,104 @@ def test_bf16_result_rounding_differs_from_f16():
     assert got == 1.0 + 2.0 ** -7             # bf16 nearest of the exact sum (8 significant bits)
     f16 = oracle.qgemm_w4(synth.f16_bits(a), b, synth.f16_bits(np.ones((1, N))), gs).view(np.float16)[0, 0]
     assert float(f16) == exact                # fp16 keeps it
+
+
+# ---------------------------------------------------------------- fixed epilogues
+# The page's optional per-element epilogue is offered as three fixed steps
+# (bias, SiLU-gated column pairs, residual); these pins check the oracle's
+# version against independent scalar code and closed forms.
+
+def _sigmoid_tanh(x):
+    """sigmoid(x) = (1 + tanh(x / 2)) / 2: a second, independent formula."""
+    import math
+    return 0.5 * (1.0 + math.tanh(0.5 * x))
+
+
+def test_silu_closed_forms():
+    import math
+    xs = np.array([-30.0, -3.0, -1.0, -0.25, 0.0, 0.5, 1.0, 2.0, 7.5, 40.0])
+    got = oracle.silu(xs)
+    for x, g in zip(xs, got):
+        assert abs(g - x * _sigmoid_tanh(x)) <= 1e-15 * (1 + abs(x))
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    # silu(x) - silu(-x) = x (sigmoid(x) + sigmoid(-x) = 1)
+    assert np.allclose(oracle.silu(xs) - oracle.silu(-xs), xs, rtol=0, atol=1e-13)
+
+
+def _brute_epilogue(a_bits, b, s_bits, gs, flags, bias_bits, res_bits):
+    y = _brute(a_bits, b, s_bits, gs)
+    M, N = y.shape
+    if flags & oracle.EPI_BIAS:
+        bias = bias_bits.view(np.float16).astype(np.float64)
+        for n in range(N):
+            y[:, n] += bias[n]
+    if flags & oracle.EPI_SILU_GATE:
+        z = np.zeros((M, N // 2))
+        for m in range(M):
+            for j in range(N // 2):
+                g, u = y[m, 2 * j], y[m, 2 * j + 1]
+                z[m, j] = g * _sigmoid_tanh(g) * u
+    else:
+        z = y
+    if flags & oracle.EPI_RESIDUAL:
+        z = z + res_bits.view(np.float16).astype(np.float64)
+    return z
+
+
+@pytest.mark.parametrize("flags", range(8))
+def test_epilogue_brute_force_every_flag_set(flags):
+    M, N, K, gs = 3, 8, 128, 64
+    w = synth.w4_inputs(M, N, K, seed=40 + flags, group_size=gs)
+    n_out = N // 2 if flags & oracle.EPI_SILU_GATE else N
+    bias, res = synth.w4_epilogue_operands(50 + flags, M, n_out, N)
+    got = oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, flags, bias, res)
+    exact = _brute_epilogue(w.a, w.b, w.scales, gs, flags, bias, res)
+    assert got.shape == (M, n_out)
+    # one rounding of the exact value: within half an fp16 ulp of it
+    diff = np.abs(got.view(np.float16).astype(np.float64) - exact)
+    ulp = np.spacing(np.abs(exact).astype(np.float16)).astype(np.float64)
+    assert np.all(diff <= 0.5 * ulp + 1e-12), flags
+    if flags == 0:
+        assert np.array_equal(got, oracle.qgemm_w4(w.a, w.b, w.scales, gs))
+
+
+def test_epilogue_zero_activations_give_bias_and_residual():
+    M, N, K, gs = 2, 16, 128, 128
+    w = synth.w4_inputs(M, N, K, seed=3, group_size=gs)
+    w.a[:] = 0
+    bias, res = synth.w4_epilogue_operands(7, M, N, N)
+    assert np.array_equal(oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_BIAS, bias, None),
+                          np.broadcast_to(bias, (M, N)))
+    assert np.array_equal(oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_RESIDUAL, None, res), res)
+    # Y = 0: the gate gives silu(0) * 0 = 0, then the residual
+    bias2, res2 = synth.w4_epilogue_operands(8, M, N // 2, N)
+    got = oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_SILU_GATE | oracle.EPI_RESIDUAL, None, res2)
+    assert np.array_equal(got, res2)
+
+
+def test_epilogue_gate_pairs_gate_then_up():
+    """A unit row picks one K row of weights, so Y[2j] and Y[2j+1] are known codes:
+    the gate must take silu of the even column and scale it by the odd one."""
+    K, N, gs = 128, 16, 128
+    w = synth.w4_inputs(1, N, K, seed=5, group_size=gs)
+    w.a = np.zeros((1, K), np.uint16)
+    w.a[0, 0] = ONE
+    w.b[0, 0::2] = (w.b[0, 0::2] & ~np.uint32(0xF)) | np.uint32(0xF)   # k = 0 code 15: gate 7
+    w.b[0, 1::2] = (w.b[0, 1::2] & ~np.uint32(0xF)) | np.uint32(0xB)   # k = 0 code 11: up 3
+    w.scales[:] = ONE
+    y = oracle.w4.qgemm_w4_f64(w.a, w.b, w.scales, gs)
+    assert np.all(y[0, 0::2] == 7.0) and np.all(y[0, 1::2] == 3.0)
+    got = oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_SILU_GATE).view(np.float16)
+    g, u = 7.0, 3.0
+    assert np.all(got == np.float16(g * _sigmoid_tanh(g) * u))
+    assert np.float16(g * _sigmoid_tanh(g) * u) != np.float16(u * _sigmoid_tanh(u) * g)
+
+
+def test_epilogue_bias_is_added_before_the_gate():
+    M, N, K, gs = 1, 16, 128, 128
+    w = synth.w4_inputs(M, N, K, seed=6, group_size=gs)
+    w.a[:] = 0
+    bias = np.array([0x4000, 0x4200] * (N // 2), np.uint16)   # gate 2, up 3
+    got = oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_BIAS | oracle.EPI_SILU_GATE, bias, None)
+    assert np.all(got.view(np.float16) == np.float16(2.0 * _sigmoid_tanh(2.0) * 3.0))
