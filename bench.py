@@ -50,6 +50,8 @@ KERNEL_SOURCES = {
     "square": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "decode_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
     "prefill_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "prefill_gate": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "decode_gate": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
@@ -89,7 +91,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "decode_bf16", "prefill_bf16",
-                                                           "grouped", "grouped_kn", "grouped_w4", "kproj"])
+                                                           "decode_gate", "prefill_gate", "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -130,11 +132,18 @@ def w4_bytes(M, N, K, gs):
     return M * K * 2 + K * N // 2 + (K // gs) * N * 2 + M * N * 2
 
 
+def epi_extra_bytes(M, N, epi):
+    """Bias read, residual read, and the output shrinking to N / 2 under the gate."""
+    n_out = N // 2 if epi & 4 else N
+    return (N * 2 if epi & 1 else 0) + (M * n_out * 2 if epi & 2 else 0) - (M * (N - n_out) * 2)
+
+
 class DecodeW4:
     name = "w4a16_decode_N4096_K4096_gs128_M1_4_16"
     kernel = "w4_decode_lds_kernel"
     bound = "hbm"
     dtype = "f16"
+    epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
@@ -149,19 +158,27 @@ class DecodeW4:
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
         b = torch.from_numpy(self.inputs[0].b.view(np.int32)).to(dev)
         s = torch.from_numpy(self.inputs[0].scales.view(np.int16)).to(dev).view(tdt)
+        n_out = N // 2 if self.epi & 4 else N
+        self.epi_ops = [synth.w4_epilogue_operands(7 + i, M, n_out, N, self.dtype) for i, M in enumerate(self.Ms)]
+        dev16 = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
+        bias = dev16(self.epi_ops[0][0]) if self.epi & 1 else None
         self.slots = []
         for r in range(self.R):
             slot = []
             for i, M in enumerate(self.Ms):
                 a = torch.from_numpy(self.inputs[i].a.view(np.int16)).to(dev).view(tdt)
-                slot.append((torch.empty(M, N, dtype=tdt, device=dev), a, b.clone(), s.clone()))
+                res = dev16(self.epi_ops[i][1]) if self.epi & 2 else None
+                slot.append((torch.empty(M, n_out, dtype=tdt, device=dev), a, b.clone(), s.clone(), bias, res))
             self.slots.append(slot)
-        self.bytes_per_step = sum(w4_bytes(M, N, K, 128) for M in self.Ms)
+        self.bytes_per_step = sum(w4_bytes(M, N, K, 128) + epi_extra_bytes(M, N, self.epi) for M in self.Ms)
         self.flops_per_step = sum(2 * M * N * K for M in self.Ms)
 
     def launches(self, step):
         slot = self.slots[step % self.R]
-        return [lambda c=c, a=a, b=b, s=s: self.q.qgemm_w4(c, a, b, s, 128) for (c, a, b, s) in slot]
+        if self.epi:
+            return [lambda c=c, a=a, b=b, s=s, bi=bi, r=r: self.q.qgemm_w4_epilogue(c, a, b, s, self.epi, bi, r, 128)
+                    for (c, a, b, s, bi, r) in slot]
+        return [lambda c=c, a=a, b=b, s=s: self.q.qgemm_w4(c, a, b, s, 128) for (c, a, b, s, _, _) in slot]
 
     def unit_bytes(self):
         return self.bytes_per_step / len(self.Ms)
@@ -171,13 +188,20 @@ class DecodeW4:
 
     def cpu_sample(self):
         import oracle
-        for w in self.inputs:
-            oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size, dtype=self.dtype)
+        for i, w in enumerate(self.inputs):
+            if self.epi:
+                oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, w.group_size, self.epi, self.epi_ops[0][0],
+                                         self.epi_ops[i][1], dtype=self.dtype)
+            else:
+                oracle.qgemm_w4(w.a, w.b, w.scales, w.group_size, dtype=self.dtype)
         return self.flops_per_step, self.bytes_per_step, "full steps (M = 1, 4, 16)"
 
     def describe(self):
-        return {"workload": self.name, "M": self.Ms, "N": self.N, "K": self.K, "group_size": self.gs,
-                "pack_factor": 8, "rotating_copies": self.R}
+        d = {"workload": self.name, "M": self.Ms, "N": self.N, "K": self.K, "group_size": self.gs,
+             "pack_factor": 8, "rotating_copies": self.R}
+        if self.epi:
+            d["epilogue"] = "bias + silu_gate + residual" if self.epi == 7 else self.epi
+        return d
 
     def dense_equivalent(self):
         return None   # a dense GEMV here measures launch overhead, not the GEMM
@@ -188,6 +212,7 @@ class PrefillW4:
     kernel = "w4_prefill_v4_kernel"
     bound = "mfma"
     dtype = "f16"
+    epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
 
     def __init__(self, torch, q, synth, square=False):
         self.torch, self.q = torch, q
@@ -196,20 +221,29 @@ class PrefillW4:
         M, N, K = self.w.shape
         self.M, self.N, self.K = M, N, K
         self.name = f"w4a16_prefill_M{M}_N{N}_K{K}_gs128" + ("_bf16" if self.dtype == "bf16" else "")
-        foot = w4_bytes(M, N, K, 128)
+        if self.epi:
+            self.name += "_bias_silugate_residual" if self.epi == 7 else f"_epi{self.epi}"
+        foot = w4_bytes(M, N, K, 128) + epi_extra_bytes(M, N, self.epi)
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
         dev = torch.device("cuda")
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
         a = torch.from_numpy(self.w.a.view(np.int16)).to(dev).view(tdt)
         b = torch.from_numpy(self.w.b.view(np.int32)).to(dev)
         sc = torch.from_numpy(self.w.scales.view(np.int16)).to(dev).view(tdt)
-        self.slots = [(torch.empty(M, N, dtype=tdt, device=dev), a.clone(), b.clone(), sc.clone())
-                      for _ in range(self.R)]
+        n_out = N // 2 if self.epi & 4 else N
+        self.bias_bits, self.res_bits = synth.w4_epilogue_operands(7, M, n_out, N, self.dtype)
+        dev16 = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
+        bias = dev16(self.bias_bits) if self.epi & 1 else None
+        res = dev16(self.res_bits) if self.epi & 2 else None
+        self.slots = [(torch.empty(M, n_out, dtype=tdt, device=dev), a.clone(), b.clone(), sc.clone(), bias,
+                       None if res is None else res.clone()) for _ in range(self.R)]
         self.bytes_per_step = foot
         self.flops_per_step = 2 * M * N * K
 
     def launches(self, step):
-        c, a, b, s = self.slots[step % self.R]
+        c, a, b, s, bi, r = self.slots[step % self.R]
+        if self.epi:
+            return [lambda: self.q.qgemm_w4_epilogue(c, a, b, s, self.epi, bi, r, 128)]
         return [lambda: self.q.qgemm_w4(c, a, b, s, 128)]
 
     def unit_bytes(self):
@@ -221,15 +255,36 @@ class PrefillW4:
     def cpu_sample(self):
         import oracle
         rows = 256
-        oracle.qgemm_w4(self.w.a[:rows], self.w.b, self.w.scales, 128, dtype=self.dtype)
-        return 2 * rows * self.N * self.K, w4_bytes(rows, self.N, self.K, 128), f"{rows} of {self.M} rows"
+        if self.epi:
+            oracle.qgemm_w4_epilogue(self.w.a[:rows], self.w.b, self.w.scales, 128, self.epi, self.bias_bits,
+                                     self.res_bits[:rows], dtype=self.dtype)
+        else:
+            oracle.qgemm_w4(self.w.a[:rows], self.w.b, self.w.scales, 128, dtype=self.dtype)
+        return (2 * rows * self.N * self.K, w4_bytes(rows, self.N, self.K, 128) + epi_extra_bytes(rows, self.N, self.epi),
+                f"{rows} of {self.M} rows")
 
     def describe(self):
-        return {"workload": self.name, "M": self.M, "N": self.N, "K": self.K, "group_size": 128,
-                "pack_factor": 8, "rotating_copies": self.R}
+        d = {"workload": self.name, "M": self.M, "N": self.N, "K": self.K, "group_size": 128,
+             "pack_factor": 8, "rotating_copies": self.R}
+        if self.epi:
+            d["epilogue"] = "bias + silu_gate + residual" if self.epi == 7 else self.epi
+        return d
 
     def dense_equivalent(self):
         return (self.M, self.K, self.N, self.torch.bfloat16 if self.dtype == "bf16" else self.torch.float16)
+
+
+class PrefillW4Gate(PrefillW4):
+    """The 2048 x 11008 x 4096 prefill as a gated MLP up-projection: bias, SiLU-gated
+    column pairs (output 2048 x 5504) and a residual add, fused into the GEMM."""
+    epi = 7
+
+
+class DecodeW4Gate(DecodeW4):
+    """The decode workload with bias, SiLU-gated column pairs (output M x 2048) and residual."""
+    name = "w4a16_decode_N4096_K4096_gs128_M1_4_16_bias_silugate_residual"
+    kernel = "w4_decode_lds_epi_kernel"
+    epi = 7
 
 
 class DecodeW4BF16(DecodeW4):
@@ -504,6 +559,7 @@ def context_numbers(torch, wl, steps):
 WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
              "decode_bf16": DecodeW4BF16, "prefill_bf16": PrefillW4BF16,
+             "decode_gate": DecodeW4Gate, "prefill_gate": PrefillW4Gate,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 

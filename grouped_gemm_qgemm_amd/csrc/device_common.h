@@ -233,35 +233,15 @@ __device__ __forceinline__ float ld16(const uint16_t* p, size_t i) {
   return BF ? bf2f(p[i]) : h2f(p[i]);
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-
-// Stores output columns (col, col + 1) of row `row` (values y0, y1 in fp32)
-// through the epilogue. N is the product's width; the output is N wide, or N / 2
-// with the gated activation (col is even).
-template <bool BF, typename Epi>
-__device__ __forceinline__ void store_pair_epi(uint16_t* __restrict__ C, int N, int row, int col, float y0,
-                                               float y1, const Epi& ep) {
-  if (ep.flags & 1) {            // bias
-    y0 += ld16<BF>(ep.bias, col);
-    y1 += ld16<BF>(ep.bias, col + 1);
-  }
-  if (ep.flags & 4) {            // gated activation: one output per (gate, up) pair
-    const size_t o = (size_t)row * (N / 2) + (col >> 1);
-    float z = silu(y0) * y1;
-    if (ep.flags & 2) z += ld16<BF>(ep.residual, o);
-    C[o] = BF ? f2bf_rn(z) : f2h_rn(z);
-    return;
-  }
-  const size_t o = (size_t)row * N + col;
-  if (ep.flags & 2) {            // residual
-    y0 += ld16<BF>(ep.residual, o);
-    y1 += ld16<BF>(ep.residual, o + 1);
-  }
-  uint32_t v;
-  if constexpr (BF) v = f2bf2_rn(y0, y1);
-  else v = (uint32_t)f2h_rn(y0) | ((uint32_t)f2h_rn(y1) << 16);
-  *reinterpret_cast<uint32_t*>(C + o) = v;
+template <bool BF>
+__device__ __forceinline__ float bits2f(uint32_t b) {
+  return BF ? bf2f((uint16_t)b) : h2f((uint16_t)b);
 }
 
+// x * sigmoid(x) = x / (1 + e^-x); v_exp_f32 and v_rcp_f32 (about 1 ulp each).
+// For x below about -88, e^-x is +inf and the result is -0.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
 
 }  // namespace qg

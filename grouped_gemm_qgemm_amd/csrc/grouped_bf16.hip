@@ -317,13 +317,12 @@ template <int W, int D, int OCC>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n) {
+    int tiles_n, int per_xcd) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * 2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * 16 * W * 8];
   constexpr int GBN = 16 * W;
   const int total = count_tiles(a_off, ids, num_active, GBM, tiles_n);
   const int xcd = blockIdx.x & 7;
-  const int per_xcd = gridDim.x >> 3;
   const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
   for (int t = lo + (int)(blockIdx.x >> 3); t < hi; t += per_xcd) {
     const TileLoc loc = locate_tile(t, a_off, ids, num_active, GBM, tiles_n);
@@ -355,7 +354,8 @@ static hipError_t launch_wl(const GroupedArgs& p, hipStream_t stream) {
   const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
   const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
   hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                     p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+                     p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
+                     grid / 8);
   return hipGetLastError();
 }
 
@@ -366,7 +366,7 @@ template <int W, int D, int OCC, bool TB, int P>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n) {
+    int tiles_n, int per_xcd) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[TB ? 1 : 2 * WRing<W>::SLOT];
 
@@ -375,7 +375,6 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
   // workgroup waits on a serial walk of it
   const int total = count_tiles(a_off, ids, num_active, GBM, tiles_n);
   const int xcd = blockIdx.x & 7;
-  const int per_xcd = gridDim.x >> 3;
   const int lo = (int)(((long)total * xcd) >> 3), hi = (int)(((long)total * (xcd + 1)) >> 3);
 
   for (int t = lo + (int)(blockIdx.x >> 3); t < hi; t += per_xcd) {
@@ -410,10 +409,12 @@ static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
   const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
   if (p.transpose_b)
     hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, true, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
+                     grid / 8);
   else
     hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, false, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n);
+                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
+                     grid / 8);
   return hipGetLastError();
 }
 

@@ -39,12 +39,9 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
   const int col16 = lane & 15;
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // run of strips so neighbouring strips share its L2.
+  // run of strips so neighbouring strips share its L2 (xcd_remap: strips per XCD).
   int strip = blockIdx.x;
-  if (xcd_remap) {
-    const int per = gridDim.x >> 3;
-    strip = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  }
+  if (xcd_remap) strip = (blockIdx.x & 7) * xcd_remap + (blockIdx.x >> 3);
   const int n0 = strip * SN;
   const int ncol_raw = n0 + CPL * col16;  // first of this lane's CPL columns
   const bool col_ok = ncol_raw < N;       // N % 8 == 0: all CPL columns in range together
@@ -142,10 +139,13 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
 // MFMA per step against a constant -136 matrix adds -136 * (sum of the row's
 // activations), so each group's partial is exactly the sum of a * (q - 8) up
 // to fp32 accumulation order.
-template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
-__global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
+//
+// EPI: the fixed epilogue (a kernel of its own, w4_decode_lds_epi_kernel, so the
+// plain kernel's arguments stay as small as before).
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF, bool EPI>
+__device__ __forceinline__ void w4_decode_lds_body(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, W4Epilogue ep) {
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, const W4Epilogue& ep) {
   constexpr int SN = 16 * CPL;
   constexpr int STEPS = SPG > BSTEPS ? SPG : BSTEPS;   // K steps per batch
   constexpr int GB = STEPS / SPG;              // groups per batch
@@ -163,15 +163,35 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
   const uint32_t m136 = 0xC308C308u;    // bf16 pair (-136, -136)
 
   int strip = blockIdx.x;
-  if (xcd_remap) {
-    const int per = gridDim.x >> 3;
-    strip = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  }
+  if (xcd_remap) strip = (blockIdx.x & 7) * xcd_remap + (blockIdx.x >> 3);
   const int n0 = strip * SN;
   const int ncol_raw = n0 + CPL * col16;
   const bool col_ok = ncol_raw < N;
   const int ncol = col_ok ? ncol_raw : N - CPL;
   const int frag_row = col16 < MROWS ? col16 : MROWS - 1;   // rows >= M hold copies; never stored
+
+  // Fixed epilogue operands of the column pairs (2c, 2c + 1) this thread finishes,
+  // loaded now so their latency hides under the main loop.
+  constexpr int PAIRS = 16 * SN / 2, PER = EPI ? (PAIRS + NW * kWave - 1) / (NW * kWave) : 1;
+  const bool gate = EPI && (ep.flags & 4) != 0;
+  const int NO = gate ? N / 2 : N;   // output width
+  uint32_t bias2[PER], res[PER];
+  if constexpr (EPI) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int e = threadIdx.x + it * NW * kWave;
+      const int row = e / (SN / 2), col = n0 + 2 * (e % (SN / 2));
+      bias2[it] = 0;
+      res[it] = 0;
+      if (e < PAIRS && row < M && col < N) {
+        if (ep.flags & 1) bias2[it] = *reinterpret_cast<const uint32_t*>(ep.bias + col);
+        if (ep.flags & 2) {
+          const uint16_t* r = ep.residual + (size_t)row * NO + (gate ? col / 2 : col);
+          res[it] = gate ? (uint32_t)*r : *reinterpret_cast<const uint32_t*>(r);
+        }
+      }
+    }
+  }
 
   const int groups = K / (SPG * 32);
   const int g_begin = (wave * groups) / NW;
@@ -271,32 +291,60 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][quarter * 4 + i][CPL * col16 + t] = acc[t][i];
   __syncthreads();
-  for (int e = threadIdx.x; e < 16 * SN; e += NW * kWave) {
-    const int row = e / SN, col = e % SN;
-    float sum = 0.f;
+  if constexpr (!EPI) {
+    for (int e = threadIdx.x; e < 16 * SN; e += NW * kWave) {
+      const int row = e / SN, col = e % SN;
+      float sum = 0.f;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) sum += red[v][row][col];
-    if (ep.flags == 0) {
+      for (int v = 0; v < NW; ++v) sum += red[v][row][col];
       if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(sum) : f2h_rn(sum);
-    } else if (!(ep.flags & 4) || !(col & 1)) {
-      // epilogue on column pairs (col, col + 1): the thread of the even column
-      // also sums the odd one (the strip width and n0 are even)
-      float sum1 = 0.f;
-      if (col + 1 < SN) {
+    }
+  } else {
+    // fixed epilogue on column pairs (2c, 2c + 1) of the strip (n0 and N are even),
+    // with the bias and residual loaded at the start
 #pragma unroll
-        for (int v = 0; v < NW; ++v) sum1 += red[v][row][col + 1];
+    for (int it = 0; it < PER; ++it) {
+      const int e = threadIdx.x + it * NW * kWave;
+      const int row = e / (SN / 2), c = 2 * (e % (SN / 2)), col = n0 + c;
+      if (e >= PAIRS || row >= M || col >= N) continue;
+      float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        y0 += red[v][row][c];
+        y1 += red[v][row][c + 1];
       }
-      if (ep.flags & 4) {
-        if (row < M && n0 + col < N) store_pair_epi<BF>(C, N, row, n0 + col, sum, sum1, ep);
-      } else if (row < M && n0 + col < N) {
-        // one column per thread without the gate
-        float y = sum;
-        if (ep.flags & 1) y += ld16<BF>(ep.bias, n0 + col);
-        if (ep.flags & 2) y += ld16<BF>(ep.residual, (size_t)row * N + n0 + col);
-        C[(size_t)row * N + n0 + col] = BF ? f2bf_rn(y) : f2h_rn(y);
+      if (ep.flags & 1) {
+        y0 += bits2f<BF>(bias2[it] & 0xFFFFu);
+        y1 += bits2f<BF>(bias2[it] >> 16);
+      }
+      if (gate) {
+        float z = silu(y0) * y1;
+        if (ep.flags & 2) z += bits2f<BF>(res[it]);
+        C[(size_t)row * NO + col / 2] = BF ? f2bf_rn(z) : f2h_rn(z);
+      } else {
+        if (ep.flags & 2) {
+          y0 += bits2f<BF>(res[it] & 0xFFFFu);
+          y1 += bits2f<BF>(res[it] >> 16);
+        }
+        *reinterpret_cast<uint32_t*>(C + (size_t)row * NO + col) =
+            BF ? f2bf2_rn(y0, y1) : (uint32_t)f2h_rn(y0) | ((uint32_t)f2h_rn(y1) << 16);
       }
     }
   }
+}
+
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
+__global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
+  w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, false>(C, A, B, S, M, N, K, xcd_remap, W4Epilogue{});
+}
+
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
+__global__ __launch_bounds__(NW * kWave) void w4_decode_lds_epi_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, W4Epilogue ep) {
+  w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, true>(C, A, B, S, M, N, K, xcd_remap, ep);
 }
 
 template <int CPL, int NW, int SPG, int MROWS>
@@ -304,13 +352,26 @@ static hipError_t launch_lds_cfg(const W4Args& p, hipStream_t stream) {
   constexpr int SN = 16 * CPL;
   constexpr int BSTEPS = NW >= 16 ? 8 : 16;   // LDS: NW * MROWS * BSTEPS * 64 bytes
   const int strips = (int)((p.N + SN - 1) / SN);
-  const int remap = (strips % 8 == 0) ? 1 : 0;
-  if (p.bf16)
-    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), dim3(strips), dim3(NW * kWave), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap, p.epi);
-  else
-    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), dim3(strips), dim3(NW * kWave), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap, p.epi);
+  // strips per XCD when they divide evenly, else 0 (no remap); passing it keeps
+  // the kernels off the hidden grid-size arguments, whose 256 extra kernarg bytes
+  // cost launch time
+  const int remap = (strips % 8 == 0) ? strips / 8 : 0;
+  const dim3 grid(strips), block(NW * kWave);
+  const int M = (int)p.M, N = (int)p.N, K = (int)p.K;
+  if (p.epi.flags) {
+    if (p.bf16)
+      hipLaunchKernelGGL((w4_decode_lds_epi_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), grid, block, 0, stream,
+                         p.C, p.A, p.B, p.S, M, N, K, remap, p.epi);
+    else
+      hipLaunchKernelGGL((w4_decode_lds_epi_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), grid, block, 0, stream,
+                         p.C, p.A, p.B, p.S, M, N, K, remap, p.epi);
+  } else if (p.bf16) {
+    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), grid, block, 0, stream,
+                       p.C, p.A, p.B, p.S, M, N, K, remap);
+  } else {
+    hipLaunchKernelGGL((w4_decode_lds_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), grid, block, 0, stream,
+                       p.C, p.A, p.B, p.S, M, N, K, remap);
+  }
   return hipGetLastError();
 }
 
@@ -338,7 +399,10 @@ template <int CPL, int NW, int SPG>
 static hipError_t launch_cfg(const W4Args& p, hipStream_t stream) {
   constexpr int SN = 16 * CPL;
   const int strips = (int)((p.N + SN - 1) / SN);
-  const int remap = (strips % 8 == 0) ? 1 : 0;
+  // strips per XCD when they divide evenly, else 0 (no remap); passing it keeps
+  // the kernels off the hidden grid-size arguments, whose 256 extra kernarg bytes
+  // cost launch time
+  const int remap = (strips % 8 == 0) ? strips / 8 : 0;
   constexpr int GB = SPG >= 4 ? 4 : 16 / SPG;  // 16 steps of loads per batch (gs <= 128)
   hipLaunchKernelGGL((w4_decode_kernel<CPL, NW, SPG, GB>), dim3(strips), dim3(NW * kWave), 0, stream,
                      p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);

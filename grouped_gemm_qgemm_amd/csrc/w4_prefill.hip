@@ -856,20 +856,61 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 
   // epilogue: two adjacent columns per 4-byte store (or one gated output)
   const int col = n0 + wn * TN + 2 * c32;
-  if (col < N) {
+  if (col >= N) return;
+  if (ep.flags == 0) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (row < M) {
-          if (ep.flags == 0)
-            *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
-                BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
-                   : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
-          else
-            store_pair_epi<BF>(C, N, row, col, acc[mt][0][i], acc[mt][1][i], ep);
+        if (row < M)
+          *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
+              BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
+                 : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+      }
+    }
+    return;
+  }
+  // Fixed epilogue. Every bias and residual value this lane needs is loaded
+  // before its first store: the compiler cannot tell that C does not alias
+  // them, and would otherwise wait for each load after the previous store.
+  const bool gate = (ep.flags & 4) != 0;
+  const int NO = gate ? N / 2 : N;                  // output width
+  const int oc = gate ? col / 2 : col;              // this lane's output column
+  uint32_t bias2 = 0;
+  if (ep.flags & 1) bias2 = *reinterpret_cast<const uint32_t*>(ep.bias + col);
+  uint32_t res[MT][16];
+  if (ep.flags & 2) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = min(m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3), M - 1);
+        const uint16_t* r = ep.residual + (size_t)row * NO + oc;
+        res[mt][i] = gate ? (uint32_t)*r : *reinterpret_cast<const uint32_t*>(r);
+      }
+    }
+  }
+  const float b0 = (ep.flags & 1) ? bits2f<BF>(bias2 & 0xFFFFu) : 0.f;
+  const float b1 = (ep.flags & 1) ? bits2f<BF>(bias2 >> 16) : 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (row >= M) continue;
+      float y0 = acc[mt][0][i] + b0, y1 = acc[mt][1][i] + b1;
+      if (gate) {
+        float z = silu(y0) * y1;
+        if (ep.flags & 2) z += bits2f<BF>(res[mt][i]);
+        C[(size_t)row * NO + oc] = BF ? f2bf_rn(z) : f2h_rn(z);
+      } else {
+        if (ep.flags & 2) {
+          y0 += bits2f<BF>(res[mt][i] & 0xFFFFu);
+          y1 += bits2f<BF>(res[mt][i] >> 16);
         }
+        *reinterpret_cast<uint32_t*>(C + (size_t)row * NO + oc) =
+            BF ? f2bf2_rn(y0, y1) : (uint32_t)f2h_rn(y0) | ((uint32_t)f2h_rn(y1) << 16);
       }
     }
   }
@@ -917,10 +958,9 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
-    int group_size, int num_active, int tiles_n) {
+    int group_size, int num_active, int tiles_n, int per_xcd) {
   __shared__ W4TileLds<BM, BN, KG> lds;
-  const int per = gridDim.x >> 3;
-  const int t = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const TileLoc loc = locate_tile(t, a_off, ids, num_active, BM, tiles_n);
   if (loc.g < 0) return;
   const int chunk = loc.local / tiles_n, nt = loc.local - chunk * tiles_n;
@@ -942,7 +982,7 @@ static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream
   const int grid = (int)((bound + 7) / 8 * 8);
   hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
                      stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
-                     p.num_active, tiles_n);
+                     p.num_active, tiles_n, grid / 8);
   return hipGetLastError();
 }
 
