@@ -56,6 +56,8 @@ KERNEL_SOURCES = {
     "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
+    "kvproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
+    "kvproj_e4m3": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
@@ -91,7 +93,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "decode_bf16", "prefill_bf16",
-                                                           "decode_gate", "prefill_gate", "grouped", "grouped_kn", "grouped_w4", "kproj"])
+                                                           "decode_gate", "prefill_gate", "kvproj", "kvproj_e4m3",
+                                                           "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -447,16 +450,19 @@ class KProjFP8:
     kernel = "kproj_fp8_v3_kernel"
     bound = "mfma"
     dtype = "bf16"
+    planes = 1          # 2: keys and values ([W_k | W_v]) in one call
+    cache = "bf16"      # or "fp8": e4m3 cache with one f32 scale per head row (G = 128)
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
-        k = synth.kproj_inputs()
+        k = synth.kproj_inputs(planes=self.planes, cache=self.cache, qgran=128)
         self.k = k
         T, Kh = k.hidden.shape
         N = k.weight.shape[1]
         self.T, self.Kh, self.N = T, Kh, N
         self.flops_per_step = 2 * T * Kh * N
-        self.bytes_per_step = (T * Kh * 2 + Kh * N + k.input_scale.nbytes + k.weight_scale.nbytes + T * N * 2
+        out_bytes = T * N * (1 + 4 / 128) if self.cache == "fp8" else T * N * 2   # codes + scales, or bf16
+        self.bytes_per_step = (T * Kh * 2 + Kh * N + k.input_scale.nbytes + k.weight_scale.nbytes + out_bytes
                                + k.row_offsets.nbytes + k.cache_lengths.nbytes + k.page_table.nbytes)
         foot = k.hidden.nbytes + k.weight.nbytes + k.blocks.nbytes + k.input_scale.nbytes
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
@@ -465,18 +471,26 @@ class KProjFP8:
         w = torch.from_numpy(k.weight).to(dev).view(torch.float8_e4m3fn)
         isc = torch.from_numpy(k.input_scale).to(dev)
         wsc = torch.from_numpy(k.weight_scale).to(dev)
-        blocks = torch.from_numpy(k.blocks.view(np.int16)).to(dev).view(torch.bfloat16)
+        if self.cache == "fp8":
+            blocks = torch.from_numpy(k.blocks).to(dev)
+            kvs = torch.from_numpy(k.scales).to(dev)
+        else:
+            blocks = torch.from_numpy(k.blocks.view(np.int16)).to(dev).view(torch.bfloat16)
+            kvs = None
         self.offs = torch.from_numpy(k.row_offsets.view(np.int32)).to(dev)
         self.cl = torch.from_numpy(k.cache_lengths.view(np.int32)).to(dev)
         self.pt = torch.from_numpy(k.page_table.view(np.int32)).to(dev)
-        self.slots = [(h.clone(), w.clone(), isc.clone(), wsc.clone(), blocks.clone()) for _ in range(self.R)]
-        self.name = f"kproj_fp8_paged_T{T}_K{Kh}_N{N}_page128"
+        self.slots = [(h.clone(), w.clone(), isc.clone(), wsc.clone(), blocks.clone(),
+                       None if kvs is None else kvs.clone()) for _ in range(self.R)]
+        self.name = (f"{'kvproj' if self.planes == 2 else 'kproj'}_fp8_paged_T{T}_K{Kh}_N{N}_page128"
+                     + ("_e4m3cache_g128" if self.cache == "fp8" else ""))
 
     def launches(self, step):
-        h, w, isc, wsc, blocks = self.slots[step % self.R]
+        h, w, isc, wsc, blocks, kvs = self.slots[step % self.R]
         k = self.k
-        return [lambda: self.q.k_matmul_ragged_paged_scale(h, self.offs, w, isc, wsc, blocks, self.cl, self.pt,
-                                                           k.layer_idx)]
+        fn = self.q.kv_matmul_ragged_paged_scale if self.planes == 2 else self.q.k_matmul_ragged_paged_scale
+        return [lambda: fn(h, self.offs, w, isc, wsc, blocks, self.cl, self.pt, k.layer_idx, kv_scales=kvs,
+                           quantization_granularity=k.qgran)]
 
     def unit_bytes(self):
         return self.bytes_per_step
@@ -488,18 +502,34 @@ class KProjFP8:
         import oracle
         k = self.k
         rows = 512
-        oracle.kproj_rows(k.hidden[:rows], k.weight, k.input_scale[:rows], k.weight_scale)
+        if self.cache == "fp8":
+            y = oracle.kproj_exact(k.hidden[:rows], k.weight, k.input_scale[:rows], k.weight_scale)
+            oracle.quantize_runs(y, 128)
+        else:
+            oracle.kproj_rows(k.hidden[:rows], k.weight, k.input_scale[:rows], k.weight_scale)
         return 2 * rows * self.Kh * self.N, rows * self.Kh * 2 + self.Kh * self.N + rows * self.N * 2, \
-            f"{rows} of {self.T} token rows (matmul + rounding; placement excluded)"
+            f"{rows} of {self.T} token rows (matmul + rounding or quantization; placement excluded)"
 
     def describe(self):
         k = self.k
         return {"workload": self.name, "tokens": self.T, "batch": len(k.row_offsets) - 1, "hidden": self.Kh,
                 "N": self.N, "page_size": int(k.blocks.shape[3]), "layers": int(k.blocks.shape[0]),
-                "layer_idx": k.layer_idx, "granularity_mnk": [1, 128, 128], "rotating_copies": self.R}
+                "layer_idx": k.layer_idx, "granularity_mnk": [1, 128, 128], "rotating_copies": self.R,
+                "planes": self.planes, "cache": "e4m3, one f32 scale per 128" if self.cache == "fp8" else "bf16"}
 
     def dense_equivalent(self):
         return (self.T, self.Kh, self.N, self.torch.bfloat16)
+
+
+class KVProjFP8(KProjFP8):
+    """Keys and values in one call: [W_k | W_v] [4096, 2048], planes 0 and 1 of the bf16 cache."""
+    planes = 2
+
+
+class KVProjFP8Cache(KProjFP8):
+    """Keys and values in one call into an e4m3 cache with one f32 scale per head row."""
+    planes = 2
+    cache = "fp8"
 
 
 def graph_time_ms(torch, launch_lists, reps=3):
@@ -560,6 +590,7 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
              "decode_bf16": DecodeW4BF16, "prefill_bf16": PrefillW4BF16,
              "decode_gate": DecodeW4Gate, "prefill_gate": PrefillW4Gate,
+             "kvproj": KVProjFP8, "kvproj_e4m3": KVProjFP8Cache,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 

@@ -15,7 +15,9 @@ Entry points (same names as the C ABI):
                     group_size=128, pack_factor=8)
     k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
                                 weight_scale, kv_blocks, cache_lengths, page_table,
-                                layer_idx, scales_granularity_mnk=(1, 128, 128))
+                                layer_idx, scales_granularity_mnk=(1, 128, 128),
+                                kv_scales=None, quantization_granularity=0)
+    kv_matmul_ragged_paged_scale(... the same, weight = [W_k | W_v] ...)
 Each returns None on success and raises QgError carrying the status otherwise.
 """
 from __future__ import annotations
@@ -26,7 +28,7 @@ import os
 import torch
 
 __all__ = ["load", "QgError", "qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4",
-           "k_matmul_ragged_paged_scale", "status_string", "LIB_PATH", "QG", "EPI_BIAS", "EPI_RESIDUAL",
+           "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale", "status_string", "LIB_PATH", "QG", "EPI_BIAS", "EPI_RESIDUAL",
            "EPI_SILU_GATE"]
 
 # qgemm_w4_epilogue flags
@@ -50,7 +52,8 @@ class QgTensor(ctypes.Structure):
 
 class QgPagedKV(ctypes.Structure):
     _fields_ = [("blocks", QgTensor), ("cache_lengths", ctypes.c_void_p),
-                ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int64)]
+                ("page_table", ctypes.c_void_p), ("max_pages_per_seq", ctypes.c_int64),
+                ("scales", QgTensor), ("quantization_granularity", ctypes.c_int64)]
 
 
 class QgError(RuntimeError):
@@ -91,6 +94,8 @@ def load(path: str | None = None):
     lib.k_matmul_ragged_paged_scale.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(QgPagedKV), ctypes.c_uint32, ctypes.c_void_p]
     lib.k_matmul_ragged_paged_scale.restype = ctypes.c_int
+    lib.kv_matmul_ragged_paged_scale.argtypes = lib.k_matmul_ragged_paged_scale.argtypes
+    lib.kv_matmul_ragged_paged_scale.restype = ctypes.c_int
     lib.qg_status_string.argtypes = [ctypes.c_int]
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
@@ -195,23 +200,49 @@ def grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_
     return st
 
 
-def k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale, weight_scale,
-                                kv_blocks, cache_lengths, page_table, layer_idx: int,
-                                scales_granularity_mnk=(1, 128, 128), stream=None,
-                                raise_on_error: bool = True) -> int:
-    """K rows = (hidden * input_scale) . (weight * weight_scale), written into the key
-    plane of layer `layer_idx` of the paged cache `kv_blocks` [L, 2, P, S, Hkv, D]."""
-    lib = load()
-    gran = (ctypes.c_int32 * 3)(*[int(v) for v in scales_granularity_mnk])
+def _paged_kv(kv_blocks, cache_lengths, page_table, kv_scales, quantization_granularity) -> QgPagedKV:
     kv = QgPagedKV()
-    kv.blocks = describe(kv_blocks)
+    kv.blocks = describe(kv_blocks, QG.FP8_E4M3 if kv_blocks is not None and kv_blocks.dtype == torch.uint8 else None)
     kv.cache_lengths = cache_lengths.data_ptr() if cache_lengths is not None else None
     kv.page_table = page_table.data_ptr() if page_table is not None else None
     kv.max_pages_per_seq = page_table.shape[1] if page_table is not None and page_table.dim() == 2 else 0
-    st = lib.k_matmul_ragged_paged_scale(
-        ctypes.byref(describe(hidden)), ctypes.byref(describe(input_row_offsets, _u32(input_row_offsets))),
-        ctypes.byref(describe(weight)), ctypes.byref(describe(input_scale)),
-        ctypes.byref(describe(weight_scale)), gran, ctypes.byref(kv), int(layer_idx), _stream(stream))
+    kv.scales = describe(kv_scales)
+    kv.quantization_granularity = int(quantization_granularity)
+    return kv
+
+
+def _kv_call(fn, hidden, input_row_offsets, weight, input_scale, weight_scale, kv_blocks, cache_lengths,
+             page_table, layer_idx, scales_granularity_mnk, kv_scales, quantization_granularity, stream,
+             raise_on_error):
+    gran = (ctypes.c_int32 * 3)(*[int(v) for v in scales_granularity_mnk])
+    kv = _paged_kv(kv_blocks, cache_lengths, page_table, kv_scales, quantization_granularity)
+    st = fn(ctypes.byref(describe(hidden)), ctypes.byref(describe(input_row_offsets, _u32(input_row_offsets))),
+            ctypes.byref(describe(weight)), ctypes.byref(describe(input_scale)),
+            ctypes.byref(describe(weight_scale)), gran, ctypes.byref(kv), int(layer_idx), _stream(stream))
     if raise_on_error:
         _check(st)
     return st
+
+
+def k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale, weight_scale,
+                                kv_blocks, cache_lengths, page_table, layer_idx: int,
+                                scales_granularity_mnk=(1, 128, 128), kv_scales=None,
+                                quantization_granularity: int = 0, stream=None,
+                                raise_on_error: bool = True) -> int:
+    """K rows = (hidden * input_scale) . (weight * weight_scale), written into the key
+    plane of layer `layer_idx` of the paged cache `kv_blocks` [L, 2, P, S, Hkv, D]
+    (bf16, or e4m3 codes held in float8_e4m3fn / uint8 with f32 `kv_scales`)."""
+    return _kv_call(load().k_matmul_ragged_paged_scale, hidden, input_row_offsets, weight, input_scale,
+                    weight_scale, kv_blocks, cache_lengths, page_table, layer_idx, scales_granularity_mnk,
+                    kv_scales, quantization_granularity, stream, raise_on_error)
+
+
+def kv_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale, weight_scale,
+                                 kv_blocks, cache_lengths, page_table, layer_idx: int,
+                                 scales_granularity_mnk=(1, 128, 128), kv_scales=None,
+                                 quantization_granularity: int = 0, stream=None,
+                                 raise_on_error: bool = True) -> int:
+    """Keys and values at once: weight = [W_k | W_v] ([Kh, 2 Hkv D]); planes 0 and 1."""
+    return _kv_call(load().kv_matmul_ragged_paged_scale, hidden, input_row_offsets, weight, input_scale,
+                    weight_scale, kv_blocks, cache_lengths, page_table, layer_idx, scales_granularity_mnk,
+                    kv_scales, quantization_granularity, stream, raise_on_error)

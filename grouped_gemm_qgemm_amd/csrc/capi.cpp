@@ -240,12 +240,11 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
   return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 8), stream));
 }
 
-qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
-                                      const qg_tensor* weight, const qg_tensor* input_scale,
-                                      const qg_tensor* weight_scale,
-                                      const int32_t* scales_granularity_mnk,
-                                      const qg_paged_kv* kv, uint32_t layer_idx,
-                                      hipStream_t stream) {
+// planes: 1 (keys only) or 2 (weight columns = [W_k | W_v])
+static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                              const qg_tensor* weight, const qg_tensor* input_scale,
+                              const qg_tensor* weight_scale, const int32_t* scales_granularity_mnk,
+                              const qg_paged_kv* kv, uint32_t layer_idx, int planes, hipStream_t stream) {
   if (!hidden || !input_row_offsets || !weight || !input_scale || !weight_scale ||
       !scales_granularity_mnk || !kv)
     return QG_ERR_NULL;
@@ -258,7 +257,8 @@ qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* 
   if ((st = check_tensor(weight, 2, QG_FP8_E4M3)) != QG_OK) return st;
   if ((st = check_tensor(input_scale, 2, QG_F32)) != QG_OK) return st;
   if ((st = check_tensor(weight_scale, 2, QG_F32)) != QG_OK) return st;
-  if ((st = check_tensor(&kv->blocks, 6, QG_BF16)) != QG_OK) return st;
+  const bool fp8 = kv->blocks.dtype == QG_FP8_E4M3;   // quantized cache
+  if ((st = check_tensor(&kv->blocks, 6, fp8 ? QG_FP8_E4M3 : QG_BF16)) != QG_OK) return st;
   if (scales_granularity_mnk[0] != 1 || scales_granularity_mnk[1] != 128 || scales_granularity_mnk[2] != 128)
     return QG_ERR_UNSUPPORTED;
   const int64_t T = hidden->shape[0], Kh = hidden->shape[1];
@@ -271,7 +271,18 @@ qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* 
   if (Kh % 128 != 0 || N % 128 != 0) return QG_ERR_SHAPE;
   if (input_scale->shape[0] != T || input_scale->shape[1] != Kh / 128) return QG_ERR_SHAPE;
   if (weight_scale->shape[0] != Kh / 128 || weight_scale->shape[1] != N / 128) return QG_ERR_SHAPE;
-  if (bs[1] != 2 || Hkv * D != N) return QG_ERR_SHAPE;
+  if (bs[1] != 2 || Hkv * D * planes != N) return QG_ERR_SHAPE;
+  if (planes > 1 && (Hkv * D) % 128 != 0) return QG_ERR_SHAPE;   // each 128-column tile in one plane
+  int64_t G = 0;
+  if (fp8) {
+    G = kv->quantization_granularity;
+    if (G != 32 && G != 64 && G != 128) return QG_ERR_UNSUPPORTED;
+    if (D % G != 0) return QG_ERR_UNSUPPORTED;
+    if (kv->scales.rank != 6) return QG_ERR_RANK;
+    if ((st = check_tensor(&kv->scales, 6, QG_F32)) != QG_OK) return st;
+    const int64_t* ss = kv->scales.shape;
+    if (ss[0] != L || ss[1] != 2 || ss[2] != P || ss[3] != S || ss[4] != Hkv || ss[5] != D / G) return QG_ERR_SHAPE;
+  }
   if ((int64_t)layer_idx >= L) return QG_ERR_INVALID_ARG;
   if (kv->max_pages_per_seq <= 0 && T > 0) return QG_ERR_INVALID_ARG;
   if (B > 0 && T > 0 && (!kv->cache_lengths || !kv->page_table)) return QG_ERR_NULL;
@@ -283,10 +294,37 @@ qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* 
                   static_cast<const uint8_t*>(weight->data),
                   static_cast<const float*>(input_scale->data),
                   static_cast<const float*>(weight_scale->data),
-                  static_cast<uint16_t*>(kv->blocks.data),
+                  kv->blocks.data,
                   kv->cache_lengths, kv->page_table,
                   T, Kh, N, B, kv->max_pages_per_seq, L, P, S, layer_idx, device_cus()};
-  return launch_status(qg::launch_kproj_fp8(p, env_variant("QG_KPROJ_VARIANT", 0), stream));
+  p.n_plane = Hkv * D;
+  p.fp8 = fp8 ? 1 : 0;
+  p.kv_scales = fp8 ? static_cast<float*>(kv->scales.data) : nullptr;
+  p.qgran = (int)G;
+  const bool wide = fp8 || planes > 1;   // the third design only, with Kh / 128 <= 32
+  const int v = env_variant("QG_KPROJ_VARIANT", 0);
+  if (wide && (Kh / 128 > 32 || (v != 0 && v < 6))) return QG_ERR_UNSUPPORTED;
+  return launch_status(qg::launch_kproj_fp8(p, v, stream));
+}
+
+qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                                      const qg_tensor* weight, const qg_tensor* input_scale,
+                                      const qg_tensor* weight_scale,
+                                      const int32_t* scales_granularity_mnk,
+                                      const qg_paged_kv* kv, uint32_t layer_idx,
+                                      hipStream_t stream) {
+  return kv_proj_impl(hidden, input_row_offsets, weight, input_scale, weight_scale, scales_granularity_mnk, kv,
+                      layer_idx, 1, stream);
+}
+
+qg_status kv_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                                       const qg_tensor* weight, const qg_tensor* input_scale,
+                                       const qg_tensor* weight_scale,
+                                       const int32_t* scales_granularity_mnk,
+                                       const qg_paged_kv* kv, uint32_t layer_idx,
+                                       hipStream_t stream) {
+  return kv_proj_impl(hidden, input_row_offsets, weight, input_scale, weight_scale, scales_granularity_mnk, kv,
+                      layer_idx, 2, stream);
 }
 
 }  // extern "C"

@@ -415,12 +415,21 @@ __global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
 // one wave's LDS and load waits are covered by the others' MFMAs; with one wave
 // per SIMD those waits were exposed on every stage. The first min(512, threads)
 // threads stage the weight tile (RPT K rows of 16 columns each).
-template <int WM, int PD>
+//
+// Cache planes and the fp8 cache: the N weight columns fill N / n_plane planes
+// from plane 0 (keys; with [W_k | W_v] the value columns land in plane 1). Each
+// 128-column tile lies in one plane. Q8: the cache holds e4m3 codes with one f32
+// scale per qgran head-dim elements of a row, s = amax / 448 and q = e4m3(x / s)
+// (nearest even); a run of 32 columns is one wave's columns of a row, spread over
+// the 16 lanes that share its rows, so amax is a 16-lane shuffle reduction, and
+// runs of 64 or 128 combine two or four waves through LDS.
+template <int WM, int PD, bool Q8>
 __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
-    const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
     const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
-    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n) {
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
+    float* __restrict__ kv_scales, int qgran) {
   constexpr int BM = 48 * WM;
   constexpr int NTHR = WM * 256;
   constexpr int MT = 3;                          // 16-row MFMA tiles per wave
@@ -586,9 +595,10 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     }
   }
 
+  const int plane = n0 / n_plane, colp = n0 - plane * n_plane;   // the tile's plane and column there
   if (tid < BM) {
     const int t = m0 + tid;
-    long long dst = -1;
+    long long dst = -1;   // cache row (layer, plane, page, slot) of token t
     if (t < T) {
       int lo = 0, hi = batch;
       while (hi - lo > 1) {
@@ -598,20 +608,75 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
       const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
       const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
       const int slot = pos % page_size;
-      dst = ((((long long)layer * 2 + 0) * num_pages + page) * page_size + slot) * (long long)N;
+      dst = (((long long)layer * 2 + plane) * num_pages + page) * page_size + slot;
     }
     row_dst[tid] = dst;
   }
   __syncthreads();
-  const int col = n0 + wn * 32 + 2 * r16;
+  const int col = colp + wn * 32 + 2 * r16;
+  if constexpr (!Q8) {
+    uint16_t* __restrict__ blocks = static_cast<uint16_t*>(blocks_v);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
-      if (d >= 0) {
-        const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
-        *reinterpret_cast<uint32_t*>(blocks + d + col) = v;
+      for (int i = 0; i < 4; ++i) {
+        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
+        if (d >= 0) {
+          const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
+          *reinterpret_cast<uint32_t*>(blocks + d * n_plane + col) = v;
+        }
+      }
+    }
+  } else {
+    uint8_t* __restrict__ blocks = static_cast<uint8_t*>(blocks_v);
+    // amax of each of the lane's rows over the wave's 32 columns
+    float am[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = fmaxf(fabsf(acc[mt][0][i]), fabsf(acc[mt][1][i]));
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+        am[mt][i] = a;
+      }
+    }
+    const int gw = qgran / 32;   // waves per run of qgran columns: 1, 2 or 4 (workgroup-uniform)
+    if (gw > 1) {
+      float* amx = lds_is;       // free after the main loop: [wave column][row]
+      if (r16 == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amx[wn * BM + wm * 48 + mt * 16 + q * 4 + i] = am[mt][i];
+      }
+      __syncthreads();
+      const int w0 = wn & ~(gw - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 48 + mt * 16 + q * 4 + i;
+          float a = amx[w0 * BM + row];
+          for (int w = 1; w < gw; ++w) a = fmaxf(a, amx[(w0 + w) * BM + row]);
+          am[mt][i] = a;
+        }
+      }
+    }
+    const int nsc = n_plane / qgran;   // scales per cache row
+    const bool scale_writer = r16 == 0 && (wn & (gw - 1)) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
+        if (d < 0) continue;
+        const float sc = am[mt][i] / 448.0f;   // correctly rounded fp32 division
+        const float v0 = sc > 0.f ? acc[mt][0][i] / sc : 0.f;
+        const float v1 = sc > 0.f ? acc[mt][1][i] / sc : 0.f;
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);   // nearest even, low half
+        *reinterpret_cast<uint16_t*>(blocks + d * n_plane + col) = (uint16_t)pk;
+        if (scale_writer) kv_scales[d * nsc + (colp + wn * 32) / qgran] = sc;
       }
     }
   }
@@ -622,10 +687,18 @@ static hipError_t launch_kproj_v3(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
-  hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden, p.row_offsets,
-                     p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
-                     (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
-                     (int)p.layer_idx, tiles_m, tiles_n);
+  if (p.fp8)
+    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD, true>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                       p.kv_scales, p.qgran);
+  else
+    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD, false>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                       nullptr, 0);
   return hipGetLastError();
 }
 
@@ -634,7 +707,7 @@ static hipError_t launch_kproj_v2(const KProjArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
   hipLaunchKernelGGL((kproj_fp8_v2_kernel<BM>), dim3(grid), dim3(256), 0, stream, p.hidden, p.row_offsets,
-                     p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                     p.weight, p.input_scale, p.weight_scale, static_cast<uint16_t*>(p.blocks), p.cache_lengths, p.page_table, (int)p.T,
                      (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                      (int)p.layer_idx, tiles_m, tiles_n);
   return hipGetLastError();
@@ -660,8 +733,13 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
 }
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
-  if (p.Kh / KBK > 32) variant = 1;   // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
+  const bool wide = p.fp8 || p.n_plane != p.N;   // fp8 cache or several planes: the third design only
+  if (p.Kh / KBK > 32) {                // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
+    if (wide) return hipErrorNotSupported;
+    variant = 1;
+  }
   if (variant == 0) variant = 6;
+  if (wide && variant < 6) return hipErrorNotSupported;
   if (variant == 10) return launch_kproj_v3<3, 2>(p, stream);
   if (variant == 11) return launch_kproj_v3<2, 2>(p, stream);
   if (variant >= 6) {
@@ -692,7 +770,7 @@ hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream)
   const int tiles = tiles_m * tiles_n;
   const int grid = ((tiles + 7) / 8) * 8;
   hipLaunchKernelGGL(kproj_fp8_paged_kernel, dim3(grid), dim3(KTHR), 0, stream, p.hidden, p.row_offsets,
-                     p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                     p.weight, p.input_scale, p.weight_scale, static_cast<uint16_t*>(p.blocks), p.cache_lengths, p.page_table, (int)p.T,
                      (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                      (int)p.layer_idx, tiles_m, tiles_n);
   return hipGetLastError();

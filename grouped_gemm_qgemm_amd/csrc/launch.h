@@ -61,13 +61,17 @@ struct KProjArgs {
   const uint8_t* weight;         // e4m3 [Kh, N]
   const float* input_scale;      // [T, Kh/128]
   const float* weight_scale;     // [Kh/128, N/128]
-  uint16_t* blocks;              // bf16 [L, 2, P, S, Hkv, D]
+  void* blocks;                  // bf16 or e4m3 [L, 2, P, S, Hkv, D]
   const uint32_t* cache_lengths; // [B]
   const uint32_t* page_table;    // [B, max_pages]
   int64_t T, Kh, N, batch, max_pages;
   int64_t num_layers, num_pages, page_size;
   uint32_t layer_idx;
   int num_cus;
+  int64_t n_plane = 0;           // columns per cache plane (Hkv * D); N / n_plane planes from plane 0
+  int fp8 = 0;                   // e4m3 cache with f32 scales
+  float* kv_scales = nullptr;    // fp8: [L, 2, P, S, Hkv, D / qgran]
+  int qgran = 0;                 // fp8: head-dim elements per scale (32, 64, 128)
 };
 
 // Decode-shaped W4A16 (M <= 16). `variant` picks columns-per-lane and waves.

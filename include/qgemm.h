@@ -9,8 +9,10 @@
  *   grouped_gemm                 per-expert bf16 GEMM routed by row offsets
  *                                (Modular MAX page "grouped_matmul_sm100_persistent")
  *   k_matmul_ragged_paged_scale  block-scaled fp8 weights, ragged rows, output
- *                                written into a paged KV cache
+ *                                written into a paged KV cache (bf16 or fp8 with
+ *                                scales)
  *                                (Modular MAX page "k_matmul_ragged_paged_scale")
+ *   kv_matmul_ragged_paged_scale the same for keys and values at once
  *   grouped_gemm_w4              the routing of grouped_gemm over experts stored in
  *                                qgemm_w4's packed 4-bit format
  *
@@ -190,13 +192,29 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
                           const uint32_t* expert_usage_stats_host, int32_t group_size,
                           int32_t pack_factor, hipStream_t stream);
 
-/* A paged KV cache collection (keys and values of every layer). */
+/*
+ * A paged KV cache collection (keys and values of every layer).
+ *
+ * The K-projection page's kv_collection parameter carries a scale type and a
+ * quantization granularity (PagedKVCacheCollection[scale_dtype_,
+ * quantization_granularity_]), so the cache may hold quantized values:
+ *   - blocks bf16: plain values; `scales` and `quantization_granularity` are
+ *     ignored (scales may be an empty descriptor).
+ *   - blocks fp8 e4m3: every run of G = quantization_granularity head-dim
+ *     elements of one (layer, plane, page, slot, kv head) has one f32 scale s in
+ *     `scales`; the stored code q stands for q * s. A writer sets
+ *     s = amax / 448 (amax: the largest |x| of the run, in fp32) and
+ *     q = e4m3(x / s) rounded to nearest even (q = 0 when amax = 0); G is 32, 64
+ *     or 128 and divides D.
+ */
 typedef struct {
-  qg_tensor blocks;                /* bf16 [L, 2, P, S, Hkv, D]: layer, K/V plane (0 = keys),
-                                      physical page, slot in page, kv head, head dim     */
+  qg_tensor blocks;                /* bf16 or fp8 e4m3 [L, 2, P, S, Hkv, D]: layer, K/V plane
+                                      (0 = keys), physical page, slot in page, kv head, head dim */
   const uint32_t* cache_lengths;   /* device u32 [B]: tokens already cached per sequence  */
   const uint32_t* page_table;      /* device u32 [B, max_pages_per_seq]: physical page ids */
   int64_t max_pages_per_seq;
+  qg_tensor scales;                /* fp8 cache: f32 [L, 2, P, S, Hkv, D / G]               */
+  int64_t quantization_granularity; /* fp8 cache: G                                          */
 } qg_paged_kv;
 
 /*
@@ -219,12 +237,16 @@ typedef struct {
  *                     p = cache_lengths[b] + j: page page_table[b][p / S], slot p % S
  *   layer_idx         < L (QG_ERR_INVALID_ARG otherwise)
  *
- * Only the addressed (page, slot) rows of plane 0 of layer layer_idx are written;
- * every other byte of the cache is left as it was, and cache_lengths is not
- * updated. Kh and N must be multiples of 128 (QG_ERR_SHAPE). Accumulation is fp32;
- * results are rounded to bf16 (nearest-even). Offsets, cache lengths and page ids
- * are not re-validated on the device: a position past max_pages_per_seq * S or a
- * page id >= P is undefined behaviour, as is two tokens addressing one slot.
+ * Only the addressed (page, slot) rows of plane 0 of layer layer_idx are written
+ * (with an fp8 cache, also their scales); every other byte of the cache is left
+ * as it was, and cache_lengths is not updated. Kh and N must be multiples of 128
+ * (QG_ERR_SHAPE). Accumulation is fp32; results are rounded to bf16
+ * (nearest-even), or quantized as described at qg_paged_kv. Offsets, cache
+ * lengths and page ids are not re-validated on the device: a position past
+ * max_pages_per_seq * S or a page id >= P is undefined behaviour, as is two
+ * tokens addressing one slot. An fp8 cache with a granularity other than 32, 64
+ * or 128, or one that does not divide D, is QG_ERR_UNSUPPORTED; a scales tensor
+ * of the wrong shape is QG_ERR_SHAPE.
  */
 qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
                                       const qg_tensor* weight, const qg_tensor* input_scale,
@@ -232,6 +254,28 @@ qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* 
                                       const int32_t* scales_granularity_mnk,
                                       const qg_paged_kv* kv, uint32_t layer_idx,
                                       hipStream_t stream);
+
+/*
+ * kv_matmul_ragged_paged_scale - the key and the value projections of the same
+ * tokens in one call, written into planes 0 (keys) and 1 (values) of layer
+ * `layer_idx`.
+ *
+ * The K-projection page's kv_collection holds keys and values; this is its
+ * computation with the value weights appended: weight = [W_k | W_v], so
+ *
+ *   weight        fp8 e4m3 [Kh, 2N], N = Hkv * D: columns 0..N-1 give keys,
+ *                 N..2N-1 values
+ *   weight_scale  f32 [Kh / 128, 2N / 128]
+ *
+ * and every other argument, check and rule is as k_matmul_ragged_paged_scale's
+ * (bf16 or fp8 cache).
+ */
+qg_status kv_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,
+                                       const qg_tensor* weight, const qg_tensor* input_scale,
+                                       const qg_tensor* weight_scale,
+                                       const int32_t* scales_granularity_mnk,
+                                       const qg_paged_kv* kv, uint32_t layer_idx,
+                                       hipStream_t stream);
 
 /* Static, never-NULL text for a status code. */
 const char* qg_status_string(qg_status s);

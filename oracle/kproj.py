@@ -22,17 +22,26 @@ Readings where the page is silent:
     the cached history); cache_lengths itself is not updated.
   * The result is rounded to bf16 (round-to-nearest-even); every byte of the
     cache that no token targets keeps its prior value.
+  * Quantized cache (kv_collection's scale_dtype_ / quantization_granularity_
+    parameters, otherwise undescribed): e4m3 codes with one float32 scale per
+    run of G head-dim elements of a cache row. The writer takes the fp32 value x
+    of each element, amax = max |x| over the run, s = amax / 448 and code =
+    e4m3(x / s) (nearest even; 0 when amax = 0), each division in float32, the
+    precision in which the GPU kernel decides the codes.
+  * Values (kv_matmul_ragged_paged_scale): the same product with the value
+    weights appended to the key weights ([W_k | W_v]); columns N..2N-1 go to
+    plane 1 of the same (page, slot).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .numerics import decode_bf16, decode_e4m3, round_to_bf16, bf16_bits_of
+from .numerics import decode_bf16, decode_e4m3, encode_e4m3, round_to_bf16, bf16_bits_of
 
 
-def kproj_rows(hidden_bits, weight_codes, input_scale, weight_scale,
-               granularity=(1, 128, 128)) -> np.ndarray:
-    """round_bf16( (hidden * input_scale) . (weight * weight_scale) ) as bf16 bits [T, N]."""
+def kproj_exact(hidden_bits, weight_codes, input_scale, weight_scale,
+                granularity=(1, 128, 128)) -> np.ndarray:
+    """(hidden * input_scale) . (weight * weight_scale) in float64, [T, N]."""
     gm, gn, gk = granularity
     if (gm, gn, gk) != (1, 128, 128):
         raise ValueError("only (1, 128, 128) scale granularity is defined here")
@@ -48,9 +57,29 @@ def kproj_rows(hidden_bits, weight_codes, input_scale, weight_scale,
         raise ValueError("scale shape mismatch")
     x = h * isc[:, np.arange(K) // gk]
     wf = w * wsc[np.arange(K) // gk][:, np.arange(N) // gn]
-    r = round_to_bf16(x @ wf)
+    return x @ wf
+
+
+def kproj_rows(hidden_bits, weight_codes, input_scale, weight_scale,
+               granularity=(1, 128, 128)) -> np.ndarray:
+    """round_bf16( (hidden * input_scale) . (weight * weight_scale) ) as bf16 bits [T, N]."""
+    r = round_to_bf16(kproj_exact(hidden_bits, weight_codes, input_scale, weight_scale, granularity))
     assert np.all(np.isfinite(r)), "bf16 overflow in the reference result"
     return bf16_bits_of(r)
+
+
+def quantize_runs(values, G: int):
+    """Rows of values -> (e4m3 codes, float32 scales [.., n / G]): per run of G
+    elements s = amax / 448 and code = e4m3(x / s), in float32 (code 0 and
+    s = 0 for an all-zero run)."""
+    x32 = np.asarray(values, dtype=np.float64).astype(np.float32)
+    T, n = x32.shape
+    runs = x32.reshape(T, n // G, G)
+    amax = np.abs(runs).max(axis=2)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0))
+    v = np.where(s[:, :, None] > 0, runs / safe[:, :, None], np.float32(0.0)).astype(np.float32)
+    return encode_e4m3(v.astype(np.float64)).reshape(T, n), s
 
 
 def token_slots(row_offsets, cache_lengths, page_table, page_size: int):
@@ -72,23 +101,58 @@ def token_slots(row_offsets, cache_lengths, page_table, page_size: int):
     return seq, page, slot
 
 
-def k_matmul_ragged_paged_scale(hidden_bits, row_offsets, weight_codes, input_scale,
-                                weight_scale, blocks_bits, cache_lengths, page_table,
-                                layer_idx: int, granularity=(1, 128, 128)) -> np.ndarray:
-    """Returns the updated cache (bf16 bits, same shape as blocks_bits)."""
-    blocks = np.array(blocks_bits, dtype=np.uint16, copy=True)
+def _project_into_cache(hidden_bits, row_offsets, weight_codes, input_scale, weight_scale, blocks_in,
+                        cache_lengths, page_table, layer_idx, granularity, planes, scales_in, qgran):
+    blocks = np.array(blocks_in, copy=True)
     if blocks.ndim != 6:
         raise ValueError("cache blocks are [L, 2, P, S, Hkv, D]")
     L, two, P, S, Hkv, D = blocks.shape
     if not (0 <= layer_idx < L):
         raise ValueError("layer_idx out of range")
-    kb = kproj_rows(hidden_bits, weight_codes, input_scale, weight_scale, granularity)
-    if kb.shape[1] != Hkv * D:
-        raise ValueError("weight columns must equal num_kv_heads * head_size")
+    exact = kproj_exact(hidden_bits, weight_codes, input_scale, weight_scale, granularity)
+    n = Hkv * D
+    if exact.shape[1] != planes * n:
+        raise ValueError("weight columns must equal planes * num_kv_heads * head_size")
     offs = np.asarray(row_offsets, dtype=np.int64)
-    if offs[-1] != kb.shape[0]:
+    if offs[-1] != exact.shape[0]:
         raise ValueError("input_row_offsets must end at sum(seq_lens)")
     _, page, slot = token_slots(row_offsets, cache_lengths, page_table, S)
-    for t in range(kb.shape[0]):
-        blocks[layer_idx, 0, page[t], slot[t]] = kb[t].reshape(Hkv, D)
-    return blocks
+    fp8 = blocks.dtype == np.uint8
+    scales = np.array(scales_in, copy=True) if fp8 else None
+    for plane in range(planes):
+        part = exact[:, plane * n:(plane + 1) * n]
+        if fp8:
+            if D % qgran:
+                raise ValueError("quantization granularity must divide head_size")
+            codes, sc = quantize_runs(part, qgran)
+        else:
+            r = round_to_bf16(part)
+            assert np.all(np.isfinite(r)), "bf16 overflow in the reference result"
+            codes = bf16_bits_of(r)
+        for t in range(exact.shape[0]):
+            blocks[layer_idx, plane, page[t], slot[t]] = codes[t].reshape(Hkv, D)
+            if fp8:
+                scales[layer_idx, plane, page[t], slot[t]] = sc[t].reshape(Hkv, D // qgran)
+    return (blocks, scales) if fp8 else blocks
+
+
+def k_matmul_ragged_paged_scale(hidden_bits, row_offsets, weight_codes, input_scale,
+                                weight_scale, blocks_bits, cache_lengths, page_table,
+                                layer_idx: int, granularity=(1, 128, 128), scales=None,
+                                quantization_granularity: int = 0):
+    """Returns the updated cache: bf16 bits shaped like blocks_bits, or, for an e4m3
+    cache (uint8 blocks), the pair (codes, float32 scales)."""
+    return _project_into_cache(hidden_bits, row_offsets, weight_codes, input_scale, weight_scale, blocks_bits,
+                               cache_lengths, page_table, layer_idx, granularity, 1, scales,
+                               quantization_granularity)
+
+
+def kv_matmul_ragged_paged_scale(hidden_bits, row_offsets, weight_codes, input_scale,
+                                 weight_scale, blocks_bits, cache_lengths, page_table,
+                                 layer_idx: int, granularity=(1, 128, 128), scales=None,
+                                 quantization_granularity: int = 0):
+    """Keys and values at once: weight_codes is [Kh, 2N] = [W_k | W_v]; columns
+    N..2N-1 are written to plane 1. Returns as k_matmul_ragged_paged_scale."""
+    return _project_into_cache(hidden_bits, row_offsets, weight_codes, input_scale, weight_scale, blocks_bits,
+                               cache_lengths, page_table, layer_idx, granularity, 2, scales,
+                               quantization_granularity)

@@ -27,6 +27,7 @@ class Fmt:
 
 F16 = Fmt("f16", p=11, emin=-14, max_finite=65504.0)
 BF16 = Fmt("bf16", p=8, emin=-126, max_finite=float(np.ldexp(255.0, 120)))  # (2 - 2^-7) * 2^127
+E4M3 = Fmt("e4m3", p=4, emin=-6, max_finite=448.0)
 
 
 def round_to(x, fmt: Fmt) -> np.ndarray:
@@ -109,3 +110,24 @@ def decode_e4m3(codes) -> np.ndarray:
                    np.ldexp((8 + m).astype(np.float64), e - 10))
     val = np.where((c & 0x7F) == 0x7F, np.nan, val)
     return sign * val
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """float64 values -> OCP E4M3 ("fn") codes, rounding to nearest (ties to even).
+
+    Magnitudes above 448 saturate to 448 (the format has no infinity; a writer
+    that scales by amax / 448 only ever exceeds 448 by a rounding error). The
+    sign is kept, also for results that round to zero (code 0x80).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert not np.any(np.isnan(x)), "NaN has no E4M3 code here"
+    r = round_to(np.clip(x, -448.0, 448.0), E4M3)
+    sign = np.signbit(r).astype(np.int64)
+    a = np.abs(r)
+    sub = a < 2.0 ** -6
+    m_sub = np.rint(a * 2.0 ** 9).astype(np.int64)             # a = m * 2^-9, m < 8
+    _, e2 = np.frexp(np.where(sub, 1.0, a))                      # a = f * 2^e2, 0.5 <= f < 1
+    e = e2 - 1                                                   # a = (8 + m) * 2^(e - 3)
+    m_norm = np.rint(np.where(sub, 8.0, a) / np.ldexp(1.0, e - 3)).astype(np.int64) - 8
+    code = np.where(sub, m_sub, ((e + 7) << 3) | m_norm)
+    return ((sign << 7) | code).astype(np.uint8)

@@ -196,22 +196,29 @@ def grouped_w4_inputs(seed: int = 6, E: int = 64, T: int = 4096, K: int = 2048, 
 class KProjInputs:
     hidden: np.ndarray        # uint16 [T, Kh] bf16 bits
     row_offsets: np.ndarray   # uint32 [B+1]
-    weight: np.ndarray        # uint8  [Kh, N] e4m3 codes
+    weight: np.ndarray        # uint8  [Kh, planes * N] e4m3 codes
     input_scale: np.ndarray   # float32 [T, Kh/128]
-    weight_scale: np.ndarray  # float32 [Kh/128, N/128]
-    blocks: np.ndarray        # uint16 [L, 2, P, S, Hkv, D] bf16 bits (prior cache content)
+    weight_scale: np.ndarray  # float32 [Kh/128, planes * N/128]
+    blocks: np.ndarray        # [L, 2, P, S, Hkv, D] prior cache content: uint16 bf16 bits, or uint8 e4m3 codes
     cache_lengths: np.ndarray  # uint32 [B]
     page_table: np.ndarray    # uint32 [B, max_pages]
     layer_idx: int
     granularity: tuple = (1, 128, 128)
+    scales: np.ndarray | None = None   # e4m3 cache: float32 [L, 2, P, S, Hkv, D / qgran]
+    qgran: int = 0                     # e4m3 cache: head-dim elements per scale
 
 
 def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4096,
                  n_kv_heads: int = 8, head_dim: int = 128, page_size: int = 128,
                  num_pages: int | None = None, num_layers: int = 2, layer_idx: int = 1,
                  cache_lengths=None, fill: int = 0xFFFF, lens=None,
-                 max_pages: int | None = None) -> KProjInputs:
+                 max_pages: int | None = None, planes: int = 1, cache: str = "bf16",
+                 qgran: int = 128) -> KProjInputs:
     """K-projection workload. Draw order: lengths, hidden, weight, input scales, page table.
+
+    planes = 2 draws [W_k | W_v] (2N columns) for the fused key/value projection.
+    cache = "fp8" gives an e4m3 cache (prior codes 0x7F, a NaN the writers never
+    produce) with float32 scales (prior value -1) per `qgran` head-dim elements.
 
     `cache_lengths` (tokens already cached per sequence) defaults to zeros; the page
     table has `max_pages` entries per sequence (default: enough for max_len new tokens on
@@ -227,11 +234,12 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
     T = int(offs[-1])
     N = n_kv_heads * head_dim
     hidden = bf16_bits(rng.standard_normal((T, Kh)))
-    w_real = rng.normal(0.0, 0.02, size=(Kh, N))
-    blk = w_real.reshape(Kh // 128, 128, N // 128, 128)
+    NW = planes * N
+    w_real = rng.normal(0.0, 0.02, size=(Kh, NW))
+    blk = w_real.reshape(Kh // 128, 128, NW // 128, 128)
     amax = np.abs(blk).max(axis=(1, 3)).astype(np.float32)
     ws = (amax / np.float32(448.0)).astype(np.float32)
-    w_codes = e4m3_codes((blk / ws[:, None, :, None].astype(np.float64)).reshape(Kh, N))
+    w_codes = e4m3_codes((blk / ws[:, None, :, None].astype(np.float64)).reshape(Kh, NW))
     in_scale = rng.uniform(0.5, 2.0, size=(T, Kh // 128)).astype(np.float32)
     if cache_lengths is None:
         cache_lengths = np.zeros(batch, dtype=np.uint32)
@@ -245,8 +253,14 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
     assert num_pages >= batch * max_pages
     perm = rng.permutation(num_pages).astype(np.uint32)
     page_table = perm[: batch * max_pages].reshape(batch, max_pages).copy()
-    blocks = np.full((num_layers, 2, num_pages, page_size, n_kv_heads, head_dim), fill,
-                     dtype=np.uint16)
+    shape = (num_layers, 2, num_pages, page_size, n_kv_heads, head_dim)
+    scales = None
+    if cache == "fp8":
+        blocks = np.full(shape, 0x7F, dtype=np.uint8)
+        scales = np.full(shape[:5] + (head_dim // qgran,), -1.0, dtype=np.float32)
+    else:
+        blocks = np.full(shape, fill, dtype=np.uint16)
     return KProjInputs(hidden=hidden, row_offsets=offs, weight=w_codes, input_scale=in_scale,
                        weight_scale=ws, blocks=blocks, cache_lengths=cache_lengths,
-                       page_table=page_table, layer_idx=layer_idx)
+                       page_table=page_table, layer_idx=layer_idx, scales=scales,
+                       qgran=qgran if cache == "fp8" else 0)

@@ -31,7 +31,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
-            "qg_status_string"} <= set(names)
+            "kv_matmul_ragged_paged_scale", "qg_status_string"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     for n in names:
@@ -208,16 +208,54 @@ def test_grouped_w4_rejections(lib):
                                ctypes.byref(s), ctypes.byref(ids), None, 128, 8, None) == QG.ERR_NULL
 
 
-def kp_call(lib, h, offs, w, isc, wsc, blocks, layer, gran=(1, 128, 128), cl=1, pt=1, maxp=2):
+def kp_call(lib, h, offs, w, isc, wsc, blocks, layer, gran=(1, 128, 128), cl=1, pt=1, maxp=2, scales=None,
+            qgran=0, fused=False):
     g = (ctypes.c_int32 * 3)(*gran)
     kv = QgPagedKV()
     kv.blocks = blocks
     kv.cache_lengths = cl
     kv.page_table = pt
     kv.max_pages_per_seq = maxp
-    return lib.k_matmul_ragged_paged_scale(ctypes.byref(h), ctypes.byref(offs), ctypes.byref(w),
-                                           ctypes.byref(isc), ctypes.byref(wsc), g, ctypes.byref(kv),
-                                           layer, None)
+    if scales is not None:
+        kv.scales = scales
+    kv.quantization_granularity = qgran
+    fn = lib.kv_matmul_ragged_paged_scale if fused else lib.k_matmul_ragged_paged_scale
+    return fn(ctypes.byref(h), ctypes.byref(offs), ctypes.byref(w), ctypes.byref(isc), ctypes.byref(wsc), g,
+              ctypes.byref(kv), layer, None)
+
+
+def test_kv_and_fp8_cache_rejections(lib):
+    bb = Buf()
+    T, Kh, Hkv, D, B = 10, 256, 2, 128, 2
+    N = Hkv * D
+    h, offs, isc = bb.t((T, Kh), QG.BF16), bb.t((B + 1,), QG.U32), bb.t((T, 2), QG.F32)
+    w, wsc = bb.t((Kh, N), QG.FP8_E4M3), bb.t((2, N // 128), QG.F32)
+    w2, wsc2 = bb.t((Kh, 2 * N), QG.FP8_E4M3), bb.t((2, 2 * N // 128), QG.F32)
+    blocks = bb.t((2, 2, 4, 16, Hkv, D), QG.BF16)
+    q8 = bb.t((2, 2, 4, 16, Hkv, D), QG.FP8_E4M3)
+    sc = lambda g: bb.t((2, 2, 4, 16, Hkv, D // g), QG.F32)
+    # fused keys and values: the weight has 2 * Hkv * D columns
+    assert kp_call(lib, h, offs, w, isc, wsc, blocks, 0, fused=True) == QG.ERR_SHAPE
+    assert kp_call(lib, h, offs, w2, isc, wsc2, blocks, 0) == QG.ERR_SHAPE
+    assert kp_call(lib, h, offs, w2, isc, wsc, blocks, 0, fused=True) == QG.ERR_SHAPE   # weight_scale columns
+    # per-plane width must be a multiple of 128 (three 64-wide heads: 192)
+    b3 = bb.t((2, 2, 4, 16, 3, 64), QG.BF16)
+    assert kp_call(lib, h, offs, bb.t((Kh, 384), QG.FP8_E4M3), isc, bb.t((2, 3), QG.F32), b3, 0,
+                   fused=True) == QG.ERR_SHAPE
+    # e4m3 cache: scales required, shaped [L, 2, P, S, Hkv, D / G], f32; G in {32, 64, 128} dividing D
+    assert kp_call(lib, h, offs, w, isc, wsc, q8, 0, qgran=128) == QG.ERR_RANK
+    assert kp_call(lib, h, offs, w, isc, wsc, q8, 0, scales=sc(64), qgran=128) == QG.ERR_SHAPE
+    assert kp_call(lib, h, offs, w, isc, wsc, q8, 0, scales=bb.t((2, 2, 4, 16, Hkv, 1), QG.BF16),
+                   qgran=128) == QG.ERR_DTYPE
+    assert kp_call(lib, h, offs, w, isc, wsc, q8, 0, scales=sc(16), qgran=16) == QG.ERR_UNSUPPORTED
+    assert kp_call(lib, h, offs, w, isc, wsc, q8, 0, scales=sc(128), qgran=0) == QG.ERR_UNSUPPORTED
+    q96 = bb.t((2, 2, 4, 16, 4, 96), QG.FP8_E4M3)
+    assert kp_call(lib, h, offs, bb.t((Kh, 384), QG.FP8_E4M3), isc, bb.t((2, 3), QG.F32), q96, 0,
+                   scales=bb.t((2, 2, 4, 16, 4, 1), QG.F32), qgran=64) == QG.ERR_UNSUPPORTED
+    # a valid e4m3-cache call with no tokens is a no-op (validation passes)
+    h0, isc0 = bb.t((0, Kh), QG.BF16), bb.t((0, 2), QG.F32)
+    assert kp_call(lib, h0, offs, w2, isc0, wsc2, q8, 0, scales=sc(32), qgran=32, fused=True) == QG.OK
+    assert kp_call(lib, h0, offs, w, isc0, wsc, q8, 1, scales=sc(128), qgran=128) == QG.OK
 
 
 def test_kproj_rejections(lib):

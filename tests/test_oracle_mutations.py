@@ -115,13 +115,59 @@ def test_kproj_mutations_are_caught(monkeypatch):
     monkeypatch.setattr(okp, "token_slots", orig)
 
     # weight scale indexed with a transposed block index
-    orig_rows = okp.kproj_rows
+    orig_exact = okp.kproj_exact
 
-    def bad_rows(hidden_bits, weight_codes, input_scale, weight_scale, granularity=(1, 128, 128)):
-        return orig_rows(hidden_bits, weight_codes, input_scale, np.ascontiguousarray(weight_scale.T), granularity)
-    monkeypatch.setattr(okp, "kproj_rows", bad_rows)
+    def bad_exact(hidden_bits, weight_codes, input_scale, weight_scale, granularity=(1, 128, 128)):
+        return orig_exact(hidden_bits, weight_codes, input_scale, np.ascontiguousarray(weight_scale.T), granularity)
+    monkeypatch.setattr(okp, "kproj_exact", bad_exact)
     with pytest.raises(AssertionError):
         tkp.test_brute_force_loops()
+
+
+def _quantize_variant(kind):
+    def f(values, G):
+        x32 = np.asarray(values, dtype=np.float64).astype(np.float32)
+        T, n = x32.shape
+        runs = x32.reshape(T, G, n // G).transpose(0, 2, 1) if kind == "run_stride" else x32.reshape(T, n // G, G)
+        amax = np.abs(runs).max(axis=2)
+        s = (amax / np.float32(240.0 if kind == "fnuz_max" else 448.0)).astype(np.float32)
+        safe = np.where(s > 0, s, np.float32(1.0))
+        v = np.where(s[:, :, None] > 0, runs / safe[:, :, None], np.float32(0.0)).astype(np.float64)
+        codes = nm.encode_e4m3(v)
+        if kind == "truncate":   # round toward zero: step back every code that rounded up in magnitude
+            over = (np.abs(nm.decode_e4m3(codes)) > np.abs(v)) & ((codes & 0x7F) > 0)
+            codes = np.where(over, codes - 1, codes).astype(np.uint8)
+        if kind == "run_stride":
+            codes = codes.reshape(T, n // G, G).transpose(0, 2, 1)
+        return codes.reshape(T, n), s
+    return f
+
+
+E4M3_CACHE_PINS = [tkp.test_e4m3_cache_reproduces_exact_codes, tkp.test_e4m3_cache_rounds_to_nearest_even_and_zero_runs]
+
+
+@pytest.mark.parametrize("kind", ["fnuz_max", "truncate", "run_stride"])
+def test_e4m3_cache_mutation_is_caught(kind, monkeypatch):
+    monkeypatch.setattr(okp, "quantize_runs", _quantize_variant(kind))
+    failures = 0
+    for pin in E4M3_CACHE_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1, kind
+
+
+def test_kv_plane_swap_is_caught(monkeypatch):
+    orig_exact = okp.kproj_exact
+
+    def swapped(hidden_bits, weight_codes, input_scale, weight_scale, granularity=(1, 128, 128)):
+        x = orig_exact(hidden_bits, weight_codes, input_scale, weight_scale, granularity)
+        h = x.shape[1] // 2
+        return np.concatenate([x[:, h:], x[:, :h]], axis=1)
+    monkeypatch.setattr(okp, "kproj_exact", swapped)
+    with pytest.raises(AssertionError):
+        tkp.test_kv_planes_fingerprint_and_untouched_bytes()
 
 
 def _grouped_w4_variant(kind):

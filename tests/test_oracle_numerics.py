@@ -101,3 +101,22 @@ def test_bits_of_roundtrip():
     assert np.array_equal(nm.bf16_bits_of(bvals), ALL16[:0x7F80])
     with pytest.raises(AssertionError):
         nm.f16_bits_of(np.array([1.0 + 2.0 ** -12]))
+
+
+def test_encode_e4m3_matches_torch_and_ties_to_even():
+    """Every finite code round-trips; a dense sweep of values (and every midpoint
+    between neighbouring codes) rounds as torch's float8_e4m3fn cast does."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    assert np.array_equal(nm.encode_e4m3(nm.decode_e4m3(codes)), codes)
+    pos = np.sort(nm.decode_e4m3(np.arange(0, 0x7F, dtype=np.uint8)))       # 0 .. 448
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(0)
+    sweep = np.concatenate([mids, -mids, rng.uniform(-448, 448, 20000), rng.uniform(-0.05, 0.05, 20000),
+                            [448.0, -448.0, 0.0, 2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -6 * 0.999]])
+    ref = torch.from_numpy(sweep.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = nm.encode_e4m3(sweep.astype(np.float32).astype(np.float64))
+    assert np.array_equal(got, ref)
+    # ties to the even code: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39)
+    assert nm.encode_e4m3(np.array([1.0625, 1.1875, -1.0625]))[:].tolist() == [0x38, 0x3A, 0xB8]
+    # saturation just above the largest finite value, signed zero kept
+    assert nm.encode_e4m3(np.array([448.0 * (1 + 2.0 ** -20), -1e-9, 0.0])).tolist() == [0x7E, 0x80, 0x00]
