@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
     "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
     "kvproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
     "kvproj_e4m3": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
+    "kproj_e4m3h": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
@@ -94,6 +95,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "decode_bf16", "prefill_bf16",
                                                            "decode_gate", "prefill_gate", "kvproj", "kvproj_e4m3",
+                                                           "kproj_e4m3h",
                                                            "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
@@ -452,22 +454,26 @@ class KProjFP8:
     dtype = "bf16"
     planes = 1          # 2: keys and values ([W_k | W_v]) in one call
     cache = "bf16"      # or "fp8": e4m3 cache with one f32 scale per head row (G = 128)
+    hidden = "bf16"     # or "fp8": e4m3 hidden rows, one f32 scale per token per 128 columns
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
-        k = synth.kproj_inputs(planes=self.planes, cache=self.cache, qgran=128)
+        k = synth.kproj_inputs(planes=self.planes, cache=self.cache, qgran=128, hidden=self.hidden)
         self.k = k
         T, Kh = k.hidden.shape
         N = k.weight.shape[1]
         self.T, self.Kh, self.N = T, Kh, N
         self.flops_per_step = 2 * T * Kh * N
         out_bytes = T * N * (1 + 4 / 128) if self.cache == "fp8" else T * N * 2   # codes + scales, or bf16
-        self.bytes_per_step = (T * Kh * 2 + Kh * N + k.input_scale.nbytes + k.weight_scale.nbytes + out_bytes
+        self.bytes_per_step = (k.hidden.nbytes + Kh * N + k.input_scale.nbytes + k.weight_scale.nbytes + out_bytes
                                + k.row_offsets.nbytes + k.cache_lengths.nbytes + k.page_table.nbytes)
         foot = k.hidden.nbytes + k.weight.nbytes + k.blocks.nbytes + k.input_scale.nbytes
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
         dev = torch.device("cuda")
-        h = torch.from_numpy(k.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        if self.hidden == "fp8":
+            h = torch.from_numpy(k.hidden).to(dev).view(torch.float8_e4m3fn)
+        else:
+            h = torch.from_numpy(k.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
         w = torch.from_numpy(k.weight).to(dev).view(torch.float8_e4m3fn)
         isc = torch.from_numpy(k.input_scale).to(dev)
         wsc = torch.from_numpy(k.weight_scale).to(dev)
@@ -483,7 +489,8 @@ class KProjFP8:
         self.slots = [(h.clone(), w.clone(), isc.clone(), wsc.clone(), blocks.clone(),
                        None if kvs is None else kvs.clone()) for _ in range(self.R)]
         self.name = (f"{'kvproj' if self.planes == 2 else 'kproj'}_fp8_paged_T{T}_K{Kh}_N{N}_page128"
-                     + ("_e4m3cache_g128" if self.cache == "fp8" else ""))
+                     + ("_e4m3cache_g128" if self.cache == "fp8" else "")
+                     + ("_e4m3hidden" if self.hidden == "fp8" else ""))
 
     def launches(self, step):
         h, w, isc, wsc, blocks, kvs = self.slots[step % self.R]
@@ -507,7 +514,7 @@ class KProjFP8:
             oracle.quantize_runs(y, 128)
         else:
             oracle.kproj_rows(k.hidden[:rows], k.weight, k.input_scale[:rows], k.weight_scale)
-        return 2 * rows * self.Kh * self.N, rows * self.Kh * 2 + self.Kh * self.N + rows * self.N * 2, \
+        return 2 * rows * self.Kh * self.N, rows * self.Kh * k.hidden.itemsize + self.Kh * self.N + rows * self.N * 2, \
             f"{rows} of {self.T} token rows (matmul + rounding or quantization; placement excluded)"
 
     def describe(self):
@@ -515,10 +522,22 @@ class KProjFP8:
         return {"workload": self.name, "tokens": self.T, "batch": len(k.row_offsets) - 1, "hidden": self.Kh,
                 "N": self.N, "page_size": int(k.blocks.shape[3]), "layers": int(k.blocks.shape[0]),
                 "layer_idx": k.layer_idx, "granularity_mnk": [1, 128, 128], "rotating_copies": self.R,
-                "planes": self.planes, "cache": "e4m3, one f32 scale per 128" if self.cache == "fp8" else "bf16"}
+                "planes": self.planes, "cache": "e4m3, one f32 scale per 128" if self.cache == "fp8" else "bf16",
+                "hidden": "e4m3, one f32 scale per 1x128" if self.hidden == "fp8" else "bf16"}
 
     def dense_equivalent(self):
         return (self.T, self.Kh, self.N, self.torch.bfloat16)
+
+
+class KProjE4M3Hidden(KProjFP8):
+    """The K-projection workload with e4m3 hidden rows: both MFMA operands are e4m3."""
+    kernel = "kproj_f8f8_kernel"
+    dtype = "e4m3"
+    hidden = "fp8"
+    mfma_peak = FP8_MFMA_PEAK_TFLOPS
+
+    def dense_equivalent(self):
+        return None
 
 
 class KVProjFP8(KProjFP8):
@@ -590,7 +609,7 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
              "decode_bf16": DecodeW4BF16, "prefill_bf16": PrefillW4BF16,
              "decode_gate": DecodeW4Gate, "prefill_gate": PrefillW4Gate,
-             "kvproj": KVProjFP8, "kvproj_e4m3": KVProjFP8Cache,
+             "kvproj": KVProjFP8, "kvproj_e4m3": KVProjFP8Cache, "kproj_e4m3h": KProjE4M3Hidden,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 
@@ -650,14 +669,15 @@ def main():
     gbs = wl.bytes_per_step / (ms_per_step * 1e-3) / 1e9
     tflops = wl.flops_per_step / (ms_per_step * 1e-3) / 1e12
     ai = wl.unit_flops() / wl.unit_bytes()        # FLOP per algorithmic byte
+    mfma_peak = getattr(wl, "mfma_peak", F16_MFMA_PEAK_TFLOPS)   # the contraction's own dtype
     if wl.bound == "hbm":
         value, unit = gbs, "GB/s"
         achieved, peak, runit = wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-        attainable = min(HBM_PEAK_GBS, F16_MFMA_PEAK_TFLOPS * 1e3 / ai)
+        attainable = min(HBM_PEAK_GBS, mfma_peak * 1e3 / ai)
     else:
         value, unit = tflops, "TFLOP/s"
-        achieved, peak, runit = wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12, F16_MFMA_PEAK_TFLOPS, "TFLOP/s"
-        attainable = min(F16_MFMA_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+        achieved, peak, runit = wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s"
+        attainable = min(mfma_peak, ai * HBM_PEAK_GBS / 1e3)
     out = {
         "metric": "W4A16 GEMM TFLOP/s + HBM GB/s (% roofline) at M=1..16 and M=2048, N=K=4096",
         "value": round(value, 3), "unit": unit,
@@ -674,7 +694,7 @@ def main():
                      "algorithmic_flops_per_launch": wl.unit_flops(),
                      "attainable": round(attainable, 1), "frac_attainable": round(achieved / attainable, 4),
                      "frac_hbm": round(wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "frac_mfma": round(wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)},
+                     "frac_mfma": round(wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12 / mfma_peak, 4)},
         "wall_s": round(wall, 3),
     }
     if not args.no_context:

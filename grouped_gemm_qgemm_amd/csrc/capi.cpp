@@ -252,7 +252,8 @@ static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_ro
       weight_scale->rank != 2 || kv->blocks.rank != 6)
     return QG_ERR_RANK;
   qg_status st;
-  if ((st = check_tensor(hidden, 2, QG_BF16)) != QG_OK) return st;
+  const bool hidden_fp8 = hidden->dtype == QG_FP8_E4M3;   // the page's dtype parameter: bf16 or e4m3
+  if ((st = check_tensor(hidden, 2, hidden_fp8 ? QG_FP8_E4M3 : QG_BF16)) != QG_OK) return st;
   if ((st = check_tensor(input_row_offsets, 1, QG_U32)) != QG_OK) return st;
   if ((st = check_tensor(weight, 2, QG_FP8_E4M3)) != QG_OK) return st;
   if ((st = check_tensor(input_scale, 2, QG_F32)) != QG_OK) return st;
@@ -301,8 +302,13 @@ static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_ro
   p.fp8 = fp8 ? 1 : 0;
   p.kv_scales = fp8 ? static_cast<float*>(kv->scales.data) : nullptr;
   p.qgran = (int)G;
-  const bool wide = fp8 || planes > 1;   // the third design only, with Kh / 128 <= 32
+  p.hidden_fp8 = hidden_fp8 ? 1 : 0;
   const int v = env_variant("QG_KPROJ_VARIANT", 0);
+  if (hidden_fp8) {                      // the fourth design only, with Kh / 128 <= 32
+    if (Kh / 128 > 32 || (v != 0 && (v < 21 || v > 23))) return QG_ERR_UNSUPPORTED;
+    return launch_status(qg::launch_kproj_fp8(p, v, stream));
+  }
+  const bool wide = fp8 || planes > 1;   // the third design only, with Kh / 128 <= 32
   if (wide && (Kh / 128 > 32 || (v != 0 && v < 6))) return QG_ERR_UNSUPPORTED;
   return launch_status(qg::launch_kproj_fp8(p, v, stream));
 }

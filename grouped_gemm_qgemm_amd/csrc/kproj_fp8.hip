@@ -408,6 +408,120 @@ __global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
   }
 }
 
+// Epilogue shared by the third and fourth designs: each token row of the tile
+// goes to (layer, plane, page, slot) of the cache, as bf16 or as e4m3 codes with
+// per-run scales (see the third design). acc holds a wave's 48 x 32 tile: rows
+// wm * 48 + mt * 16 + 4q + i, columns wn * 32 + 2 r16 + j (BLK false: a lane owns
+// two adjacent columns) or wn * 32 + 16 j + r16 (BLK true). `scratch` is LDS of
+// at least 4 * BM floats that no wave reads any more.
+template <int BM, bool Q8, bool BLK = false>
+__device__ __forceinline__ void kproj_store_tile(
+    const float4_t (&acc)[3][2], long long* row_dst, float* scratch, int tid, int m0, int n0, int T,
+    const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cache_len,
+    const uint32_t* __restrict__ page_table, int batch, int max_pages, int num_pages, int page_size, int layer,
+    int n_plane, void* __restrict__ blocks_v, float* __restrict__ kv_scales, int qgran) {
+  constexpr int MT = 3;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int plane = n0 / n_plane, colp = n0 - plane * n_plane;   // the tile's plane and column there
+  if (tid < BM) {
+    const int t = m0 + tid;
+    long long dst = -1;   // cache row (layer, plane, page, slot) of token t
+    if (t < T) {
+      int lo = 0, hi = batch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
+      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
+      const int slot = pos % page_size;
+      dst = (((long long)layer * 2 + plane) * num_pages + page) * page_size + slot;
+    }
+    row_dst[tid] = dst;
+  }
+  __syncthreads();
+  const int col = colp + wn * 32 + (BLK ? r16 : 2 * r16);   // column of acc[.][0]; acc[.][1]: +16 or +1
+  if constexpr (!Q8) {
+    uint16_t* __restrict__ blocks = static_cast<uint16_t*>(blocks_v);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
+        if (d >= 0) {
+          if constexpr (BLK) {
+            blocks[d * n_plane + col] = f2bf_rn(acc[mt][0][i]);
+            blocks[d * n_plane + col + 16] = f2bf_rn(acc[mt][1][i]);
+          } else {
+            const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
+            *reinterpret_cast<uint32_t*>(blocks + d * n_plane + col) = v;
+          }
+        }
+      }
+    }
+  } else {
+    uint8_t* __restrict__ blocks = static_cast<uint8_t*>(blocks_v);
+    // amax of each of the lane's rows over the wave's 32 columns
+    float am[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = fmaxf(fabsf(acc[mt][0][i]), fabsf(acc[mt][1][i]));
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
+        am[mt][i] = a;
+      }
+    }
+    const int gw = qgran / 32;   // waves per run of qgran columns: 1, 2 or 4 (workgroup-uniform)
+    if (gw > 1) {
+      float* amx = scratch;      // [wave column][row]
+      if (r16 == 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) amx[wn * BM + wm * 48 + mt * 16 + q * 4 + i] = am[mt][i];
+      }
+      __syncthreads();
+      const int w0 = wn & ~(gw - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 48 + mt * 16 + q * 4 + i;
+          float a = amx[w0 * BM + row];
+          for (int w = 1; w < gw; ++w) a = fmaxf(a, amx[(w0 + w) * BM + row]);
+          am[mt][i] = a;
+        }
+      }
+    }
+    const int nsc = n_plane / qgran;   // scales per cache row
+    const bool scale_writer = r16 == 0 && (wn & (gw - 1)) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
+        if (d < 0) continue;
+        const float sc = am[mt][i] / 448.0f;   // correctly rounded fp32 division
+        const float v0 = sc > 0.f ? acc[mt][0][i] / sc : 0.f;
+        const float v1 = sc > 0.f ? acc[mt][1][i] / sc : 0.f;
+        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);   // nearest even, low half
+        if constexpr (BLK) {
+          blocks[d * n_plane + col] = (uint8_t)pk;
+          blocks[d * n_plane + col + 16] = (uint8_t)(pk >> 8);
+        } else {
+          *reinterpret_cast<uint16_t*>(blocks + d * n_plane + col) = (uint16_t)pk;
+        }
+        if (scale_writer) kv_scales[d * nsc + (colp + wn * 32) / qgran] = sc;
+      }
+    }
+  }
+}
+
 // Third design: the second design's tiles (BM = 48 * WM rows x 128 columns,
 // one 128-deep stage per scale block) with WM x 4 waves, each owning a 48 x 32
 // wave tile (three 16-row by two 16-column MFMA tiles). With WM = 3 (the
@@ -595,91 +709,178 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     }
   }
 
-  const int plane = n0 / n_plane, colp = n0 - plane * n_plane;   // the tile's plane and column there
-  if (tid < BM) {
-    const int t = m0 + tid;
-    long long dst = -1;   // cache row (layer, plane, page, slot) of token t
-    if (t < T) {
-      int lo = 0, hi = batch;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
-      }
-      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
-      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
-      const int slot = pos % page_size;
-      dst = (((long long)layer * 2 + plane) * num_pages + page) * page_size + slot;
+  kproj_store_tile<WM * 48, Q8>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch, max_pages,
+                                 num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
+}
+
+// Fourth design: fp8 (e4m3) hidden rows, so both operands are fp8 and one
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) covers a 16 x 16 output
+// tile over a whole 128-deep scale block; its fp32 result is scaled by
+// is[t][kb] * ws[kb][nb] and added to the accumulator, as in the third design,
+// whose tiles, waves and epilogue it shares (BM = 48 * WM rows x 128 columns,
+// 48 x 32 wave tiles).
+//   * Both tiles stay fp8 in LDS, copied as they are: hidden rows [BM][128 B]
+//     and the weight tile [128 k][128 n], 16-byte chunks XOR-swizzled by the
+//     low three row bits. No conversion, no transposed writes.
+//   * A fragment (row r16, K 32q .. 32q + 31): two 16-byte reads. B fragment
+//     (column r16, the same K): four 8-bit transpose reads
+//     (ds_read_b64_tr_b8); within each 16-lane group, lane m names K row
+//     32q + 8s + m / 2 and byte 8 (m % 2) of the column chunk, and lane i
+//     receives the eight K values of column i.
+//   * Staging: the stage's hidden and weight chunks form one list dealt to the
+//     threads round-robin; every thread issues the same number of loads (the
+//     last round re-reads its own chunks where the list runs out) so the
+//     compiler's in-order load counting sees one fixed sequence, and only
+//     in-list chunks are stored.
+template <int WM, bool Q8>
+__global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
+    const uint8_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
+    float* __restrict__ kv_scales, int qgran) {
+  constexpr int BM = 48 * WM;
+  constexpr int NTHR = WM * 256;
+  constexpr int MT = 3;
+  constexpr int ACH = BM * 8;                          // 16-byte hidden chunks per stage
+  constexpr int BCH = 128 * 8;                         // 16-byte weight chunks per stage
+  constexpr int LOADS = (ACH + BCH + NTHR - 1) / NTHR;  // loads per thread per stage
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][ACH];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
+  __shared__ long long row_dst[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  // this thread's chunks: source (byte offset at stage 0, bytes per stage) and LDS slot
+  const uint8_t* src[LOADS];
+  uint32_t sstep[LOADS];
+  int slot[LOADS];   // index into lds_a (< ACH) or ACH + index into lds_b; -1: not stored
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int id0 = tid + i * NTHR;
+    const bool in_list = id0 < ACH + BCH;
+    const int id = in_list ? id0 : id0 - NTHR;   // re-read this thread's previous chunk
+    if (id < ACH) {
+      const int row = id >> 3, ch = id & 7;
+      src[i] = H + (size_t)min(m0 + row, T - 1) * Kh + ch * 16;
+      sstep[i] = KBK;
+      slot[i] = row * 8 + (ch ^ (row & 7));
+    } else {
+      const int j = id - ACH, kr = j >> 3, ch = j & 7;
+      src[i] = W + (size_t)kr * N + n0 + ch * 16;
+      sstep[i] = (uint32_t)KBK * (uint32_t)N;
+      slot[i] = ACH + kr * 8 + (ch ^ (kr & 7));
     }
-    row_dst[tid] = dst;
+    if (!in_list) slot[i] = -1;
   }
+  auto load_stage = [&](int kb, u32x4_t (&r)[LOADS]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (size_t)kb * sstep[i]);
+  };
+  auto store_stage = [&](int buf, const u32x4_t (&r)[LOADS]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if (slot[i] < 0) continue;
+      if (slot[i] < ACH) lds_a[buf][slot[i]] = r[i];
+      else lds_b[buf][slot[i] - ACH] = r[i];
+    }
+  };
+
+  for (int e = tid; e < KB * BM; e += NTHR) {
+    const int row = e % BM, kb = e / BM;
+    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
+  }
+
+  float4_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  auto compute = [&](int kb, int buf) {
+    i32x8_t bf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = wn * 2 + t;   // the column chunk of column tile t
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kr = 32 * q + 8 * s4 + (r16 >> 1);
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + (c ^ (kr & 7))]) +
+                                    8 * (r16 & 1);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(__attribute__((address_space(3))) const unsigned char*)base);
+        bf[t][2 * s4] = v.x;
+        bf[t][2 * s4 + 1] = v.y;
+      }
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = wm * 48 + mt * 16 + r16;
+      const u32x4_t lo = lds_a[buf][row * 8 + ((2 * q) ^ (row & 7))];
+      const u32x4_t hi = lds_a[buf][row * 8 + ((2 * q + 1) ^ (row & 7))];
+      const i32x8_t av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bf[t], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, unit scales
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][t][i] += is4[i] * wsv * part[i];
+      }
+    }
+  };
+
+  u32x4_t rg[LOADS];
+  load_stage(0, rg);
+  store_stage(0, rg);
   __syncthreads();
-  const int col = colp + wn * 32 + 2 * r16;
-  if constexpr (!Q8) {
-    uint16_t* __restrict__ blocks = static_cast<uint16_t*>(blocks_v);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
-        if (d >= 0) {
-          const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
-          *reinterpret_cast<uint32_t*>(blocks + d * n_plane + col) = v;
-        }
-      }
-    }
-  } else {
-    uint8_t* __restrict__ blocks = static_cast<uint8_t*>(blocks_v);
-    // amax of each of the lane's rows over the wave's 32 columns
-    float am[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float a = fmaxf(fabsf(acc[mt][0][i]), fabsf(acc[mt][1][i]));
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) a = fmaxf(a, __shfl_xor(a, off));
-        am[mt][i] = a;
-      }
-    }
-    const int gw = qgran / 32;   // waves per run of qgran columns: 1, 2 or 4 (workgroup-uniform)
-    if (gw > 1) {
-      float* amx = lds_is;       // free after the main loop: [wave column][row]
-      if (r16 == 0) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) amx[wn * BM + wm * 48 + mt * 16 + q * 4 + i] = am[mt][i];
-      }
-      __syncthreads();
-      const int w0 = wn & ~(gw - 1);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = wm * 48 + mt * 16 + q * 4 + i;
-          float a = amx[w0 * BM + row];
-          for (int w = 1; w < gw; ++w) a = fmaxf(a, amx[(w0 + w) * BM + row]);
-          am[mt][i] = a;
-        }
-      }
-    }
-    const int nsc = n_plane / qgran;   // scales per cache row
-    const bool scale_writer = r16 == 0 && (wn & (gw - 1)) == 0;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
-        if (d < 0) continue;
-        const float sc = am[mt][i] / 448.0f;   // correctly rounded fp32 division
-        const float v0 = sc > 0.f ? acc[mt][0][i] / sc : 0.f;
-        const float v1 = sc > 0.f ? acc[mt][1][i] / sc : 0.f;
-        const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);   // nearest even, low half
-        *reinterpret_cast<uint16_t*>(blocks + d * n_plane + col) = (uint16_t)pk;
-        if (scale_writer) kv_scales[d * nsc + (colp + wn * 32) / qgran] = sc;
-      }
-    }
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    load_stage(more ? kb + 1 : kb, rg);   // unconditional: the last stage re-reads itself, unstored
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb, kb & 1);
+    if (more) store_stage((kb + 1) & 1, rg);
+    __syncthreads();
   }
+
+  // column tile t of a wave holds 16 consecutive columns (the transpose read's order)
+  kproj_store_tile<BM, Q8, true>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
+                                 max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
+}
+
+template <int WM>
+static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
+  constexpr int BM = 48 * WM;
+  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  const uint8_t* h = static_cast<const uint8_t*>(static_cast<const void*>(p.hidden));
+  if (p.fp8)
+    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, true>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
+                       p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                       (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                       (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, p.kv_scales, p.qgran);
+  else
+    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, false>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
+                       p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                       (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                       (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
+  return hipGetLastError();
 }
 
 template <int WM, int PD = 1>
@@ -733,6 +934,19 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
 }
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
+  if (p.hidden_fp8) {                   // fourth design: 48, 96 or 144-row tiles (auto), or forced
+    if (p.Kh / KBK > 32) return hipErrorNotSupported;
+    int wm = variant == 21 ? 1 : (variant == 22 ? 2 : (variant == 23 ? 3 : 0));
+    if (wm == 0) {
+      static const int cand[] = {48, 96, 144};
+      wm = pick_kproj_rows(p, cand, 3) / 48;
+    }
+    switch (wm) {
+      case 1: return launch_kproj_f8f8<1>(p, stream);
+      case 2: return launch_kproj_f8f8<2>(p, stream);
+      default: return launch_kproj_f8f8<3>(p, stream);
+    }
+  }
   const bool wide = p.fp8 || p.n_plane != p.N;   // fp8 cache or several planes: the third design only
   if (p.Kh / KBK > 32) {                // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
     if (wide) return hipErrorNotSupported;

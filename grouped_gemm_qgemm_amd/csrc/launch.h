@@ -72,6 +72,7 @@ struct KProjArgs {
   int fp8 = 0;                   // e4m3 cache with f32 scales
   float* kv_scales = nullptr;    // fp8: [L, 2, P, S, Hkv, D / qgran]
   int qgran = 0;                 // fp8: head-dim elements per scale (32, 64, 128)
+  int hidden_fp8 = 0;            // hidden is e4m3 [T, Kh] (then `hidden` points at bytes)
 };
 
 // Decode-shaped W4A16 (M <= 16). `variant` picks columns-per-lane and waves.

@@ -14,8 +14,9 @@ Readings where the page is silent:
   * Granularity (1, 128, 128): input_scale is [T, K/128] (one per row per 128
     K-elements), weight_scale is [K/128, N/128] (one per 128x128 weight block,
     oriented like weight [K, N]).
-  * weight is OCP fp8 E4M3; hidden is bf16 and is multiplied by its scale in
-    full precision (the activations are not quantized).
+  * weight is OCP fp8 E4M3; hidden is bf16 (the workload's type) or E4M3 (the
+    page's separate dtype parameter; a uint8 array here), and is multiplied by
+    its scale in full precision.
   * Cache layout blocks[L][2][P][S][Hkv][D] with plane 0 = keys, 1 = values;
     page_table[b][j] is the physical page of the j-th logical page of sequence b;
     token j of sequence b goes to position cache_lengths[b] + j (appended after
@@ -41,11 +42,13 @@ from .numerics import decode_bf16, decode_e4m3, encode_e4m3, round_to_bf16, bf16
 
 def kproj_exact(hidden_bits, weight_codes, input_scale, weight_scale,
                 granularity=(1, 128, 128)) -> np.ndarray:
-    """(hidden * input_scale) . (weight * weight_scale) in float64, [T, N]."""
+    """(hidden * input_scale) . (weight * weight_scale) in float64, [T, N]; hidden is
+    bf16 bits (uint16) or E4M3 codes (uint8)."""
     gm, gn, gk = granularity
     if (gm, gn, gk) != (1, 128, 128):
         raise ValueError("only (1, 128, 128) scale granularity is defined here")
-    h = decode_bf16(hidden_bits)
+    hb = np.asarray(hidden_bits)
+    h = decode_e4m3(hb) if hb.dtype == np.uint8 else decode_bf16(hb)
     w = decode_e4m3(weight_codes)
     T, K = h.shape
     K2, N = w.shape

@@ -194,7 +194,7 @@ def grouped_w4_inputs(seed: int = 6, E: int = 64, T: int = 4096, K: int = 2048, 
 
 @dataclasses.dataclass
 class KProjInputs:
-    hidden: np.ndarray        # uint16 [T, Kh] bf16 bits
+    hidden: np.ndarray        # [T, Kh]: uint16 bf16 bits, or uint8 e4m3 codes
     row_offsets: np.ndarray   # uint32 [B+1]
     weight: np.ndarray        # uint8  [Kh, planes * N] e4m3 codes
     input_scale: np.ndarray   # float32 [T, Kh/128]
@@ -213,12 +213,15 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
                  num_pages: int | None = None, num_layers: int = 2, layer_idx: int = 1,
                  cache_lengths=None, fill: int = 0xFFFF, lens=None,
                  max_pages: int | None = None, planes: int = 1, cache: str = "bf16",
-                 qgran: int = 128) -> KProjInputs:
+                 qgran: int = 128, hidden: str = "bf16") -> KProjInputs:
     """K-projection workload. Draw order: lengths, hidden, weight, input scales, page table.
 
     planes = 2 draws [W_k | W_v] (2N columns) for the fused key/value projection.
     cache = "fp8" gives an e4m3 cache (prior codes 0x7F, a NaN the writers never
     produce) with float32 scales (prior value -1) per `qgran` head-dim elements.
+    hidden = "fp8" stores the same normal draws as e4m3 codes with one float32
+    input scale per token per 128 columns (amax / 448 of the block), in place of
+    the uniform input scales (which are still drawn, keeping the draw order).
 
     `cache_lengths` (tokens already cached per sequence) defaults to zeros; the page
     table has `max_pages` entries per sequence (default: enough for max_len new tokens on
@@ -233,7 +236,8 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
     offs[1:] = np.cumsum(lens)
     T = int(offs[-1])
     N = n_kv_heads * head_dim
-    hidden = bf16_bits(rng.standard_normal((T, Kh)))
+    h_real = rng.standard_normal((T, Kh))
+    hidden_bits = bf16_bits(h_real)
     NW = planes * N
     w_real = rng.normal(0.0, 0.02, size=(Kh, NW))
     blk = w_real.reshape(Kh // 128, 128, NW // 128, 128)
@@ -241,6 +245,10 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
     ws = (amax / np.float32(448.0)).astype(np.float32)
     w_codes = e4m3_codes((blk / ws[:, None, :, None].astype(np.float64)).reshape(Kh, NW))
     in_scale = rng.uniform(0.5, 2.0, size=(T, Kh // 128)).astype(np.float32)
+    if hidden == "fp8":
+        hb = h_real.reshape(T, Kh // 128, 128)
+        in_scale = (np.abs(hb).max(axis=2) / 448.0).astype(np.float32)
+        hidden_bits = e4m3_codes((hb / in_scale[:, :, None].astype(np.float64)).reshape(T, Kh))
     if cache_lengths is None:
         cache_lengths = np.zeros(batch, dtype=np.uint32)
     cache_lengths = np.asarray(cache_lengths, dtype=np.uint32)
@@ -260,7 +268,7 @@ def kproj_inputs(seed: int = 5, batch: int = 8, max_len: int = 1024, Kh: int = 4
         scales = np.full(shape[:5] + (head_dim // qgran,), -1.0, dtype=np.float32)
     else:
         blocks = np.full(shape, fill, dtype=np.uint16)
-    return KProjInputs(hidden=hidden, row_offsets=offs, weight=w_codes, input_scale=in_scale,
+    return KProjInputs(hidden=hidden_bits, row_offsets=offs, weight=w_codes, input_scale=in_scale,
                        weight_scale=ws, blocks=blocks, cache_lengths=cache_lengths,
                        page_table=page_table, layer_idx=layer_idx, scales=scales,
                        qgran=qgran if cache == "fp8" else 0)

@@ -281,3 +281,27 @@ def test_e4m3_coarser_runs_take_the_largest_scale():
         c32 = o32[1, 0, page, slot].ravel()
         c128 = o128[1, 0, page, slot].ravel()
         assert np.array_equal(c32[same], c128[same])
+
+
+# ---------------------------------------------------------------- e4m3 hidden rows
+
+def test_e4m3_hidden_codes_through_the_op():
+    """Every finite code once in hidden column 0 against a unit weight: read back exactly."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    h = np.zeros((254, 256), np.uint8)
+    h[:, 0] = codes
+    w = np.zeros((256, 128), np.uint8)
+    w[0, 0] = 0x38
+    y = oracle.kproj_exact(h, w, np.ones((254, 2), np.float32), np.ones((2, 1), np.float32))
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(y[:, 0], ref)
+
+
+def test_e4m3_hidden_equals_the_bf16_path_on_the_same_values():
+    """Every e4m3 value is a bf16 value: the same numbers as bf16 bits give the same cache."""
+    k8 = synth.kproj_inputs(seed=9, lens=[7, 40], Kh=256, n_kv_heads=2, head_dim=128, page_size=16, max_len=40,
+                            hidden="fp8")
+    as_bf16 = nm.bf16_bits_of(nm.decode_e4m3(k8.hidden))
+    a = _run(k8)
+    b = _run(k8, hidden_bits=as_bf16)
+    assert np.array_equal(a, b)
