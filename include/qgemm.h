@@ -227,7 +227,8 @@ typedef struct {
  * input_scale / weight_scale multiply the input / the weight; the layer's cache is
  * chosen by layer_idx (Parameters: scales_granularity_mnk gives the scale blocks).
  *
- *   hidden            bf16 [T, Kh]
+ *   hidden            bf16 or fp8 e4m3 [T, Kh] (the page's dtype parameter; e4m3 runs
+ *                     both MFMA operands in e4m3, with Kh <= 4096)
  *   input_row_offsets u32  [B + 1]   offs[0] = 0, non-decreasing, offs[B] = T
  *   weight            fp8 e4m3 [Kh, N], N = Hkv * D
  *   input_scale       f32  [T, Kh / 128]
