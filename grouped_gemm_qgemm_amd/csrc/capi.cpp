@@ -305,7 +305,7 @@ static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_ro
   p.hidden_fp8 = hidden_fp8 ? 1 : 0;
   const int v = env_variant("QG_KPROJ_VARIANT", 0);
   if (hidden_fp8) {                      // the fourth design only, with Kh / 128 <= 32
-    if (Kh / 128 > 32 || (v != 0 && (v < 21 || v > 23))) return QG_ERR_UNSUPPORTED;
+    if (Kh / 128 > 32 || (v != 0 && (v < 21 || v > 27))) return QG_ERR_UNSUPPORTED;
     return launch_status(qg::launch_kproj_fp8(p, v, stream));
   }
   const bool wide = fp8 || planes > 1;   // the third design only, with Kh / 128 <= 32

@@ -731,8 +731,11 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
 //     threads round-robin; every thread issues the same number of loads (the
 //     last round re-reads its own chunks where the list runs out) so the
 //     compiler's in-order load counting sees one fixed sequence, and only
-//     in-list chunks are stored.
-template <int WM, bool Q8>
+//     in-list chunks are stored. PD stages are in flight in registers: stage
+//     kb + PD is requested while stage kb is multiplied, and stage kb + 1,
+//     requested PD - 1 stages earlier, is stored after it (a stage's MFMAs take
+//     far less time than a global load's latency).
+template <int WM, bool Q8, int PD>
 __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
     const uint8_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
     const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
@@ -846,17 +849,22 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
     }
   };
 
-  u32x4_t rg[LOADS];
-  load_stage(0, rg);
-  store_stage(0, rg);
+  u32x4_t rg[PD][LOADS];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_stage(min(p, KB - 1), rg[p]);
+  store_stage(0, rg[0]);
   __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
-    load_stage(more ? kb + 1 : kb, rg);   // unconditional: the last stage re-reads itself, unstored
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kb, kb & 1);
-    if (more) store_stage((kb + 1) & 1, rg);
-    __syncthreads();
+  for (int kb = 0; kb < KB; kb += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int i = kb + p;   // stage multiplied now; rg[p] (stage i, stored) takes stage i + PD
+      if constexpr (PD > 1) load_stage(min(i + PD, KB - 1), rg[p]);   // past the end: re-reads, unstored
+      else load_stage(min(i + 1, KB - 1), rg[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < KB) compute(i, i & 1);
+      if (i + 1 < KB) store_stage((i + 1) & 1, rg[(p + 1) % PD]);
+      __syncthreads();
+    }
   }
 
   // column tile t of a wave holds 16 consecutive columns (the transpose read's order)
@@ -864,19 +872,19 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
                                  max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
-template <int WM>
+template <int WM, int PD>
 static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
   const uint8_t* h = static_cast<const uint8_t*>(static_cast<const void*>(p.hidden));
   if (p.fp8)
-    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, true>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
+    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
                        p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
                        (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                        (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, p.kv_scales, p.qgran);
   else
-    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, false>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
+    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
                        p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
                        (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                        (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
@@ -934,18 +942,30 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
 }
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
-  if (p.hidden_fp8) {                   // fourth design: 48, 96 or 144-row tiles (auto), or forced
+  if (p.hidden_fp8) {
+    // fourth design: 48, 96 or 144-row tiles (auto: 0, 24-27; forced: 21-23) with
+    // PD stages in flight (24-27: PD = 1..4; otherwise 2, which measured 10 %
+    // faster than 1 and level with 3 and 4 at 4312 tokens)
     if (p.Kh / KBK > 32) return hipErrorNotSupported;
     int wm = variant == 21 ? 1 : (variant == 22 ? 2 : (variant == 23 ? 3 : 0));
+    const int pd = variant >= 24 && variant <= 27 ? variant - 23 : 2;
     if (wm == 0) {
       static const int cand[] = {48, 96, 144};
       wm = pick_kproj_rows(p, cand, 3) / 48;
     }
+#define QG_F8F8(W)                                            \
+  switch (pd) {                                               \
+    case 1: return launch_kproj_f8f8<W, 1>(p, stream);        \
+    case 2: return launch_kproj_f8f8<W, 2>(p, stream);        \
+    case 4: return launch_kproj_f8f8<W, 4>(p, stream);        \
+    default: return launch_kproj_f8f8<W, 3>(p, stream);       \
+  }
     switch (wm) {
-      case 1: return launch_kproj_f8f8<1>(p, stream);
-      case 2: return launch_kproj_f8f8<2>(p, stream);
-      default: return launch_kproj_f8f8<3>(p, stream);
+      case 1: QG_F8F8(1)
+      case 2: QG_F8F8(2)
+      default: QG_F8F8(3)
     }
+#undef QG_F8F8
   }
   const bool wide = p.fp8 || p.n_plane != p.N;   // fp8 cache or several planes: the third design only
   if (p.Kh / KBK > 32) {                // the v2/v3 kernels keep at most 32 input-scale blocks in LDS

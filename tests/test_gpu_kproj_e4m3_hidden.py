@@ -76,7 +76,8 @@ def test_e4m3_hidden_codes_bit_exact(gpu, lib):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("variant", [21, 22, 23])
+# 21-23: 48 / 96 / 144-row tiles; 24-27: automatic rows with 1-4 stages in flight
+@pytest.mark.parametrize("variant", [21, 22, 23, 24, 25, 26, 27])
 def test_every_launch_shape(gpu, lib, variant):
     check(lib, kv_inputs(40 + variant, (100, 1, 64, 65, 0, 130), Kh=512, cache_lengths=(0, 3, 17, 128, 5, 250),
                          planes=1, hidden="fp8"), "keys bf16", variant)
