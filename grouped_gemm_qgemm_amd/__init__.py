@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
     grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats,
                     group_size=128, pack_factor=8)
+    grouped_gemm_epilogue / grouped_gemm_w4_epilogue(..., epilogue, bias=None, residual=None, ...)
     k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
                                 weight_scale, kv_blocks, cache_lengths, page_table,
                                 layer_idx, scales_granularity_mnk=(1, 128, 128),
@@ -28,6 +29,7 @@ import os
 import torch
 
 __all__ = ["load", "QgError", "qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4",
+           "grouped_gemm_epilogue", "grouped_gemm_w4_epilogue",
            "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale", "status_string", "LIB_PATH", "QG", "EPI_BIAS", "EPI_RESIDUAL",
            "EPI_SILU_GATE"]
 
@@ -91,6 +93,12 @@ def load(path: str | None = None):
     lib.grouped_gemm_w4.argtypes = [T, T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p]
     lib.grouped_gemm_w4.restype = ctypes.c_int
+    lib.grouped_gemm_epilogue.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                          ctypes.c_int32, T, T, ctypes.c_void_p]
+    lib.grouped_gemm_epilogue.restype = ctypes.c_int
+    lib.grouped_gemm_w4_epilogue.argtypes = [T, T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, T, T, ctypes.c_void_p]
+    lib.grouped_gemm_w4_epilogue.restype = ctypes.c_int
     lib.k_matmul_ragged_paged_scale.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(QgPagedKV), ctypes.c_uint32, ctypes.c_void_p]
     lib.k_matmul_ragged_paged_scale.restype = ctypes.c_int
@@ -195,6 +203,40 @@ def grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_
                              ctypes.byref(describe(a_offsets, _u32(a_offsets))),
                              ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
                              ctypes.byref(describe(expert_ids)), usage, group_size, pack_factor, _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def _opt(t):
+    return ctypes.byref(describe(t)) if t is not None else None
+
+
+def grouped_gemm_epilogue(c, a, a_offsets, b, expert_ids, expert_usage_stats, epilogue: int, bias=None,
+                          residual=None, transpose_b: bool = True, stream=None, raise_on_error: bool = True) -> int:
+    """grouped_gemm followed by the fixed epilogue (bias [E, N] by expert, SiLU gate, residual)."""
+    lib = load()
+    usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
+    st = lib.grouped_gemm_epilogue(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                                   ctypes.byref(describe(a_offsets, _u32(a_offsets))), ctypes.byref(describe(b)),
+                                   ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)), int(epilogue),
+                                   _opt(bias), _opt(residual), _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def grouped_gemm_w4_epilogue(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats, epilogue: int,
+                             bias=None, residual=None, group_size: int = 128, pack_factor: int = 8, stream=None,
+                             raise_on_error: bool = True) -> int:
+    """grouped_gemm_w4 followed by the fixed epilogue (bias [E, N] by expert, SiLU gate, residual)."""
+    lib = load()
+    usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
+    st = lib.grouped_gemm_w4_epilogue(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                                      ctypes.byref(describe(a_offsets, _u32(a_offsets))),
+                                      ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
+                                      ctypes.byref(describe(expert_ids)), usage, group_size, pack_factor,
+                                      int(epilogue), _opt(bias), _opt(residual), _stream(stream))
     if raise_on_error:
         _check(st)
     return st

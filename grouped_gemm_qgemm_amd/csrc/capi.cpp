@@ -80,6 +80,32 @@ const char* qg_status_string(qg_status s) {
 
 int32_t qg_version(void) { return 100; }
 
+// Epilogue operands of a product Y [M, N] (gated output [M, N / 2]): bias has
+// the output type and shape [N] (E == 0) or one row per expert [E, N]; residual
+// is shaped like the output.
+static qg_status check_epilogue(int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual, qg_dtype act,
+                                int64_t E, int64_t M, int64_t N, qg::Epilogue* out) {
+  qg_status st;
+  const int64_t N_out = (epilogue & QG_EPI_SILU_GATE) ? N / 2 : N;
+  out->flags = epilogue;
+  if (epilogue & QG_EPI_BIAS) {
+    if (!bias) return QG_ERR_NULL;
+    const int rank = E == 0 ? 1 : 2;
+    if (bias->rank != rank) return QG_ERR_RANK;
+    if ((st = check_tensor(bias, rank, act)) != QG_OK) return st;
+    if (E == 0 ? bias->shape[0] != N : (bias->shape[0] != E || bias->shape[1] != N)) return QG_ERR_SHAPE;
+    out->bias = static_cast<const uint16_t*>(bias->data);
+  }
+  if (epilogue & QG_EPI_RESIDUAL) {
+    if (!residual) return QG_ERR_NULL;
+    if (residual->rank != 2) return QG_ERR_RANK;
+    if ((st = check_tensor(residual, 2, act)) != QG_OK) return st;
+    if (residual->shape[0] != M || residual->shape[1] != N_out) return QG_ERR_SHAPE;
+    out->residual = static_cast<const uint16_t*>(residual->data);
+  }
+  return QG_OK;
+}
+
 static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
                                const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
                                int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
@@ -109,22 +135,8 @@ static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_
   if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
     return QG_ERR_UNSUPPORTED;
   if (N % 8 != 0) return QG_ERR_ALIGN;
-  qg::W4Epilogue epi;
-  epi.flags = epilogue;
-  if (epilogue & QG_EPI_BIAS) {
-    if (!bias) return QG_ERR_NULL;
-    if (bias->rank != 1) return QG_ERR_RANK;
-    if ((st = check_tensor(bias, 1, act)) != QG_OK) return st;
-    if (bias->shape[0] != N) return QG_ERR_SHAPE;
-    epi.bias = static_cast<const uint16_t*>(bias->data);
-  }
-  if (epilogue & QG_EPI_RESIDUAL) {
-    if (!residual) return QG_ERR_NULL;
-    if (residual->rank != 2) return QG_ERR_RANK;
-    if ((st = check_tensor(residual, 2, act)) != QG_OK) return st;
-    if (residual->shape[0] != M || residual->shape[1] != N_out) return QG_ERR_SHAPE;
-    epi.residual = static_cast<const uint16_t*>(residual->data);
-  }
+  qg::Epilogue epi;
+  if ((st = check_epilogue(epilogue, bias, residual, act, 0, M, N, &epi)) != QG_OK) return st;
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of C
@@ -164,10 +176,10 @@ qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_ten
   return qgemm_w4_impl(c, a, b_packed, scales, group_size, pack_factor, epilogue, bias, residual, stream);
 }
 
-qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
-                       const qg_tensor* b, const qg_tensor* expert_ids,
-                       const uint32_t* expert_usage_stats_host, int32_t transpose_b,
-                       hipStream_t stream) {
+static qg_status grouped_gemm_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                   const qg_tensor* b, const qg_tensor* expert_ids,
+                                   const uint32_t* expert_usage_stats_host, int32_t transpose_b, int32_t epilogue,
+                                   const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
   if (!c || !a || !a_offsets || !b || !expert_ids || !expert_usage_stats_host) return QG_ERR_NULL;
   if (c->rank != 2 || a->rank != 2 || a_offsets->rank != 1 || b->rank != 3 || expert_ids->rank != 1)
     return QG_ERR_RANK;
@@ -182,11 +194,17 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
   const int64_t N = transpose_b ? b->shape[1] : b->shape[2];
   const int64_t Kb = transpose_b ? b->shape[2] : b->shape[1];
   const int64_t G = expert_ids->shape[0];
-  if (c->shape[0] != T || c->shape[1] != N || Kb != K) return QG_ERR_SHAPE;
+  if (epilogue & ~(QG_EPI_BIAS | QG_EPI_RESIDUAL | QG_EPI_SILU_GATE)) return QG_ERR_INVALID_ARG;
+  const bool gate = (epilogue & QG_EPI_SILU_GATE) != 0;
+  if (gate && N % 16 != 0) return QG_ERR_ALIGN;   // (gate, up) pairs, and an 8-aligned output
+  const int64_t N_out = gate ? N / 2 : N;
+  if (c->shape[0] != T || c->shape[1] != N_out || Kb != K) return QG_ERR_SHAPE;
   if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
   const uint32_t num_active = expert_usage_stats_host[1];
   if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
   if (K % 8 != 0 || N % 8 != 0) return QG_ERR_ALIGN;
+  qg::Epilogue epi;
+  if ((st = check_epilogue(epilogue, bias, residual, QG_BF16, E, T, N, &epi)) != QG_OK) return st;
   if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   if (N * K * 2 > 0xFFFFFFFFLL) return QG_ERR_UNSUPPORTED;   // 32-bit buffer offsets within an expert
   if (num_active == 0 || T == 0 || N == 0 || E == 0) return QG_OK;
@@ -194,16 +212,33 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
   qg::GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                     static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
                     static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
-                    (int)expert_usage_stats_host[0], device_cus(), transpose_b ? 1 : 0};
+                    (int)expert_usage_stats_host[0], device_cus(), transpose_b ? 1 : 0, epi};
   // both layouts stage the weights through LDS as whole 128-byte row segments:
   // [E, N, K] in 64-deep steps (19), [E, K, N] with transpose reads (12)
   return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", transpose_b ? 19 : 12), stream));
 }
 
-qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
-                          const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
-                          const uint32_t* expert_usage_stats_host, int32_t group_size, int32_t pack_factor,
-                          hipStream_t stream) {
+qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                       const qg_tensor* b, const qg_tensor* expert_ids,
+                       const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                       hipStream_t stream) {
+  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b, 0, nullptr,
+                           nullptr, stream);
+}
+
+qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                const qg_tensor* b, const qg_tensor* expert_ids,
+                                const uint32_t* expert_usage_stats_host, int32_t transpose_b, int32_t epilogue,
+                                const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
+  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b, epilogue, bias,
+                           residual, stream);
+}
+
+static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                      const qg_tensor* b_packed, const qg_tensor* scales,
+                                      const qg_tensor* expert_ids, const uint32_t* expert_usage_stats_host,
+                                      int32_t group_size, int32_t pack_factor, int32_t epilogue,
+                                      const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
   if (!c || !a || !a_offsets || !b_packed || !scales || !expert_ids || !expert_usage_stats_host)
     return QG_ERR_NULL;
   if (c->rank != 2 || a->rank != 2 || a_offsets->rank != 1 || b_packed->rank != 3 || scales->rank != 3 ||
@@ -218,11 +253,14 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
   if ((st = check_tensor(expert_ids, 1, QG_I32)) != QG_OK) return st;
   if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
   if (group_size <= 0) return QG_ERR_INVALID_ARG;
-  const int64_t T = a->shape[0], K = a->shape[1], N = c->shape[1];
+  if (epilogue & ~(QG_EPI_BIAS | QG_EPI_RESIDUAL | QG_EPI_SILU_GATE)) return QG_ERR_INVALID_ARG;
+  const int64_t T = a->shape[0], K = a->shape[1], N = b_packed->shape[2];
   const int64_t E = b_packed->shape[0], G = expert_ids->shape[0];
-  if (c->shape[0] != T) return QG_ERR_SHAPE;
+  const bool gate = (epilogue & QG_EPI_SILU_GATE) != 0;
+  if (gate && N % 16 != 0) return QG_ERR_ALIGN;   // (gate, up) pairs, and an 8-aligned output
+  if (c->shape[0] != T || c->shape[1] != (gate ? N / 2 : N)) return QG_ERR_SHAPE;
   if (K % group_size != 0) return QG_ERR_SHAPE;
-  if (b_packed->shape[1] * pack_factor != K || b_packed->shape[2] != N) return QG_ERR_SHAPE;
+  if (b_packed->shape[1] * pack_factor != K) return QG_ERR_SHAPE;
   if (scales->shape[0] != E || scales->shape[1] != K / group_size || scales->shape[2] != N) return QG_ERR_SHAPE;
   if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
   if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
@@ -230,14 +268,33 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
   if (N % 8 != 0) return QG_ERR_ALIGN;
   const uint32_t num_active = expert_usage_stats_host[1];
   if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
+  qg::Epilogue epi;
+  if ((st = check_epilogue(epilogue, bias, residual, QG_F16, E, T, N, &epi)) != QG_OK) return st;
   if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || E > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   if (T == 0 || N == 0 || num_active == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of the routed rows
   qg::W4GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                       static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
                       static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
-                      T, N, K, E, group_size, (int)num_active};
+                      T, N, K, E, group_size, (int)num_active, epi};
   return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 8), stream));
+}
+
+qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                          const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
+                          const uint32_t* expert_usage_stats_host, int32_t group_size, int32_t pack_factor,
+                          hipStream_t stream) {
+  return grouped_gemm_w4_impl(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats_host, group_size,
+                              pack_factor, 0, nullptr, nullptr, stream);
+}
+
+qg_status grouped_gemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                   const qg_tensor* b_packed, const qg_tensor* scales,
+                                   const qg_tensor* expert_ids, const uint32_t* expert_usage_stats_host,
+                                   int32_t group_size, int32_t pack_factor, int32_t epilogue,
+                                   const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
+  return grouped_gemm_w4_impl(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats_host, group_size,
+                              pack_factor, epilogue, bias, residual, stream);
 }
 
 // planes: 1 (keys only) or 2 (weight columns = [W_k | W_v])

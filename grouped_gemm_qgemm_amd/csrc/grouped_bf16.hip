@@ -63,13 +63,68 @@ struct WRing {
   static constexpr int SLOT = 32 * ROW;
 };
 
+// Stores a wave's 16-column slice of a tile (lane: column n0 + 16 wave + r16,
+// rows 16 mt + 4q + i of the group's chunk), plain or through the fixed
+// epilogue: bias row of expert e, SiLU gate of column pairs (the odd column's
+// value comes from the neighbouring lane, and the even lane stores
+// silu(gate) * up at column col / 2 of the N / 2 wide output), residual.
+// Residual values are loaded before the first store (the compiler cannot rule
+// out that C aliases them).
+// EPI false: the plain store only (the kernels without an epilogue are their
+// own instantiations, so the epilogue code costs them nothing).
+template <int MT, bool EPI>
+__device__ __forceinline__ void grouped_store(uint16_t* __restrict__ C, const float4_t (&acc)[MT], int N, int e,
+                                              int r_begin, int rows, int col, int q, const Epilogue& ep) {
+  if (!EPI || ep.flags == 0) {
+    if (col < N) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = mt * 16 + q * 4 + i;
+          if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
+        }
+      }
+    }
+    return;
+  }
+  const bool gate = (ep.flags & EPI_SILU_GATE) != 0;
+  const int NO = gate ? N / 2 : N;
+  const int oc = gate ? col / 2 : col;
+  const bool owner = col < N && (!gate || (col & 1) == 0);   // lanes that store
+  const float b = (ep.flags & EPI_BIAS) && col < N ? bf2f(ep.bias[(size_t)e * N + col]) : 0.f;
+  float res[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mt * 16 + q * 4 + i;
+      res[mt][i] = (ep.flags & EPI_RESIDUAL) && owner && r < rows ? bf2f(ep.residual[(size_t)(r_begin + r) * NO + oc])
+                                                                 : 0.f;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mt * 16 + q * 4 + i;
+      float y = acc[mt][i] + b;
+      if (gate) {
+        const float up = __shfl_xor(y, 1);   // every lane takes part
+        y = silu(y) * up;
+      }
+      if (owner && r < rows) C[(size_t)(r_begin + r) * NO + oc] = f2bf_rn(y + res[mt][i]);
+    }
+  }
+}
+
 // P > 1: the loads of P consecutive steps are issued together (a weight row's
 // P * 64 contiguous bytes requested back to back).
-template <int W, int MT, int D, bool TB, int P>
+template <int W, int MT, int D, bool TB, int P, bool EPI>
 __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                              u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
-                                             int rows, int n0) {
+                                             int rows, int n0, const Epilogue& ep) {
   constexpr int FPW = (MT + W - 1) / W;   // activation fragments per wave per step
   static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   const int lane = threadIdx.x & 63;
@@ -177,17 +232,7 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   }
 
   // ---- epilogue: bf16 RNE ----
-  const int col = n0 + wave * 16 + r16;
-  if (col < N) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + q * 4 + i;
-        if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
-      }
-    }
-  }
+  grouped_store<MT, EPI>(C, acc, N, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
 }
 
 // Transposed weights ([E, N, K]) staged through LDS in 64-deep steps. A 16-byte
@@ -198,11 +243,11 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
 // slot (16-byte chunks XOR-swizzled by row) and every wave reads its fragments
 // back with 16-byte LDS reads. A step is two 32-deep MFMA sub-steps; the
 // activation ring holds both. D steps are in flight.
-template <int W, int MT, int D>
+template <int W, int MT, int D, bool EPI>
 __device__ __forceinline__ void grouped_tile_wl(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                                 u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
-                                                int rows, int n0) {
+                                                int rows, int n0, const Epilogue& ep) {
   constexpr int FPW = (MT + W - 1) / W;
   static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   constexpr int WSLOT = 16 * W * 8;   // 16-byte chunks of one weight step
@@ -299,25 +344,15 @@ __device__ __forceinline__ void grouped_tile_wl(uint16_t* __restrict__ C, const 
     step(ns & 1, ra[0], rb[0]);
   }
 
-  const int col = n0 + wave * 16 + r16;
-  if (col < N) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + q * 4 + i;
-        if (r < rows) C[(size_t)(r_begin + r) * N + col] = f2bf_rn(acc[mt][i]);
-      }
-    }
-  }
+  grouped_store<MT, EPI>(C, acc, N, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
 }
 
 // Persistent workgroups over the same tile list, weights through LDS (above).
-template <int W, int D, int OCC>
+template <int W, int D, int OCC, bool EPI>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n, int per_xcd) {
+    int tiles_n, int per_xcd, Epilogue ep) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * 2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * 16 * W * 8];
   constexpr int GBN = 16 * W;
@@ -336,14 +371,14 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     // (four waves): half as many steps in flight
     constexpr int D5 = W >= 8 ? D : (D + 1) / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile_wl<W, 1, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 2: grouped_tile_wl<W, 2, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 3: grouped_tile_wl<W, 3, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 4: grouped_tile_wl<W, 4, D>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 5: grouped_tile_wl<W, 5, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 6: grouped_tile_wl<W, 6, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 7: grouped_tile_wl<W, 7, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      default: grouped_tile_wl<W, 8, D5>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 1: grouped_tile_wl<W, 1, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 2: grouped_tile_wl<W, 2, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 3: grouped_tile_wl<W, 3, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 4: grouped_tile_wl<W, 4, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 5: grouped_tile_wl<W, 5, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 6: grouped_tile_wl<W, 6, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 7: grouped_tile_wl<W, 7, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      default: grouped_tile_wl<W, 8, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
     }
   }
 }
@@ -353,20 +388,25 @@ static hipError_t launch_wl(const GroupedArgs& p, hipStream_t stream) {
   if (!p.transpose_b) return hipErrorInvalidValue;
   const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
   const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
-  hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                     p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
-                     grid / 8);
+  if (p.epi.flags)
+    hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                       p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                       p.epi);
+  else
+    hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                       p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                       p.epi);
   return hipGetLastError();
 }
 
 template <int D, int P>
 constexpr int fit_group() { return D % P == 0 ? P : (D % 2 == 0 ? 2 : 1); }
 
-template <int W, int D, int OCC, bool TB, int P>
+template <int W, int D, int OCC, bool TB, int P, bool EPI>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n, int per_xcd) {
+    int tiles_n, int per_xcd, Epilogue ep) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[TB ? 1 : 2 * WRing<W>::SLOT];
 
@@ -390,14 +430,14 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     // same registers and about the same bytes in flight.
     constexpr int D5 = W >= 8 ? D : D / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile<W, 1, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 2: grouped_tile<W, 2, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 3: grouped_tile<W, 3, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 4: grouped_tile<W, 4, D, TB, fit_group<D, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 5: grouped_tile<W, 5, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 6: grouped_tile<W, 6, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      case 7: grouped_tile<W, 7, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
-      default: grouped_tile<W, 8, D5, TB, fit_group<D5, P>()>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0); break;
+      case 1: grouped_tile<W, 1, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 2: grouped_tile<W, 2, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 3: grouped_tile<W, 3, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 4: grouped_tile<W, 4, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 5: grouped_tile<W, 5, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 6: grouped_tile<W, 6, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 7: grouped_tile<W, 7, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      default: grouped_tile<W, 8, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
     }
   }
 }
@@ -407,14 +447,16 @@ static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
   const int wg_per_cu = OCC;
   const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
   const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
-  if (p.transpose_b)
-    hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, true, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
-                     grid / 8);
-  else
-    hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, false, P>), dim3(grid), dim3(W * kWave), 0, stream, p.C, p.A,
-                       p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n,
-                     grid / 8);
+#define QG_GROUPED_LAUNCH(TBV, EPIV)                                                                      \
+  hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, TBV, P, EPIV>), dim3(grid), dim3(W * kWave), 0, stream, p.C, \
+                     p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,   \
+                     p.epi)
+  if (p.transpose_b) {
+    if (p.epi.flags) QG_GROUPED_LAUNCH(true, true); else QG_GROUPED_LAUNCH(true, false);
+  } else {
+    if (p.epi.flags) QG_GROUPED_LAUNCH(false, true); else QG_GROUPED_LAUNCH(false, false);
+  }
+#undef QG_GROUPED_LAUNCH
   return hipGetLastError();
 }
 

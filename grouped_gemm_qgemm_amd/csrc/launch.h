@@ -7,13 +7,14 @@
 
 namespace qg {
 
-// Fixed epilogue of the W4 GEMM, applied in fp32 before the output rounding.
-// EPI_BIAS: y += bias[n]; EPI_SILU_GATE: columns come in (gate, up) pairs and
+// Fixed epilogue of the GEMMs, applied in fp32 before the output rounding.
+// EPI_BIAS: y += bias[n] (the grouped GEMMs: the row of the group's expert,
+// bias [E, N]); EPI_SILU_GATE: columns come in (gate, up) pairs and
 // z[m][j] = silu(y[m][2j]) * y[m][2j+1] (output N / 2 wide); EPI_RESIDUAL:
 // z += residual[m][j] (residual shaped like the output). Bias and residual have
 // the output type.
 enum { EPI_BIAS = 1, EPI_RESIDUAL = 2, EPI_SILU_GATE = 4 };
-struct W4Epilogue {
+struct Epilogue {
   const uint16_t* bias = nullptr;      // [N]
   const uint16_t* residual = nullptr;  // [M, N_out]
   int flags = 0;
@@ -27,7 +28,7 @@ struct W4Args {
   int64_t M, N, K;
   int group_size;
   int bf16;             // A, S and C are bf16
-  W4Epilogue epi;       // C is [M, N / 2] with EPI_SILU_GATE
+  Epilogue epi;       // C is [M, N / 2] with EPI_SILU_GATE
 };
 
 struct W4GroupedArgs {
@@ -40,6 +41,7 @@ struct W4GroupedArgs {
   int64_t T, N, K, E;
   int group_size;
   int num_active;
+  Epilogue epi;               // C is [T, N / 2] with EPI_SILU_GATE; bias [E, N]
 };
 
 struct GroupedArgs {
@@ -53,6 +55,7 @@ struct GroupedArgs {
   int max_rows_hint;
   int num_cus;
   int transpose_b;
+  Epilogue epi;             // C is [T, N / 2] with EPI_SILU_GATE; bias [E, N]
 };
 
 struct KProjArgs {

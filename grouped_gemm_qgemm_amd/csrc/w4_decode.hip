@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
 template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF, bool EPI>
 __device__ __forceinline__ void w4_decode_lds_body(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, const W4Epilogue& ep) {
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, const Epilogue& ep) {
   constexpr int SN = 16 * CPL;
   constexpr int STEPS = SPG > BSTEPS ? SPG : BSTEPS;   // K steps per batch
   constexpr int GB = STEPS / SPG;              // groups per batch
@@ -337,13 +337,13 @@ template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
 __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
-  w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, false>(C, A, B, S, M, N, K, xcd_remap, W4Epilogue{});
+  w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, false>(C, A, B, S, M, N, K, xcd_remap, Epilogue{});
 }
 
 template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
 __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_epi_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, W4Epilogue ep) {
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, Epilogue ep) {
   w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, true>(C, A, B, S, M, N, K, xcd_remap, ep);
 }
 

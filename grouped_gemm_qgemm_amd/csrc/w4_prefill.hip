@@ -614,7 +614,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = fa
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
-                                             W4TileLds<BM, BN, KG>& lds, const W4Epilogue& ep) {
+                                             W4TileLds<BM, BN, KG>& lds, const Epilogue& ep) {
   constexpr int NTHR = WAVES_M * WAVES_N * kWave;   // threads of one K group
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
@@ -923,7 +923,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bo
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
-    W4Epilogue ep) {
+    Epilogue ep) {
   __shared__ W4TileLds<BM, BN, KG> lds;
   const int tiles = tiles_m * tiles_n;
   const int per = (tiles + 7) >> 3;
@@ -958,7 +958,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
-    int group_size, int num_active, int tiles_n, int per_xcd) {
+    int group_size, int num_active, int tiles_n, int per_xcd, Epilogue ep) {
   __shared__ W4TileLds<BM, BN, KG> lds;
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   const TileLoc loc = locate_tile(t, a_off, ids, num_active, BM, tiles_n);
@@ -968,8 +968,15 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   const int r_begin = (int)a_off[loc.g] + chunk * BM;
   const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
   const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false>(C + (size_t)r_begin * N, A + (size_t)r_begin * K, B + e * wpe,
-                                               S + e * spe, rows, N, K, group_size, 0, nt * BN, lds, W4Epilogue{});
+  // the fixed epilogue sees the group's rows as a matrix of their own: C and the
+  // residual from row r_begin (N / 2 wide with the gate), the expert's bias row
+  const int NO = (ep.flags & EPI_SILU_GATE) ? N / 2 : N;
+  Epilogue ept = ep;
+  if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
+  if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K,
+                                                        B + e * wpe, S + e * spe, rows, N, K, group_size, 0,
+                                                        nt * BN, lds, ept);
 }
 
 template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1>
@@ -982,7 +989,7 @@ static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream
   const int grid = (int)((bound + 7) / 8 * 8);
   hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
                      stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
-                     p.num_active, tiles_n, grid / 8);
+                     p.num_active, tiles_n, grid / 8, p.epi);
   return hipGetLastError();
 }
 

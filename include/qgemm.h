@@ -161,6 +161,27 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
                        hipStream_t stream);
 
 /*
+ * grouped_gemm_epilogue - grouped_gemm with a fixed epilogue
+ *
+ * Stands in for the grouped page's elementwise_lambda_fn parameter (a device
+ * function on the stored C fragments): the steps of qgemm_w4_epilogue applied to
+ * each processed row's fp32 product before its rounding, with
+ *
+ *   bias      bf16 [E, N]      QG_EPI_BIAS: the row of the group's expert is added
+ *   residual  bf16 [T, N_out]  QG_EPI_RESIDUAL: added last (row of the token)
+ *   c         bf16 [T, N_out]  N_out = N / 2 with QG_EPI_SILU_GATE (N % 16 == 0,
+ *                              else QG_ERR_ALIGN), N otherwise
+ *
+ * Rows of skipped or unprocessed groups keep their prior content. Everything else
+ * as grouped_gemm; epilogue 0 is grouped_gemm.
+ */
+qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                const qg_tensor* b, const qg_tensor* expert_ids,
+                                const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                                int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
+                                hipStream_t stream);
+
+/*
  * grouped_gemm_w4 - per-group W4A16 GEMM over routed rows (MoE with 4-bit experts)
  *
  * The routing of "grouped_matmul_sm100_persistent" (Args: a_offsets, expert_ids
@@ -191,6 +212,17 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
                           const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
                           const uint32_t* expert_usage_stats_host, int32_t group_size,
                           int32_t pack_factor, hipStream_t stream);
+
+/*
+ * grouped_gemm_w4_epilogue - grouped_gemm_w4 with the fixed epilogue of
+ * grouped_gemm_epilogue (bias f16 [E, N], residual f16 [T, N_out], c f16
+ * [T, N_out]). Everything else as grouped_gemm_w4; epilogue 0 is grouped_gemm_w4.
+ */
+qg_status grouped_gemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
+                                   const qg_tensor* b_packed, const qg_tensor* scales,
+                                   const qg_tensor* expert_ids, const uint32_t* expert_usage_stats_host,
+                                   int32_t group_size, int32_t pack_factor, int32_t epilogue,
+                                   const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream);
 
 /*
  * A paged KV cache collection (keys and values of every layer).

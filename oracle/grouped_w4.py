@@ -13,18 +13,20 @@ reading:
   * group g < expert_usage_stats[1] with expert_ids[g] = e >= 0 sets
     C[a_offsets[g] .. a_offsets[g+1]-1] = round_fp16(A[those rows] . W_e);
   * rows of skipped or unprocessed groups keep whatever C held.
+  * the optional epilogue is the W4 GEMM's fixed steps with one bias row per
+    expert (bias [E, N] fp16) and the residual shaped like C ([T, N_out]).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .numerics import decode_f16, f16_bits_of, round_to_f16
-from .w4 import dequant_w4
+from .w4 import dequant_w4, fixed_epilogue, EPI_BIAS, EPI_RESIDUAL
 
 
 def grouped_gemm_w4(c_bits, a_bits, a_offsets, b_packed, scales_bits, expert_ids, usage_stats,
-                    group_size: int) -> np.ndarray:
-    """Returns the new C (fp16 bit patterns [T, N]); the input array is not modified."""
+                    group_size: int, epilogue: int = 0, bias_bits=None, residual_bits=None) -> np.ndarray:
+    """Returns the new C (fp16 bit patterns [T, N_out]); the input array is not modified."""
     out = np.array(c_bits, dtype=np.uint16, copy=True)
     a_off = np.asarray(a_offsets, dtype=np.int64)
     ids = np.asarray(expert_ids, dtype=np.int64)
@@ -45,7 +47,12 @@ def grouped_gemm_w4(c_bits, a_bits, a_offsets, b_packed, scales_bits, expert_ids
             continue
         if e not in weights:
             weights[e] = dequant_w4(b[e], s[e], group_size)
-        r = round_to_f16(decode_f16(a_bits[r0:r1]) @ weights[e])
+        prod = decode_f16(a_bits[r0:r1]) @ weights[e]
+        if epilogue:
+            prod = fixed_epilogue(prod, epilogue,
+                                  decode_f16(np.asarray(bias_bits)[e]) if epilogue & EPI_BIAS else None,
+                                  decode_f16(np.asarray(residual_bits)[r0:r1]) if epilogue & EPI_RESIDUAL else None)
+        r = round_to_f16(prod)
         assert np.all(np.isfinite(r)), "fp16 overflow in the reference result"
         out[r0:r1] = f16_bits_of(r)
     return out

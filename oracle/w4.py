@@ -90,6 +90,18 @@ def silu(x):
     return x / (1.0 + np.exp(-x))
 
 
+def fixed_epilogue(y, epilogue: int, bias=None, residual=None) -> np.ndarray:
+    """The fixed steps on exact products y [M, N] (float64): y += bias [N]
+    (EPI_BIAS); z = silu(y[:, 0::2]) * y[:, 1::2] (EPI_SILU_GATE, else z = y);
+    z += residual [M, N_out] (EPI_RESIDUAL)."""
+    if epilogue & EPI_BIAS:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    z = silu(y[:, 0::2]) * y[:, 1::2] if epilogue & EPI_SILU_GATE else y
+    if epilogue & EPI_RESIDUAL:
+        z = z + np.asarray(residual, dtype=np.float64)
+    return z
+
+
 def qgemm_w4_epilogue(a_bits, b_packed, scales_bits, group_size: int, epilogue: int, bias_bits=None,
                       residual_bits=None, pack_factor: int = 8, dtype: str = "f16") -> np.ndarray:
     """Y = A . dequant(B) in fp64; Y += bias (EPI_BIAS); Z = silu(Y[:, 0::2]) * Y[:, 1::2]
@@ -97,11 +109,8 @@ def qgemm_w4_epilogue(a_bits, b_packed, scales_bits, group_size: int, epilogue: 
     dec = _DECODE[dtype]
     rnd, bits_of = _ROUND[dtype]
     y = qgemm_w4_f64(a_bits, b_packed, scales_bits, group_size, pack_factor, dtype)
-    if epilogue & EPI_BIAS:
-        y = y + dec(bias_bits)[None, :]
-    z = silu(y[:, 0::2]) * y[:, 1::2] if epilogue & EPI_SILU_GATE else y
-    if epilogue & EPI_RESIDUAL:
-        z = z + dec(residual_bits)
+    z = fixed_epilogue(y, epilogue, dec(bias_bits) if epilogue & EPI_BIAS else None,
+                       dec(residual_bits) if epilogue & EPI_RESIDUAL else None)
     c = rnd(z)
     assert np.all(np.isfinite(c)), "overflow in the reference result"
     return bits_of(c)

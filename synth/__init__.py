@@ -111,6 +111,16 @@ def w4_epilogue_operands(seed: int, M: int, N_out: int, N: int, dtype: str = "f1
     return bias, residual
 
 
+def grouped_epilogue_operands(seed: int, E: int, T: int, N_out: int, N: int, dtype: str = "bf16",
+                              std: float = 1.0):
+    """Per-expert bias [E, N] and residual [T, N_out] for the grouped GEMMs' fixed
+    epilogues (draw order: bias, residual), normal with standard deviation `std`."""
+    rng = np.random.default_rng(seed)
+    bias = _bits(rng.normal(0.0, std, size=(E, N)), dtype)
+    residual = _bits(rng.normal(0.0, std, size=(T, N_out)), dtype)
+    return bias, residual
+
+
 # Named W4 workloads: (M, N, K, weight seed, activation seed)
 W4_TINY = dict(M=16, N=256, K=512, seed=1, a_seed=101)
 W4_DECODE = [dict(M=m, N=4096, K=4096, seed=2, a_seed=200 + m) for m in (1, 4, 16)]

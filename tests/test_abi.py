@@ -30,8 +30,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale",
-            "kv_matmul_ragged_paged_scale", "qg_status_string"} <= set(names)
+    assert {"qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "grouped_gemm_epilogue",
+            "grouped_gemm_w4_epilogue", "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale",
+            "qg_status_string"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     for n in names:
@@ -206,6 +207,46 @@ def test_grouped_w4_rejections(lib):
     u = (ctypes.c_uint32 * 2)(8, 4)
     assert lib.grouped_gemm_w4(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
                                ctypes.byref(s), ctypes.byref(ids), None, 128, 8, None) == QG.ERR_NULL
+
+
+def test_grouped_epilogue_rejections(lib):
+    bb = Buf()
+    T, K, N, E, G = 32, 64, 48, 4, 4
+    a, off, ids = bb.t((T, K), QG.BF16), bb.t((G + 1,), QG.U32), bb.t((G,), QG.I32)
+    b = bb.t((E, N, K), QG.BF16)
+    u = (ctypes.c_uint32 * 2)(8, 4)
+    r = lambda t: ctypes.byref(t) if t is not None else None
+
+    def ge(c, flags, bias=None, res=None, bm=b):
+        return lib.grouped_gemm_epilogue(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(bm),
+                                         ctypes.byref(ids), u, 1, flags, r(bias), r(res), None)
+    c, half = bb.t((T, N), QG.BF16), bb.t((T, N // 2), QG.BF16)
+    assert ge(c, 8) == QG.ERR_INVALID_ARG
+    assert ge(c, q.EPI_BIAS) == QG.ERR_NULL
+    assert ge(c, q.EPI_BIAS, bias=bb.t((N,), QG.BF16)) == QG.ERR_RANK          # one row per expert
+    assert ge(c, q.EPI_BIAS, bias=bb.t((E - 1, N), QG.BF16)) == QG.ERR_SHAPE
+    assert ge(c, q.EPI_BIAS, bias=bb.t((E, N), QG.F16)) == QG.ERR_DTYPE
+    assert ge(c, q.EPI_RESIDUAL, res=bb.t((T, N // 2), QG.BF16)) == QG.ERR_SHAPE
+    assert ge(c, q.EPI_SILU_GATE) == QG.ERR_SHAPE                              # output is N / 2 wide
+    b40 = bb.t((E, 40, K), QG.BF16)                                           # 40 % 16 != 0
+    assert ge(bb.t((T, 20), QG.BF16), q.EPI_SILU_GATE, bm=b40) == QG.ERR_ALIGN
+    u[1] = 0
+    assert ge(half, 7, bias=bb.t((E, N), QG.BF16), res=bb.t((T, N // 2), QG.BF16)) == QG.OK   # nothing active
+    # W4 experts: f16 operands
+    c4, a4 = bb.t((T, 24), QG.F16), bb.t((T, 256), QG.F16)
+    b4, s4 = bb.t((E, 32, N), QG.U32), bb.t((E, 2, N), QG.F16)
+    u[1] = 4
+
+    def gw(c, flags, bias=None, res=None):
+        return lib.grouped_gemm_w4_epilogue(ctypes.byref(c), ctypes.byref(a4), ctypes.byref(off), ctypes.byref(b4),
+                                            ctypes.byref(s4), ctypes.byref(ids), u, 128, 8, flags, r(bias), r(res),
+                                            None)
+    assert gw(c4, q.EPI_SILU_GATE | q.EPI_BIAS) == QG.ERR_NULL
+    assert gw(c4, q.EPI_SILU_GATE | q.EPI_BIAS, bias=bb.t((E, N), QG.BF16)) == QG.ERR_DTYPE
+    assert gw(bb.t((T, N), QG.F16), q.EPI_SILU_GATE) == QG.ERR_SHAPE
+    assert gw(c4, -1) == QG.ERR_INVALID_ARG
+    u[1] = 0
+    assert gw(c4, 7, bias=bb.t((E, N), QG.F16), res=bb.t((T, 24), QG.F16)) == QG.OK
 
 
 def kp_call(lib, h, offs, w, isc, wsc, blocks, layer, gran=(1, 128, 128), cl=1, pt=1, maxp=2, scales=None,

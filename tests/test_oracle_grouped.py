@@ -107,3 +107,60 @@ def test_brute_force_loops_and_both_b_layouts():
     bt = np.ascontiguousarray(d.b.transpose(0, 2, 1))
     c2 = oracle.grouped_gemm(c0, d.a, a_off, bt, ids, usage, transpose_b=False)
     assert np.array_equal(c2, c)
+
+
+# ---------------------------------------------------------------- fixed epilogues
+
+def _sig(x):
+    import math
+    return 0.5 * (1.0 + math.tanh(0.5 * x))
+
+
+def test_epilogue_brute_force_loops():
+    """Bias row of the group's expert, SiLU-gated column pairs, residual, one rounding."""
+    E, G, T, K, N = 4, 5, 30, 32, 32
+    rng = np.random.default_rng(6)
+    d = synth.grouped_inputs(seed=6, E=E, T=T, K=K, N=N, skip_frac=0.0)
+    cuts = np.sort(rng.integers(0, T + 1, G - 1))
+    a_off = np.concatenate([[0], cuts, [T]]).astype(np.uint32)
+    ids = np.array([3, -1, 0, 3, 1], np.int32)
+    usage = np.array([T, G], np.uint32)
+    a, b = nm.decode_bf16(d.a), nm.decode_bf16(d.b)
+    for flags in range(8):
+        n_out = N // 2 if flags & oracle.EPI_SILU_GATE else N
+        bias, res = synth.grouped_epilogue_operands(flags, E, T, n_out, N, std=0.02)
+        c0 = np.full((T, n_out), SENT, np.uint16)
+        c = oracle.grouped_gemm(c0, d.a, a_off, d.b, ids, usage, epilogue=flags, bias_bits=bias, residual_bits=res)
+        bf, rf = nm.decode_bf16(bias), nm.decode_bf16(res)
+        for g in range(G):
+            for r in range(a_off[g], a_off[g + 1]):
+                if ids[g] < 0:
+                    assert np.all(c[r] == SENT)
+                    continue
+                y = [sum(a[r, k] * b[ids[g], n, k] for k in range(K)) for n in range(N)]
+                if flags & oracle.EPI_BIAS:
+                    y = [y[n] + bf[ids[g], n] for n in range(N)]
+                z = [y[2 * j] * _sig(y[2 * j]) * y[2 * j + 1] for j in range(N // 2)] \
+                    if flags & oracle.EPI_SILU_GATE else y
+                if flags & oracle.EPI_RESIDUAL:
+                    z = [z[j] + rf[r, j] for j in range(n_out)]
+                got = nm.decode_bf16(c[r])
+                exact = np.array(z)
+                ulp = np.abs(nm.round_to_bf16(exact * (1 + 2.0 ** -7)) - nm.round_to_bf16(exact)) + 1e-40
+                assert np.all(np.abs(got - exact) <= ulp), (flags, g, r)
+
+
+def test_epilogue_bias_row_is_the_groups_expert():
+    """A = 0: every written row is its group's expert's bias row, exactly."""
+    E, T, K, N = 4, 12, 32, 16
+    d = synth.grouped_inputs(seed=7, E=E, T=T, K=K, N=N, skip_frac=0.0)
+    a = np.zeros_like(d.a)
+    a_off = np.array([0, 3, 5, 9, 12], np.uint32)
+    ids = np.array([2, -1, 0, 2], np.int32)
+    bias, _ = synth.grouped_epilogue_operands(1, E, T, N, N)
+    c0 = np.full((T, N), SENT, np.uint16)
+    c = oracle.grouped_gemm(c0, a, a_off, d.b, ids, np.array([4, 4], np.uint32), epilogue=oracle.EPI_BIAS,
+                            bias_bits=bias)
+    for g, e in enumerate(ids):
+        rows = slice(a_off[g], a_off[g + 1])
+        assert np.all(c[rows] == (SENT if e < 0 else bias[e])), g

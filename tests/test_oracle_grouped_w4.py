@@ -103,3 +103,27 @@ def test_each_group_uses_its_expert():
             else:
                 want = 2.0 ** (r % 4) * c_e[ids[g]] / 16
                 assert np.all(nm.decode_f16(got[r]) == want), (g, r)
+
+
+def test_epilogue_each_group_uses_its_experts_bias_and_gate():
+    """Zero activations: y = bias[e]; the gated output is silu(bias[e][2j]) * bias[e][2j+1]
+    plus the residual, rounded once; skipped rows keep C."""
+    import math
+    a, off, b, s, ids, gs = _tiny(9)
+    a[:] = 0
+    T, N, E = a.shape[0], b.shape[2], b.shape[0]
+    flags = oracle.EPI_BIAS | oracle.EPI_SILU_GATE | oracle.EPI_RESIDUAL
+    bias, res = synth.grouped_epilogue_operands(2, E, T, N // 2, N, dtype="f16")
+    c0 = np.full((T, N // 2), SENT, np.uint16)
+    c = oracle.grouped_gemm_w4(c0, a, off, b, s, ids, np.array([T, len(ids)], np.uint32), gs, epilogue=flags,
+                               bias_bits=bias, residual_bits=res)
+    bf, rf = nm.decode_f16(bias), nm.decode_f16(res)
+    for g, e in enumerate(ids):
+        for r in range(off[g], off[g + 1]):
+            if e < 0:
+                assert np.all(c[r] == SENT)
+                continue
+            # silu(g) = g * sigmoid(g), sigmoid(g) = (1 + tanh(g / 2)) / 2
+            x = [bf[e, 2 * j] * 0.5 * (1 + math.tanh(0.5 * bf[e, 2 * j])) * bf[e, 2 * j + 1] + rf[r, j]
+                 for j in range(N // 2)]
+            assert np.array_equal(c[r], nm.f16_bits_of(nm.round_to_f16(np.array(x)))), (g, r)
