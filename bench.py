@@ -62,13 +62,20 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9019628, "f5be18eb391916bd"),
-    "prefill": (271155781, "7e88e26862b0c500"),
-    "square": (101378817, "7e88e26862b0c500"),
-    "grouped": (367992844, "846169e22572cd19"),
-    "grouped_kn": (365854045, "846169e22572cd19"),
-    "grouped_w4": (117818797, "7e88e26862b0c500"),
-    "kproj": (85578290, "7e7880aa3aaf52ae"),
+    "decode": (9023723, "c5047a03e5d045de"),
+    "prefill": (269374050, "426062eecd50ed1e"),
+    "square": (101398272, "426062eecd50ed1e"),
+    "grouped": (367980987, "71e5ce2e08f4edd1"),
+    "grouped_kn": (365849708, "71e5ce2e08f4edd1"),
+    "grouped_w4": (117997597, "426062eecd50ed1e"),
+    "kproj": (85586482, "57c92363b76839f7"),
+    "decode_gate": (9037033, "c5047a03e5d045de"),
+    "prefill_gate": (269572374, "426062eecd50ed1e"),
+    "decode_bf16": (9019628, "c5047a03e5d045de"),
+    "prefill_bf16": (270145182, "426062eecd50ed1e"),
+    "kvproj": (202279226, "57c92363b76839f7"),
+    "kvproj_e4m3": (193902382, "57c92363b76839f7"),
+    "kproj_e4m3h": (64355704, "57c92363b76839f7"),
 }
 
 
