@@ -52,6 +52,8 @@ KERNEL_SOURCES = {
     "prefill_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "prefill_gate": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "decode_gate": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
+    "decode_nk": ["capi.cpp", "device_common.h", "launch.h", "w4_decode.hip"],
+    "prefill_nk": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
@@ -101,7 +103,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="decode", choices=["decode", "prefill", "square", "decode_bf16", "prefill_bf16",
-                                                           "decode_gate", "prefill_gate", "kvproj", "kvproj_e4m3",
+                                                           "decode_gate", "prefill_gate", "decode_nk", "prefill_nk",
+                                                           "kvproj", "kvproj_e4m3",
                                                            "kproj_e4m3h",
                                                            "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -156,6 +159,7 @@ class DecodeW4:
     bound = "hbm"
     dtype = "f16"
     epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
+    nk = False   # weights and scales stored [N, K/8] / [N, K/gs] (qgemm_w4_nk)
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
@@ -168,8 +172,11 @@ class DecodeW4:
         self.R = max(1, math.ceil(ROTATE_BYTES / foot))
         dev = torch.device("cuda")
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
-        b = torch.from_numpy(self.inputs[0].b.view(np.int32)).to(dev)
-        s = torch.from_numpy(self.inputs[0].scales.view(np.int16)).to(dev).view(tdt)
+        bh, sh = self.inputs[0].b, self.inputs[0].scales
+        if self.nk:
+            bh, sh = np.ascontiguousarray(bh.T), np.ascontiguousarray(sh.T)
+        b = torch.from_numpy(bh.view(np.int32)).to(dev)
+        s = torch.from_numpy(sh.view(np.int16)).to(dev).view(tdt)
         n_out = N // 2 if self.epi & 4 else N
         self.epi_ops = [synth.w4_epilogue_operands(7 + i, M, n_out, N, self.dtype) for i, M in enumerate(self.Ms)]
         dev16 = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
@@ -190,7 +197,8 @@ class DecodeW4:
         if self.epi:
             return [lambda c=c, a=a, b=b, s=s, bi=bi, r=r: self.q.qgemm_w4_epilogue(c, a, b, s, self.epi, bi, r, 128)
                     for (c, a, b, s, bi, r) in slot]
-        return [lambda c=c, a=a, b=b, s=s: self.q.qgemm_w4(c, a, b, s, 128) for (c, a, b, s, _, _) in slot]
+        fn = self.q.qgemm_w4_nk if self.nk else self.q.qgemm_w4
+        return [lambda c=c, a=a, b=b, s=s: fn(c, a, b, s, 128) for (c, a, b, s, _, _) in slot]
 
     def unit_bytes(self):
         return self.bytes_per_step / len(self.Ms)
@@ -213,6 +221,8 @@ class DecodeW4:
              "pack_factor": 8, "rotating_copies": self.R}
         if self.epi:
             d["epilogue"] = "bias + silu_gate + residual" if self.epi == 7 else self.epi
+        if self.nk:
+            d["layout"] = "b_packed [N, K/8], scales [N, K/128]"
         return d
 
     def dense_equivalent(self):
@@ -225,6 +235,7 @@ class PrefillW4:
     bound = "mfma"
     dtype = "f16"
     epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
+    nk = False   # weights and scales stored [N, K/8] / [N, K/gs] (qgemm_w4_nk)
 
     def __init__(self, torch, q, synth, square=False):
         self.torch, self.q = torch, q
@@ -240,8 +251,12 @@ class PrefillW4:
         dev = torch.device("cuda")
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
         a = torch.from_numpy(self.w.a.view(np.int16)).to(dev).view(tdt)
-        b = torch.from_numpy(self.w.b.view(np.int32)).to(dev)
-        sc = torch.from_numpy(self.w.scales.view(np.int16)).to(dev).view(tdt)
+        bh, sh = self.w.b, self.w.scales
+        if self.nk:
+            bh, sh = np.ascontiguousarray(bh.T), np.ascontiguousarray(sh.T)
+            self.name += "_nk"
+        b = torch.from_numpy(bh.view(np.int32)).to(dev)
+        sc = torch.from_numpy(sh.view(np.int16)).to(dev).view(tdt)
         n_out = N // 2 if self.epi & 4 else N
         self.bias_bits, self.res_bits = synth.w4_epilogue_operands(7, M, n_out, N, self.dtype)
         dev16 = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(tdt)
@@ -256,6 +271,8 @@ class PrefillW4:
         c, a, b, s, bi, r = self.slots[step % self.R]
         if self.epi:
             return [lambda: self.q.qgemm_w4_epilogue(c, a, b, s, self.epi, bi, r, 128)]
+        if self.nk:
+            return [lambda: self.q.qgemm_w4_nk(c, a, b, s, 128)]
         return [lambda: self.q.qgemm_w4(c, a, b, s, 128)]
 
     def unit_bytes(self):
@@ -280,6 +297,8 @@ class PrefillW4:
              "pack_factor": 8, "rotating_copies": self.R}
         if self.epi:
             d["epilogue"] = "bias + silu_gate + residual" if self.epi == 7 else self.epi
+        if self.nk:
+            d["layout"] = "b_packed [N, K/8], scales [N, K/128]"
         return d
 
     def dense_equivalent(self):
@@ -297,6 +316,18 @@ class DecodeW4Gate(DecodeW4):
     name = "w4a16_decode_N4096_K4096_gs128_M1_4_16_bias_silugate_residual"
     kernel = "w4_decode_lds_epi_kernel"
     epi = 7
+
+
+class DecodeW4NK(DecodeW4):
+    """The decode workload with weights and scales stored [N, K/8] / [N, K/128]."""
+    name = "w4a16_decode_N4096_K4096_gs128_M1_4_16_nk"
+    kernel = "w4_decode_lds_nk_kernel"
+    nk = True
+
+
+class PrefillW4NK(PrefillW4):
+    """The 2048 x 11008 x 4096 prefill with weights and scales stored [N, K/8] / [N, K/128]."""
+    nk = True
 
 
 class DecodeW4BF16(DecodeW4):
@@ -616,6 +647,7 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "square": lambda t, q, sy: PrefillW4(t, q, sy, square=True),
              "decode_bf16": DecodeW4BF16, "prefill_bf16": PrefillW4BF16,
              "decode_gate": DecodeW4Gate, "prefill_gate": PrefillW4Gate,
+             "decode_nk": DecodeW4NK, "prefill_nk": PrefillW4NK,
              "kvproj": KVProjFP8, "kvproj_e4m3": KVProjFP8Cache, "kproj_e4m3h": KProjE4M3Hidden,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 

@@ -8,6 +8,7 @@ built, load() raises: there is no fallback path.
 
 Entry points (same names as the C ABI):
     qgemm_w4(c, a, b_packed, scales, group_size=128, pack_factor=8)
+    qgemm_w4_nk(c, a, b_packed_nk, scales_nk, group_size=128, pack_factor=8)
     qgemm_w4_epilogue(c, a, b_packed, scales, epilogue, bias=None, residual=None,
                       group_size=128, pack_factor=8)
     grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
@@ -28,7 +29,7 @@ import os
 
 import torch
 
-__all__ = ["load", "QgError", "qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4",
+__all__ = ["load", "QgError", "qgemm_w4", "qgemm_w4_nk", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4",
            "grouped_gemm_epilogue", "grouped_gemm_w4_epilogue",
            "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale", "status_string", "LIB_PATH", "QG", "EPI_BIAS", "EPI_RESIDUAL",
            "EPI_SILU_GATE"]
@@ -84,6 +85,8 @@ def load(path: str | None = None):
     T = ctypes.POINTER(QgTensor)
     lib.qgemm_w4.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.qgemm_w4.restype = ctypes.c_int
+    lib.qgemm_w4_nk.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.qgemm_w4_nk.restype = ctypes.c_int
     lib.qgemm_w4_epilogue.argtypes = [T, T, T, T, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, T, T,
                                       ctypes.c_void_p]
     lib.qgemm_w4_epilogue.restype = ctypes.c_int
@@ -160,6 +163,18 @@ def qgemm_w4(c, a, b_packed, scales, group_size: int = 128, pack_factor: int = 8
     st = lib.qgemm_w4(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
                       ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
                       group_size, pack_factor, _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def qgemm_w4_nk(c, a, b_packed, scales, group_size: int = 128, pack_factor: int = 8, stream=None,
+                raise_on_error: bool = True) -> int:
+    """qgemm_w4 with B stored [N, K/8] and the scales [N, K/group_size]."""
+    lib = load()
+    st = lib.qgemm_w4_nk(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
+                         ctypes.byref(describe(b_packed, _u32(b_packed))), ctypes.byref(describe(scales)),
+                         group_size, pack_factor, _stream(stream))
     if raise_on_error:
         _check(st)
     return st

@@ -106,10 +106,11 @@ static qg_status check_epilogue(int32_t epilogue, const qg_tensor* bias, const q
   return QG_OK;
 }
 
+// nk: B is [N, K/8] and the scales [N, K/group_size] (no epilogue)
 static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
                                const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
                                int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool nk = false) {
   if (!c || !a || !b_packed || !scales) return QG_ERR_NULL;
   // rank-2 requirement first: the page's only stated error condition
   if (c->rank != 2 || a->rank != 2 || b_packed->rank != 2 || scales->rank != 2) return QG_ERR_RANK;
@@ -124,14 +125,16 @@ static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_
   if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
   if (group_size <= 0) return QG_ERR_INVALID_ARG;
   if (epilogue & ~(QG_EPI_BIAS | QG_EPI_RESIDUAL | QG_EPI_SILU_GATE)) return QG_ERR_INVALID_ARG;
-  const int64_t M = a->shape[0], K = a->shape[1], N = b_packed->shape[1];
+  const int64_t M = a->shape[0], K = a->shape[1], N = b_packed->shape[nk ? 0 : 1];
   const bool gate = (epilogue & QG_EPI_SILU_GATE) != 0;
   if (gate && N % 16 != 0) return QG_ERR_ALIGN;   // (gate, up) pairs, and an 8-aligned output
   const int64_t N_out = gate ? N / 2 : N;
   if (c->shape[0] != M || c->shape[1] != N_out) return QG_ERR_SHAPE;
   if (K % group_size != 0) return QG_ERR_SHAPE;
-  if (b_packed->shape[0] * pack_factor != K) return QG_ERR_SHAPE;
-  if (scales->shape[0] != K / group_size || scales->shape[1] != N) return QG_ERR_SHAPE;
+  if (b_packed->shape[nk ? 1 : 0] * pack_factor != K) return QG_ERR_SHAPE;
+  if (nk ? (scales->shape[0] != N || scales->shape[1] != K / group_size)
+         : (scales->shape[0] != K / group_size || scales->shape[1] != N))
+    return QG_ERR_SHAPE;
   if (group_size % 32 != 0 || group_size > 256 || (group_size & (group_size - 1)) != 0)
     return QG_ERR_UNSUPPORTED;
   if (N % 8 != 0) return QG_ERR_ALIGN;
@@ -143,7 +146,8 @@ static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_
   qg::W4Args p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
                M, N, K, group_size, act == QG_BF16 ? 1 : 0, epi};
-  const bool wide = p.bf16 || epilogue;   // bf16 and epilogues run in the newer kernels
+  p.nk = nk ? 1 : 0;
+  const bool wide = p.bf16 || epilogue || nk;   // bf16, epilogues and [N, K/8] run in the newer kernels
   if (M <= 16) {
     const int v = env_variant("QG_W4_DECODE_VARIANT", 9);
     if (wide && v < 9) return QG_ERR_UNSUPPORTED;   // the LDS-staged decode kernel
@@ -160,7 +164,14 @@ static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_
   }
   const int v = env_variant("QG_W4_PREFILL_VARIANT", dflt);
   if (wide && v < 11) return QG_ERR_UNSUPPORTED;   // the fourth design
+  if (nk && (v == 12 || v > 17)) return QG_ERR_UNSUPPORTED;   // [N, K/8]: one stage in flight
   return launch_status(qg::launch_w4_prefill(p, v, stream));
+}
+
+qg_status qgemm_w4_nk(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                      const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                      hipStream_t stream) {
+  return qgemm_w4_impl(c, a, b_packed, scales, group_size, pack_factor, 0, nullptr, nullptr, stream, true);
 }
 
 qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,

@@ -29,6 +29,7 @@ struct W4Args {
   int group_size;
   int bf16;             // A, S and C are bf16
   Epilogue epi;       // C is [M, N / 2] with EPI_SILU_GATE
+  int nk = 0;         // B is [N, K/8] and S is [N, K/group_size] (no epilogue)
 };
 
 struct W4GroupedArgs {

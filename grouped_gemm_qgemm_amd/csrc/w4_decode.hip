@@ -142,7 +142,14 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
 //
 // EPI: the fixed epilogue (a kernel of its own, w4_decode_lds_epi_kernel, so the
 // plain kernel's arguments stay as small as before).
-template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF, bool EPI>
+//
+// NK: B stored [N, K/8] and scales [N, K/group_size] (each column's words and
+// scales contiguous). Within a group, lane quarter q then takes the SPG
+// consecutive words q * SPG .. q * SPG + SPG - 1 of its column (one 4 to
+// 32-byte load) instead of every fourth word, and reads the matching
+// activation chunks: the MFMA's K slots are a permutation of the group's K
+// rows, the same for A and B, so each group's sum is unchanged.
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF, bool EPI, bool NK = false>
 __device__ __forceinline__ void w4_decode_lds_body(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, const Epilogue& ep) {
@@ -220,6 +227,27 @@ __device__ __forceinline__ void w4_decode_lds_body(
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
       const int g = g0 + j < g_end ? g0 + j : g_end - 1;
+      if constexpr (NK) {
+        const int groups_per_col = K / (SPG * 32);
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) {
+          sc[j][t] = S[(size_t)(ncol + t) * groups_per_col + g];
+          const uint32_t* bp = B + (size_t)(ncol + t) * (K / 8) + (g * SPG * 4 + quarter * SPG);
+#pragma unroll
+          for (int s4 = 0; s4 < SPG; s4 += 4) {
+            if constexpr (SPG >= 4) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp + s4);
+              w[j][s4][t] = v.x; w[j][s4 + 1][t] = v.y; w[j][s4 + 2][t] = v.z; w[j][s4 + 3][t] = v.w;
+            } else if constexpr (SPG == 2) {
+              const u32x2_t v = *reinterpret_cast<const u32x2_t*>(bp);
+              w[j][0][t] = v.x; w[j][1][t] = v.y;
+            } else {
+              w[j][0][t] = *bp;
+            }
+          }
+        }
+        continue;
+      }
       if constexpr (CPL == 4) {
         const uint2 v = *reinterpret_cast<const uint2*>(S + (size_t)g * N + ncol);
         sc[j][0] = v.x & 0xFFFF; sc[j][1] = v.x >> 16; sc[j][2] = v.y & 0xFFFF; sc[j][3] = v.y >> 16;
@@ -260,7 +288,8 @@ __device__ __forceinline__ void w4_decode_lds_body(
       for (int t = 0; t < CPL; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < SPG; ++s) {
-        const int chunk = (j * SPG + s) * 4 + quarter;
+        // the 8-deep K chunk of this quarter at step s (see NK above)
+        const int chunk = NK ? j * SPG * 4 + quarter * SPG + s : (j * SPG + s) * 4 + quarter;
         const u32x4_t a = a_lds[wave][frag_row * CH + (chunk ^ (frag_row & 15 & (CH - 1)))];
         if constexpr (BF) {
           corr = mfma16x16x32_bf16(a, u32x4_t{m136, m136, m136, m136}, corr);
@@ -341,6 +370,13 @@ __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_kernel(
 }
 
 template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
+__global__ __launch_bounds__(NW * kWave) void w4_decode_lds_nk_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
+  w4_decode_lds_body<CPL, NW, SPG, MROWS, BSTEPS, BF, false, true>(C, A, B, S, M, N, K, xcd_remap, Epilogue{});
+}
+
+template <int CPL, int NW, int SPG, int MROWS, int BSTEPS, bool BF>
 __global__ __launch_bounds__(NW * kWave) void w4_decode_lds_epi_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap, Epilogue ep) {
@@ -358,7 +394,14 @@ static hipError_t launch_lds_cfg(const W4Args& p, hipStream_t stream) {
   const int remap = (strips % 8 == 0) ? strips / 8 : 0;
   const dim3 grid(strips), block(NW * kWave);
   const int M = (int)p.M, N = (int)p.N, K = (int)p.K;
-  if (p.epi.flags) {
+  if (p.nk) {                     // [N, K/8] weights (no epilogue)
+    if (p.bf16)
+      hipLaunchKernelGGL((w4_decode_lds_nk_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), grid, block, 0, stream,
+                         p.C, p.A, p.B, p.S, M, N, K, remap);
+    else
+      hipLaunchKernelGGL((w4_decode_lds_nk_kernel<CPL, NW, SPG, MROWS, BSTEPS, false>), grid, block, 0, stream,
+                         p.C, p.A, p.B, p.S, M, N, K, remap);
+  } else if (p.epi.flags) {
     if (p.bf16)
       hipLaunchKernelGGL((w4_decode_lds_epi_kernel<CPL, NW, SPG, MROWS, BSTEPS, true>), grid, block, 0, stream,
                          p.C, p.A, p.B, p.S, M, N, K, remap, p.epi);

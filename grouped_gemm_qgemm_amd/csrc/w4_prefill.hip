@@ -610,7 +610,11 @@ struct W4TileLds {
 // and columns n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
 // BF: activations, scales and output are bf16 (weights (q - 8) * s rounded to
 // bf16 through fp32, bf16 MFMAs); otherwise fp16.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false>
+// NK: B stored [N, K/8] and scales [N, K/group_size]. The stage's B tile is
+// then read as each column's eight words (two 16-byte loads per column) and
+// written into the same [8][BN] LDS tile word by word, so the MFMA loop is
+// unchanged; the lane's two scales are two 2-byte loads.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
@@ -643,7 +647,9 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   // which is what the packed rows past K of a partial last stage need.
   const int rows = min(BM, M - m0);
   const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)m0 * K, (uint32_t)rows * K * 2);
-  const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + n0, (uint32_t)((size_t)(K / 8) * N - n0) * 4);
+  const __amdgpu_buffer_rsrc_t b_src =
+      NK ? buffer_rsrc(B + (size_t)n0 * (K / 8), (uint32_t)((size_t)(N - n0) * (K / 8) * 4))
+         : buffer_rsrc(B + n0, (uint32_t)((size_t)(K / 8) * N - n0) * 4);
   const __amdgpu_buffer_rsrc_t s_src = buffer_rsrc(S, (uint32_t)((size_t)(K / group_size) * N * 2));
   const int gshift = __builtin_ctz(group_size);
   uint32_t a_voff[A_PER_T];
@@ -661,8 +667,13 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
     const int id = tid + i * NTHR;
-    const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
-    b_voff[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4) - n0) * 4;
+    if constexpr (NK) {   // column id % BN, words 4 (id / BN) .. + 3 of its stage
+      const int half = id / BN, c = id % BN;
+      b_voff[i] = (uint32_t)(min(c, N - n0 - 1) * (K / 8) + 4 * half) * 4;
+    } else {
+      const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
+      b_voff[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4) - n0) * 4;
+    }
   }
   // this lane's two output columns (scale columns)
   const uint32_t s_voff = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2) * 2;
@@ -678,10 +689,19 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) r.a[i] = buffer_load16(a_src, a_voff[i], (uint32_t)k0 * 2);
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) r.b[i] = buffer_load16(b_src, b_voff[i], (uint32_t)(k0 / 8) * N * 4);
+    for (int i = 0; i < B_PER_T; ++i)
+      r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : (uint32_t)(k0 / 8) * N * 4);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)(min(k0 + 32 * s, K - 1) >> gshift) * N * 2);
+    for (int s = 0; s < 2; ++s) {
+      const int g = min(k0 + 32 * s, K - 1) >> gshift;
+      if constexpr (NK) {
+        const int col0 = (int)(s_voff / 2);
+        const uint16_t* sp = S + (size_t)col0 * (K >> gshift) + g;
+        r.sc[s] = (uint32_t)sp[0] | ((uint32_t)sp[K >> gshift] << 16);
+      } else {
+        r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)g * N * 2);
+      }
+    }
     // partial last stage (K % 64 == 32): A chunks past K must enter as zeros
     if (k0 + BK > K && k0 + a_ch0 * 8 >= K) {
 #pragma unroll
@@ -693,7 +713,18 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) lds_b[buf][tid + i * NTHR] = r.b[i];
+    for (int i = 0; i < B_PER_T; ++i) {
+      if constexpr (NK) {
+        const int id = tid + i * NTHR, half = id / BN, c = id % BN;
+        uint32_t* wb = reinterpret_cast<uint32_t*>(lds_b[buf]);
+        wb[(4 * half + 0) * BN + c] = r.b[i].x;
+        wb[(4 * half + 1) * BN + c] = r.b[i].y;
+        wb[(4 * half + 2) * BN + c] = r.b[i].z;
+        wb[(4 * half + 3) * BN + c] = r.b[i].w;
+      } else {
+        lds_b[buf][tid + i * NTHR] = r.b[i];
+      }
+    }
   };
 
   float16_t acc[MT][2];
@@ -919,7 +950,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 // Dense fourth-design kernel: one tile per workgroup, tile order within each
 // XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
 // swept across N.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF, bool NK = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
@@ -944,7 +975,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
     tm = first + r % gm;
     tn = r / gm;
   }
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds, ep);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds,
+                                                         ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -1027,12 +1059,24 @@ static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order 
   if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL || p.K / p.group_size * p.N * 2 > 0xFFFFFFFFLL) return hipErrorNotSupported;
   const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
   const int grid = ((tm * tn + 7) / 8) * 8;
-  if (p.bf16)
-    hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, true>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order, p.epi);
-  else
-    hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, false>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
-                       stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, order, p.epi);
+#define QG_V4_LAUNCH(BFV, NKV)                                                                                  \
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BFV, NKV>), dim3(grid),              \
+                     dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,     \
+                     p.group_size, tm, tn, order, p.epi)
+  if (p.nk) {   // [N, K/8] weights: the default launch shapes only (15, 16)
+    if constexpr (PD == 1 && BM == 128 && BN == 256 && MINB == 2 && KG == 1) {
+      if (p.bf16) QG_V4_LAUNCH(true, true); else QG_V4_LAUNCH(false, true);
+    } else if constexpr (PD == 1 && BM == 128 && BN == 256 && MINB == 1 && KG == 2) {
+      if (p.bf16) QG_V4_LAUNCH(true, true); else QG_V4_LAUNCH(false, true);
+    } else {
+      return hipErrorNotSupported;
+    }
+  } else if (p.bf16) {
+    QG_V4_LAUNCH(true, false);
+  } else {
+    QG_V4_LAUNCH(false, false);
+  }
+#undef QG_V4_LAUNCH
   return hipGetLastError();
 }
 

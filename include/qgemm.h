@@ -104,6 +104,26 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
                    hipStream_t stream);
 
 /*
+ * qgemm_w4_nk - qgemm_w4 with the weights stored the other way round
+ *
+ * The page's configuration type carries a transpose_b flag (its signature's
+ * MatmulConfig[a_type, b_type, c_type, True]); this is that layout: each output
+ * column's codes and scales are contiguous.
+ *
+ *   b_packed  u32 [N, K / pack_factor]   word (n, kp): codes of K rows 8 kp + i in
+ *                                        bits 4i .. 4i + 3
+ *   scales    f16 or bf16 [N, K / group_size]
+ *
+ * Every other argument, type, check and result as qgemm_w4 (the same values:
+ * b_packed and scales are the transposes of qgemm_w4's). M > 16 runs the
+ * fourth prefill design with one stage in flight (QG_ERR_UNSUPPORTED for the
+ * others); B beyond 2^32 - 1 bytes is QG_ERR_UNSUPPORTED.
+ */
+qg_status qgemm_w4_nk(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
+                      const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
+                      hipStream_t stream);
+
+/*
  * qgemm_w4_epilogue - qgemm_w4 with a fixed epilogue
  *
  * Stands in for the page's elementwise_lambda_fn parameter (Parameters: a

@@ -19,7 +19,7 @@ Readings where the pages are silent are listed in each function's docstring.
 """
 from .numerics import (round_to_f16, round_to_bf16, round_to, decode_f16, decode_bf16,
                        decode_e4m3, encode_e4m3, f16_bits_of, bf16_bits_of, F16, BF16, E4M3)
-from .w4 import dequant_w4, qgemm_w4, qgemm_w4_epilogue, silu, EPI_BIAS, EPI_RESIDUAL, EPI_SILU_GATE
+from .w4 import dequant_w4, qgemm_w4, qgemm_w4_nk, qgemm_w4_epilogue, silu, EPI_BIAS, EPI_RESIDUAL, EPI_SILU_GATE
 from .grouped import grouped_gemm
 from .grouped_w4 import grouped_gemm_w4
 from .kproj import (k_matmul_ragged_paged_scale, kv_matmul_ragged_paged_scale, kproj_exact, kproj_rows,
@@ -28,7 +28,7 @@ from .kproj import (k_matmul_ragged_paged_scale, kv_matmul_ragged_paged_scale, k
 __all__ = [
     "round_to_f16", "round_to_bf16", "round_to", "decode_f16", "decode_bf16", "decode_e4m3",
     "encode_e4m3", "f16_bits_of", "bf16_bits_of", "F16", "BF16", "E4M3",
-    "dequant_w4", "qgemm_w4", "qgemm_w4_epilogue", "silu", "EPI_BIAS", "EPI_RESIDUAL", "EPI_SILU_GATE",
+    "dequant_w4", "qgemm_w4", "qgemm_w4_nk", "qgemm_w4_epilogue", "silu", "EPI_BIAS", "EPI_RESIDUAL", "EPI_SILU_GATE",
     "grouped_gemm", "grouped_gemm_w4", "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale",
     "kproj_exact", "kproj_rows", "quantize_runs",
     "token_slots",

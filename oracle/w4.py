@@ -114,3 +114,13 @@ def qgemm_w4_epilogue(a_bits, b_packed, scales_bits, group_size: int, epilogue: 
     c = rnd(z)
     assert np.all(np.isfinite(c)), "overflow in the reference result"
     return bits_of(c)
+
+
+def qgemm_w4_nk(a_bits, b_packed_nk, scales_nk, group_size: int, pack_factor: int = 8,
+                dtype: str = "f16") -> np.ndarray:
+    """The same product with B stored [N, K / pack_factor] and the scales
+    [N, K / group_size] (the page's transpose_b configuration): word (n, kp) holds
+    the codes of K rows pack_factor * kp + i of column n."""
+    b = np.ascontiguousarray(np.asarray(b_packed_nk, dtype=np.uint32).T)
+    s = np.ascontiguousarray(np.asarray(scales_nk, dtype=np.uint16).T)
+    return qgemm_w4(a_bits, b, s, group_size, pack_factor, dtype)

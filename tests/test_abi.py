@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert {"qgemm_w4", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "grouped_gemm_epilogue",
+    assert {"qgemm_w4", "qgemm_w4_nk", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "grouped_gemm_epilogue",
             "grouped_gemm_w4_epilogue", "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale",
             "qg_status_string"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
@@ -101,6 +101,23 @@ def test_w4_rejections(lib):
     nul.data = None
     assert w4_call(lib, nul, a, b, s) == QG.ERR_NULL
     assert lib.qgemm_w4(None, ctypes.byref(a), ctypes.byref(b), ctypes.byref(s), 128, 8, None) == QG.ERR_NULL
+
+
+def test_w4_nk_rejections(lib):
+    bb = Buf()
+    M, N, K = 4, 64, 256
+    c, a = bb.t((M, N), QG.F16), bb.t((M, K), QG.F16)
+    b_nk, s_nk = bb.t((N, K // 8), QG.U32), bb.t((N, K // 128), QG.F16)
+    call = lambda b, s, c=c: lib.qgemm_w4_nk(ctypes.byref(c), ctypes.byref(a), ctypes.byref(b), ctypes.byref(s),
+                                             128, 8, None)
+    assert call(bb.t((K // 8, N), QG.U32), s_nk) == QG.ERR_SHAPE     # [K/8, N] is qgemm_w4's layout
+    assert call(b_nk, bb.t((K // 128, N), QG.F16)) == QG.ERR_SHAPE
+    assert call(b_nk, bb.t((N, K // 128), QG.BF16)) == QG.ERR_DTYPE
+    assert call(bb.t((N * K // 8,), QG.U32), s_nk) == QG.ERR_RANK
+    assert call(b_nk, s_nk, c=bb.t((0, N), QG.F16)) == QG.ERR_SHAPE   # rows disagree with A
+    a0 = bb.t((0, K), QG.F16)
+    assert lib.qgemm_w4_nk(ctypes.byref(bb.t((0, N), QG.F16)), ctypes.byref(a0), ctypes.byref(b_nk),
+                           ctypes.byref(s_nk), 128, 8, None) == QG.OK
 
 
 def test_w4_empty_problem_is_a_noop(lib):

@@ -317,3 +317,23 @@ def test_epilogue_bias_is_added_before_the_gate():
     bias = np.array([0x4000, 0x4200] * (N // 2), np.uint16)   # gate 2, up 3
     got = oracle.qgemm_w4_epilogue(w.a, w.b, w.scales, gs, oracle.EPI_BIAS | oracle.EPI_SILU_GATE, bias, None)
     assert np.all(got.view(np.float16) == np.float16(2.0 * _sigmoid_tanh(2.0) * 3.0))
+
+
+# ---------------------------------------------------------------- [N, K/8] storage
+
+def test_nk_layout_brute_force():
+    """Scalar loops reading word (n, k // 8) of the [N, K/8] array and scale (n, k // gs)."""
+    for (M, N, K, gs) in [(2, 5, 64, 32), (3, 8, 128, 64)]:
+        w = synth.w4_inputs(M, N, K, seed=M + N, group_size=gs)
+        b_nk = np.ascontiguousarray(w.b.T)
+        s_nk = np.ascontiguousarray(w.scales.T)
+        a = w.a.view(np.float16).astype(np.float64)
+        s = s_nk.view(np.float16).astype(np.float64)
+        ref = np.zeros((M, N))
+        for m in range(M):
+            for n in range(N):
+                for k in range(K):
+                    q = (int(b_nk[n, k // 8]) >> (4 * (k % 8))) & 0xF
+                    ref[m, n] += a[m, k] * (q - 8) * s[n, k // gs]
+        got = oracle.qgemm_w4_nk(w.a, b_nk, s_nk, gs).view(np.float16).astype(np.float64)
+        assert np.array_equal(got, nm.round_to_f16(ref))
