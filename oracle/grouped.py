@@ -4,7 +4,7 @@ Follows the Modular page "grouped_matmul_sm100_persistent" (linalg /
 grouped_matmul_sm100), Args section:
   * a_offsets: per-expert prefix sum of A row offsets (uint32);
   * expert_ids: per-group expert id (int32); negative entries skip the tile;
-  * expert_usage_stats: index 1 holds the active expert count;
+  * expert_usage_stats: its second entry is the number of active experts;
   * b: the weights, one matrix per expert; Parameters: transpose_b says
     whether each expert's matrix is stored transposed ([N, K]).
 
