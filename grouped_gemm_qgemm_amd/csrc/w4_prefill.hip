@@ -623,7 +623,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
   static_assert(TN == 64 && TM % 32 == 0, "wave tile");
-  static_assert(PD == 1 || PD == 2, "prefetch distance");
+  static_assert(PD >= 1 && PD <= 4, "prefetch distance");
   static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
   static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
@@ -845,7 +845,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       sc_cur[0] = r.sc[0];
       sc_cur[1] = r.sc[1];
     }
-  } else {
+  } else if constexpr (PD == 2) {
     // Stage kt + 1 waits in one register set while stage kt + 2 loads into the
     // other; unrolled by two so the sets are static. Set u holds stages of
     // parity u. Loads retire in issue order, so waiting for the older set never
@@ -883,6 +883,34 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       __syncthreads();
     }
     if (kt < nk) compute(0, sc_cur);   // nk odd: the last stage sits in buffer 0
+  } else {
+    // PD register sets, unrolled by PD so each set is static: stage i + PD is
+    // requested into the set that held stage i (already in LDS) while stage i is
+    // multiplied, and stage i + 1, requested PD - 1 stages earlier, is stored
+    // after it. Loads past the last stage re-read it and are never stored.
+    Regs r[PD];
+    uint32_t sc_cur[2];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_stage(min(p, nk - 1), r[p]);
+    store_stage(0, 0, r[0]);
+    sc_cur[0] = r[0].sc[0];
+    sc_cur[1] = r[0].sc[1];
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += PD) {
+#pragma unroll
+      for (int p = 0; p < PD; ++p) {
+        const int i = kt + p;
+        load_stage(min(i + PD, nk - 1), r[p]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < nk) compute(i & 1, sc_cur);
+        if (i + 1 < nk) {
+          store_stage(i + 1, (i + 1) & 1, r[(p + 1) % PD]);
+          sc_cur[0] = r[(p + 1) % PD].sc[0];
+          sc_cur[1] = r[(p + 1) % PD].sc[1];
+        }
+        __syncthreads();
+      }
+    }
   }
 
   // epilogue: two adjacent columns per 4-byte store (or one gated output)
@@ -1040,6 +1068,11 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t st
     case 9: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2>(p, stream);
     case 10: return launch_grouped_tile<64, 128, 1, 2, 4, 1, 2>(p, stream);
     case 11: return launch_grouped_tile<128, 256, 1, 4, 2, 1, 2>(p, stream);
+    // three or four stages of prefetch in registers
+    case 12: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 3>(p, stream);
+    case 13: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3>(p, stream);
+    case 14: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 4>(p, stream);
+    case 15: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 3>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1114,6 +1147,9 @@ hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
     // two K groups of four waves (128 x 64 wave tiles), one workgroup per CU
     case 16: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 8);
     case 17: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 0);
+    // three stages in flight in registers
+    case 18: return launch_v4_tile<128, 256, 1, 4, 2, 3>(p, stream, 8);
+    case 19: return launch_v4_tile<128, 256, 1, 4, 1, 3>(p, stream, 8);
     default: return hipErrorInvalidValue;
   }
 }

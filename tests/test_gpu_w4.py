@@ -131,7 +131,7 @@ def test_decode_zero_point_and_determinism(gpu, lib):
 
 # ---------------------------------------------------------------- prefill (M > 16)
 
-PREFILL_VARIANTS = range(18)
+PREFILL_VARIANTS = range(20)
 
 
 @pytest.mark.parametrize("variant", PREFILL_VARIANTS)
@@ -178,7 +178,7 @@ def test_prefill_zero_point_and_determinism(gpu, lib):
 # ---------------------------------------------------------------- bf16 activations (a_type = c_type = bf16)
 
 BF16_DECODE_VARIANTS = range(9, 16)     # the LDS-staged decode kernel
-BF16_PREFILL_VARIANTS = range(11, 18)   # the fourth prefill design
+BF16_PREFILL_VARIANTS = range(11, 20)   # the fourth prefill design
 
 
 @pytest.mark.parametrize("variant", BF16_DECODE_VARIANTS)

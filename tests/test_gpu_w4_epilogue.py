@@ -154,7 +154,7 @@ def test_decode_variants(gpu, lib, variant):
                 check(lib, w, flags, 7 + flags, f"decode v{variant}", env="QG_W4_DECODE_VARIANT", variant=variant)
 
 
-@pytest.mark.parametrize("variant", range(11, 18))
+@pytest.mark.parametrize("variant", range(11, 20))
 def test_prefill_variants(gpu, lib, variant):
     for flags in (BIAS, RES, GATE, BIAS | GATE | RES):
         for dtype in ("f16", "bf16"):
