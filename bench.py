@@ -64,20 +64,22 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9023723, "c5047a03e5d045de"),
-    "prefill": (269374050, "426062eecd50ed1e"),
-    "square": (101398272, "426062eecd50ed1e"),
-    "grouped": (367980987, "71e5ce2e08f4edd1"),
-    "grouped_kn": (365849708, "71e5ce2e08f4edd1"),
-    "grouped_w4": (117997597, "426062eecd50ed1e"),
-    "kproj": (85586482, "57c92363b76839f7"),
-    "decode_gate": (9037033, "c5047a03e5d045de"),
-    "prefill_gate": (269572374, "426062eecd50ed1e"),
-    "decode_bf16": (9019628, "c5047a03e5d045de"),
-    "prefill_bf16": (270145182, "426062eecd50ed1e"),
-    "kvproj": (202279226, "57c92363b76839f7"),
-    "kvproj_e4m3": (193902382, "57c92363b76839f7"),
-    "kproj_e4m3h": (64355704, "57c92363b76839f7"),
+    "decode": (9026795, "e2fdc13d1458ea2a"),
+    "prefill": (269374882, "ba710398326892f7"),
+    "square": (101394176, "ba710398326892f7"),
+    "grouped": (367979046, "58f5acd539693f37"),
+    "grouped_kn": (365850457, "58f5acd539693f37"),
+    "grouped_w4": (118069335, "ba710398326892f7"),
+    "kproj": (85586482, "9a8699f600436574"),
+    "decode_gate": (9043176, "e2fdc13d1458ea2a"),
+    "prefill_gate": (269690828, "ba710398326892f7"),
+    "decode_bf16": (9021675, "e2fdc13d1458ea2a"),
+    "prefill_bf16": (270211544, "ba710398326892f7"),
+    "decode_nk": (9019628, "e2fdc13d1458ea2a"),
+    "prefill_nk": (232415436, "ba710398326892f7"),
+    "kvproj": (202279226, "9a8699f600436574"),
+    "kvproj_e4m3": (193902382, "9a8699f600436574"),
+    "kproj_e4m3h": (64355704, "9a8699f600436574"),
 }
 
 
