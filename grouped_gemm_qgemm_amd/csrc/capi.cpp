@@ -288,7 +288,7 @@ static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, co
                       static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
                       static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
                       T, N, K, E, group_size, (int)num_active, epi};
-  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 8), stream));
+  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 16), stream));
 }
 
 qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,

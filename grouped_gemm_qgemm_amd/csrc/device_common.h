@@ -62,6 +62,10 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+__device__ __forceinline__ uint64_t buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
 // Locates work tile t of a routed (grouped) GEMM. Group g < num_active with
 // ids[g] >= 0 and rows = a_off[g+1] - a_off[g] > 0 owns ceil(rows / bm) * tiles_n
 // consecutive tiles, in group order. The calling wave scans 64 groups at a
@@ -94,7 +98,8 @@ __device__ __forceinline__ TileLoc locate_tile(int t, const uint32_t* __restrict
     if (hit) {
       const int first = __ffsll((long long)hit) - 1;
       const int excl = __shfl(incl - cnt, first);
-      return TileLoc{g0 + first, t - base - excl};
+      // the same in every lane: readfirstlane lets the compiler keep it in SGPRs
+      return TileLoc{__builtin_amdgcn_readfirstlane(g0 + first), __builtin_amdgcn_readfirstlane(t - base - excl)};
     }
     base += __shfl(incl, 63);
   }
@@ -117,7 +122,7 @@ __device__ __forceinline__ int count_tiles(const uint32_t* __restrict__ a_off, c
     for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
     total += cnt;
   }
-  return total;
+  return __builtin_amdgcn_readfirstlane(total);   // the same in every lane
 }
 
 // One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
@@ -143,6 +148,15 @@ __device__ __forceinline__ u32x4_t dequant_w4_word(uint32_t w) {
 // do not cover instructions hidden in inline assembly, and a VGPR write issued
 // right after an MFMA that reads the same register as an operand must be
 // spaced by the compiler.
+// x in a VGPR, opaque to constant folding: the empty asm statement emits no
+// instruction. v_and_or_b32 takes no literal operand on gfx950, so a mask the
+// compiler can see as a constant turns each fused mask-and-bias into two
+// instructions (v_and_b32 and v_or_b32 with literals).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+  asm("" : "=v"(x) : "0"(x));
+  return x;
+}
+
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
   return (a & m) | b;
 }

@@ -363,9 +363,10 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     const TileLoc loc = locate_tile(t, a_off, ids, num_active, GBM, tiles_n);
     const int g = loc.g;
     const int chunk = loc.local / tiles_n, nt = loc.local % tiles_n;
-    const int e = ids[g];
-    const int r_begin = (int)a_off[g] + chunk * GBM;
-    const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
+    // uniform values in SGPRs: buffer descriptors and row-tile dispatch stay scalar
+    const int e = __builtin_amdgcn_readfirstlane(ids[g]);
+    const int r_begin = __builtin_amdgcn_readfirstlane((int)a_off[g] + chunk * GBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(GBM, (int)a_off[g + 1] - r_begin));
     const int n0 = nt * GBN;
     // two activation fragments per wave per sub-step beyond four row tiles
     // (four waves): half as many steps in flight
@@ -421,9 +422,10 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     const TileLoc loc = locate_tile(t, a_off, ids, num_active, GBM, tiles_n);
     const int g = loc.g;
     const int chunk = loc.local / tiles_n, nt = loc.local % tiles_n;
-    const int e = ids[g];
-    const int r_begin = (int)a_off[g] + chunk * GBM;
-    const int rows = min(GBM, (int)a_off[g + 1] - r_begin);
+    // uniform values in SGPRs: buffer descriptors and row-tile dispatch stay scalar
+    const int e = __builtin_amdgcn_readfirstlane(ids[g]);
+    const int r_begin = __builtin_amdgcn_readfirstlane((int)a_off[g] + chunk * GBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(GBM, (int)a_off[g + 1] - r_begin));
     const int n0 = nt * GBN;
     // With four waves, tiles of more than four row tiles load two activation
     // fragments per wave per step, so they run half as many steps ahead: the

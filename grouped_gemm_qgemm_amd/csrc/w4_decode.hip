@@ -165,7 +165,7 @@ __device__ __forceinline__ void w4_decode_lds_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quarter = lane >> 4;
   const int col16 = lane & 15;
-  const uint32_t vmask = 0x000F000Fu;   // lives in a VGPR for the fused unpack
+  const uint32_t vmask = in_vgpr(0x000F000Fu);   // a VGPR operand for the fused unpack
   const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
   const uint32_t m136 = 0xC308C308u;    // bf16 pair (-136, -136)
 

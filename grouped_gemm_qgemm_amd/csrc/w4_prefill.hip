@@ -304,7 +304,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_lds_kern
       if (k0 + a_ch[i] * 8 >= K) v = u32x4_t{0u, 0u, 0u, 0u};   // K tail
       lds_a[buf][a_row[i] * CHUNKS + swz(a_row[i], a_ch[i])] = v;
     }
-    const uint32_t vmask = 0x000F000Fu;
+    const uint32_t vmask = in_vgpr(0x000F000Fu);
     const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
 #pragma unroll
     for (int j = 0; j < W_PER_T; ++j) {
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_ke
 #pragma unroll
     for (int j = 0; j < NB * 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t vmask = 0x000F000Fu;
+  const uint32_t vmask = in_vgpr(0x000F000Fu);
   const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
   const int nk = (K + BK - 1) / BK;
   load_stage(0);
@@ -599,11 +599,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_ke
 // their accumulators through LDS at the end: the same tile and the same unpack
 // work per wave, twice the waves per SIMD to cover each other's waits (for
 // shapes with about one tile per CU).
-// LDS of one fourth-design tile: per K group, two stages of A chunks and of packed B.
-template <int BM, int BN, int KG>
+// LDS of one fourth-design tile: per K group, two stages of A chunks and of
+// packed B (no B when each wave loads its own B words, BD).
+template <int BM, int BN, int KG, bool BD = false>
 struct W4TileLds {
   u32x4_t a[KG][2][BM * CHUNKS];
-  u32x4_t b[KG][2][(BK / 8) * BN / 4];
+  u32x4_t b[KG][2][BD ? 1 : (BK / 8) * BN / 4];
 };
 
 // One BM x BN output tile of the fourth design: rows m0 .. m0+BM-1 (those < M)
@@ -614,17 +615,24 @@ struct W4TileLds {
 // then read as each column's eight words (two 16-byte loads per column) and
 // written into the same [8][BN] LDS tile word by word, so the MFMA loop is
 // unchanged; the lane's two scales are two 2-byte loads.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false>
+// BD: B does not pass through LDS. Each lane loads the packed words its MFMAs
+// take (two adjacent columns of one packed row per 16-deep step: 8 bytes, 256
+// contiguous bytes per half-wave) one stage ahead, like the scales. This pays
+// when a wave's B columns are its own (WAVES_M == 1, as in the grouped tiles).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false,
+          bool BD = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
-                                             W4TileLds<BM, BN, KG>& lds, const Epilogue& ep) {
+                                             W4TileLds<BM, BN, KG, BD>& lds, const Epilogue& ep) {
   constexpr int NTHR = WAVES_M * WAVES_N * kWave;   // threads of one K group
   constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   constexpr int MT = TM / 32;
   static_assert(TN == 64 && TM % 32 == 0, "wave tile");
   static_assert(PD >= 1 && PD <= 4, "prefetch distance");
   static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
+  static_assert(!BD || (KG == 1 && !NK), "direct B: one K group, [K/8, N] layout");
+  constexpr int NBD = BD ? BK / 16 : 1;      // direct B words per lane and stage
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
   static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
   constexpr int B_CHUNKS = (BK / 8) * (BN / 4);
@@ -677,20 +685,41 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   }
   // this lane's two output columns (scale columns)
   const uint32_t s_voff = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2) * 2;
+  // direct B: packed row h of each 16-deep step, the same two columns (from n0)
+  const uint32_t bd_voff = (uint32_t)(h * N + min(wn * TN + 2 * c32, N - n0 - 2)) * 4;
 
   // one stage of prefetched operands: A chunks, packed B chunks, the lane's scale pairs
   struct Regs {
     u32x4_t a[A_PER_T];
-    u32x4_t b[B_PER_T];
+    u32x4_t b[BD ? 1 : B_PER_T];
+    uint64_t bd[NBD];
     uint32_t sc[2];
+  };
+  // what the MFMA loop takes from a stage's registers: scale pairs, direct B words
+  struct Cur {
+    uint32_t sc[2];
+    uint64_t bd[NBD];
+  };
+  auto cur_of = [](const Regs& r) {
+    Cur c;
+    c.sc[0] = r.sc[0];
+    c.sc[1] = r.sc[1];
+#pragma unroll
+    for (int j = 0; j < NBD; ++j) c.bd[j] = BD ? r.bd[j] : 0ull;
+    return c;
   };
   auto load_stage = [&](int kt, Regs& r) {
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) r.a[i] = buffer_load16(a_src, a_voff[i], (uint32_t)k0 * 2);
+    if constexpr (BD) {
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i)
-      r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : (uint32_t)(k0 / 8) * N * 4);
+      for (int j = 0; j < NBD; ++j) r.bd[j] = buffer_load8(b_src, bd_voff, (uint32_t)(k0 / 8 + 2 * j) * N * 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_PER_T; ++i)
+        r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : (uint32_t)(k0 / 8) * N * 4);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = min(k0 + 32 * s, K - 1) >> gshift;
@@ -713,7 +742,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
+    for (int i = 0; i < (BD ? 0 : B_PER_T); ++i) {
       if constexpr (NK) {
         const int id = tid + i * NTHR, half = id / BN, c = id % BN;
         uint32_t* wb = reinterpret_cast<uint32_t*>(lds_b[buf]);
@@ -735,16 +764,16 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
-  const uint32_t vmask = 0x000F000Fu;
+  const uint32_t vmask = in_vgpr(0x000F000Fu);
   const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
-  // one stage out of LDS buffer `buf` with the scale pairs `sc`
-  auto compute = [&](int buf, const uint32_t (&sc)[2]) {
+  // one stage out of LDS buffer `buf` with the stage's scale pairs (and direct B words)
+  auto compute = [&](int buf, const Cur& cur) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds_b[buf]);
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       // packed row 2j + h of the stage, columns 2*c32 and 2*c32 + 1 of the wave's 64
-      const uint64_t w2 = bw[(2 * j + h) * (BN / 2) + wn * (TN / 2) + c32];
-      const uint32_t sp = sc[j >> 1];
+      const uint64_t w2 = BD ? cur.bd[BD ? j : 0] : bw[(2 * j + h) * (BN / 2) + wn * (TN / 2) + c32];
+      const uint32_t sp = cur.sc[j >> 1];
       u32x4_t bq[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -778,12 +807,11 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     // group kg takes stages kg, kg + 2, ...; both groups run the same number of
     // iterations so every wave reaches every barrier
     Regs r;
-    uint32_t sc_cur[2] = {0u, 0u};
+    Cur cur{};
     if (kg < nk) {
       load_stage(kg, r);
       store_stage(kg, 0, r);
-      sc_cur[0] = r.sc[0];
-      sc_cur[1] = r.sc[1];
+      cur = cur_of(r);
     }
     __syncthreads();
     const int iters = (nk + 1) / 2;
@@ -792,13 +820,10 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       const bool more = kt + 2 < nk;
       if (more) load_stage(kt + 2, r);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt < nk) compute(j & 1, sc_cur);
+      if (kt < nk) compute(j & 1, cur);
       if (more) store_stage(kt + 2, (j + 1) & 1, r);
       __syncthreads();
-      if (more) {
-        sc_cur[0] = r.sc[0];
-        sc_cur[1] = r.sc[1];
-      }
+      if (more) cur = cur_of(r);
     }
     // group 1 hands its partial sums to group 0 through the (now free) stage
     // buffers, two row tiles at a time; lane-major so the accesses are
@@ -829,21 +854,18 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     if (kg == 1) return;
   } else if constexpr (PD == 1) {
     Regs r;
-    uint32_t sc_cur[2];
     load_stage(0, r);
     store_stage(0, 0, r);
-    sc_cur[0] = r.sc[0];
-    sc_cur[1] = r.sc[1];
+    Cur cur = cur_of(r);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + 1 < nk;
       if (more) load_stage(kt + 1, r);
       __builtin_amdgcn_sched_barrier(0);
-      compute(kt & 1, sc_cur);
+      compute(kt & 1, cur);
       if (more) store_stage(kt + 1, (kt + 1) & 1, r);
       __syncthreads();
-      sc_cur[0] = r.sc[0];
-      sc_cur[1] = r.sc[1];
+      cur = cur_of(r);
     }
   } else if constexpr (PD == 2) {
     // Stage kt + 1 waits in one register set while stage kt + 2 loads into the
@@ -851,12 +873,10 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     // parity u. Loads retire in issue order, so waiting for the older set never
     // waits for the newer one.
     Regs r0, r1;
-    uint32_t sc_cur[2];
     load_stage(0, r0);
     if (nk > 1) load_stage(1, r1);
     store_stage(0, 0, r0);
-    sc_cur[0] = r0.sc[0];
-    sc_cur[1] = r0.sc[1];
+    Cur cur = cur_of(r0);
     __syncthreads();
     int kt = 0;
     // Loads past the last stage re-read it (their copies are never stored), so
@@ -866,35 +886,31 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       // even stage kt: buffer 0; stage kt + 1 is in r1
       load_stage(min(kt + 2, nk - 1), r0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, sc_cur);
+      compute(0, cur);
       store_stage(kt + 1, 1, r1);
       __syncthreads();
-      sc_cur[0] = r1.sc[0];
-      sc_cur[1] = r1.sc[1];
+      cur = cur_of(r1);
       // odd stage kt + 1: buffer 1; stage kt + 2 (if any) is in r0
       load_stage(min(kt + 3, nk - 1), r1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(1, sc_cur);
+      compute(1, cur);
       if (kt + 2 < nk) {
         store_stage(kt + 2, 0, r0);
-        sc_cur[0] = r0.sc[0];
-        sc_cur[1] = r0.sc[1];
+        cur = cur_of(r0);
       }
       __syncthreads();
     }
-    if (kt < nk) compute(0, sc_cur);   // nk odd: the last stage sits in buffer 0
+    if (kt < nk) compute(0, cur);   // nk odd: the last stage sits in buffer 0
   } else {
     // PD register sets, unrolled by PD so each set is static: stage i + PD is
     // requested into the set that held stage i (already in LDS) while stage i is
     // multiplied, and stage i + 1, requested PD - 1 stages earlier, is stored
     // after it. Loads past the last stage re-read it and are never stored.
     Regs r[PD];
-    uint32_t sc_cur[2];
 #pragma unroll
     for (int p = 0; p < PD; ++p) load_stage(min(p, nk - 1), r[p]);
     store_stage(0, 0, r[0]);
-    sc_cur[0] = r[0].sc[0];
-    sc_cur[1] = r[0].sc[1];
+    Cur cur = cur_of(r[0]);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += PD) {
 #pragma unroll
@@ -902,11 +918,10 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const int i = kt + p;
         load_stage(min(i + PD, nk - 1), r[p]);
         __builtin_amdgcn_sched_barrier(0);
-        if (i < nk) compute(i & 1, sc_cur);
+        if (i < nk) compute(i & 1, cur);
         if (i + 1 < nk) {
           store_stage(i + 1, (i + 1) & 1, r[(p + 1) % PD]);
-          sc_cur[0] = r[(p + 1) % PD].sc[0];
-          sc_cur[1] = r[(p + 1) % PD].sc[1];
+          cur = cur_of(r[(p + 1) % PD]);
         }
         __syncthreads();
       }
@@ -1013,20 +1028,30 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
 // takes a contiguous run, so a group's column tiles share that XCD's L2 for its
 // activation rows. Expert e's packed words and scales are b[e] ([K/8, N]) and
 // s[e] ([K/group_size, N]). Rows of skipped groups are never written. The grid
-// is an upper bound on the tile count; workgroups past the last tile exit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD>
+// holds an upper bound on the tile count (only the device knows the group
+// sizes); the real count is split evenly over the eight XCDs, at most
+// ceil(count / 8) <= grid / 8 tiles each, and workgroups past their XCD's run exit.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
-    int group_size, int num_active, int tiles_n, int per_xcd, Epilogue ep) {
-  __shared__ W4TileLds<BM, BN, KG> lds;
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    int group_size, int num_active, int tiles_n, Epilogue ep) {
+  __shared__ W4TileLds<BM, BN, KG, BD> lds;
+  // The tile's coordinates are the same in every lane; readfirstlane makes that
+  // visible to the compiler, so the buffer descriptors built from them stay in
+  // SGPRs (otherwise every buffer load becomes a loop over distinct values).
+  const int total = __builtin_amdgcn_readfirstlane(count_tiles(a_off, ids, num_active, BM, tiles_n));
+  const int xcd = blockIdx.x & 7;
+  const int t = (int)(((long long)total * xcd) >> 3) + (int)(blockIdx.x >> 3);
+  if (t >= (int)(((long long)total * (xcd + 1)) >> 3)) return;
   const TileLoc loc = locate_tile(t, a_off, ids, num_active, BM, tiles_n);
-  if (loc.g < 0) return;
-  const int chunk = loc.local / tiles_n, nt = loc.local - chunk * tiles_n;
-  const int e = ids[loc.g];
-  const int r_begin = (int)a_off[loc.g] + chunk * BM;
-  const int rows = min(BM, (int)a_off[loc.g + 1] - r_begin);
+  const int g = __builtin_amdgcn_readfirstlane(loc.g);
+  if (g < 0) return;
+  const int local = __builtin_amdgcn_readfirstlane(loc.local);
+  const int chunk = local / tiles_n, nt = local - chunk * tiles_n;
+  const int e = __builtin_amdgcn_readfirstlane(ids[g]);
+  const int r_begin = __builtin_amdgcn_readfirstlane((int)a_off[g] + chunk * BM);
+  const int rows = __builtin_amdgcn_readfirstlane(min(BM, (int)a_off[g + 1] - r_begin));
   const size_t wpe = (size_t)(K / 8) * N, spe = (size_t)(K / group_size) * N;   // per-expert sizes
   // the fixed epilogue sees the group's rows as a matrix of their own: C and the
   // residual from row r_begin (N / 2 wide with the gate), the expert's bias row
@@ -1034,12 +1059,13 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   Epilogue ept = ep;
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K,
-                                                        B + e * wpe, S + e * spe, rows, N, K, group_size, 0,
-                                                        nt * BN, lds, ept);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false, false, BD>(C + (size_t)r_begin * NO,
+                                                                   A + (size_t)r_begin * K, B + e * wpe,
+                                                                   S + e * spe, rows, N, K, group_size, 0,
+                                                                   nt * BN, lds, ept);
 }
 
-template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1>
+template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1, bool BD = false>
 static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream) {
   if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL) return hipErrorNotSupported;
   const int tiles_n = (int)((p.N + BN - 1) / BN);
@@ -1047,9 +1073,9 @@ static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
   if (bound > INT32_MAX / 2) return hipErrorNotSupported;
   const int grid = (int)((bound + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
                      stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
-                     p.num_active, tiles_n, grid / 8, p.epi);
+                     p.num_active, tiles_n, p.epi);
   return hipGetLastError();
 }
 
@@ -1073,6 +1099,11 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t st
     case 13: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3>(p, stream);
     case 14: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 4>(p, stream);
     case 15: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 3>(p, stream);
+    // B words loaded straight into each wave's registers (no LDS for B)
+    case 16: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 2, true>(p, stream);
+    case 17: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 1, true>(p, stream);
+    case 18: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3, true>(p, stream);
+    case 19: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2, true>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
