@@ -1104,6 +1104,12 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t st
     case 17: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 1, true>(p, stream);
     case 18: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3, true>(p, stream);
     case 19: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2, true>(p, stream);
+    // taller row chunks (one per group of up to 96 or 128 rows): each weight
+    // is unpacked once per group, narrower column tiles keep the tile count up
+    case 20: return launch_grouped_tile<96, 128, 1, 2, 4, 1, 2, true>(p, stream);
+    case 21: return launch_grouped_tile<96, 256, 1, 4, 2, 1, 2, true>(p, stream);
+    case 22: return launch_grouped_tile<128, 128, 1, 2, 3, 1, 2, true>(p, stream);
+    case 23: return launch_grouped_tile<64, 128, 1, 2, 2, 1, 2, true>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -201,7 +201,7 @@ def test_w4_every_flag_set(gpu, lib, flags):
         run_w4(lib, d, flags, seed + 10 * flags)
 
 
-@pytest.mark.parametrize("variant", range(20))
+@pytest.mark.parametrize("variant", range(24))
 def test_w4_every_launch_shape(gpu, lib, variant):
     d = synth.grouped_w4_inputs(seed=50 + variant, E=6, T=500, K=256, N=144, skip_frac=0.2)
     say(f"[grouped-epi] w4 variant {variant}")

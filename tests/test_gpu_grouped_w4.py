@@ -19,7 +19,7 @@ from oracle import numerics as nm
 pytestmark = pytest.mark.gpu
 
 SENT = 0x7E00  # fp16 NaN pattern: never produced by the kernel
-VARIANTS = range(20)
+VARIANTS = range(24)
 
 
 def run_gw4(lib, d, a_off=None, ids=None, usage=None, a=None, variant=None):
