@@ -64,22 +64,22 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9026795, "e2fdc13d1458ea2a"),
-    "prefill": (269374882, "ba710398326892f7"),
-    "square": (101394176, "ba710398326892f7"),
-    "grouped": (367979046, "58f5acd539693f37"),
-    "grouped_kn": (365850457, "58f5acd539693f37"),
-    "grouped_w4": (118069335, "ba710398326892f7"),
-    "kproj": (85586482, "9a8699f600436574"),
-    "decode_gate": (9043176, "e2fdc13d1458ea2a"),
-    "prefill_gate": (269690828, "ba710398326892f7"),
-    "decode_bf16": (9021675, "e2fdc13d1458ea2a"),
-    "prefill_bf16": (270211544, "ba710398326892f7"),
-    "decode_nk": (9019628, "e2fdc13d1458ea2a"),
-    "prefill_nk": (232415436, "ba710398326892f7"),
-    "kvproj": (202279226, "9a8699f600436574"),
-    "kvproj_e4m3": (193902382, "9a8699f600436574"),
-    "kproj_e4m3h": (64355704, "9a8699f600436574"),
+    "decode": (9011436, "e278b08f0b34864e"),
+    "prefill": (273511159, "e12318fb1ae26289"),
+    "square": (101390080, "e12318fb1ae26289"),
+    "grouped": (368071126, "f833eb3207a13024"),
+    "grouped_kn": (365856348, "f833eb3207a13024"),
+    "grouped_w4": (116607127, "e12318fb1ae26289"),
+    "kproj": (85586482, "ef6983f121e9e52b"),
+    "decode_gate": (9036009, "e278b08f0b34864e"),
+    "prefill_gate": (273751528, "e12318fb1ae26289"),
+    "decode_bf16": (8999149, "e278b08f0b34864e"),
+    "prefill_bf16": (268257156, "e12318fb1ae26289"),
+    "decode_nk": (9012460, "e278b08f0b34864e"),
+    "prefill_nk": (232412813, "e12318fb1ae26289"),
+    "kvproj": (202279226, "ef6983f121e9e52b"),
+    "kvproj_e4m3": (193902382, "ef6983f121e9e52b"),
+    "kproj_e4m3h": (64355704, "ef6983f121e9e52b"),
 }
 
 
