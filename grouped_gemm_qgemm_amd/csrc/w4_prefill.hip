@@ -731,10 +731,13 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)g * N * 2);
       }
     }
-    // partial last stage (K % 64 == 32): A chunks past K must enter as zeros
-    if (k0 + BK > K && k0 + a_ch0 * 8 >= K) {
+    // partial last stage (K % 64 == 32): A chunks past K must enter as zeros.
+    // The outer test is uniform, so full stages branch past the per-lane selects.
+    if (__builtin_expect(k0 + BK > K, 0)) {
+      if (k0 + a_ch0 * 8 >= K) {
 #pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) r.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < A_PER_T; ++i) r.a[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
   };
   auto store_stage = [&](int kt, int buf, const Regs& r) {

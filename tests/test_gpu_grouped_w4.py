@@ -65,7 +65,8 @@ def check(lib, d, what, **kw):
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_small_ragged(gpu, lib, variant):
     for (E, T, K, N, gs, seed) in [(8, 200, 256, 64, 128, 1), (5, 77, 128, 24, 32, 2),
-                                   (16, 600, 512, 264, 64, 3), (3, 300, 256, 136, 256, 4)]:
+                                   (16, 600, 512, 264, 64, 3), (3, 300, 256, 136, 256, 4),
+                                   (6, 150, 96, 40, 32, 5), (4, 90, 160, 48, 32, 6)]:   # K % 64 == 32: partial last stage
         d = synth.grouped_w4_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25, group_size=gs)
         check(lib, d, f"small seed{seed}", variant=variant)
 
