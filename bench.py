@@ -65,18 +65,18 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
     "decode": (9011436, "e278b08f0b34864e"),
-    "prefill": (273511159, "e12318fb1ae26289"),
-    "square": (101390080, "e12318fb1ae26289"),
+    "prefill": (270609845, "af6802a75e8ff835"),
+    "square": (101399295, "af6802a75e8ff835"),
     "grouped": (368071126, "f833eb3207a13024"),
     "grouped_kn": (365856348, "f833eb3207a13024"),
-    "grouped_w4": (116607127, "e12318fb1ae26289"),
+    "grouped_w4": (115068766, "af6802a75e8ff835"),
     "kproj": (85586482, "ef6983f121e9e52b"),
     "decode_gate": (9036009, "e278b08f0b34864e"),
-    "prefill_gate": (273751528, "e12318fb1ae26289"),
+    "prefill_gate": (270840999, "af6802a75e8ff835"),
     "decode_bf16": (8999149, "e278b08f0b34864e"),
-    "prefill_bf16": (268257156, "e12318fb1ae26289"),
+    "prefill_bf16": (271275515, "af6802a75e8ff835"),
     "decode_nk": (9012460, "e278b08f0b34864e"),
-    "prefill_nk": (232412813, "e12318fb1ae26289"),
+    "prefill_nk": (232414284, "af6802a75e8ff835"),
     "kvproj": (202279226, "ef6983f121e9e52b"),
     "kvproj_e4m3": (193902382, "ef6983f121e9e52b"),
     "kproj_e4m3h": (64355704, "ef6983f121e9e52b"),
