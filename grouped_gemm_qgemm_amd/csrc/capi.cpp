@@ -1,8 +1,6 @@
-// C ABI entry points: host-side argument checks, kernel-variant choice and
+// C ABI entry points: host-side argument checks, launch-shape choice and
 // launch. Every check runs before the first HIP call, so a rejected call
 // enqueues nothing and touches no output.
-#include <cstdlib>
-#include <cstring>
 #include <mutex>
 
 #include <hip/hip_runtime.h>
@@ -30,13 +28,6 @@ qg_status check_tensor(const qg_tensor* t, int rank, qg_dtype dt) {
     if (!aligned16(t->data)) return QG_ERR_ALIGN;
   }
   return QG_OK;
-}
-
-// Optional variant override for tuning sweeps: QG_<NAME>_VARIANT=<int>.
-int env_variant(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  return std::atoi(v);
 }
 
 int device_cus() {
@@ -147,25 +138,11 @@ static qg_status qgemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_
                static_cast<const uint32_t*>(b_packed->data), static_cast<const uint16_t*>(scales->data),
                M, N, K, group_size, act == QG_BF16 ? 1 : 0, epi};
   p.nk = nk ? 1 : 0;
-  const bool wide = p.bf16 || epilogue || nk;   // bf16, epilogues and [N, K/8] run in the newer kernels
-  if (M <= 16) {
-    const int v = env_variant("QG_W4_DECODE_VARIANT", 9);
-    if (wide && v < 9) return QG_ERR_UNSUPPORTED;   // the LDS-staged decode kernel
-    return launch_status(qg::launch_w4_decode(p, v, stream));
-  }
-  // 128 x 256 tiles of 32x32x16 MFMAs, each XCD sweeping groups of eight row
-  // panels across N: with at most one tile per CU one workgroup of two K
-  // groups per CU (16), otherwise two workgroups of one K group (15)
-  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
-  int dflt = tiles <= (int64_t)device_cus() ? 16 : 15;
-  if (K / 8 * N * 4 > 0xFFFFFFFFLL) {           // beyond 32-bit buffer offsets: the third design
-    if (wide) return QG_ERR_UNSUPPORTED;         // (fp16 only, no epilogue)
-    dflt = 9;
-  }
-  const int v = env_variant("QG_W4_PREFILL_VARIANT", dflt);
-  if (wide && v < 11) return QG_ERR_UNSUPPORTED;   // the fourth design
-  if (nk && (v == 12 || v > 17)) return QG_ERR_UNSUPPORTED;   // [N, K/8]: one stage in flight
-  return launch_status(qg::launch_w4_prefill(p, v, stream));
+  if (M <= 16) return launch_status(qg::launch_w4_decode(p, stream));
+  // the tiled kernel addresses 128 rows of A and eight packed rows of B (from a
+  // stage's first packed row) with 32-bit buffer offsets
+  if (K >= (1LL << 24) || N >= (1LL << 27)) return QG_ERR_UNSUPPORTED;
+  return launch_status(qg::launch_w4_prefill(p, device_cus(), stream));
 }
 
 qg_status qgemm_w4_nk(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
@@ -224,9 +201,7 @@ static qg_status grouped_gemm_impl(const qg_tensor* c, const qg_tensor* a, const
                     static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
                     static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
                     (int)expert_usage_stats_host[0], device_cus(), transpose_b ? 1 : 0, epi};
-  // both layouts stage the weights through LDS as whole 128-byte row segments:
-  // [E, N, K] in 64-deep steps (19), [E, K, N] with transpose reads (12)
-  return launch_status(qg::launch_grouped_bf16(p, env_variant("QG_GROUPED_VARIANT", transpose_b ? 19 : 12), stream));
+  return launch_status(qg::launch_grouped_bf16(p, stream));
 }
 
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
@@ -282,13 +257,16 @@ static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, co
   qg::Epilogue epi;
   if ((st = check_epilogue(epilogue, bias, residual, QG_F16, E, T, N, &epi)) != QG_OK) return st;
   if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || E > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  // the tiled kernel addresses a tile's rows of A and eight packed rows of an
+  // expert's B with 32-bit buffer offsets
+  if (K >= (1LL << 24) || N >= (1LL << 27)) return QG_ERR_UNSUPPORTED;
   if (T == 0 || N == 0 || num_active == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;  // would need a zero fill of the routed rows
   qg::W4GroupedArgs p{static_cast<uint16_t*>(c->data), static_cast<const uint16_t*>(a->data),
                       static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
                       static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
                       T, N, K, E, group_size, (int)num_active, epi};
-  return launch_status(qg::launch_w4_grouped(p, env_variant("QG_W4_GROUPED_VARIANT", 16), stream));
+  return launch_status(qg::launch_w4_grouped(p, stream));
 }
 
 qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
@@ -371,14 +349,10 @@ static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_ro
   p.kv_scales = fp8 ? static_cast<float*>(kv->scales.data) : nullptr;
   p.qgran = (int)G;
   p.hidden_fp8 = hidden_fp8 ? 1 : 0;
-  const int v = env_variant("QG_KPROJ_VARIANT", 0);
-  if (hidden_fp8) {                      // the fourth design only, with Kh / 128 <= 32
-    if (Kh / 128 > 32 || (v != 0 && (v < 21 || v > 27))) return QG_ERR_UNSUPPORTED;
-    return launch_status(qg::launch_kproj_fp8(p, v, stream));
-  }
-  const bool wide = fp8 || planes > 1;   // the third design only, with Kh / 128 <= 32
-  if (wide && (Kh / 128 > 32 || (v != 0 && v < 6))) return QG_ERR_UNSUPPORTED;
-  return launch_status(qg::launch_kproj_fp8(p, v, stream));
+  // e4m3 hidden rows, an e4m3 cache and the value plane need at most 32 scale
+  // blocks of K (the designs that keep the tile's input scales in LDS)
+  if ((hidden_fp8 || fp8 || planes > 1) && Kh / 128 > 32) return QG_ERR_UNSUPPORTED;
+  return launch_status(qg::launch_kproj_fp8(p, stream));
 }
 
 qg_status k_matmul_ragged_paged_scale(const qg_tensor* hidden, const qg_tensor* input_row_offsets,

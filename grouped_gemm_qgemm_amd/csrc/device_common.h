@@ -125,25 +125,6 @@ __device__ __forceinline__ int count_tiles(const uint32_t* __restrict__ a_off, c
   return __builtin_amdgcn_readfirstlane(total);   // the same in every lane
 }
 
-// One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
-// weights (q - 8), exact, as four packed half pairs in the K-slot order
-// (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of
-// 1024.0 (0x6400) gives 1024 + q exactly; subtracting 1032 leaves q - 8.
-__device__ __forceinline__ u32x4_t dequant_w4_word(uint32_t w) {
-  const uint32_t m = 0x000F000Fu, bias = 0x64006400u;
-  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  uint32_t p0 = (w & m) | bias;
-  uint32_t p1 = ((w >> 4) & m) | bias;
-  uint32_t p2 = ((w >> 8) & m) | bias;
-  uint32_t p3 = ((w >> 12) & m) | bias;
-  u32x4_t r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p0) - off);
-  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p1) - off);
-  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p2) - off);
-  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p3) - off);
-  return r;
-}
-
 // (a & m) | b. Written in C (no inline assembly): the compiler's hazard checks
 // do not cover instructions hidden in inline assembly, and a VGPR write issued
 // right after an MFMA that reads the same register as an operand must be
@@ -161,8 +142,12 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t b) {
   return (a & m) | b;
 }
 
-// Same unpack as dequant_w4_word with fused mask-and-bias operations; `m` must
-// hold 0x000F000F (in a VGPR) and `bias` 0x64006400.
+// One 32-bit word of eight 4-bit codes (code i in bits 4i..4i+3) -> eight fp16
+// weights (q - 8), exact, as four packed half pairs in the K-slot order
+// (0,4), (1,5), (2,6), (3,7). OR-ing a code into the low mantissa bits of
+// 1024.0 (0x6400) gives 1024 + q exactly; subtracting 1032 leaves q - 8.
+// The mask and bias are fused (v_and_or_b32); `m` must hold 0x000F000F (in a
+// VGPR) and `bias` 0x64006400.
 __device__ __forceinline__ u32x4_t dequant_w4_word_fused(uint32_t w, uint32_t m, uint32_t bias) {
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const uint32_t p0 = and_or(w, m, bias);
@@ -178,7 +163,7 @@ __device__ __forceinline__ u32x4_t dequant_w4_word_fused(uint32_t w, uint32_t m,
 }
 
 // Eight consecutive fp16 values (a0..a7 in four registers) reordered to the
-// K-slot order used by dequant_w4_word: (a0,a4), (a1,a5), (a2,a6), (a3,a7).
+// K-slot order used by dequant_w4_word_fused: (a0,a4), (a1,a5), (a2,a6), (a3,a7).
 __device__ __forceinline__ u32x4_t permute_k_0415(u32x4_t v) {
   u32x4_t r;
   r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
@@ -215,36 +200,11 @@ __device__ __forceinline__ uint32_t f2bf2_rn(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
-// One packed word -> its eight weights (q - 8) * s rounded to bf16, as four bf16
-// pairs in the K-slot order of dequant_w4_word_fused: (0,4), (1,5), (2,6),
-// (3,7). The nibbles are spread into bytes (even codes of w & 0x0F0F0F0F, odd
-// codes of (w >> 4) & 0x0F0F0F0F), each byte converts to float in one
-// instruction, and q * s - 8s is exact in fp32 (at most 12 significant bits),
-// so the only rounding is the final one to bf16.
-__device__ __forceinline__ u32x4_t dequant_w4_word_bf16(uint32_t w, float s) {
-  const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
-  const float m8s = -8.0f * s;
-  // (v_cvt_f32_ubyte0..3: one instruction per byte)
-  const float q0 = (float)(ev & 0xFFu), q2 = (float)((ev >> 8) & 0xFFu);
-  const float q4 = (float)((ev >> 16) & 0xFFu), q6 = (float)(ev >> 24);
-  const float q1 = (float)(od & 0xFFu), q3 = (float)((od >> 8) & 0xFFu);
-  const float q5 = (float)((od >> 16) & 0xFFu), q7 = (float)(od >> 24);
-  return u32x4_t{f2bf2_rn(__builtin_fmaf(q0, s, m8s), __builtin_fmaf(q4, s, m8s)),
-                 f2bf2_rn(__builtin_fmaf(q1, s, m8s), __builtin_fmaf(q5, s, m8s)),
-                 f2bf2_rn(__builtin_fmaf(q2, s, m8s), __builtin_fmaf(q6, s, m8s)),
-                 f2bf2_rn(__builtin_fmaf(q3, s, m8s), __builtin_fmaf(q7, s, m8s))};
-}
-
 // fp32 -> bf16, round to nearest even (inputs are finite).
 __device__ __forceinline__ uint16_t f2bf_rn(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-
-template <bool BF>
-__device__ __forceinline__ float ld16(const uint16_t* p, size_t i) {
-  return BF ? bf2f(p[i]) : h2f(p[i]);
 }
 
 template <bool BF>

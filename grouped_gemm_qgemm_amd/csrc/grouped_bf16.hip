@@ -9,13 +9,11 @@
 // streams the tile's columns of the expert's weights from HBM exactly once
 // while it multiplies every row of the block against them. All loads are raw
 // buffer loads (descriptor in SGPRs, uniform per-step offset).
-//   * Three weight paths. The default for each layout stages the weights
-//     through LDS, loaded as whole 128-byte row segments: the vector memory
-//     path spends one request per cache line an instruction touches, and a
-//     per-wave MFMA fragment can only cover half a line of each of 16 weight
-//     rows ([E, N, K]: 64-deep steps, ds_read_b128 fragments; [E, K, N]: LDS
-//     transpose reads). The first design loads [E, N, K] fragments straight
-//     into registers (16 bytes per lane per 32-deep step), 18 % slower.
+//   * Both weight layouts are staged through LDS, loaded as whole 128-byte
+//     row segments: the vector memory path spends one request per cache line
+//     an instruction touches, and a per-wave MFMA fragment can only cover half
+//     a line of each of 16 weight rows ([E, N, K]: 64-deep steps, ds_read_b128
+//     fragments; [E, K, N]: LDS transpose reads).
 //   * The rows' activation fragments are loaded once per workgroup (split over
 //     the waves, several steps ahead) and shared through an LDS ring in MFMA
 //     fragment order (read back as lane * 16 bytes: no bank conflicts).
@@ -39,19 +37,19 @@ constexpr int GBM = 16 * GMAXMT;
 
 }  // namespace
 
-// One work tile with MT row tiles. D = steps of prefetch (ring depth).
+// One work tile with MT row tiles over weights stored [E, K, N]. D = steps of
+// prefetch (ring depth).
 //
-// Every wave issues, per 32-deep K step, one 16-byte load of its own weight
-// fragment and (MT / 4, rounded up) of the tile's activation fragments. Loads
-// run D steps ahead. At step s each wave copies its activation fragments of
+// Every thread issues, per 32-deep K step, one 16-byte load of the step's
+// weight tile and every wave (MT / W, rounded up) of the tile's activation
+// fragments. Loads run D steps ahead. At step s each wave copies its activation fragments of
 // step s into the LDS ring, one barrier makes all of them visible, and each
 // wave multiplies every row tile against its own weight fragment. Because a
 // wave's loads are issued in step order and each step waits only for its own
 // (oldest) loads, the hardware's in-order load counter never forces a wave to
 // wait for a prefetch that lies further ahead.
 //
-// With the weights stored [E, K, N] (TB false) the workgroup loads the step's
-// 32 x 16W weight tile cooperatively (one 16-byte chunk per thread, whole
+// The workgroup loads the step's 32 x 16W weight tile cooperatively (one 16-byte chunk per thread, whole
 // 32W-byte row segments), stores it into a second LDS ring and every wave reads
 // its B fragment with two 16-bit LDS transpose reads: within each 16-lane
 // group, element j of lane i comes from the 8 bytes named by lane 4j + i / 4, at
@@ -120,7 +118,7 @@ __device__ __forceinline__ void grouped_store(uint16_t* __restrict__ C, const fl
 
 // P > 1: the loads of P consecutive steps are issued together (a weight row's
 // P * 64 contiguous bytes requested back to back).
-template <int W, int MT, int D, bool TB, int P, bool EPI>
+template <int W, int MT, int D, int P, bool EPI>
 __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                              u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
@@ -136,8 +134,8 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   // per-lane byte offsets, the step's K offset is uniform (an SGPR)
   const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)r_begin * K, (uint32_t)rows * K * 2);
   const __amdgpu_buffer_rsrc_t b_src = buffer_rsrc(B + (size_t)e * N * K, (uint32_t)N * K * 2);
-  // TB false: this thread's chunk of the step's weight tile (K rows past the
-  // expert's end read as zeros)
+  // this thread's chunk of the step's weight tile (K rows past the expert's end
+  // read as zeros)
   constexpr int WROW = WRing<W>::ROW;
   const int w_kr = threadIdx.x / (2 * W), w_c = threadIdx.x % (2 * W);
   const uint32_t wt_voff = (uint32_t)(w_kr * N + n0 + 8 * w_c) * 2;
@@ -154,20 +152,20 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
     a_frag[i] = wave + i * W;
     a_voff[i] = a_frag[i] < MT ? (uint32_t)(min(a_frag[i] * 16 + r16, rows - 1) * K + q * 8) * 2 : 0x80000000u;
   }
-  const uint32_t b_voff = TB ? (uint32_t)(min(n0 + wave * 16 + r16, N - 1) * K + q * 8) * 2 : wt_voff;
+  const uint32_t b_voff = wt_voff;
 
   u32x4_t ra[D][FPW], rb[D];
   // whole step s: K elements 32s .. 32s + 31
   auto load_step = [&](int s, u32x4_t (&a)[FPW], u32x4_t& b) {
     const uint32_t soff = (uint32_t)s * 64;
-    b = buffer_load16(b_src, b_voff, TB ? soff : (uint32_t)s * 32 * N * 2);
+    b = buffer_load16(b_src, b_voff, (uint32_t)s * 32 * N * 2);
 #pragma unroll
     for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i], soff);
   };
   // partial last step (K % 32 != 0): each lane's chunk start is clamped into its row
   auto load_tail = [&](u32x4_t (&a)[FPW], u32x4_t& b) {
     const uint32_t k2 = (uint32_t)max(0, min(nfull * 32, K - 8 - q * 8)) * 2;
-    b = TB ? buffer_load16(b_src, b_voff + k2, 0) : buffer_load16(b_src, b_voff, (uint32_t)nfull * 32 * N * 2);
+    b = buffer_load16(b_src, b_voff, (uint32_t)nfull * 32 * N * 2);
 #pragma unroll
     for (int i = 0; i < FPW; ++i) a[i] = buffer_load16(a_src, a_voff[i] + k2, 0);
   };
@@ -182,10 +180,10 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   auto step = [&](int slot, const u32x4_t (&a)[FPW], const u32x4_t& b) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) ring[(slot * GMAXMT + a_frag[i]) * kWave + lane] = a[i];
-    if constexpr (!TB) wring[slot * WRing<W>::SLOT + wt_lds] = b;
+    wring[slot * WRing<W>::SLOT + wt_lds] = b;
     __syncthreads();
-    u32x4_t bf = b;
-    if constexpr (!TB) {
+    u32x4_t bf;
+    {
       const unsigned char* base = reinterpret_cast<const unsigned char*>(wring + slot * WRing<W>::SLOT) + tr_off;
       typedef short s16x4_t __attribute__((ext_vector_type(4)));
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -220,12 +218,11 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
   for (int u = 0; u < D - 1; ++u)
     if (u < nfull - s0) step((s0 + u) & 1, ra[u], rb[u]);
-  // partial last step (K % 32 != 0): chunks past K enter the MFMA as zeros on
-  // both sides
+  // partial last step (K % 32 != 0): activation chunks past K enter the MFMA
+  // as zeros (weight rows past the expert's end read as zeros too)
   if (K & 31) {
     load_tail(ra[0], rb[0]);
     const bool past = nfull * 32 + q * 8 >= K;
-    if constexpr (TB) rb[0] = past ? u32x4_t{0u, 0u, 0u, 0u} : rb[0];
 #pragma unroll
     for (int i = 0; i < FPW; ++i) ra[0][i] = past ? u32x4_t{0u, 0u, 0u, 0u} : ra[0][i];
     step(nfull & 1, ra[0], rb[0]);
@@ -384,32 +381,17 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
   }
 }
 
-template <int W, int D, int OCC>
-static hipError_t launch_wl(const GroupedArgs& p, hipStream_t stream) {
-  if (!p.transpose_b) return hipErrorInvalidValue;
-  const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
-  const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
-  if (p.epi.flags)
-    hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
-                       p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                       p.epi);
-  else
-    hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
-                       p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                       p.epi);
-  return hipGetLastError();
-}
-
 template <int D, int P>
 constexpr int fit_group() { return D % P == 0 ? P : (D % 2 == 0 ? 2 : 1); }
 
-template <int W, int D, int OCC, bool TB, int P, bool EPI>
+// Persistent workgroups over the tile list, weights stored [E, K, N] (above).
+template <int W, int D, int OCC, int P, bool EPI>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
     int tiles_n, int per_xcd, Epilogue ep) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
-  __shared__ __attribute__((aligned(16))) u32x4_t wring[TB ? 1 : 2 * WRing<W>::SLOT];
+  __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * WRing<W>::SLOT];
 
   constexpr int GBN = 16 * W;   // columns per work tile: 16 per wave
   // every wave scans the group table itself (one group per lane), so no
@@ -432,65 +414,49 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     // same registers and about the same bytes in flight.
     constexpr int D5 = W >= 8 ? D : D / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile<W, 1, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 2: grouped_tile<W, 2, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 3: grouped_tile<W, 3, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 4: grouped_tile<W, 4, D, TB, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 5: grouped_tile<W, 5, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 6: grouped_tile<W, 6, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 7: grouped_tile<W, 7, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      default: grouped_tile<W, 8, D5, TB, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 1: grouped_tile<W, 1, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 2: grouped_tile<W, 2, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 3: grouped_tile<W, 3, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 4: grouped_tile<W, 4, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 5: grouped_tile<W, 5, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 6: grouped_tile<W, 6, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 7: grouped_tile<W, 7, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      default: grouped_tile<W, 8, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
     }
   }
 }
 
-template <int W, int D, int OCC, int P = 1>
-static hipError_t launch_g(const GroupedArgs& p, hipStream_t stream) {
-  const int wg_per_cu = OCC;
+// Launch: persistent workgroups, a whole number per XCD. Weights [E, N, K]:
+// eight waves (128 columns), four 64-deep steps in flight, two workgroups per
+// CU. Weights [E, K, N]: eight waves, eight 32-deep steps in flight issued in
+// pairs, one workgroup per CU.
+hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream) {
+  constexpr int W = 8;
   const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
-  const int grid = 8 * ((wg_per_cu * p.num_cus + 7) / 8);
-#define QG_GROUPED_LAUNCH(TBV, EPIV)                                                                      \
-  hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, TBV, P, EPIV>), dim3(grid), dim3(W * kWave), 0, stream, p.C, \
-                     p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,   \
-                     p.epi)
   if (p.transpose_b) {
-    if (p.epi.flags) QG_GROUPED_LAUNCH(true, true); else QG_GROUPED_LAUNCH(true, false);
+    constexpr int D = 4, OCC = 2;
+    const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
+    if (p.epi.flags)
+      hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                         p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                         p.epi);
+    else
+      hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                         p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                         p.epi);
   } else {
-    if (p.epi.flags) QG_GROUPED_LAUNCH(false, true); else QG_GROUPED_LAUNCH(false, false);
+    constexpr int D = 8, OCC = 1, P = 2;
+    const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
+    if (p.epi.flags)
+      hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, P, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                         p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                         p.epi);
+    else
+      hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, P, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
+                         p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
+                         p.epi);
   }
-#undef QG_GROUPED_LAUNCH
   return hipGetLastError();
-}
-
-hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream) {
-  switch (variant) {
-    // <waves (16 columns each), steps ahead, workgroups per CU>
-    case 0: return launch_g<4, 8, 2>(p, stream);
-    case 1: return launch_g<4, 4, 2>(p, stream);
-    case 2: return launch_g<4, 8, 1>(p, stream);
-    case 3: return launch_g<4, 12, 2>(p, stream);
-    case 4: return launch_g<4, 8, 3>(p, stream);
-    case 5: return launch_g<8, 8, 1>(p, stream);
-    case 6: return launch_g<8, 12, 1>(p, stream);
-    case 7: return launch_g<8, 16, 1>(p, stream);
-    // loads of 2 or 4 consecutive steps issued together
-    case 8: return launch_g<4, 8, 2, 2>(p, stream);
-    case 9: return launch_g<4, 8, 2, 4>(p, stream);
-    case 10: return launch_g<4, 12, 2, 2>(p, stream);
-    case 11: return launch_g<4, 12, 2, 4>(p, stream);
-    case 12: return launch_g<8, 8, 1, 2>(p, stream);
-    case 13: return launch_g<8, 8, 1, 4>(p, stream);
-    // transposed weights staged through LDS as whole 128-byte row segments
-    case 14: return launch_wl<4, 4, 2>(p, stream);
-    case 15: return launch_wl<4, 6, 2>(p, stream);
-    case 16: return launch_wl<4, 4, 3>(p, stream);
-    case 17: return launch_wl<8, 4, 1>(p, stream);
-    case 18: return launch_wl<8, 6, 1>(p, stream);
-    case 19: return launch_wl<8, 4, 2>(p, stream);
-    case 20: return launch_wl<8, 2, 2>(p, stream);
-    case 21: return launch_wl<4, 3, 3>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace qg

@@ -8,10 +8,10 @@
 // with 128 x 128 weight-scale blocks and 1 x 128 input-scale blocks. Tokens of
 // all sequences are one flat row dimension (raggedness costs nothing in the
 // GEMM); the sequence only matters for where a finished row is stored.
-//   * Three designs: 64 x 128 tiles (first), BM x 128 tiles with four waves
-//     (second), and the same tiles with 4 * BM / 48 waves (third, the default;
-//     described above its kernel). Each 128-deep K stage is exactly one scale
-//     block, so the stage's MFMA partial is scaled once, in fp32, by
+//   * Two designs for bf16 hidden rows: BM x 128 tiles with 4 * BM / 48 waves
+//     (the default, described above its kernel; at most 32 scale blocks of K)
+//     and 64 x 128 tiles for longer rows; a third for e4m3 hidden rows. Each
+//     128-deep K stage is exactly one scale block, so the stage's MFMA partial is scaled once, in fp32, by
 //     is[t][kb] * ws[kb][nb] (ws is uniform over the tile) and added to the
 //     accumulator. Activations are never re-rounded.
 //   * The fp8 weight tile [128 k][128 n] is fetched with coalesced 16-byte row
@@ -21,9 +21,9 @@
 //   * Hidden rows are staged through LDS with an XOR swizzle; double-buffered
 //     stages, one barrier per stage.
 //   * 16x16x32 bf16 MFMA, fp32 accumulation. Column tile t of a wave holds
-//     columns 4j + t (j = lane % 16) in the first design, so each lane finishes
-//     four adjacent columns of a row (one 8-byte write); the second and third
-//     designs use columns 2j + t and 4-byte writes.
+//     columns 4j + t (j = lane % 16) in the long-row design, so each lane
+//     finishes four adjacent columns of a row (one 8-byte write); the default
+//     uses columns 2j + t and 4-byte writes.
 //   * Epilogue: token t -> sequence b (binary search of the row offsets) ->
 //     position cache_lengths[b] + (t - offs[b]) -> (page_table entry, slot);
 //     the bf16 row lands in plane 0 (keys) of layer layer_idx. Nothing else in
@@ -221,196 +221,13 @@ __global__ __launch_bounds__(KTHR) void kproj_fp8_paged_kernel(
   }
 }
 
-// Second design: workgroup tile BM tokens x 128 columns with BM chosen on the
-// host so the tile count fits the CU count (4312 tokens -> 144-row tiles ->
-// 240 tiles on 256 CUs). Four waves each own 32 columns and all BM rows (wave
-// tile BM x 32, BM/16 MFMA row tiles), so every fp8 weight element is
-// converted once per workgroup and every hidden fragment is read by all four
-// waves from LDS. One 128-deep stage = one scale block: the stage's MFMA
-// partial is scaled once per element by is[t][kb] * ws[kb][nb] (is for the
-// tile's rows sits in LDS, transposed, so a lane's four rows are one 16-byte
-// read). Hidden rows and the transposed bf16 weights are double-buffered in LDS
-// and prefetched one stage ahead through registers.
+// transposed bf16 weight rows of the default design (one per column n): the
+// 16 rows {base + 2j + t} an MFMA fragment read touches get distinct chunks
 __device__ __forceinline__ int swz_bt(int n, int c) { return c ^ (((n >> 1) ^ (n >> 5)) & 15); }
 
-template <int BM>
-__global__ __launch_bounds__(256) void kproj_fp8_v2_kernel(
-    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
-    const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
-    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
-    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n) {
-  constexpr int MT = BM / 16;
-  constexpr int A_PER_T = BM * KCH / 256;
-  static_assert((BM * KCH) % 256 == 0, "A staging");
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * KCH];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][KBN * KCH];
-  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32 per pass
-  __shared__ long long row_dst[BM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane >> 4, r16 = lane & 15;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
-  const int nb = lin % tiles_n;
-  const int n0 = nb * KBN;
-  const int KB = Kh / KBK;
-
-  // staging maps
-  uint32_t a_off[A_PER_T];
-  int a_lds[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + i * 256;
-    const int row = id / KCH, ch = id % KCH;
-    a_off[i] = (uint32_t)(min(m0 + row, T - 1) * Kh + ch * 8);
-    a_lds[i] = row * KCH + swz_a(row, ch);
-  }
-  const int ng = tid & 7, kq = tid >> 3;                 // weight block: 4 K rows x 16 columns
-  const uint32_t w_off = (uint32_t)(4 * kq * N + n0 + 16 * ng);
-
-  struct ARegs {
-    u32x4_t a[A_PER_T];
-  };
-  u32x4_t rw[4];
-  auto load_a = [&](int kb, ARegs& r) {
-    const int k0 = kb * KBK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) r.a[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
-  };
-  auto load_w = [&](int kb) {
-    const uint8_t* wb = W + (size_t)(kb * KBK) * N;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rw[j] = *reinterpret_cast<const u32x4_t*>(wb + w_off + j * N);
-  };
-  auto store_stage = [&](int buf, const ARegs& rr) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = rr.a[i];
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      float2_t f[4][2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t word = rw[r][c4];
-        f[r][0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-        f[r][1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = 16 * ng + 4 * c4 + b;
-        const float x0 = f[0][b >> 1][b & 1], x1 = f[1][b >> 1][b & 1];
-        const float x2 = f[2][b >> 1][b & 1], x3 = f[3][b >> 1][b & 1];
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 1)]) + (kq & 1) * 2;
-        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{bf16pair_hi(x0, x1), bf16pair_hi(x2, x3)};
-      }
-    }
-  };
-
-  // input scales of the tile's rows, transposed to [kb][row]
-  for (int e = tid; e < KB * BM; e += 256) {
-    const int row = e % BM, kb = e / BM;
-    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
-  }
-
-  float4_t acc[MT][2];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // one 128-deep stage out of LDS buffer `buf`: MFMA partial, then scaled add
-  auto compute = [&](int kb, int buf) {
-    float4_t part[MT][2];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t bf[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int n = wave * 32 + 2 * r16 + t;   // column tile t of the wave: lane j holds column 2j + t
-        bf[t] = lds_b[buf][n * KCH + swz_bt(n, s * 4 + q)];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + r16;
-        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
-        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
-        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
-      }
-      // keep each K step's fragment reads next to its MFMAs (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + mt * 16 + q * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f = is4[i] * wsv;
-        acc[mt][0][i] += f * part[mt][0][i];
-        acc[mt][1][i] += f * part[mt][1][i];
-      }
-    }
-  };
-
-  // Stage kb is multiplied out of LDS buffer kb & 1 while stage kb+1 loads into
-  // registers; it is converted into the other buffer after the multiply. One
-  // barrier per stage: the buffer written at stage kb was last read at kb-1.
-  ARegs ra;
-  load_w(0);
-  load_a(0, ra);
-  store_stage(0, ra);
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
-    if (more) {
-      load_w(kb + 1);
-      load_a(kb + 1, ra);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kb, kb & 1);
-    if (more) store_stage((kb + 1) & 1, ra);
-    __syncthreads();
-  }
-
-  if (tid < BM) {
-    const int t = m0 + tid;
-    long long dst = -1;
-    if (t < T) {
-      int lo = 0, hi = batch;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
-      }
-      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
-      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
-      const int slot = pos % page_size;
-      dst = ((((long long)layer * 2 + 0) * num_pages + page) * page_size + slot) * (long long)N;
-    }
-    row_dst[tid] = dst;
-  }
-  __syncthreads();
-  const int col = n0 + wave * 32 + 2 * r16;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long d = row_dst[mt * 16 + q * 4 + i];
-      if (d >= 0) {
-        const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
-        *reinterpret_cast<uint32_t*>(blocks + d + col) = v;
-      }
-    }
-  }
-}
-
-// Epilogue shared by the third and fourth designs: each token row of the tile
+// Epilogue shared by the default and the e4m3-hidden designs: each token row of the tile
 // goes to (layer, plane, page, slot) of the cache, as bf16 or as e4m3 codes with
-// per-run scales (see the third design). acc holds a wave's 48 x 32 tile: rows
+// per-run scales (see the default design). acc holds a wave's 48 x 32 tile: rows
 // wm * 48 + mt * 16 + 4q + i, columns wn * 32 + 2 r16 + j (BLK false: a lane owns
 // two adjacent columns) or wn * 32 + 16 j + r16 (BLK true). `scratch` is LDS of
 // at least 4 * BM floats that no wave reads any more.
@@ -522,8 +339,8 @@ __device__ __forceinline__ void kproj_store_tile(
   }
 }
 
-// Third design: the second design's tiles (BM = 48 * WM rows x 128 columns,
-// one 128-deep stage per scale block) with WM x 4 waves, each owning a 48 x 32
+// Default design: BM = 48 * WM rows x 128 columns (one 128-deep stage per
+// scale block) with WM x 4 waves, each owning a 48 x 32
 // wave tile (three 16-row by two 16-column MFMA tiles). With WM = 3 (the
 // 144-row tiles that fill 256 CUs at 4312 tokens) a SIMD runs three waves, so
 // one wave's LDS and load waits are covered by the others' MFMAs; with one wave
@@ -537,7 +354,7 @@ __device__ __forceinline__ void kproj_store_tile(
 // (nearest even); a run of 32 columns is one wave's columns of a row, spread over
 // the 16 lanes that share its rows, so amax is a 16-lane shuffle reduction, and
 // runs of 64 or 128 combine two or four waves through LDS.
-template <int WM, int PD, bool Q8>
+template <int WM, bool Q8>
 __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
     const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
@@ -585,17 +402,14 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
   const int ng = tid & 7, kq = (tid >> 3) & (WT / 8 - 1);  // 16-column group, K-row group
   const uint32_t w_off = (uint32_t)(RPT * kq * N + n0 + 16 * ng);
 
-  // staging registers: PD stages of loads in flight
-  u32x4_t ra[PD][A_PER_T];
-  u32x4_t rw[PD][RPT];
-  // With two stages in flight every thread issues every load (threads past the
-  // weight stagers read weight rows they never store): the compiler's in-order
-  // load counting then sees one fixed sequence and waits only for the older set.
+  // staging registers: the next stage's loads are in flight while a stage is multiplied
+  u32x4_t ra[1][A_PER_T];
+  u32x4_t rw[1][RPT];
   auto load_stage = [&](int kb, u32x4_t (&ra)[A_PER_T], u32x4_t (&rw)[RPT]) {
     const int k0 = kb * KBK;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
-    if (PD == 2 || wstage) {
+    if (wstage) {
       const uint8_t* wb = W + (size_t)k0 * N;
 #pragma unroll
       for (int r = 0; r < RPT; ++r) rw[r] = *reinterpret_cast<const u32x4_t*>(wb + w_off + r * N);
@@ -675,48 +489,26 @@ __global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
     }
   };
 
-  if constexpr (PD == 1) {
-    load_stage(0, ra[0], rw[0]);
-    store_stage(0, ra[0], rw[0]);
+  load_stage(0, ra[0], rw[0]);
+  store_stage(0, ra[0], rw[0]);
+  __syncthreads();
+  for (int kb = 0; kb < KB; ++kb) {
+    const bool more = kb + 1 < KB;
+    if (more) load_stage(kb + 1, ra[0], rw[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kb, kb & 1);
+    if (more) store_stage((kb + 1) & 1, ra[0], rw[0]);
     __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-      const bool more = kb + 1 < KB;
-      if (more) load_stage(kb + 1, ra[0], rw[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(kb, kb & 1);
-      if (more) store_stage((kb + 1) & 1, ra[0], rw[0]);
-      __syncthreads();
-    }
-  } else {
-    // two stages in flight: stage kb + 2 is requested while stage kb is
-    // multiplied, stage kb + 1 (already in registers) is stored after it
-    // (loads past the last stage re-read it; the copies stored from them are never read)
-    load_stage(0, ra[0], rw[0]);
-    load_stage(min(1, KB - 1), ra[1], rw[1]);
-    store_stage(0, ra[0], rw[0]);
-    __syncthreads();
-    for (int kb = 0; kb < KB; kb += 2) {
-      load_stage(min(kb + 2, KB - 1), ra[0], rw[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(kb, 0);
-      store_stage(1, ra[1], rw[1]);
-      __syncthreads();
-      load_stage(min(kb + 3, KB - 1), ra[1], rw[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kb + 1 < KB) compute(kb + 1, 1);
-      store_stage(0, ra[0], rw[0]);
-      __syncthreads();
-    }
   }
 
   kproj_store_tile<WM * 48, Q8>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch, max_pages,
                                  num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
-// Fourth design: fp8 (e4m3) hidden rows, so both operands are fp8 and one
+// e4m3-hidden design: fp8 (e4m3) hidden rows, so both operands are fp8 and one
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) covers a 16 x 16 output
 // tile over a whole 128-deep scale block; its fp32 result is scaled by
-// is[t][kb] * ws[kb][nb] and added to the accumulator, as in the third design,
+// is[t][kb] * ws[kb][nb] and added to the accumulator, as in the default design,
 // whose tiles, waves and epilogue it shares (BM = 48 * WM rows x 128 columns,
 // 48 x 32 wave tiles).
 //   * Both tiles stay fp8 in LDS, copied as they are: hidden rows [BM][128 B]
@@ -891,34 +683,23 @@ static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int WM, int PD = 1>
+template <int WM>
 static hipError_t launch_kproj_v3(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
   if (p.fp8)
-    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD, true>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, true>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
                        p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
                        p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
                        (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
                        p.kv_scales, p.qgran);
   else
-    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, PD, false>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, false>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
                        p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
                        p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
                        (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
                        nullptr, 0);
-  return hipGetLastError();
-}
-
-template <int BM>
-static hipError_t launch_kproj_v2(const KProjArgs& p, hipStream_t stream) {
-  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
-  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
-  hipLaunchKernelGGL((kproj_fp8_v2_kernel<BM>), dim3(grid), dim3(256), 0, stream, p.hidden, p.row_offsets,
-                     p.weight, p.input_scale, p.weight_scale, static_cast<uint16_t*>(p.blocks), p.cache_lengths, p.page_table, (int)p.T,
-                     (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
-                     (int)p.layer_idx, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -941,65 +722,26 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
   return cand[n - 1];
 }
 
-hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream) {
+hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream) {
+  static const int cand[] = {48, 96, 144};
   if (p.hidden_fp8) {
-    // fourth design: 48, 96 or 144-row tiles (auto: 0, 24-27; forced: 21-23) with
-    // PD stages in flight (24-27: PD = 1..4; otherwise 2, which measured 10 %
-    // faster than 1 and level with 3 and 4 at 4312 tokens)
+    // e4m3 hidden rows: 48, 96 or 144-row tiles, two stages of loads in flight
     if (p.Kh / KBK > 32) return hipErrorNotSupported;
-    int wm = variant == 21 ? 1 : (variant == 22 ? 2 : (variant == 23 ? 3 : 0));
-    const int pd = variant >= 24 && variant <= 27 ? variant - 23 : 2;
-    if (wm == 0) {
-      static const int cand[] = {48, 96, 144};
-      wm = pick_kproj_rows(p, cand, 3) / 48;
+    switch (pick_kproj_rows(p, cand, 3) / 48) {
+      case 1: return launch_kproj_f8f8<1, 2>(p, stream);
+      case 2: return launch_kproj_f8f8<2, 2>(p, stream);
+      default: return launch_kproj_f8f8<3, 2>(p, stream);
     }
-#define QG_F8F8(W)                                            \
-  switch (pd) {                                               \
-    case 1: return launch_kproj_f8f8<W, 1>(p, stream);        \
-    case 2: return launch_kproj_f8f8<W, 2>(p, stream);        \
-    case 4: return launch_kproj_f8f8<W, 4>(p, stream);        \
-    default: return launch_kproj_f8f8<W, 3>(p, stream);       \
   }
-    switch (wm) {
-      case 1: QG_F8F8(1)
-      case 2: QG_F8F8(2)
-      default: QG_F8F8(3)
-    }
-#undef QG_F8F8
-  }
-  const bool wide = p.fp8 || p.n_plane != p.N;   // fp8 cache or several planes: the third design only
-  if (p.Kh / KBK > 32) {                // the v2/v3 kernels keep at most 32 input-scale blocks in LDS
-    if (wide) return hipErrorNotSupported;
-    variant = 1;
-  }
-  if (variant == 0) variant = 6;
-  if (wide && variant < 6) return hipErrorNotSupported;
-  if (variant == 10) return launch_kproj_v3<3, 2>(p, stream);
-  if (variant == 11) return launch_kproj_v3<2, 2>(p, stream);
-  if (variant >= 6) {
-    // third design: 48, 96 or 144-row tiles (auto), or forced
-    int wm = variant == 7 ? 1 : (variant == 8 ? 2 : (variant == 9 ? 3 : 0));
-    if (wm == 0) {
-      static const int cand[] = {48, 96, 144};
-      wm = pick_kproj_rows(p, cand, 3) / 48;
-    }
-    switch (wm) {
+  if (p.Kh / KBK <= 32) {   // default design: at most 32 input-scale blocks in LDS
+    switch (pick_kproj_rows(p, cand, 3) / 48) {
       case 1: return launch_kproj_v3<1>(p, stream);
       case 2: return launch_kproj_v3<2>(p, stream);
       default: return launch_kproj_v3<3>(p, stream);
     }
   }
-  if (variant >= 2) {
-    static const int cand[] = {48, 64, 96, 128, 144};
-    int bm = variant == 2 ? pick_kproj_rows(p, cand, 5) : (variant == 3 ? 128 : (variant == 4 ? 64 : 144));
-    switch (bm) {
-      case 48: return launch_kproj_v2<48>(p, stream);
-      case 64: return launch_kproj_v2<64>(p, stream);
-      case 96: return launch_kproj_v2<96>(p, stream);
-      case 128: return launch_kproj_v2<128>(p, stream);
-      default: return launch_kproj_v2<144>(p, stream);
-    }
-  }
+  // longer hidden rows: the long-row design (bf16 cache, keys only)
+  if (p.fp8 || p.n_plane != p.N) return hipErrorNotSupported;
   const int tiles_m = (int)((p.T + KBM - 1) / KBM), tiles_n = (int)(p.N / KBN);
   const int tiles = tiles_m * tiles_n;
   const int grid = ((tiles + 7) / 8) * 8;

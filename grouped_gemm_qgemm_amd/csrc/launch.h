@@ -79,17 +79,17 @@ struct KProjArgs {
   int hidden_fp8 = 0;            // hidden is e4m3 [T, Kh] (then `hidden` points at bytes)
 };
 
-// Decode-shaped W4A16 (M <= 16). `variant` picks columns-per-lane and waves.
-hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream);
+// Decode-shaped W4A16 (M <= 16).
+hipError_t launch_w4_decode(const W4Args& p, hipStream_t stream);
 
-// Prefill-shaped W4A16 (M > 16).
-hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream);
+// Prefill-shaped W4A16 (M > 16); num_cus picks the launch shape.
+hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream);
 
-hipError_t launch_grouped_bf16(const GroupedArgs& p, int variant, hipStream_t stream);
+hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream);
 
 // Grouped W4A16 (int4 experts, fp16 activations).
-hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t stream);
+hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream);
 
-hipError_t launch_kproj_fp8(const KProjArgs& p, int variant, hipStream_t stream);
+hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream);
 
 }  // namespace qg

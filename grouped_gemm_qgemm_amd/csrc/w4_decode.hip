@@ -22,117 +22,10 @@
 
 namespace qg {
 
-// Steps are 32-deep K slices (one MFMA); GB whole groups are loaded per batch.
-// All loads are unconditional (addresses clamped into range) so the compiler
-// issues them back to back with no divergent branches between them; lanes or
-// groups that are out of range contribute zero through a zero scale.
-template <int CPL, int NW, int SPG, int GB>
-__global__ __launch_bounds__(NW * kWave) void w4_decode_kernel(
-    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int xcd_remap) {
-  constexpr int SN = 16 * CPL;  // columns per workgroup
-  __shared__ float red[NW][16][SN];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int quarter = lane >> 4;  // which packed row of a step / which 8-wide K slot
-  const int col16 = lane & 15;
-
-  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // run of strips so neighbouring strips share its L2 (xcd_remap: strips per XCD).
-  int strip = blockIdx.x;
-  if (xcd_remap) strip = (blockIdx.x & 7) * xcd_remap + (blockIdx.x >> 3);
-  const int n0 = strip * SN;
-  const int ncol_raw = n0 + CPL * col16;  // first of this lane's CPL columns
-  const bool col_ok = ncol_raw < N;       // N % 8 == 0: all CPL columns in range together
-  const int ncol = col_ok ? ncol_raw : N - CPL;
-  const int m = col16 < M ? col16 : M - 1;  // A row this lane supplies (rows >= M never stored)
-
-  const int groups = K / (SPG * 32);
-  const int g_begin = (wave * groups) / NW;
-  const int g_end = ((wave + 1) * groups) / NW;
-
-  float4_t acc[CPL];
-#pragma unroll
-  for (int t = 0; t < CPL; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int g0 = g_begin; g0 < g_end; g0 += GB) {
-    uint32_t w[GB][SPG][CPL];
-    u32x4_t af[GB][SPG];
-    uint16_t sc[GB][CPL];
-    // Issue every load of the batch, group by group, before any arithmetic.
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      const int g = g0 + j < g_end ? g0 + j : g_end - 1;
-      if constexpr (CPL == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(S + (size_t)g * N + ncol);
-        sc[j][0] = v.x & 0xFFFF; sc[j][1] = v.x >> 16; sc[j][2] = v.y & 0xFFFF; sc[j][3] = v.y >> 16;
-      } else if constexpr (CPL == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(S + (size_t)g * N + ncol);
-        sc[j][0] = v & 0xFFFF; sc[j][1] = v >> 16;
-      } else {
-        sc[j][0] = S[(size_t)g * N + ncol];
-      }
-#pragma unroll
-      for (int s = 0; s < SPG; ++s) {
-        const int step = g * SPG + s;
-        const uint32_t* bp = B + (size_t)(step * 4 + quarter) * N + ncol;
-        if constexpr (CPL == 4) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp);
-          w[j][s][0] = v.x; w[j][s][1] = v.y; w[j][s][2] = v.z; w[j][s][3] = v.w;
-        } else if constexpr (CPL == 2) {
-          const u32x2_t v = *reinterpret_cast<const u32x2_t*>(bp);
-          w[j][s][0] = v.x; w[j][s][1] = v.y;
-        } else {
-          w[j][s][0] = *bp;
-        }
-        af[j][s] = *reinterpret_cast<const u32x4_t*>(A + (size_t)m * K + step * 32 + quarter * 8);
-      }
-    }
-    // Keep the scheduler from sinking loads into the arithmetic below: all of
-    // the batch's HBM reads must be in flight before the first wait.
-    __builtin_amdgcn_sched_barrier(0);
-    // Arithmetic: per group, MFMA chain on (q - 8), then one scaled FMA.
-#pragma unroll
-    for (int j = 0; j < GB; ++j) {
-      float4_t part[CPL];
-#pragma unroll
-      for (int t = 0; t < CPL; ++t) part[t] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < SPG; ++s) {
-        const u32x4_t a = permute_k_0415(af[j][s]);
-#pragma unroll
-        for (int t = 0; t < CPL; ++t) part[t] = mfma16x16x32_f16(a, dequant_w4_word(w[j][s][t]), part[t]);
-      }
-      // Groups past this wave's share and columns past N contribute nothing; the
-      // mask is applied here, after the loads, so it never waits on them early.
-      const bool keep = col_ok && (g0 + j < g_end);
-#pragma unroll
-      for (int t = 0; t < CPL; ++t) acc[t] += (keep ? h2f(sc[j][t]) : 0.f) * part[t];
-    }
-  }
-
-  // Cross-wave reduction in a fixed order.
-#pragma unroll
-  for (int t = 0; t < CPL; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][quarter * 4 + i][CPL * col16 + t] = acc[t][i];
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * SN; e += NW * kWave) {
-    const int row = e / SN, col = e % SN;
-    float sum = 0.f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) sum += red[v][row][col];
-    if (row < M && n0 + col < N) C[(size_t)row * N + n0 + col] = f2h_rn(sum);
-  }
-}
-
-// Variant with the activations staged through LDS. Each wave copies the A
-// columns of its own K batch (MROWS >= M rows, 512 columns) into a private LDS
-// slice with one coalesced 16-byte load per lane per row, reordering the K slots
-// once on the way in; the MFMA A fragments are then read from LDS. For small M
-// this removes the per-step A loads and K-slot permutes of the variant above
-// (rows >= M are never loaded), and the fused mask/bias unpack trims the B path.
+// The activations are staged through LDS: each wave copies the A columns of
+// its own K batch (MROWS >= M rows) into a private LDS slice with one coalesced
+// 16-byte load per lane per row, reordering the K slots once on the way in;
+// the MFMA A fragments are then read from LDS (rows >= M are never loaded).
 //
 // BF: bf16 activations, scales and output. A packed code q then enters the bf16
 // MFMA as 128 + q (exact: the pair is 0x4300 | q in each half), and one more
@@ -438,53 +331,7 @@ static hipError_t launch_lds(const W4Args& p, hipStream_t stream) {
   return launch_lds_spg<CPL, NW, 16>(p, stream);
 }
 
-template <int CPL, int NW, int SPG>
-static hipError_t launch_cfg(const W4Args& p, hipStream_t stream) {
-  constexpr int SN = 16 * CPL;
-  const int strips = (int)((p.N + SN - 1) / SN);
-  // strips per XCD when they divide evenly, else 0 (no remap); passing it keeps
-  // the kernels off the hidden grid-size arguments, whose 256 extra kernarg bytes
-  // cost launch time
-  const int remap = (strips % 8 == 0) ? strips / 8 : 0;
-  constexpr int GB = SPG >= 4 ? 4 : 16 / SPG;  // 16 steps of loads per batch (gs <= 128)
-  hipLaunchKernelGGL((w4_decode_kernel<CPL, NW, SPG, GB>), dim3(strips), dim3(NW * kWave), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, remap);
-  return hipGetLastError();
-}
-
-template <int CPL, int NW>
-static hipError_t launch_spg(const W4Args& p, hipStream_t stream) {
-  switch (p.group_size) {
-    case 32: return launch_cfg<CPL, NW, 1>(p, stream);
-    case 64: return launch_cfg<CPL, NW, 2>(p, stream);
-    case 128: return launch_cfg<CPL, NW, 4>(p, stream);
-    case 256: return launch_cfg<CPL, NW, 8>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// Variants: (columns per lane, waves per workgroup).
-hipError_t launch_w4_decode(const W4Args& p, int variant, hipStream_t stream) {
-  if ((p.bf16 || p.epi.flags) && variant < 9) return hipErrorInvalidValue;   // bf16, epilogues: LDS-staged kernel
-  switch (variant) {
-    case 0: return launch_spg<1, 8>(p, stream);
-    case 1: return launch_spg<2, 8>(p, stream);
-    case 2: return launch_spg<4, 8>(p, stream);
-    case 3: return launch_spg<1, 4>(p, stream);
-    case 4: return launch_spg<2, 16>(p, stream);
-    case 5: return launch_spg<1, 16>(p, stream);
-    case 6: return launch_spg<2, 4>(p, stream);
-    case 7: return launch_spg<4, 4>(p, stream);
-    case 8: return launch_spg<4, 16>(p, stream);
-    case 9: return launch_lds<1, 8>(p, stream);
-    case 10: return launch_lds<2, 8>(p, stream);
-    case 11: return launch_lds<1, 4>(p, stream);
-    case 12: return launch_lds<2, 4>(p, stream);
-    case 13: return launch_lds<4, 4>(p, stream);
-    case 14: return launch_lds<1, 16>(p, stream);
-    case 15: return launch_lds<2, 16>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
+// One 16-column strip per workgroup of eight waves.
+hipError_t launch_w4_decode(const W4Args& p, hipStream_t stream) { return launch_lds<1, 8>(p, stream); }
 
 }  // namespace qg

@@ -1,24 +1,15 @@
 // MFMA-tiled W4A16 GEMM for M > 16 (the prefill-shaped case of the group-
 // quantized GEMM on the Modular page "multistage_gemm_q"; Parameters:
 // group_size, pack_factor; its Description's multi-stage shared-memory
-// pipeline becomes an LDS double buffer here).
+// pipeline becomes an LDS double buffer here), and the grouped (MoE) form of
+// the same GEMM over the routing of the page "grouped_matmul_sm100_persistent"
+// (Args: a_offsets, expert_ids, expert_usage_stats).
 //
-// Workgroup tile BM x BN, K advanced BK = 64 at a time:
-//   * A (fp16) and the packed B words of the next K tile are fetched from HBM
-//     into registers while the current tile is multiplied out of LDS, then
-//     written to the other LDS buffer (one barrier per K tile).
-//   * A rows sit in LDS with an XOR swizzle on their 16-byte chunks so the
-//     MFMA operand reads of 16 consecutive rows hit distinct banks; the eight
-//     fp16 values of each chunk are stored in the K-slot order (0,4,1,5,2,6,3,7)
-//     that the in-register 4-bit unpack produces for B.
-//   * Each wave reads 16 bytes of packed B per lane per 32-deep K step: four
-//     words = four MFMA column tiles (lane j of tile t is column 4j + t), so its
-//     fp16 results for one row come out as four adjacent columns.
-//   * Dequantization happens once per wave per word, in VGPRs: nibble -> fp16
-//     (q - 8) exactly, then one packed multiply by the column's group scale.
-//   * 16x16x32 fp16 MFMA, fp32 accumulation, fp16 round-to-nearest-even store.
-//   * Workgroup ids are remapped so each XCD works on a contiguous run of tiles,
-//     M-fastest, sharing B panels (and A panels) in its own L2.
+// One tile body (w4_mfma_tile) serves both kernels: a BM x BN output tile, K
+// advanced BK = 64 at a time, A and the packed B words of the next stage
+// fetched with raw buffer loads into registers while the current stage is
+// multiplied out of LDS, 32x32x16 MFMAs with fp32 accumulation, and the
+// 4-bit codes unpacked in VGPRs. Its comment below gives the details.
 #include "device_common.h"
 #include "launch.h"
 
@@ -30,595 +21,51 @@ constexpr int BK = 64;            // K per LDS stage (two 32-deep MFMA steps)
 constexpr int CHUNKS = BK / 8;    // 16-byte chunks per A row in LDS
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
-// transposed fp16 B rows: the 16 rows {4j + t} one fragment read touches get
-// distinct chunk positions
-__device__ __forceinline__ int swzb(int n, int chunk) { return chunk ^ ((n >> 2) & 7); }
 
 }  // namespace
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_kernel(
-    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
-  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
-  constexpr int TM = BM / WAVES_M;       // rows per wave
-  constexpr int TN = BN / WAVES_N;       // columns per wave
-  constexpr int MT = TM / 16;            // MFMA row tiles per wave
-  constexpr int NB = TN / 64;            // 64-column blocks per wave (4 MFMA column tiles each)
-  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
-  constexpr int A_CHUNKS = BM * CHUNKS;              // 16-byte chunks of A per stage
-  constexpr int A_PER_T = A_CHUNKS / NTHR;
-  static_assert(A_CHUNKS % NTHR == 0, "A chunks per thread");
-  constexpr int B_CHUNKS = (BK / 8) * (BN / 4);      // 16-byte chunks of packed B per stage
-  constexpr int B_PER_T = B_CHUNKS >= NTHR ? B_CHUNKS / NTHR : 1;
-  static_assert(B_CHUNKS % NTHR == 0 || NTHR % B_CHUNKS == 0, "B chunks per thread");
-
-  __shared__ __attribute__((aligned(16))) uint32_t lds_a[2][BM * BK / 2];     // fp16 pairs
-  __shared__ __attribute__((aligned(16))) uint32_t lds_b[2][(BK / 8) * BN];   // packed words
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous
-  // range of the M-fastest linear tile order.
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin % tiles_m) * BM;
-  const int n0 = (lin / tiles_m) * BN;
-
-  // ---- global -> register staging (addresses clamped into range) ----
-  int a_row[A_PER_T], a_chunk[A_PER_T];
-  const uint16_t* a_src[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + i * NTHR;
-    a_row[i] = id / CHUNKS;
-    a_chunk[i] = id % CHUNKS;
-    const int gr = min(m0 + a_row[i], M - 1);
-    a_src[i] = A + (size_t)gr * K + a_chunk[i] * 8;
-  }
-  const bool b_loader = tid < B_CHUNKS;
-  int b_kp[B_PER_T], b_c4[B_PER_T], b_col[B_PER_T];
-#pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) {
-    const int id = (tid + i * NTHR) % B_CHUNKS;
-    b_kp[i] = id / (BN / 4);
-    b_c4[i] = id % (BN / 4);
-    b_col[i] = min(n0 + 4 * b_c4[i], N - 4);
-  }
-  const int kp_total = K / 8;
-
-  // this lane's scale columns: 4 adjacent columns per 64-column block
-  int s_col[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s_col[nb] = min(n0 + wn * TN + nb * 64 + 4 * (lane & 15), N - 4);
-
-  u32x4_t ra[A_PER_T];
-  u32x4_t rb[B_PER_T];
-
-  auto load_stage = [&](int kt, u32x2_t (&sc)[2][NB]) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int kk = min(k0 + a_chunk[i] * 8, K - 8) - a_chunk[i] * 8;
-      ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + kk);
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-      const int kp = min(k0 / 8 + b_kp[i], kp_total - 1);
-      rb[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)kp * N + b_col[i]);
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int g = min(k0 + 32 * s, K - 1) / group_size;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[s][nb] = *reinterpret_cast<const u32x2_t*>(S + (size_t)g * N + s_col[nb]);
-    }
-  };
-
-  auto store_stage = [&](int kt, int buf) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      u32x4_t v = permute_k_0415(ra[i]);
-      if (k0 + a_chunk[i] * 8 >= K) v = u32x4_t{0u, 0u, 0u, 0u};  // K tail
-      *reinterpret_cast<u32x4_t*>(&lds_a[buf][(a_row[i] * CHUNKS + swz(a_row[i], a_chunk[i])) * 4]) = v;
-    }
-    if (b_loader) {
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) *reinterpret_cast<u32x4_t*>(&lds_b[buf][b_kp[i] * BN + 4 * b_c4[i]]) = rb[i];
-    }
-  };
-
-  float4_t acc[MT][NB * 4];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NB * 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = (K + BK - 1) / BK;
-  u32x2_t sc_cur[2][NB], sc_nxt[2][NB];
-  load_stage(0, sc_cur);
-  store_stage(0, 0);
-  __syncthreads();
-
-  const int q = lane >> 4;      // K slot group within a 32-deep step
-  const int r16 = lane & 15;    // row / column index within an MFMA tile
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load_stage(kt + 1, sc_nxt);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      // B: 16 bytes per lane per 64-column block -> 4 column tiles
-      u32x4_t bq[NB * 4];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(
-            &lds_b[cur][(s * 4 + q) * BN + wn * TN + nb * 64 + 4 * r16]);
-        const uint32_t words[4] = {wv.x, wv.y, wv.z, wv.w};
-        const uint32_t sp[2] = {sc_cur[s][nb].x, sc_cur[s][nb].y};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t sh = (sp[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-          const half2_t s2 = __builtin_bit_cast(half2_t, sh | (sh << 16));
-          const u32x4_t d = dequant_w4_word(words[t]);
-          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
-          bq[nb * 4 + t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * TM + mt * 16 + r16;
-        const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
-            &lds_a[cur][(row * CHUNKS + swz(row, s * 4 + q)) * 4]);
-#pragma unroll
-        for (int j = 0; j < NB * 4; ++j) acc[mt][j] = mfma16x16x32_f16(av, bq[j], acc[mt][j]);
-      }
-    }
-    if (more) store_stage(kt + 1, cur ^ 1);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
-  }
-
-  // ---- epilogue: fp32 -> fp16 (RNE), four adjacent columns per 8-byte store ----
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
-        if (col >= N) continue;
-        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
-        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
-        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
-      }
-    }
-  }
-}
-
-// Second design: the workgroup dequantizes each packed word once (not once per
-// wave) into an fp16 copy of the B tile in LDS, stored transposed ([n][k], k
-// contiguous) so both MFMA operands are plain 16-byte LDS reads; 8 waves
-// (2 per SIMD) overlap one wave's VALU work with the other's MFMAs; global
-// loads run two K tiles ahead through a pair of register sets.
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave) void w4_prefill_lds_kernel(
-    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
-  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
-  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
-  constexpr int MT = TM / 16, NT = TN / 16;
-  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
-  constexpr int A_PER_T = BM * CHUNKS / NTHR;               // 16-byte A chunks per thread per stage
-  static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
-  constexpr int WORDS = (BK / 8) * BN;                      // packed words per stage
-  constexpr int W_PER_T = WORDS / NTHR;                     // 1, 2 or 4 adjacent columns per thread
-  static_assert(WORDS % NTHR == 0 && (W_PER_T == 1 || W_PER_T == 2 || W_PER_T == 4), "B staging");
-
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BN * CHUNKS];   // [n][k chunk]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int q = lane >> 4, r16 = lane & 15;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin % tiles_m) * BM;
-  const int n0 = (lin / tiles_m) * BN;
-
-  // A staging map
-  int a_row[A_PER_T], a_ch[A_PER_T];
-  uint32_t a_off[A_PER_T];
-  const uint16_t* a_base = A;
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + i * NTHR;
-    a_row[i] = id / CHUNKS;
-    a_ch[i] = id % CHUNKS;
-    a_off[i] = (uint32_t)(min(m0 + a_row[i], M - 1) * K + a_ch[i] * 8);
-  }
-  // B staging map: packed row kp of the stage, W_PER_T adjacent columns
-  constexpr int CPT = BN / W_PER_T;   // threads per packed row
-  const int b_kp = tid / CPT;
-  const int b_c = (tid % CPT) * W_PER_T;
-  const int b_col = min(n0 + b_c, N - W_PER_T);
-  const int kp_total = K / 8;
-
-  struct Regs {
-    u32x4_t a[A_PER_T];
-    uint32_t w[W_PER_T];
-    uint32_t s[(W_PER_T + 1) / 2];
-  };
-  auto load_stage = [&](int kt, Regs& r) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int kk = min(k0 + a_ch[i] * 8, K - 8) - a_ch[i] * 8;
-      r.a[i] = *reinterpret_cast<const u32x4_t*>(a_base + (a_off[i] + kk));
-    }
-    const int kp = min(k0 / 8 + b_kp, kp_total - 1);
-    const uint32_t* bp = B + (size_t)kp * N + b_col;
-    if constexpr (W_PER_T == 4) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp);
-      r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-    } else if constexpr (W_PER_T == 2) {
-      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(bp);
-      r.w[0] = v.x; r.w[1] = v.y;
-    } else {
-      r.w[0] = *bp;
-    }
-    const int g = (kp * 8) / group_size;
-    const uint16_t* sp = S + (size_t)g * N + b_col;
-    if constexpr (W_PER_T == 4) {
-      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sp);
-      r.s[0] = v.x; r.s[1] = v.y;
-    } else if constexpr (W_PER_T == 2) {
-      r.s[0] = *reinterpret_cast<const uint32_t*>(sp);
-    } else {
-      r.s[0] = *sp;
-    }
-  };
-  auto store_stage = [&](int kt, int buf, const Regs& r) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      u32x4_t v = permute_k_0415(r.a[i]);
-      if (k0 + a_ch[i] * 8 >= K) v = u32x4_t{0u, 0u, 0u, 0u};   // K tail
-      lds_a[buf][a_row[i] * CHUNKS + swz(a_row[i], a_ch[i])] = v;
-    }
-    const uint32_t vmask = in_vgpr(0x000F000Fu);
-    const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
-#pragma unroll
-    for (int j = 0; j < W_PER_T; ++j) {
-      const uint32_t sh = (r.s[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const half2_t s2 = __builtin_bit_cast(half2_t, sh | (sh << 16));
-      const u32x4_t d = dequant_w4_word_fused(r.w[j], vmask, bias);
-      const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
-      const int n = b_c + j;
-      lds_b[buf][n * CHUNKS + swzb(n, b_kp)] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
-    }
-  };
-
-  float4_t acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t bf[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        // column tile t of the wave: lane j holds column 4j + (t & 3) of 64-column block t / 4
-        const int n = wn * TN + (t >> 2) * 64 + 4 * r16 + (t & 3);
-        bf[t] = lds_b[buf][n * CHUNKS + swzb(n, s * 4 + q)];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * TM + mt * 16 + r16;
-        const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, s * 4 + q)];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16x16x32_f16(av, bf[t], acc[mt][t]);
-      }
-    }
-  };
-
-  const int nk = (K + BK - 1) / BK;
-  Regs r0, r1;
-  load_stage(0, r0);
-  if (nk > 1) load_stage(1, r1);
-  store_stage(0, 0, r0);
-  __syncthreads();
-  if (nk > 2) load_stage(2, r0);
-  // iteration kt: compute stage kt; stage kt+1 (in the other register set) goes
-  // to LDS; the freed set fetches stage kt+3. Unrolled by two so set indices are static.
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    compute(0);
-    store_stage(kt + 1, 1, r1);
-    __syncthreads();
-    if (kt + 3 < nk) load_stage(kt + 3, r1);
-    if (kt + 2 < nk) {
-      compute(1);
-      store_stage(kt + 2, 0, r0);
-      __syncthreads();
-      if (kt + 4 < nk) load_stage(kt + 4, r0);
-    } else {
-      compute(1);
-      kt += 2;
-      break;
-    }
-  }
-  if (kt < nk) compute(kt & 1);
-
-  // epilogue: four adjacent columns per 8-byte store
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int nb = 0; nb < NT / 4; ++nb) {
-        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
-        if (col >= N) continue;
-        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
-        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
-        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
-      }
-    }
-  }
-}
-
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_lds_tile(const W4Args& p, hipStream_t stream) {
-  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
-  const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_lds_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
-  return hipGetLastError();
-}
-
-// Third design (the default for large N): per-wave dequantization as in the
-// first kernel, but sized so the unpack work is amortised over eight MFMA row
-// tiles (wave tile 128 x 64, 2 x 2 waves, 256 x 128 workgroup tile), and lean
-// enough (<= 256 registers, 72 KiB LDS) for two workgroups per CU, so one
-// workgroup's VALU unpack overlaps the other's MFMAs. Unpack uses the fused
-// mask/bias form; scale pairs are built with one byte permute; the K tail is
-// handled only in the last stage; addresses are 32-bit offsets from
-// wave-uniform bases.
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(WAVES_M * WAVES_N * kWave, 2) void w4_prefill_v3_kernel(
-    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
-    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n) {
-  constexpr int NTHR = WAVES_M * WAVES_N * kWave;
-  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
-  constexpr int MT = TM / 16, NB = TN / 64;
-  static_assert(TN % 64 == 0 && TM % 16 == 0, "wave tile");
-  constexpr int A_PER_T = BM * CHUNKS / NTHR;
-  static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
-  constexpr int B_CHUNKS = (BK / 8) * (BN / 4);
-  constexpr int B_PER_T = B_CHUNKS / NTHR;   // 16-byte packed chunks per thread
-  static_assert(B_CHUNKS % NTHR == 0, "B staging");
-
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * CHUNKS];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][(BK / 8) * BN / 4];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int q = lane >> 4, r16 = lane & 15;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin % tiles_m) * BM;
-  const int n0 = (lin / tiles_m) * BN;
-
-  // A staging: chunk id -> (row, chunk); 32-bit element offsets
-  uint32_t a_off[A_PER_T];
-  int a_lds[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + i * NTHR;
-    const int row = id / CHUNKS, ch = id % CHUNKS;
-    a_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + ch * 8);
-    a_lds[i] = row * CHUNKS + swz(row, ch);
-  }
-  const int a_ch0 = tid % CHUNKS;   // the chunk index is the same for all of a thread's A chunks
-  // B staging: 16-byte chunks (4 words, 4 adjacent columns of one packed row)
-  uint32_t b_off[B_PER_T];
-#pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) {
-    const int id = tid + i * NTHR;
-    const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
-    b_off[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4));
-  }
-  const int kp_total = K / 8;
-  // this lane's 4 output columns per 64-column block (scale columns)
-  uint32_t s_off[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s_off[nb] = (uint32_t)min(n0 + wn * TN + nb * 64 + 4 * r16, N - 4);
-
-  u32x4_t ra[A_PER_T];
-  u32x4_t rb[B_PER_T];
-  u32x2_t sc_nxt[2][NB], sc_cur[2][NB];
-  auto load_stage = [&](int kt) {
-    const int k0 = kt * BK;
-    if (k0 + BK <= K) {
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(A + k0 + a_off[i]);
-      const uint32_t* bbase = B + (size_t)(k0 / 8) * N;
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bbase + b_off[i]);
-    } else {
-      // partial last stage (K % 64 == 32): per-chunk clamped addresses; A chunks
-      // past K are zeroed when stored, so the clamped B rows never contribute
-      const int k = min(k0 + a_ch0 * 8, K - 8) - a_ch0 * 8;
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(A + k + a_off[i]);
-#pragma unroll
-      for (int i = 0; i < B_PER_T; ++i) {
-        const int b_kp = (tid + i * NTHR) / (BN / 4);
-        const int kp = min(k0 / 8 + b_kp, kp_total - 1);
-        rb[i] = *reinterpret_cast<const u32x4_t*>(B + (size_t)(kp - b_kp) * N + b_off[i]);
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint16_t* sbase = S + (size_t)(min(k0 + 32 * s, K - 1) / group_size) * N;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc_nxt[s][nb] = *reinterpret_cast<const u32x2_t*>(sbase + s_off[nb]);
-    }
-  };
-  auto store_stage = [&](int kt, int buf) {
-    const int k0 = kt * BK;
-    if (k0 + BK <= K) {
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(ra[i]);
-    } else {
-      // partial last stage: chunks past K enter as zeros
-#pragma unroll
-      for (int i = 0; i < A_PER_T; ++i) {
-        const bool past = k0 + a_ch0 * 8 >= K;
-        lds_a[buf][a_lds[i]] = past ? u32x4_t{0u, 0u, 0u, 0u} : permute_k_0415(ra[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) lds_b[buf][tid + i * NTHR] = rb[i];
-  };
-
-  float4_t acc[MT][NB * 4];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NB * 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const uint32_t vmask = in_vgpr(0x000F000Fu);
-  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
-  const int nk = (K + BK - 1) / BK;
-  load_stage(0);
-  store_stage(0, 0);
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load_stage(kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t bq[NB * 4];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // packed row s*4+q of the stage, this lane's 4 adjacent columns
-        const u32x4_t wv = lds_b[cur][(s * 4 + q) * (BN / 4) + (wn * TN + nb * 64) / 4 + r16];
-        const uint32_t w4[4] = {wv.x, wv.y, wv.z, wv.w};
-        const uint32_t sp[2] = {sc_cur[s][nb].x, sc_cur[s][nb].y};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // (s_t, s_t) from the packed scales with one byte permute
-          const uint32_t pair = __builtin_amdgcn_perm(sp[t >> 1], sp[t >> 1], (t & 1) ? 0x03020302u : 0x01000100u);
-          const half2_t s2 = __builtin_bit_cast(half2_t, pair);
-          const u32x4_t d = dequant_w4_word_fused(w4[t], vmask, bias);
-          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
-          bq[nb * 4 + t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
-        }
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * TM + mt * 16 + r16;
-        const u32x4_t av = lds_a[cur][row * CHUNKS + swz(row, s * 4 + q)];
-#pragma unroll
-        for (int j = 0; j < NB * 4; ++j) acc[mt][j] = mfma16x16x32_f16(av, bq[j], acc[mt][j]);
-      }
-    }
-    if (more) store_stage(kt + 1, cur ^ 1);
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc_cur[s][nb] = sc_nxt[s][nb];
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + wm * TM + mt * 16 + q * 4 + i;
-      if (row >= M) continue;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = n0 + wn * TN + nb * 64 + 4 * r16;
-        if (col >= N) continue;
-        const uint32_t lo = (uint32_t)f2h_rn(acc[mt][nb * 4 + 0][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 1][i]) << 16);
-        const uint32_t hi = (uint32_t)f2h_rn(acc[mt][nb * 4 + 2][i]) | ((uint32_t)f2h_rn(acc[mt][nb * 4 + 3][i]) << 16);
-        *reinterpret_cast<u32x2_t*>(C + (size_t)row * N + col) = u32x2_t{lo, hi};
-      }
-    }
-  }
-}
-
-// Fourth design: the third design's staging with 32x32x16 MFMA tiles, which
-// gfx950 runs at twice the rate of 16x16x32. A wave tile is TM x 64: TM / 32
-// row tiles by two column tiles of 32, where column tile t holds the columns
-// 2j + t (lane j of the tile), so one 8-byte read of packed B per lane per
-// 16-deep K step yields both tiles' words and the results of a row come out as
-// two adjacent columns. Per 16-deep step a wave unpacks two words per lane and
-// issues 2 * TM / 32 MFMAs. Global loads run PD stages ahead of the multiply
-// (PD register sets); a stage's loads are written to LDS at the end of the
-// stage before it is multiplied, so with PD = 2 they have two stages to land.
-// With KG = 2 the workgroup holds two groups of WAVES_M x WAVES_N waves that
-// take the even and the odd K stages (each with its own LDS buffers) and sum
-// their accumulators through LDS at the end: the same tile and the same unpack
-// work per wave, twice the waves per SIMD to cover each other's waits (for
-// shapes with about one tile per CU).
-// LDS of one fourth-design tile: per K group, two stages of A chunks and of
-// packed B (no B when each wave loads its own B words, BD).
+// LDS of one tile: per K group, two stages of A chunks and of packed B (no B
+// when each wave loads its own B words, BD).
 template <int BM, int BN, int KG, bool BD = false>
 struct W4TileLds {
   u32x4_t a[KG][2][BM * CHUNKS];
   u32x4_t b[KG][2][BD ? 1 : (BK / 8) * BN / 4];
 };
 
-// One BM x BN output tile of the fourth design: rows m0 .. m0+BM-1 (those < M)
-// and columns n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
-// BF: activations, scales and output are bf16 (weights (q - 8) * s rounded to
-// bf16 through fp32, bf16 MFMAs); otherwise fp16.
-// NK: B stored [N, K/8] and scales [N, K/group_size]. The stage's B tile is
-// then read as each column's eight words (two 16-byte loads per column) and
-// written into the same [8][BN] LDS tile word by word, so the MFMA loop is
-// unchanged; the lane's two scales are two 2-byte loads.
-// BD: B does not pass through LDS. Each lane loads the packed words its MFMAs
-// take (two adjacent columns of one packed row per 16-deep step: 8 bytes, 256
-// contiguous bytes per half-wave) one stage ahead, like the scales. This pays
-// when a wave's B columns are its own (WAVES_M == 1, as in the grouped tiles).
+// One BM x BN output tile: rows m0 .. m0+BM-1 (those < M) and columns
+// n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
+//
+// A wave tile is TM x 64: TM / 32 row tiles by two column tiles of 32, where
+// column tile t holds the columns 2j + t (lane j of the tile), so one 8-byte
+// read of packed B per lane per 16-deep K step yields both tiles' words and
+// the results of a row come out as two adjacent columns.
+//   * Staging: A, the packed B words and the lane's scale pairs of stage
+//     kt + PD are fetched with raw buffer loads (descriptors in SGPRs, per-lane
+//     byte offsets) while stage kt is multiplied; a stage is written to LDS
+//     right before it is needed. The B and scale descriptors are rebuilt at
+//     each stage's first packed row, so a packed B of any size is addressed
+//     with 32-bit offsets. Reads past a descriptor's end return zeros.
+//   * A rows sit in LDS with an XOR swizzle on their 16-byte chunks and in the
+//     K-slot order (0,4,1,5,2,6,3,7) that the unpack produces for B.
+//   * fp16: each word unpacks to (q - 8) exactly (code OR-ed into the mantissa
+//     of 1024.0, minus 1032), then one packed multiply by the column's group
+//     scale rounds each weight to fp16 before the MFMA.
+//   * bf16 (BF): the weights stay exact. A code enters the bf16 MFMA as
+//     128 + q (0x4300 | q per half), one more MFMA per row tile against a
+//     constant -136 operand adds -136 * (sum of the row's activations), and the
+//     fp32 partial of each quantization group is scaled once by the group's
+//     scale when the group ends (deferred scaling).
+//   * KG = 2: two groups of WAVES_M x WAVES_N waves take the even and the odd
+//     K stages (each with its own LDS buffers) and sum their accumulators
+//     through LDS at the end (for shapes with about one tile per CU).
+//   * NK: B stored [N, K/8] and scales [N, K/group_size]. The stage's B tile
+//     is read as each column's eight words (two 16-byte loads per column) and
+//     written into the same [8][BN] LDS tile word by word, so the MFMA loop is
+//     unchanged; the lane's two scales are two 2-byte loads.
+//   * BD: B does not pass through LDS. Each lane loads the packed words its
+//     MFMAs take (8 bytes per 16-deep step, 256 contiguous bytes per
+//     half-wave) with the stage; this pays when a wave's B columns are its own
+//     (WAVES_M == 1, as in the grouped tiles).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false,
           bool BD = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
@@ -632,6 +79,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   static_assert(PD >= 1 && PD <= 4, "prefetch distance");
   static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
   static_assert(!BD || (KG == 1 && !NK), "direct B: one K group, [K/8, N] layout");
+  static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
   constexpr int NBD = BD ? BK / 16 : 1;      // direct B words per lane and stage
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
   static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
@@ -654,12 +102,24 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   // K offset is uniform (an SGPR). Reads past a descriptor's end return zeros,
   // which is what the packed rows past K of a partial last stage need.
   const int rows = min(BM, M - m0);
+  // (the host limits K so that BM rows of A stay below 4 GiB)
   const __amdgpu_buffer_rsrc_t a_src = buffer_rsrc(A + (size_t)m0 * K, (uint32_t)rows * K * 2);
-  const __amdgpu_buffer_rsrc_t b_src =
-      NK ? buffer_rsrc(B + (size_t)n0 * (K / 8), (uint32_t)((size_t)(N - n0) * (K / 8) * 4))
-         : buffer_rsrc(B + n0, (uint32_t)((size_t)(K / 8) * N - n0) * 4);
-  const __amdgpu_buffer_rsrc_t s_src = buffer_rsrc(S, (uint32_t)((size_t)(K / group_size) * N * 2));
   const int gshift = __builtin_ctz(group_size);
+  // a descriptor's size: bytes from its base to the end of the tensor, capped
+  // at 2^32 - 1 (a capped descriptor lies wholly inside the tensor)
+  auto cap32 = [](size_t bytes) { return (uint32_t)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFull : bytes); };
+  // [N, K/8]: one descriptor from column n0 on (the stage's K offset goes in soffset)
+  const __amdgpu_buffer_rsrc_t bnk_src =
+      buffer_rsrc(B + (size_t)n0 * (K / 8), cap32((size_t)(N - n0) * (K / 8) * 4));
+  // [K/8, N]: packed row k0 / 8 from column n0 on, and the scales from row k0 >> gshift
+  auto b_stage = [&](int k0) {
+    const size_t at = (size_t)(k0 / 8) * N + n0;
+    return buffer_rsrc(B + at, cap32(((size_t)(K / 8) * N - at) * 4));
+  };
+  auto s_stage = [&](int g0) {
+    const size_t at = (size_t)g0 * N;
+    return buffer_rsrc(S + at, cap32(((size_t)(K >> gshift) * N - at) * 2));
+  };
   uint32_t a_voff[A_PER_T];
   int a_lds[A_PER_T];
 #pragma unroll
@@ -680,7 +140,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       b_voff[i] = (uint32_t)(min(c, N - n0 - 1) * (K / 8) + 4 * half) * 4;
     } else {
       const int b_kp = id / (BN / 4), b_c4 = id % (BN / 4);
-      b_voff[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4) - n0) * 4;
+      b_voff[i] = (uint32_t)(b_kp * N + min(n0 + 4 * b_c4, N - 4) - n0) * 4;   // from the stage's base
     }
   }
   // this lane's two output columns (scale columns)
@@ -712,14 +172,16 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     const int k0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) r.a[i] = buffer_load16(a_src, a_voff[i], (uint32_t)k0 * 2);
+    const __amdgpu_buffer_rsrc_t b_src = NK ? bnk_src : b_stage(k0);
     if constexpr (BD) {
 #pragma unroll
-      for (int j = 0; j < NBD; ++j) r.bd[j] = buffer_load8(b_src, bd_voff, (uint32_t)(k0 / 8 + 2 * j) * N * 4);
+      for (int j = 0; j < NBD; ++j) r.bd[j] = buffer_load8(b_src, bd_voff, (uint32_t)(2 * j) * N * 4);
     } else {
 #pragma unroll
-      for (int i = 0; i < B_PER_T; ++i)
-        r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : (uint32_t)(k0 / 8) * N * 4);
+      for (int i = 0; i < B_PER_T; ++i) r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : 0u);
     }
+    const int g0 = min(k0, K - 1) >> gshift;
+    const __amdgpu_buffer_rsrc_t s_src = s_stage(NK ? 0 : g0);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = min(k0 + 32 * s, K - 1) >> gshift;
@@ -728,7 +190,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const uint16_t* sp = S + (size_t)col0 * (K >> gshift) + g;
         r.sc[s] = (uint32_t)sp[0] | ((uint32_t)sp[K >> gshift] << 16);
       } else {
-        r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)g * N * 2);
+        r.sc[s] = buffer_load4(s_src, s_voff, (uint32_t)(g - g0) * N * 2);
       }
     }
     // partial last stage (K % 64 == 32): A chunks past K must enter as zeros.
@@ -768,9 +230,22 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
   const uint32_t vmask = in_vgpr(0x000F000Fu);
-  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
-  // one stage out of LDS buffer `buf` with the stage's scale pairs (and direct B words)
-  auto compute = [&](int buf, const Cur& cur) {
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
+  // bf16: per row tile, the group partials of both column tiles and the
+  // row-sum correction -136 * sum(a) (the same for every column)
+  constexpr int MP = BF ? MT : 1;
+  float16_t part[MP][2], corr[MP];
+  auto clear_partials = [&]() {
+#pragma unroll
+    for (int i = 0; i < MP; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part[i][0][e] = part[i][1][e] = corr[i][e] = 0.f;
+  };
+  if constexpr (BF) clear_partials();
+  const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
+  // one stage (K offset k0) out of LDS buffer `buf` with the stage's scale pairs
+  // (and direct B words)
+  auto compute = [&](int buf, const Cur& cur, int k0) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds_b[buf]);
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
@@ -780,12 +255,15 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       u32x4_t bq[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        const uint32_t wd = (uint32_t)(w2 >> (32 * t));
         if constexpr (BF) {
-          bq[t] = dequant_w4_word_bf16((uint32_t)(w2 >> (32 * t)), bf2f((uint16_t)(t ? sp >> 16 : sp & 0xFFFFu)));
+          // 128 + q per half, exact; K-slot pairs (0,4), (1,5), (2,6), (3,7)
+          bq[t] = u32x4_t{and_or(wd, vmask, bias), and_or(wd >> 4, vmask, bias), and_or(wd >> 8, vmask, bias),
+                          and_or(wd >> 12, vmask, bias)};
         } else {
           const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
           const half2_t s2 = __builtin_bit_cast(half2_t, pair);
-          const u32x4_t d = dequant_w4_word_fused((uint32_t)(w2 >> (32 * t)), vmask, bias);
+          const u32x4_t d = dequant_w4_word_fused(wd, vmask, bias);
           const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
           bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
         }
@@ -795,11 +273,27 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const int row = wm * TM + mt * 32 + c32;
         const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
         if constexpr (BF) {
-          acc[mt][0] = mfma32x32x16_bf16(av, bq[0], acc[mt][0]);
-          acc[mt][1] = mfma32x32x16_bf16(av, bq[1], acc[mt][1]);
+          part[mt][0] = mfma32x32x16_bf16(av, bq[0], part[mt][0]);
+          part[mt][1] = mfma32x32x16_bf16(av, bq[1], part[mt][1]);
+          corr[mt] = mfma32x32x16_bf16(av, u32x4_t{m136, m136, m136, m136}, corr[mt]);
         } else {
           acc[mt][0] = mfma32x32x16_f16(av, bq[0], acc[mt][0]);
           acc[mt][1] = mfma32x32x16_f16(av, bq[1], acc[mt][1]);
+        }
+      }
+      if constexpr (BF) {
+        // the quantization group ends with this 16-deep step: scale its partials
+        // once (uniform test; steps past K hold zero activations)
+        if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
+          const float s0 = bf2f((uint16_t)(sp & 0xFFFFu)), s1 = bf2f((uint16_t)(sp >> 16));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              acc[mt][0][e] += s0 * (part[mt][0][e] + corr[mt][e]);
+              acc[mt][1][e] += s1 * (part[mt][1][e] + corr[mt][e]);
+            }
+          clear_partials();
         }
       }
     }
@@ -823,7 +317,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       const bool more = kt + 2 < nk;
       if (more) load_stage(kt + 2, r);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt < nk) compute(j & 1, cur);
+      if (kt < nk) compute(j & 1, cur, kt * BK);
       if (more) store_stage(kt + 2, (j + 1) & 1, r);
       __syncthreads();
       if (more) cur = cur_of(r);
@@ -865,7 +359,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       const bool more = kt + 1 < nk;
       if (more) load_stage(kt + 1, r);
       __builtin_amdgcn_sched_barrier(0);
-      compute(kt & 1, cur);
+      compute(kt & 1, cur, kt * BK);
       if (more) store_stage(kt + 1, (kt + 1) & 1, r);
       __syncthreads();
       cur = cur_of(r);
@@ -889,21 +383,21 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       // even stage kt: buffer 0; stage kt + 1 is in r1
       load_stage(min(kt + 2, nk - 1), r0);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, cur);
+      compute(0, cur, kt * BK);
       store_stage(kt + 1, 1, r1);
       __syncthreads();
       cur = cur_of(r1);
       // odd stage kt + 1: buffer 1; stage kt + 2 (if any) is in r0
       load_stage(min(kt + 3, nk - 1), r1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(1, cur);
+      compute(1, cur, (kt + 1) * BK);
       if (kt + 2 < nk) {
         store_stage(kt + 2, 0, r0);
         cur = cur_of(r0);
       }
       __syncthreads();
     }
-    if (kt < nk) compute(0, cur);   // nk odd: the last stage sits in buffer 0
+    if (kt < nk) compute(0, cur, kt * BK);   // nk odd: the last stage sits in buffer 0
   } else {
     // PD register sets, unrolled by PD so each set is static: stage i + PD is
     // requested into the set that held stage i (already in LDS) while stage i is
@@ -921,7 +415,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const int i = kt + p;
         load_stage(min(i + PD, nk - 1), r[p]);
         __builtin_amdgcn_sched_barrier(0);
-        if (i < nk) compute(i & 1, cur);
+        if (i < nk) compute(i & 1, cur, i * BK);
         if (i + 1 < nk) {
           store_stage(i + 1, (i + 1) & 1, r[(p + 1) % PD]);
           cur = cur_of(r[(p + 1) % PD]);
@@ -1068,9 +562,12 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
                                                                    nt * BN, lds, ept);
 }
 
-template <int BM, int BN, int WM, int WN, int MINB, int KG, int PD = 1, bool BD = false>
-static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream) {
-  if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL) return hipErrorNotSupported;
+// Grouped launch: 64-row chunks of a group by 256 columns, three workgroups
+// per CU, two stages of loads in flight, B words loaded straight into the
+// lanes' registers (one wave per column strip, so no B word is shared).
+hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
+  constexpr int BM = 64, BN = 256, WM = 1, WN = 4, MINB = 3, KG = 1, PD = 2;
+  constexpr bool BD = true;
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   // every group has at most ceil(rows / BM) <= rows / BM + 1 row chunks
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
@@ -1082,116 +579,35 @@ static hipError_t launch_grouped_tile(const W4GroupedArgs& p, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_w4_grouped(const W4GroupedArgs& p, int variant, hipStream_t stream) {
-  switch (variant) {
-    case 0: return launch_grouped_tile<128, 256, 1, 4, 1, 2>(p, stream);
-    case 1: return launch_grouped_tile<128, 256, 1, 4, 2, 1>(p, stream);
-    case 2: return launch_grouped_tile<64, 256, 1, 4, 2, 1>(p, stream);
-    case 3: return launch_grouped_tile<64, 256, 1, 4, 1, 2>(p, stream);
-    case 4: return launch_grouped_tile<64, 256, 1, 4, 3, 1>(p, stream);
-    case 5: return launch_grouped_tile<32, 256, 1, 4, 4, 1>(p, stream);
-    case 6: return launch_grouped_tile<64, 128, 1, 2, 4, 1>(p, stream);
-    // two stages of prefetch in registers
-    case 7: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 2>(p, stream);
-    case 8: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 2>(p, stream);
-    case 9: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2>(p, stream);
-    case 10: return launch_grouped_tile<64, 128, 1, 2, 4, 1, 2>(p, stream);
-    case 11: return launch_grouped_tile<128, 256, 1, 4, 2, 1, 2>(p, stream);
-    // three or four stages of prefetch in registers
-    case 12: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 3>(p, stream);
-    case 13: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3>(p, stream);
-    case 14: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 4>(p, stream);
-    case 15: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 3>(p, stream);
-    // B words loaded straight into each wave's registers (no LDS for B)
-    case 16: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 2, true>(p, stream);
-    case 17: return launch_grouped_tile<64, 256, 1, 4, 3, 1, 1, true>(p, stream);
-    case 18: return launch_grouped_tile<64, 256, 1, 4, 2, 1, 3, true>(p, stream);
-    case 19: return launch_grouped_tile<32, 256, 1, 4, 4, 1, 2, true>(p, stream);
-    // taller row chunks (one per group of up to 96 or 128 rows): each weight
-    // is unpacked once per group, narrower column tiles keep the tile count up
-    case 20: return launch_grouped_tile<96, 128, 1, 2, 4, 1, 2, true>(p, stream);
-    case 21: return launch_grouped_tile<96, 256, 1, 4, 2, 1, 2, true>(p, stream);
-    case 22: return launch_grouped_tile<128, 128, 1, 2, 3, 1, 2, true>(p, stream);
-    case 23: return launch_grouped_tile<64, 128, 1, 2, 2, 1, 2, true>(p, stream);
-    default: return hipErrorInvalidValue;
-  }
+// Dense launch: 128 x 256 tiles, each XCD sweeping groups of eight row panels
+// across N. fp16: one K group of four 128 x 64 wave tiles, two workgroups per
+// CU, or (at most one tile per CU) one workgroup of two K groups per CU. bf16:
+// eight 64 x 64 wave tiles (two waves per column strip), one workgroup per CU:
+// the exact-code path keeps a group partial and a row-sum correction beside
+// each accumulator, which leaves no registers for a second workgroup.
+template <int WM, int MINB, int KG, bool BF, bool NK>
+static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
+  constexpr int BM = 128, BN = 256, WN = 4, PD = 1;
+  const int grid = ((tm * tn + 7) / 8) * 8;
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK>), dim3(grid),
+                     dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,
+                     p.group_size, tm, tn, 8, p.epi);
 }
 
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_v3_tile(const W4Args& p, hipStream_t stream) {
-  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
-  const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_v3_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
-  return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int MINB, int PD, int KG = 1>
-static hipError_t launch_v4_tile(const W4Args& p, hipStream_t stream, int order = 0) {
-  // byte offsets into B and the scales are 32-bit buffer offsets
-  if (p.K / 8 * p.N * 4 > 0xFFFFFFFFLL || p.K / p.group_size * p.N * 2 > 0xFFFFFFFFLL) return hipErrorNotSupported;
-  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
-  const int grid = ((tm * tn + 7) / 8) * 8;
-#define QG_V4_LAUNCH(BFV, NKV)                                                                                  \
-  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BFV, NKV>), dim3(grid),              \
-                     dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,     \
-                     p.group_size, tm, tn, order, p.epi)
-  if (p.nk) {   // [N, K/8] weights: the default launch shapes only (15, 16)
-    if constexpr (PD == 1 && BM == 128 && BN == 256 && MINB == 2 && KG == 1) {
-      if (p.bf16) QG_V4_LAUNCH(true, true); else QG_V4_LAUNCH(false, true);
-    } else if constexpr (PD == 1 && BM == 128 && BN == 256 && MINB == 1 && KG == 2) {
-      if (p.bf16) QG_V4_LAUNCH(true, true); else QG_V4_LAUNCH(false, true);
-    } else {
-      return hipErrorNotSupported;
-    }
-  } else if (p.bf16) {
-    QG_V4_LAUNCH(true, false);
+hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
+  const int tm = (int)((p.M + 127) / 128), tn = (int)((p.N + 255) / 256);
+  const bool one_pass = (long long)tm * tn <= num_cus;
+  if (p.bf16) {
+    if (p.nk) launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
+    else launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
+  } else if (p.nk) {
+    if (one_pass) launch_v4<1, 1, 2, false, true>(p, stream, tm, tn);
+    else launch_v4<1, 2, 1, false, true>(p, stream, tm, tn);
   } else {
-    QG_V4_LAUNCH(false, false);
+    if (one_pass) launch_v4<1, 1, 2, false, false>(p, stream, tm, tn);
+    else launch_v4<1, 2, 1, false, false>(p, stream, tm, tn);
   }
-#undef QG_V4_LAUNCH
   return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN>
-static hipError_t launch_tile(const W4Args& p, hipStream_t stream) {
-  const int tm = (int)((p.M + BM - 1) / BM), tn = (int)((p.N + BN - 1) / BN);
-  const int tiles = tm * tn;
-  const int grid = ((tiles + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_kernel<BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * kWave), 0, stream,
-                     p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn);
-  return hipGetLastError();
-}
-
-// Variants: tile shapes (BM x BN, wave grid).
-hipError_t launch_w4_prefill(const W4Args& p, int variant, hipStream_t stream) {
-  if ((p.bf16 || p.epi.flags) && variant < 11) return hipErrorInvalidValue;   // bf16 and epilogues: fourth design
-  switch (variant) {
-    case 0: return launch_tile<256, 128, 2, 2>(p, stream);
-    case 1: return launch_tile<128, 128, 2, 2>(p, stream);
-    case 2: return launch_tile<128, 256, 2, 2>(p, stream);
-    case 3: return launch_tile<64, 128, 1, 2>(p, stream);
-    case 4: return launch_lds_tile<256, 128, 4, 2>(p, stream);
-    case 5: return launch_lds_tile<128, 128, 2, 2>(p, stream);
-    case 6: return launch_lds_tile<256, 128, 2, 2>(p, stream);
-    case 7: return launch_lds_tile<128, 256, 2, 4>(p, stream);
-    case 8: return launch_v3_tile<256, 128, 2, 2>(p, stream);
-    case 9: return launch_v3_tile<128, 256, 1, 4>(p, stream);
-    case 10: return launch_v3_tile<128, 128, 1, 2>(p, stream);
-    // fourth design, 128 x 256 tiles; the last argument is the tile order
-    case 11: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 0);
-    case 12: return launch_v4_tile<128, 256, 1, 4, 2, 2>(p, stream, 8);
-    case 13: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 1);
-    case 14: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 4);
-    case 15: return launch_v4_tile<128, 256, 1, 4, 2, 1>(p, stream, 8);
-    // two K groups of four waves (128 x 64 wave tiles), one workgroup per CU
-    case 16: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 8);
-    case 17: return launch_v4_tile<128, 256, 1, 4, 1, 1, 2>(p, stream, 0);
-    // three stages in flight in registers
-    case 18: return launch_v4_tile<128, 256, 1, 4, 2, 3>(p, stream, 8);
-    case 19: return launch_v4_tile<128, 256, 1, 4, 1, 3>(p, stream, 8);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace qg

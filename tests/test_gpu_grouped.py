@@ -112,38 +112,17 @@ def test_determinism(gpu, lib):
     assert np.array_equal(run_grouped(lib, d), run_grouped(lib, d))
 
 
-# every launch shape: waves per workgroup, steps in flight, workgroups per CU,
-# steps whose loads are issued together (variant 7 is left out: it spills)
-GROUPED_VARIANTS = [0, 1, 2, 3, 4, 5, 6, 8, 9, 10, 11, 12, 13]
-# transposed weights staged through LDS as whole 128-byte row segments (transposed weights only)
-GROUPED_VARIANTS_TB = GROUPED_VARIANTS + [14, 15, 16, 17, 18, 19, 20, 21]
+# ragged shapes: K tails (K % 32 != 0), N tails, tiny and large groups, 25% skipped
+GROUPED_SHAPES = [(8, 200, 64, 64, 21), (5, 77, 40, 24, 22), (16, 600, 456, 200, 23), (3, 300, 96, 136, 24),
+                  (4, 520, 384, 72, 25), (6, 900, 136, 48, 26), (4, 520, 72, 1032, 15)]
 
 
-@pytest.mark.parametrize("variant", GROUPED_VARIANTS_TB)
-def test_every_launch_shape(gpu, lib, variant):
-    import os
-    os.environ["QG_GROUPED_VARIANT"] = str(variant)
-    try:
-        for (E, T, K, N, seed) in [(8, 200, 64, 64, 21), (5, 77, 40, 24, 22), (16, 600, 456, 200, 23),
-                                   (3, 300, 96, 136, 24), (4, 520, 384, 72, 25), (6, 900, 136, 48, 26)]:
-            d = synth.grouped_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
-            check(lib, d, f"v{variant} seed{seed}")
-    finally:
-        del os.environ["QG_GROUPED_VARIANT"]
-
-
-# transpose_b == False ([E, K, N] experts): LDS-transposed weight fragments
-@pytest.mark.parametrize("variant", GROUPED_VARIANTS)
-def test_b_not_transposed(gpu, lib, variant):
-    import os
-    os.environ["QG_GROUPED_VARIANT"] = str(variant)
-    try:
-        for (E, T, K, N, seed) in [(8, 200, 64, 64, 11), (5, 77, 40, 24, 12), (16, 600, 256, 200, 13),
-                                   (3, 300, 96, 136, 14), (4, 520, 72, 1032, 15)]:
-            d = synth.grouped_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
-            check(lib, d, f"[E,K,N] v{variant} seed{seed}", transpose_b=False)
-    finally:
-        del os.environ["QG_GROUPED_VARIANT"]
+@pytest.mark.parametrize("transpose_b", [True, False], ids=["ENK", "EKN"])
+@pytest.mark.parametrize("shape", GROUPED_SHAPES, ids=lambda s: f"E{s[0]}_T{s[1]}_K{s[2]}_N{s[3]}")
+def test_ragged_shapes(gpu, lib, shape, transpose_b):
+    E, T, K, N, seed = shape
+    d = synth.grouped_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
+    check(lib, d, f"seed{seed} tb={transpose_b}", transpose_b=transpose_b)
 
 
 def test_b_not_transposed_full_size(gpu, lib):

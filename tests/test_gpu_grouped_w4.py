@@ -5,8 +5,6 @@ prefix sum, expert_ids with negative entries skipped, expert_usage_stats[1]
 active count) over experts in the packed 4-bit format of "multistage_gemm_q"
 (group_size, pack_factor). Floats: |gpu - oracle| <= 1e-2 (|oracle| + 1);
 routing (which rows are written) and unpacked weights: bit-exact."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -19,10 +17,9 @@ from oracle import numerics as nm
 pytestmark = pytest.mark.gpu
 
 SENT = 0x7E00  # fp16 NaN pattern: never produced by the kernel
-VARIANTS = range(24)
 
 
-def run_gw4(lib, d, a_off=None, ids=None, usage=None, a=None, variant=None):
+def run_gw4(lib, d, a_off=None, ids=None, usage=None, a=None):
     a_off = d.a_offsets if a_off is None else a_off
     ids = d.expert_ids if ids is None else ids
     usage = d.usage if usage is None else usage
@@ -30,15 +27,9 @@ def run_gw4(lib, d, a_off=None, ids=None, usage=None, a=None, variant=None):
     T = a.shape[0]
     N = d.b.shape[2]
     out = Guarded((T, N), torch.float16, SENT)
-    if variant is not None:
-        os.environ["QG_W4_GROUPED_VARIANT"] = str(variant)
-    try:
-        lib.grouped_gemm_w4(out.view, dev16(a, torch.float16), dev32(a_off), dev32(d.b),
-                            dev16(d.scales, torch.float16), dev32(np.asarray(ids, np.int32)),
-                            [int(v) for v in usage], d.group_size)
-    finally:
-        if variant is not None:
-            del os.environ["QG_W4_GROUPED_VARIANT"]
+    lib.grouped_gemm_w4(out.view, dev16(a, torch.float16), dev32(a_off), dev32(d.b),
+                        dev16(d.scales, torch.float16), dev32(np.asarray(ids, np.int32)),
+                        [int(v) for v in usage], d.group_size)
     got = host16(out.view)
     assert out.bands_intact(), "write outside C"
     return got
@@ -47,7 +38,7 @@ def run_gw4(lib, d, a_off=None, ids=None, usage=None, a=None, variant=None):
 def check(lib, d, what, **kw):
     a = kw.get("a", d.a)
     say(f"[grouped_w4] {what}: T={a.shape[0]} K={a.shape[1]} N={d.b.shape[2]} E={d.b.shape[0]} "
-        f"gs={d.group_size} {dict((k, v) for k, v in kw.items() if k == 'variant')}")
+        f"gs={d.group_size}")
     got = run_gw4(lib, d, **kw)
     a_off = kw.get("a_off", d.a_offsets)
     ids = kw.get("ids", d.expert_ids)
@@ -62,23 +53,21 @@ def check(lib, d, what, **kw):
     return {}
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
-def test_small_ragged(gpu, lib, variant):
+def test_small_ragged(gpu, lib):
     for (E, T, K, N, gs, seed) in [(8, 200, 256, 64, 128, 1), (5, 77, 128, 24, 32, 2),
                                    (16, 600, 512, 264, 64, 3), (3, 300, 256, 136, 256, 4),
                                    (6, 150, 96, 40, 32, 5), (4, 90, 160, 48, 32, 6)]:   # K % 64 == 32: partial last stage
         d = synth.grouped_w4_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25, group_size=gs)
-        check(lib, d, f"small seed{seed}", variant=variant)
+        check(lib, d, f"small seed{seed}")
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
-def test_large_groups_and_edges(gpu, lib, variant):
+def test_large_groups_and_edges(gpu, lib):
     """Groups of 0, 1, 127, 128, 129 and 300 rows; a_offsets[0] > 0; a repeated
     expert; num_active below the table length (the last group is not processed)."""
     d = synth.grouped_w4_inputs(seed=7, E=4, T=700, K=256, N=72)
     a_off = np.array([5, 5, 6, 133, 261, 390, 690, 700], np.uint32)
     ids = np.array([1, 0, 2, -1, 3, 1, 2], np.int32)
-    check(lib, d, "edges", a_off=a_off, ids=ids, usage=np.array([300, 6], np.uint32), variant=variant)
+    check(lib, d, "edges", a_off=a_off, ids=ids, usage=np.array([300, 6], np.uint32))
 
 
 def test_all_skipped_is_untouched(gpu, lib):

@@ -120,18 +120,14 @@ def test_determinism(gpu, lib):
     assert np.array_equal(run_kproj(lib, k), run_kproj(lib, k))
 
 
-# every selectable design: 1 first, 2-5 second (auto / 128 / 64 / 144 rows),
-# 6-9 third (auto / 48 / 96 / 144 rows), 10-11 third with two stages in flight
-KPROJ_VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]
+@pytest.mark.parametrize("i", range(3))
+def test_tile_heights(gpu, lib, i):
+    """48, 96 and 144-row tiles (the height follows the token count)."""
+    from test_gpu_kv_cache import TILE_LENS
+    check(lib, small(40 + i, TILE_LENS[1024][i], Kh=384, hkv=8, D=128, page_size=128), f"tile set {i}")
 
 
-@pytest.mark.parametrize("variant", KPROJ_VARIANTS)
-def test_every_design(gpu, lib, variant):
-    import os
-    os.environ["QG_KPROJ_VARIANT"] = str(variant)
-    try:
-        check(lib, small(40 + variant, (100, 1, 64, 65, 0, 130), Kh=512, cache_lengths=(0, 3, 17, 128, 5, 250)),
-              f"v{variant} ragged")
-        check(lib, small(60 + variant, (300, 7), Kh=384, hkv=2, D=128, page_size=16), f"v{variant} odd stages")
-    finally:
-        del os.environ["QG_KPROJ_VARIANT"]
+def test_long_hidden_rows(gpu, lib):
+    """More than 32 scale blocks of K (the long-row design): ragged, with history."""
+    check(lib, small(70, (100, 1, 64, 65, 0, 130), Kh=33 * 128, cache_lengths=(0, 3, 17, 128, 5, 250)), "Kh=4224")
+    check(lib, small(71, (300, 7), Kh=40 * 128, hkv=2, D=128, page_size=16), "Kh=5120")

@@ -19,7 +19,6 @@ Bars:
     dequantized value q * s within half a code step of the exact product:
     |q s - y| <= max(2^-4 |y|, 2^-10 s) + 1e-4 (|y| + s).
 """
-import os
 
 import numpy as np
 import pytest
@@ -45,23 +44,36 @@ def planes_of(k):
     return k.weight.shape[1] // (k.blocks.shape[4] * k.blocks.shape[5])
 
 
-def run_gpu(lib, k, variant=None, **over):
+def tile_rows(T, N):
+    """Row-tile height the library picks for T tokens and N columns: the tallest of
+    48, 96 and 144 rows within 3 % of the best fill of the last pass over the CUs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tn = N // 128
+    eff = {}
+    for bm in (48, 96, 144):
+        tiles = -(-T // bm) * tn
+        eff[bm] = T * tn / (-(-tiles // cus) * cus * bm)
+    best = max(eff.values())
+    return max(bm for bm in eff if eff[bm] >= best - 0.03)
+
+
+# token lengths that select each row-tile height for N = 1024 and N = 2048
+# (checked by test_tile_heights_are_covered)
+TILE_LENS = {1024: [(700, 800), (1000, 2000), (687, 825, 24, 828, 481, 528, 646, 293)],
+             2048: [(300, 400), (700, 800), (687, 825, 24, 828, 481, 528, 646, 293)]}
+
+
+def run_gpu(lib, k, **over):
     v = dict(hidden=k.hidden, weight=k.weight, input_scale=k.input_scale, weight_scale=k.weight_scale)
     v.update(over)
     fp8 = k.scales is not None
     blocks = torch.from_numpy(k.blocks.copy()).cuda() if fp8 else dev16(k.blocks, torch.bfloat16)
     scales = devf32(k.scales) if fp8 else None
     fn = lib.kv_matmul_ragged_paged_scale if planes_of(k) == 2 else lib.k_matmul_ragged_paged_scale
-    if variant is not None:
-        os.environ["QG_KPROJ_VARIANT"] = str(variant)
-    try:
-        hid = dev8(v["hidden"]) if v["hidden"].dtype == np.uint8 else dev16(v["hidden"], torch.bfloat16)
-        fn(hid, dev32(k.row_offsets), dev8(v["weight"]), devf32(v["input_scale"]),
-           devf32(v["weight_scale"]), blocks, dev32(k.cache_lengths), dev32(k.page_table), k.layer_idx,
-           kv_scales=scales, quantization_granularity=k.qgran)
-    finally:
-        if variant is not None:
-            del os.environ["QG_KPROJ_VARIANT"]
+    hid = dev8(v["hidden"]) if v["hidden"].dtype == np.uint8 else dev16(v["hidden"], torch.bfloat16)
+    fn(hid, dev32(k.row_offsets), dev8(v["weight"]), devf32(v["input_scale"]),
+       devf32(v["weight_scale"]), blocks, dev32(k.cache_lengths), dev32(k.page_table), k.layer_idx,
+       kv_scales=scales, quantization_granularity=k.qgran)
     torch.cuda.synchronize()
     if fp8:
         return blocks.cpu().numpy(), scales.cpu().numpy()
@@ -102,10 +114,11 @@ def exact_rows_in_cache(k, magnitude=False, **over):
     return out
 
 
-def check(lib, k, what, variant=None):
-    say(f"[kv] {what}: T={k.hidden.shape[0]} Kh={k.hidden.shape[1]} cols={k.weight.shape[1]} planes={planes_of(k)} "
-        f"cache={'e4m3 G=%d' % k.qgran if k.scales is not None else 'bf16'} variant={variant}")
-    got, gsc = run_gpu(lib, k, variant)
+def check(lib, k, what):
+    T, N = k.hidden.shape[0], k.weight.shape[1]
+    say(f"[kv] {what}: T={T} Kh={k.hidden.shape[1]} cols={N} planes={planes_of(k)} "
+        f"cache={'e4m3 G=%d' % k.qgran if k.scales is not None else 'bf16'} tile rows={tile_rows(T, N)}")
+    got, gsc = run_gpu(lib, k)
     ref, rsc = run_ref(k)
     tw = touched_rows(k)
     assert np.array_equal(got[~tw], ref[~tw]), "cache bytes outside the written slots changed"
@@ -209,13 +222,19 @@ def test_e4m3_cache_ties_and_zero_tokens_bit_exact(gpu, lib):
     assert np.array_equal(got, ref) and np.array_equal(gsc, rsc)
 
 
-# the third design's launch shapes: auto / 48 / 96 / 144 rows, two stages in flight (3 x 48, 2 x 48)
-@pytest.mark.parametrize("variant", [6, 7, 8, 9, 10, 11])
-def test_every_launch_shape(gpu, lib, variant):
-    check(lib, kv_inputs(40 + variant, (100, 1, 64, 65, 0, 130), Kh=512, cache_lengths=(0, 3, 17, 128, 5, 250)),
-          "bf16", variant)
-    check(lib, kv_inputs(50 + variant, (300, 7), Kh=384, page_size=16, cache="fp8", qgran=64), "e4m3", variant)
-    check(lib, kv_inputs(60 + variant, (129,), Kh=256, planes=1, cache="fp8", qgran=128), "e4m3 keys", variant)
+def test_tile_heights_are_covered(gpu):
+    for N, sets in TILE_LENS.items():
+        assert sorted(tile_rows(sum(l), N) for l in sets) == [48, 96, 144], N
+
+
+# every row-tile height (48, 96, 144 rows), keys and values, both caches
+@pytest.mark.parametrize("i", range(3))
+def test_tile_heights(gpu, lib, i):
+    check(lib, kv_inputs(40 + i, TILE_LENS[2048][i], Kh=256, hkv=8, D=128, page_size=128), "bf16")
+    check(lib, kv_inputs(50 + i, TILE_LENS[2048][i], Kh=384, hkv=8, D=128, page_size=16, cache="fp8", qgran=64),
+          "e4m3")
+    check(lib, kv_inputs(60 + i, TILE_LENS[1024][i], Kh=256, hkv=8, D=128, planes=1, page_size=128, cache="fp8",
+                         qgran=128), "e4m3 keys")
 
 
 def test_full_size(gpu, lib):
@@ -228,19 +247,15 @@ def test_full_size(gpu, lib):
                                                                               np.uint32)), "full keys e4m3 history"))
 
 
-def test_rejects_older_designs_and_long_hidden(gpu, lib):
-    k = kv_inputs(70, (10,), cache="fp8", qgran=128)
-    for v in (1, 3):
-        os.environ["QG_KPROJ_VARIANT"] = str(v)
-        try:
-            fp8 = torch.from_numpy(k.blocks.copy()).cuda()
-            st = lib.kv_matmul_ragged_paged_scale(
-                dev16(k.hidden, torch.bfloat16), dev32(k.row_offsets), dev8(k.weight), devf32(k.input_scale),
-                devf32(k.weight_scale), fp8, dev32(k.cache_lengths), dev32(k.page_table), k.layer_idx,
-                kv_scales=devf32(k.scales), quantization_granularity=128, raise_on_error=False)
-            assert st == lib.QG.ERR_UNSUPPORTED
-        finally:
-            del os.environ["QG_KPROJ_VARIANT"]
+def test_rejects_long_hidden(gpu, lib):
+    """Keys and values, or an e4m3 cache, with more than 32 scale blocks of K are refused."""
+    k = kv_inputs(70, (10,), Kh=33 * 128, cache="fp8", qgran=128)
+    fp8 = torch.from_numpy(k.blocks.copy()).cuda()
+    st = lib.kv_matmul_ragged_paged_scale(
+        dev16(k.hidden, torch.bfloat16), dev32(k.row_offsets), dev8(k.weight), devf32(k.input_scale),
+        devf32(k.weight_scale), fp8, dev32(k.cache_lengths), dev32(k.page_table), k.layer_idx,
+        kv_scales=devf32(k.scales), quantization_granularity=128, raise_on_error=False)
+    assert st == lib.QG.ERR_UNSUPPORTED
 
 
 def test_determinism(gpu, lib):

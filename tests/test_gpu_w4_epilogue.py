@@ -6,25 +6,18 @@ fixed steps in its place: bias over columns, a SiLU-gated product of column
 pairs (2j, 2j+1) that halves N, and a residual add, all on the fp32 product
 before its one rounding.
 
-Tolerance. Bias and residual outputs: the common bar |gpu - oracle| <=
-1e-2 (|oracle| + 1) per element. A gated output z = silu(g) u amplifies the
-GEMM's own error: with g ~ 8 and u ~ 0.2, the fp16 rounding of each weight
-(q - 8) s alone moves z by more than 1e-2 (|z| + 1) (seen on the full-size
-prefill, and reproduced on the CPU by rounding the weights to fp16 before an
-exact product). So for gated outputs the common bar is put on the GEMM result
-(tau_g = 1e-2 (|g| + 1), tau_u likewise) and carried through the gate to first
-order with silu' in [-0.1, 1.1]: 1.1 |u| tau_g + (|silu(g)| + 1.1 tau_g) tau_u,
-plus the common bar on z itself.
-The bf16 prefill path rounds every weight to bf16 before the MFMAs; there the
-bound follows from that arithmetic, per element:
-  * Y's error: u_w = 2^-8 relative to |A| . |W| for the weight rounding, plus
-    K * 2^-24 of fp32 accumulation slack;
-  * the gate propagates it as above, plus fp32 rounding and exp error of a
-    few ulps (2^-20 of |g u| and |z|);
-  * both sides round to bf16 once: + 2 u_o |z| with u_o = 2^-8.
+Tolerance. Every output: the common bar |gpu - oracle| <= 1e-2 (|oracle| + 1)
+per element, with one exception. The fp16 prefill path rounds each weight
+(q - 8) s to fp16 before its MFMAs (the other paths keep the weights exact and
+scale fp32 group partials), and a gated output z = silu(g) u amplifies that
+GEMM error: with g ~ 8 and u ~ 0.2 the weight rounding alone moves z by more
+than 1e-2 (|z| + 1) (seen on the full-size prefill, and reproduced on the CPU
+by rounding the weights to fp16 before an exact product). For gated outputs of
+that path the common bar is put on the GEMM result (tau_g = 1e-2 (|g| + 1),
+tau_u likewise) and carried through the gate to first order with silu' in
+[-0.1, 1.1]: 1.1 |u| tau_g + (|silu(g)| + 1.1 tau_g) tau_u, plus the common bar
+on z itself.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -51,49 +44,17 @@ def operands(w, flags, seed):
     return (bias if flags & BIAS else None), (res if flags & RES else None)
 
 
-def run_epi(lib, w, flags, bias, res, env=None, variant=None):
+def run_epi(lib, w, flags, bias, res):
     M, N, K = w.shape
     tdt = TDT[w.dtype]
     out = Guarded((M, n_out(N, flags)), tdt, SENT[w.dtype])
-    if variant is not None:
-        os.environ[env] = str(variant)
-    try:
-        lib.qgemm_w4_epilogue(out.view, dev16(w.a, tdt), dev32(w.b), dev16(w.scales, tdt), flags,
-                              bias=dev16(bias, tdt) if bias is not None else None,
-                              residual=dev16(res, tdt) if res is not None else None,
-                              group_size=w.group_size)
-    finally:
-        if variant is not None:
-            del os.environ[env]
+    lib.qgemm_w4_epilogue(out.view, dev16(w.a, tdt), dev32(w.b), dev16(w.scales, tdt), flags,
+                          bias=dev16(bias, tdt) if bias is not None else None,
+                          residual=dev16(res, tdt) if res is not None else None,
+                          group_size=w.group_size)
     got = host16(out.view)
     assert out.bands_intact(), "write outside C"
     return got
-
-
-def bound(w, flags, bias, res, rows=None):
-    M, N, K = w.shape
-    a_bits = w.a if rows is None else w.a[rows]
-    dec = DEC[w.dtype]
-    mag = np.abs(dec(a_bits)) @ np.abs(oracle.w4.dequant_w4(w.b, w.scales, w.group_size, dtype=w.dtype))
-    y = oracle.w4.qgemm_w4_f64(a_bits, w.b, w.scales, w.group_size, dtype=w.dtype)
-    prefill_bf16 = w.dtype == "bf16" and M > 16
-    u_w = 2.0 ** -8 if prefill_bf16 else 2.0 ** -11
-    e = (u_w + K * 2.0 ** -24) * mag
-    if flags & BIAS:
-        y = y + dec(bias)[None, :]
-    e = e + 2.0 ** -20 * np.abs(y)
-    if flags & GATE:
-        g, u, eg, eu = y[:, 0::2], y[:, 1::2], e[:, 0::2], e[:, 1::2]
-        z = oracle.silu(g) * u
-        e = 1.1 * np.abs(u) * eg + (np.abs(oracle.silu(g)) + 1.1 * eg) * eu + 2.0 ** -20 * (np.abs(g * u) + np.abs(z))
-    else:
-        z = y
-    if flags & RES:
-        z = z + dec(res if rows is None else res[rows])
-        e = e + 2.0 ** -22 * np.abs(z)
-    u_o = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
-    floor = 2.0 ** -24 if w.dtype == "f16" else 1e-30
-    return e * (1 + u_o) + 2 * u_o * np.abs(z) + floor
 
 
 def gate_tolerance(w, flags, bias, r, rows=None):
@@ -107,11 +68,11 @@ def gate_tolerance(w, flags, bias, r, rows=None):
     return 1.1 * np.abs(u) * tg + (np.abs(oracle.silu(g)) + 1.1 * tg) * tu + REL * (np.abs(r) + 1.0)
 
 
-def check(lib, w, flags, seed, what, rows=None, **kw):
+def check(lib, w, flags, seed, what, rows=None):
     M, N, K = w.shape
-    say(f"[w4-epi] {what}: M={M} N={N} K={K} gs={w.group_size} {w.dtype} flags={flags} {kw}")
+    say(f"[w4-epi] {what}: M={M} N={N} K={K} gs={w.group_size} {w.dtype} flags={flags}")
     bias, res = operands(w, flags, seed)
-    got = run_epi(lib, w, flags, bias, res, **kw)
+    got = run_epi(lib, w, flags, bias, res)
     if rows is not None:
         got = got[rows]
     ref = oracle.qgemm_w4_epilogue(w.a if rows is None else w.a[rows], w.b, w.scales, w.group_size, flags,
@@ -120,9 +81,7 @@ def check(lib, w, flags, seed, what, rows=None, **kw):
     dec = DEC[w.dtype]
     g, r = dec(got), dec(ref)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
-    if w.dtype == "bf16" and M > 16:
-        b = bound(w, flags, bias, res, rows)
-    elif flags & GATE:
+    if flags & GATE and w.dtype == "f16" and M > 16:
         b = gate_tolerance(w, flags, bias, r, rows)
     else:
         b = REL * (np.abs(r) + 1.0)
@@ -145,38 +104,26 @@ def test_every_flag_set_default_paths(gpu, lib, flags, dtype):
         check(lib, w, flags, 1000 + i, "default")
 
 
-@pytest.mark.parametrize("variant", range(9, 16))
-def test_decode_variants(gpu, lib, variant):
-    for flags in (BIAS, RES, GATE, BIAS | GATE | RES):
-        for dtype in ("f16", "bf16"):
-            for (M, N, K, gs) in DECODE_SHAPES[:3]:
-                w = synth.w4_inputs(M, N, K, seed=3 * M + N, group_size=gs, dtype=dtype)
-                check(lib, w, flags, 7 + flags, f"decode v{variant}", env="QG_W4_DECODE_VARIANT", variant=variant)
-
-
-@pytest.mark.parametrize("variant", range(11, 20))
-def test_prefill_variants(gpu, lib, variant):
-    for flags in (BIAS, RES, GATE, BIAS | GATE | RES):
-        for dtype in ("f16", "bf16"):
-            for (M, N, K, gs) in PREFILL_SHAPES[:3]:
-                w = synth.w4_inputs(M, N, K, seed=M + 5 * N, group_size=gs, dtype=dtype)
-                check(lib, w, flags, 9 + flags, f"prefill v{variant}", env="QG_W4_PREFILL_VARIANT",
-                      variant=variant)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(2100, 4112, 480, 32), (2200, 4352, 512, 128)], ids=["2100x4112", "2200x4352"])
+def test_prefill_more_tiles_than_cus(gpu, lib, shape, dtype):
+    """Shapes with more 128 x 256 tiles than CUs (two workgroups per CU)."""
+    M, N, K, gs = shape
+    for flags in (BIAS | RES, BIAS | GATE | RES):
+        w = synth.w4_inputs(M, N, K, seed=M + 5 * N + flags, group_size=gs, dtype=dtype)
+        check(lib, w, flags, 9 + flags, "prefill many tiles")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_full_size(gpu, lib, dtype):
-    """Decode M = 1, 16 at N = K = 4096 and the 2048 x 11008 x 4096 prefill (48
-    sampled rows), with bias and residual, ungated and gated (output N / 2)."""
-    for flags in (BIAS | RES, BIAS | GATE | RES):
-        for c in synth.W4_DECODE:
-            if c["M"] in (1, 16):
-                check(lib, synth.w4_inputs(**c, dtype=dtype), flags, 21, "decode full")
-        w = synth.w4_inputs(**synth.W4_PREFILL, dtype=dtype)
-        M = w.shape[0]
-        rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(2).choice(M, 48, replace=False)]))
-        d = check(lib, w, flags, 22, "prefill full", rows=rows)
-        say("  worst error / tolerance", d)
+@pytest.mark.parametrize("flags", [BIAS | RES, BIAS | GATE | RES], ids=["bias_res", "bias_gate_res"])
+def test_full_size(gpu, lib, dtype, flags):
+    """Decode M = 1, 16 at N = K = 4096 and the 2048 x 11008 x 4096 prefill, with
+    bias and residual, ungated and gated (output N / 2), every element."""
+    for c in synth.W4_DECODE:
+        if c["M"] in (1, 16):
+            check(lib, synth.w4_inputs(**c, dtype=dtype), flags, 21, "decode full")
+    d = check(lib, synth.w4_inputs(**synth.W4_PREFILL, dtype=dtype), flags, 22, "prefill full")
+    say("  worst error / tolerance", d)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
