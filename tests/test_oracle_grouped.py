@@ -164,3 +164,95 @@ def test_epilogue_bias_row_is_the_groups_expert():
     for g, e in enumerate(ids):
         rows = slice(a_off[g], a_off[g + 1])
         assert np.all(c[rows] == (SENT if e < 0 else bias[e])), g
+
+
+# ---------------------------------------------------------------- a_plane_splits (fused LoRA QKV planes)
+
+GOLD_PLANES = os.path.join(os.path.dirname(__file__), "golden", "grouped_planes_worked_example.json")
+
+
+def _bits(x):
+    return nm.bf16_bits_of(np.asarray(x, dtype=np.float64))
+
+
+def test_planes_worked_example_from_fixture():
+    g = json.load(open(GOLD_PLANES))
+    c = oracle.grouped_gemm(_bits(g["C_prior"]), _bits(g["A"]), np.array(g["a_offsets"], np.uint32), _bits(g["B"]),
+                            np.array(g["expert_ids"], np.int32), np.array(g["usage"], np.uint32),
+                            a_plane_splits=g["a_plane_splits"])
+    assert np.array_equal(nm.decode_bf16(c), np.array(g["C_expected"], dtype=np.float64))
+
+
+def test_planes_off_is_the_plain_product():
+    d = synth.grouped_inputs(seed=30, E=5, T=70, K=48, N=40, skip_frac=0.2)
+    c0 = np.full((70, 40), SENT, np.uint16)
+    plain = oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, d.usage)
+    assert np.array_equal(oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, d.usage,
+                                              a_plane_splits=(0, 0)), plain)
+
+
+def _plane_of(n, s0, s1):
+    return 0 if n < s0 else (1 if n < s0 + s1 else 2)
+
+
+def test_planes_route_columns_exactly():
+    """B[e] = c_e I and plane p of A = (p + 1) X: column n of row r is c_e (p(n) + 1) X[r, n],
+    exact in bf16 (power-of-two factors and small integers), for both B layouts and
+    splits that include an empty plane."""
+    E, T, K = 4, 40, 48
+    rng = np.random.default_rng(31)
+    x = rng.integers(-8, 9, size=(T, K)).astype(np.float64)
+    a = _bits(np.concatenate([x, 2 * x, 3 * x]))
+    fac = np.ldexp(1.0, np.arange(E) - 2)
+    b = _bits(fac[:, None, None] * np.eye(K)[None])
+    a_off = np.array([0, 7, 7, 30, 40], np.uint32)
+    ids = np.array([2, 0, -1, 3], np.int32)
+    for s0, s1 in [(16, 8), (0, 24), (48, 0), (5, 40)]:
+        for tb in (True, False):
+            c = oracle.grouped_gemm(np.full((T, K), SENT, np.uint16), a, a_off, b, ids, [23, 4], transpose_b=tb,
+                                    a_plane_splits=(s0, s1))
+            got = nm.decode_bf16(c)
+            for g in range(4):
+                r0, r1 = int(a_off[g]), int(a_off[g + 1])
+                if ids[g] < 0:
+                    assert np.all(c[r0:r1] == SENT)
+                    continue
+                for n in range(K):
+                    want = fac[ids[g]] * (_plane_of(n, s0, s1) + 1) * x[r0:r1, n]
+                    assert np.array_equal(got[r0:r1, n], want), (s0, s1, tb, g, n)
+
+
+def test_planes_brute_force_integers():
+    """Scalar loops over rows, columns and K with the plane looked up per column; small
+    integer operands keep every sum exact, so the results agree bit for bit."""
+    rng = np.random.default_rng(32)
+    E, T, K, N = 3, 11, 5, 9
+    a = rng.integers(-4, 5, size=(3 * T, K)).astype(np.float64)
+    b = rng.integers(-4, 5, size=(E, N, K)).astype(np.float64)
+    a_off = np.array([0, 4, 4, 9, 11], np.uint32)
+    ids = np.array([1, 2, 0, -1], np.int32)
+    s0, s1 = 2, 4
+    c = oracle.grouped_gemm(np.full((T, N), SENT, np.uint16), _bits(a), a_off, _bits(b), ids, [5, 4],
+                            a_plane_splits=(s0, s1))
+    want = np.full((T, N), np.nan)
+    for g in range(4):
+        if ids[g] < 0:
+            continue
+        for r in range(int(a_off[g]), int(a_off[g + 1])):
+            for n in range(N):
+                p = _plane_of(n, s0, s1)
+                want[r, n] = sum(a[p * T + r, k] * b[ids[g], n, k] for k in range(K))
+    written = ~np.isnan(want)
+    assert np.array_equal(nm.decode_bf16(c)[written], want[written])
+    assert np.all(c[~written] == SENT)
+
+
+def test_planes_reject_bad_shapes():
+    d = synth.grouped_inputs(seed=33, E=2, T=10, K=16, N=16)
+    c0 = np.full((10, 16), SENT, np.uint16)
+    import pytest
+    with pytest.raises(ValueError):   # A must hold three planes
+        oracle.grouped_gemm(c0, d.a, d.a_offsets, d.b, d.expert_ids, d.usage, a_plane_splits=(8, 4))
+    a3 = np.concatenate([d.a, d.a, d.a])
+    with pytest.raises(ValueError):   # splits beyond N
+        oracle.grouped_gemm(c0, a3, d.a_offsets, d.b, d.expert_ids, d.usage, a_plane_splits=(12, 8))

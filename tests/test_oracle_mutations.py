@@ -195,3 +195,38 @@ def test_grouped_w4_mutation_is_caught(kind, monkeypatch):
         except AssertionError:
             failures += 1
     assert failures >= 1, kind
+
+
+def _plane_columns_variant(kind):
+    from oracle import grouped as og
+    orig = og.plane_columns
+
+    def f(a_plane_splits, n):
+        r = orig(a_plane_splits, n)
+        if len(r) == 1:
+            return r
+        (a0, a1), (b0, b1), (c0, c1) = r
+        if kind == "boundary_off_by_one":
+            return [(a0, a1 + 1), (b0 + 1, b1), (c0, c1)] if a1 < b1 else r
+        if kind == "planes_reversed":      # the first column range reads plane 2, the last plane 0
+            return [(c0, c1), (b0, b1), (a0, a1)]
+        if kind == "second_split_absolute":  # s1 taken as an end column instead of a size
+            s1 = b1 - b0
+            return [(a0, a1), (a1, max(a1, s1)), (max(a1, s1), n)]
+        return r
+    return f
+
+
+@pytest.mark.parametrize("kind", ["boundary_off_by_one", "planes_reversed", "second_split_absolute"])
+def test_plane_split_mutation_is_caught(kind, monkeypatch):
+    import test_oracle_grouped as tg
+    from oracle import grouped as og
+    monkeypatch.setattr(og, "plane_columns", _plane_columns_variant(kind))
+    failed = 0
+    for pin in (tg.test_planes_worked_example_from_fixture, tg.test_planes_route_columns_exactly,
+                tg.test_planes_brute_force_integers):
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed += 1
+    assert failed > 0, f"no pin catches the {kind} mutation"
