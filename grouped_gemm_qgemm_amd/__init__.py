@@ -11,10 +11,13 @@ Entry points (same names as the C ABI):
     qgemm_w4_nk(c, a, b_packed_nk, scales_nk, group_size=128, pack_factor=8)
     qgemm_w4_epilogue(c, a, b_packed, scales, epilogue, bias=None, residual=None,
                       group_size=128, pack_factor=8)
-    grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True)
+    grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b=True,
+                 a_plane_splits=(0, 0))
     grouped_gemm_w4(c, a, a_offsets, b_packed, scales, expert_ids, expert_usage_stats,
                     group_size=128, pack_factor=8)
-    grouped_gemm_epilogue / grouped_gemm_w4_epilogue(..., epilogue, bias=None, residual=None, ...)
+    grouped_gemm_epilogue(c, a, a_offsets, b, expert_ids, expert_usage_stats, epilogue, bias=None,
+                          residual=None, transpose_b=True, a_plane_splits=(0, 0))
+    grouped_gemm_w4_epilogue(..., epilogue, bias=None, residual=None, ...)
     k_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
                                 weight_scale, kv_blocks, cache_lengths, page_table,
                                 layer_idx, scales_granularity_mnk=(1, 128, 128),
@@ -91,13 +94,13 @@ def load(path: str | None = None):
                                       ctypes.c_void_p]
     lib.qgemm_w4_epilogue.restype = ctypes.c_int
     lib.grouped_gemm.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
-                                 ctypes.c_void_p]
+                                 ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]
     lib.grouped_gemm.restype = ctypes.c_int
     lib.grouped_gemm_w4.argtypes = [T, T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p]
     lib.grouped_gemm_w4.restype = ctypes.c_int
     lib.grouped_gemm_epilogue.argtypes = [T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
-                                          ctypes.c_int32, T, T, ctypes.c_void_p]
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, T, T, ctypes.c_void_p]
     lib.grouped_gemm_epilogue.restype = ctypes.c_int
     lib.grouped_gemm_w4_epilogue.argtypes = [T, T, T, T, T, T, ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32,
                                              ctypes.c_int32, ctypes.c_int32, T, T, ctypes.c_void_p]
@@ -195,15 +198,21 @@ def qgemm_w4_epilogue(c, a, b_packed, scales, epilogue: int, bias=None, residual
     return st
 
 
+def _splits(a_plane_splits):
+    return (ctypes.c_int32 * 2)(*[int(v) for v in a_plane_splits])
+
+
 def grouped_gemm(c, a, a_offsets, b, expert_ids, expert_usage_stats, transpose_b: bool = True,
-                 stream=None, raise_on_error: bool = True) -> int:
-    """Rows of each active, non-skipped group g: C = A . B[expert_ids[g]]^T (bf16)."""
+                 a_plane_splits=(0, 0), stream=None, raise_on_error: bool = True) -> int:
+    """Rows of each active, non-skipped group g: C = A . B[expert_ids[g]]^T (bf16); with
+    a_plane_splits (s0, s1) != (0, 0), A is [3 T, K] and column ranges [0, s0),
+    [s0, s0 + s1), [s0 + s1, N) read planes 0, 1, 2 of A."""
     lib = load()
     usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
     st = lib.grouped_gemm(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
                           ctypes.byref(describe(a_offsets, _u32(a_offsets))), ctypes.byref(describe(b)),
                           ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)),
-                          _stream(stream))
+                          _splits(a_plane_splits), _stream(stream))
     if raise_on_error:
         _check(st)
     return st
@@ -228,14 +237,16 @@ def _opt(t):
 
 
 def grouped_gemm_epilogue(c, a, a_offsets, b, expert_ids, expert_usage_stats, epilogue: int, bias=None,
-                          residual=None, transpose_b: bool = True, stream=None, raise_on_error: bool = True) -> int:
+                          residual=None, transpose_b: bool = True, a_plane_splits=(0, 0), stream=None,
+                          raise_on_error: bool = True) -> int:
     """grouped_gemm followed by the fixed epilogue (bias [E, N] by expert, SiLU gate, residual)."""
     lib = load()
     usage = (ctypes.c_uint32 * 2)(*[int(v) for v in expert_usage_stats])
     st = lib.grouped_gemm_epilogue(ctypes.byref(describe(c)), ctypes.byref(describe(a)),
                                    ctypes.byref(describe(a_offsets, _u32(a_offsets))), ctypes.byref(describe(b)),
-                                   ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)), int(epilogue),
-                                   _opt(bias), _opt(residual), _stream(stream))
+                                   ctypes.byref(describe(expert_ids)), usage, int(bool(transpose_b)),
+                                   _splits(a_plane_splits), int(epilogue), _opt(bias), _opt(residual),
+                                   _stream(stream))
     if raise_on_error:
         _check(st)
     return st

@@ -166,8 +166,9 @@ qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_ten
 
 static qg_status grouped_gemm_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                    const qg_tensor* b, const qg_tensor* expert_ids,
-                                   const uint32_t* expert_usage_stats_host, int32_t transpose_b, int32_t epilogue,
-                                   const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
+                                   const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                                   const int32_t* a_plane_splits, int32_t epilogue, const qg_tensor* bias,
+                                   const qg_tensor* residual, hipStream_t stream) {
   if (!c || !a || !a_offsets || !b || !expert_ids || !expert_usage_stats_host) return QG_ERR_NULL;
   if (c->rank != 2 || a->rank != 2 || a_offsets->rank != 1 || b->rank != 3 || expert_ids->rank != 1)
     return QG_ERR_RANK;
@@ -177,23 +178,30 @@ static qg_status grouped_gemm_impl(const qg_tensor* c, const qg_tensor* a, const
   if ((st = check_tensor(a_offsets, 1, QG_U32)) != QG_OK) return st;
   if ((st = check_tensor(b, 3, QG_BF16)) != QG_OK) return st;
   if ((st = check_tensor(expert_ids, 1, QG_I32)) != QG_OK) return st;
-  const int64_t T = a->shape[0], K = a->shape[1];
+  const int64_t T = c->shape[0], K = a->shape[1];
   const int64_t E = b->shape[0];
   const int64_t N = transpose_b ? b->shape[1] : b->shape[2];
   const int64_t Kb = transpose_b ? b->shape[2] : b->shape[1];
   const int64_t G = expert_ids->shape[0];
+  // planes of A (fused LoRA QKV): splits (s0, s1) != (0, 0) cut the columns into
+  // [0, s0), [s0, s0 + s1), [s0 + s1, N), read from three planes of T rows of A
+  const int64_t s0 = a_plane_splits ? a_plane_splits[0] : 0, s1 = a_plane_splits ? a_plane_splits[1] : 0;
+  const bool planes = s0 != 0 || s1 != 0;
+  if (s0 < 0 || s1 < 0 || s0 + s1 > N) return QG_ERR_SHAPE;
+  if (s0 % 8 != 0 || s1 % 8 != 0) return QG_ERR_ALIGN;   // 8-aligned like N; gate pairs stay in one plane
+  if (a->shape[0] != (planes ? 3 * T : T)) return QG_ERR_SHAPE;
   if (epilogue & ~(QG_EPI_BIAS | QG_EPI_RESIDUAL | QG_EPI_SILU_GATE)) return QG_ERR_INVALID_ARG;
   const bool gate = (epilogue & QG_EPI_SILU_GATE) != 0;
   if (gate && N % 16 != 0) return QG_ERR_ALIGN;   // (gate, up) pairs, and an 8-aligned output
   const int64_t N_out = gate ? N / 2 : N;
-  if (c->shape[0] != T || c->shape[1] != N_out || Kb != K) return QG_ERR_SHAPE;
+  if (c->shape[1] != N_out || Kb != K) return QG_ERR_SHAPE;
   if (a_offsets->shape[0] != G + 1) return QG_ERR_SHAPE;
   const uint32_t num_active = expert_usage_stats_host[1];
   if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
   if (K % 8 != 0 || N % 8 != 0) return QG_ERR_ALIGN;
   qg::Epilogue epi;
   if ((st = check_epilogue(epilogue, bias, residual, QG_BF16, E, T, N, &epi)) != QG_OK) return st;
-  if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
+  if (3 * T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   if (N * K * 2 > 0xFFFFFFFFLL) return QG_ERR_UNSUPPORTED;   // 32-bit buffer offsets within an expert
   if (num_active == 0 || T == 0 || N == 0 || E == 0) return QG_OK;
   if (K == 0) return QG_ERR_UNSUPPORTED;
@@ -201,23 +209,25 @@ static qg_status grouped_gemm_impl(const qg_tensor* c, const qg_tensor* a, const
                     static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint16_t*>(b->data),
                     static_cast<const int32_t*>(expert_ids->data), T, N, K, E, (int)num_active,
                     (int)expert_usage_stats_host[0], device_cus(), transpose_b ? 1 : 0, epi};
+  p.planes = planes ? qg::Planes{(int)s0, (int)(s0 + s1), (int)T} : qg::Planes{(int)N, (int)N, 0};
   return launch_status(qg::launch_grouped_bf16(p, stream));
 }
 
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                        const qg_tensor* b, const qg_tensor* expert_ids,
                        const uint32_t* expert_usage_stats_host, int32_t transpose_b,
-                       hipStream_t stream) {
-  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b, 0, nullptr,
-                           nullptr, stream);
+                       const int32_t* a_plane_splits_host, hipStream_t stream) {
+  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b,
+                           a_plane_splits_host, 0, nullptr, nullptr, stream);
 }
 
 qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                 const qg_tensor* b, const qg_tensor* expert_ids,
-                                const uint32_t* expert_usage_stats_host, int32_t transpose_b, int32_t epilogue,
-                                const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream) {
-  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b, epilogue, bias,
-                           residual, stream);
+                                const uint32_t* expert_usage_stats_host, int32_t transpose_b,
+                                const int32_t* a_plane_splits_host, int32_t epilogue, const qg_tensor* bias,
+                                const qg_tensor* residual, hipStream_t stream) {
+  return grouped_gemm_impl(c, a, a_offsets, b, expert_ids, expert_usage_stats_host, transpose_b,
+                           a_plane_splits_host, epilogue, bias, residual, stream);
 }
 
 static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,

@@ -37,6 +37,21 @@ constexpr int GBM = 16 * GMAXMT;
 
 }  // namespace
 
+// Column tile nt of a row chunk -> its plane, first column and column limit.
+// The planes' column ranges are [0, pb1), [pb1, pb2) and [pb2, N), each cut
+// into tiles of GBN columns; without planes pb1 = pb2 = N (one range). A plane
+// p reads its activation rows from A + p * plane_rows * K.
+struct PlaneTile {
+  int plane, n0, n_lim;
+};
+
+__device__ __forceinline__ PlaneTile plane_tile(const Planes& pl, int nt, int N, int gbn) {
+  const int t0 = (pl.pb1 + gbn - 1) / gbn, t1 = (pl.pb2 - pl.pb1 + gbn - 1) / gbn;
+  if (nt < t0) return PlaneTile{0, nt * gbn, pl.pb1};
+  if (nt < t0 + t1) return PlaneTile{1, pl.pb1 + (nt - t0) * gbn, pl.pb2};
+  return PlaneTile{2, pl.pb2 + (nt - t0 - t1) * gbn, N};
+}
+
 // One work tile with MT row tiles over weights stored [E, K, N]. D = steps of
 // prefetch (ring depth).
 //
@@ -70,11 +85,13 @@ struct WRing {
 // out that C aliases them).
 // EPI false: the plain store only (the kernels without an epilogue are their
 // own instantiations, so the epilogue code costs them nothing).
+// Columns at or past n_lim (the end of the tile's plane, at most N) belong to
+// another tile and are not stored.
 template <int MT, bool EPI>
-__device__ __forceinline__ void grouped_store(uint16_t* __restrict__ C, const float4_t (&acc)[MT], int N, int e,
-                                              int r_begin, int rows, int col, int q, const Epilogue& ep) {
+__device__ __forceinline__ void grouped_store(uint16_t* __restrict__ C, const float4_t (&acc)[MT], int N, int n_lim,
+                                              int e, int r_begin, int rows, int col, int q, const Epilogue& ep) {
   if (!EPI || ep.flags == 0) {
-    if (col < N) {
+    if (col < n_lim) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -89,8 +106,8 @@ __device__ __forceinline__ void grouped_store(uint16_t* __restrict__ C, const fl
   const bool gate = (ep.flags & EPI_SILU_GATE) != 0;
   const int NO = gate ? N / 2 : N;
   const int oc = gate ? col / 2 : col;
-  const bool owner = col < N && (!gate || (col & 1) == 0);   // lanes that store
-  const float b = (ep.flags & EPI_BIAS) && col < N ? bf2f(ep.bias[(size_t)e * N + col]) : 0.f;
+  const bool owner = col < n_lim && (!gate || (col & 1) == 0);   // lanes that store
+  const float b = (ep.flags & EPI_BIAS) && col < n_lim ? bf2f(ep.bias[(size_t)e * N + col]) : 0.f;
   float res[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -122,7 +139,7 @@ template <int W, int MT, int D, int P, bool EPI>
 __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                              u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
-                                             int rows, int n0, const Epilogue& ep) {
+                                             int rows, int n0, int n_lim, const Epilogue& ep) {
   constexpr int FPW = (MT + W - 1) / W;   // activation fragments per wave per step
   static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   const int lane = threadIdx.x & 63;
@@ -229,7 +246,7 @@ __device__ __forceinline__ void grouped_tile(uint16_t* __restrict__ C, const uin
   }
 
   // ---- epilogue: bf16 RNE ----
-  grouped_store<MT, EPI>(C, acc, N, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
+  grouped_store<MT, EPI>(C, acc, N, n_lim, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
 }
 
 // Transposed weights ([E, N, K]) staged through LDS in 64-deep steps. A 16-byte
@@ -244,7 +261,7 @@ template <int W, int MT, int D, bool EPI>
 __device__ __forceinline__ void grouped_tile_wl(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                                 const uint16_t* __restrict__ B, u32x4_t* __restrict__ ring,
                                                 u32x4_t* __restrict__ wring, int N, int K, int e, int r_begin,
-                                                int rows, int n0, const Epilogue& ep) {
+                                                int rows, int n0, int n_lim, const Epilogue& ep) {
   constexpr int FPW = (MT + W - 1) / W;
   static_assert(FPW * W <= GMAXMT, "LDS slots for every loaded fragment");
   constexpr int WSLOT = 16 * W * 8;   // 16-byte chunks of one weight step
@@ -341,7 +358,7 @@ __device__ __forceinline__ void grouped_tile_wl(uint16_t* __restrict__ C, const 
     step(ns & 1, ra[0], rb[0]);
   }
 
-  grouped_store<MT, EPI>(C, acc, N, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
+  grouped_store<MT, EPI>(C, acc, N, n_lim, e, r_begin, rows, n0 + wave * 16 + r16, q, ep);
 }
 
 // Persistent workgroups over the same tile list, weights through LDS (above).
@@ -349,7 +366,7 @@ template <int W, int D, int OCC, bool EPI>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n, int per_xcd, Epilogue ep) {
+    int tiles_n, int per_xcd, Planes pl, Epilogue ep) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * 2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * 16 * W * 8];
   constexpr int GBN = 16 * W;
@@ -364,19 +381,21 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_wl_kernel(
     const int e = __builtin_amdgcn_readfirstlane(ids[g]);
     const int r_begin = __builtin_amdgcn_readfirstlane((int)a_off[g] + chunk * GBM);
     const int rows = __builtin_amdgcn_readfirstlane(min(GBM, (int)a_off[g + 1] - r_begin));
-    const int n0 = nt * GBN;
+    const PlaneTile pt = plane_tile(pl, nt, N, GBN);
+    const int n0 = pt.n0, n_lim = pt.n_lim;
+    const uint16_t* Ap = A + (size_t)pt.plane * pl.plane_rows * K;
     // two activation fragments per wave per sub-step beyond four row tiles
     // (four waves): half as many steps in flight
     constexpr int D5 = W >= 8 ? D : (D + 1) / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile_wl<W, 1, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 2: grouped_tile_wl<W, 2, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 3: grouped_tile_wl<W, 3, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 4: grouped_tile_wl<W, 4, D, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 5: grouped_tile_wl<W, 5, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 6: grouped_tile_wl<W, 6, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 7: grouped_tile_wl<W, 7, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      default: grouped_tile_wl<W, 8, D5, EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 1: grouped_tile_wl<W, 1, D, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 2: grouped_tile_wl<W, 2, D, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 3: grouped_tile_wl<W, 3, D, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 4: grouped_tile_wl<W, 4, D, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 5: grouped_tile_wl<W, 5, D5, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 6: grouped_tile_wl<W, 6, D5, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 7: grouped_tile_wl<W, 7, D5, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      default: grouped_tile_wl<W, 8, D5, EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
     }
   }
 }
@@ -389,7 +408,7 @@ template <int W, int D, int OCC, int P, bool EPI>
 __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint16_t* __restrict__ B, const int32_t* __restrict__ ids, int N, int K, int num_active,
-    int tiles_n, int per_xcd, Epilogue ep) {
+    int tiles_n, int per_xcd, Planes pl, Epilogue ep) {
   __shared__ __attribute__((aligned(16))) u32x4_t ring[2 * GMAXMT * kWave];
   __shared__ __attribute__((aligned(16))) u32x4_t wring[2 * WRing<W>::SLOT];
 
@@ -408,20 +427,22 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
     const int e = __builtin_amdgcn_readfirstlane(ids[g]);
     const int r_begin = __builtin_amdgcn_readfirstlane((int)a_off[g] + chunk * GBM);
     const int rows = __builtin_amdgcn_readfirstlane(min(GBM, (int)a_off[g + 1] - r_begin));
-    const int n0 = nt * GBN;
+    const PlaneTile pt = plane_tile(pl, nt, N, GBN);
+    const int n0 = pt.n0, n_lim = pt.n_lim;
+    const uint16_t* Ap = A + (size_t)pt.plane * pl.plane_rows * K;
     // With four waves, tiles of more than four row tiles load two activation
     // fragments per wave per step, so they run half as many steps ahead: the
     // same registers and about the same bytes in flight.
     constexpr int D5 = W >= 8 ? D : D / 2;
     switch ((rows + 15) >> 4) {
-      case 1: grouped_tile<W, 1, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 2: grouped_tile<W, 2, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 3: grouped_tile<W, 3, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 4: grouped_tile<W, 4, D, fit_group<D, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 5: grouped_tile<W, 5, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 6: grouped_tile<W, 6, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      case 7: grouped_tile<W, 7, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
-      default: grouped_tile<W, 8, D5, fit_group<D5, P>(), EPI>(C, A, B, ring, wring, N, K, e, r_begin, rows, n0, ep); break;
+      case 1: grouped_tile<W, 1, D, fit_group<D, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 2: grouped_tile<W, 2, D, fit_group<D, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 3: grouped_tile<W, 3, D, fit_group<D, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 4: grouped_tile<W, 4, D, fit_group<D, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 5: grouped_tile<W, 5, D5, fit_group<D5, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 6: grouped_tile<W, 6, D5, fit_group<D5, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      case 7: grouped_tile<W, 7, D5, fit_group<D5, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
+      default: grouped_tile<W, 8, D5, fit_group<D5, P>(), EPI>(C, Ap, B, ring, wring, N, K, e, r_begin, rows, n0, n_lim, ep); break;
     }
   }
 }
@@ -431,30 +452,32 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
 // CU. Weights [E, K, N]: eight waves, eight 32-deep steps in flight issued in
 // pairs, one workgroup per CU.
 hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream) {
-  constexpr int W = 8;
-  const int tiles_n = (int)((p.N + 16 * W - 1) / (16 * W));
+  constexpr int W = 8, GBN = 16 * W;
+  // column tiles per row chunk: each plane's columns in tiles of their own
+  const int tiles_n = (int)((p.planes.pb1 + GBN - 1) / GBN + (p.planes.pb2 - p.planes.pb1 + GBN - 1) / GBN +
+                            (p.N - p.planes.pb2 + GBN - 1) / GBN);
   if (p.transpose_b) {
     constexpr int D = 4, OCC = 2;
     const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
     if (p.epi.flags)
       hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
                          p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                         p.epi);
+                         p.planes, p.epi);
     else
       hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
                          p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                         p.epi);
+                         p.planes, p.epi);
   } else {
     constexpr int D = 8, OCC = 1, P = 2;
     const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
     if (p.epi.flags)
       hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, P, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
                          p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                         p.epi);
+                         p.planes, p.epi);
     else
       hipLaunchKernelGGL((grouped_bf16_kernel<W, D, OCC, P, false>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
                          p.A, p.a_offsets, p.B, p.expert_ids, (int)p.N, (int)p.K, p.num_active, tiles_n, grid / 8,
-                         p.epi);
+                         p.planes, p.epi);
   }
   return hipGetLastError();
 }

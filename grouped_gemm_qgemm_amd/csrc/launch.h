@@ -45,6 +45,14 @@ struct W4GroupedArgs {
   Epilogue epi;               // C is [T, N / 2] with EPI_SILU_GATE; bias [E, N]
 };
 
+// Planes of A for the grouped GEMM (fused LoRA QKV): output columns [0, pb1),
+// [pb1, pb2) and [pb2, N) read their activation rows from planes 0, 1 and 2 of
+// A, plane p starting at row p * plane_rows. Without planes pb1 = pb2 = N.
+struct Planes {
+  int pb1, pb2;
+  int plane_rows;
+};
+
 struct GroupedArgs {
   uint16_t* C;              // bf16 [T, N]
   const uint16_t* A;        // bf16 [T, K]
@@ -57,6 +65,7 @@ struct GroupedArgs {
   int num_cus;
   int transpose_b;
   Epilogue epi;             // C is [T, N / 2] with EPI_SILU_GATE; bias [E, N]
+  Planes planes;
 };
 
 struct KProjArgs {

@@ -153,22 +153,30 @@ qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_ten
 /*
  * grouped_gemm - per-group GEMM over routed rows (MoE expert GEMM)
  *
- * Follows "grouped_matmul_sm100_persistent" (Args): a_offsets is the per-expert
- * prefix sum of A row offsets; expert_ids gives each group's expert, negative
- * entries skip the group; expert_usage_stats[1] is the active count; transpose_b
- * (Parameters) says each expert matrix is stored [N, K].
+ * Follows "grouped_matmul_sm100_persistent" (Args): a_offsets is a prefix sum of
+ * the groups' row counts; expert_ids gives each group's expert, and a group
+ * whose id is negative is not computed; expert_usage_stats[1] is the active
+ * count; transpose_b (Parameters) says each expert matrix is stored [N, K];
+ * a_plane_splits (Parameters) gives the planes of A of a fused LoRA QKV product.
  *
  *   c          bf16 [T, N]   output; for g < num_active with expert_ids[g] >= 0,
  *                            rows a_offsets[g] .. a_offsets[g+1]-1 are set to
  *                            A[rows] . B[expert_ids[g]]^T (transpose_b != 0) or
  *                            A[rows] . B[expert_ids[g]] (transpose_b == 0); all
  *                            other rows keep their prior content
- *   a          bf16 [T, K]
+ *   a          bf16 [T, K], or [3 T, K] with planes (below)
  *   a_offsets  u32  [G + 1]  non-decreasing, a_offsets[num_active] <= T
  *   b          bf16 [E, N, K] when transpose_b != 0, else [E, K, N]
  *   expert_ids i32  [G]      each < E, or negative to skip
  *   expert_usage_stats_host  HOST u32[2]: [1] = num_active (<= G) groups to
  *                            process; [0] = largest rows-per-group (a hint only)
+ *   a_plane_splits_host      HOST i32[2] (s0, s1), or NULL for (0, 0). (0, 0):
+ *                            no planes. Otherwise a holds three planes of T rows
+ *                            (the LoRA shrink outputs of q, k, v) and output
+ *                            columns [0, s0), [s0, s0 + s1), [s0 + s1, N) read
+ *                            their rows from planes 0, 1, 2: row r of plane p is
+ *                            a row p T + r. s0, s1 >= 0, s0 + s1 <= N
+ *                            (QG_ERR_SHAPE) and multiples of 8 (QG_ERR_ALIGN).
  *
  * K and N must be multiples of 8 (QG_ERR_ALIGN). Accumulation is fp32; results are
  * rounded to bf16 (nearest-even). The device-side tables are not re-validated:
@@ -178,7 +186,7 @@ qg_status qgemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_ten
 qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                        const qg_tensor* b, const qg_tensor* expert_ids,
                        const uint32_t* expert_usage_stats_host, int32_t transpose_b,
-                       hipStream_t stream);
+                       const int32_t* a_plane_splits_host, hipStream_t stream);
 
 /*
  * grouped_gemm_epilogue - grouped_gemm with a fixed epilogue
@@ -193,13 +201,13 @@ qg_status grouped_gemm(const qg_tensor* c, const qg_tensor* a, const qg_tensor* 
  *                              else QG_ERR_ALIGN), N otherwise
  *
  * Rows of skipped or unprocessed groups keep their prior content. Everything else
- * as grouped_gemm; epilogue 0 is grouped_gemm.
+ * (planes included) as grouped_gemm; epilogue 0 is grouped_gemm.
  */
 qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                 const qg_tensor* b, const qg_tensor* expert_ids,
                                 const uint32_t* expert_usage_stats_host, int32_t transpose_b,
-                                int32_t epilogue, const qg_tensor* bias, const qg_tensor* residual,
-                                hipStream_t stream);
+                                const int32_t* a_plane_splits_host, int32_t epilogue,
+                                const qg_tensor* bias, const qg_tensor* residual, hipStream_t stream);
 
 /*
  * grouped_gemm_w4 - per-group W4A16 GEMM over routed rows (MoE with 4-bit experts)

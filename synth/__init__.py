@@ -143,8 +143,9 @@ class GroupedInputs:
 
 
 def grouped_inputs(seed: int = 4, E: int = 64, T: int = 4096, K: int = 2048, N: int = 1408,
-                   skip_frac: float = 0.10, transpose_b: bool = True) -> GroupedInputs:
-    """Grouped workload. Draw order: counts, skipped groups, A, B."""
+                   skip_frac: float = 0.10, transpose_b: bool = True, a_planes: int = 1) -> GroupedInputs:
+    """Grouped workload. Draw order: counts, skipped groups, A, B. a_planes = 3
+    draws A as three planes of T rows ([3 T, K], fused LoRA QKV inputs)."""
     rng = np.random.default_rng(seed)
     counts = rng.multinomial(T, [1.0 / E] * E)
     a_off = np.zeros(E + 1, dtype=np.uint32)
@@ -153,7 +154,7 @@ def grouped_inputs(seed: int = 4, E: int = 64, T: int = 4096, K: int = 2048, N: 
     skip = rng.choice(E, n_skip, replace=False)
     ids = np.arange(E, dtype=np.int32)
     ids[skip] = -1
-    a = bf16_bits(rng.normal(0.0, 0.02, size=(T, K)))
+    a = bf16_bits(rng.normal(0.0, 0.02, size=(a_planes * T, K)))
     bshape = (E, N, K) if transpose_b else (E, K, N)
     b = bf16_bits(rng.normal(0.0, 0.02, size=bshape))
     usage = np.array([counts.max(), E], dtype=np.uint32)

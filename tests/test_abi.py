@@ -164,10 +164,11 @@ def test_w4_epilogue_rejections(lib):
     assert epi_call(lib, c0, a0, b0, s0, 0) == QG.OK
 
 
-def gg_call(lib, c, a, off, b, ids, usage, tb=1):
+def gg_call(lib, c, a, off, b, ids, usage, tb=1, splits=None):
     u = (ctypes.c_uint32 * 2)(*usage)
+    sp = (ctypes.c_int32 * 2)(*splits) if splits is not None else None
     return lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
-                            ctypes.byref(ids), u, tb, None)
+                            ctypes.byref(ids), u, tb, sp, None)
 
 
 def test_grouped_rejections(lib):
@@ -196,7 +197,22 @@ def test_grouped_rejections(lib):
     assert gg_call(lib, c, a, off, b, ids, [8, 0]) == QG.OK       # nothing active: no-op
     u = (ctypes.c_uint32 * 2)(8, 4)
     assert lib.grouped_gemm(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(b),
-                            ctypes.byref(ids), None, 1, None) == QG.ERR_NULL
+                            ctypes.byref(ids), None, 1, None, None) == QG.ERR_NULL
+
+
+def test_grouped_plane_split_rejections(lib):
+    """a_plane_splits (fused LoRA QKV planes of A): shape and alignment checks."""
+    bb = Buf()
+    T, K, N, E, G = 32, 64, 48, 4, 4
+    c, a, a3 = bb.t((T, N), QG.BF16), bb.t((T, K), QG.BF16), bb.t((3 * T, K), QG.BF16)
+    off, b, ids = bb.t((G + 1,), QG.U32), bb.t((E, N, K), QG.BF16), bb.t((G,), QG.I32)
+    assert gg_call(lib, c, a, off, b, ids, [8, 0], splits=(8, 16)) == QG.ERR_SHAPE    # A must hold 3 planes
+    assert gg_call(lib, c, a3, off, b, ids, [8, 0]) == QG.ERR_SHAPE                    # planes off: A is [T, K]
+    assert gg_call(lib, c, a3, off, b, ids, [8, 0], splits=(4, 8)) == QG.ERR_ALIGN
+    assert gg_call(lib, c, a3, off, b, ids, [8, 0], splits=(40, 16)) == QG.ERR_SHAPE  # past N
+    assert gg_call(lib, c, a3, off, b, ids, [8, 0], splits=(-8, 16)) == QG.ERR_SHAPE
+    assert gg_call(lib, c, a3, off, b, ids, [8, 0], splits=(8, 16)) == QG.OK          # nothing active: no-op
+    assert gg_call(lib, c, a, off, b, ids, [8, 0], splits=(0, 0)) == QG.OK
 
 
 def gw_call(lib, c, a, off, b, s, ids, usage, gs=128, pf=8):
@@ -236,7 +252,7 @@ def test_grouped_epilogue_rejections(lib):
 
     def ge(c, flags, bias=None, res=None, bm=b):
         return lib.grouped_gemm_epilogue(ctypes.byref(c), ctypes.byref(a), ctypes.byref(off), ctypes.byref(bm),
-                                         ctypes.byref(ids), u, 1, flags, r(bias), r(res), None)
+                                         ctypes.byref(ids), u, 1, None, flags, r(bias), r(res), None)
     c, half = bb.t((T, N), QG.BF16), bb.t((T, N // 2), QG.BF16)
     assert ge(c, 8) == QG.ERR_INVALID_ARG
     assert ge(c, q.EPI_BIAS) == QG.ERR_NULL
