@@ -5,7 +5,10 @@ Default workload (the headline): decode-shaped W4A16 GEMM, N = K = 4096,
 group_size 128, M in {1, 4, 16}. One step = one qgemm_w4 call per M (three
 launches). Weights, scales, activations and outputs are rotated over enough
 device copies (>= 1 GiB) that every launch reads its operands from HBM, not
-from the 256 MB Infinity Cache or the L2s.
+from the 256 MB Infinity Cache or the L2s. The default line also carries the
+other half of the metric, the M = 2048, N = K = 4096 W4A16 GEMM, timed the same
+way over its own K steps (object `prefill_square`, TFLOP/s and its own
+roofline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--config decode|prefill|square|decode_bf16|prefill_bf16|grouped|grouped_kn|grouped_w4|kproj]
@@ -17,8 +20,11 @@ events on the launch stream; `cpu_baseline` times the CPU oracle on a bounded
 sample of the same workload. `roofline.attainable` is min(peak, arithmetic
 intensity x bandwidth) for the bound that applies. `context` (skip with
 --no-context) frames the result: the same launches on one cache-resident input
-set, a device copy moving the same byte count over rotated buffers (a
-practical HBM figure) and, for the MFMA-bound configs, torch.matmul on dense
+set; for the HBM-bound configs the library's read-only streaming kernels over
+rotated buffers of the same byte count (one contiguous chunk per workgroup: a
+practical HBM ceiling; for the decode also the column-strip pattern that any
+full-K kernel must use on a [K/8, N] weight), with the GEMM's launch time as a
+fraction of theirs; and, for the MFMA-bound configs, torch.matmul on dense
 operands of the same GEMM shape (a practical MFMA figure).
 """
 from __future__ import annotations
@@ -110,7 +116,9 @@ def parse():
                                                            "kproj_e4m3h",
                                                            "grouped", "grouped_kn", "grouped_w4", "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--no-context", action="store_true", help="skip the hot / copy / dense-GEMM context numbers")
+    p.add_argument("--no-context", action="store_true", help="skip the hot / read / dense-GEMM context numbers")
+    p.add_argument("--no-square", action="store_true",
+                   help="decode config: skip the M = 2048, N = K = 4096 half of the metric")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--source-hash", action="store_true", help="print the kernel source hash of --config and exit")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -207,6 +215,11 @@ class DecodeW4:
 
     def unit_flops(self):
         return self.flops_per_step / len(self.Ms)
+
+    @property
+    def read_strip_shape(self):
+        # packed B [K/8, N] words, one 16-column strip (64 bytes) per workgroup
+        return None if self.nk else (self.K // 8, self.N, 64)
 
     def cpu_sample(self):
         import oracle
@@ -607,25 +620,41 @@ def graph_time_ms(torch, launch_lists, reps=3):
     return best / len(fns)
 
 
-def context_numbers(torch, wl, steps):
+def context_numbers(torch, q, wl, steps, avg_launch_ms):
     """Numbers that frame the result (outside the timed region):
     * hot: the same launches on one input set, so the inputs stay in cache;
-    * copy: a device copy moving the workload's algorithmic byte count (half read,
-      half written), rotated over >= 1 GiB like the workload: a practical HBM figure;
+    * read_contiguous: the library's read-only streaming kernel over the workload's
+      algorithmic byte count per launch, one contiguous chunk per workgroup, rotated
+      over >= 1 GiB like the workload: a practical HBM ceiling for that many bytes;
+    * read_strips (decode): the same kernel reading the packed weight matrix one
+      16-column strip per workgroup, every packed row: the pattern of a kernel that
+      gives each workgroup a column strip and all of K;
     * torch_dense: torch.matmul (hipBLASLt) on dense operands of the same GEMM shape,
       timed eagerly: a practical MFMA figure for the MFMA-bound workloads."""
     out = {}
     n_launch = len(wl.launches(0))
     hot_ms = graph_time_ms(torch, [wl.launches(0) for _ in range(max(steps // 2, 10))])
     out["hot_avg_launch_us"] = round(hot_ms * 1e3, 3)
-    half = int(wl.unit_bytes()) // 2 // 16 * 4            # int32 elements, 16-byte multiple
-    R = max(2, math.ceil(ROTATE_BYTES / (8 * half)))
-    src = [torch.ones(half, dtype=torch.int32, device="cuda") for _ in range(R)]
-    dst = [torch.empty_like(x) for x in src]
-    cp_ms = graph_time_ms(torch, [[lambda a=a, b=b: b.copy_(a)] for a, b in zip(src, dst)] * 3)
-    out["copy_same_bytes_us"] = round(cp_ms * 1e3, 3)
-    out["copy_same_bytes_GBs"] = round(8 * half / (cp_ms * 1e-3) / 1e9, 1)
-    del src, dst
+    if wl.bound == "hbm":
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        nbytes = int(wl.unit_bytes()) // 16 * 16
+        R = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(R)]
+        rd_ms = graph_time_ms(torch, [[lambda b=b: q.read_contiguous(b, sink, 2 * 256)] for b in bufs] * 3)
+        out["read_contiguous_us"] = round(rd_ms * 1e3, 3)
+        out["read_contiguous_GBs"] = round(nbytes / (rd_ms * 1e-3) / 1e9, 1)
+        out["gemm_frac_of_read_contiguous"] = round(rd_ms / avg_launch_ms, 4)
+        del bufs
+        strip = getattr(wl, "read_strip_shape", None)
+        if strip is not None:
+            rows, cols, strip_bytes = strip
+            R = max(2, math.ceil(ROTATE_BYTES / (rows * cols * 4)))
+            bufs = [torch.ones(rows, cols, dtype=torch.int32, device="cuda") for _ in range(R)]
+            st_ms = graph_time_ms(torch, [[lambda b=b: q.read_strips(b, strip_bytes, sink)] for b in bufs] * 3)
+            out["read_strips_us"] = round(st_ms * 1e3, 3)
+            out["read_strips_shape"] = {"rows": rows, "row_bytes": cols * 4, "strip_bytes": strip_bytes}
+            out["gemm_frac_of_read_strips"] = round(st_ms / avg_launch_ms, 4)
+            del bufs
     dense = wl.dense_equivalent()
     if dense is not None:
         M, K, N, dt = dense
@@ -654,6 +683,78 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
 
 
+def time_workload(torch, wl, steps, warmup):
+    """Warm up, capture `steps` steps in one HIP graph and time one replay with events
+    on the stream it runs on (synchronised on both sides). Returns (ms, wall_s)."""
+    for i in range(warmup):
+        for f in wl.launches(i):
+            f()
+    torch.cuda.synchronize()
+    # The K steps are captured once into a HIP graph so the GPU runs the kernels
+    # back to back; from Python each launch costs more than the kernel itself.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            for f in wl.launches(i):
+                f()
+    torch.cuda.synchronize()
+    graph.replay()                      # warm replay
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = event_time_ms(torch, graph.replay, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    return ms, wall
+
+
+def roofline_of(wl, ms, steps, traffic):
+    """The value, its unit and the roofline object of the dominant kernel."""
+    ms_per_step = ms / steps
+    n_launch = len(wl.launches(0))
+    avg_launch_ms = ms / (steps * n_launch)
+    gbs = wl.bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    tflops = wl.flops_per_step / (ms_per_step * 1e-3) / 1e12
+    ai = wl.unit_flops() / wl.unit_bytes()        # FLOP per algorithmic byte
+    mfma_peak = getattr(wl, "mfma_peak", F16_MFMA_PEAK_TFLOPS)   # the contraction's own dtype
+    if wl.bound == "hbm":
+        value, unit = gbs, "GB/s"
+        achieved, peak, runit = wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        attainable = min(HBM_PEAK_GBS, mfma_peak * 1e3 / ai)
+    else:
+        value, unit = tflops, "TFLOP/s"
+        achieved, peak, runit = wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s"
+        attainable = min(mfma_peak, ai * HBM_PEAK_GBS / 1e3)
+    roof = {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": runit, "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": wl.kernel, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": wl.unit_bytes(),
+            "algorithmic_flops_per_launch": wl.unit_flops(),
+            "attainable": round(attainable, 1), "frac_attainable": round(achieved / attainable, 4),
+            "frac_hbm": round(wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac_mfma": round(wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12 / mfma_peak, 4)}
+    return value, unit, gbs, tflops, ms_per_step, avg_launch_ms, roof
+
+
+def cpu_baseline(wl, seconds, unit):
+    t0 = time.perf_counter()
+    n = 0
+    fl = by = 0
+    while True:
+        f, b, what = wl.cpu_sample()
+        fl += f
+        by += b
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cv = by / dt / 1e9 if wl.bound == "hbm" else fl / dt / 1e12
+    return {"value": round(cv, 6), "unit": unit, "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"{n} x ({what}) of the same workload, fp64 numpy oracle, {dt:.1f} s"}
+
+
 def main():
     args = parse()
     if args.source_hash:
@@ -680,45 +781,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        for f in wl.launches(i):
-            f()
-    torch.cuda.synchronize()
-
-    # The K steps are captured once into a HIP graph so the GPU runs the kernels
-    # back to back; from Python each launch costs more than the kernel itself.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(args.steps):
-            for f in wl.launches(i):
-                f()
-    torch.cuda.synchronize()
-    graph.replay()                      # warm replay
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps, events on the stream the graph runs on
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms = event_time_ms(torch, graph.replay, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ms / args.steps
-    n_launch = len(wl.launches(0))
-    avg_launch_ms = ms / (args.steps * n_launch)
-
-    gbs = wl.bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    tflops = wl.flops_per_step / (ms_per_step * 1e-3) / 1e12
-    ai = wl.unit_flops() / wl.unit_bytes()        # FLOP per algorithmic byte
-    mfma_peak = getattr(wl, "mfma_peak", F16_MFMA_PEAK_TFLOPS)   # the contraction's own dtype
-    if wl.bound == "hbm":
-        value, unit = gbs, "GB/s"
-        achieved, peak, runit = wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-        attainable = min(HBM_PEAK_GBS, mfma_peak * 1e3 / ai)
-    else:
-        value, unit = tflops, "TFLOP/s"
-        achieved, peak, runit = wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12, mfma_peak, "TFLOP/s"
-        attainable = min(mfma_peak, ai * HBM_PEAK_GBS / 1e3)
+    # timed region: exactly K steps
+    ms, wall = time_workload(torch, wl, args.steps, args.warmup)
+    value, unit, gbs, tflops, ms_per_step, avg_launch_ms, roof = roofline_of(wl, ms, args.steps,
+                                                                             measured_traffic(args.config))
     out = {
         "metric": "W4A16 GEMM TFLOP/s + HBM GB/s (% roofline) at M=1..16 and M=2048, N=K=4096",
         "value": round(value, 3), "unit": unit,
@@ -728,33 +794,26 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic",
         "config": wl.describe(),
-        "roofline": {"bound": wl.bound, "achieved": round(achieved, 3), "peak": peak,
-                     "unit": runit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config),
-                     "kernel": wl.kernel, "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                     "algorithmic_bytes_per_launch": wl.unit_bytes(),
-                     "algorithmic_flops_per_launch": wl.unit_flops(),
-                     "attainable": round(attainable, 1), "frac_attainable": round(achieved / attainable, 4),
-                     "frac_hbm": round(wl.unit_bytes() / (avg_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "frac_mfma": round(wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12 / mfma_peak, 4)},
+        "roofline": roof,
         "wall_s": round(wall, 3),
     }
     if not args.no_context:
-        out["context"] = context_numbers(torch, wl, args.steps)
+        out["context"] = context_numbers(torch, q, wl, args.steps, avg_launch_ms)
+    if args.config == "decode" and not args.no_square:
+        # the metric's other half: M = 2048, N = K = 4096, its own K timed steps
+        sq = PrefillW4(torch, q, synth, square=True)
+        sq_ms, sq_wall = time_workload(torch, sq, args.steps, args.warmup)
+        sv, su, _, _, sq_ms_step, sq_avg, sq_roof = roofline_of(sq, sq_ms, args.steps, measured_traffic("square"))
+        out["prefill_square"] = {"workload": sq.describe(), "value": round(sv, 3), "unit": su,
+                                 "ms_per_step": round(sq_ms_step, 6), "steps": args.steps, "wall_s": round(sq_wall, 3),
+                                 "roofline": sq_roof}
+        if not args.no_context:
+            out["prefill_square"]["context"] = context_numbers(torch, q, sq, args.steps, sq_avg)
+        if not args.no_cpu:
+            out["prefill_square"]["cpu_baseline"] = cpu_baseline(sq, args.cpu_seconds / 2, su)
+        del sq
     if not args.no_cpu:
-        t0 = time.perf_counter()
-        n = 0
-        fl = by = 0
-        while True:
-            f, b, what = wl.cpu_sample()
-            fl += f
-            by += b
-            n += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        dt = time.perf_counter() - t0
-        cv = by / dt / 1e9 if wl.bound == "hbm" else fl / dt / 1e12
-        out["cpu_baseline"] = {"value": round(cv, 6), "unit": unit, "cores": cpu_cores(), "kind": "oracle",
-                               "sample": f"{n} x ({what}) of the same workload, fp64 numpy oracle, {dt:.1f} s"}
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, unit)
     print(json.dumps(out), flush=True)
 
 

@@ -24,6 +24,7 @@ Entry points (same names as the C ABI):
                                 kv_scales=None, quantization_granularity=0)
     kv_matmul_ragged_paged_scale(... the same, weight = [W_k | W_v] ...)
 Each returns None on success and raises QgError carrying the status otherwise.
+Measurement yardsticks (include/qgemm_probe.h): read_contiguous, read_strips.
 """
 from __future__ import annotations
 
@@ -114,6 +115,13 @@ def load(path: str | None = None):
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
     lib.qg_version.restype = ctypes.c_int32
+    # read-only HBM yardsticks (include/qgemm_probe.h)
+    lib.qg_read_contiguous.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.qg_read_contiguous.restype = ctypes.c_int
+    lib.qg_read_strips.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.qg_read_strips.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -314,3 +322,25 @@ def kv_matmul_ragged_paged_scale(hidden, input_row_offsets, weight, input_scale,
     return _kv_call(load().kv_matmul_ragged_paged_scale, hidden, input_row_offsets, weight, input_scale,
                     weight_scale, kv_blocks, cache_lengths, page_table, layer_idx, scales_granularity_mnk,
                     kv_scales, quantization_granularity, stream, raise_on_error)
+
+
+def read_contiguous(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 512, stream=None,
+                    raise_on_error: bool = True) -> int:
+    """Stream the bytes of `src` once (a measurement yardstick; writes nothing)."""
+    st = load().qg_read_contiguous(src.data_ptr(), src.numel() * src.element_size(), int(workgroups),
+                                   sink.data_ptr(), _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def read_strips(src: torch.Tensor, strip_bytes: int, sink: torch.Tensor, stream=None,
+                raise_on_error: bool = True) -> int:
+    """Read a 2-D `src` one column strip of `strip_bytes` per workgroup, every row in
+    order (a measurement yardstick; writes nothing)."""
+    row_bytes = src.shape[1] * src.element_size()
+    st = load().qg_read_strips(src.data_ptr(), src.shape[0], row_bytes, int(strip_bytes), sink.data_ptr(),
+                               _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st

@@ -1,7 +1,8 @@
 """CPU checks of the C ABI boundary: the library loads, exports every function
-include/qgemm.h declares, and rejects bad arguments before touching the GPU.
+include/*.h declares, and rejects bad arguments before touching the GPU.
 No call here reaches a kernel launch."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -13,13 +14,14 @@ import grouped_gemm_qgemm_amd as q
 from grouped_gemm_qgemm_amd import QG, QgTensor, QgPagedKV
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "qgemm.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\*?([A-Za-z_]\w*)\s*\(", txt, flags=re.M)
+    names = []
+    for h in HEADERS:
+        txt = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\*?\s+\*?([A-Za-z_]\w*)\s*\(", txt, flags=re.M)
     return sorted(set(n for n in names if not n.startswith("QG")))
 
 
@@ -32,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"qgemm_w4", "qgemm_w4_nk", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "grouped_gemm_epilogue",
             "grouped_gemm_w4_epilogue", "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale",
-            "qg_status_string"} <= set(names)
+            "qg_status_string", "qg_read_contiguous", "qg_read_strips"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     for n in names:
@@ -353,3 +355,25 @@ def test_kproj_rejections(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         q.load(str(tmp_path / "missing.so"))
+
+
+def test_read_probe_rejections(lib):
+    lib.qg_read_contiguous.restype = ctypes.c_int
+    lib.qg_read_contiguous.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.qg_read_strips.restype = ctypes.c_int
+    lib.qg_read_strips.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    buf = np.zeros(4096 + 16, np.uint8)
+    base = (buf.ctypes.data + 15) & ~15
+    sink = np.zeros(4, np.uint32)
+    s = sink.ctypes.data
+    assert lib.qg_read_contiguous(base, 4096, 4, None, None) == QG.ERR_NULL
+    assert lib.qg_read_contiguous(base + 4, 4096, 4, s, None) == QG.ERR_ALIGN
+    assert lib.qg_read_contiguous(base, 4008, 4, s, None) == QG.ERR_ALIGN
+    assert lib.qg_read_contiguous(base, 4096, 0, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_read_contiguous(base, 0, 4, s, None) == QG.OK
+    assert lib.qg_read_strips(base, 8, 512, 48, s, None) == QG.ERR_SHAPE
+    assert lib.qg_read_strips(base, 8, 512, 40, s, None) == QG.ERR_ALIGN
+    assert lib.qg_read_strips(base, 8, 512, 0, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_read_strips(base, 0, 512, 64, s, None) == QG.OK
