@@ -8,26 +8,30 @@
 // with 128 x 128 weight-scale blocks and 1 x 128 input-scale blocks. Tokens of
 // all sequences are one flat row dimension (raggedness costs nothing in the
 // GEMM); the sequence only matters for where a finished row is stored.
-//   * Two designs for bf16 hidden rows: BM x 128 tiles with 4 * BM / 48 waves
-//     (the default, described above its kernel; at most 32 scale blocks of K)
-//     and 64 x 128 tiles for longer rows; a third for e4m3 hidden rows. Each
-//     128-deep K stage is exactly one scale block, so the stage's MFMA partial is scaled once, in fp32, by
+//   * Three tiled designs: the raw-weight design (bf16 hidden rows, BM x 128
+//     tiles with 4 * BM / 48 waves, at most 32 scale blocks of K; the
+//     default), the e4m3-hidden design (the same tiles with both MFMA
+//     operands e4m3), and a 64 x 128 long-row design for bf16 hidden rows of
+//     more than 32 scale blocks. Each 128-deep K stage is exactly one scale
+//     block, so the stage's MFMA partial is scaled once, in fp32, by
 //     is[t][kb] * ws[kb][nb] (ws is uniform over the tile) and added to the
 //     accumulator. Activations are never re-rounded.
 //   * The fp8 weight tile [128 k][128 n] is fetched with coalesced 16-byte row
-//     loads, converted to bf16 in registers (exact: every E4M3 value fits in
-//     bf16) and written transposed into LDS ([n][k], XOR-swizzled 16-byte
-//     chunks) so MFMA B fragments are plain 16-byte LDS reads.
+//     loads. The raw-weight and e4m3-hidden designs copy it into LDS as it is
+//     and read MFMA B fragments with 8-bit transpose reads; the long-row design
+//     converts it to bf16 in registers (exact: every E4M3 value fits in bf16)
+//     and writes it transposed into LDS.
 //   * Hidden rows are staged through LDS with an XOR swizzle; double-buffered
 //     stages, one barrier per stage.
 //   * 16x16x32 bf16 MFMA, fp32 accumulation. Column tile t of a wave holds
 //     columns 4j + t (j = lane % 16) in the long-row design, so each lane
-//     finishes four adjacent columns of a row (one 8-byte write); the default
-//     uses columns 2j + t and 4-byte writes.
+//     finishes four adjacent columns of a row (one 8-byte write); the other
+//     designs hold 16 consecutive columns per column tile.
 //   * Epilogue: token t -> sequence b (binary search of the row offsets) ->
 //     position cache_lengths[b] + (t - offs[b]) -> (page_table entry, slot);
-//     the bf16 row lands in plane 0 (keys) of layer layer_idx. Nothing else in
-//     the cache is written.
+//     the row lands in its plane (keys, or values for the second half of
+//     [W_k | W_v]) of layer layer_idx, as bf16 or as e4m3 codes with per-run
+//     scales. Nothing else in the cache is written.
 #include "device_common.h"
 #include "launch.h"
 
@@ -221,13 +225,9 @@ __global__ __launch_bounds__(KTHR) void kproj_fp8_paged_kernel(
   }
 }
 
-// transposed bf16 weight rows of the default design (one per column n): the
-// 16 rows {base + 2j + t} an MFMA fragment read touches get distinct chunks
-__device__ __forceinline__ int swz_bt(int n, int c) { return c ^ (((n >> 1) ^ (n >> 5)) & 15); }
-
-// Epilogue shared by the default and the e4m3-hidden designs: each token row of the tile
+// Epilogue shared by the tiled designs: each token row of the tile
 // goes to (layer, plane, page, slot) of the cache, as bf16 or as e4m3 codes with
-// per-run scales (see the default design). acc holds a wave's 48 x 32 tile: rows
+// per-run scales (described below). acc holds a wave's 48 x 32 tile: rows
 // wm * 48 + mt * 16 + 4q + i, columns wn * 32 + 2 r16 + j (BLK false: a lane owns
 // two adjacent columns) or wn * 32 + 16 j + r16 (BLK true). `scratch` is LDS of
 // at least 4 * BM floats that no wave reads any more.
@@ -339,176 +339,10 @@ __device__ __forceinline__ void kproj_store_tile(
   }
 }
 
-// Default design: BM = 48 * WM rows x 128 columns (one 128-deep stage per
-// scale block) with WM x 4 waves, each owning a 48 x 32
-// wave tile (three 16-row by two 16-column MFMA tiles). With WM = 3 (the
-// 144-row tiles that fill 256 CUs at 4312 tokens) a SIMD runs three waves, so
-// one wave's LDS and load waits are covered by the others' MFMAs; with one wave
-// per SIMD those waits were exposed on every stage. The first min(512, threads)
-// threads stage the weight tile (RPT K rows of 16 columns each).
-//
-// Cache planes and the fp8 cache: the N weight columns fill N / n_plane planes
-// from plane 0 (keys; with [W_k | W_v] the value columns land in plane 1). Each
-// 128-column tile lies in one plane. Q8: the cache holds e4m3 codes with one f32
-// scale per qgran head-dim elements of a row, s = amax / 448 and q = e4m3(x / s)
-// (nearest even); a run of 32 columns is one wave's columns of a row, spread over
-// the 16 lanes that share its rows, so amax is a 16-lane shuffle reduction, and
-// runs of 64 or 128 combine two or four waves through LDS.
-template <int WM, bool Q8>
-__global__ __launch_bounds__(WM * 256) void kproj_fp8_v3_kernel(
-    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
-    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
-    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
-    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
-    float* __restrict__ kv_scales, int qgran) {
-  constexpr int BM = 48 * WM;
-  constexpr int NTHR = WM * 256;
-  constexpr int MT = 3;                          // 16-row MFMA tiles per wave
-  constexpr int A_PER_T = BM * KCH / NTHR;       // 16-byte hidden chunks per thread per stage
-  static_assert(A_PER_T * NTHR == BM * KCH, "A staging");
-  constexpr int WT = NTHR < 512 ? NTHR : 512;    // threads that stage the weight tile
-  constexpr int RPT = 1024 / WT;                 // K rows per staging thread (128 rows x 8 column groups)
-  static_assert(RPT == 2 || RPT == 4, "weight staging");
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][BM * KCH];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][KBN * KCH];
-  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
-  __shared__ long long row_dst[BM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int q = lane >> 4, r16 = lane & 15;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
-  const int nb = lin % tiles_n;
-  const int n0 = nb * KBN;
-  const int KB = Kh / KBK;
-
-  uint32_t a_off[A_PER_T];
-  int a_lds[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int id = tid + i * NTHR;
-    const int row = id / KCH, ch = id % KCH;
-    a_off[i] = (uint32_t)(min(m0 + row, T - 1) * Kh + ch * 8);
-    a_lds[i] = row * KCH + swz_a(row, ch);
-  }
-  const bool wstage = tid < WT;                          // wave-uniform
-  const int ng = tid & 7, kq = (tid >> 3) & (WT / 8 - 1);  // 16-column group, K-row group
-  const uint32_t w_off = (uint32_t)(RPT * kq * N + n0 + 16 * ng);
-
-  // staging registers: the next stage's loads are in flight while a stage is multiplied
-  u32x4_t ra[1][A_PER_T];
-  u32x4_t rw[1][RPT];
-  auto load_stage = [&](int kb, u32x4_t (&ra)[A_PER_T], u32x4_t (&rw)[RPT]) {
-    const int k0 = kb * KBK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(H + k0 + a_off[i]);
-    if (wstage) {
-      const uint8_t* wb = W + (size_t)k0 * N;
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) rw[r] = *reinterpret_cast<const u32x4_t*>(wb + w_off + r * N);
-    }
-  };
-  auto store_stage = [&](int buf, const u32x4_t (&ra)[A_PER_T], const u32x4_t (&rw)[RPT]) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = ra[i];
-    if (wstage) {
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        float2_t f[RPT][2];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-          const uint32_t word = rw[r][c4];
-          f[r][0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-          f[r][1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int n = 16 * ng + 4 * c4 + b;
-          if constexpr (RPT == 4) {
-            // K rows 4kq .. 4kq+3: half of a 16-byte chunk
-            uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 1)]) + (kq & 1) * 2;
-            *reinterpret_cast<u32x2_t*>(dst) =
-                u32x2_t{bf16pair_hi(f[0][b >> 1][b & 1], f[1][b >> 1][b & 1]),
-                        bf16pair_hi(f[2][b >> 1][b & 1], f[3][b >> 1][b & 1])};
-          } else {
-            // K rows 2kq, 2kq+1: one word of a 16-byte chunk
-            uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_bt(n, kq >> 2)]) + (kq & 3);
-            *dst = bf16pair_hi(f[0][b >> 1][b & 1], f[1][b >> 1][b & 1]);
-          }
-        }
-      }
-    }
-  };
-
-  for (int e = tid; e < KB * BM; e += NTHR) {
-    const int row = e % BM, kb = e / BM;
-    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
-  }
-
-  float4_t acc[MT][2];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int kb, int buf) {
-    float4_t part[MT][2];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t bf[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int n = wn * 32 + 2 * r16 + t;   // column tile t of the wave: lane j holds column 2j + t
-        bf[t] = lds_b[buf][n * KCH + swz_bt(n, s * 4 + q)];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * 48 + mt * 16 + r16;
-        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
-        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
-        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
-      }
-    }
-    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float f = is4[i] * wsv;
-        acc[mt][0][i] += f * part[mt][0][i];
-        acc[mt][1][i] += f * part[mt][1][i];
-      }
-    }
-  };
-
-  load_stage(0, ra[0], rw[0]);
-  store_stage(0, ra[0], rw[0]);
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const bool more = kb + 1 < KB;
-    if (more) load_stage(kb + 1, ra[0], rw[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(kb, kb & 1);
-    if (more) store_stage((kb + 1) & 1, ra[0], rw[0]);
-    __syncthreads();
-  }
-
-  kproj_store_tile<WM * 48, Q8>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch, max_pages,
-                                 num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
-}
-
 // e4m3-hidden design: fp8 (e4m3) hidden rows, so both operands are fp8 and one
 // v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) covers a 16 x 16 output
 // tile over a whole 128-deep scale block; its fp32 result is scaled by
-// is[t][kb] * ws[kb][nb] and added to the accumulator, as in the default design,
+// is[t][kb] * ws[kb][nb] and added to the accumulator, as in the raw-weight design below,
 // whose tiles, waves and epilogue it shares (BM = 48 * WM rows x 128 columns,
 // 48 x 32 wave tiles).
 //   * Both tiles stay fp8 in LDS, copied as they are: hidden rows [BM][128 B]
@@ -664,6 +498,185 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
                                  max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
+// Raw-weight design for bf16 hidden rows: the e4m3-hidden design's staging
+// (both tiles copied into LDS as they are, one round-robin list of 16-byte
+// chunks, PD stages of loads in flight) with bf16 MFMAs.
+//   * Hidden rows: [BM][256 B] per 128-deep stage, 16-byte chunks XOR-swizzled
+//     by the low four row bits. A fragment (row r16, K 32s + 8q .. + 7): one
+//     16-byte read.
+//   * Weight tile: [128 k][128 n] e4m3, chunks swizzled by the low three row
+//     bits. B fragment (column 16c + r16 of chunk c, the same K): one 8-bit
+//     transpose read (lane m names K row 32s + 8q + m / 2 and byte 8 (m % 2) of
+//     the chunk; lane i receives the eight K values of column i), then four
+//     v_cvt_scalef32_pk_bf16_fp8 at scale 1 (exact: every e4m3 value is a bf16
+//     value). Each wave converts its own fragments; nothing is transposed or
+//     converted on the way into LDS.
+//   * 16x16x32 bf16 MFMAs on 48 x 32 wave tiles (column tile t of a wave holds
+//     16 consecutive columns), the stage's partials scaled once by
+//     is[t][kb] * ws[kb][nb], and the shared epilogue.
+template <int WM, bool Q8, int PD>
+__global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
+    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
+    float* __restrict__ kv_scales, int qgran) {
+  constexpr int BM = 48 * WM;
+  constexpr int NTHR = WM * 256;
+  constexpr int MT = 3;
+  constexpr int ACH = BM * KCH;                        // 16-byte hidden chunks per stage (16 per row)
+  constexpr int BCH = 128 * 8;                         // 16-byte weight chunks per stage (8 per K row)
+  constexpr int LOADS = (ACH + BCH + NTHR - 1) / NTHR;  // loads per thread per stage
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][ACH];
+  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
+  __shared__ long long row_dst[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  // this thread's chunks: source at stage 0, bytes per stage, LDS slot
+  const uint8_t* src[LOADS];
+  uint32_t sstep[LOADS];
+  int slot[LOADS];   // index into lds_a (< ACH) or ACH + index into lds_b; -1: not stored
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int id0 = tid + i * NTHR;
+    const bool in_list = id0 < ACH + BCH;
+    const int id = in_list ? id0 : id0 - NTHR;   // re-read this thread's previous chunk
+    if (id < ACH) {
+      const int row = id / KCH, ch = id % KCH;
+      src[i] = reinterpret_cast<const uint8_t*>(H + (size_t)min(m0 + row, T - 1) * Kh) + ch * 16;
+      sstep[i] = KBK * 2;
+      slot[i] = row * KCH + swz_a(row, ch);
+    } else {
+      const int j = id - ACH, kr = j >> 3, ch = j & 7;
+      src[i] = W + (size_t)kr * N + n0 + ch * 16;
+      sstep[i] = (uint32_t)KBK * (uint32_t)N;
+      slot[i] = ACH + kr * 8 + (ch ^ (kr & 7));
+    }
+    if (!in_list) slot[i] = -1;
+  }
+  auto load_stage = [&](int kb, u32x4_t (&r)[LOADS]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      r[i] = *reinterpret_cast<const u32x4_t*>(src[i] + (size_t)kb * sstep[i]);
+  };
+  auto store_stage = [&](int buf, const u32x4_t (&r)[LOADS]) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      if (slot[i] < 0) continue;
+      if (slot[i] < ACH) lds_a[buf][slot[i]] = r[i];
+      else lds_b[buf][slot[i] - ACH] = r[i];
+    }
+  };
+
+  for (int e = tid; e < KB * BM; e += NTHR) {
+    const int row = e % BM, kb = e / BM;
+    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
+  }
+
+  float4_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  auto compute = [&](int kb, int buf) {
+    float4_t part[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = wn * 2 + t;   // the column chunk of column tile t
+        const int kr = 32 * s + 8 * q + (r16 >> 1);
+        const unsigned char* base =
+            reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + (c ^ (kr & 7))]) + 8 * (r16 & 1);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(__attribute__((address_space(3))) const unsigned char*)base);
+        bf[t] = u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true))};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 48 + mt * 16 + r16;
+        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
+        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
+        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
+      }
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float f = is4[i] * wsv;
+        acc[mt][0][i] += f * part[mt][0][i];
+        acc[mt][1][i] += f * part[mt][1][i];
+      }
+    }
+  };
+
+  u32x4_t rg[PD][LOADS];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_stage(min(p, KB - 1), rg[p]);
+  store_stage(0, rg[0]);
+  __syncthreads();
+  for (int kb = 0; kb < KB; kb += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int i = kb + p;   // stage multiplied now; rg[p] (stage i, stored) takes stage i + PD
+      if constexpr (PD > 1) load_stage(min(i + PD, KB - 1), rg[p]);   // past the end: re-reads, unstored
+      else load_stage(min(i + 1, KB - 1), rg[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < KB) compute(i, i & 1);
+      if (i + 1 < KB) store_stage((i + 1) & 1, rg[(p + 1) % PD]);
+      __syncthreads();
+    }
+  }
+
+  kproj_store_tile<BM, Q8, true>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
+                                 max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
+}
+
+template <int WM, int PD>
+static hipError_t launch_kproj_bf16(const KProjArgs& p, hipStream_t stream) {
+  constexpr int BM = 48 * WM;
+  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
+  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
+  if (p.fp8)
+    hipLaunchKernelGGL((kproj_bf16_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                       p.kv_scales, p.qgran);
+  else
+    hipLaunchKernelGGL((kproj_bf16_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                       nullptr, 0);
+  return hipGetLastError();
+}
+
 template <int WM, int PD>
 static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
@@ -680,26 +693,6 @@ static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
                        p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
                        (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
                        (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
-  return hipGetLastError();
-}
-
-template <int WM>
-static hipError_t launch_kproj_v3(const KProjArgs& p, hipStream_t stream) {
-  constexpr int BM = 48 * WM;
-  const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
-  const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
-  if (p.fp8)
-    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, true>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
-                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
-                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
-                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
-                       p.kv_scales, p.qgran);
-  else
-    hipLaunchKernelGGL((kproj_fp8_v3_kernel<WM, false>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
-                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
-                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
-                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
-                       nullptr, 0);
   return hipGetLastError();
 }
 
@@ -733,11 +726,11 @@ hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream) {
       default: return launch_kproj_f8f8<3, 2>(p, stream);
     }
   }
-  if (p.Kh / KBK <= 32) {   // default design: at most 32 input-scale blocks in LDS
+  if (p.Kh / KBK <= 32) {   // raw-weight design: at most 32 input-scale blocks in LDS
     switch (pick_kproj_rows(p, cand, 3) / 48) {
-      case 1: return launch_kproj_v3<1>(p, stream);
-      case 2: return launch_kproj_v3<2>(p, stream);
-      default: return launch_kproj_v3<3>(p, stream);
+      case 1: return launch_kproj_bf16<1, 2>(p, stream);
+      case 2: return launch_kproj_bf16<2, 2>(p, stream);
+      default: return launch_kproj_bf16<3, 2>(p, stream);
     }
   }
   // longer hidden rows: the long-row design (bf16 cache, keys only)

@@ -20,7 +20,7 @@ namespace {
 constexpr int BK = 64;            // K per LDS stage (two 32-deep MFMA steps)
 constexpr int CHUNKS = BK / 8;    // 16-byte chunks per A row in LDS
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 }  // namespace
 
