@@ -70,22 +70,22 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9011436, "e278b08f0b34864e"),
-    "prefill": (270609845, "af6802a75e8ff835"),
-    "square": (101399295, "af6802a75e8ff835"),
-    "grouped": (368071126, "f833eb3207a13024"),
-    "grouped_kn": (365856348, "f833eb3207a13024"),
-    "grouped_w4": (115068766, "af6802a75e8ff835"),
-    "kproj": (85586482, "ef6983f121e9e52b"),
-    "decode_gate": (9036009, "e278b08f0b34864e"),
-    "prefill_gate": (270840999, "af6802a75e8ff835"),
-    "decode_bf16": (8999149, "e278b08f0b34864e"),
-    "prefill_bf16": (271275515, "af6802a75e8ff835"),
-    "decode_nk": (9012460, "e278b08f0b34864e"),
-    "prefill_nk": (232414284, "af6802a75e8ff835"),
-    "kvproj": (202279226, "ef6983f121e9e52b"),
-    "kvproj_e4m3": (193902382, "ef6983f121e9e52b"),
-    "kproj_e4m3h": (64355704, "ef6983f121e9e52b"),
+    "decode": (9239429, "65549ccb19902118"),
+    "prefill": (272885614, "b9ce07adc0ce9e99"),
+    "square": (101390016, "b9ce07adc0ce9e99"),
+    "grouped": (368005065, "62666b1085d60043"),
+    "grouped_kn": (365904491, "62666b1085d60043"),
+    "grouped_w4": (115101915, "b9ce07adc0ce9e99"),
+    "kproj": (85578482, "da405049647d86e7"),
+    "decode_gate": (9258198, "65549ccb19902118"),
+    "prefill_gate": (272898482, "b9ce07adc0ce9e99"),
+    "decode_bf16": (9238405, "65549ccb19902118"),
+    "prefill_bf16": (302812268, "b9ce07adc0ce9e99"),
+    "decode_nk": (9233840, "65549ccb19902118"),
+    "prefill_nk": (232416972, "b9ce07adc0ce9e99"),
+    "kvproj": (202271867, "da405049647d86e7"),
+    "kvproj_e4m3": (193909613, "da405049647d86e7"),
+    "kproj_e4m3h": (64369079, "da405049647d86e7"),
 }
 
 
