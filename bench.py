@@ -11,7 +11,9 @@ way over its own K steps (object `prefill_square`, TFLOP/s and its own
 roofline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config decode|prefill|square|decode_bf16|prefill_bf16|grouped|grouped_kn|grouped_w4|kproj]
+                    [--config decode|prefill|square|decode_bf16|prefill_bf16|decode_gate|prefill_gate|
+                              decode_nk|prefill_nk|grouped|grouped_kn|grouped_w4|kproj|kvproj|
+                              kvproj_e4m3|kproj_e4m3h]
 
 Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
 steps (the decode shapes are bound by HBM); TFLOP/s is reported beside it. The

@@ -487,7 +487,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   }
 }
 
-// Dense fourth-design kernel: one tile per workgroup, tile order within each
+// Dense kernel: one tile per workgroup, tile order within each
 // XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
 // swept across N.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF, bool NK = false>

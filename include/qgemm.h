@@ -87,17 +87,20 @@ typedef struct {
  *   a        f16 or bf16 [M, K]              activations
  *   b_packed u32 [K / pack_factor, N]        packed 4-bit weight codes
  *   scales   f16 or bf16 [K / group_size, N] one scale per group per column
- *   group_size   multiple of 32, divides K   (QG_ERR_SHAPE / QG_ERR_UNSUPPORTED)
+ *   group_size   a power of two in 32 .. 256 that divides K
+ *                (QG_ERR_SHAPE when it does not divide K, QG_ERR_UNSUPPORTED
+ *                for other values)
  *   pack_factor  must be 8                   (QG_ERR_UNSUPPORTED otherwise)
  *
  * a, scales and c share one type, fp16 or bf16 (the page's a_type and c_type
  * parameters; QG_ERR_DTYPE when they differ). Accumulation is fp32; the result
  * is rounded to the output type (nearest-even). N must be a multiple of 8 and K a
  * multiple of group_size (QG_ERR_ALIGN / QG_ERR_SHAPE). M <= 16 runs the
- * skinny-M (decode) kernel, which keeps (q - 8) exact and scales each group's
- * fp32 partial; larger M the MFMA-tiled (prefill) kernel, which rounds each
- * weight (q - 8) * scale to the activation type before its MFMAs. bf16 with a
- * packed matrix beyond 2^32 - 1 bytes returns QG_ERR_UNSUPPORTED.
+ * skinny-M (decode) kernel, larger M the MFMA-tiled (prefill) kernel. With bf16
+ * both keep (q - 8) exact and scale each group's fp32 partial once; with fp16
+ * the decode kernel does the same and the prefill kernel rounds each weight
+ * (q - 8) * scale to fp16 before its MFMAs. For M > 16, K >= 2^24 or N >= 2^27
+ * returns QG_ERR_UNSUPPORTED (32-bit offsets within a tile's rows).
  */
 qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
                    const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
@@ -115,9 +118,8 @@ qg_status qgemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_pa
  *   scales    f16 or bf16 [N, K / group_size]
  *
  * Every other argument, type, check and result as qgemm_w4 (the same values:
- * b_packed and scales are the transposes of qgemm_w4's). M > 16 runs the
- * fourth prefill design with one stage in flight (QG_ERR_UNSUPPORTED for the
- * others); B beyond 2^32 - 1 bytes is QG_ERR_UNSUPPORTED.
+ * b_packed and scales are the transposes of qgemm_w4's). M > 16 returns
+ * results bit-identical to qgemm_w4 on the transposed operands.
  */
 qg_status qgemm_w4_nk(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b_packed,
                       const qg_tensor* scales, int32_t group_size, int32_t pack_factor,
