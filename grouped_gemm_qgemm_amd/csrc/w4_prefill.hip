@@ -247,10 +247,25 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   // (and direct B words)
   auto compute = [&](int buf, const Cur& cur, int k0) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds_b[buf]);
+    // The stage's A fragments and packed B words are read out of LDS first, so
+    // the MFMAs do not each wait for a read issued just before them; on the bf16
+    // path (two row tiles per wave) the reads are pinned ahead of the math.
+    u32x4_t afr[BK / 16][MT];
+    uint64_t bwr[BK / 16];
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       // packed row 2j + h of the stage, columns 2*c32 and 2*c32 + 1 of the wave's 64
-      const uint64_t w2 = BD ? cur.bd[BD ? j : 0] : bw[(2 * j + h) * (BN / 2) + wn * (TN / 2) + c32];
+      bwr[j] = BD ? cur.bd[BD ? j : 0] : bw[(2 * j + h) * (BN / 2) + wn * (TN / 2) + c32];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * TM + mt * 32 + c32;
+        afr[j][mt] = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
+      }
+    }
+    if constexpr (BF && MT <= 2) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < BK / 16; ++j) {
+      const uint64_t w2 = bwr[j];
       const uint32_t sp = cur.sc[j >> 1];
       u32x4_t bq[2];
 #pragma unroll
@@ -270,8 +285,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row = wm * TM + mt * 32 + c32;
-        const u32x4_t av = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
+        const u32x4_t av = afr[j][mt];
         if constexpr (BF) {
           part[mt][0] = mfma32x32x16_bf16(av, bq[0], part[mt][0]);
           part[mt][1] = mfma32x32x16_bf16(av, bq[1], part[mt][1]);
@@ -326,7 +340,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     // buffers, two row tiles at a time; lane-major so the accesses are
     // conflict-free
     float* red = reinterpret_cast<float*>(&lds);
-    static_assert(sizeof(W4TileLds<BM, BN, KG>) >= 64 * NTHR * sizeof(float), "reduction space");
+    static_assert(sizeof(W4TileLds<BM, BN, KG, BD>) >= 64 * NTHR * sizeof(float), "reduction space");
 #pragma unroll
     for (int p = 0; p < MT / 2; ++p) {
       if (kg == 1) {
@@ -490,12 +504,13 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 // Dense kernel: one tile per workgroup, tile order within each
 // XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
 // swept across N.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF, bool NK = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF, bool NK = false,
+          bool BD = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
     Epilogue ep) {
-  __shared__ W4TileLds<BM, BN, KG> lds;
+  __shared__ W4TileLds<BM, BN, KG, BD> lds;
   const int tiles = tiles_m * tiles_n;
   const int per = (tiles + 7) >> 3;
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -515,8 +530,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
     tm = first + r % gm;
     tn = r / gm;
   }
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN, lds,
-                                                         ep);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK, BD>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN,
+                                                             lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -587,9 +602,12 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
 // each accumulator, which leaves no registers for a second workgroup.
 template <int WM, int MINB, int KG, bool BF, bool NK>
 static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
-  constexpr int BM = 128, BN = 256, WN = 4, PD = 1;
+  // one K group of waves with a column strip each (fp16, [K/8, N]): B words go
+  // straight into the lanes' registers, two stages ahead
+  constexpr bool BD = (KG == 1 && !NK && !BF && WM == 1);
+  constexpr int BM = 128, BN = 256, WN = 4, PD = BD ? 2 : 1;
   const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK>), dim3(grid),
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK, BD>), dim3(grid),
                      dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,
                      p.group_size, tm, tn, 8, p.epi);
 }
