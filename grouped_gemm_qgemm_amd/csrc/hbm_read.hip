@@ -7,7 +7,10 @@
 //   * strips: the buffer is `rows` rows of `row_bytes`, and each workgroup
 //     reads one `strip_bytes`-wide column strip of every row, which is how a
 //     kernel that gives each workgroup a column strip and all of K must read a
-//     [K/8, N] packed weight matrix.
+//     [K/8, N] packed weight matrix. When the strip count is a multiple of
+//     eight, each XCD takes a contiguous run of strips (workgroup b reads strip
+//     (b % 8) * strips / 8 + b / 8), as the decode GEMM does, so neighbouring
+//     strips that share a cache line are read through the same L2.
 #include "qgemm_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -39,11 +42,13 @@ __global__ __launch_bounds__(kThreads) void read_contiguous_kernel(const u32x4_t
   if (acc == kNever) sink[0] = acc;
 }
 
-// one workgroup per strip; threads take (row, 16-byte chunk) pairs in row order
+// one workgroup per strip; threads take (row, 16-byte chunk) pairs in row order;
+// xcd_run > 0: strips per XCD (workgroup b takes strip (b % 8) * xcd_run + b / 8)
 __global__ __launch_bounds__(kThreads) void read_strips_kernel(const unsigned char* __restrict__ src, int64_t rows,
-                                                              int64_t row_bytes, int32_t strip_chunks,
+                                                              int64_t row_bytes, int32_t strip_chunks, int32_t xcd_run,
                                                               uint32_t* __restrict__ sink) {
-  const int64_t col0 = (int64_t)blockIdx.x * strip_chunks * 16;
+  const int64_t strip = xcd_run > 0 ? (int64_t)(blockIdx.x & 7) * xcd_run + (blockIdx.x >> 3) : (int64_t)blockIdx.x;
+  const int64_t col0 = strip * strip_chunks * 16;
   const int64_t total = rows * strip_chunks;
   uint32_t acc = 0;
   for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)kThreads * kUnroll) {
@@ -89,8 +94,9 @@ qg_status qg_read_strips(const void* src, int64_t rows, int64_t row_bytes, int32
   if (rows == 0 || row_bytes == 0) return QG_OK;
   const int64_t strips = row_bytes / strip_bytes;
   if (strips > INT32_MAX) return QG_ERR_UNSUPPORTED;
+  const int32_t xcd_run = strips % 8 == 0 ? (int32_t)(strips / 8) : 0;
   hipLaunchKernelGGL(read_strips_kernel, dim3((unsigned)strips), dim3(kThreads), 0, stream,
-                     static_cast<const unsigned char*>(src), rows, row_bytes, strip_bytes / 16, sink);
+                     static_cast<const unsigned char*>(src), rows, row_bytes, strip_bytes / 16, xcd_run, sink);
   return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 

@@ -33,7 +33,9 @@ qg_status qg_read_contiguous(const void* src, uint64_t bytes, int32_t workgroups
  * reads bytes [s * strip_bytes, (s + 1) * strip_bytes) of every row, rows in
  * order (row_bytes / strip_bytes workgroups). This is the access pattern of a
  * kernel that gives each workgroup a column strip of a [K/8, N] packed weight
- * matrix and all of K.
+ * matrix and all of K. With a strip count that is a multiple of eight, each
+ * of the eight XCDs reads a contiguous run of strips (as qgemm_w4's decode
+ * kernel does).
  *   src 16-byte aligned, row_bytes and strip_bytes multiples of 16
  *   (QG_ERR_ALIGN); strip_bytes divides row_bytes (QG_ERR_SHAPE).
  */
