@@ -73,18 +73,18 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
     "decode": (9239429, "ec78a7e77d980bda"),
-    "prefill": (272885614, "a15a6232abda3785"),
-    "square": (101390016, "a15a6232abda3785"),
+    "prefill": (276791696, "4f7241325a7d6b62"),
+    "square": (101391104, "4f7241325a7d6b62"),
     "grouped": (368005065, "9807d009efbaa9a2"),
     "grouped_kn": (365904491, "9807d009efbaa9a2"),
-    "grouped_w4": (115101915, "a15a6232abda3785"),
+    "grouped_w4": (114656386, "4f7241325a7d6b62"),
     "kproj": (85578482, "6f07c4251351596e"),
     "decode_gate": (9258198, "ec78a7e77d980bda"),
-    "prefill_gate": (272898482, "a15a6232abda3785"),
+    "prefill_gate": (276948233, "4f7241325a7d6b62"),
     "decode_bf16": (9238405, "ec78a7e77d980bda"),
-    "prefill_bf16": (302812268, "a15a6232abda3785"),
+    "prefill_bf16": (302809964, "4f7241325a7d6b62"),
     "decode_nk": (9233840, "ec78a7e77d980bda"),
-    "prefill_nk": (232416972, "a15a6232abda3785"),
+    "prefill_nk": (232418124, "4f7241325a7d6b62"),
     "kvproj": (202271867, "6f07c4251351596e"),
     "kvproj_e4m3": (193909613, "6f07c4251351596e"),
     "kproj_e4m3h": (64369079, "6f07c4251351596e"),
