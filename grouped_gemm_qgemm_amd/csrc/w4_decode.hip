@@ -49,6 +49,7 @@ __device__ __forceinline__ void w4_decode_lds_body(
   constexpr int SN = 16 * CPL;
   constexpr int STEPS = SPG > BSTEPS ? SPG : BSTEPS;   // K steps per batch
   constexpr int GB = STEPS / SPG;              // groups per batch
+  static_assert(!NK || (GB >= 2 && GB % 2 == 0 && GB <= 16), "scale runs");
   constexpr int CH = STEPS * 4;                // 16-byte A chunks per row per batch
   constexpr int AIT = (MROWS * CH + kWave - 1) / kWave;   // A chunk loads per lane
   __shared__ u32x4_t a_lds[NW][MROWS * CH];
@@ -117,14 +118,43 @@ __device__ __forceinline__ void w4_decode_lds_body(
     // 2. scales and packed weights of the batch
     uint32_t w[GB][SPG][CPL];
     uint16_t sc[GB][CPL];
+    if constexpr (NK) {
+      // [N, K/group_size] scales: the batch's GB scales of a column are
+      // contiguous, so when the run is aligned and whole (a wave-uniform test)
+      // it is one 4 to 32-byte load instead of GB scattered 2-byte loads
+      const int groups_per_col = K / (SPG * 32);
+      const bool run = groups_per_col % GB == 0 && g0 % GB == 0 && g0 + GB <= g_end;
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) {
+        const uint16_t* sp = S + (size_t)(ncol + t) * groups_per_col;
+        if (run) {
+          uint32_t words[GB / 2];
+          if constexpr (GB == 2) {
+            words[0] = *reinterpret_cast<const uint32_t*>(sp + g0);
+          } else if constexpr (GB == 4) {
+            const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sp + g0);
+            words[0] = v.x; words[1] = v.y;
+          } else {
+#pragma unroll
+            for (int i = 0; i < GB / 8; ++i) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sp + g0 + 8 * i);
+              words[4 * i] = v.x; words[4 * i + 1] = v.y; words[4 * i + 2] = v.z; words[4 * i + 3] = v.w;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < GB; ++j) sc[j][t] = (uint16_t)(words[j / 2] >> (16 * (j % 2)));
+        } else {
+#pragma unroll
+          for (int j = 0; j < GB; ++j) sc[j][t] = sp[g0 + j < g_end ? g0 + j : g_end - 1];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < GB; ++j) {
       const int g = g0 + j < g_end ? g0 + j : g_end - 1;
       if constexpr (NK) {
-        const int groups_per_col = K / (SPG * 32);
 #pragma unroll
         for (int t = 0; t < CPL; ++t) {
-          sc[j][t] = S[(size_t)(ncol + t) * groups_per_col + g];
           const uint32_t* bp = B + (size_t)(ncol + t) * (K / 8) + (g * SPG * 4 + quarter * SPG);
 #pragma unroll
           for (int s4 = 0; s4 < SPG; s4 += 4) {
