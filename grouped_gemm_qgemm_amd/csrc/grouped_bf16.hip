@@ -448,7 +448,7 @@ __global__ __launch_bounds__(W * kWave, OCC) void grouped_bf16_kernel(
 }
 
 // Launch: persistent workgroups, a whole number per XCD. Weights [E, N, K]:
-// eight waves (128 columns), four 64-deep steps in flight, two workgroups per
+// eight waves (128 columns), three 64-deep steps in flight, two workgroups per
 // CU. Weights [E, K, N]: eight waves, eight 32-deep steps in flight issued in
 // pairs, one workgroup per CU.
 hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream) {
@@ -457,7 +457,7 @@ hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream) {
   const int tiles_n = (int)((p.planes.pb1 + GBN - 1) / GBN + (p.planes.pb2 - p.planes.pb1 + GBN - 1) / GBN +
                             (p.N - p.planes.pb2 + GBN - 1) / GBN);
   if (p.transpose_b) {
-    constexpr int D = 4, OCC = 2;
+    constexpr int D = 3, OCC = 2;
     const int grid = 8 * ((OCC * p.num_cus + 7) / 8);
     if (p.epi.flags)
       hipLaunchKernelGGL((grouped_bf16_wl_kernel<W, D, OCC, true>), dim3(grid), dim3(W * kWave), 0, stream, p.C,
