@@ -359,9 +359,6 @@ static qg_status kv_proj_impl(const qg_tensor* hidden, const qg_tensor* input_ro
   p.kv_scales = fp8 ? static_cast<float*>(kv->scales.data) : nullptr;
   p.qgran = (int)G;
   p.hidden_fp8 = hidden_fp8 ? 1 : 0;
-  // e4m3 hidden rows, an e4m3 cache and the value plane need at most 32 scale
-  // blocks of K (the designs that keep the tile's input scales in LDS)
-  if ((hidden_fp8 || fp8 || planes > 1) && Kh / 128 > 32) return QG_ERR_UNSUPPORTED;
   return launch_status(qg::launch_kproj_fp8(p, stream));
 }
 

@@ -8,25 +8,20 @@
 // with 128 x 128 weight-scale blocks and 1 x 128 input-scale blocks. Tokens of
 // all sequences are one flat row dimension (raggedness costs nothing in the
 // GEMM); the sequence only matters for where a finished row is stored.
-//   * Three tiled designs: the raw-weight design (bf16 hidden rows, BM x 128
-//     tiles with 4 * BM / 48 waves, at most 32 scale blocks of K; the
-//     default), the e4m3-hidden design (the same tiles with both MFMA
-//     operands e4m3), and a 64 x 128 long-row design for bf16 hidden rows of
-//     more than 32 scale blocks. Each 128-deep K stage is exactly one scale
-//     block, so the stage's MFMA partial is scaled once, in fp32, by
+//   * Two tiled designs on BM x 128 tiles with 4 * BM / 48 waves: the
+//     raw-weight design (bf16 hidden rows) and the e4m3-hidden design (both
+//     MFMA operands e4m3). Each 128-deep K stage is exactly one scale block,
+//     so the stage's MFMA partial is scaled once, in fp32, by
 //     is[t][kb] * ws[kb][nb] (ws is uniform over the tile) and added to the
-//     accumulator. Activations are never re-rounded.
+//     accumulator. Activations are never re-rounded. The tile rows' input
+//     scales sit in LDS, 32 blocks at a time (refilled every 32 stages).
 //   * The fp8 weight tile [128 k][128 n] is fetched with coalesced 16-byte row
-//     loads. The raw-weight and e4m3-hidden designs copy it into LDS as it is
-//     and read MFMA B fragments with 8-bit transpose reads; the long-row design
-//     converts it to bf16 in registers (exact: every E4M3 value fits in bf16)
-//     and writes it transposed into LDS.
+//     loads, copied into LDS as it is, and MFMA B fragments are read with
+//     8-bit transpose reads.
 //   * Hidden rows are staged through LDS with an XOR swizzle; double-buffered
 //     stages, one barrier per stage.
-//   * 16x16x32 bf16 MFMA, fp32 accumulation. Column tile t of a wave holds
-//     columns 4j + t (j = lane % 16) in the long-row design, so each lane
-//     finishes four adjacent columns of a row (one 8-byte write); the other
-//     designs hold 16 consecutive columns per column tile.
+//   * Column tile t of a wave holds 16 consecutive columns (the transpose
+//     read's order); fp32 accumulation.
 //   * Epilogue: token t -> sequence b (binary search of the row offsets) ->
 //     position cache_lengths[b] + (t - offs[b]) -> (page_table entry, slot);
 //     the row lands in its plane (keys, or values for the second half of
@@ -39,199 +34,23 @@ namespace qg {
 
 namespace {
 
-constexpr int KBM = 64;       // tokens per tile
 constexpr int KBN = 128;      // columns per tile (one weight-scale column block)
 constexpr int KBK = 128;      // K per stage (one scale block)
 constexpr int KCH = KBK / 8;  // 16-byte chunks per LDS row (16)
-constexpr int KTHR = 256;
+constexpr int KSW = 32;       // input-scale blocks held in LDS at a time
 
 // hidden rows: chunk c of row r lives at chunk c ^ (r & 15)
 __device__ __forceinline__ int swz_a(int r, int c) { return c ^ (r & 15); }
-// transposed weight rows (one per column n): distinct chunks for the 16 rows
-// {base + 4j + t} an MFMA fragment read touches and spread for the writes
-__device__ __forceinline__ int swz_b(int n, int c) { return c ^ (((n >> 2) ^ (n >> 6)) & 15); }
-
-__device__ __forceinline__ uint32_t bf16pair_hi(float lo, float hi) {
-  // top halves of two floats (exact bf16 images of e4m3 values) -> bf16 pair
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
-}
 
 }  // namespace
-
-__global__ __launch_bounds__(KTHR) void kproj_fp8_paged_kernel(
-    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
-    const float* __restrict__ in_scale, const float* __restrict__ w_scale, uint16_t* __restrict__ blocks,
-    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
-    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][KBM * KCH];
-  __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][KBN * KCH];
-  __shared__ long long row_dst[KBM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves: 32 rows x 64 columns each
-  const int q = lane >> 4, r16 = lane & 15;
-
-  const int tiles = tiles_m * tiles_n;
-  const int per = (tiles + 7) >> 3;
-  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (lin >= tiles) return;
-  const int m0 = (lin / tiles_n) * KBM;   // N-fastest: the n-tiles of a row block share an XCD
-  const int nb = lin % tiles_n;
-  const int n0 = nb * KBN;
-  const int KB = Kh / KBK;
-
-  // ---- staging maps ----
-  // hidden: 64 rows x 16 chunks = 1024 chunks, 4 per thread
-  int a_row[4], a_ch[4];
-  const uint16_t* a_src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + i * KTHR;
-    a_row[i] = id >> 4;
-    a_ch[i] = id & 15;
-    a_src[i] = H + (size_t)min(m0 + a_row[i], T - 1) * Kh + a_ch[i] * 8;
-  }
-  // weight: thread owns 4 K rows (kq) x 16 columns (ng)
-  const int ng = tid & 7, kq = tid >> 3;
-  const uint8_t* w_src = W + (size_t)(4 * kq) * N + n0 + 16 * ng;
-
-  u32x4_t ra[4], rw[4];
-  auto load_stage = [&](int kb) {
-    const int k0 = kb * KBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(a_src[i] + k0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rw[r] = *reinterpret_cast<const u32x4_t*>(w_src + (size_t)(k0 + r) * N);
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_a[buf][a_row[i] * KCH + swz_a(a_row[i], a_ch[i])] = ra[i];
-    // 4 x 16 fp8 -> for each of the 16 columns, bf16 of K rows 4kq..4kq+3
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      float2_t f[4][2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t word = rw[r][c4];
-        f[r][0] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-        f[r][1] = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int n = 16 * ng + 4 * c4 + b;
-        const float x0 = f[0][b >> 1][b & 1], x1 = f[1][b >> 1][b & 1];
-        const float x2 = f[2][b >> 1][b & 1], x3 = f[3][b >> 1][b & 1];
-        const u32x2_t v = u32x2_t{bf16pair_hi(x0, x1), bf16pair_hi(x2, x3)};
-        const int c = kq >> 1;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&lds_b[buf][n * KCH + swz_b(n, c)]) + (kq & 1) * 2;
-        *reinterpret_cast<u32x2_t*>(dst) = v;
-      }
-    }
-  };
-
-  float4_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  // this lane's output rows (for the per-row input scale)
-  int srow[2][4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) srow[mt][i] = min(m0 + wm * 32 + mt * 16 + q * 4 + i, T - 1);
-
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const int cur = kb & 1;
-    const bool more = kb + 1 < KB;
-    if (more) load_stage(kb + 1);
-    float fac[2][4];
-    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fac[mt][i] = in_scale[(size_t)srow[mt][i] * KB + kb];
-    __builtin_amdgcn_sched_barrier(0);
-
-    float4_t part[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t bf[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int n = wn * 64 + 4 * r16 + t;
-        bf[t] = lds_b[cur][n * KCH + swz_b(n, s * 4 + q)];
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int row = wm * 32 + mt * 16 + r16;
-        const u32x4_t av = lds_a[cur][row * KCH + swz_a(row, s * 4 + q)];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) part[mt][t] = mfma16x16x32_bf16(av, bf[t], part[mt][t]);
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][t][i] += (fac[mt][i] * wsv) * part[mt][t][i];
-
-    if (more) store_stage(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: token -> (page, slot) destination of each of the tile's rows ----
-  if (tid < KBM) {
-    const int t = m0 + tid;
-    long long dst = -1;
-    if (t < T) {
-      int lo = 0, hi = batch;            // find the last b with offs[b] <= t
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if ((int)offs[mid] <= t) lo = mid; else hi = mid;
-      }
-      const int pos = (int)cache_len[lo] + (t - (int)offs[lo]);
-      const int page = (int)page_table[(size_t)lo * max_pages + pos / page_size];
-      const int slot = pos % page_size;
-      dst = ((((long long)layer * 2 + 0) * num_pages + page) * page_size + slot) * (long long)N;
-    }
-    row_dst[tid] = dst;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long d = row_dst[wm * 32 + mt * 16 + q * 4 + i];
-      const int col = n0 + wn * 64 + 4 * r16;
-      if (d >= 0 && col < N) {
-        const uint32_t lo = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
-        const uint32_t hi = (uint32_t)f2bf_rn(acc[mt][2][i]) | ((uint32_t)f2bf_rn(acc[mt][3][i]) << 16);
-        *reinterpret_cast<u32x2_t*>(blocks + d + col) = u32x2_t{lo, hi};
-      }
-    }
-  }
-}
 
 // Epilogue shared by the tiled designs: each token row of the tile
 // goes to (layer, plane, page, slot) of the cache, as bf16 or as e4m3 codes with
 // per-run scales (described below). acc holds a wave's 48 x 32 tile: rows
-// wm * 48 + mt * 16 + 4q + i, columns wn * 32 + 2 r16 + j (BLK false: a lane owns
-// two adjacent columns) or wn * 32 + 16 j + r16 (BLK true). `scratch` is LDS of
-// at least 4 * BM floats that no wave reads any more.
-template <int BM, bool Q8, bool BLK = false>
+// wm * 48 + mt * 16 + 4q + i, columns wn * 32 + 16 j + r16 (column tile j holds
+// 16 consecutive columns). `scratch` is LDS of at least 4 * BM floats that no
+// wave reads any more.
+template <int BM, bool Q8>
 __device__ __forceinline__ void kproj_store_tile(
     const float4_t (&acc)[3][2], long long* row_dst, float* scratch, int tid, int m0, int n0, int T,
     const uint32_t* __restrict__ offs, const uint32_t* __restrict__ cache_len,
@@ -260,7 +79,7 @@ __device__ __forceinline__ void kproj_store_tile(
     row_dst[tid] = dst;
   }
   __syncthreads();
-  const int col = colp + wn * 32 + (BLK ? r16 : 2 * r16);   // column of acc[.][0]; acc[.][1]: +16 or +1
+  const int col = colp + wn * 32 + r16;   // column of acc[.][0]; acc[.][1]: +16
   if constexpr (!Q8) {
     uint16_t* __restrict__ blocks = static_cast<uint16_t*>(blocks_v);
 #pragma unroll
@@ -269,13 +88,8 @@ __device__ __forceinline__ void kproj_store_tile(
       for (int i = 0; i < 4; ++i) {
         const long long d = row_dst[wm * 48 + mt * 16 + q * 4 + i];
         if (d >= 0) {
-          if constexpr (BLK) {
-            blocks[d * n_plane + col] = f2bf_rn(acc[mt][0][i]);
-            blocks[d * n_plane + col + 16] = f2bf_rn(acc[mt][1][i]);
-          } else {
-            const uint32_t v = (uint32_t)f2bf_rn(acc[mt][0][i]) | ((uint32_t)f2bf_rn(acc[mt][1][i]) << 16);
-            *reinterpret_cast<uint32_t*>(blocks + d * n_plane + col) = v;
-          }
+          blocks[d * n_plane + col] = f2bf_rn(acc[mt][0][i]);
+          blocks[d * n_plane + col + 16] = f2bf_rn(acc[mt][1][i]);
         }
       }
     }
@@ -327,12 +141,8 @@ __device__ __forceinline__ void kproj_store_tile(
         const float v0 = sc > 0.f ? acc[mt][0][i] / sc : 0.f;
         const float v1 = sc > 0.f ? acc[mt][1][i] / sc : 0.f;
         const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);   // nearest even, low half
-        if constexpr (BLK) {
-          blocks[d * n_plane + col] = (uint8_t)pk;
-          blocks[d * n_plane + col + 16] = (uint8_t)(pk >> 8);
-        } else {
-          *reinterpret_cast<uint16_t*>(blocks + d * n_plane + col) = (uint16_t)pk;
-        }
+        blocks[d * n_plane + col] = (uint8_t)pk;
+        blocks[d * n_plane + col + 16] = (uint8_t)(pk >> 8);
         if (scale_writer) kv_scales[d * nsc + (colp + wn * 32) / qgran] = sc;
       }
     }
@@ -376,7 +186,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
   constexpr int LOADS = (ACH + BCH + NTHR - 1) / NTHR;  // loads per thread per stage
   __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][ACH];
   __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BCH];
-  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
+  __shared__ __attribute__((aligned(16))) float lds_is[KSW * BM];   // [kb % KSW][row]: a window of KSW blocks
   __shared__ long long row_dst[BM];
 
   const int tid = threadIdx.x;
@@ -430,10 +240,15 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
     }
   };
 
-  for (int e = tid; e < KB * BM; e += NTHR) {
-    const int row = e % BM, kb = e / BM;
-    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
-  }
+  // input scales of the tile's rows, KSW blocks at a time (refilled every KSW stages)
+  auto fill_is = [&](int kb0) {
+    const int nb_is = min(KSW, KB - kb0);
+    for (int e = tid; e < nb_is * BM; e += NTHR) {
+      const int row = e % BM, kb = e / BM;
+      lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb0 + kb];
+    }
+  };
+  fill_is(0);
 
   float4_t acc[MT][2];
 #pragma unroll
@@ -464,7 +279,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
       const u32x4_t lo = lds_a[buf][row * 8 + ((2 * q) ^ (row & 7))];
       const u32x4_t hi = lds_a[buf][row * 8 + ((2 * q + 1) ^ (row & 7))];
       const i32x8_t av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[(kb % KSW) * BM + wm * 48 + mt * 16 + q * 4]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const float4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -484,6 +299,10 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
 #pragma unroll
     for (int p = 0; p < PD; ++p) {
       const int i = kb + p;   // stage multiplied now; rg[p] (stage i, stored) takes stage i + PD
+      if (i < KB && i > 0 && i % KSW == 0) {   // the next window of input scales (uniform test;
+        fill_is(i);                            // every wave left the previous one at the last barrier)
+        __syncthreads();
+      }
       if constexpr (PD > 1) load_stage(min(i + PD, KB - 1), rg[p]);   // past the end: re-reads, unstored
       else load_stage(min(i + 1, KB - 1), rg[0]);
       __builtin_amdgcn_sched_barrier(0);
@@ -494,7 +313,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_f8f8_kernel(
   }
 
   // column tile t of a wave holds 16 consecutive columns (the transpose read's order)
-  kproj_store_tile<BM, Q8, true>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
+  kproj_store_tile<BM, Q8>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
                                  max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
@@ -529,7 +348,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
   constexpr int LOADS = (ACH + BCH + NTHR - 1) / NTHR;  // loads per thread per stage
   __shared__ __attribute__((aligned(16))) u32x4_t lds_a[2][ACH];
   __shared__ __attribute__((aligned(16))) u32x4_t lds_b[2][BCH];
-  __shared__ __attribute__((aligned(16))) float lds_is[32 * BM];   // [kb][row], kb < Kh/128 <= 32
+  __shared__ __attribute__((aligned(16))) float lds_is[KSW * BM];   // [kb % KSW][row]: a window of KSW blocks
   __shared__ long long row_dst[BM];
 
   const int tid = threadIdx.x;
@@ -583,10 +402,15 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
     }
   };
 
-  for (int e = tid; e < KB * BM; e += NTHR) {
-    const int row = e % BM, kb = e / BM;
-    lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb];
-  }
+  // input scales of the tile's rows, KSW blocks at a time (refilled every KSW stages)
+  auto fill_is = [&](int kb0) {
+    const int nb_is = min(KSW, KB - kb0);
+    for (int e = tid; e < nb_is * BM; e += NTHR) {
+      const int row = e % BM, kb = e / BM;
+      lds_is[kb * BM + row] = in_scale[(size_t)min(m0 + row, T - 1) * KB + kb0 + kb];
+    }
+  };
+  fill_is(0);
 
   float4_t acc[MT][2];
 #pragma unroll
@@ -625,7 +449,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
     const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[kb * BM + wm * 48 + mt * 16 + q * 4]);
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[(kb % KSW) * BM + wm * 48 + mt * 16 + q * 4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float f = is4[i] * wsv;
@@ -644,6 +468,10 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
 #pragma unroll
     for (int p = 0; p < PD; ++p) {
       const int i = kb + p;   // stage multiplied now; rg[p] (stage i, stored) takes stage i + PD
+      if (i < KB && i > 0 && i % KSW == 0) {   // the next window of input scales (uniform test;
+        fill_is(i);                            // every wave left the previous one at the last barrier)
+        __syncthreads();
+      }
       if constexpr (PD > 1) load_stage(min(i + PD, KB - 1), rg[p]);   // past the end: re-reads, unstored
       else load_stage(min(i + 1, KB - 1), rg[0]);
       __builtin_amdgcn_sched_barrier(0);
@@ -653,7 +481,7 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
     }
   }
 
-  kproj_store_tile<BM, Q8, true>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
+  kproj_store_tile<BM, Q8>(acc, row_dst, lds_is, tid, m0, n0, T, offs, cache_len, page_table, batch,
                                  max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
@@ -719,30 +547,17 @@ hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream) {
   static const int cand[] = {48, 96, 144};
   if (p.hidden_fp8) {
     // e4m3 hidden rows: 48, 96 or 144-row tiles, two stages of loads in flight
-    if (p.Kh / KBK > 32) return hipErrorNotSupported;
     switch (pick_kproj_rows(p, cand, 3) / 48) {
       case 1: return launch_kproj_f8f8<1, 2>(p, stream);
       case 2: return launch_kproj_f8f8<2, 2>(p, stream);
       default: return launch_kproj_f8f8<3, 2>(p, stream);
     }
   }
-  if (p.Kh / KBK <= 32) {   // raw-weight design: at most 32 input-scale blocks in LDS
-    switch (pick_kproj_rows(p, cand, 3) / 48) {
-      case 1: return launch_kproj_bf16<1, 2>(p, stream);
-      case 2: return launch_kproj_bf16<2, 2>(p, stream);
-      default: return launch_kproj_bf16<3, 2>(p, stream);
-    }
+  switch (pick_kproj_rows(p, cand, 3) / 48) {
+    case 1: return launch_kproj_bf16<1, 2>(p, stream);
+    case 2: return launch_kproj_bf16<2, 2>(p, stream);
+    default: return launch_kproj_bf16<3, 2>(p, stream);
   }
-  // longer hidden rows: the long-row design (bf16 cache, keys only)
-  if (p.fp8 || p.n_plane != p.N) return hipErrorNotSupported;
-  const int tiles_m = (int)((p.T + KBM - 1) / KBM), tiles_n = (int)(p.N / KBN);
-  const int tiles = tiles_m * tiles_n;
-  const int grid = ((tiles + 7) / 8) * 8;
-  hipLaunchKernelGGL(kproj_fp8_paged_kernel, dim3(grid), dim3(KTHR), 0, stream, p.hidden, p.row_offsets,
-                     p.weight, p.input_scale, p.weight_scale, static_cast<uint16_t*>(p.blocks), p.cache_lengths, p.page_table, (int)p.T,
-                     (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
-                     (int)p.layer_idx, tiles_m, tiles_n);
-  return hipGetLastError();
 }
 
 }  // namespace qg

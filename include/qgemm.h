@@ -290,7 +290,7 @@ typedef struct {
  * chosen by layer_idx (Parameters: scales_granularity_mnk gives the scale blocks).
  *
  *   hidden            bf16 or fp8 e4m3 [T, Kh] (the page's dtype parameter; e4m3 runs
- *                     both MFMA operands in e4m3, with Kh <= 4096)
+ *                     both MFMA operands in e4m3)
  *   input_row_offsets u32  [B + 1]   offs[0] = 0, non-decreasing, offs[B] = T
  *   weight            fp8 e4m3 [Kh, N], N = Hkv * D
  *   input_scale       f32  [T, Kh / 128]

@@ -128,6 +128,8 @@ def test_tile_heights(gpu, lib, i):
 
 
 def test_long_hidden_rows(gpu, lib):
-    """More than 32 scale blocks of K (the long-row design): ragged, with history."""
+    """More than 32 scale blocks of K (input scales refilled in LDS every 32
+    blocks): ragged, with history; 33, 40 and 97 blocks (one, one and three refills)."""
     check(lib, small(70, (100, 1, 64, 65, 0, 130), Kh=33 * 128, cache_lengths=(0, 3, 17, 128, 5, 250)), "Kh=4224")
     check(lib, small(71, (300, 7), Kh=40 * 128, hkv=2, D=128, page_size=16), "Kh=5120")
+    check(lib, small(72, (500, 60), Kh=97 * 128, hkv=2, D=128, page_size=32), "Kh=12416")

@@ -91,6 +91,12 @@ def test_full_size(gpu, lib):
                                "full fused e4m3 cache"))
 
 
+def test_long_hidden(gpu, lib):
+    """More than 32 scale blocks of K (input scales refilled every 32 blocks)."""
+    check(lib, kv_inputs(90, (100, 1, 64), Kh=33 * 128, planes=1, hidden="fp8"), "Kh=4224 keys bf16")
+    check(lib, kv_inputs(91, (150, 20), Kh=65 * 128, cache="fp8", qgran=64, hidden="fp8"), "Kh=8320 kv e4m3")
+
+
 def test_determinism(gpu, lib):
     k = kv_inputs(80, (200, 31), cache="fp8", qgran=32, hidden="fp8")
     a, sa = run_gpu(lib, k)

@@ -247,15 +247,12 @@ def test_full_size(gpu, lib):
                                                                               np.uint32)), "full keys e4m3 history"))
 
 
-def test_rejects_long_hidden(gpu, lib):
-    """Keys and values, or an e4m3 cache, with more than 32 scale blocks of K are refused."""
-    k = kv_inputs(70, (10,), Kh=33 * 128, cache="fp8", qgran=128)
-    fp8 = torch.from_numpy(k.blocks.copy()).cuda()
-    st = lib.kv_matmul_ragged_paged_scale(
-        dev16(k.hidden, torch.bfloat16), dev32(k.row_offsets), dev8(k.weight), devf32(k.input_scale),
-        devf32(k.weight_scale), fp8, dev32(k.cache_lengths), dev32(k.page_table), k.layer_idx,
-        kv_scales=devf32(k.scales), quantization_granularity=128, raise_on_error=False)
-    assert st == lib.QG.ERR_UNSUPPORTED
+def test_long_hidden(gpu, lib):
+    """More than 32 scale blocks of K: the tile rows' input scales are refilled in
+    LDS every 32 blocks (33 blocks: one refill with a one-block window; 65: two)."""
+    check(lib, kv_inputs(70, (10, 130, 1), Kh=33 * 128, cache="fp8", qgran=128), "Kh=4224 e4m3")
+    check(lib, kv_inputs(71, (77, 64, 3), Kh=65 * 128, cache_lengths=(5, 0, 200)), "Kh=8320 bf16")
+    check(lib, kv_inputs(72, (200,), Kh=65 * 128, cache="fp8", qgran=32, planes=1), "Kh=8320 keys e4m3")
 
 
 def test_determinism(gpu, lib):
