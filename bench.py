@@ -75,19 +75,19 @@ MEASURED_TRAFFIC = {
     "decode": (9239429, "ec78a7e77d980bda"),
     "prefill": (276791696, "4f7241325a7d6b62"),
     "square": (101391104, "4f7241325a7d6b62"),
-    "grouped": (368005065, "9807d009efbaa9a2"),
-    "grouped_kn": (365904491, "9807d009efbaa9a2"),
+    "grouped": (367971168, "7a9d825f74180d39"),
+    "grouped_kn": (365907538, "7a9d825f74180d39"),
     "grouped_w4": (114656386, "4f7241325a7d6b62"),
-    "kproj": (85578482, "6f07c4251351596e"),
+    "kproj": (85592817, "7b5abd03aad04665"),
     "decode_gate": (9258198, "ec78a7e77d980bda"),
     "prefill_gate": (276948233, "4f7241325a7d6b62"),
     "decode_bf16": (9238405, "ec78a7e77d980bda"),
     "prefill_bf16": (302809964, "4f7241325a7d6b62"),
     "decode_nk": (9233840, "ec78a7e77d980bda"),
     "prefill_nk": (232418124, "4f7241325a7d6b62"),
-    "kvproj": (202271867, "6f07c4251351596e"),
-    "kvproj_e4m3": (193909613, "6f07c4251351596e"),
-    "kproj_e4m3h": (64369079, "6f07c4251351596e"),
+    "kvproj": (202287161, "7b5abd03aad04665"),
+    "kvproj_e4m3": (193909293, "7b5abd03aad04665"),
+    "kproj_e4m3h": (64374327, "7b5abd03aad04665"),
 }
 
 
