@@ -168,21 +168,23 @@ def grouped_inputs(seed: int = 4, E: int = 64, T: int = 4096, K: int = 2048, N: 
 
 @dataclasses.dataclass
 class GroupedW4Inputs:
-    a: np.ndarray           # uint16 [T, K] fp16 bits
+    a: np.ndarray           # uint16 [T, K] fp16 (or bf16) bits
     a_offsets: np.ndarray   # uint32 [G+1]
     b: np.ndarray           # uint32 [E, K/8, N] packed 4-bit codes
-    scales: np.ndarray      # uint16 [E, K/group_size, N] fp16 bits
+    scales: np.ndarray      # uint16 [E, K/group_size, N] fp16 (or bf16) bits
     expert_ids: np.ndarray  # int32 [G]
     usage: np.ndarray       # uint32 [2]: [0] max rows in a group, [1] active group count
     group_size: int = 128
+    dtype: str = "f16"
 
 
 def grouped_w4_inputs(seed: int = 6, E: int = 64, T: int = 4096, K: int = 2048, N: int = 1408,
-                      skip_frac: float = 0.10, group_size: int = 128) -> GroupedW4Inputs:
+                      skip_frac: float = 0.10, group_size: int = 128, dtype: str = "f16") -> GroupedW4Inputs:
     """Grouped W4A16 workload: the grouped workload's routing (multinomial counts,
-    floor(skip_frac * E) skipped groups) with W4A16 operands (A ~ N(0,1) fp16,
-    uniform 4-bit codes, scales U(0.005, 0.02) fp16). Draw order: counts, skipped
-    groups, A, packed words, scales."""
+    floor(skip_frac * E) skipped groups) with W4A16 operands (A ~ N(0,1), uniform
+    4-bit codes, scales U(0.005, 0.02); A and the scales stored as `dtype`, fp16 or
+    bf16, from the same draws). Draw order: counts, skipped groups, A, packed
+    words, scales."""
     rng = np.random.default_rng(seed)
     counts = rng.multinomial(T, [1.0 / E] * E)
     a_off = np.zeros(E + 1, dtype=np.uint32)
@@ -191,12 +193,12 @@ def grouped_w4_inputs(seed: int = 6, E: int = 64, T: int = 4096, K: int = 2048, 
     skip = rng.choice(E, n_skip, replace=False)
     ids = np.arange(E, dtype=np.int32)
     ids[skip] = -1
-    a = f16_bits(rng.standard_normal((T, K)))
+    a = _bits(rng.standard_normal((T, K)), dtype)
     b = rng.integers(0, 2**32, size=(E, K // 8, N), dtype=np.uint32)
-    s = f16_bits(rng.uniform(0.005, 0.02, size=(E, K // group_size, N)))
+    s = _bits(rng.uniform(0.005, 0.02, size=(E, K // group_size, N)), dtype)
     usage = np.array([counts.max(), E], dtype=np.uint32)
     return GroupedW4Inputs(a=a, a_offsets=a_off, b=b, scales=s, expert_ids=ids, usage=usage,
-                           group_size=group_size)
+                           group_size=group_size, dtype=dtype)
 
 
 # ---------------------------------------------------------------------------

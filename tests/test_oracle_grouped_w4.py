@@ -127,3 +127,76 @@ def test_epilogue_each_group_uses_its_experts_bias_and_gate():
             x = [bf[e, 2 * j] * 0.5 * (1 + math.tanh(0.5 * bf[e, 2 * j])) * bf[e, 2 * j + 1] + rf[r, j]
                  for j in range(N // 2)]
             assert np.array_equal(c[r], nm.f16_bits_of(nm.round_to_f16(np.array(x)))), (g, r)
+
+
+# ------------------------------------------------------------------ bf16 activations, scales and output
+
+def test_bf16_single_group_reduces_to_w4():
+    w = synth.w4_inputs(24, 40, 256, seed=12, group_size=64, dtype="bf16")
+    T, N = w.a.shape[0], w.b.shape[1]
+    got = oracle.grouped_gemm_w4(np.full((T, N), SENT, np.uint16), w.a, np.array([0, T], np.uint32),
+                                 w.b[None], w.scales[None], np.array([0], np.int32), np.array([T, 1], np.uint32), 64,
+                                 dtype="bf16")
+    assert np.array_equal(got, oracle.qgemm_w4(w.a, w.b, w.scales, 64, dtype="bf16"))
+
+
+def test_bf16_brute_force_tiny():
+    """bf16 operands decoded by shifting the bits into a float32; scalar loops with
+    their own nibble extraction. Every written value must be a nearest bf16 to
+    the exact sum: no closer value is one bit pattern up or down."""
+    for seed in range(3):
+        rng = np.random.default_rng(100 + seed)
+        E, G, T, K, N, gs = 3, 4, 18, 64, 8, 32
+        counts = rng.multinomial(T, [1.0 / G] * G)
+        off = np.zeros(G + 1, np.uint32)
+        off[1:] = np.cumsum(counts)
+        ids = rng.integers(-1, E, size=G).astype(np.int32)
+        a = synth.bf16_bits(rng.standard_normal((T, K)))
+        b = rng.integers(0, 2**32, size=(E, K // 8, N), dtype=np.uint32)
+        s = synth.bf16_bits(rng.uniform(0.005, 0.02, size=(E, K // gs, N)))
+        c0 = np.full((T, N), SENT, np.uint16)
+        got = oracle.grouped_gemm_w4(c0, a, off, b, s, ids, np.array([0, G], np.uint32), gs, dtype="bf16")
+        av = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        sv = (s.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        dec = lambda v: float((np.uint32(v) << 16).view(np.float32))
+        written = np.zeros((T, N), bool)
+        for g in range(G):
+            e = int(ids[g])
+            if e < 0:
+                continue
+            for r in range(int(off[g]), int(off[g + 1])):
+                written[r] = True
+                for n in range(N):
+                    acc = 0.0
+                    for k in range(K):
+                        q = (int(b[e, k // 8, n]) >> (4 * (k % 8))) & 0xF
+                        acc += av[r, k] * (q - 8) * sv[e, k // gs, n]
+                    v = int(got[r, n])
+                    err = abs(acc - dec(v))
+                    for nb in (v - 1, v + 1):
+                        if 0 <= nb < 0x10000 and (nb & 0x7FFF) < 0x7F80:   # finite neighbours
+                            assert err <= abs(acc - dec(nb)), (seed, r, n)
+        assert np.all(got[~written] == SENT)
+
+
+def test_bf16_each_group_uses_its_expert_exactly():
+    """The expert fingerprint of the fp16 pin above in bf16: C[r][n] = 2^(r mod 4) c_e / 16, exact."""
+    E, G, T, K, N, gs = 5, 7, 30, 64, 8, 32
+    c_e = np.array([1, 2, 3, 5, 7])
+    b = np.full((E, K // 8, N), 0x88888888, np.uint32)
+    for e in range(E):
+        b[e, 0, :] = 0x88888880 | (8 + c_e[e])
+    s = np.full((E, K // gs, N), nm.bf16_bits_of(np.array(2.0 ** -4)), np.uint16)
+    a = np.zeros((T, K))
+    a[:, 0] = 2.0 ** (np.arange(T) % 4)
+    off = np.array([0, 3, 3, 9, 17, 20, 26, 30], np.uint32)
+    ids = np.array([4, 0, -1, 2, 1, 3, 0], np.int32)
+    c0 = np.full((T, N), SENT, np.uint16)
+    got = oracle.grouped_gemm_w4(c0, nm.bf16_bits_of(a), off, b, s, ids, np.array([8, G], np.uint32), gs,
+                                 dtype="bf16")
+    for g in range(G):
+        for r in range(off[g], off[g + 1]):
+            if ids[g] < 0:
+                assert np.all(got[r] == SENT)
+            else:
+                assert np.all(nm.decode_bf16(got[r]) == 2.0 ** (r % 4) * c_e[ids[g]] / 16), (g, r)
