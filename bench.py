@@ -12,7 +12,7 @@ roofline).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
                     [--config decode|prefill|square|decode_bf16|prefill_bf16|decode_gate|prefill_gate|
-                              decode_nk|prefill_nk|grouped|grouped_kn|grouped_w4|kproj|kvproj|
+                              decode_nk|prefill_nk|grouped|grouped_kn|grouped_w4|grouped_w4_bf16|kproj|kvproj|
                               kvproj_e4m3|kproj_e4m3h]
 
 Prints one JSON line. `value` is algorithmic HBM bytes per second over the timed
@@ -65,6 +65,7 @@ KERNEL_SOURCES = {
     "grouped": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_kn": ["capi.cpp", "device_common.h", "launch.h", "grouped_bf16.hip"],
     "grouped_w4": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
+    "grouped_w4_bf16": ["capi.cpp", "device_common.h", "launch.h", "w4_prefill.hip"],
     "kproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
     "kvproj": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
     "kvproj_e4m3": ["capi.cpp", "device_common.h", "launch.h", "kproj_fp8.hip"],
@@ -122,7 +123,8 @@ def parse():
                                                            "decode_gate", "prefill_gate", "decode_nk", "prefill_nk",
                                                            "kvproj", "kvproj_e4m3",
                                                            "kproj_e4m3h",
-                                                           "grouped", "grouped_kn", "grouped_w4", "kproj"])
+                                                           "grouped", "grouped_kn", "grouped_w4", "grouped_w4_bf16",
+                                                           "kproj"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip the hot / read / dense-GEMM context numbers")
     p.add_argument("--no-square", action="store_true",
@@ -449,8 +451,9 @@ class GroupedW4:
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
-        d = synth.grouped_w4_inputs()
+        d = synth.grouped_w4_inputs(dtype=self.dtype)
         self.d = d
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float16
         T, K = d.a.shape
         E, _, N = d.b.shape
         self.T, self.K, self.N, self.E = T, K, N, E
@@ -465,15 +468,16 @@ class GroupedW4:
         self.flops_per_step = 2 * self.active_rows * N * K
         self.R = max(1, math.ceil(ROTATE_BYTES / (d.b.nbytes + d.scales.nbytes + d.a.nbytes + T * N * 2)))
         dev = torch.device("cuda")
-        a = torch.from_numpy(d.a.view(np.int16)).to(dev).view(torch.float16)
+        a = torch.from_numpy(d.a.view(np.int16)).to(dev).view(tdt)
         b = torch.from_numpy(d.b.view(np.int32)).to(dev)
-        s = torch.from_numpy(d.scales.view(np.int16)).to(dev).view(torch.float16)
+        s = torch.from_numpy(d.scales.view(np.int16)).to(dev).view(tdt)
         off_t = torch.from_numpy(d.a_offsets.view(np.int32)).to(dev)
         ids = torch.from_numpy(d.expert_ids).to(dev)
-        self.slots = [(torch.empty(T, N, dtype=torch.float16, device=dev), a.clone(), off_t, b.clone(), s.clone(),
+        self.slots = [(torch.empty(T, N, dtype=tdt, device=dev), a.clone(), off_t, b.clone(), s.clone(),
                        ids) for _ in range(self.R)]
         self.usage = [int(v) for v in d.usage]
-        self.name = f"grouped_w4a16_E{E}_T{T}_K{K}_N{N}_gs{gs}_skip10pct"
+        self.name = (f"grouped_w4a16_E{E}_T{T}_K{K}_N{N}_gs{gs}_skip10pct"
+                     + ("_bf16" if self.dtype == "bf16" else ""))
 
     def launches(self, step):
         c, a, off, b, s, ids = self.slots[step % self.R]
@@ -491,7 +495,8 @@ class GroupedW4:
         G = 8
         usage = np.array([d.usage[0], G], np.uint32)
         c0 = np.zeros((self.T, self.N), np.uint16)
-        oracle.grouped_gemm_w4(c0, d.a, d.a_offsets, d.b, d.scales, d.expert_ids, usage, d.group_size)
+        oracle.grouped_gemm_w4(c0, d.a, d.a_offsets, d.b, d.scales, d.expert_ids, usage, d.group_size,
+                               dtype=self.dtype)
         off = d.a_offsets.astype(np.int64)
         rows = sum(int(off[g + 1] - off[g]) for g in range(G) if d.expert_ids[g] >= 0)
         ne = sum(1 for g in range(G) if d.expert_ids[g] >= 0)
@@ -505,6 +510,11 @@ class GroupedW4:
 
     def dense_equivalent(self):
         return None
+
+
+class GroupedW4BF16(GroupedW4):
+    """The grouped W4 workload with bf16 activations, scales and output."""
+    dtype = "bf16"
 
 
 class KProjFP8:
@@ -688,7 +698,8 @@ WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,
              "decode_gate": DecodeW4Gate, "prefill_gate": PrefillW4Gate,
              "decode_nk": DecodeW4NK, "prefill_nk": PrefillW4NK,
              "kvproj": KVProjFP8, "kvproj_e4m3": KVProjFP8Cache, "kproj_e4m3h": KProjE4M3Hidden,
-             "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4, "kproj": KProjFP8}
+             "grouped": GroupedBF16, "grouped_kn": GroupedBF16KN, "grouped_w4": GroupedW4,
+             "grouped_w4_bf16": GroupedW4BF16, "kproj": KProjFP8}
 
 
 def time_workload(torch, wl, steps, warmup):

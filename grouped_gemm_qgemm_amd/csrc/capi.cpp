@@ -241,11 +241,13 @@ static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, co
       expert_ids->rank != 1)
     return QG_ERR_RANK;
   qg_status st;
-  if ((st = check_tensor(c, 2, QG_F16)) != QG_OK) return st;
-  if ((st = check_tensor(a, 2, QG_F16)) != QG_OK) return st;
+  // a, scales and c (and bias, residual) share one type, fp16 or bf16
+  const qg_dtype act = a->dtype == QG_BF16 ? QG_BF16 : QG_F16;
+  if ((st = check_tensor(c, 2, act)) != QG_OK) return st;
+  if ((st = check_tensor(a, 2, act)) != QG_OK) return st;
   if ((st = check_tensor(a_offsets, 1, QG_U32)) != QG_OK) return st;
   if ((st = check_tensor(b_packed, 3, QG_U32)) != QG_OK) return st;
-  if ((st = check_tensor(scales, 3, QG_F16)) != QG_OK) return st;
+  if ((st = check_tensor(scales, 3, act)) != QG_OK) return st;
   if ((st = check_tensor(expert_ids, 1, QG_I32)) != QG_OK) return st;
   if (pack_factor != 8) return QG_ERR_UNSUPPORTED;
   if (group_size <= 0) return QG_ERR_INVALID_ARG;
@@ -265,7 +267,7 @@ static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, co
   const uint32_t num_active = expert_usage_stats_host[1];
   if ((int64_t)num_active > G) return QG_ERR_INVALID_ARG;
   qg::Epilogue epi;
-  if ((st = check_epilogue(epilogue, bias, residual, QG_F16, E, T, N, &epi)) != QG_OK) return st;
+  if ((st = check_epilogue(epilogue, bias, residual, act, E, T, N, &epi)) != QG_OK) return st;
   if (T > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2 || E > INT32_MAX / 2) return QG_ERR_UNSUPPORTED;
   // the tiled kernel addresses a tile's rows of A and eight packed rows of an
   // expert's B with 32-bit buffer offsets
@@ -276,6 +278,7 @@ static qg_status grouped_gemm_w4_impl(const qg_tensor* c, const qg_tensor* a, co
                       static_cast<const uint32_t*>(a_offsets->data), static_cast<const uint32_t*>(b_packed->data),
                       static_cast<const uint16_t*>(scales->data), static_cast<const int32_t*>(expert_ids->data),
                       T, N, K, E, group_size, (int)num_active, epi};
+  p.bf16 = act == QG_BF16 ? 1 : 0;
   return launch_status(qg::launch_w4_grouped(p, stream));
 }
 

@@ -33,16 +33,17 @@ struct W4Args {
 };
 
 struct W4GroupedArgs {
-  uint16_t* C;                // f16 [T, N]
-  const uint16_t* A;          // f16 [T, K]
+  uint16_t* C;                // f16 or bf16 [T, N]
+  const uint16_t* A;          // f16 or bf16 [T, K]
   const uint32_t* a_offsets;  // [G+1]
   const uint32_t* B;          // u32 [E, K/8, N]
-  const uint16_t* S;          // f16 [E, K/group_size, N]
+  const uint16_t* S;          // f16 or bf16 [E, K/group_size, N]
   const int32_t* expert_ids;  // [G]
   int64_t T, N, K, E;
   int group_size;
   int num_active;
   Epilogue epi;               // C is [T, N / 2] with EPI_SILU_GATE; bias [E, N]
+  int bf16 = 0;               // A, S, C (and bias, residual) are bf16
 };
 
 // Planes of A for the grouped GEMM (fused LoRA QKV): output columns [0, pb1),
@@ -96,7 +97,7 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream);
 
 hipError_t launch_grouped_bf16(const GroupedArgs& p, hipStream_t stream);
 
-// Grouped W4A16 (int4 experts, fp16 activations).
+// Grouped W4A16 (int4 experts, fp16 or bf16 activations).
 hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream);
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream);

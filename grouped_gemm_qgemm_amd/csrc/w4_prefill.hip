@@ -543,7 +543,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
 // holds an upper bound on the tile count (only the device knows the group
 // sizes); the real count is split evenly over the eight XCDs, at most
 // ceil(count / 8) <= grid / 8 tiles each, and workgroups past their XCD's run exit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD, bool BF>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
@@ -571,27 +571,34 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   Epilogue ept = ep;
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, false, false, BD>(C + (size_t)r_begin * NO,
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
                                                                    A + (size_t)r_begin * K, B + e * wpe,
                                                                    S + e * spe, rows, N, K, group_size, 0,
                                                                    nt * BN, lds, ept);
 }
 
-// Grouped launch: 64-row chunks of a group by 256 columns, three workgroups
-// per CU, two stages of loads in flight, B words loaded straight into the
-// lanes' registers (one wave per column strip, so no B word is shared).
-hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
-  constexpr int BM = 64, BN = 256, WM = 1, WN = 4, MINB = 3, KG = 1, PD = 2;
+// Grouped launch: 64-row chunks of a group by 256 columns, B words loaded
+// straight into the lanes' registers (one wave per column strip, so no B word
+// is shared). fp16: three workgroups per CU, two stages of loads in flight;
+// bf16 (exact codes, a group partial and a row-sum correction beside each
+// accumulator): two workgroups per CU, one stage in flight.
+template <int MINB, int PD, bool BF>
+static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream) {
+  constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KG = 1;
   constexpr bool BD = true;
   const int tiles_n = (int)((p.N + BN - 1) / BN);
   // every group has at most ceil(rows / BM) <= rows / BM + 1 row chunks
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
   if (bound > INT32_MAX / 2) return hipErrorNotSupported;
   const int grid = (int)((bound + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD>), dim3(grid), dim3(WM * WN * kWave * KG), 0,
-                     stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N, (int)p.K, p.group_size,
-                     p.num_active, tiles_n, p.epi);
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD, BF>), dim3(grid),
+                     dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N,
+                     (int)p.K, p.group_size, p.num_active, tiles_n, p.epi);
   return hipGetLastError();
+}
+
+hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
+  return p.bf16 ? launch_w4_grouped_t<2, 1, true>(p, stream) : launch_w4_grouped_t<3, 2, false>(p, stream);
 }
 
 // Dense launch: 128 x 256 tiles, each XCD sweeping groups of eight row panels

@@ -220,23 +220,27 @@ qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg
  * pack_factor = 8 codes per uint32, group_size K elements per scale). Neither page
  * defines the combination; this is the plain joint reading: for g < num_active
  * with e = expert_ids[g] >= 0, rows a_offsets[g] .. a_offsets[g+1]-1 of c are set to
- * round_fp16(A[rows] . W_e) with W_e[k][n] = (q - 8) * scales[e][k / group_size][n],
+ * round(A[rows] . W_e) with W_e[k][n] = (q - 8) * scales[e][k / group_size][n],
  * q = code k % 8 of b_packed[e][k / 8][n] (bits 4(k%8) .. 4(k%8)+3). All other
  * rows of c keep their prior content.
  *
- *   c          f16 [T, N]
- *   a          f16 [T, K]
+ *   c          f16 or bf16 [T, N]
+ *   a          f16 or bf16 [T, K]
  *   a_offsets  u32 [G + 1]   non-decreasing, a_offsets[num_active] <= T
  *   b_packed   u32 [E, K / 8, N]
- *   scales     f16 [E, K / group_size, N]
+ *   scales     f16 or bf16 [E, K / group_size, N]
  *   expert_ids i32 [G]       each < E, or negative to skip
  *   expert_usage_stats_host  HOST u32[2]: [1] = num_active (<= G); [0] a hint only
  *   group_size multiple of 32 and a power of two, at most 256, dividing K
  *   pack_factor must be 8
  *
- * N must be a multiple of 8 (QG_ERR_ALIGN). Accumulation is fp32; results are
- * rounded to fp16 (nearest-even). The device-side tables are not re-validated:
- * offsets past T, or expert ids >= E, are undefined behaviour.
+ * a, scales and c share one type (the W4 page's a_type and c_type; QG_ERR_DTYPE
+ * when they differ). N must be a multiple of 8 (QG_ERR_ALIGN). Accumulation is
+ * fp32; results are rounded to the output type (nearest-even). With fp16 each
+ * weight (q - 8) * scale is rounded to fp16 before the MFMAs; with bf16 the
+ * codes enter the MFMAs exactly and each group's fp32 partial is scaled once.
+ * The device-side tables are not re-validated: offsets past T, or expert ids
+ * >= E, are undefined behaviour.
  */
 qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                           const qg_tensor* b_packed, const qg_tensor* scales, const qg_tensor* expert_ids,
@@ -245,8 +249,9 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
 
 /*
  * grouped_gemm_w4_epilogue - grouped_gemm_w4 with the fixed epilogue of
- * grouped_gemm_epilogue (bias f16 [E, N], residual f16 [T, N_out], c f16
- * [T, N_out]). Everything else as grouped_gemm_w4; epilogue 0 is grouped_gemm_w4.
+ * grouped_gemm_epilogue (bias [E, N], residual [T, N_out], c [T, N_out], all of
+ * the activation type). Everything else as grouped_gemm_w4; epilogue 0 is
+ * grouped_gemm_w4.
  */
 qg_status grouped_gemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                    const qg_tensor* b_packed, const qg_tensor* scales,

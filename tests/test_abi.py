@@ -231,6 +231,9 @@ def test_grouped_w4_rejections(lib):
     b, s = bb.t((E, K // 8, N), QG.U32), bb.t((E, K // 128, N), QG.F16)
     assert gw_call(lib, c, a, off, bb.t((E * K // 8, N), QG.U32), s, ids, [8, 4]) == QG.ERR_RANK
     assert gw_call(lib, c, bb.t((T, K), QG.BF16), off, b, s, ids, [8, 4]) == QG.ERR_DTYPE
+    cb, ab, sb = bb.t((T, N), QG.BF16), bb.t((T, K), QG.BF16), bb.t((E, K // 128, N), QG.BF16)
+    assert gw_call(lib, cb, ab, off, b, s, ids, [8, 4]) == QG.ERR_DTYPE      # bf16 a and c, f16 scales
+    assert gw_call(lib, cb, ab, off, b, sb, ids, [8, 0]) == QG.OK            # all bf16: accepted (no-op)
     assert gw_call(lib, c, a, off, b, bb.t((E, K // 64, N), QG.F16), ids, [8, 4]) == QG.ERR_SHAPE
     assert gw_call(lib, c, a, off, b, bb.t((E + 1, K // 128, N), QG.F16), ids, [8, 4]) == QG.ERR_SHAPE
     assert gw_call(lib, c, a, bb.t((G,), QG.U32), b, s, ids, [8, 4]) == QG.ERR_SHAPE

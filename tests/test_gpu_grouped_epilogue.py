@@ -45,19 +45,21 @@ def exact_products(a, w_of, a_off, ids, usage):
     return y
 
 
-def tolerance(y, flags, bias_rows, ref):
-    """Per-element bound for the written rows (ref decoded, y the exact product)."""
+def tolerance(y, flags, bias_rows, ref, carry_gate=True):
+    """Per-element bound for the written rows (ref decoded, y the exact product);
+    carry_gate=False keeps the common bar for gated outputs too (GEMMs whose
+    weights enter the MFMAs exactly)."""
     if flags & BIAS:
         y = y + bias_rows
     base = REL * (np.abs(ref) + 1.0)
-    if not flags & GATE:
+    if not flags & GATE or not carry_gate:
         return base
     g, u = y[:, 0::2], y[:, 1::2]
     tg, tu = REL * (np.abs(g) + 1.0), REL * (np.abs(u) + 1.0)
     return 1.1 * np.abs(u) * tg + (np.abs(oracle.silu(g)) + 1.1 * tg) * tu + base
 
 
-def compare(got, ref, sent, dec, y, flags, bias_rows_fn, what, rel_rms=None):
+def compare(got, ref, sent, dec, y, flags, bias_rows_fn, what, rel_rms=None, carry_gate=True):
     written = ref[:, 0] != sent
     assert np.array_equal(got[:, 0] != sent, written), f"{what}: row routing differs"
     assert np.all(got[~written] == sent), f"{what}: rows outside the groups changed"
@@ -65,7 +67,7 @@ def compare(got, ref, sent, dec, y, flags, bias_rows_fn, what, rel_rms=None):
         return {}
     g, r = dec(got[written]), dec(ref[written])
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
-    tol = tolerance(y[written], flags, bias_rows_fn(written), r)
+    tol = tolerance(y[written], flags, bias_rows_fn(written), r, carry_gate)
     err = np.abs(g - r)
     bad = err > tol
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the tolerance, first {np.argwhere(bad)[:3].tolist()}"
@@ -146,44 +148,49 @@ def test_bf16_edges_and_full_size(gpu, lib):
 # ---------------------------------------------------------------- W4 experts
 
 def run_w4(lib, d, flags, seed, a_off=None, ids=None, usage=None):
+    """fp16 or bf16 (d.dtype). The bf16 kernel keeps the 4-bit weights exact in its
+    MFMAs, so its gated outputs are held to the common bar."""
     a_off = d.a_offsets if a_off is None else a_off
     ids = d.expert_ids if ids is None else ids
     usage = d.usage if usage is None else usage
     T, K = d.a.shape
     E, _, N = d.b.shape
     n_out = N // 2 if flags & GATE else N
-    bias, res = synth.grouped_epilogue_operands(seed, E, T, n_out, N, "f16")
-    out = Guarded((T, n_out), torch.float16, SENT["f16"])
-    lib.grouped_gemm_w4_epilogue(out.view, dev16(d.a, torch.float16), dev32(a_off), dev32(d.b),
-                                 dev16(d.scales, torch.float16), dev32(np.asarray(ids, np.int32)),
+    bf16 = d.dtype == "bf16"
+    tdt, sent, dec = (torch.bfloat16, SENT["bf16"], nm.decode_bf16) if bf16 else (torch.float16, SENT["f16"], nm.decode_f16)
+    bias, res = synth.grouped_epilogue_operands(seed, E, T, n_out, N, d.dtype)
+    out = Guarded((T, n_out), tdt, sent)
+    lib.grouped_gemm_w4_epilogue(out.view, dev16(d.a, tdt), dev32(a_off), dev32(d.b),
+                                 dev16(d.scales, tdt), dev32(np.asarray(ids, np.int32)),
                                  [int(v) for v in usage], flags,
-                                 bias=dev16(bias, torch.float16) if flags & BIAS else None,
-                                 residual=dev16(res, torch.float16) if flags & RES else None,
+                                 bias=dev16(bias, tdt) if flags & BIAS else None,
+                                 residual=dev16(res, tdt) if flags & RES else None,
                                  group_size=d.group_size)
     got = host16(out.view)
     assert out.bands_intact(), "write outside C"
-    c0 = np.full((T, n_out), SENT["f16"], np.uint16)
+    c0 = np.full((T, n_out), sent, np.uint16)
     ref = oracle.grouped_gemm_w4(c0, d.a, a_off, d.b, d.scales, ids, usage, d.group_size, epilogue=flags,
-                                 bias_bits=bias, residual_bits=res)
-    a = nm.decode_f16(d.a)
+                                 bias_bits=bias, residual_bits=res, dtype=d.dtype)
+    a = dec(d.a)
     cache = {}
 
     def w_of(e):
         if e not in cache:
-            cache[e] = oracle.w4.dequant_w4(d.b[e], d.scales[e], d.group_size)
+            cache[e] = oracle.w4.dequant_w4(d.b[e], d.scales[e], d.group_size, dtype=d.dtype)
         return cache[e]
     y = exact_products(a, w_of, a_off, ids, usage)
     e_of = row_expert(a_off, ids, usage, T)
-    bf = nm.decode_f16(bias)
-    return compare(got, ref, SENT["f16"], nm.decode_f16, y, flags, lambda w: bf[e_of[w]],
-                   f"w4 flags={flags}")
+    bf = dec(bias)
+    return compare(got, ref, sent, dec, y, flags, lambda w: bf[e_of[w]], f"w4 {d.dtype} flags={flags}",
+                   carry_gate=not bf16)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("flags", range(1, 8))
-def test_w4_every_flag_set(gpu, lib, flags):
+def test_w4_every_flag_set(gpu, lib, flags, dtype):
     for (E, T, K, N, seed) in [(8, 200, 256, 64, 1), (5, 77, 128, 48, 2), (16, 600, 512, 208, 3)]:
-        d = synth.grouped_w4_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25)
-        say(f"[grouped-epi] w4 flags={flags} E={E} T={T} K={K} N={N}")
+        d = synth.grouped_w4_inputs(seed=seed, E=E, T=T, K=K, N=N, skip_frac=0.25, dtype=dtype)
+        say(f"[grouped-epi] w4 {dtype} flags={flags} E={E} T={T} K={K} N={N}")
         run_w4(lib, d, flags, seed + 10 * flags)
 
 
@@ -195,9 +202,10 @@ def test_w4_ragged(gpu, lib, seed):
     run_w4(lib, d, BIAS | GATE | RES, seed)
 
 
-def test_w4_full_size(gpu, lib):
-    d = synth.grouped_w4_inputs()
-    say("[grouped-epi] w4 full size, gated")
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_w4_full_size(gpu, lib, dtype):
+    d = synth.grouped_w4_inputs(dtype=dtype)
+    say(f"[grouped-epi] w4 {dtype} full size, gated")
     say("  diagnostics", run_w4(lib, d, 7, 4))
     say("  diagnostics", run_w4(lib, d, BIAS | RES, 5))
 
