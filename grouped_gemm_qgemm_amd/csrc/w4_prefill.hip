@@ -63,9 +63,14 @@ struct W4TileLds {
 //     written into the same [8][BN] LDS tile word by word, so the MFMA loop is
 //     unchanged; the lane's two scales are two 2-byte loads.
 //   * BD: B does not pass through LDS. Each lane loads the packed words its
-//     MFMAs take (8 bytes per 16-deep step, 256 contiguous bytes per
-//     half-wave) with the stage; this pays when a wave's B columns are its own
-//     (WAVES_M == 1, as in the grouped tiles).
+//     MFMAs take with the stage; this pays when a wave's B columns are its own
+//     (WAVES_M == 1). [K/8, N]: 8 bytes (two columns) per packed row, 256
+//     contiguous bytes per half-wave. [N, K/8]: one 16-byte load per column
+//     (the lane's four words of the stage). On the fp16 path lane half h then
+//     takes K rows 32h + 8j .. + 7 at 16-deep step j (A fragments read to
+//     match), so a lane's words of a column are contiguous; the bf16 path keeps
+//     rows 16j + 8h .. + 7, which keeps every step inside one quantization
+//     group for the group partials.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false,
           bool BD = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
@@ -78,7 +83,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   static_assert(TN == 64 && TM % 32 == 0, "wave tile");
   static_assert(PD >= 1 && PD <= 4, "prefetch distance");
   static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
-  static_assert(!BD || (KG == 1 && !NK), "direct B: one K group, [K/8, N] layout");
+  static_assert(!BD || (KG == 1 && !(NK && BF)), "direct B: one K group");
   static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
   constexpr int NBD = BD ? BK / 16 : 1;      // direct B words per lane and stage
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
@@ -145,8 +150,16 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   }
   // this lane's two output columns (scale columns)
   const uint32_t s_voff = (uint32_t)min(n0 + wn * TN + 2 * c32, N - 2) * 2;
-  // direct B: packed row h of each 16-deep step, the same two columns (from n0)
-  const uint32_t bd_voff = (uint32_t)(h * N + min(wn * TN + 2 * c32, N - n0 - 2)) * 4;
+  // direct B: packed rows of the stage, the same two columns (from n0). The fp16
+  // path takes rows 4h .. 4h + 3 in the lane half h (K rows 32h + 8j .. + 7 at
+  // step j); the bf16 path, whose group partials need each step inside one
+  // quantization group, takes row 2j + h at step j.
+  constexpr bool KH = BD && !BF;   // the lane half's K rows are contiguous in the stage
+  const uint32_t bd_voff = (uint32_t)((KH ? 4 * h : h) * N + min(wn * TN + 2 * c32, N - n0 - 2)) * 4;
+  // direct B, [N, K/8]: words 4h .. 4h + 3 of the stage of the lane's two columns
+  const int bdn_col = min(wn * TN + 2 * c32, N - n0 - 2);
+  const uint32_t bdn_voff0 = (uint32_t)(bdn_col * (K / 8) + 4 * h) * 4;
+  const uint32_t bdn_voff1 = (uint32_t)((bdn_col + 1) * (K / 8) + 4 * h) * 4;
 
   // one stage of prefetched operands: A chunks, packed B chunks, the lane's scale pairs
   struct Regs {
@@ -173,9 +186,17 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) r.a[i] = buffer_load16(a_src, a_voff[i], (uint32_t)k0 * 2);
     const __amdgpu_buffer_rsrc_t b_src = NK ? bnk_src : b_stage(k0);
-    if constexpr (BD) {
+    if constexpr (BD && NK) {
+      // one 16-byte load per column: the lane's four words of the stage
+      const u32x4_t w0 = buffer_load16(b_src, bdn_voff0, (uint32_t)(k0 / 8) * 4);
+      const u32x4_t w1 = buffer_load16(b_src, bdn_voff1, (uint32_t)(k0 / 8) * 4);
+      r.bd[0] = (uint64_t)w0.x | ((uint64_t)w1.x << 32);
+      r.bd[1] = (uint64_t)w0.y | ((uint64_t)w1.y << 32);
+      r.bd[2] = (uint64_t)w0.z | ((uint64_t)w1.z << 32);
+      r.bd[3] = (uint64_t)w0.w | ((uint64_t)w1.w << 32);
+    } else if constexpr (BD) {
 #pragma unroll
-      for (int j = 0; j < NBD; ++j) r.bd[j] = buffer_load8(b_src, bd_voff, (uint32_t)(2 * j) * N * 4);
+      for (int j = 0; j < NBD; ++j) r.bd[j] = buffer_load8(b_src, bd_voff, (uint32_t)(KH ? j : 2 * j) * N * 4);
     } else {
 #pragma unroll
       for (int i = 0; i < B_PER_T; ++i) r.b[i] = buffer_load16(b_src, b_voff[i], NK ? (uint32_t)(k0 / 8) * 4 : 0u);
@@ -259,14 +280,14 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = wm * TM + mt * 32 + c32;
-        afr[j][mt] = lds_a[buf][row * CHUNKS + swz(row, 2 * j + h)];
+        afr[j][mt] = lds_a[buf][row * CHUNKS + swz(row, KH ? 4 * h + j : 2 * j + h)];
       }
     }
     if constexpr (BF && MT <= 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       const uint64_t w2 = bwr[j];
-      const uint32_t sp = cur.sc[j >> 1];
+      const uint32_t sp = KH ? (h ? cur.sc[1] : cur.sc[0]) : cur.sc[j >> 1];
       u32x4_t bq[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -609,9 +630,9 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
 // each accumulator, which leaves no registers for a second workgroup.
 template <int WM, int MINB, int KG, bool BF, bool NK>
 static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
-  // one K group of waves with a column strip each (fp16, [K/8, N]): B words go
-  // straight into the lanes' registers, two stages ahead
-  constexpr bool BD = (KG == 1 && !NK && !BF && WM == 1);
+  // one K group of waves with a column strip each (fp16): B words go straight
+  // into the lanes' registers, two stages ahead
+  constexpr bool BD = (KG == 1 && !BF && WM == 1);
   constexpr int BM = 128, BN = 256, WN = 4, PD = BD ? 2 : 1;
   const int grid = ((tm * tn + 7) / 8) * 8;
   hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK, BD>), dim3(grid),
