@@ -73,21 +73,22 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9239429, "ec78a7e77d980bda"),
-    "prefill": (276791696, "4f7241325a7d6b62"),
-    "square": (101391104, "4f7241325a7d6b62"),
+    "decode": (9243183, "27db1fe4c6bd946a"),
+    "prefill": (277266343, "8fc3b1e6f5f196ec"),
+    "square": (101393920, "8fc3b1e6f5f196ec"),
     "grouped": (367971168, "7a9d825f74180d39"),
     "grouped_kn": (365907538, "7a9d825f74180d39"),
-    "grouped_w4": (114656386, "4f7241325a7d6b62"),
+    "grouped_w4": (114583689, "8fc3b1e6f5f196ec"),
     "kproj": (85592817, "7b5abd03aad04665"),
-    "decode_gate": (9258198, "ec78a7e77d980bda"),
-    "prefill_gate": (276948233, "4f7241325a7d6b62"),
-    "decode_bf16": (9238405, "ec78a7e77d980bda"),
-    "prefill_bf16": (302809964, "4f7241325a7d6b62"),
-    "decode_nk": (9233840, "ec78a7e77d980bda"),
-    "prefill_nk": (232418124, "4f7241325a7d6b62"),
+    "decode_gate": (9260246, "27db1fe4c6bd946a"),
+    "prefill_gate": (277581777, "8fc3b1e6f5f196ec"),
+    "decode_bf16": (9235675, "27db1fe4c6bd946a"),
+    "prefill_bf16": (302816299, "8fc3b1e6f5f196ec"),
+    "decode_nk": (9239024, "27db1fe4c6bd946a"),
+    "prefill_nk": (279726805, "8fc3b1e6f5f196ec"),
     "kvproj": (202287161, "7b5abd03aad04665"),
     "kvproj_e4m3": (193909293, "7b5abd03aad04665"),
+    "grouped_w4_bf16": (113713621, "8fc3b1e6f5f196ec"),
     "kproj_e4m3h": (64374327, "7b5abd03aad04665"),
 }
 
