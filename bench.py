@@ -79,17 +79,17 @@ MEASURED_TRAFFIC = {
     "grouped": (367971168, "7a9d825f74180d39"),
     "grouped_kn": (365907538, "7a9d825f74180d39"),
     "grouped_w4": (114583689, "8fc3b1e6f5f196ec"),
-    "kproj": (85592817, "7b5abd03aad04665"),
+    "kproj": (85680745, "cb51f5b26f601731"),
     "decode_gate": (9260246, "27db1fe4c6bd946a"),
     "prefill_gate": (277581777, "8fc3b1e6f5f196ec"),
     "decode_bf16": (9235675, "27db1fe4c6bd946a"),
     "prefill_bf16": (302816299, "8fc3b1e6f5f196ec"),
     "decode_nk": (9239024, "27db1fe4c6bd946a"),
     "prefill_nk": (279726805, "8fc3b1e6f5f196ec"),
-    "kvproj": (202287161, "7b5abd03aad04665"),
-    "kvproj_e4m3": (193909293, "7b5abd03aad04665"),
+    "kvproj": (202263739, "cb51f5b26f601731"),
+    "kvproj_e4m3": (193906221, "cb51f5b26f601731"),
     "grouped_w4_bf16": (113713621, "8fc3b1e6f5f196ec"),
-    "kproj_e4m3h": (64374327, "7b5abd03aad04665"),
+    "kproj_e4m3h": (64450544, "cb51f5b26f601731"),
 }
 
 
@@ -521,7 +521,7 @@ class GroupedW4BF16(GroupedW4):
 class KProjFP8:
     """8 sequences (lengths U[1,1024], seed 5: T=4312), hidden 4096 bf16, W [4096,1024] e4m3 with 1x128x128
     block scales, bf16 keys written into a paged cache (page 128, 2 layers, layer 1)."""
-    kernel = "kproj_fp8_v3_kernel"
+    kernel = "kproj_bf16_dma_kernel"
     bound = "mfma"
     dtype = "bf16"
     planes = 1          # 2: keys and values ([W_k | W_v]) in one call
@@ -603,7 +603,7 @@ class KProjFP8:
 
 class KProjE4M3Hidden(KProjFP8):
     """The K-projection workload with e4m3 hidden rows: both MFMA operands are e4m3."""
-    kernel = "kproj_f8f8_kernel"
+    kernel = "kproj_f8f8_dma_kernel"
     dtype = "e4m3"
     hidden = "fp8"
     mfma_peak = FP8_MFMA_PEAK_TFLOPS

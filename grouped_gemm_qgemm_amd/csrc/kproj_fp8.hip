@@ -18,8 +18,10 @@
 //   * The fp8 weight tile [128 k][128 n] is fetched with coalesced 16-byte row
 //     loads, copied into LDS as it is, and MFMA B fragments are read with
 //     8-bit transpose reads.
-//   * Hidden rows are staged through LDS with an XOR swizzle; double-buffered
-//     stages, one barrier per stage.
+//   * Hidden rows are staged through LDS with an XOR swizzle, one barrier per
+//     stage: on 144-row tiles straight from global memory into three LDS
+//     stage buffers (global_load_lds), on smaller tiles through registers into
+//     two.
 //   * Column tile t of a wave holds 16 consecutive columns (the transpose
 //     read's order); fp32 accumulation.
 //   * Epilogue: token t -> sequence b (binary search of the row offsets) ->
@@ -41,6 +43,9 @@ constexpr int KSW = 32;       // input-scale blocks held in LDS at a time
 
 // hidden rows: chunk c of row r lives at chunk c ^ (r & 15)
 __device__ __forceinline__ int swz_a(int r, int c) { return c ^ (r & 15); }
+// 128-byte rows (the fp8 tiles of the direct-to-LDS kernels): chunk c of row r lives at
+// chunk c ^ (r & 7) ^ (bit 3 of r), so rows r and r + 8, which share LDS banks, differ too
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
 }  // namespace
 
@@ -485,23 +490,413 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
                                  max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales, qgran);
 }
 
+
+// global_load_lds, written out so that the compiler neither waits on these
+// loads before unrelated LDS reads nor keeps per-lane 64-bit addresses: the
+// wave's 64 lanes each fetch 16 (or 4) bytes at sbase + voff and the data
+// lands at LDS byte lds + 16 * lane (4 * lane). Completion is tracked by the
+// caller with explicit vmcnt waits, so the kernels that use these issue no
+// other vector-memory loads in their main loops. M0 is listed as clobbered
+// and the compiler warns that it does not preserve reserved registers around
+// inline asm; in these kernels nothing but these loads reads M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// the same with 4 bytes per lane, for the lanes where `on` holds
+__device__ __forceinline__ void dma4_lanes(const void* sbase, uint32_t voff, uint32_t lds, bool on) {
+  if (on)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Direct-to-LDS design for 144-row tiles (bf16 hidden rows).
+//   * Staging: every 16-byte chunk of the hidden and weight tiles, and the
+//     tile rows' input scales, go from global memory straight into LDS with
+//     global_load_lds (a wave's instruction fills 1 KiB of LDS, lane l at
+//     byte 16 l, so each lane fetches the chunk that the swizzled layout puts
+//     there). No registers hold staged data, so three stage buffers keep two
+//     stages of loads in flight behind the one being multiplied.
+//   * Twelve waves on 48 x 32 tiles, fragments and conversions as in
+//     kproj_bf16_kernel.
+//   * A stage's partials are scaled by is[t][kb] * ws[kb][nb] and added to the
+//     accumulators during the next stage, among its MFMAs, so no wave waits
+//     for its last MFMAs before the stage barrier.
+template <bool Q8>
+__global__ __launch_bounds__(768) void kproj_bf16_dma_kernel(
+    const uint16_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
+    float* __restrict__ kv_scales, int qgran) {
+  constexpr int BM = 144, MT = 3, NBUF = 3;
+  constexpr int ACH = BM * KCH;   // 16-byte hidden chunks per stage: 36 wave loads of 1 KiB
+  constexpr int BCH = 128 * 8;    // 16-byte weight chunks per stage: 16 wave loads
+  __shared__ __attribute__((aligned(1024))) u32x4_t lds_a[NBUF][ACH];
+  __shared__ __attribute__((aligned(1024))) u32x4_t lds_b[NBUF][BCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[NBUF][BM];
+  __shared__ long long row_dst[BM];
+  static_assert(sizeof(lds_b) >= 4 * BM * sizeof(float), "room for the epilogue's scratch");
+  static_assert(ACH == 36 * 64 && BCH == 16 * 64, "wave loads per stage");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  // wave loads: hidden 1 KiB blocks wave, wave + 12, wave + 24 (rows 4a .. 4a + 3 each);
+  // weight blocks wave and, for waves 0-3, wave + 12 (K rows 8b .. 8b + 7 each);
+  // waves 4-6: the input scales of rows 64 (wave - 4) + lane
+  const uint8_t* hb = reinterpret_cast<const uint8_t*>(H + (size_t)m0 * Kh);
+  uint32_t aoff[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int row = 4 * (wave + 12 * j) + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    aoff[j] = (uint32_t)(min(m0 + row, T - 1) - m0) * (uint32_t)(Kh * 2) + ch * 16;
+  }
+  uint32_t boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kr = 8 * (wave + 12 * j) + (lane >> 3);
+    boff[j] = (uint32_t)kr * (uint32_t)N + swz8(kr, lane & 7) * 16;
+  }
+  const int is_row = 64 * (wave - 4) + lane;
+  const bool is_loader = wave >= 4 && wave < 7;
+  const uint32_t is_off = (uint32_t)min(m0 + (is_loader ? is_row : 0), T - 1) * (uint32_t)KB * 4u;
+  // LDS byte address of a __shared__ location (the global_load_lds destination base, in M0)
+  auto lds_addr = [](const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  };
+  auto issue = [&](int kb, int buf) {
+    const uint8_t* ha = hb + (size_t)kb * (KBK * 2);
+    const uint8_t* wk = W + (size_t)kb * KBK * N + n0;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma16(ha, aoff[j], lds_addr(&lds_a[buf][(wave + 12 * j) * 64]));
+    dma16(wk, boff[0], lds_addr(&lds_b[buf][wave * 64]));
+    if (wave < 4) dma16(wk, boff[1], lds_addr(&lds_b[buf][(wave + 12) * 64]));
+    if (is_loader) dma4_lanes(in_scale + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 4)]), is_row < BM);
+  };
+  // wait until at most the last stage's loads of this wave are in flight
+  auto wait_all_but_one_stage = [&]() {
+    if (wave < 7) __builtin_amdgcn_s_waitcnt(0xF75);   // vmcnt(5): waves 0-6 issue five loads per stage
+    else __builtin_amdgcn_s_waitcnt(0xF74);            // vmcnt(4)
+  };
+
+  float4_t acc[MT][2], pp[MT][2];   // accumulators; the previous stage's partials
+  float pf[MT][4];                   // and their factors is * ws
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    acc[i][0] = acc[i][1] = pp[i][0] = pp[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pf[i][j] = 0.f;
+  }
+  auto fold_prev = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[mt][0][i] += pf[mt][i] * pp[mt][0][i];
+        acc[mt][1][i] += pf[mt][i] * pp[mt][1][i];
+      }
+    // keep the additions here: left to itself the compiler sinks them to the
+    // end of the unrolled loop and keeps every stage's partials alive
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(acc[mt][0]), "+v"(acc[mt][1]));
+  };
+
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  auto compute = [&](int kb, int buf) {
+    float4_t part[MT][2];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) part[i][0] = part[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t bf[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int c = wn * 2 + t;   // the column chunk of column tile t
+        const int kr = 32 * s + 8 * q + (r16 >> 1);
+        const unsigned char* base =
+            reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + swz8(kr, c)]) + 8 * (r16 & 1);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(__attribute__((address_space(3))) const unsigned char*)base);
+        bf[t] = u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true))};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = wm * 48 + mt * 16 + r16;
+        const u32x4_t av = lds_a[buf][row * KCH + swz_a(row, s * 4 + q)];
+        part[mt][0] = mfma16x16x32_bf16(av, bf[0], part[mt][0]);
+        part[mt][1] = mfma16x16x32_bf16(av, bf[1], part[mt][1]);
+      }
+      if (s == 1) fold_prev();   // the previous stage's partials, while these MFMAs run
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[buf][wm * 48 + mt * 16 + q * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pf[mt][i] = is4[i] * wsv;
+      pp[mt][0] = part[mt][0];
+      pp[mt][1] = part[mt][1];
+    }
+  };
+
+  issue(0, 0);
+  if (KB > 1) {
+    issue(1, 1);
+    wait_all_but_one_stage();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0xF70);
+  }
+  __syncthreads();
+  // one stage: loads for stage i + 2 (into the buffer that stage i - 1 left at the
+  // last barrier), the MFMAs of stage i, then wait until stage i + 1 has landed
+  auto stage = [&](int i, int buf) {
+    if (i + 2 < KB) issue(i + 2, (buf + 2) % NBUF);
+    compute(i, buf);
+    if (i + 2 < KB) wait_all_but_one_stage();
+    else __builtin_amdgcn_s_waitcnt(0xF70);
+    __syncthreads();
+  };
+  int kb0 = 0;
+  for (; kb0 + 2 * NBUF <= KB; kb0 += 2 * NBUF) {   // two rounds of the buffers: the partials alternate too
+#pragma unroll
+    for (int u = 0; u < 2 * NBUF; ++u) stage(kb0 + u, u % NBUF);
+  }
+  for (; kb0 < KB; ++kb0) stage(kb0, kb0 % NBUF);
+  fold_prev();
+
+  kproj_store_tile<BM, Q8>(acc, row_dst, reinterpret_cast<float*>(&lds_b[0][0]), tid, m0, n0, T, offs, cache_len,
+                           page_table, batch, max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales,
+                           qgran);
+}
+
+// Direct-to-LDS design of the e4m3-hidden kernel for 144-row tiles: staging as
+// in kproj_bf16_dma_kernel (hidden, weight and input-scale chunks straight into
+// NBUF LDS stage buffers, NBUF - 1 stages of loads in flight), fragments and
+// MFMAs as in kproj_f8f8_kernel, and each stage's six MFMA results scaled and
+// added during the next stage.
+template <bool Q8, int NBUF>
+__global__ __launch_bounds__(768) void kproj_f8f8_dma_kernel(
+    const uint8_t* __restrict__ H, const uint32_t* __restrict__ offs, const uint8_t* __restrict__ W,
+    const float* __restrict__ in_scale, const float* __restrict__ w_scale, void* __restrict__ blocks_v,
+    const uint32_t* __restrict__ cache_len, const uint32_t* __restrict__ page_table, int T, int Kh, int N,
+    int batch, int max_pages, int num_pages, int page_size, int layer, int tiles_m, int tiles_n, int n_plane,
+    float* __restrict__ kv_scales, int qgran) {
+  constexpr int BM = 144, MT = 3;
+  constexpr int ACH = BM * 8;     // 16-byte hidden chunks per stage: 18 wave loads of 1 KiB
+  constexpr int BCH = 128 * 8;    // 16-byte weight chunks per stage: 16 wave loads
+  __shared__ __attribute__((aligned(1024))) u32x4_t lds_a[NBUF][ACH];
+  __shared__ __attribute__((aligned(1024))) u32x4_t lds_b[NBUF][BCH];
+  __shared__ __attribute__((aligned(16))) float lds_is[NBUF][BM];
+  __shared__ long long row_dst[BM];
+  static_assert(sizeof(lds_b) >= 4 * BM * sizeof(float), "room for the epilogue's scratch");
+  static_assert(ACH == 18 * 64 && BCH == 16 * 64, "wave loads per stage");
+  static_assert(NBUF == 3 || NBUF == 4, "stage buffers");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int m0 = (lin / tiles_n) * BM;   // N-fastest: the column tiles of a row block share an XCD
+  const int nb = lin % tiles_n;
+  const int n0 = nb * KBN;
+  const int KB = Kh / KBK;
+
+  // wave loads: hidden 1 KiB blocks wave and, for waves 0-5, wave + 12 (rows 8a .. 8a + 7 each);
+  // weight blocks wave and, for waves 0-3, wave + 12 (K rows 8b .. 8b + 7 each);
+  // waves 6-8: the input scales of rows 64 (wave - 6) + lane
+  const uint8_t* hb = H + (size_t)m0 * Kh;
+  uint32_t aoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * (wave + 12 * j) + (lane >> 3);
+    const int ch = swz8(row, lane & 7);
+    aoff[j] = (uint32_t)(min(m0 + row, T - 1) - m0) * (uint32_t)Kh + ch * 16;
+  }
+  uint32_t boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int kr = 8 * (wave + 12 * j) + (lane >> 3);
+    boff[j] = (uint32_t)kr * (uint32_t)N + swz8(kr, lane & 7) * 16;
+  }
+  const int is_row = 64 * (wave - 6) + lane;
+  const bool is_loader = wave >= 6 && wave < 9;
+  const uint32_t is_off = (uint32_t)min(m0 + (is_loader ? is_row : 0), T - 1) * (uint32_t)KB * 4u;
+  const int nw = 2 + (wave < 6) + (wave < 4) + is_loader;   // loads per stage of this wave: 2 .. 4
+  auto lds_addr = [](const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  };
+  auto issue = [&](int kb, int buf) {
+    const uint8_t* ha = hb + (size_t)kb * KBK;
+    const uint8_t* wk = W + (size_t)kb * KBK * N + n0;
+    dma16(ha, aoff[0], lds_addr(&lds_a[buf][wave * 64]));
+    if (wave < 6) dma16(ha, aoff[1], lds_addr(&lds_a[buf][(wave + 12) * 64]));
+    dma16(wk, boff[0], lds_addr(&lds_b[buf][wave * 64]));
+    if (wave < 4) dma16(wk, boff[1], lds_addr(&lds_b[buf][(wave + 12) * 64]));
+    if (is_loader) dma4_lanes(in_scale + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 6)]), is_row < BM);
+  };
+  // wait until at most `n` of this wave's loads are in flight (n: 0 .. 8, uniform)
+  auto wait_loads = [](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0xF71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0xF72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+      default: __builtin_amdgcn_s_waitcnt(0xF78); break;
+    }
+  };
+
+  float4_t acc[MT][2], pp[MT][2];   // accumulators; the previous stage's MFMA results
+  float pf[MT][4];                   // and their factors is * ws
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    acc[i][0] = acc[i][1] = pp[i][0] = pp[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pf[i][j] = 0.f;
+  }
+  auto fold_prev = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[mt][0][i] += pf[mt][i] * pp[mt][0][i];
+        acc[mt][1][i] += pf[mt][i] * pp[mt][1][i];
+      }
+    // keep the additions here (see kproj_bf16_dma_kernel)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(acc[mt][0]), "+v"(acc[mt][1]));
+  };
+
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  auto compute = [&](int kb, int buf) {
+    i32x8_t bf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int c = wn * 2 + t;   // the column chunk of column tile t
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kr = 32 * q + 8 * s4 + (r16 >> 1);
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + swz8(kr, c)]) +
+                                    8 * (r16 & 1);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(__attribute__((address_space(3))) const unsigned char*)base);
+        bf[t][2 * s4] = v.x;
+        bf[t][2 * s4 + 1] = v.y;
+      }
+    }
+    float4_t part[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = wm * 48 + mt * 16 + r16;
+      const u32x4_t lo = lds_a[buf][row * 8 + swz8(row, 2 * q)];
+      const u32x4_t hi = lds_a[buf][row * 8 + swz8(row, 2 * q + 1)];
+      const i32x8_t av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        part[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            av, bf[t], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);   // e4m3 x e4m3, unit scales
+      if (mt == 0) fold_prev();   // the previous stage's results, while these MFMAs run
+    }
+    const float wsv = w_scale[(size_t)kb * (N / KBN) + nb];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float4_t is4 = *reinterpret_cast<const float4_t*>(&lds_is[buf][wm * 48 + mt * 16 + q * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pf[mt][i] = is4[i] * wsv;
+      pp[mt][0] = part[mt][0];
+      pp[mt][1] = part[mt][1];
+    }
+  };
+
+  // prologue: stages 0 .. NBUF - 2 in flight, stage 0 landed
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < KB) issue(p, p);
+  wait_loads(nw * (min(NBUF - 1, KB) - 1));
+  __syncthreads();
+  // one stage: loads for stage i + NBUF - 1 (into the buffer that stage i - 1 left
+  // at the last barrier), the MFMAs of stage i, then wait until stage i + 1 has landed
+  auto stage = [&](int i, int buf) {
+    const bool more = i + NBUF - 1 < KB;
+    if (more) issue(i + NBUF - 1, (buf + NBUF - 1) % NBUF);
+    compute(i, buf);
+    wait_loads(nw * max(0, min(NBUF - 2, KB - 2 - i)));   // stages i + 2 .. may stay in flight
+    __syncthreads();
+  };
+  constexpr int UNR = NBUF % 2 ? 2 * NBUF : NBUF;   // whole rounds of the buffers and of the alternating partials
+  int kb0 = 0;
+  for (; kb0 + UNR <= KB; kb0 += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) stage(kb0 + u, u % NBUF);
+  }
+  for (; kb0 < KB; ++kb0) stage(kb0, kb0 % NBUF);
+  fold_prev();
+
+  kproj_store_tile<BM, Q8>(acc, row_dst, reinterpret_cast<float*>(&lds_b[0][0]), tid, m0, n0, T, offs, cache_len,
+                           page_table, batch, max_pages, num_pages, page_size, layer, n_plane, blocks_v, kv_scales,
+                           qgran);
+}
+
 template <int WM, int PD>
 static hipError_t launch_kproj_bf16(const KProjArgs& p, hipStream_t stream) {
   constexpr int BM = 48 * WM;
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
-  if (p.fp8)
-    hipLaunchKernelGGL((kproj_bf16_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
-                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
-                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
-                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
-                       p.kv_scales, p.qgran);
-  else
-    hipLaunchKernelGGL((kproj_bf16_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
-                       p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
-                       p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
-                       (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
-                       nullptr, 0);
+  // 144-row tiles: the direct-to-LDS design; 48 and 96 rows: staging through registers
+  if constexpr (WM == 3) {
+    if (p.fp8)
+      hipLaunchKernelGGL((kproj_bf16_dma_kernel<true>), dim3(grid), dim3(768), 0, stream, p.hidden, p.row_offsets,
+                         p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                         (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                         (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, p.kv_scales, p.qgran);
+    else
+      hipLaunchKernelGGL((kproj_bf16_dma_kernel<false>), dim3(grid), dim3(768), 0, stream, p.hidden, p.row_offsets,
+                         p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                         (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                         (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
+  } else {
+    if (p.fp8)
+      hipLaunchKernelGGL((kproj_bf16_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                         p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                         p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                         (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                         p.kv_scales, p.qgran);
+    else
+      hipLaunchKernelGGL((kproj_bf16_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, p.hidden,
+                         p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                         p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                         (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                         nullptr, 0);
+  }
   return hipGetLastError();
 }
 
@@ -511,16 +906,33 @@ static hipError_t launch_kproj_f8f8(const KProjArgs& p, hipStream_t stream) {
   const int tiles_m = (int)((p.T + BM - 1) / BM), tiles_n = (int)(p.N / KBN);
   const int grid = ((tiles_m * tiles_n + 7) / 8) * 8;
   const uint8_t* h = static_cast<const uint8_t*>(static_cast<const void*>(p.hidden));
-  if (p.fp8)
-    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
-                       p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
-                       (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
-                       (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, p.kv_scales, p.qgran);
-  else
-    hipLaunchKernelGGL((kproj_f8f8_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, h, p.row_offsets,
-                       p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
-                       (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
-                       (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
+  // 144-row tiles: the direct-to-LDS design; 48 and 96 rows: staging through registers
+  if constexpr (WM == 3) {
+    constexpr int NB = 3;   // a fourth buffer measured slower
+    if (p.fp8)
+      hipLaunchKernelGGL((kproj_f8f8_dma_kernel<true, NB>), dim3(grid), dim3(768), 0, stream, h, p.row_offsets,
+                         p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                         (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                         (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, p.kv_scales, p.qgran);
+    else
+      hipLaunchKernelGGL((kproj_f8f8_dma_kernel<false, NB>), dim3(grid), dim3(768), 0, stream, h, p.row_offsets,
+                         p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths, p.page_table, (int)p.T,
+                         (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages, (int)p.num_pages, (int)p.page_size,
+                         (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane, nullptr, 0);
+  } else {
+    if (p.fp8)
+      hipLaunchKernelGGL((kproj_f8f8_kernel<WM, true, PD>), dim3(grid), dim3(WM * 256), 0, stream, h,
+                         p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                         p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                         (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                         p.kv_scales, p.qgran);
+    else
+      hipLaunchKernelGGL((kproj_f8f8_kernel<WM, false, PD>), dim3(grid), dim3(WM * 256), 0, stream, h,
+                         p.row_offsets, p.weight, p.input_scale, p.weight_scale, p.blocks, p.cache_lengths,
+                         p.page_table, (int)p.T, (int)p.Kh, (int)p.N, (int)p.batch, (int)p.max_pages,
+                         (int)p.num_pages, (int)p.page_size, (int)p.layer_idx, tiles_m, tiles_n, (int)p.n_plane,
+                         nullptr, 0);
+  }
   return hipGetLastError();
 }
 
