@@ -162,6 +162,53 @@ __device__ __forceinline__ u32x4_t dequant_w4_word_fused(uint32_t w, uint32_t m,
   return r;
 }
 
+// One 32-bit word of eight 4-bit codes -> eight fp16 weights (q - 8), exact, as
+// four packed half pairs in natural K order (0,1), (2,3), (4,5), (6,7): byte i of
+// the word (codes 2i, 2i + 1) and byte i of the word shifted right by 4 (code
+// 2i + 1 in its low nibble) are placed in the two halves by one byte permute,
+// then masked into the mantissa of 1024.0 as in dequant_w4_word_fused. Two more
+// instructions per word than that K-slot order, so activations can enter LDS as
+// they are in memory. `m` must hold 0x000F000F (in a VGPR), `bias` 0x64006400
+// (fp16) or 0x43004300 (bf16: 128 + q, no subtraction).
+template <bool SUB1032>
+__device__ __forceinline__ u32x4_t unpack_w4_word_natural(uint32_t w, uint32_t m, uint32_t bias) {
+  const uint32_t x = w >> 4;
+  const uint32_t p0 = and_or(__builtin_amdgcn_perm(x, w, 0x0C040C00u), m, bias);
+  const uint32_t p1 = and_or(__builtin_amdgcn_perm(x, w, 0x0C050C01u), m, bias);
+  const uint32_t p2 = and_or(__builtin_amdgcn_perm(x, w, 0x0C060C02u), m, bias);
+  const uint32_t p3 = and_or(__builtin_amdgcn_perm(x, w, 0x0C070C03u), m, bias);
+  if constexpr (!SUB1032) return u32x4_t{p0, p1, p2, p3};
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p0) - off);
+  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p1) - off);
+  r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p2) - off);
+  r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p3) - off);
+  return r;
+}
+
+// global_load_lds, written out so that the compiler neither waits on these
+// loads before unrelated LDS reads nor keeps per-lane 64-bit addresses: the
+// wave's 64 lanes each fetch 16 (or 4) bytes at sbase + voff and the data
+// lands at LDS byte lds + 16 * lane (4 * lane). Completion is tracked by the
+// caller with explicit vmcnt waits, so the kernels that use these issue no
+// other vector-memory loads in their main loops. M0 is listed as clobbered
+// and the compiler warns that it does not preserve reserved registers around
+// inline asm; in these kernels nothing but these loads reads M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// the same with 4 bytes per lane, for the lanes where `on` holds
+__device__ __forceinline__ void dma4_lanes(const void* sbase, uint32_t voff, uint32_t lds, bool on) {
+  if (on)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Eight consecutive fp16 values (a0..a7 in four registers) reordered to the
 // K-slot order used by dequant_w4_word_fused: (a0,a4), (a1,a5), (a2,a6), (a3,a7).
 __device__ __forceinline__ u32x4_t permute_k_0415(u32x4_t v) {

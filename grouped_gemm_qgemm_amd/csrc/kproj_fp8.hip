@@ -491,27 +491,6 @@ __global__ __launch_bounds__(WM * 256) void kproj_bf16_kernel(
 }
 
 
-// global_load_lds, written out so that the compiler neither waits on these
-// loads before unrelated LDS reads nor keeps per-lane 64-bit addresses: the
-// wave's 64 lanes each fetch 16 (or 4) bytes at sbase + voff and the data
-// lands at LDS byte lds + 16 * lane (4 * lane). Completion is tracked by the
-// caller with explicit vmcnt waits, so the kernels that use these issue no
-// other vector-memory loads in their main loops. M0 is listed as clobbered
-// and the compiler warns that it does not preserve reserved registers around
-// inline asm; in these kernels nothing but these loads reads M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-// the same with 4 bytes per lane, for the lanes where `on` holds
-__device__ __forceinline__ void dma4_lanes(const void* sbase, uint32_t voff, uint32_t lds, bool on) {
-  if (on)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Direct-to-LDS design for 144-row tiles (bf16 hidden rows).
 //   * Staging: every 16-byte chunk of the hidden and weight tiles, and the

@@ -9,7 +9,10 @@
 // advanced BK = 64 at a time, A and the packed B words of the next stage
 // fetched with raw buffer loads into registers while the current stage is
 // multiplied out of LDS, 32x32x16 MFMAs with fp32 accumulation, and the
-// 4-bit codes unpacked in VGPRs. Its comment below gives the details.
+// 4-bit codes unpacked in VGPRs. Its comment below gives the details. For fp16
+// with [K/8, N] weights and K a multiple of 64, the dense kernel uses a
+// direct-to-LDS form of the tile (w4_tile_dma): every operand of a stage goes
+// from global memory straight into LDS, three stages deep.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,6 +35,73 @@ struct W4TileLds {
   u32x4_t b[KG][2][BD ? 1 : (BK / 8) * BN / 4];
 };
 
+// Store of a wave's TM x 64 tile (rows r0 .., columns c0 + 2 c32, + 1 per lane
+// half h) from the 32x32 MFMA accumulators, with the fixed epilogue: two
+// adjacent columns per 4-byte store (or one gated output).
+template <int MT, bool BF>
+__device__ __forceinline__ void w4_tile_store(const float16_t (&acc)[MT][2], uint16_t* __restrict__ C, int M, int N,
+                                              int r0, int c0, int h, int c32, const Epilogue& ep) {
+  const int col = c0 + 2 * c32;
+  if (col >= N) return;
+  if (ep.flags == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = r0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (row < M)
+          *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
+              BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
+                 : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
+      }
+    }
+    return;
+  }
+  // Fixed epilogue. Every bias and residual value this lane needs is loaded
+  // before its first store: the compiler cannot tell that C does not alias
+  // them, and would otherwise wait for each load after the previous store.
+  const bool gate = (ep.flags & 4) != 0;
+  const int NO = gate ? N / 2 : N;                  // output width
+  const int oc = gate ? col / 2 : col;              // this lane's output column
+  uint32_t bias2 = 0;
+  if (ep.flags & 1) bias2 = *reinterpret_cast<const uint32_t*>(ep.bias + col);
+  uint32_t res[MT][16];
+  if (ep.flags & 2) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = min(r0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3), M - 1);
+        const uint16_t* r = ep.residual + (size_t)row * NO + oc;
+        res[mt][i] = gate ? (uint32_t)*r : *reinterpret_cast<const uint32_t*>(r);
+      }
+    }
+  }
+  const float b0 = (ep.flags & 1) ? bits2f<BF>(bias2 & 0xFFFFu) : 0.f;
+  const float b1 = (ep.flags & 1) ? bits2f<BF>(bias2 >> 16) : 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = r0 + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (row >= M) continue;
+      float y0 = acc[mt][0][i] + b0, y1 = acc[mt][1][i] + b1;
+      if (gate) {
+        float z = silu(y0) * y1;
+        if (ep.flags & 2) z += bits2f<BF>(res[mt][i]);
+        C[(size_t)row * NO + oc] = BF ? f2bf_rn(z) : f2h_rn(z);
+      } else {
+        if (ep.flags & 2) {
+          y0 += bits2f<BF>(res[mt][i] & 0xFFFFu);
+          y1 += bits2f<BF>(res[mt][i] >> 16);
+        }
+        *reinterpret_cast<uint32_t*>(C + (size_t)row * NO + oc) =
+            BF ? f2bf2_rn(y0, y1) : (uint32_t)f2h_rn(y0) | ((uint32_t)f2h_rn(y1) << 16);
+      }
+    }
+  }
+}
+
 // One BM x BN output tile: rows m0 .. m0+BM-1 (those < M) and columns
 // n0 .. n0+BN-1 (those < N) of C = A . dequant(B, S).
 //
@@ -45,8 +115,10 @@ struct W4TileLds {
 //     right before it is needed. The B and scale descriptors are rebuilt at
 //     each stage's first packed row, so a packed B of any size is addressed
 //     with 32-bit offsets. Reads past a descriptor's end return zeros.
-//   * A rows sit in LDS with an XOR swizzle on their 16-byte chunks and in the
-//     K-slot order (0,4,1,5,2,6,3,7) that the unpack produces for B.
+//   * A rows sit in LDS in memory order with an XOR swizzle on their 16-byte
+//     chunks; the weights are unpacked in natural K order
+//     (unpack_w4_word_natural), as in the direct-to-LDS tile, so every path
+//     feeds the MFMAs the same operands slot for slot.
 //   * fp16: each word unpacks to (q - 8) exactly (code OR-ed into the mantissa
 //     of 1024.0, minus 1032), then one packed multiply by the column's group
 //     scale rounds each weight to fp16 before the MFMA.
@@ -226,7 +298,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   auto store_stage = [&](int kt, int buf, const Regs& r) {
     (void)kt;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = permute_k_0415(r.a[i]);
+    for (int i = 0; i < A_PER_T; ++i) lds_a[buf][a_lds[i]] = r.a[i];
 #pragma unroll
     for (int i = 0; i < (BD ? 0 : B_PER_T); ++i) {
       if constexpr (NK) {
@@ -294,12 +366,11 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         const uint32_t wd = (uint32_t)(w2 >> (32 * t));
         if constexpr (BF) {
           // 128 + q per half, exact; K-slot pairs (0,4), (1,5), (2,6), (3,7)
-          bq[t] = u32x4_t{and_or(wd, vmask, bias), and_or(wd >> 4, vmask, bias), and_or(wd >> 8, vmask, bias),
-                          and_or(wd >> 12, vmask, bias)};
+          bq[t] = unpack_w4_word_natural<false>(wd, vmask, bias);
         } else {
           const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
           const half2_t s2 = __builtin_bit_cast(half2_t, pair);
-          const u32x4_t d = dequant_w4_word_fused(wd, vmask, bias);
+          const u32x4_t d = unpack_w4_word_natural<true>(wd, vmask, bias);
           const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
           bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
         }
@@ -460,66 +531,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
     }
   }
 
-  // epilogue: two adjacent columns per 4-byte store (or one gated output)
-  const int col = n0 + wn * TN + 2 * c32;
-  if (col >= N) return;
-  if (ep.flags == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (row < M)
-          *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) =
-              BF ? f2bf2_rn(acc[mt][0][i], acc[mt][1][i])
-                 : (uint32_t)f2h_rn(acc[mt][0][i]) | ((uint32_t)f2h_rn(acc[mt][1][i]) << 16);
-      }
-    }
-    return;
-  }
-  // Fixed epilogue. Every bias and residual value this lane needs is loaded
-  // before its first store: the compiler cannot tell that C does not alias
-  // them, and would otherwise wait for each load after the previous store.
-  const bool gate = (ep.flags & 4) != 0;
-  const int NO = gate ? N / 2 : N;                  // output width
-  const int oc = gate ? col / 2 : col;              // this lane's output column
-  uint32_t bias2 = 0;
-  if (ep.flags & 1) bias2 = *reinterpret_cast<const uint32_t*>(ep.bias + col);
-  uint32_t res[MT][16];
-  if (ep.flags & 2) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = min(m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3), M - 1);
-        const uint16_t* r = ep.residual + (size_t)row * NO + oc;
-        res[mt][i] = gate ? (uint32_t)*r : *reinterpret_cast<const uint32_t*>(r);
-      }
-    }
-  }
-  const float b0 = (ep.flags & 1) ? bits2f<BF>(bias2 & 0xFFFFu) : 0.f;
-  const float b1 = (ep.flags & 1) ? bits2f<BF>(bias2 >> 16) : 0.f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = m0 + wm * TM + mt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (row >= M) continue;
-      float y0 = acc[mt][0][i] + b0, y1 = acc[mt][1][i] + b1;
-      if (gate) {
-        float z = silu(y0) * y1;
-        if (ep.flags & 2) z += bits2f<BF>(res[mt][i]);
-        C[(size_t)row * NO + oc] = BF ? f2bf_rn(z) : f2h_rn(z);
-      } else {
-        if (ep.flags & 2) {
-          y0 += bits2f<BF>(res[mt][i] & 0xFFFFu);
-          y1 += bits2f<BF>(res[mt][i] >> 16);
-        }
-        *reinterpret_cast<uint32_t*>(C + (size_t)row * NO + oc) =
-            BF ? f2bf2_rn(y0, y1) : (uint32_t)f2h_rn(y0) | ((uint32_t)f2h_rn(y1) << 16);
-      }
-    }
-  }
+  w4_tile_store<MT, BF>(acc, C, M, N, m0 + wm * TM, n0 + wn * TN, h, c32, ep);
 }
 
 // Dense kernel: one tile per workgroup, tile order within each
@@ -553,6 +565,221 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
   }
   w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK, BD>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN,
                                                              lds, ep);
+}
+
+// Direct-to-LDS form of the fp16 tile body for [K/8, N] weights and K a multiple
+// of 64: a 128 x 256 tile per K group of four waves (128 x 64 wave tiles).
+//   * Every stage's A rows (16 KiB), packed B rows (8 packed rows x 256 columns,
+//     8 KiB) and the scale rows of its two 32-deep halves (1 KiB) go from global
+//     memory straight into LDS with global_load_lds (lane l of a wave load fills
+//     bytes 16 l .. 16 l + 15 of a 1 KiB block), into NBUF stage buffers, so
+//     NBUF - 1 stages of loads are in flight without registers; each wave
+//     waits with an explicit vmcnt for all but its newest stage's loads and one
+//     barrier per stage publishes the next stage and frees the oldest buffer.
+//   * A stays in memory order (16-byte chunks XOR-swizzled by (row >> 1) & 7);
+//     the weights are unpacked in natural K order (unpack_w4_word_natural).
+//   * KG = 2: two groups of four waves take the even and the odd stages, each
+//     with its own buffers, and add their accumulators through LDS at the end.
+template <int KG, int NBUF>
+struct W4DmaLds {
+  u32x4_t a[KG][NBUF][128 * 8];    // [row][chunk], 128 B per row
+  uint32_t b[KG][NBUF][8 * 256];   // [packed row][column]
+  uint32_t s[KG][NBUF][2 * 128];   // [half][column pair]: the fp16 scales of two columns
+};
+
+template <int KG, int NBUF>
+__device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
+                                            const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
+                                            int N, int K, int group_size, int m0, int n0, W4DmaLds<KG, NBUF>& lds,
+                                            const Epilogue& ep) {
+  constexpr int BM = 128, BN = 256, NTHR = 4 * kWave, MT = 4;
+  // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one K group
+  // (as the register-staged tile with direct B does) and rows 16j + 8h .. + 7
+  // with two (as its staged-B form does), so both weight layouts give the same
+  // results bit for bit
+  constexpr bool KH = KG == 1;
+  const int lane = threadIdx.x & 63;
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kg = wave_all >> 2;     // K group
+  const int wn = wave_all & 3;      // the wave's 64-column strip
+  const int tid = threadIdx.x % NTHR;
+  const int h = lane >> 5, c32 = lane & 31;
+  const int rows = min(BM, M - m0);
+  const int gshift = __builtin_ctz(group_size);
+  const int nk = K / BK;
+
+  // wave loads of a stage (per K group): A blocks wn + 4i (rows 8a .. 8a + 7),
+  // packed B rows wn and wn + 4, and (wave 0) the two scale rows
+  uint32_t aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * (wn + 4 * i) + (lane >> 3);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);   // the chunk that swz puts at slot lane & 7
+    aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)K * 2u + ch * 16;
+  }
+  const int c4 = min(n0 + 4 * lane, N - 4) - n0;   // this lane's four columns of a packed row
+  uint32_t boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) boff[i] = (uint32_t)(wn + 4 * i) * (uint32_t)N * 4u + c4 * 4;
+  const int c8 = min(n0 + 8 * (lane & 31), N - 8) - n0;   // eight columns of a scale row
+  const int nw = 6 + (wn == 0);                            // loads per stage of this wave
+  auto lds_addr = [](const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+  };
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * BK;
+    const uint16_t* ab = A + (size_t)m0 * K + k0;
+    const uint32_t* bb = B + (size_t)(k0 / 8) * N + n0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wn + 4 * i) * 64]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(bb, boff[i], lds_addr(&lds.b[kg][buf][(wn + 4 * i) * 256]));
+    if (wn == 0) {
+      const int g0 = k0 >> gshift;
+      const int dg = ((k0 + 32) >> gshift) - g0;   // 1 when the second half starts a new group
+      const uint16_t* sb = S + (size_t)g0 * N + n0;
+      const uint32_t soff = (uint32_t)((lane >> 5) * dg) * (uint32_t)N * 2u + c8 * 2;
+      dma16(sb, soff, lds_addr(&lds.s[kg][buf][0]));
+    }
+  };
+  auto wait_loads = [](int n) {   // at most n of this wave's loads in flight (n uniform, 0 .. 14)
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+      case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;
+      case 14: __builtin_amdgcn_s_waitcnt(0xF7E); break;
+      default: __builtin_amdgcn_s_waitcnt(0xF70); break;
+    }
+  };
+
+  float16_t acc[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
+  const uint32_t vmask = in_vgpr(0x000F000Fu);
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+
+  auto compute = [&](int buf) {
+    const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds.b[kg][buf]);
+    u32x4_t afr[BK / 16][MT];
+    uint64_t bwr[BK / 16];
+    uint32_t spr[2];
+#pragma unroll
+    for (int j = 0; j < BK / 16; ++j) {
+      const int kc = KH ? 4 * h + j : 2 * j + h;   // the lane half's 8-deep K chunk (packed row) at step j
+      bwr[j] = bw[kc * (BN / 2) + wn * 32 + c32];   // columns 2 c32, 2 c32 + 1 of the strip
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 32 + c32;
+        afr[j][mt] = lds.a[kg][buf][row * CHUNKS + swz(row, kc)];
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) spr[s2] = lds.s[kg][buf][s2 * 128 + wn * 32 + c32];
+#pragma unroll
+    for (int j = 0; j < BK / 16; ++j) {
+      const uint64_t w2 = bwr[j];
+      const uint32_t sp = KH ? spr[h] : spr[j >> 1];
+      u32x4_t bq[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t wd = (uint32_t)(w2 >> (32 * t));
+        const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
+        const half2_t s2 = __builtin_bit_cast(half2_t, pair);
+        const u32x4_t d = unpack_w4_word_natural<true>(wd, vmask, bias);
+        const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+        bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][0] = mfma32x32x16_f16(afr[j][mt], bq[0], acc[mt][0]);
+        acc[mt][1] = mfma32x32x16_f16(afr[j][mt], bq[1], acc[mt][1]);
+      }
+    }
+  };
+
+  // group kg takes stages kg, kg + KG, ...; t counts its own stages. Both groups
+  // run the same number of iterations so every wave reaches every barrier.
+  const int iters = (nk + KG - 1) / KG;
+  auto valid = [&](int t) { return kg + KG * t < nk; };
+  if (valid(0)) issue(kg, 0);   // (with KG = 2 and one stage, group 1 has none)
+  if (valid(1)) {
+    issue(kg + KG, 1);
+    wait_loads(nw);
+  } else {
+    wait_loads(0);
+  }
+  __syncthreads();
+  auto stage = [&](int t, int buf) {
+    const bool more = valid(t + NBUF - 1);
+    if (more) issue(kg + KG * (t + NBUF - 1), (buf + NBUF - 1) % NBUF);
+    if (valid(t)) compute(buf);
+    // stage t + 1 must have landed; stages t + 2 .. t + NBUF - 1 may stay in flight
+    int inflight = 0;
+#pragma unroll
+    for (int d = 2; d < NBUF; ++d) inflight += valid(t + d) ? nw : 0;
+    wait_loads(inflight);
+    __syncthreads();
+  };
+  int t0 = 0;
+  for (; t0 + NBUF <= iters; t0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) stage(t0 + u, u);
+  }
+  for (; t0 < iters; ++t0) stage(t0, t0 % NBUF);
+
+  if constexpr (KG == 2) {
+    // group 1 hands its sums to group 0 through the (now free) stage buffers,
+    // two row tiles at a time, lane-major so the accesses are conflict-free
+    float* red = reinterpret_cast<float*>(&lds);
+    static_assert(sizeof(W4DmaLds<KG, NBUF>) >= 64 * NTHR * sizeof(float), "reduction space");
+#pragma unroll
+    for (int p = 0; p < MT / 2; ++p) {
+      if (kg == 1) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[((m * 2 + t) * 16 + i) * NTHR + tid] = acc[2 * p + m][t][i];
+      }
+      __syncthreads();
+      if (kg == 0) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[2 * p + m][t][i] += red[((m * 2 + t) * 16 + i) * NTHR + tid];
+      }
+      __syncthreads();
+    }
+    if (kg == 1) return;
+  }
+  w4_tile_store<MT, false>(acc, C, M, N, m0, n0 + wn * 64, h, c32, ep);
+}
+
+// Dense kernel of the direct-to-LDS tile body (tile order as in w4_prefill_v4_kernel).
+template <int KG, int MINB, int NBUF>
+__global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
+    uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
+    const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
+    Epilogue ep) {
+  __shared__ W4DmaLds<KG, NBUF> lds;
+  const int tiles = tiles_m * tiles_n;
+  const int per = (tiles + 7) >> 3;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= tiles) return;
+  const int span = order * tiles_n;
+  const int first = (lin / span) * order;
+  const int gm = min(tiles_m - first, order);
+  const int r = lin % span;
+  const int tm = first + r % gm, tn = r / gm;
+  w4_tile_dma<KG, NBUF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -649,6 +876,16 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
   } else if (p.nk) {
     if (one_pass) launch_v4<1, 1, 2, false, true>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, true>(p, stream, tm, tn);
+  } else if (p.K % BK == 0) {
+    // fp16, [K/8, N], whole stages: the direct-to-LDS tile (two workgroups per
+    // CU, or one of two K groups when the tiles fit in one pass)
+    const int grid = ((tm * tn + 7) / 8) * 8;
+    if (one_pass)
+      hipLaunchKernelGGL((w4_prefill_dma_kernel<2, 1, 3>), dim3(grid), dim3(8 * kWave), 0, stream, p.C, p.A, p.B,
+                         p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
+    else
+      hipLaunchKernelGGL((w4_prefill_dma_kernel<1, 2, 3>), dim3(grid), dim3(4 * kWave), 0, stream, p.C, p.A, p.B,
+                         p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
   } else {
     if (one_pass) launch_v4<1, 1, 2, false, false>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, false>(p, stream, tm, tn);

@@ -45,10 +45,13 @@ def check(lib, w, what):
 DECODE_SHAPES = [(16, 256, 512, 128), (3, 264, 384, 128), (13, 72, 256, 32), (7, 520, 512, 64),
                  (16, 8, 256, 256), (1, 4104, 1024, 128), (5, 1024, 2048, 64), (2, 192, 8192, 256),
                  (9, 128, 1024, 32)]
-# prefill: the first five run one workgroup of two K groups per CU (at most one
-# tile per CU), the last two more tiles than CUs (two workgroups per CU)
+# prefill: up to (129, 256, 64, 32) one workgroup of two K groups per CU (at most
+# one tile per CU; with K = 64 the second group has no stage), the last three
+# more tiles than CUs (two workgroups per CU); K % 64 == 32 takes the register-
+# staged tile, whole 64-deep stages the direct-to-LDS one (fp16, [K/8, N])
 PREFILL_SHAPES = [(48, 256, 512, 128), (17, 64, 256, 128), (100, 136, 96, 32), (257, 1000, 448, 64),
-                  (300, 264, 1024, 256), (129, 8, 128, 128), (2100, 4104, 480, 32), (2200, 4352, 512, 128)]
+                  (300, 264, 1024, 256), (129, 8, 128, 128), (129, 256, 64, 32), (2100, 4104, 480, 32),
+                  (2200, 4352, 512, 128), (2056, 4104, 320, 32)]
 
 
 def test_tiny_config(gpu, lib):
