@@ -680,6 +680,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) spr[s2] = lds.s[kg][buf][s2 * 128 + wn * 32 + c32];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       const uint64_t w2 = bwr[j];
