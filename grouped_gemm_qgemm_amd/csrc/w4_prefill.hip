@@ -16,6 +16,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
 namespace qg {
 
 namespace {
@@ -580,19 +581,21 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
 //     the weights are unpacked in natural K order (unpack_w4_word_natural).
 //   * KG = 2: two groups of four waves take the even and the odd stages, each
 //     with its own buffers, and add their accumulators through LDS at the end.
-template <int KG, int NBUF>
+template <int BM, int KG, int NBUF>
 struct W4DmaLds {
-  u32x4_t a[KG][NBUF][128 * 8];    // [row][chunk], 128 B per row
+  u32x4_t a[KG][NBUF][BM * 8];     // [row][chunk], 128 B per row
   uint32_t b[KG][NBUF][8 * 256];   // [packed row][column]
   uint32_t s[KG][NBUF][2 * 128];   // [half][column pair]: the fp16 scales of two columns
 };
 
-template <int KG, int NBUF>
+template <int BM, int KG, int NBUF>
 __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
-                                            int N, int K, int group_size, int m0, int n0, W4DmaLds<KG, NBUF>& lds,
-                                            const Epilogue& ep) {
-  constexpr int BM = 128, BN = 256, NTHR = 4 * kWave, MT = 4;
+                                            int N, int K, int group_size, int m0, int n0,
+                                            W4DmaLds<BM, KG, NBUF>& lds, const Epilogue& ep) {
+  constexpr int BN = 256, NTHR = 4 * kWave, MT = BM / 32;
+  constexpr int AW = BM / 32;   // A wave loads per stage and wave (BM / 8 rows-of-8 over four waves)
+  static_assert(BM == 64 || BM == 128, "tile rows");
   // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one K group
   // (as the register-staged tile with direct B does) and rows 16j + 8h .. + 7
   // with two (as its staged-B form does), so both weight layouts give the same
@@ -610,9 +613,9 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 
   // wave loads of a stage (per K group): A blocks wn + 4i (rows 8a .. 8a + 7),
   // packed B rows wn and wn + 4, and (wave 0) the two scale rows
-  uint32_t aoff[4];
+  uint32_t aoff[AW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < AW; ++i) {
     const int row = 8 * (wn + 4 * i) + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);   // the chunk that swz puts at slot lane & 7
     aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)K * 2u + ch * 16;
@@ -622,7 +625,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 #pragma unroll
   for (int i = 0; i < 2; ++i) boff[i] = (uint32_t)(wn + 4 * i) * (uint32_t)N * 4u + c4 * 4;
   const int c8 = min(n0 + 8 * (lane & 31), N - 8) - n0;   // eight columns of a scale row
-  const int nw = 6 + (wn == 0);                            // loads per stage of this wave
+  const int nw = AW + 2 + (wn == 0);                       // loads per stage of this wave
   auto lds_addr = [](const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
   };
@@ -631,7 +634,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     const uint16_t* ab = A + (size_t)m0 * K + k0;
     const uint32_t* bb = B + (size_t)(k0 / 8) * N + n0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wn + 4 * i) * 64]));
+    for (int i = 0; i < AW; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wn + 4 * i) * 64]));
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(bb, boff[i], lds_addr(&lds.b[kg][buf][(wn + 4 * i) * 256]));
     if (wn == 0) {
@@ -645,6 +648,8 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   auto wait_loads = [](int n) {   // at most n of this wave's loads in flight (n uniform, 0 .. 14)
     switch (n) {
       case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
       case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
       case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
       case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;
@@ -737,7 +742,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     // group 1 hands its sums to group 0 through the (now free) stage buffers,
     // two row tiles at a time, lane-major so the accesses are conflict-free
     float* red = reinterpret_cast<float*>(&lds);
-    static_assert(sizeof(W4DmaLds<KG, NBUF>) >= 64 * NTHR * sizeof(float), "reduction space");
+    static_assert(sizeof(W4DmaLds<BM, KG, NBUF>) >= 64 * NTHR * sizeof(float), "reduction space");
 #pragma unroll
     for (int p = 0; p < MT / 2; ++p) {
       if (kg == 1) {
@@ -770,7 +775,7 @@ __global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
     Epilogue ep) {
-  __shared__ W4DmaLds<KG, NBUF> lds;
+  __shared__ W4DmaLds<128, KG, NBUF> lds;
   const int tiles = tiles_m * tiles_n;
   const int per = (tiles + 7) >> 3;
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -780,7 +785,7 @@ __global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
   const int gm = min(tiles_m - first, order);
   const int r = lin % span;
   const int tm = first + r % gm, tn = r / gm;
-  w4_tile_dma<KG, NBUF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
+  w4_tile_dma<128, KG, NBUF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -792,12 +797,13 @@ __global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
 // holds an upper bound on the tile count (only the device knows the group
 // sizes); the real count is split evenly over the eight XCDs, at most
 // ceil(count / 8) <= grid / 8 tiles each, and workgroups past their XCD's run exit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD, bool BF>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD, bool BF, bool DMA = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
     int group_size, int num_active, int tiles_n, Epilogue ep) {
-  __shared__ W4TileLds<BM, BN, KG, BD> lds;
+  // the direct-to-LDS tile (fp16, K a multiple of 64) or the register-staged one
+  __shared__ std::conditional_t<DMA, W4DmaLds<BM, 1, 3>, W4TileLds<BM, BN, KG, BD>> lds;
   // The tile's coordinates are the same in every lane; readfirstlane makes that
   // visible to the compiler, so the buffer descriptors built from them stay in
   // SGPRs (otherwise every buffer load becomes a loop over distinct values).
@@ -820,18 +826,24 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   Epilogue ept = ep;
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
-                                                                   A + (size_t)r_begin * K, B + e * wpe,
-                                                                   S + e * spe, rows, N, K, group_size, 0,
-                                                                   nt * BN, lds, ept);
+  if constexpr (DMA)
+    w4_tile_dma<BM, 1, 3>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe, S + e * spe, rows, N, K,
+                          group_size, 0, nt * BN, lds, ept);
+  else
+    w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
+                                                                     A + (size_t)r_begin * K, B + e * wpe,
+                                                                     S + e * spe, rows, N, K, group_size, 0,
+                                                                     nt * BN, lds, ept);
 }
 
-// Grouped launch: 64-row chunks of a group by 256 columns, B words loaded
-// straight into the lanes' registers (one wave per column strip, so no B word
-// is shared). fp16: three workgroups per CU, two stages of loads in flight;
-// bf16 (exact codes, a group partial and a row-sum correction beside each
-// accumulator): two workgroups per CU, one stage in flight.
-template <int MINB, int PD, bool BF>
+// Grouped launch: 64-row chunks of a group by 256 columns. fp16 with K a
+// multiple of 64: the direct-to-LDS tile, three workgroups per CU (three stage
+// buffers of 17 KiB each). Otherwise the register-staged tile with B words
+// loaded straight into the lanes' registers (one wave per column strip, so no
+// B word is shared): fp16 with three workgroups per CU, two stages of loads in
+// flight; bf16 (exact codes, a group partial and a row-sum correction beside
+// each accumulator) with two workgroups per CU, one stage in flight.
+template <int MINB, int PD, bool BF, bool DMA = false>
 static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream) {
   constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KG = 1;
   constexpr bool BD = true;
@@ -840,14 +852,16 @@ static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
   if (bound > INT32_MAX / 2) return hipErrorNotSupported;
   const int grid = (int)((bound + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD, BF>), dim3(grid),
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD, BF, DMA>), dim3(grid),
                      dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N,
                      (int)p.K, p.group_size, p.num_active, tiles_n, p.epi);
   return hipGetLastError();
 }
 
 hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
-  return p.bf16 ? launch_w4_grouped_t<2, 1, true>(p, stream) : launch_w4_grouped_t<3, 2, false>(p, stream);
+  if (p.bf16) return launch_w4_grouped_t<2, 1, true>(p, stream);
+  if (p.K % BK == 0) return launch_w4_grouped_t<3, 2, false, true>(p, stream);   // fp16, whole stages: direct-to-LDS
+  return launch_w4_grouped_t<3, 2, false>(p, stream);
 }
 
 // Dense launch: 128 x 256 tiles, each XCD sweeping groups of eight row panels
