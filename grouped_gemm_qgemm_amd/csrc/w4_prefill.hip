@@ -588,44 +588,48 @@ struct W4DmaLds {
   uint32_t s[KG][NBUF][2 * 128];   // [half][column pair]: the fp16 scales of two columns
 };
 
-template <int BM, int KG, int NBUF>
+template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false>
 __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
                                             int N, int K, int group_size, int m0, int n0,
                                             W4DmaLds<BM, KG, NBUF>& lds, const Epilogue& ep) {
-  constexpr int BN = 256, NTHR = 4 * kWave, MT = BM / 32;
-  constexpr int AW = BM / 32;   // A wave loads per stage and wave (BM / 8 rows-of-8 over four waves)
-  static_assert(BM == 64 || BM == 128, "tile rows");
-  // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one K group
-  // (as the register-staged tile with direct B does) and rows 16j + 8h .. + 7
-  // with two (as its staged-B form does), so both weight layouts give the same
-  // results bit for bit
-  constexpr bool KH = KG == 1;
+  constexpr int BN = 256, WAVES = 4 * WAVES_M, NTHR = WAVES * kWave;
+  constexpr int TM = BM / WAVES_M, MT = TM / 32;
+  constexpr int AW = BM / 8 / WAVES;   // A wave loads (1 KiB, eight rows) per stage and wave
+  constexpr int BW = 8 / WAVES;        // packed B rows per stage and wave
+  static_assert(BM % (8 * WAVES) == 0 && TM % 32 == 0 && BW >= 1, "tile shape");
+  static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
+  // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one fp16 K
+  // group (as the register-staged tile with direct B does), else rows
+  // 16j + 8h .. + 7 (as its staged-B and bf16 forms do: a bf16 step stays in one
+  // quantization group), so both weight layouts give the same results bit for bit
+  constexpr bool KH = KG == 1 && !BF;
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kg = wave_all >> 2;     // K group
-  const int wn = wave_all & 3;      // the wave's 64-column strip
+  const int kg = wave_all / WAVES;   // K group
+  const int wave = wave_all % WAVES;
+  const int wm = wave >> 2, wn = wave & 3;   // the wave's row block and 64-column strip
   const int tid = threadIdx.x % NTHR;
   const int h = lane >> 5, c32 = lane & 31;
   const int rows = min(BM, M - m0);
   const int gshift = __builtin_ctz(group_size);
   const int nk = K / BK;
 
-  // wave loads of a stage (per K group): A blocks wn + 4i (rows 8a .. 8a + 7),
-  // packed B rows wn and wn + 4, and (wave 0) the two scale rows
+  // wave loads of a stage (per K group): A blocks wave + WAVES i (rows 8a .. 8a + 7),
+  // packed B rows wave + WAVES i, and (wave 0) the scale rows of the two halves
   uint32_t aoff[AW];
 #pragma unroll
   for (int i = 0; i < AW; ++i) {
-    const int row = 8 * (wn + 4 * i) + (lane >> 3);
+    const int row = 8 * (wave + WAVES * i) + (lane >> 3);
     const int ch = (lane & 7) ^ ((row >> 1) & 7);   // the chunk that swz puts at slot lane & 7
     aoff[i] = (uint32_t)min(row, rows - 1) * (uint32_t)K * 2u + ch * 16;
   }
   const int c4 = min(n0 + 4 * lane, N - 4) - n0;   // this lane's four columns of a packed row
-  uint32_t boff[2];
+  uint32_t boff[BW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) boff[i] = (uint32_t)(wn + 4 * i) * (uint32_t)N * 4u + c4 * 4;
+  for (int i = 0; i < BW; ++i) boff[i] = (uint32_t)(wave + WAVES * i) * (uint32_t)N * 4u + c4 * 4;
   const int c8 = min(n0 + 8 * (lane & 31), N - 8) - n0;   // eight columns of a scale row
-  const int nw = AW + 2 + (wn == 0);                       // loads per stage of this wave
+  const int nw = AW + BW + (wave == 0);                    // loads per stage of this wave
   auto lds_addr = [](const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
   };
@@ -634,10 +638,10 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     const uint16_t* ab = A + (size_t)m0 * K + k0;
     const uint32_t* bb = B + (size_t)(k0 / 8) * N + n0;
 #pragma unroll
-    for (int i = 0; i < AW; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wn + 4 * i) * 64]));
+    for (int i = 0; i < AW; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wave + WAVES * i) * 64]));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(bb, boff[i], lds_addr(&lds.b[kg][buf][(wn + 4 * i) * 256]));
-    if (wn == 0) {
+    for (int i = 0; i < BW; ++i) dma16(bb, boff[i], lds_addr(&lds.b[kg][buf][(wave + WAVES * i) * 256]));
+    if (wave == 0) {
       const int g0 = k0 >> gshift;
       const int dg = ((k0 + 32) >> gshift) - g0;   // 1 when the second half starts a new group
       const uint16_t* sb = S + (size_t)g0 * N + n0;
@@ -645,15 +649,14 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       dma16(sb, soff, lds_addr(&lds.s[kg][buf][0]));
     }
   };
-  auto wait_loads = [](int n) {   // at most n of this wave's loads in flight (n uniform, 0 .. 14)
+  auto wait_loads = [](int n) {   // at most n of this wave's loads in flight (n uniform)
     switch (n) {
       case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0xF73); break;
       case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
       case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
       case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
       case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
-      case 12: __builtin_amdgcn_s_waitcnt(0xF7C); break;
-      case 14: __builtin_amdgcn_s_waitcnt(0xF7E); break;
       default: __builtin_amdgcn_s_waitcnt(0xF70); break;
     }
   };
@@ -666,9 +669,21 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
   const uint32_t vmask = in_vgpr(0x000F000Fu);
-  const uint32_t bias = __builtin_amdgcn_readfirstlane(0x64006400u);
+  const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
+  // bf16: per row tile, the group partials of both column tiles and the
+  // row-sum correction -136 * sum(a) (the same for every column)
+  constexpr int MP = BF ? MT : 1;
+  float16_t part[MP][2], corr[MP];
+  auto clear_partials = [&]() {
+#pragma unroll
+    for (int i = 0; i < MP; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) part[i][0][e] = part[i][1][e] = corr[i][e] = 0.f;
+  };
+  if constexpr (BF) clear_partials();
+  const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
-  auto compute = [&](int buf) {
+  auto compute = [&](int buf, int k0) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds.b[kg][buf]);
     u32x4_t afr[BK / 16][MT];
     uint64_t bwr[BK / 16];
@@ -679,13 +694,13 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       bwr[j] = bw[kc * (BN / 2) + wn * 32 + c32];   // columns 2 c32, 2 c32 + 1 of the strip
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 32 + c32;
+        const int row = wm * TM + mt * 32 + c32;
         afr[j][mt] = lds.a[kg][buf][row * CHUNKS + swz(row, kc)];
       }
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) spr[s2] = lds.s[kg][buf][s2 * 128 + wn * 32 + c32];
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);   // every read of the stage ahead of its arithmetic
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       const uint64_t w2 = bwr[j];
@@ -694,16 +709,41 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t wd = (uint32_t)(w2 >> (32 * t));
-        const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
-        const half2_t s2 = __builtin_bit_cast(half2_t, pair);
-        const u32x4_t d = unpack_w4_word_natural<true>(wd, vmask, bias);
-        const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
-        bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        if constexpr (BF) {
+          bq[t] = unpack_w4_word_natural<false>(wd, vmask, bias);   // 128 + q, exact
+        } else {
+          const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
+          const half2_t s2 = __builtin_bit_cast(half2_t, pair);
+          const u32x4_t d = unpack_w4_word_natural<true>(wd, vmask, bias);
+          const uint32_t d0 = d.x, d1 = d.y, d2 = d.z, d3 = d.w;
+          bq[t] = u32x4_t{hmul2(d0, s2), hmul2(d1, s2), hmul2(d2, s2), hmul2(d3, s2)};
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][0] = mfma32x32x16_f16(afr[j][mt], bq[0], acc[mt][0]);
-        acc[mt][1] = mfma32x32x16_f16(afr[j][mt], bq[1], acc[mt][1]);
+        if constexpr (BF) {
+          part[mt][0] = mfma32x32x16_bf16(afr[j][mt], bq[0], part[mt][0]);
+          part[mt][1] = mfma32x32x16_bf16(afr[j][mt], bq[1], part[mt][1]);
+          corr[mt] = mfma32x32x16_bf16(afr[j][mt], u32x4_t{m136, m136, m136, m136}, corr[mt]);
+        } else {
+          acc[mt][0] = mfma32x32x16_f16(afr[j][mt], bq[0], acc[mt][0]);
+          acc[mt][1] = mfma32x32x16_f16(afr[j][mt], bq[1], acc[mt][1]);
+        }
+      }
+      if constexpr (BF) {
+        // the quantization group ends with this 16-deep step: scale its partials
+        // once (uniform test)
+        if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
+          const float s0 = bf2f((uint16_t)(sp & 0xFFFFu)), s1 = bf2f((uint16_t)(sp >> 16));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              acc[mt][0][e] += s0 * (part[mt][0][e] + corr[mt][e]);
+              acc[mt][1][e] += s1 * (part[mt][1][e] + corr[mt][e]);
+            }
+          clear_partials();
+        }
       }
     }
   };
@@ -723,7 +763,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   auto stage = [&](int t, int buf) {
     const bool more = valid(t + NBUF - 1);
     if (more) issue(kg + KG * (t + NBUF - 1), (buf + NBUF - 1) % NBUF);
-    if (valid(t)) compute(buf);
+    if (valid(t)) compute(buf, (kg + KG * t) * BK);
     // stage t + 1 must have landed; stages t + 2 .. t + NBUF - 1 may stay in flight
     int inflight = 0;
 #pragma unroll
@@ -743,6 +783,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     // two row tiles at a time, lane-major so the accesses are conflict-free
     float* red = reinterpret_cast<float*>(&lds);
     static_assert(sizeof(W4DmaLds<BM, KG, NBUF>) >= 64 * NTHR * sizeof(float), "reduction space");
+    static_assert(KG == 1 || MT % 2 == 0, "row tile pairs");
 #pragma unroll
     for (int p = 0; p < MT / 2; ++p) {
       if (kg == 1) {
@@ -766,12 +807,12 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     }
     if (kg == 1) return;
   }
-  w4_tile_store<MT, false>(acc, C, M, N, m0, n0 + wn * 64, h, c32, ep);
+  w4_tile_store<MT, BF>(acc, C, M, N, m0 + wm * TM, n0 + wn * 64, h, c32, ep);
 }
 
 // Dense kernel of the direct-to-LDS tile body (tile order as in w4_prefill_v4_kernel).
-template <int KG, int MINB, int NBUF>
-__global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
+template <int KG, int MINB, int NBUF, int WAVES_M = 1, bool BF = false>
+__global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
     Epilogue ep) {
@@ -785,7 +826,7 @@ __global__ __launch_bounds__(4 * kWave * KG, MINB) void w4_prefill_dma_kernel(
   const int gm = min(tiles_m - first, order);
   const int r = lin % span;
   const int tm = first + r % gm, tn = r / gm;
-  w4_tile_dma<128, KG, NBUF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
+  w4_tile_dma<128, KG, NBUF, WAVES_M, BF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -827,8 +868,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
   if constexpr (DMA)
-    w4_tile_dma<BM, 1, 3>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe, S + e * spe, rows, N, K,
-                          group_size, 0, nt * BN, lds, ept);
+    w4_tile_dma<BM, 1, 3, 1, BF>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe, S + e * spe, rows,
+                                 N, K, group_size, 0, nt * BN, lds, ept);
   else
     w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
                                                                      A + (size_t)r_begin * K, B + e * wpe,
@@ -859,7 +900,8 @@ static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream
 }
 
 hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
-  if (p.bf16) return launch_w4_grouped_t<2, 1, true>(p, stream);
+  if (p.bf16) return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, true, true>(p, stream)
+                                   : launch_w4_grouped_t<2, 1, true>(p, stream);
   if (p.K % BK == 0) return launch_w4_grouped_t<3, 2, false, true>(p, stream);   // fp16, whole stages: direct-to-LDS
   return launch_w4_grouped_t<3, 2, false>(p, stream);
 }
@@ -886,8 +928,17 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
   const int tm = (int)((p.M + 127) / 128), tn = (int)((p.N + 255) / 256);
   const bool one_pass = (long long)tm * tn <= num_cus;
   if (p.bf16) {
-    if (p.nk) launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
-    else launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
+    if (p.nk) {
+      launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
+    } else if (p.K % BK == 0) {
+      // bf16, [K/8, N], whole stages: the direct-to-LDS tile with eight 64 x 64
+      // wave tiles, one workgroup per CU
+      const int grid = ((tm * tn + 7) / 8) * 8;
+      hipLaunchKernelGGL((w4_prefill_dma_kernel<1, 1, 3, 2, true>), dim3(grid), dim3(8 * kWave), 0, stream, p.C,
+                         p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
+    } else {
+      launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
+    }
   } else if (p.nk) {
     if (one_pass) launch_v4<1, 1, 2, false, true>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, true>(p, stream, tm, tn);
