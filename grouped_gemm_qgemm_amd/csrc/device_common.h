@@ -207,6 +207,11 @@ __device__ __forceinline__ void dma4_lanes(const void* sbase, uint32_t voff, uin
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+// 2 bytes per lane; lane l's value lands in the 4-byte LDS word at lds + 4 l
+__device__ __forceinline__ void dma2(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Eight consecutive fp16 values (a0..a7 in four registers) reordered to the

@@ -9,10 +9,10 @@
 // advanced BK = 64 at a time, A and the packed B words of the next stage
 // fetched with raw buffer loads into registers while the current stage is
 // multiplied out of LDS, 32x32x16 MFMAs with fp32 accumulation, and the
-// 4-bit codes unpacked in VGPRs. Its comment below gives the details. For fp16
-// with [K/8, N] weights and K a multiple of 64, the dense kernel uses a
-// direct-to-LDS form of the tile (w4_tile_dma): every operand of a stage goes
-// from global memory straight into LDS, three stages deep.
+// 4-bit codes unpacked in VGPRs. Its comment below gives the details. When K
+// is a multiple of 64 (whole stages), both kernels use a direct-to-LDS form of
+// the tile (w4_tile_dma): every operand of a stage goes from global memory
+// straight into LDS, three stages deep.
 #include "device_common.h"
 #include "launch.h"
 
@@ -568,35 +568,44 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
                                                              lds, ep);
 }
 
-// Direct-to-LDS form of the fp16 tile body for [K/8, N] weights and K a multiple
-// of 64: a 128 x 256 tile per K group of four waves (128 x 64 wave tiles).
-//   * Every stage's A rows (16 KiB), packed B rows (8 packed rows x 256 columns,
-//     8 KiB) and the scale rows of its two 32-deep halves (1 KiB) go from global
-//     memory straight into LDS with global_load_lds (lane l of a wave load fills
-//     bytes 16 l .. 16 l + 15 of a 1 KiB block), into NBUF stage buffers, so
-//     NBUF - 1 stages of loads are in flight without registers; each wave
-//     waits with an explicit vmcnt for all but its newest stage's loads and one
-//     barrier per stage publishes the next stage and frees the oldest buffer.
+// Direct-to-LDS form of the tile body for K a multiple of 64: a BM x 256 tile
+// (BM = 128 or 64) per K group of 4 WAVES_M waves (TM x 64 wave tiles), fp16 or
+// bf16 (BF: exact codes, group partials as in w4_mfma_tile), weights [K/8, N]
+// or [N, K/8] (NK).
+//   * Every stage's A rows (BM x 128 B), packed B words (8 KiB) and the scales
+//     of its two 32-deep halves go from global memory straight into LDS with
+//     global_load_lds (lane l of a 16-byte wave load fills bytes 16 l .. + 15 of
+//     a 1 KiB block; the [N, K/gs] scales come with 2-byte loads, one scale per
+//     4-byte LDS word), into NBUF stage buffers, so NBUF - 1 stages of loads are
+//     in flight without registers; each wave waits with an explicit vmcnt for
+//     all but its newest stage's loads and one barrier per stage publishes the
+//     next stage and frees the oldest buffer.
 //   * A stays in memory order (16-byte chunks XOR-swizzled by (row >> 1) & 7);
 //     the weights are unpacked in natural K order (unpack_w4_word_natural).
+//     [K/8, N]: B in LDS as [packed row][column]. [N, K/8]: as each column's
+//     eight words, in 16-byte halves placed so that a read phase meets 16
+//     different bank groups; a lane reads its columns' halves whole.
 //   * KG = 2: two groups of four waves take the even and the odd stages, each
 //     with its own buffers, and add their accumulators through LDS at the end.
-template <int BM, int KG, int NBUF>
+template <int BM, int KG, int NBUF, bool NK = false>
 struct W4DmaLds {
   u32x4_t a[KG][NBUF][BM * 8];     // [row][chunk], 128 B per row
   uint32_t b[KG][NBUF][8 * 256];   // [packed row][column]
-  uint32_t s[KG][NBUF][2 * 128];   // [half][column pair]: the fp16 scales of two columns
+  // [half][column pair]: the scales of two columns; [N, K/gs] scales: [half][column],
+  // one scale in the low half of each word (a 2-byte LDS load fills 4 bytes per lane)
+  uint32_t s[KG][NBUF][NK ? 2 * 256 : 2 * 128];
 };
 
-template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false>
+template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false>
 __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
                                             int N, int K, int group_size, int m0, int n0,
-                                            W4DmaLds<BM, KG, NBUF>& lds, const Epilogue& ep) {
+                                            W4DmaLds<BM, KG, NBUF, NK>& lds, const Epilogue& ep) {
   constexpr int BN = 256, WAVES = 4 * WAVES_M, NTHR = WAVES * kWave;
   constexpr int TM = BM / WAVES_M, MT = TM / 32;
   constexpr int AW = BM / 8 / WAVES;   // A wave loads (1 KiB, eight rows) per stage and wave
-  constexpr int BW = 8 / WAVES;        // packed B rows per stage and wave
+  constexpr int BW = 8 / WAVES;        // B wave loads (1 KiB) per stage and wave
+  constexpr int SW = NK ? 8 / WAVES : 0;   // [N, K/gs] scales: 2-byte wave loads (64 columns) per wave
   static_assert(BM % (8 * WAVES) == 0 && TM % 32 == 0 && BW >= 1, "tile shape");
   static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
   // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one fp16 K
@@ -627,21 +636,51 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   const int c4 = min(n0 + 4 * lane, N - 4) - n0;   // this lane's four columns of a packed row
   uint32_t boff[BW];
 #pragma unroll
-  for (int i = 0; i < BW; ++i) boff[i] = (uint32_t)(wave + WAVES * i) * (uint32_t)N * 4u + c4 * 4;
+  for (int i = 0; i < BW; ++i) {
+    if constexpr (NK) {
+      // [N, K/8]: 16-byte slot s' of the stage's B area holds half s & 1 (words
+      // 4 (s & 1) .. + 3) of column s >> 1, s = s' ^ ((s' >> 4) & 3), so that the
+      // 16 lanes of a read phase, which read the same half of 16 even (or odd)
+      // columns, meet 16 different bank groups
+      const int sp = 64 * (wave + WAVES * i) + lane;
+      const int sl = sp ^ ((sp >> 4) & 3);
+      const int col = min(n0 + (sl >> 1), N - 1) - n0;
+      boff[i] = ((uint32_t)col * (uint32_t)(K / 8) + 4 * (sl & 1)) * 4u;
+    } else {
+      boff[i] = (uint32_t)(wave + WAVES * i) * (uint32_t)N * 4u + c4 * 4;
+    }
+  }
   const int c8 = min(n0 + 8 * (lane & 31), N - 8) - n0;   // eight columns of a scale row
-  const int nw = AW + BW + (wave == 0);                    // loads per stage of this wave
+  // [N, K/gs] scales: wave load q (0..7) brings half q >> 2, columns 64 (q & 3) + lane
+  uint32_t soffk[NK ? SW : 1];
+#pragma unroll
+  for (int i = 0; i < (NK ? SW : 1); ++i) {
+    const int q = wave + WAVES * i;
+    const int col = min(n0 + 64 * (q & 3) + lane, N - 1) - n0;
+    soffk[i] = (uint32_t)col * (uint32_t)(K >> gshift) * 2u;
+  }
+  const int nw = AW + BW + (NK ? SW : (wave == 0));        // loads per stage of this wave
   auto lds_addr = [](const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
   };
   auto issue = [&](int kt, int buf) {
     const int k0 = kt * BK;
     const uint16_t* ab = A + (size_t)m0 * K + k0;
-    const uint32_t* bb = B + (size_t)(k0 / 8) * N + n0;
+    const uint32_t* bb = NK ? B + (size_t)n0 * (K / 8) + k0 / 8 : B + (size_t)(k0 / 8) * N + n0;
 #pragma unroll
     for (int i = 0; i < AW; ++i) dma16(ab, aoff[i], lds_addr(&lds.a[kg][buf][(wave + WAVES * i) * 64]));
 #pragma unroll
     for (int i = 0; i < BW; ++i) dma16(bb, boff[i], lds_addr(&lds.b[kg][buf][(wave + WAVES * i) * 256]));
-    if (wave == 0) {
+    if constexpr (NK) {
+      const int g0 = k0 >> gshift;
+      const int dg = ((k0 + 32) >> gshift) - g0;
+      const uint16_t* sb = S + (size_t)n0 * (K >> gshift) + g0;
+#pragma unroll
+      for (int i = 0; i < SW; ++i) {
+        const int q = wave + WAVES * i;
+        dma2(sb, soffk[i] + (uint32_t)((q >> 2) * dg) * 2u, lds_addr(&lds.s[kg][buf][256 * (q >> 2) + 64 * (q & 3)]));
+      }
+    } else if (wave == 0) {
       const int g0 = k0 >> gshift;
       const int dg = ((k0 + 32) >> gshift) - g0;   // 1 when the second half starts a new group
       const uint16_t* sb = S + (size_t)g0 * N + n0;
@@ -657,6 +696,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       case 5: __builtin_amdgcn_s_waitcnt(0xF75); break;
       case 6: __builtin_amdgcn_s_waitcnt(0xF76); break;
       case 7: __builtin_amdgcn_s_waitcnt(0xF77); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
       default: __builtin_amdgcn_s_waitcnt(0xF70); break;
     }
   };
@@ -688,10 +728,45 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     u32x4_t afr[BK / 16][MT];
     uint64_t bwr[BK / 16];
     uint32_t spr[2];
+    if constexpr (NK) {
+      // the lane's two columns: words 4h .. 4h + 3 (KH), or all eight
+      const u32x4_t* bq4 = reinterpret_cast<const u32x4_t*>(lds.b[kg][buf]);
+      auto slot = [](int col, int half) { const int s = 2 * col + half; return s ^ ((s >> 4) & 3); };
+      u32x4_t wv[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int col = wn * 64 + 2 * c32 + t;
+        if constexpr (KH) {
+          wv[t][0] = bq4[slot(col, h)];
+        } else {
+          wv[t][0] = bq4[slot(col, 0)];
+          wv[t][1] = bq4[slot(col, 1)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BK / 16; ++j) {
+        uint32_t w01[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if constexpr (KH) {
+            w01[t] = wv[t][0][j];
+          } else {   // word 2j + h
+            const u32x4_t& v = wv[t][j >> 1];
+            w01[t] = h ? v[2 * (j & 1) + 1] : v[2 * (j & 1)];
+          }
+        }
+        bwr[j] = (uint64_t)w01[0] | ((uint64_t)w01[1] << 32);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < BK / 16; ++j) {
+        const int kc = KH ? 4 * h + j : 2 * j + h;   // the lane half's 8-deep K chunk (packed row) at step j
+        bwr[j] = bw[kc * (BN / 2) + wn * 32 + c32];   // columns 2 c32, 2 c32 + 1 of the strip
+      }
+    }
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
-      const int kc = KH ? 4 * h + j : 2 * j + h;   // the lane half's 8-deep K chunk (packed row) at step j
-      bwr[j] = bw[kc * (BN / 2) + wn * 32 + c32];   // columns 2 c32, 2 c32 + 1 of the strip
+      const int kc = KH ? 4 * h + j : 2 * j + h;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = wm * TM + mt * 32 + c32;
@@ -699,7 +774,14 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       }
     }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) spr[s2] = lds.s[kg][buf][s2 * 128 + wn * 32 + c32];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if constexpr (NK) {   // the low halves of two column words
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(&lds.s[kg][buf][s2 * 256 + wn * 64 + 2 * c32]);
+        spr[s2] = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);
+      } else {
+        spr[s2] = lds.s[kg][buf][s2 * 128 + wn * 32 + c32];
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);   // every read of the stage ahead of its arithmetic
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
@@ -782,7 +864,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     // group 1 hands its sums to group 0 through the (now free) stage buffers,
     // two row tiles at a time, lane-major so the accesses are conflict-free
     float* red = reinterpret_cast<float*>(&lds);
-    static_assert(sizeof(W4DmaLds<BM, KG, NBUF>) >= 64 * NTHR * sizeof(float), "reduction space");
+    static_assert(sizeof(W4DmaLds<BM, KG, NBUF, NK>) >= 64 * NTHR * sizeof(float), "reduction space");
     static_assert(KG == 1 || MT % 2 == 0, "row tile pairs");
 #pragma unroll
     for (int p = 0; p < MT / 2; ++p) {
@@ -811,12 +893,12 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 }
 
 // Dense kernel of the direct-to-LDS tile body (tile order as in w4_prefill_v4_kernel).
-template <int KG, int MINB, int NBUF, int WAVES_M = 1, bool BF = false>
+template <int KG, int MINB, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false>
 __global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
     Epilogue ep) {
-  __shared__ W4DmaLds<128, KG, NBUF> lds;
+  __shared__ W4DmaLds<128, KG, NBUF, NK> lds;
   const int tiles = tiles_m * tiles_n;
   const int per = (tiles + 7) >> 3;
   const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -826,7 +908,7 @@ __global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma
   const int gm = min(tiles_m - first, order);
   const int r = lin % span;
   const int tm = first + r % gm, tn = r / gm;
-  w4_tile_dma<128, KG, NBUF, WAVES_M, BF>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
+  w4_tile_dma<128, KG, NBUF, WAVES_M, BF, NK>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -927,31 +1009,34 @@ static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
 hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
   const int tm = (int)((p.M + 127) / 128), tn = (int)((p.N + 255) / 256);
   const bool one_pass = (long long)tm * tn <= num_cus;
-  if (p.bf16) {
-    if (p.nk) {
-      launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
-    } else if (p.K % BK == 0) {
-      // bf16, [K/8, N], whole stages: the direct-to-LDS tile with eight 64 x 64
-      // wave tiles, one workgroup per CU
-      const int grid = ((tm * tn + 7) / 8) * 8;
-      hipLaunchKernelGGL((w4_prefill_dma_kernel<1, 1, 3, 2, true>), dim3(grid), dim3(8 * kWave), 0, stream, p.C,
-                         p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
+  const int grid = ((tm * tn + 7) / 8) * 8;
+  // whole 64-deep stages: the direct-to-LDS tile. fp16: two workgroups of four
+  // 128 x 64 wave tiles per CU, or (at most one tile per CU) one workgroup of two
+  // K groups; bf16: one workgroup of eight 64 x 64 wave tiles per CU.
+  auto dma = [&](auto kernel, int waves) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(waves * kWave), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N,
+                       (int)p.K, p.group_size, tm, tn, 8, p.epi);
+  };
+  if (p.K % BK == 0) {
+    if (p.bf16) {
+      if (p.nk) dma(w4_prefill_dma_kernel<1, 1, 3, 2, true, true>, 8);
+      else dma(w4_prefill_dma_kernel<1, 1, 3, 2, true, false>, 8);
+    } else if (one_pass) {
+      if (p.nk) dma(w4_prefill_dma_kernel<2, 1, 3, 1, false, true>, 8);
+      else dma(w4_prefill_dma_kernel<2, 1, 3, 1, false, false>, 8);
     } else {
-      launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
+      if (p.nk) dma(w4_prefill_dma_kernel<1, 2, 3, 1, false, true>, 4);
+      else dma(w4_prefill_dma_kernel<1, 2, 3, 1, false, false>, 4);
     }
+    return hipGetLastError();
+  }
+  // K = 32 mod 64: the register-staged tile (its partial last stage)
+  if (p.bf16) {
+    if (p.nk) launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
+    else launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
   } else if (p.nk) {
     if (one_pass) launch_v4<1, 1, 2, false, true>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, true>(p, stream, tm, tn);
-  } else if (p.K % BK == 0) {
-    // fp16, [K/8, N], whole stages: the direct-to-LDS tile (two workgroups per
-    // CU, or one of two K groups when the tiles fit in one pass)
-    const int grid = ((tm * tn + 7) / 8) * 8;
-    if (one_pass)
-      hipLaunchKernelGGL((w4_prefill_dma_kernel<2, 1, 3>), dim3(grid), dim3(8 * kWave), 0, stream, p.C, p.A, p.B,
-                         p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
-    else
-      hipLaunchKernelGGL((w4_prefill_dma_kernel<1, 2, 3>), dim3(grid), dim3(4 * kWave), 0, stream, p.C, p.A, p.B,
-                         p.S, (int)p.M, (int)p.N, (int)p.K, p.group_size, tm, tn, 8, p.epi);
   } else {
     if (one_pass) launch_v4<1, 1, 2, false, false>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, false>(p, stream, tm, tn);
