@@ -73,23 +73,23 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9243183, "27db1fe4c6bd946a"),
-    "prefill": (277266343, "8fc3b1e6f5f196ec"),
-    "square": (101393920, "8fc3b1e6f5f196ec"),
-    "grouped": (367971168, "7a9d825f74180d39"),
-    "grouped_kn": (365907538, "7a9d825f74180d39"),
-    "grouped_w4": (114583689, "8fc3b1e6f5f196ec"),
-    "kproj": (85680745, "cb51f5b26f601731"),
-    "decode_gate": (9260246, "27db1fe4c6bd946a"),
-    "prefill_gate": (277581777, "8fc3b1e6f5f196ec"),
-    "decode_bf16": (9235675, "27db1fe4c6bd946a"),
-    "prefill_bf16": (302816299, "8fc3b1e6f5f196ec"),
-    "decode_nk": (9239024, "27db1fe4c6bd946a"),
-    "prefill_nk": (279726805, "8fc3b1e6f5f196ec"),
-    "kvproj": (202263739, "cb51f5b26f601731"),
-    "kvproj_e4m3": (193906221, "cb51f5b26f601731"),
-    "grouped_w4_bf16": (113713621, "8fc3b1e6f5f196ec"),
-    "kproj_e4m3h": (64450544, "cb51f5b26f601731"),
+    "decode": (9243183, "76549ddc9471fadf"),
+    "prefill": (270633779, "a657a8903987b748"),
+    "square": (101489975, "a657a8903987b748"),
+    "grouped": (367974254, "f021ee2cd95f4c65"),
+    "grouped_kn": (365920284, "f021ee2cd95f4c65"),
+    "grouped_w4": (114560267, "a657a8903987b748"),
+    "kproj": (85680873, "8291f9a09df6d461"),
+    "decode_gate": (9260246, "76549ddc9471fadf"),
+    "prefill_gate": (270921568, "a657a8903987b748"),
+    "decode_bf16": (9235675, "76549ddc9471fadf"),
+    "prefill_bf16": (303086484, "a657a8903987b748"),
+    "decode_nk": (9239066, "76549ddc9471fadf"),
+    "prefill_nk": (263379632, "a657a8903987b748"),
+    "kvproj": (202263867, "8291f9a09df6d461"),
+    "kvproj_e4m3": (193906093, "8291f9a09df6d461"),
+    "grouped_w4_bf16": (113997500, "a657a8903987b748"),
+    "kproj_e4m3h": (64450800, "8291f9a09df6d461"),
 }
 
 
@@ -257,7 +257,7 @@ class DecodeW4:
 
 class PrefillW4:
     """Prefill-shaped W4A16: M=2048, K=4096, N=11008 (or N=4096 for the square shape)."""
-    kernel = "w4_prefill_v4_kernel"
+    kernel = "w4_prefill_dma_kernel"
     bound = "mfma"
     dtype = "f16"
     epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
