@@ -46,6 +46,9 @@ __device__ __forceinline__ int swz_a(int r, int c) { return c ^ (r & 15); }
 // 128-byte rows (the fp8 tiles of the direct-to-LDS kernels): chunk c of row r lives at
 // chunk c ^ (r & 7) ^ (bit 3 of r), so rows r and r + 8, which share LDS banks, differ too
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
+// the e4m3-hidden kernel's weight tile: its transpose reads take K rows 32 apart in
+// one read phase, so bit 5 of the row (not bit 3) goes into chunk bit 0
+__device__ __forceinline__ int swz8b5(int r, int c) { return c ^ (r & 7) ^ ((r >> 5) & 1); }
 
 }  // namespace
 
@@ -721,7 +724,7 @@ __global__ __launch_bounds__(768) void kproj_f8f8_dma_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int kr = 8 * (wave + 12 * j) + (lane >> 3);
-    boff[j] = (uint32_t)kr * (uint32_t)N + swz8(kr, lane & 7) * 16;
+    boff[j] = (uint32_t)kr * (uint32_t)N + swz8b5(kr, lane & 7) * 16;
   }
   const int is_row = 64 * (wave - 6) + lane;
   const bool is_loader = wave >= 6 && wave < 9;
@@ -785,7 +788,7 @@ __global__ __launch_bounds__(768) void kproj_f8f8_dma_kernel(
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const int kr = 32 * q + 8 * s4 + (r16 >> 1);
-        const unsigned char* base = reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + swz8(kr, c)]) +
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(&lds_b[buf][kr * 8 + swz8b5(kr, c)]) +
                                     8 * (r16 & 1);
         const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2_t*)(__attribute__((address_space(3))) const unsigned char*)base);
