@@ -79,17 +79,17 @@ MEASURED_TRAFFIC = {
     "grouped": (367974254, "f021ee2cd95f4c65"),
     "grouped_kn": (365920284, "f021ee2cd95f4c65"),
     "grouped_w4": (114560267, "a657a8903987b748"),
-    "kproj": (85680873, "8291f9a09df6d461"),
+    "kproj": (85680489, "5ee8476366591581"),
     "decode_gate": (9260246, "76549ddc9471fadf"),
     "prefill_gate": (270921568, "a657a8903987b748"),
     "decode_bf16": (9235675, "76549ddc9471fadf"),
     "prefill_bf16": (303086484, "a657a8903987b748"),
     "decode_nk": (9239066, "76549ddc9471fadf"),
     "prefill_nk": (263379632, "a657a8903987b748"),
-    "kvproj": (202263867, "8291f9a09df6d461"),
-    "kvproj_e4m3": (193906093, "8291f9a09df6d461"),
+    "kvproj": (202264507, "5ee8476366591581"),
+    "kvproj_e4m3": (193908141, "5ee8476366591581"),
     "grouped_w4_bf16": (113997500, "a657a8903987b748"),
-    "kproj_e4m3h": (64450800, "8291f9a09df6d461"),
+    "kproj_e4m3h": (64451824, "5ee8476366591581"),
 }
 
 

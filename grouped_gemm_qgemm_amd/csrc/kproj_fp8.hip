@@ -558,7 +558,7 @@ __global__ __launch_bounds__(768) void kproj_bf16_dma_kernel(
   }
   const int is_row = 64 * (wave - 4) + lane;
   const bool is_loader = wave >= 4 && wave < 7;
-  const uint32_t is_off = (uint32_t)min(m0 + (is_loader ? is_row : 0), T - 1) * (uint32_t)KB * 4u;
+  const uint32_t is_off = (uint32_t)(min(m0 + (is_loader ? is_row : 0), T - 1) - m0) * (uint32_t)KB * 4u;
   // LDS byte address of a __shared__ location (the global_load_lds destination base, in M0)
   auto lds_addr = [](const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(768) void kproj_bf16_dma_kernel(
     for (int j = 0; j < 3; ++j) dma16(ha, aoff[j], lds_addr(&lds_a[buf][(wave + 12 * j) * 64]));
     dma16(wk, boff[0], lds_addr(&lds_b[buf][wave * 64]));
     if (wave < 4) dma16(wk, boff[1], lds_addr(&lds_b[buf][(wave + 12) * 64]));
-    if (is_loader) dma4_lanes(in_scale + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 4)]), is_row < BM);
+    if (is_loader) dma4_lanes(in_scale + (size_t)m0 * KB + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 4)]), is_row < BM);
   };
   // wait until at most the last stage's loads of this wave are in flight
   auto wait_all_but_one_stage = [&]() {
@@ -728,7 +728,7 @@ __global__ __launch_bounds__(768) void kproj_f8f8_dma_kernel(
   }
   const int is_row = 64 * (wave - 6) + lane;
   const bool is_loader = wave >= 6 && wave < 9;
-  const uint32_t is_off = (uint32_t)min(m0 + (is_loader ? is_row : 0), T - 1) * (uint32_t)KB * 4u;
+  const uint32_t is_off = (uint32_t)(min(m0 + (is_loader ? is_row : 0), T - 1) - m0) * (uint32_t)KB * 4u;
   const int nw = 2 + (wave < 6) + (wave < 4) + is_loader;   // loads per stage of this wave: 2 .. 4
   auto lds_addr = [](const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
@@ -740,7 +740,7 @@ __global__ __launch_bounds__(768) void kproj_f8f8_dma_kernel(
     if (wave < 6) dma16(ha, aoff[1], lds_addr(&lds_a[buf][(wave + 12) * 64]));
     dma16(wk, boff[0], lds_addr(&lds_b[buf][wave * 64]));
     if (wave < 4) dma16(wk, boff[1], lds_addr(&lds_b[buf][(wave + 12) * 64]));
-    if (is_loader) dma4_lanes(in_scale + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 6)]), is_row < BM);
+    if (is_loader) dma4_lanes(in_scale + (size_t)m0 * KB + kb, is_off, lds_addr(&lds_is[buf][64 * (wave - 6)]), is_row < BM);
   };
   // wait until at most `n` of this wave's loads are in flight (n: 0 .. 8, uniform)
   auto wait_loads = [](int n) {
@@ -939,15 +939,19 @@ static int pick_kproj_rows(const KProjArgs& p, const int* cand, int n) {
 
 hipError_t launch_kproj_fp8(const KProjArgs& p, hipStream_t stream) {
   static const int cand[] = {48, 96, 144};
+  // the 144-row (direct-to-LDS) kernels address a tile's hidden rows and a
+  // stage's weight rows with 32-bit offsets: up to 2^23 hidden columns and 2^24
+  // output columns; beyond that the 48 / 96-row kernels (64-bit addresses)
+  const int nc = (p.Kh <= (1 << 23) && p.N <= (1 << 24)) ? 3 : 2;
   if (p.hidden_fp8) {
-    // e4m3 hidden rows: 48, 96 or 144-row tiles, two stages of loads in flight
-    switch (pick_kproj_rows(p, cand, 3) / 48) {
+    // e4m3 hidden rows: 48, 96 or 144-row tiles
+    switch (pick_kproj_rows(p, cand, nc) / 48) {
       case 1: return launch_kproj_f8f8<1, 2>(p, stream);
       case 2: return launch_kproj_f8f8<2, 2>(p, stream);
       default: return launch_kproj_f8f8<3, 2>(p, stream);
     }
   }
-  switch (pick_kproj_rows(p, cand, 3) / 48) {
+  switch (pick_kproj_rows(p, cand, nc) / 48) {
     case 1: return launch_kproj_bf16<1, 2>(p, stream);
     case 2: return launch_kproj_bf16<2, 2>(p, stream);
     default: return launch_kproj_bf16<3, 2>(p, stream);
