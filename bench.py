@@ -179,6 +179,7 @@ class DecodeW4:
     kernel = "w4_decode_lds_kernel"
     bound = "hbm"
     dtype = "f16"
+    launch_shape = (256, 512)   # the decode kernel's grid: N / 16 workgroups of eight waves
     epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
     nk = False   # weights and scales stored [N, K/8] / [N, K/gs] (qgemm_w4_nk)
 
@@ -260,6 +261,7 @@ class PrefillW4:
     kernel = "w4_prefill_dma_kernel"
     bound = "mfma"
     dtype = "f16"
+    mfma_kind = 0   # the MFMA issue loop of the same kind (qg_mfma_loop): fp16
     epi = 0   # qgemm_w4_epilogue flags (0: plain qgemm_w4)
     nk = False   # weights and scales stored [N, K/8] / [N, K/gs] (qgemm_w4_nk)
 
@@ -365,6 +367,7 @@ class DecodeW4BF16(DecodeW4):
 class PrefillW4BF16(PrefillW4):
     """The 2048 x 11008 x 4096 prefill with bf16 activations, scales and output."""
     dtype = "bf16"
+    mfma_kind = 1
 
 
 class GroupedBF16:
@@ -449,6 +452,7 @@ class GroupedW4:
     kernel = "w4_grouped_kernel"
     bound = "hbm"
     dtype = "f16"
+    mfma_kind = 0
 
     def __init__(self, torch, q, synth):
         self.torch, self.q = torch, q
@@ -516,6 +520,7 @@ class GroupedW4:
 class GroupedW4BF16(GroupedW4):
     """The grouped W4 workload with bf16 activations, scales and output."""
     dtype = "bf16"
+    mfma_kind = 1
 
 
 class KProjFP8:
@@ -524,6 +529,7 @@ class KProjFP8:
     kernel = "kproj_bf16_dma_kernel"
     bound = "mfma"
     dtype = "bf16"
+    mfma_kind = 1   # bf16 MFMAs on weights converted from e4m3
     planes = 1          # 2: keys and values ([W_k | W_v]) in one call
     cache = "bf16"      # or "fp8": e4m3 cache with one f32 scale per head row (G = 128)
     hidden = "bf16"     # or "fp8": e4m3 hidden rows, one f32 scale per token per 128 columns
@@ -605,6 +611,7 @@ class KProjE4M3Hidden(KProjFP8):
     """The K-projection workload with e4m3 hidden rows: both MFMA operands are e4m3."""
     kernel = "kproj_f8f8_dma_kernel"
     dtype = "e4m3"
+    mfma_kind = 2
     hidden = "fp8"
     mfma_peak = FP8_MFMA_PEAK_TFLOPS
 
@@ -649,7 +656,13 @@ def context_numbers(torch, q, wl, steps, avg_launch_ms):
       16-column strip per workgroup, every packed row: the pattern of a kernel that
       gives each workgroup a column strip and all of K;
     * torch_dense: torch.matmul (hipBLASLt) on dense operands of the same GEMM shape,
-      timed eagerly: a practical MFMA figure for the MFMA-bound workloads."""
+      timed eagerly: a practical MFMA figure for the MFMA-bound workloads;
+    * mfma_loop (MFMA-bound and grouped W4 workloads): the library's MFMA issue loop
+      of the workload's MFMA kind on every CU (two waves per SIMD, nothing but
+      MFMAs), its FLOP rate and the shader clock it held: what the matrix cores
+      sustain on this chip, against the published peak;
+    * empty_launch (decode): a kernel that does nothing, in the GEMM's launch shape:
+      the floor under one launch of that shape."""
     out = {}
     n_launch = len(wl.launches(0))
     hot_ms = graph_time_ms(torch, [wl.launches(0) for _ in range(max(steps // 2, 10))])
@@ -689,8 +702,33 @@ def context_numbers(torch, q, wl, steps, avg_launch_ms):
         out["torch_dense_us"] = round(ms * 1e3, 3)
         out["torch_dense_TFLOPs"] = round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)
         del a, b, c
+    kind = getattr(wl, "mfma_kind", None)
+    if kind is not None:
+        out["mfma_loop"] = mfma_loop_numbers(torch, q, kind)
+        out["gemm_frac_of_mfma_loop"] = round(wl.unit_flops() / (avg_launch_ms * 1e-3) / 1e12
+                                              / out["mfma_loop"]["TFLOPs"], 4)
+    shape = getattr(wl, "launch_shape", None)
+    if shape is not None:
+        e_ms = graph_time_ms(torch, [[lambda: q.empty_launch(*shape)] for _ in range(200)])
+        out["empty_launch_us"] = round(e_ms * 1e3, 3)
+        out["empty_launch_shape"] = {"workgroups": shape[0], "threads": shape[1]}
     out["launches_per_step"] = n_launch
     return out
+
+
+def mfma_loop_numbers(torch, q, kind, workgroups=256, iters=512, launches=20):
+    """FLOP rate of the MFMA issue loop (graph-timed, best of three) and the mean
+    shader clock its workgroups measured (s_memtime against the 100 MHz counter)."""
+    clocks = torch.zeros(2 * workgroups, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms = graph_time_ms(torch, [[lambda: q.mfma_loop(kind, iters, workgroups, clocks, sink)]
+                               for _ in range(launches)])
+    c = clocks.view(workgroups, 2).double()
+    mhz = float((c[:, 0] / c[:, 1]).mean()) * 100.0
+    flops = workgroups * 8 * iters * 8 * q.MFMA_LOOP_FLOPS[kind]
+    name = {v: k for k, v in q.MFMA_LOOP_KINDS.items()}[kind]
+    return {"kind": name, "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1), "clock_MHz": round(mhz),
+            "us_per_launch": round(ms * 1e3, 3), "workgroups": workgroups, "iters": iters}
 
 
 WORKLOADS = {"decode": DecodeW4, "prefill": PrefillW4,

@@ -24,7 +24,8 @@ Entry points (same names as the C ABI):
                                 kv_scales=None, quantization_granularity=0)
     kv_matmul_ragged_paged_scale(... the same, weight = [W_k | W_v] ...)
 Each returns None on success and raises QgError carrying the status otherwise.
-Measurement yardsticks (include/qgemm_probe.h): read_contiguous, read_strips.
+Measurement yardsticks (include/qgemm_probe.h): read_contiguous, read_strips, mfma_loop,
+empty_launch.
 """
 from __future__ import annotations
 
@@ -115,13 +116,18 @@ def load(path: str | None = None):
     lib.qg_status_string.restype = ctypes.c_char_p
     lib.qg_version.argtypes = []
     lib.qg_version.restype = ctypes.c_int32
-    # read-only HBM yardsticks (include/qgemm_probe.h)
+    # measurement yardsticks (include/qgemm_probe.h)
     lib.qg_read_contiguous.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p]
     lib.qg_read_contiguous.restype = ctypes.c_int
     lib.qg_read_strips.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.qg_read_strips.restype = ctypes.c_int
+    lib.qg_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    lib.qg_mfma_loop.restype = ctypes.c_int
+    lib.qg_empty_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.qg_empty_launch.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -341,6 +347,32 @@ def read_strips(src: torch.Tensor, strip_bytes: int, sink: torch.Tensor, stream=
     row_bytes = src.shape[1] * src.element_size()
     st = load().qg_read_strips(src.data_ptr(), src.shape[0], row_bytes, int(strip_bytes), sink.data_ptr(),
                                _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+MFMA_LOOP_KINDS = {"f16": 0, "bf16": 1, "e4m3": 2}
+MFMA_LOOP_FLOPS = {0: 32768, 1: 32768, 2: 65536}   # FLOPs per MFMA of each kind
+
+
+def mfma_loop(kind: int, iters: int, workgroups: int, clocks: torch.Tensor, sink: torch.Tensor, stream=None,
+              raise_on_error: bool = True) -> int:
+    """MFMA issue loop (a measurement yardstick): `clocks` is an int64 tensor of
+    2 * workgroups elements that receives each workgroup's shader-clock cycles and
+    100 MHz reference ticks across its loop."""
+    if clocks.dtype != torch.int64 or clocks.numel() < 2 * int(workgroups):
+        raise ValueError("clocks: int64 tensor of at least 2 * workgroups elements")
+    st = load().qg_mfma_loop(int(kind), int(iters), int(workgroups), clocks.data_ptr(), sink.data_ptr(),
+                             _stream(stream))
+    if raise_on_error:
+        _check(st)
+    return st
+
+
+def empty_launch(workgroups: int, threads: int, stream=None, raise_on_error: bool = True) -> int:
+    """Launch a kernel that does nothing (a measurement yardstick)."""
+    st = load().qg_empty_launch(int(workgroups), int(threads), _stream(stream))
     if raise_on_error:
         _check(st)
     return st

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"qgemm_w4", "qgemm_w4_nk", "qgemm_w4_epilogue", "grouped_gemm", "grouped_gemm_w4", "grouped_gemm_epilogue",
             "grouped_gemm_w4_epilogue", "k_matmul_ragged_paged_scale", "kv_matmul_ragged_paged_scale",
-            "qg_status_string", "qg_read_contiguous", "qg_read_strips"} <= set(names)
+            "qg_status_string", "qg_read_contiguous", "qg_read_strips", "qg_mfma_loop",
+            "qg_empty_launch"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
     for n in names:
@@ -380,3 +381,24 @@ def test_read_probe_rejections(lib):
     assert lib.qg_read_strips(base, 8, 512, 40, s, None) == QG.ERR_ALIGN
     assert lib.qg_read_strips(base, 8, 512, 0, s, None) == QG.ERR_INVALID_ARG
     assert lib.qg_read_strips(base, 0, 512, 64, s, None) == QG.OK
+
+
+def test_compute_probe_rejections(lib):
+    # host checks only: every call here returns before any launch
+    lib.qg_mfma_loop.restype = ctypes.c_int
+    lib.qg_mfma_loop.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    lib.qg_empty_launch.restype = ctypes.c_int
+    lib.qg_empty_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    clocks = np.zeros(8, np.uint64)
+    sink = np.zeros(4, np.uint32)
+    c, s = clocks.ctypes.data, sink.ctypes.data
+    assert lib.qg_mfma_loop(0, 8, 4, None, s, None) == QG.ERR_NULL
+    assert lib.qg_mfma_loop(0, 8, 4, c, None, None) == QG.ERR_NULL
+    assert lib.qg_mfma_loop(3, 8, 4, c, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_mfma_loop(-1, 8, 4, c, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_mfma_loop(0, 0, 4, c, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_mfma_loop(1, 8, 0, c, s, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_empty_launch(0, 64, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_empty_launch(4, 0, None) == QG.ERR_INVALID_ARG
+    assert lib.qg_empty_launch(4, 1025, None) == QG.ERR_INVALID_ARG
