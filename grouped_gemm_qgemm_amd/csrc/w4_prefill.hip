@@ -988,8 +988,13 @@ hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
   return launch_w4_grouped_t<3, 2, false>(p, stream);
 }
 
-// Dense launch: 128 x 256 tiles, each XCD sweeping groups of eight row panels
-// across N. fp16: one K group of four 128 x 64 wave tiles, two workgroups per
+// Row panels per group of the dense tile order: each XCD takes a contiguous run
+// of tiles in which groups of this many 128-row panels are swept across N. At
+// M = 2048 an XCD's run then covers four A panels and eight (N = 4096) or about
+// twenty (N = 11008) B panels, whose sum is smaller than with eight A panels.
+constexpr int kPanelGroup = 4;
+
+// Dense launch: 128 x 256 tiles in the order above. fp16: one K group of four 128 x 64 wave tiles, two workgroups per
 // CU, or (at most one tile per CU) one workgroup of two K groups per CU. bf16:
 // eight 64 x 64 wave tiles (two waves per column strip), one workgroup per CU:
 // the exact-code path keeps a group partial and a row-sum correction beside
@@ -1003,7 +1008,7 @@ static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
   const int grid = ((tm * tn + 7) / 8) * 8;
   hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK, BD>), dim3(grid),
                      dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,
-                     p.group_size, tm, tn, 8, p.epi);
+                     p.group_size, tm, tn, kPanelGroup, p.epi);
 }
 
 hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
@@ -1015,7 +1020,7 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
   // K groups; bf16: one workgroup of eight 64 x 64 wave tiles per CU.
   auto dma = [&](auto kernel, int waves) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(waves * kWave), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N,
-                       (int)p.K, p.group_size, tm, tn, 8, p.epi);
+                       (int)p.K, p.group_size, tm, tn, kPanelGroup, p.epi);
   };
   if (p.K % BK == 0) {
     if (p.bf16) {
