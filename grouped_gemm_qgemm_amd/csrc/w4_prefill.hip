@@ -596,7 +596,7 @@ struct W4DmaLds {
   uint32_t s[KG][NBUF][NK ? 2 * 256 : 2 * 128];
 };
 
-template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false>
+template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false, bool PART = false>
 __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
                                             int N, int K, int group_size, int m0, int n0,
@@ -723,7 +723,15 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   if constexpr (BF) clear_partials();
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
-  auto compute = [&](int buf, int k0) {
+  // PART (routed tiles): a wave does no arithmetic when its column strip lies
+  // wholly past N and (fp16) skips the fragment reads and MFMAs of a row tile
+  // wholly past the tile's rows; the loads and barriers stay the same. ME row
+  // tiles are multiplied (MT, or 1 when at most 32 rows are real).
+  static_assert(!PART || (MT == 2 && KG == 1), "partial tiles: two row tiles, one K group");
+  const int live_mt = __builtin_amdgcn_readfirstlane(
+      n0 + wn * 64 >= N ? 0 : min(MT, max(0, (rows - wm * TM + 31) / 32)));
+  auto compute = [&](int buf, int k0, auto me) {
+    constexpr int ME = decltype(me)::value;
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds.b[kg][buf]);
     u32x4_t afr[BK / 16][MT];
     uint64_t bwr[BK / 16];
@@ -768,7 +776,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     for (int j = 0; j < BK / 16; ++j) {
       const int kc = KH ? 4 * h + j : 2 * j + h;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < ME; ++mt) {
         const int row = wm * TM + mt * 32 + c32;
         afr[j][mt] = lds.a[kg][buf][row * CHUNKS + swz(row, kc)];
       }
@@ -802,7 +810,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < ME; ++mt) {
         if constexpr (BF) {
           part[mt][0] = mfma32x32x16_bf16(afr[j][mt], bq[0], part[mt][0]);
           part[mt][1] = mfma32x32x16_bf16(afr[j][mt], bq[1], part[mt][1]);
@@ -818,7 +826,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
         if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
           const float s0 = bf2f((uint16_t)(sp & 0xFFFFu)), s1 = bf2f((uint16_t)(sp >> 16));
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < ME; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               acc[mt][0][e] += s0 * (part[mt][0][e] + corr[mt][e]);
@@ -845,7 +853,17 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   auto stage = [&](int t, int buf) {
     const bool more = valid(t + NBUF - 1);
     if (more) issue(kg + KG * (t + NBUF - 1), (buf + NBUF - 1) % NBUF);
-    if (valid(t)) compute(buf, (kg + KG * t) * BK);
+    if (valid(t)) {
+      const int k0 = (kg + KG * t) * BK;
+      if constexpr (PART && !BF) {
+        if (live_mt == MT) compute(buf, k0, std::integral_constant<int, MT>{});
+        else if (live_mt > 0) compute(buf, k0, std::integral_constant<int, 1>{});
+      } else if constexpr (PART) {
+        if (live_mt > 0) compute(buf, k0, std::integral_constant<int, MT>{});
+      } else {
+        compute(buf, k0, std::integral_constant<int, MT>{});
+      }
+    }
     // stage t + 1 must have landed; stages t + 2 .. t + NBUF - 1 may stay in flight
     int inflight = 0;
 #pragma unroll
@@ -950,8 +968,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
   if constexpr (DMA)
-    w4_tile_dma<BM, 1, 3, 1, BF>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe, S + e * spe, rows,
-                                 N, K, group_size, 0, nt * BN, lds, ept);
+    w4_tile_dma<BM, 1, 3, 1, BF, false, true>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe,
+                                              S + e * spe, rows, N, K, group_size, 0, nt * BN, lds, ept);
   else
     w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
                                                                      A + (size_t)r_begin * K, B + e * wpe,
