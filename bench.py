@@ -73,22 +73,22 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
-    "decode": (9243183, "76549ddc9471fadf"),
-    "prefill": (270633779, "a657a8903987b748"),
-    "square": (101489975, "a657a8903987b748"),
+    "decode": (9240453, "76549ddc9471fadf"),
+    "prefill": (224961818, "75b7b65ab71659dd"),
+    "square": (85237833, "75b7b65ab71659dd"),
     "grouped": (367974254, "f021ee2cd95f4c65"),
     "grouped_kn": (365920284, "f021ee2cd95f4c65"),
-    "grouped_w4": (114560267, "a657a8903987b748"),
+    "grouped_w4": (114093044, "75b7b65ab71659dd"),
     "kproj": (85680489, "5ee8476366591581"),
-    "decode_gate": (9260246, "76549ddc9471fadf"),
-    "prefill_gate": (270921568, "a657a8903987b748"),
-    "decode_bf16": (9235675, "76549ddc9471fadf"),
-    "prefill_bf16": (303086484, "a657a8903987b748"),
-    "decode_nk": (9239066, "76549ddc9471fadf"),
-    "prefill_nk": (263379632, "a657a8903987b748"),
+    "decode_gate": (9252737, "76549ddc9471fadf"),
+    "prefill_gate": (224442766, "75b7b65ab71659dd"),
+    "decode_bf16": (9230896, "76549ddc9471fadf"),
+    "prefill_bf16": (245728636, "75b7b65ab71659dd"),
+    "decode_nk": (9234587, "76549ddc9471fadf"),
+    "prefill_nk": (221526728, "75b7b65ab71659dd"),
     "kvproj": (202264507, "5ee8476366591581"),
     "kvproj_e4m3": (193908141, "5ee8476366591581"),
-    "grouped_w4_bf16": (113997500, "a657a8903987b748"),
+    "grouped_w4_bf16": (114006715, "75b7b65ab71659dd"),
     "kproj_e4m3h": (64451824, "5ee8476366591581"),
 }
 
