@@ -27,7 +27,9 @@
  *     value says what was wrong (qg_status_string gives a message).
  *   - Work is enqueued on `stream` and the call returns without synchronizing.
  *     Empty problems (a zero-sized M, T, N or no active group) are a successful
- *     no-op that enqueues nothing.
+ *     no-op that enqueues nothing. A zero reduction depth (K = 0, or Kh = 0 for
+ *     the projections), whose result would be the epilogue of an all-zero
+ *     product, returns QG_ERR_UNSUPPORTED.
  *   - Outputs must not alias inputs. Calls on different streams may run
  *     concurrently; the library holds no mutable global state besides a cache of
  *     device properties.

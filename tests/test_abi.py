@@ -129,6 +129,16 @@ def test_w4_empty_problem_is_a_noop(lib):
     assert w4_call(lib, c, a, b, s) == QG.OK
 
 
+def test_w4_zero_depth_is_rejected(lib):
+    """K = 0 (a zero-depth product) is refused before anything is launched."""
+    bb = Buf()
+    c, a, b, s = w4_args(bb, M=4, K=0)
+    assert w4_call(lib, c, a, b, s) == QG.ERR_UNSUPPORTED
+    nk = lib.qgemm_w4_nk(ctypes.byref(c), ctypes.byref(a), ctypes.byref(bb.t((64, 0), QG.U32)),
+                         ctypes.byref(bb.t((64, 0), QG.F16)), 128, 8, None)
+    assert nk == QG.ERR_UNSUPPORTED
+
+
 def epi_call(lib, c, a, b, s, flags, bias=None, res=None, gs=128):
     r = lambda t: ctypes.byref(t) if t is not None else None
     return lib.qgemm_w4_epilogue(ctypes.byref(c), ctypes.byref(a), ctypes.byref(b), ctypes.byref(s), gs, 8,
