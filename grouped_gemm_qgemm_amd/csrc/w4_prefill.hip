@@ -128,6 +128,8 @@ __device__ __forceinline__ void w4_tile_store(const float16_t (&acc)[MT][2], uin
 //     constant -136 operand adds -136 * (sum of the row's activations), and the
 //     fp32 partial of each quantization group is scaled once by the group's
 //     scale when the group ends (deferred scaling).
+//   * exact fp16 (XH, for gated outputs): the bf16 form's tiles and group
+//     partials with the exact fp16 codes q - 8 and no correction MFMA.
 //   * KG = 2: two groups of WAVES_M x WAVES_N waves take the even and the odd
 //     K stages (each with its own LDS buffers) and sum their accumulators
 //     through LDS at the end (for shapes with about one tile per CU).
@@ -145,7 +147,7 @@ __device__ __forceinline__ void w4_tile_store(const float16_t (&acc)[MT][2], uin
 //     rows 16j + 8h .. + 7, which keeps every step inside one quantization
 //     group for the group partials.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int PD, int KG, bool BF = false, bool NK = false,
-          bool BD = false>
+          bool BD = false, bool XH = false>
 __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                              const uint32_t* __restrict__ B, const uint16_t* __restrict__ S,
                                              int M, int N, int K, int group_size, int m0, int n0,
@@ -157,7 +159,8 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   static_assert(PD >= 1 && PD <= 4, "prefetch distance");
   static_assert(KG == 1 || (KG == 2 && PD == 1 && MT % 2 == 0), "K groups");
   static_assert(!BD || (KG == 1 && !(NK && BF)), "direct B: one K group");
-  static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
+  constexpr bool GP = BF || XH;   // exact codes and group partials (bf16, or fp16 with XH)
+  static_assert(!GP || KG == 1, "group partials: a quantization group's stages stay in one K group");
   constexpr int NBD = BD ? BK / 16 : 1;      // direct B words per lane and stage
   constexpr int A_PER_T = BM * CHUNKS / NTHR;
   static_assert((BM * CHUNKS) % NTHR == 0, "A staging");
@@ -227,7 +230,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   // path takes rows 4h .. 4h + 3 in the lane half h (K rows 32h + 8j .. + 7 at
   // step j); the bf16 path, whose group partials need each step inside one
   // quantization group, takes row 2j + h at step j.
-  constexpr bool KH = BD && !BF;   // the lane half's K rows are contiguous in the stage
+  constexpr bool KH = BD && !GP;   // the lane half's K rows are contiguous in the stage
   const uint32_t bd_voff = (uint32_t)((KH ? 4 * h : h) * N + min(wn * TN + 2 * c32, N - n0 - 2)) * 4;
   // direct B, [N, K/8]: words 4h .. 4h + 3 of the stage of the lane's two columns
   const int bdn_col = min(wn * TN + 2 * c32, N - n0 - 2);
@@ -327,7 +330,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
   const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
   // bf16: per row tile, the group partials of both column tiles and the
   // row-sum correction -136 * sum(a) (the same for every column)
-  constexpr int MP = BF ? MT : 1;
+  constexpr int MP = GP ? MT : 1;
   float16_t part[MP][2], corr[MP];
   auto clear_partials = [&]() {
 #pragma unroll
@@ -335,7 +338,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int e = 0; e < 16; ++e) part[i][0][e] = part[i][1][e] = corr[i][e] = 0.f;
   };
-  if constexpr (BF) clear_partials();
+  if constexpr (GP) clear_partials();
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
   // one stage (K offset k0) out of LDS buffer `buf` with the stage's scale pairs
   // (and direct B words)
@@ -356,7 +359,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
         afr[j][mt] = lds_a[buf][row * CHUNKS + swz(row, KH ? 4 * h + j : 2 * j + h)];
       }
     }
-    if constexpr (BF && MT <= 2) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GP && MT <= 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < BK / 16; ++j) {
       const uint64_t w2 = bwr[j];
@@ -365,9 +368,9 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t wd = (uint32_t)(w2 >> (32 * t));
-        if constexpr (BF) {
-          // 128 + q per half, exact; K-slot pairs (0,4), (1,5), (2,6), (3,7)
-          bq[t] = unpack_w4_word_natural<false>(wd, vmask, bias);
+        if constexpr (GP) {
+          // 128 + q (bf16) or q - 8 (fp16) per half, exact
+          bq[t] = unpack_w4_word_natural<!BF>(wd, vmask, bias);
         } else {
           const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
           const half2_t s2 = __builtin_bit_cast(half2_t, pair);
@@ -379,26 +382,26 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4_t av = afr[j][mt];
-        if constexpr (BF) {
-          part[mt][0] = mfma32x32x16_bf16(av, bq[0], part[mt][0]);
-          part[mt][1] = mfma32x32x16_bf16(av, bq[1], part[mt][1]);
-          corr[mt] = mfma32x32x16_bf16(av, u32x4_t{m136, m136, m136, m136}, corr[mt]);
+        if constexpr (GP) {
+          part[mt][0] = mfma32x32x16_t<BF>(av, bq[0], part[mt][0]);
+          part[mt][1] = mfma32x32x16_t<BF>(av, bq[1], part[mt][1]);
+          if constexpr (BF) corr[mt] = mfma32x32x16_bf16(av, u32x4_t{m136, m136, m136, m136}, corr[mt]);
         } else {
           acc[mt][0] = mfma32x32x16_f16(av, bq[0], acc[mt][0]);
           acc[mt][1] = mfma32x32x16_f16(av, bq[1], acc[mt][1]);
         }
       }
-      if constexpr (BF) {
+      if constexpr (GP) {
         // the quantization group ends with this 16-deep step: scale its partials
         // once (uniform test; steps past K hold zero activations)
         if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
-          const float s0 = bf2f((uint16_t)(sp & 0xFFFFu)), s1 = bf2f((uint16_t)(sp >> 16));
+          const float s0 = bits2f<BF>(sp & 0xFFFFu), s1 = bits2f<BF>(sp >> 16);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              acc[mt][0][e] += s0 * (part[mt][0][e] + corr[mt][e]);
-              acc[mt][1][e] += s1 * (part[mt][1][e] + corr[mt][e]);
+              acc[mt][0][e] += s0 * (BF ? part[mt][0][e] + corr[mt][e] : part[mt][0][e]);
+              acc[mt][1][e] += s1 * (BF ? part[mt][1][e] + corr[mt][e] : part[mt][1][e]);
             }
           clear_partials();
         }
@@ -539,7 +542,7 @@ __device__ __forceinline__ void w4_mfma_tile(uint16_t* __restrict__ C, const uin
 // XCD's run: 0 = M fastest, 1 = N fastest, else groups of `order` row panels
 // swept across N.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int PD, int KG, bool BF, bool NK = false,
-          bool BD = false>
+          bool BD = false, bool XH = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefill_v4_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
@@ -564,8 +567,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
     tm = first + r % gm;
     tn = r / gm;
   }
-  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK, BD>(C, A, B, S, M, N, K, group_size, tm * BM, tn * BN,
-                                                             lds, ep);
+  w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, NK, BD, XH>(C, A, B, S, M, N, K, group_size, tm * BM,
+                                                                 tn * BN, lds, ep);
 }
 
 // Direct-to-LDS form of the tile body for K a multiple of 64: a BM x 256 tile
@@ -596,7 +599,8 @@ struct W4DmaLds {
   uint32_t s[KG][NBUF][NK ? 2 * 256 : 2 * 128];
 };
 
-template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false, bool PART = false>
+template <int BM, int KG, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false, bool PART = false,
+          bool XH = false>
 __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint16_t* __restrict__ A,
                                             const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, int M,
                                             int N, int K, int group_size, int m0, int n0,
@@ -607,12 +611,13 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   constexpr int BW = 8 / WAVES;        // B wave loads (1 KiB) per stage and wave
   constexpr int SW = NK ? 8 / WAVES : 0;   // [N, K/gs] scales: 2-byte wave loads (64 columns) per wave
   static_assert(BM % (8 * WAVES) == 0 && TM % 32 == 0 && BW >= 1, "tile shape");
-  static_assert(!BF || KG == 1, "bf16: a quantization group's stages stay in one K group");
+  constexpr bool GP = BF || XH;   // exact codes and group partials (bf16, or fp16 with XH)
+  static_assert(!GP || KG == 1, "group partials: a quantization group's stages stay in one K group");
   // lane half h takes K rows 32h + 8j .. + 7 at 16-deep step j with one fp16 K
   // group (as the register-staged tile with direct B does), else rows
   // 16j + 8h .. + 7 (as its staged-B and bf16 forms do: a bf16 step stays in one
   // quantization group), so both weight layouts give the same results bit for bit
-  constexpr bool KH = KG == 1 && !BF;
+  constexpr bool KH = KG == 1 && !GP;
   const int lane = threadIdx.x & 63;
   const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kg = wave_all / WAVES;   // K group
@@ -712,7 +717,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   const uint32_t bias = __builtin_amdgcn_readfirstlane(BF ? 0x43004300u : 0x64006400u);
   // bf16: per row tile, the group partials of both column tiles and the
   // row-sum correction -136 * sum(a) (the same for every column)
-  constexpr int MP = BF ? MT : 1;
+  constexpr int MP = GP ? MT : 1;
   float16_t part[MP][2], corr[MP];
   auto clear_partials = [&]() {
 #pragma unroll
@@ -720,7 +725,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 #pragma unroll
       for (int e = 0; e < 16; ++e) part[i][0][e] = part[i][1][e] = corr[i][e] = 0.f;
   };
-  if constexpr (BF) clear_partials();
+  if constexpr (GP) clear_partials();
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
   // PART (routed tiles): a wave does no arithmetic when its column strip lies
@@ -799,8 +804,8 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t wd = (uint32_t)(w2 >> (32 * t));
-        if constexpr (BF) {
-          bq[t] = unpack_w4_word_natural<false>(wd, vmask, bias);   // 128 + q, exact
+        if constexpr (GP) {
+          bq[t] = unpack_w4_word_natural<!BF>(wd, vmask, bias);   // 128 + q (bf16) or q - 8 (fp16), exact
         } else {
           const uint32_t pair = __builtin_amdgcn_perm(sp, sp, t ? 0x03020302u : 0x01000100u);
           const half2_t s2 = __builtin_bit_cast(half2_t, pair);
@@ -811,26 +816,26 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       }
 #pragma unroll
       for (int mt = 0; mt < ME; ++mt) {
-        if constexpr (BF) {
-          part[mt][0] = mfma32x32x16_bf16(afr[j][mt], bq[0], part[mt][0]);
-          part[mt][1] = mfma32x32x16_bf16(afr[j][mt], bq[1], part[mt][1]);
-          corr[mt] = mfma32x32x16_bf16(afr[j][mt], u32x4_t{m136, m136, m136, m136}, corr[mt]);
+        if constexpr (GP) {
+          part[mt][0] = mfma32x32x16_t<BF>(afr[j][mt], bq[0], part[mt][0]);
+          part[mt][1] = mfma32x32x16_t<BF>(afr[j][mt], bq[1], part[mt][1]);
+          if constexpr (BF) corr[mt] = mfma32x32x16_bf16(afr[j][mt], u32x4_t{m136, m136, m136, m136}, corr[mt]);
         } else {
           acc[mt][0] = mfma32x32x16_f16(afr[j][mt], bq[0], acc[mt][0]);
           acc[mt][1] = mfma32x32x16_f16(afr[j][mt], bq[1], acc[mt][1]);
         }
       }
-      if constexpr (BF) {
+      if constexpr (GP) {
         // the quantization group ends with this 16-deep step: scale its partials
         // once (uniform test)
         if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
-          const float s0 = bf2f((uint16_t)(sp & 0xFFFFu)), s1 = bf2f((uint16_t)(sp >> 16));
+          const float s0 = bits2f<BF>(sp & 0xFFFFu), s1 = bits2f<BF>(sp >> 16);
 #pragma unroll
           for (int mt = 0; mt < ME; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              acc[mt][0][e] += s0 * (part[mt][0][e] + corr[mt][e]);
-              acc[mt][1][e] += s1 * (part[mt][1][e] + corr[mt][e]);
+              acc[mt][0][e] += s0 * (BF ? part[mt][0][e] + corr[mt][e] : part[mt][0][e]);
+              acc[mt][1][e] += s1 * (BF ? part[mt][1][e] + corr[mt][e] : part[mt][1][e]);
             }
           clear_partials();
         }
@@ -855,7 +860,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     if (more) issue(kg + KG * (t + NBUF - 1), (buf + NBUF - 1) % NBUF);
     if (valid(t)) {
       const int k0 = (kg + KG * t) * BK;
-      if constexpr (PART && !BF) {
+      if constexpr (PART && !GP) {
         if (live_mt == MT) compute(buf, k0, std::integral_constant<int, MT>{});
         else if (live_mt > 0) compute(buf, k0, std::integral_constant<int, 1>{});
       } else if constexpr (PART) {
@@ -911,7 +916,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
 }
 
 // Dense kernel of the direct-to-LDS tile body (tile order as in w4_prefill_v4_kernel).
-template <int KG, int MINB, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false>
+template <int KG, int MINB, int NBUF, int WAVES_M = 1, bool BF = false, bool NK = false, bool XH = false>
 __global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ B,
     const uint16_t* __restrict__ S, int M, int N, int K, int group_size, int tiles_m, int tiles_n, int order,
@@ -926,7 +931,8 @@ __global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma
   const int gm = min(tiles_m - first, order);
   const int r = lin % span;
   const int tm = first + r % gm, tn = r / gm;
-  w4_tile_dma<128, KG, NBUF, WAVES_M, BF, NK>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256, lds, ep);
+  w4_tile_dma<128, KG, NBUF, WAVES_M, BF, NK, false, XH>(C, A, B, S, M, N, K, group_size, tm * 128, tn * 256,
+                                                          lds, ep);
 }
 
 // Grouped (MoE) W4A16 GEMM on the same tiles: group g (expert ids[g] >= 0,
@@ -938,7 +944,8 @@ __global__ __launch_bounds__(4 * WAVES_M * kWave * KG, MINB) void w4_prefill_dma
 // holds an upper bound on the tile count (only the device knows the group
 // sizes); the real count is split evenly over the eight XCDs, at most
 // ceil(count / 8) <= grid / 8 tiles each, and workgroups past their XCD's run exit.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD, bool BF, bool DMA = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MINB, int KG, int PD, bool BD, bool BF, bool DMA = false,
+          bool XH = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_grouped_kernel(
     uint16_t* __restrict__ C, const uint16_t* __restrict__ A, const uint32_t* __restrict__ a_off,
     const uint32_t* __restrict__ B, const uint16_t* __restrict__ S, const int32_t* __restrict__ ids, int N, int K,
@@ -968,10 +975,10 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
   if (ep.flags & EPI_BIAS) ept.bias = ep.bias + (size_t)e * N;
   if (ep.flags & EPI_RESIDUAL) ept.residual = ep.residual + (size_t)r_begin * NO;
   if constexpr (DMA)
-    w4_tile_dma<BM, 1, 3, 1, BF, false, true>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe,
+    w4_tile_dma<BM, 1, 3, 1, BF, false, true, XH>(C + (size_t)r_begin * NO, A + (size_t)r_begin * K, B + e * wpe,
                                               S + e * spe, rows, N, K, group_size, 0, nt * BN, lds, ept);
   else
-    w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD>(C + (size_t)r_begin * NO,
+    w4_mfma_tile<BM, BN, WAVES_M, WAVES_N, PD, KG, BF, false, BD, XH>(C + (size_t)r_begin * NO,
                                                                      A + (size_t)r_begin * K, B + e * wpe,
                                                                      S + e * spe, rows, N, K, group_size, 0,
                                                                      nt * BN, lds, ept);
@@ -983,8 +990,11 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
 // loaded straight into the lanes' registers (one wave per column strip, so no
 // B word is shared): fp16 with three workgroups per CU, two stages of loads in
 // flight; bf16 (exact codes, a group partial and a row-sum correction beside
-// each accumulator) with two workgroups per CU, one stage in flight.
-template <int MINB, int PD, bool BF, bool DMA = false>
+// each accumulator) with two workgroups per CU, one stage in flight. fp16 with
+// the SiLU gate (XH) takes the bf16 form with exact (q - 8) fp16 codes and no
+// correction, so the gated outputs see exact weights as well: the gate would
+// magnify the rounding of each weight to fp16.
+template <int MINB, int PD, bool BF, bool DMA = false, bool XH = false>
 static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream) {
   constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KG = 1;
   constexpr bool BD = true;
@@ -993,7 +1003,7 @@ static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream
   const long long bound = ((p.T + BM - 1) / BM + p.num_active) * (long long)tiles_n;
   if (bound > INT32_MAX / 2) return hipErrorNotSupported;
   const int grid = (int)((bound + 7) / 8 * 8);
-  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD, BF, DMA>), dim3(grid),
+  hipLaunchKernelGGL((w4_grouped_kernel<BM, BN, WM, WN, MINB, KG, PD, BD, BF, DMA, XH>), dim3(grid),
                      dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.a_offsets, p.B, p.S, p.expert_ids, (int)p.N,
                      (int)p.K, p.group_size, p.num_active, tiles_n, p.epi);
   return hipGetLastError();
@@ -1002,6 +1012,9 @@ static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream
 hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
   if (p.bf16) return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, true, true>(p, stream)
                                    : launch_w4_grouped_t<2, 1, true>(p, stream);
+  if (p.epi.flags & EPI_SILU_GATE)
+    return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, false, true, true>(p, stream)
+                         : launch_w4_grouped_t<2, 1, false, false, true>(p, stream);
   if (p.K % BK == 0) return launch_w4_grouped_t<3, 2, false, true>(p, stream);   // fp16, whole stages: direct-to-LDS
   return launch_w4_grouped_t<3, 2, false>(p, stream);
 }
@@ -1016,15 +1029,18 @@ constexpr int kPanelGroup = 4;
 // CU, or (at most one tile per CU) one workgroup of two K groups per CU. bf16:
 // eight 64 x 64 wave tiles (two waves per column strip), one workgroup per CU:
 // the exact-code path keeps a group partial and a row-sum correction beside
-// each accumulator, which leaves no registers for a second workgroup.
-template <int WM, int MINB, int KG, bool BF, bool NK>
+// each accumulator, which leaves no registers for a second workgroup. fp16 with
+// the SiLU gate (XH): the same tiles with exact (q - 8) fp16 codes and fp32
+// group partials (no correction), so that the gate does not magnify a rounding
+// of the weights.
+template <int WM, int MINB, int KG, bool BF, bool NK, bool XH = false>
 static void launch_v4(const W4Args& p, hipStream_t stream, int tm, int tn) {
   // one K group of waves with a column strip each (fp16): B words go straight
   // into the lanes' registers, two stages ahead
-  constexpr bool BD = (KG == 1 && !BF && WM == 1);
+  constexpr bool BD = (KG == 1 && !BF && !XH && WM == 1);
   constexpr int BM = 128, BN = 256, WN = 4, PD = BD ? 2 : 1;
   const int grid = ((tm * tn + 7) / 8) * 8;
-  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK, BD>), dim3(grid),
+  hipLaunchKernelGGL((w4_prefill_v4_kernel<BM, BN, WM, WN, MINB, PD, KG, BF, NK, BD, XH>), dim3(grid),
                      dim3(WM * WN * kWave * KG), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N, (int)p.K,
                      p.group_size, tm, tn, kPanelGroup, p.epi);
 }
@@ -1040,10 +1056,15 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(waves * kWave), 0, stream, p.C, p.A, p.B, p.S, (int)p.M, (int)p.N,
                        (int)p.K, p.group_size, tm, tn, kPanelGroup, p.epi);
   };
+  // fp16 with the SiLU gate: exact weights as on the bf16 path (the [N, K/8]
+  // layout has no epilogue)
+  const bool xh = !p.bf16 && (p.epi.flags & EPI_SILU_GATE) != 0;
   if (p.K % BK == 0) {
     if (p.bf16) {
       if (p.nk) dma(w4_prefill_dma_kernel<1, 1, 3, 2, true, true>, 8);
       else dma(w4_prefill_dma_kernel<1, 1, 3, 2, true, false>, 8);
+    } else if (xh) {
+      dma(w4_prefill_dma_kernel<1, 1, 3, 2, false, false, true>, 8);
     } else if (one_pass) {
       if (p.nk) dma(w4_prefill_dma_kernel<2, 1, 3, 1, false, true>, 8);
       else dma(w4_prefill_dma_kernel<2, 1, 3, 1, false, false>, 8);
@@ -1057,6 +1078,8 @@ hipError_t launch_w4_prefill(const W4Args& p, int num_cus, hipStream_t stream) {
   if (p.bf16) {
     if (p.nk) launch_v4<2, 1, 1, true, true>(p, stream, tm, tn);
     else launch_v4<2, 1, 1, true, false>(p, stream, tm, tn);
+  } else if (xh) {
+    launch_v4<2, 1, 1, false, false, true>(p, stream, tm, tn);
   } else if (p.nk) {
     if (one_pass) launch_v4<1, 1, 2, false, true>(p, stream, tm, tn);
     else launch_v4<1, 2, 1, false, true>(p, stream, tm, tn);

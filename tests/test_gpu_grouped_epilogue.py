@@ -7,11 +7,10 @@ the bias row of the group's expert (bias [E, N]), a SiLU-gated product of column
 pairs (2j, 2j+1) that halves N, a residual add, all before the one rounding.
 
 Bars: routing (which rows are written) and every untouched row bit-exact;
-bias / residual outputs within 1e-2 (|oracle| + 1); gated outputs within that
-bar carried through the gate from the GEMM results (the bound of
-test_gpu_w4_epilogue: 1.1 |u| tau_g + (|silu g| + 1.1 tau_g) tau_u plus the bar
-on the output, tau = 1e-2 (|.| + 1)); and, for the bf16 GEMM whose values are
-small next to the bar's floor, a relative RMS error below 3e-3 over the rows.
+every written output within 1e-2 (|oracle| + 1), gated ones included (every
+kernel that computes a gated output keeps the weights exact in its MFMAs); and,
+for the bf16 GEMM whose values are small next to the bar's floor, a relative RMS
+error below 3e-3 over the rows.
 """
 
 import numpy as np
@@ -29,37 +28,7 @@ BIAS, RES, GATE = oracle.EPI_BIAS, oracle.EPI_RESIDUAL, oracle.EPI_SILU_GATE
 SENT = {"bf16": 0xFFC1, "f16": 0x7E00}
 
 
-def exact_products(a, w_of, a_off, ids, usage):
-    """float64 rows of the processed groups (NaN elsewhere): A[rows] . W_e."""
-    T = a.shape[0]
-    y = None
-    for g in range(int(usage[1])):
-        e = int(ids[g])
-        r0, r1 = int(a_off[g]), int(a_off[g + 1])
-        if e < 0 or r1 <= r0:
-            continue
-        p = a[r0:r1] @ w_of(e)
-        if y is None:
-            y = np.full((T, p.shape[1]), np.nan)
-        y[r0:r1] = p
-    return y
-
-
-def tolerance(y, flags, bias_rows, ref, carry_gate=True):
-    """Per-element bound for the written rows (ref decoded, y the exact product);
-    carry_gate=False keeps the common bar for gated outputs too (GEMMs whose
-    weights enter the MFMAs exactly)."""
-    if flags & BIAS:
-        y = y + bias_rows
-    base = REL * (np.abs(ref) + 1.0)
-    if not flags & GATE or not carry_gate:
-        return base
-    g, u = y[:, 0::2], y[:, 1::2]
-    tg, tu = REL * (np.abs(g) + 1.0), REL * (np.abs(u) + 1.0)
-    return 1.1 * np.abs(u) * tg + (np.abs(oracle.silu(g)) + 1.1 * tg) * tu + base
-
-
-def compare(got, ref, sent, dec, y, flags, bias_rows_fn, what, rel_rms=None, carry_gate=True):
+def compare(got, ref, sent, dec, what, rel_rms=None):
     written = ref[:, 0] != sent
     assert np.array_equal(got[:, 0] != sent, written), f"{what}: row routing differs"
     assert np.all(got[~written] == sent), f"{what}: rows outside the groups changed"
@@ -67,22 +36,15 @@ def compare(got, ref, sent, dec, y, flags, bias_rows_fn, what, rel_rms=None, car
         return {}
     g, r = dec(got[written]), dec(ref[written])
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
-    tol = tolerance(y[written], flags, bias_rows_fn(written), r, carry_gate)
+    tol = REL * (np.abs(r) + 1.0)
     err = np.abs(g - r)
     bad = err > tol
-    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the tolerance, first {np.argwhere(bad)[:3].tolist()}"
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the tolerance, first "
+                           f"{np.argwhere(bad)[:3].tolist()}, worst {float((err / tol).max()):.3f} x bound")
     rms = float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(r ** 2)), 1e-30))
     if rel_rms is not None:
         assert rms < rel_rms, f"{what}: relative RMS error {rms:.2e}"
-    return {"rel_rms": rms}
-
-
-def row_expert(a_off, ids, usage, T):
-    e_of = np.full(T, -1)
-    for g in range(int(usage[1])):
-        if ids[g] >= 0:
-            e_of[int(a_off[g]):int(a_off[g + 1])] = ids[g]
-    return e_of
+    return {"rel_rms": rms, "worst_over_bar": float((err / tol).max())}
 
 
 # ---------------------------------------------------------------- bf16 experts
@@ -107,13 +69,7 @@ def run_bf16(lib, d, flags, seed, transpose_b=True, a_off=None, ids=None, usage=
     c0 = np.full((T, n_out), SENT["bf16"], np.uint16)
     ref = oracle.grouped_gemm(c0, d.a, a_off, b, ids, usage, transpose_b=transpose_b, epilogue=flags,
                               bias_bits=bias, residual_bits=res)
-    a = nm.decode_bf16(d.a)
-    wb = nm.decode_bf16(d.b)
-    y = exact_products(a, lambda e: wb[e].T, a_off, ids, usage)
-    e_of = row_expert(a_off, ids, usage, T)
-    bf = nm.decode_bf16(bias)
-    return compare(got, ref, SENT["bf16"], nm.decode_bf16, y, flags, lambda w: bf[e_of[w]],
-                   f"bf16 flags={flags} tb={transpose_b}", rel_rms=3e-3)
+    return compare(got, ref, SENT["bf16"], nm.decode_bf16, f"bf16 flags={flags} tb={transpose_b}", rel_rms=3e-3)
 
 
 @pytest.mark.parametrize("flags", range(1, 8))
@@ -148,8 +104,8 @@ def test_bf16_edges_and_full_size(gpu, lib):
 # ---------------------------------------------------------------- W4 experts
 
 def run_w4(lib, d, flags, seed, a_off=None, ids=None, usage=None):
-    """fp16 or bf16 (d.dtype). The bf16 kernel keeps the 4-bit weights exact in its
-    MFMAs, so its gated outputs are held to the common bar."""
+    """fp16 or bf16 (d.dtype). Gated outputs come from kernels that keep the 4-bit
+    weights exact in their MFMAs (both types), so every output has the common bar."""
     a_off = d.a_offsets if a_off is None else a_off
     ids = d.expert_ids if ids is None else ids
     usage = d.usage if usage is None else usage
@@ -171,18 +127,7 @@ def run_w4(lib, d, flags, seed, a_off=None, ids=None, usage=None):
     c0 = np.full((T, n_out), sent, np.uint16)
     ref = oracle.grouped_gemm_w4(c0, d.a, a_off, d.b, d.scales, ids, usage, d.group_size, epilogue=flags,
                                  bias_bits=bias, residual_bits=res, dtype=d.dtype)
-    a = dec(d.a)
-    cache = {}
-
-    def w_of(e):
-        if e not in cache:
-            cache[e] = oracle.w4.dequant_w4(d.b[e], d.scales[e], d.group_size, dtype=d.dtype)
-        return cache[e]
-    y = exact_products(a, w_of, a_off, ids, usage)
-    e_of = row_expert(a_off, ids, usage, T)
-    bf = dec(bias)
-    return compare(got, ref, sent, dec, y, flags, lambda w: bf[e_of[w]], f"w4 {d.dtype} flags={flags}",
-                   carry_gate=not bf16)
+    return compare(got, ref, sent, dec, f"w4 {d.dtype} flags={flags}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

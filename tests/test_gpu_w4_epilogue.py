@@ -6,17 +6,14 @@ fixed steps in its place: bias over columns, a SiLU-gated product of column
 pairs (2j, 2j+1) that halves N, and a residual add, all on the fp32 product
 before its one rounding.
 
-Tolerance. Every output: the common bar |gpu - oracle| <= 1e-2 (|oracle| + 1)
-per element, with one exception. The fp16 prefill path rounds each weight
-(q - 8) s to fp16 before its MFMAs (the other paths keep the weights exact and
-scale fp32 group partials), and a gated output z = silu(g) u amplifies that
-GEMM error: with g ~ 8 and u ~ 0.2 the weight rounding alone moves z by more
-than 1e-2 (|z| + 1) (seen on the full-size prefill, and reproduced on the CPU
-by rounding the weights to fp16 before an exact product). For gated outputs of
-that path the common bar is put on the GEMM result (tau_g = 1e-2 (|g| + 1),
-tau_u likewise) and carried through the gate to first order with silu' in
-[-0.1, 1.1]: 1.1 |u| tau_g + (|silu(g)| + 1.1 tau_g) tau_u, plus the common bar
-on z itself.
+Tolerance: every output, gated or not, within the common bar
+|gpu - oracle| <= 1e-2 (|oracle| + 1) per element. The plain fp16 prefill path
+rounds each weight (q - 8) s to fp16 before its MFMAs; a gated output
+z = silu(g) u would magnify that rounding (with g ~ 8 and u ~ 0.2 it alone moves
+z past the bar on the full-size prefill, as rounding the weights to fp16 before
+an exact product shows on the CPU), so gated fp16 outputs come from the
+exact-weight path that bf16 also uses (1024 + q in the MFMAs, a -1032 row-sum
+correction, fp32 group partials scaled once).
 """
 import numpy as np
 import pytest
@@ -57,17 +54,6 @@ def run_epi(lib, w, flags, bias, res):
     return got
 
 
-def gate_tolerance(w, flags, bias, r, rows=None):
-    """The common bar on the gate's inputs, carried through the gate, plus the bar on z."""
-    a_bits = w.a if rows is None else w.a[rows]
-    y = oracle.w4.qgemm_w4_f64(a_bits, w.b, w.scales, w.group_size, dtype=w.dtype)
-    if flags & BIAS:
-        y = y + DEC[w.dtype](bias)[None, :]
-    g, u = y[:, 0::2], y[:, 1::2]
-    tg, tu = REL * (np.abs(g) + 1.0), REL * (np.abs(u) + 1.0)
-    return 1.1 * np.abs(u) * tg + (np.abs(oracle.silu(g)) + 1.1 * tg) * tu + REL * (np.abs(r) + 1.0)
-
-
 def check(lib, w, flags, seed, what, rows=None):
     M, N, K = w.shape
     say(f"[w4-epi] {what}: M={M} N={N} K={K} gs={w.group_size} {w.dtype} flags={flags}")
@@ -81,10 +67,7 @@ def check(lib, w, flags, seed, what, rows=None):
     dec = DEC[w.dtype]
     g, r = dec(got), dec(ref)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
-    if flags & GATE and w.dtype == "f16" and M > 16:
-        b = gate_tolerance(w, flags, bias, r, rows)
-    else:
-        b = REL * (np.abs(r) + 1.0)
+    b = REL * (np.abs(r) + 1.0)
     err = np.abs(g - r)
     bad = err > b
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond the tolerance, first "
