@@ -46,13 +46,6 @@ __device__ __forceinline__ float16_t mfma32x32x16_bf16(u32x4_t a, u32x4_t b, flo
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// The 32x32x16 MFMA of the operand type: bf16 (BF) or fp16.
-template <bool BF>
-__device__ __forceinline__ float16_t mfma32x32x16_t(u32x4_t a, u32x4_t b, float16_t c) {
-  if constexpr (BF) return mfma32x32x16_bf16(a, b, c);
-  else return mfma32x32x16_f16(a, b, c);
-}
-
 // Raw buffer access: a 128-bit descriptor (base, size in bytes) in SGPRs, a
 // per-lane byte offset in one VGPR and a uniform byte offset in an SGPR, so a
 // loop of loads that advance together costs no per-load 64-bit address math.

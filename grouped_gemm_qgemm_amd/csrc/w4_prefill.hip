@@ -26,6 +26,13 @@ constexpr int CHUNKS = BK / 8;    // 16-byte chunks per A row in LDS
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
+// The 32x32x16 MFMA of the operand type: bf16 (BF) or fp16.
+template <bool BF>
+__device__ __forceinline__ float16_t mfma32x32x16_t(u32x4_t a, u32x4_t b, float16_t c) {
+  if constexpr (BF) return mfma32x32x16_bf16(a, b, c);
+  else return mfma32x32x16_f16(a, b, c);
+}
+
 }  // namespace
 
 // LDS of one tile: per K group, two stages of A chunks and of packed B (no B
