@@ -74,21 +74,21 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
     "decode": (9240453, "76549ddc9471fadf"),
-    "prefill": (224961818, "75b7b65ab71659dd"),
-    "square": (85237833, "75b7b65ab71659dd"),
+    "prefill": (225261120, "1c99bb8aebe1f4eb"),
+    "square": (85234442, "1c99bb8aebe1f4eb"),
     "grouped": (367974254, "f021ee2cd95f4c65"),
     "grouped_kn": (365920284, "f021ee2cd95f4c65"),
-    "grouped_w4": (114093044, "75b7b65ab71659dd"),
+    "grouped_w4": (114153582, "1c99bb8aebe1f4eb"),
     "kproj": (85680489, "5ee8476366591581"),
     "decode_gate": (9252737, "76549ddc9471fadf"),
-    "prefill_gate": (224442766, "75b7b65ab71659dd"),
+    "prefill_gate": (245812155, "1c99bb8aebe1f4eb"),
     "decode_bf16": (9230896, "76549ddc9471fadf"),
-    "prefill_bf16": (245728636, "75b7b65ab71659dd"),
+    "prefill_bf16": (245757050, "1c99bb8aebe1f4eb"),
     "decode_nk": (9234587, "76549ddc9471fadf"),
-    "prefill_nk": (221526728, "75b7b65ab71659dd"),
+    "prefill_nk": (221288989, "1c99bb8aebe1f4eb"),
     "kvproj": (202264507, "5ee8476366591581"),
     "kvproj_e4m3": (193908141, "5ee8476366591581"),
-    "grouped_w4_bf16": (114006715, "75b7b65ab71659dd"),
+    "grouped_w4_bf16": (113990333, "1c99bb8aebe1f4eb"),
     "kproj_e4m3h": (64451824, "5ee8476366591581"),
 }
 
