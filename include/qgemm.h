@@ -144,7 +144,10 @@ qg_status qgemm_w4_nk(const qg_tensor* c, const qg_tensor* a, const qg_tensor* b
  * bias and residual have the activations' type (fp16 or bf16) and may be NULL
  * when their operation is not requested (QG_ERR_NULL otherwise). Other flag bits
  * are QG_ERR_INVALID_ARG; with QG_EPI_SILU_GATE, N must be a multiple of 16
- * (QG_ERR_ALIGN). Everything else as qgemm_w4; epilogue 0 is qgemm_w4.
+ * (QG_ERR_ALIGN). With QG_EPI_SILU_GATE every kernel keeps the weights
+ * (q - 8) * scale exact (fp32 group partials scaled once), fp16 prefill
+ * included, since the gate would magnify a rounding of the weights. Everything
+ * else as qgemm_w4; epilogue 0 is qgemm_w4.
  */
 #define QG_EPI_BIAS 1
 #define QG_EPI_RESIDUAL 2
@@ -252,8 +255,9 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
 /*
  * grouped_gemm_w4_epilogue - grouped_gemm_w4 with the fixed epilogue of
  * grouped_gemm_epilogue (bias [E, N], residual [T, N_out], c [T, N_out], all of
- * the activation type). Everything else as grouped_gemm_w4; epilogue 0 is
- * grouped_gemm_w4.
+ * the activation type). With QG_EPI_SILU_GATE the fp16 kernel keeps the
+ * weights exact as the bf16 one does (fp32 group partials scaled once).
+ * Everything else as grouped_gemm_w4; epilogue 0 is grouped_gemm_w4.
  */
 qg_status grouped_gemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                    const qg_tensor* b_packed, const qg_tensor* scales,
