@@ -736,7 +736,8 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
   // PART (routed tiles): a wave does no arithmetic when its column strip lies
-  // wholly past N and (fp16) skips the fragment reads and MFMAs of a row tile
+  // wholly past N and (rounded fp16 weights only: the group-partial forms spill
+  // with a second instance) skips the fragment reads and MFMAs of a row tile
   // wholly past the tile's rows; the loads and barriers stay the same. ME row
   // tiles are multiplied (MT, or 1 when at most 32 rows are real).
   static_assert(!PART || (MT == 2 && KG == 1), "partial tiles: two row tiles, one K group");
@@ -991,16 +992,14 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_group
                                                                      nt * BN, lds, ept);
 }
 
-// Grouped launch: 64-row chunks of a group by 256 columns. fp16 with K a
-// multiple of 64: the direct-to-LDS tile, three workgroups per CU (three stage
-// buffers of 17 KiB each). Otherwise the register-staged tile with B words
-// loaded straight into the lanes' registers (one wave per column strip, so no
-// B word is shared): fp16 with three workgroups per CU, two stages of loads in
-// flight; bf16 (exact codes, a group partial and a row-sum correction beside
-// each accumulator) with two workgroups per CU, one stage in flight. fp16 with
-// the SiLU gate (XH) takes the bf16 form with exact (q - 8) fp16 codes and no
-// correction, so the gated outputs see exact weights as well: the gate would
-// magnify the rounding of each weight to fp16.
+// Grouped launch: 64-row chunks of a group by 256 columns, both types with
+// exact weights: bf16 (128 + q codes, a group partial and a row-sum correction
+// beside each accumulator) and fp16 (XH: exact (q - 8) codes and a group
+// partial, no correction; within 3 % of rounding each weight to fp16 per
+// launch), two workgroups per CU. K a multiple of 64: the direct-to-LDS tile
+// (three stage buffers); otherwise the register-staged tile with B words loaded
+// straight into the lanes' registers (one wave per column strip, so no B word
+// is shared), one stage in flight.
 template <int MINB, int PD, bool BF, bool DMA = false, bool XH = false>
 static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream) {
   constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KG = 1;
@@ -1019,11 +1018,8 @@ static hipError_t launch_w4_grouped_t(const W4GroupedArgs& p, hipStream_t stream
 hipError_t launch_w4_grouped(const W4GroupedArgs& p, hipStream_t stream) {
   if (p.bf16) return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, true, true>(p, stream)
                                    : launch_w4_grouped_t<2, 1, true>(p, stream);
-  if (p.epi.flags & EPI_SILU_GATE)
-    return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, false, true, true>(p, stream)
-                         : launch_w4_grouped_t<2, 1, false, false, true>(p, stream);
-  if (p.K % BK == 0) return launch_w4_grouped_t<3, 2, false, true>(p, stream);   // fp16, whole stages: direct-to-LDS
-  return launch_w4_grouped_t<3, 2, false>(p, stream);
+  return p.K % BK == 0 ? launch_w4_grouped_t<2, 1, false, true, true>(p, stream)
+                       : launch_w4_grouped_t<2, 1, false, false, true>(p, stream);
 }
 
 // Row panels per group of the dense tile order: each XCD takes a contiguous run

@@ -241,9 +241,9 @@ qg_status grouped_gemm_epilogue(const qg_tensor* c, const qg_tensor* a, const qg
  *
  * a, scales and c share one type (the W4 page's a_type and c_type; QG_ERR_DTYPE
  * when they differ). N must be a multiple of 8 (QG_ERR_ALIGN). Accumulation is
- * fp32; results are rounded to the output type (nearest-even). With fp16 each
- * weight (q - 8) * scale is rounded to fp16 before the MFMAs; with bf16 the
- * codes enter the MFMAs exactly and each group's fp32 partial is scaled once.
+ * fp32; results are rounded to the output type (nearest-even). In both types
+ * the codes enter the MFMAs exactly and each group's fp32 partial is scaled
+ * once (no weight is rounded).
  * The device-side tables are not re-validated: offsets past T, or expert ids
  * >= E, are undefined behaviour.
  */
@@ -255,9 +255,8 @@ qg_status grouped_gemm_w4(const qg_tensor* c, const qg_tensor* a, const qg_tenso
 /*
  * grouped_gemm_w4_epilogue - grouped_gemm_w4 with the fixed epilogue of
  * grouped_gemm_epilogue (bias [E, N], residual [T, N_out], c [T, N_out], all of
- * the activation type). With QG_EPI_SILU_GATE the fp16 kernel keeps the
- * weights exact as the bf16 one does (fp32 group partials scaled once).
- * Everything else as grouped_gemm_w4; epilogue 0 is grouped_gemm_w4.
+ * the activation type). Everything else as grouped_gemm_w4; epilogue 0 is
+ * grouped_gemm_w4.
  */
 qg_status grouped_gemm_w4_epilogue(const qg_tensor* c, const qg_tensor* a, const qg_tensor* a_offsets,
                                    const qg_tensor* b_packed, const qg_tensor* scales,
