@@ -12,7 +12,10 @@
 // 4-bit codes unpacked in VGPRs. Its comment below gives the details. When K
 // is a multiple of 64 (whole stages), both kernels use a direct-to-LDS form of
 // the tile (w4_tile_dma): every operand of a stage goes from global memory
-// straight into LDS, three stages deep.
+// straight into LDS, three stages deep. Dense fp16 calls without the SiLU gate
+// round each weight (q - 8) * scale to fp16; every other form (bf16, gated
+// fp16, the grouped kernel in both types) keeps the codes exact and scales fp32
+// group partials.
 #include "device_common.h"
 #include "launch.h"
 
@@ -580,8 +583,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * kWave * KG, MINB) void w4_prefi
 
 // Direct-to-LDS form of the tile body for K a multiple of 64: a BM x 256 tile
 // (BM = 128 or 64) per K group of 4 WAVES_M waves (TM x 64 wave tiles), fp16 or
-// bf16 (BF: exact codes, group partials as in w4_mfma_tile), weights [K/8, N]
-// or [N, K/8] (NK).
+// bf16 (BF: exact codes, group partials as in w4_mfma_tile) or fp16 with exact
+// codes and group partials (XH), weights [K/8, N] or [N, K/8] (NK).
 //   * Every stage's A rows (BM x 128 B), packed B words (8 KiB) and the scales
 //     of its two 32-deep halves go from global memory straight into LDS with
 //     global_load_lds (lane l of a 16-byte wave load fills bytes 16 l .. + 15 of
