@@ -412,3 +412,16 @@ def test_compute_probe_rejections(lib):
     assert lib.qg_empty_launch(0, 64, None) == QG.ERR_INVALID_ARG
     assert lib.qg_empty_launch(4, 0, None) == QG.ERR_INVALID_ARG
     assert lib.qg_empty_launch(4, 1025, None) == QG.ERR_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so,
+    before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout and "--gpus 1" in r.stderr
