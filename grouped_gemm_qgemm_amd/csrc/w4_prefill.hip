@@ -738,16 +738,11 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   if constexpr (GP) clear_partials();
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
-  // PART (routed tiles): a wave does no arithmetic when its column strip lies
-  // wholly past N and (rounded fp16 weights only: the group-partial forms spill
-  // with a second instance) skips the fragment reads and MFMAs of a row tile
-  // wholly past the tile's rows; the loads and barriers stay the same. ME row
-  // tiles are multiplied (MT, or 1 when at most 32 rows are real).
-  static_assert(!PART || (MT == 2 && KG == 1), "partial tiles: two row tiles, one K group");
-  const int live_mt = __builtin_amdgcn_readfirstlane(
-      n0 + wn * 64 >= N ? 0 : min(MT, max(0, (rows - wm * TM + 31) / 32)));
-  auto compute = [&](int buf, int k0, auto me) {
-    constexpr int ME = decltype(me)::value;
+  // PART (routed tiles): a wave whose column strip lies wholly past N does no
+  // arithmetic; its loads and barriers stay the same.
+  static_assert(!PART || KG == 1, "partial tiles: one K group");
+  const bool strip_live = n0 + wn * 64 < N;   // uniform
+  auto compute = [&](int buf, int k0) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds.b[kg][buf]);
     u32x4_t afr[BK / 16][MT];
     uint64_t bwr[BK / 16];
@@ -792,7 +787,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
     for (int j = 0; j < BK / 16; ++j) {
       const int kc = KH ? 4 * h + j : 2 * j + h;
 #pragma unroll
-      for (int mt = 0; mt < ME; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const int row = wm * TM + mt * 32 + c32;
         afr[j][mt] = lds.a[kg][buf][row * CHUNKS + swz(row, kc)];
       }
@@ -826,7 +821,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < ME; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         if constexpr (GP) {
           part[mt][0] = mfma32x32x16_t<BF>(afr[j][mt], bq[0], part[mt][0]);
           part[mt][1] = mfma32x32x16_t<BF>(afr[j][mt], bq[1], part[mt][1]);
@@ -842,7 +837,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
         if (((k0 + 16 * (j + 1)) & (group_size - 1)) == 0) {
           const float s0 = bits2f<BF>(sp & 0xFFFFu), s1 = bits2f<BF>(sp >> 16);
 #pragma unroll
-          for (int mt = 0; mt < ME; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               acc[mt][0][e] += s0 * (BF ? part[mt][0][e] + corr[mt][e] : part[mt][0][e]);
@@ -869,17 +864,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   auto stage = [&](int t, int buf) {
     const bool more = valid(t + NBUF - 1);
     if (more) issue(kg + KG * (t + NBUF - 1), (buf + NBUF - 1) % NBUF);
-    if (valid(t)) {
-      const int k0 = (kg + KG * t) * BK;
-      if constexpr (PART && !GP) {
-        if (live_mt == MT) compute(buf, k0, std::integral_constant<int, MT>{});
-        else if (live_mt > 0) compute(buf, k0, std::integral_constant<int, 1>{});
-      } else if constexpr (PART) {
-        if (live_mt > 0) compute(buf, k0, std::integral_constant<int, MT>{});
-      } else {
-        compute(buf, k0, std::integral_constant<int, MT>{});
-      }
-    }
+    if (valid(t) && (!PART || strip_live)) compute(buf, (kg + KG * t) * BK);
     // stage t + 1 must have landed; stages t + 2 .. t + NBUF - 1 may stay in flight
     int inflight = 0;
 #pragma unroll
