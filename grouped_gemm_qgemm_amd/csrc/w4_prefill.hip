@@ -853,13 +853,17 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   // run the same number of iterations so every wave reaches every barrier.
   const int iters = (nk + KG - 1) / KG;
   auto valid = [&](int t) { return kg + KG * t < nk; };
-  if (valid(0)) issue(kg, 0);   // (with KG = 2 and one stage, group 1 has none)
-  if (valid(1)) {
-    issue(kg + KG, 1);
-    wait_loads(nw);
-  } else {
-    wait_loads(0);
+  // prologue: stages 0 .. NBUF - 2 in flight (with KG = 2 and one stage, group 1
+  // has none), then stage 0 landed
+  int pro_inflight = 0;
+#pragma unroll
+  for (int d = 0; d < NBUF - 1; ++d) {
+    if (valid(d)) {
+      issue(kg + KG * d, d);
+      if (d > 0) pro_inflight += nw;
+    }
   }
+  wait_loads(pro_inflight);
   __syncthreads();
   auto stage = [&](int t, int buf) {
     const bool more = valid(t + NBUF - 1);
