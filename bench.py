@@ -74,21 +74,21 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     # workload: (bytes per launch, source hash the counters were taken at)
     "decode": (9240453, "76549ddc9471fadf"),
-    "prefill": (225102734, "b282a53aec04bdb5"),
-    "square": (85233546, "b282a53aec04bdb5"),
+    "prefill": (224980633, "46aa373959a6e520"),
+    "square": (85233930, "46aa373959a6e520"),
     "grouped": (367974254, "f021ee2cd95f4c65"),
     "grouped_kn": (365920284, "f021ee2cd95f4c65"),
-    "grouped_w4": (113987645, "b282a53aec04bdb5"),
+    "grouped_w4": (113938561, "46aa373959a6e520"),
     "kproj": (85680489, "5ee8476366591581"),
     "decode_gate": (9252737, "76549ddc9471fadf"),
-    "prefill_gate": (245861111, "b282a53aec04bdb5"),
+    "prefill_gate": (245829817, "46aa373959a6e520"),
     "decode_bf16": (9230896, "76549ddc9471fadf"),
-    "prefill_bf16": (245866096, "b282a53aec04bdb5"),
+    "prefill_bf16": (245911596, "46aa373959a6e520"),
     "decode_nk": (9234587, "76549ddc9471fadf"),
-    "prefill_nk": (222690850, "b282a53aec04bdb5"),
+    "prefill_nk": (222580139, "46aa373959a6e520"),
     "kvproj": (202264507, "5ee8476366591581"),
     "kvproj_e4m3": (193908141, "5ee8476366591581"),
-    "grouped_w4_bf16": (114002876, "b282a53aec04bdb5"),
+    "grouped_w4_bf16": (113988733, "46aa373959a6e520"),
     "kproj_e4m3h": (64451824, "5ee8476366591581"),
 }
 

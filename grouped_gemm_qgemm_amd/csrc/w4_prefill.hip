@@ -739,9 +739,14 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
   const uint32_t m136 = 0xC308C308u;   // bf16 pair (-136, -136)
 
   // PART (routed tiles): a wave whose column strip lies wholly past N does no
-  // arithmetic; its loads and barriers stay the same.
+  // arithmetic, and one whose second row tile holds only padding rows skips that
+  // tile's fragment reads and MFMAs (a uniform branch, no second instance of the
+  // tile body); the loads and barriers stay the same.
   static_assert(!PART || KG == 1, "partial tiles: one K group");
   const bool strip_live = n0 + wn * 64 < N;   // uniform
+  // routed tiles: row tiles past the first hold real rows only when the chunk
+  // has more than 32 rows (uniform); a padding-only row tile is skipped
+  const bool rows_hi = !PART || rows - wm * TM > 32;
   auto compute = [&](int buf, int k0) {
     const uint64_t* bw = reinterpret_cast<const uint64_t*>(lds.b[kg][buf]);
     u32x4_t afr[BK / 16][MT];
@@ -788,6 +793,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       const int kc = KH ? 4 * h + j : 2 * j + h;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        if (mt > 0 && !rows_hi) continue;
         const int row = wm * TM + mt * 32 + c32;
         afr[j][mt] = lds.a[kg][buf][row * CHUNKS + swz(row, kc)];
       }
@@ -822,6 +828,7 @@ __device__ __forceinline__ void w4_tile_dma(uint16_t* __restrict__ C, const uint
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        if (mt > 0 && !rows_hi) continue;
         if constexpr (GP) {
           part[mt][0] = mfma32x32x16_t<BF>(afr[j][mt], bq[0], part[mt][0]);
           part[mt][1] = mfma32x32x16_t<BF>(afr[j][mt], bq[1], part[mt][1]);
