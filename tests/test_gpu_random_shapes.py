@@ -3,7 +3,8 @@
 The fixed-shape tests pick their sizes by hand; this one draws them (row counts
 on and off the tile heights, any multiple of 16 columns, depths of one to many
 quantisation groups, 1 to 19 experts with skipped rows, ragged sequences with
-cached history, every epilogue flag, both types, both weight layouts) so that an
+cached history, keys or keys and values, bf16 or e4m3 cache and hidden rows,
+every epilogue flag, both types, both weight layouts) so that an
 edge a hand-picked list misses still meets the common bar
 |gpu - oracle| <= 1e-2 (|oracle| + 1). Each case prints its shape before it runs.
 
@@ -17,7 +18,7 @@ import pytest
 
 import synth
 import test_gpu_grouped_epilogue as tg
-import test_gpu_kproj as tk
+import test_gpu_kv_cache as tkv
 import test_gpu_w4_epilogue as te
 import test_gpu_w4_nk as tn
 from gpu_util import say
@@ -64,16 +65,18 @@ def grouped_case(lib, rng, i, w4):
 def kproj_case(lib, rng, i):
     B = int(rng.integers(1, 9))
     lens = [int(x) for x in rng.integers(0, 300, B)]
-    lens[int(rng.integers(0, B))] = max(1, lens[0])
+    lens[int(rng.integers(0, B))] = int(rng.integers(1, 300))
     history = [int(x) for x in rng.integers(0, 200, B)]
     D = int(rng.choice([64, 128]))
     hkv = int(rng.choice([2, 4])) if D == 64 else int(rng.choice([1, 2, 4]))
-    Kh = int(128 * rng.integers(1, 9))
-    S = int(rng.choice([16, 32, 64, 128]))
-    k = synth.kproj_inputs(seed=4000 + i, lens=lens, Kh=Kh, n_kv_heads=hkv, head_dim=D, page_size=S,
-                           num_layers=2, layer_idx=int(rng.integers(0, 2)),
-                           cache_lengths=np.array(history, np.uint32), max_len=max(lens))
-    tk.check(lib, k, f"random {i}")
+    planes = int(rng.integers(1, 3))
+    cache = str(rng.choice(["bf16", "fp8"]))
+    qgran = int(rng.choice([g for g in (32, 64, 128) if g <= D]))
+    hidden = str(rng.choice(["bf16", "fp8"]))
+    k = tkv.kv_inputs(4000 + i, lens, cache_lengths=history, Kh=int(128 * rng.integers(1, 9)), hkv=hkv, D=D,
+                      page_size=int(rng.choice([1, 16, 32, 64, 128])), planes=planes, cache=cache, qgran=qgran,
+                      layer=int(rng.integers(0, 2)), hidden=hidden)
+    tkv.check(lib, k, f"random {i}")
 
 
 @pytest.mark.parametrize("seed", range(4))
